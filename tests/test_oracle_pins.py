@@ -1,0 +1,421 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks an oracle function against a closed form, a hand-made fixture
+under tests/golden/ (with its source), an independent library routine (LAPACK
+Cholesky, scipy distances, numpy complex arithmetic), an identity of the
+mathematics, or brute force on tiny inputs.  Several tests plant a plausible
+mistake (a transposed operand, a centred covariance, a flipped rotation) in a
+copy of the computation on the CPU and show that the pin would catch it.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.spatial.distance import cdist
+
+import oracle
+from kv_cache_vector_windowed_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def random_spd_l(rng, d, cond=30.0):
+    """A random lower-triangular factor with positive diagonal (anisotropic)."""
+    l = np.tril(rng.standard_normal((d, d)) * 0.3)
+    l[np.diag_indices(d)] = np.exp(rng.uniform(0, math.log(cond), d))
+    return l
+
+
+# ============================================================ calibrate
+class TestSecondMoment:
+    def test_orthogonal_rows_closed_form(self):
+        # q_m = sqrt(M) e_m for m < d: H = (1/M) sum M e_m e_m^T = I on those rows.
+        d = 8
+        m = 8
+        q = np.sqrt(m) * np.eye(d)
+        h = oracle.second_moment(q, ridge=0.25)
+        np.testing.assert_allclose(h, 1.25 * np.eye(d), rtol=0, atol=1e-15)
+
+    def test_moment_identity_with_library_covariance(self):
+        # E[q^T q] = Cov(q) + mu mu^T (np.cov with bias=True is the library's centred form).
+        rng = np.random.default_rng(1)
+        q = rng.standard_normal((300, 16)) + rng.standard_normal(16) * 3.0
+        ridge = 1e-4
+        h = oracle.second_moment(q, ridge)
+        mu = q.mean(axis=0)
+        ref = np.cov(q, rowvar=False, bias=True) + np.outer(mu, mu) + ridge * np.eye(16)
+        np.testing.assert_allclose(h, ref, rtol=1e-12, atol=1e-12)
+        # planted mistake: a centred covariance (what np.cov alone gives) is not the moment
+        assert np.abs(h - np.cov(q, rowvar=False, bias=True)).max() > 1.0
+
+    def test_ridge_only_on_diagonal(self):
+        rng = np.random.default_rng(2)
+        q = rng.standard_normal((50, 6))
+        a = oracle.second_moment(q, 0.0)
+        b = oracle.second_moment(q, 0.5)
+        off = ~np.eye(6, dtype=bool)
+        np.testing.assert_array_equal(a[off], b[off])
+        np.testing.assert_allclose(np.diag(b) - np.diag(a), 0.5, rtol=1e-14)
+
+    def test_rejects_negative_ridge(self):
+        with pytest.raises(oracle.OracleError):
+            oracle.second_moment(np.ones((4, 2)), -1.0)
+
+
+class TestCholesky:
+    def test_textbook_2x2(self):
+        g = golden("cholesky_2x2.json")
+        l = oracle.cholesky(np.array(g["h"]))
+        np.testing.assert_allclose(l, np.array(g["l"]), rtol=0, atol=1e-15)
+
+    def test_matches_lapack(self):
+        rng = np.random.default_rng(3)
+        a = rng.standard_normal((128, 128)) / np.sqrt(128)
+        h = a @ a.T + 1e-4 * np.eye(128)
+        l = oracle.cholesky(h)
+        ref = np.linalg.cholesky(h)  # LAPACK potrf
+        assert np.abs(l - ref).max() <= 1e-12 * np.abs(ref).max()
+        assert np.linalg.norm(l @ l.T - h) <= 1e-13 * np.linalg.norm(h)
+        assert np.all(np.triu(l, 1) == 0.0)
+
+    def test_diagonal(self):
+        h = np.diag([4.0, 9.0, 0.25, 2.0])
+        np.testing.assert_allclose(oracle.cholesky(h), np.diag([2.0, 3.0, 0.5, math.sqrt(2.0)]),
+                                   rtol=0, atol=1e-15)
+
+    @pytest.mark.parametrize("h", [
+        [[1.0, 2.0], [2.0, 1.0]],                      # negative second pivot: 1 - 4
+        [[1.0, 0.0, 0.0], [0.0, 0.0, 0.0], [0.0, 0.0, 2.0]],  # exact zero pivot
+    ])
+    def test_not_spd(self, h):
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.cholesky(np.array(h))
+        assert e.value.status == oracle.ENOTSPD
+
+    def test_calibrate_on_synthetic_queries(self):
+        q = synth.queries(0, 1, 2048)
+        H, L = oracle.calibrate(q, 1e-4)
+        # L is the factor of the fp32 H: checked against LAPACK on the same fp32 matrix
+        ref = np.linalg.cholesky(H[0].astype(np.float64))
+        assert np.abs(L[0] - ref).max() <= 1e-6 * np.abs(ref).max()
+        # H is symmetric positive definite and its mean eigen-scale matches A A^T (~1)
+        assert np.all(np.linalg.eigvalsh(H[0].astype(np.float64)) > 0)
+
+
+# ============================================================ encode
+def brute_force_eq14(x, cb, l):
+    """(x - c_j) H (x - c_j)^T with H = L L^T, computed directly (no change of variables)."""
+    h = l @ l.T
+    diff = x[:, None, :] - cb[None, :, :]
+    return np.einsum("nja,ab,njb->nj", diff, h, diff)
+
+
+class TestAssignH:
+    @pytest.mark.parametrize("seed,n,c,d", [(0, 40, 24, 6), (1, 64, 64, 16), (2, 13, 5, 2)])
+    def test_matches_bruteforce_eq14(self, seed, n, c, d):
+        rng = np.random.default_rng(seed)
+        x = rng.standard_normal((n, d))
+        cb = rng.standard_normal((c, d))
+        l = random_spd_l(rng, d)
+        code, d1, d2 = oracle.assign_h(x, cb, l)
+        q = brute_force_eq14(x, cb, l)
+        srt = np.sort(q, axis=1)
+        gap = (srt[:, 1] - srt[:, 0]) / srt[:, 0]
+        ok = gap > 1e-9
+        assert ok.sum() >= n - 1
+        np.testing.assert_array_equal(code[ok], q.argmin(axis=1)[ok])
+        np.testing.assert_allclose(d1, srt[:, 0], rtol=1e-10)
+        np.testing.assert_allclose(d2, srt[:, 1], rtol=1e-10)
+
+    def test_d128_spot_rows_synthetic(self):
+        x = synth.keys(3, 1, 12, "bf16").values[0]
+        cb = synth.codebook(3, 1, 64)[0]
+        q = synth.queries(3, 1, 512)
+        _, L = oracle.calibrate(q)
+        l = L[0].astype(np.float64)
+        code, d1, _ = oracle.assign_h(x, cb, l)
+        qf = brute_force_eq14(x.astype(np.float64), cb.astype(np.float64), l)
+        np.testing.assert_array_equal(code, qf.argmin(axis=1))
+        np.testing.assert_allclose(d1, qf.min(axis=1), rtol=1e-9)
+
+    def test_transposed_factor_is_caught(self):
+        # planted mistake: using L^T in place of L changes the metric; the brute-force pin sees it
+        rng = np.random.default_rng(5)
+        x = rng.standard_normal((200, 8))
+        cb = rng.standard_normal((32, 8))
+        l = random_spd_l(rng, 8, cond=100.0)
+        wrong, _, _ = oracle.assign_h(x, cb, l.T.copy())
+        assert np.any(wrong != brute_force_eq14(x, cb, l).argmin(axis=1))
+
+    @pytest.mark.parametrize("alpha", [1.0, 3.5])
+    def test_identity_reduces_to_plain_nearest(self, alpha):
+        rng = np.random.default_rng(6)
+        x = rng.standard_normal((300, 12))
+        cb = rng.standard_normal((40, 12))
+        ref = cdist(x, cb, "sqeuclidean").argmin(axis=1)  # scipy, lowest index on ties
+        c_plain, d1p, _ = oracle.assign_h(x, cb, None)
+        c_id, _, _ = oracle.assign_h(x, cb, alpha * np.eye(12))
+        np.testing.assert_array_equal(c_plain, ref)
+        np.testing.assert_array_equal(c_id, ref)
+        np.testing.assert_allclose(d1p, cdist(x, cb, "sqeuclidean").min(axis=1), rtol=1e-12)
+
+    def test_anisotropic_hand_case(self):
+        g = golden("anisotropic_assign.json")
+        x = np.array(g["x"])
+        cb = np.array(g["codebook"])
+        code, d1, d2 = oracle.assign_h(x, cb, np.array(g["l"]))
+        assert code[0] == g["code_h_expected"]
+        assert (d1[0], d2[0]) == (min(g["d_h"]), max(g["d_h"]))
+        code, d1, d2 = oracle.assign_h(x, cb, None)
+        assert code[0] == g["code_plain_expected"]
+        assert (d1[0], d2[0]) == (min(g["d_plain"]), max(g["d_plain"]))
+
+    def test_ties_go_to_lowest_index_and_single_centroid(self):
+        x = np.zeros((1, 2))
+        cb = np.array([[1.0, 0.0], [0.0, 1.0], [-1.0, 0.0]])
+        code, d1, d2 = oracle.assign_h(x, cb, None)
+        assert code[0] == 0 and d1[0] == d2[0] == 1.0
+        code, d1, d2 = oracle.assign_h(x, cb[:1], None)
+        assert code[0] == 0 and d1[0] == 1.0 and math.isinf(d2[0])
+
+    def test_codes_in_range_and_empty(self):
+        rng = np.random.default_rng(7)
+        code, _, _ = oracle.assign_h(rng.standard_normal((50, 4)), rng.standard_normal((9, 4)), None)
+        assert code.min() >= 0 and code.max() < 9
+        code, _, _ = oracle.assign_h(np.zeros((0, 4)), rng.standard_normal((9, 4)), None)
+        assert code.size == 0
+
+
+# ============================================================ cosine blend
+class TestAssignCosine:
+    def test_beta_one_is_plain_nearest(self):
+        rng = np.random.default_rng(8)
+        x = rng.standard_normal((200, 10))
+        cb = rng.standard_normal((30, 10))
+        code, _, _ = oracle.assign_cosine(x, x[-1], cb, 1.0)
+        np.testing.assert_array_equal(code, cdist(x, cb, "sqeuclidean").argmin(axis=1))
+
+    def test_beta_zero_is_pure_query_alignment(self):
+        rng = np.random.default_rng(9)
+        x = rng.standard_normal((50, 10))
+        cb = rng.standard_normal((30, 10))
+        q = rng.standard_normal(10)
+        code, s1, _ = oracle.assign_cosine(x, q, cb, 0.0)
+        best = cdist(q[None], cb, "cosine")[0].argmin()  # scipy cosine distance = 1 - cos
+        assert np.all(code == best)
+        np.testing.assert_allclose(s1, 1.0 - cdist(q[None], cb, "cosine")[0].min(), rtol=1e-12)
+
+    def test_per_row_query(self):
+        rng = np.random.default_rng(10)
+        x = rng.standard_normal((40, 6))
+        cb = rng.standard_normal((12, 6))
+        code, _, _ = oracle.assign_cosine(x, x, cb, 0.0)
+        np.testing.assert_array_equal(code, cdist(x, cb, "cosine").argmin(axis=1))
+
+    def test_prefers_relevant_centroid_hand_case(self):
+        g = golden("blend_prefers_relevant.json")
+        for case in g["cases"]:
+            code, s1, s2 = oracle.assign_cosine(np.array(g["x"]), np.array(g["query"]),
+                                                np.array(g["codebook"]), case["beta"])
+            assert code[0] == case["code"]
+            assert s1[0] == pytest.approx(case["s1"], abs=1e-15)
+            assert s2[0] == pytest.approx(case["s2"], abs=1e-15)
+
+    def test_degenerate_zero_query_and_zero_error(self):
+        cb = np.array([[1.0, 0.0], [0.0, 1.0]])
+        code, s1, _ = oracle.assign_cosine(np.array([[0.5, 0.5]]), np.zeros(2), cb, 0.0)
+        assert code[0] == 0 and s1[0] == 0.0  # all cosines 0: lowest index
+        cb = np.array([[2.0, 2.0], [2.0, 2.0]])
+        code, s1, _ = oracle.assign_cosine(np.array([[2.0, 2.0]]), np.array([1.0, 0.0]), cb, 0.5)
+        assert code[0] == 0 and s1[0] == pytest.approx(0.5 * math.cos(math.pi / 4))
+
+    def test_rejects_bad_beta(self):
+        for beta in (-0.1, 1.1, float("nan")):
+            with pytest.raises(oracle.OracleError):
+                oracle.assign_cosine(np.zeros((1, 2)), np.zeros(2), np.ones((2, 2)), beta)
+
+
+# ============================================================ retrieval split
+class TestSelectRetrieval:
+    def test_count_arithmetic(self):
+        for n, f, want in golden("retrieval_count.json")["cases"]:
+            assert oracle.retrieval_count(n, f) == want, (n, f)
+        assert oracle.retrieval_count(10, 1.5) == -1
+        assert oracle.retrieval_count(10, float("nan")) == -1
+
+    def test_hand_ranking(self):
+        g = golden("retrieval_ranking.json")
+        ang = np.radians(np.array(g["angles_deg"], float))
+        keys = np.stack([np.cos(ang), np.sin(ang)], 1) * np.array(g["norms"])[:, None]
+        ret, bulk, _ = oracle.select_retrieval(keys, np.array(g["query"]), g["fraction"])
+        assert ret.tolist() == g["retrieval"]
+        assert bulk.tolist() == g["bulk"]
+
+    @pytest.mark.parametrize("f", [0.0, 0.05, 0.1, 0.5, 1.0])
+    def test_cover_disjoint_sorted_and_library_ranking(self, f):
+        rng = np.random.default_rng(11)
+        keys = rng.standard_normal((777, 16))
+        q = rng.standard_normal(16)
+        ret, bulk, cosv = oracle.select_retrieval(keys, q, f)
+        nr = math.ceil(f * 777)
+        assert len(ret) == nr and len(bulk) == 777 - nr
+        assert np.array_equal(np.sort(np.concatenate([ret, bulk])), np.arange(777))
+        assert np.all(np.diff(ret) > 0) and np.all(np.diff(bulk) > 0)
+        # independent ranking: scipy cosine distance, stable sort
+        dist = cdist(keys, q[None], "cosine")[:, 0]
+        np.testing.assert_allclose(1.0 - dist, cosv, atol=1e-12)
+        ref = np.sort(np.argsort(dist, kind="stable")[:nr])
+        assert np.array_equal(ret, ref)
+
+    def test_proxy_is_own_key(self):
+        keys = synth.keys(0, 1, 4096, "f32").values[0]
+        ret, _, cosv = oracle.select_retrieval(keys, keys[-1], 0.1)
+        assert 4095 in ret and cosv[-1] == pytest.approx(1.0, abs=1e-15)
+
+    def test_zero_norm_key_has_zero_cosine_and_ties_prefer_low_index(self):
+        keys = np.array([[0.0, 0.0], [1.0, 0.0], [2.0, 0.0], [0.0, 1.0]])
+        ret, bulk, cosv = oracle.select_retrieval(keys, np.array([1.0, 0.0]), 0.25)
+        assert cosv[0] == 0.0 and ret.tolist() == [1]   # keys 1 and 2 tie at cos 1
+        ret, _, _ = oracle.select_retrieval(keys, np.array([1.0, 0.0]), 0.75)
+        assert ret.tolist() == [0, 1, 2]                # keys 0 and 3 tie at cos 0
+
+
+# ============================================================ reconstruct
+def rope_complex(x, pos, base=10000.0):
+    """Independent RoPE: pair (i, i+d/2) as the complex number x_i + 1j x_{i+d/2},
+    multiplied by exp(1j * pos * base^(-2i/d))."""
+    x = np.asarray(x, float)
+    d = x.shape[-1]
+    h = d // 2
+    theta = base ** (-2.0 * np.arange(h) / d)
+    z = (x[..., :h] + 1j * x[..., h:]) * np.exp(1j * np.asarray(pos, float)[..., None] * theta)
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+class TestReconstruct:
+    def setup_method(self):
+        rng = np.random.default_rng(12)
+        self.cb = rng.standard_normal((64, 16)) * 3
+        self.n = 300
+        self.codes = rng.integers(0, 64, self.n).astype(np.uint16)
+        self.pos = np.arange(self.n, dtype=np.int32)
+
+    def test_hand_values(self):
+        for case in golden("rope_values.json")["cases"]:
+            out, _ = oracle.reconstruct(np.zeros(1, np.uint16), np.array([case["pos"]], np.int32),
+                                        np.array([case["x"]]), cur=case["pos"], window=1,
+                                        base=case["base"])
+            np.testing.assert_allclose(out[0], case["out"], atol=1e-15)
+
+    def test_window_beyond_length_is_exact_rope(self):
+        out, far = oracle.reconstruct(self.codes, self.pos, self.cb, cur=self.n - 1,
+                                      window=self.n + 5)
+        assert far == 0
+        ref = rope_complex(self.cb[self.codes], self.pos)
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+    def test_flipped_rotation_is_caught(self):
+        # planted mistake: rotating the other way (-sin) disagrees with the complex form
+        x = self.cb[self.codes]
+        wrong = rope_complex(x, -self.pos.astype(float))
+        ref = rope_complex(x, self.pos)
+        out, _ = oracle.reconstruct(self.codes, self.pos, self.cb, cur=self.n - 1, window=self.n)
+        assert np.abs(wrong - out).max() > 1.0 and np.abs(ref - out).max() < 1e-12
+
+    @pytest.mark.parametrize("window", [0, -3])
+    def test_window_nonpositive_is_all_far(self, window):
+        cur = self.n - 1
+        out, far = oracle.reconstruct(self.codes, self.pos, self.cb, cur=cur, window=window,
+                                      far_b=2048)
+        assert far == self.n
+        np.testing.assert_allclose(out, rope_complex(self.cb[self.codes], cur - 2048), atol=1e-12)
+        out, _ = oracle.reconstruct(self.codes, self.pos, self.cb, cur=cur, window=window,
+                                    far_mode=oracle.FAR_UNROTATED)
+        np.testing.assert_array_equal(out, self.cb[self.codes])
+
+    def test_window_boundary_and_far_position_independence(self):
+        cur, w = self.n - 1, 40
+        out, far = oracle.reconstruct(self.codes, self.pos, self.cb, cur=cur, window=w, far_b=77)
+        near = (cur - self.pos) < w
+        assert far == self.n - w and near.sum() == w
+        np.testing.assert_allclose(out[near], rope_complex(self.cb[self.codes[near]],
+                                                           self.pos[near]), atol=1e-12)
+        # far rows depend only on the code, not on the position
+        far_rows = out[~near]
+        far_codes = self.codes[~near]
+        for cval in np.unique(far_codes)[:10]:
+            rows = far_rows[far_codes == cval]
+            assert np.all(rows == rows[0])
+        np.testing.assert_allclose(far_rows, rope_complex(self.cb[far_codes], cur - 77), atol=1e-12)
+
+    def test_norm_preserved_per_pair_and_position_zero_identity(self):
+        out, _ = oracle.reconstruct(self.codes, self.pos, self.cb, cur=self.n - 1, window=self.n)
+        x = self.cb[self.codes]
+        h = 8
+        np.testing.assert_allclose(out[:, :h] ** 2 + out[:, h:] ** 2, x[:, :h] ** 2 + x[:, h:] ** 2,
+                                   rtol=1e-12)
+        np.testing.assert_array_equal(out[0], x[0])
+
+    def test_eq11_composition(self):
+        # RoPE(q, cur) . RoPE(k, cur - b) == RoPE(q, b) . k : the far-key rotation at cur - b
+        # reproduces the paper's query-side R_b score for an unrotated key.
+        rng = np.random.default_rng(13)
+        d, cur, b = 128, 131071, 2048
+        k = rng.standard_normal((5, d))
+        q = rng.standard_normal((1, d))
+        cb = np.concatenate([k, q])
+        codes_k = np.arange(5, dtype=np.uint16)
+        far_k, far = oracle.reconstruct(codes_k, np.zeros(5, np.int32), cb, cur=cur, window=1,
+                                        far_b=b)
+        assert far == 5
+        q_cur, _ = oracle.reconstruct(np.array([5], np.uint16), np.array([cur], np.int32), cb,
+                                      cur=cur, window=1)
+        q_b, _ = oracle.reconstruct(np.array([5], np.uint16), np.array([b], np.int32), cb,
+                                    cur=b, window=1)
+        lhs = far_k @ q_cur[0]
+        rhs = k @ q_b[0]
+        np.testing.assert_allclose(lhs, rhs, rtol=1e-10, atol=1e-9)
+
+    def test_advancing_position_moves_one_token(self):
+        w = 32
+        fars = []
+        for cur in (self.n - 1, self.n, self.n + 1):
+            _, far = oracle.reconstruct(self.codes, self.pos, self.cb, cur=cur, window=w)
+            fars.append(far)
+        assert fars[1] - fars[0] == 1 and fars[2] - fars[1] == 1
+
+    def test_window_fractions_from_the_pages(self):
+        g = golden("window_fractions.json")
+        for case in g["cases"]:
+            n = case["n"]
+            codes = np.zeros(n, np.uint16)
+            _, far = oracle.reconstruct(codes, np.arange(n, dtype=np.int32), self.cb, cur=n - 1,
+                                        window=g["window"])
+            assert far == case["far"] and far / n == pytest.approx(case["far_fraction"])
+
+    def test_invalid_code_or_position_gives_nan_row(self):
+        codes = np.array([3, 64, 5], np.uint16)
+        pos = np.array([0, 1, -1], np.int32)
+        out, _ = oracle.reconstruct(codes, pos, self.cb, cur=10, window=4)
+        assert np.all(np.isfinite(out[0])) and np.all(np.isnan(out[1])) and np.all(np.isnan(out[2]))
+
+
+# ============================================================ bf16 rounding
+class TestRoundBf16:
+    def test_hand_values(self):
+        for x, want in golden("bf16_rounding.json")["cases"]:
+            assert int(oracle.round_bf16(np.array([x]))[0]) == want, x
+
+    def test_agrees_with_fp32_exact_inputs(self):
+        # values that are exactly representable in fp32 round the same from fp32 and fp64
+        rng = np.random.default_rng(14)
+        x = (rng.standard_normal(10000) * 10.0 ** rng.uniform(-3, 3, 10000)).astype(np.float32)
+        np.testing.assert_array_equal(oracle.round_bf16(x.astype(np.float64)),
+                                      synth.f32_to_bf16_bits(x))
