@@ -1,0 +1,201 @@
+/* a2ats.h -- C ABI of the A2ATS key-cache hot path on gfx950 (MI355X).
+ *
+ * Five operations of the A2ATS method ("A2ATS: Retrieval-Based KV Cache Reduction via
+ * Windowed Rotary Position Embedding and Query-Aware Vector Quantization", as adapted and
+ * documented by the "A2ATS-adapted" VeloxQuant-MLX pages):
+ *   calibrate          H = E[q^T q] + ridge I and its Cholesky factor L
+ *   encode             H-weighted (or plain) nearest-centroid codes, uint16
+ *   assign_cosine      the cosine-blend assignment of the decode path
+ *   select_retrieval   top-fraction cosine split of token indices
+ *   reconstruct        centroid gather + windowed RoPE
+ *
+ * Conventions shared by every call:
+ *  - All array pointers are DEVICE pointers owned by the caller, row-major, contiguous,
+ *    and must not alias one another unless stated.  The library never allocates device
+ *    memory and keeps no state between calls (apart from optional profiling, below).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every call
+ *    enqueues its kernels on that stream and returns without waiting, except
+ *    a2ats_calibrate, which waits for its own work so it can report a non-positive-definite
+ *    input.
+ *  - Scratch memory is passed in as `workspace` (device, 256-byte aligned) of at least the
+ *    size returned by the matching *_workspace() query; its contents on entry are ignored.
+ *  - Arguments are validated on the host before anything is launched; an invalid call
+ *    returns a negative status and launches nothing.  Conditions that only the data can
+ *    reveal (an out-of-range code or position) do not fault: they produce NaN outputs as
+ *    documented per call.
+ *  - Results are deterministic: the same inputs give bitwise identical outputs.
+ *  - This header needs no HIP headers.
+ */
+#ifndef A2ATS_H
+#define A2ATS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define A2ATS_VERSION 1
+
+/* Status codes. */
+#define A2ATS_OK 0
+#define A2ATS_EINVAL (-1)     /* a size, pointer or parameter is invalid */
+#define A2ATS_EDTYPE (-2)     /* unsupported dtype */
+#define A2ATS_EWORKSPACE (-3) /* workspace missing, too small or misaligned */
+#define A2ATS_ENOTSPD (-4)    /* calibrate: H is not positive definite */
+#define A2ATS_EHIP (-5)       /* the HIP runtime reported an error */
+
+/* Element types of key / query / output arrays. */
+#define A2ATS_F32 0
+#define A2ATS_BF16 1
+
+/* Far-token treatment in reconstruct. */
+#define A2ATS_FAR_FIXED_OFFSET 0 /* rotate far keys at position cur_pos - far_offset */
+#define A2ATS_FAR_UNROTATED 1    /* leave far keys unrotated */
+
+/* Head dimension supported by encode, select_retrieval and reconstruct. */
+#define A2ATS_HEAD_DIM 128
+
+/* Human-readable text for a status code (static storage). */
+const char* a2ats_strerror(int status);
+
+/* A2ATS_VERSION of the library actually loaded. */
+int a2ats_version(void);
+
+/* ---------------------------------------------------------------------------------------
+ * Retrieval-set size: ceil(fraction * n) evaluated as an fp64 product, as the API page
+ * "veloxquant_mlx.quantizers.a2ats module" defines for a2ats_select_retrieval_set.
+ * Returns -1 if n < 0 or fraction is NaN or outside [0, 1].  Host only.
+ */
+int64_t a2ats_retrieval_count(int64_t n, double fraction);
+
+/* ---------------------------------------------------------------------------------------
+ * calibrate -- "veloxquant_mlx.quantizers.a2ats module", a2ats_query_second_moment (Eq. 10)
+ * and a2ats_cholesky_factor (Eq. 15).
+ *
+ *   queries  [heads, m, d] fp32   post-position-embedding query states
+ *   h_out    [heads, d, d] fp32   H = (1/m) sum_r q_r^T q_r + ridge I   (uncentred mean)
+ *   l_out    [heads, d, d] fp32   lower-triangular L with L L^T = H, upper triangle zero;
+ *                                 factored in fp64 from the fp32 H written to h_out
+ * Accumulation is fp64; each output is rounded once to fp32.
+ * Requires 1 <= d <= 128, m >= 1, heads >= 1, ridge >= 0.  Waits for completion.
+ * Returns A2ATS_ENOTSPD (h_out still written, l_out undefined) if a pivot is <= 0.
+ */
+size_t a2ats_calibrate_workspace(int64_t heads, int64_t m, int64_t d);
+int a2ats_calibrate(const float* queries, int64_t heads, int64_t m, int64_t d, double ridge,
+                    float* h_out, float* l_out, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * encode -- "veloxquant_mlx.quantizers.a2ats module", a2ats_h_weighted_assignment
+ * (Eq. 14 through the Eq. 17 identity): for every selected key k of head h,
+ *     codes[h, row] = argmin_j (k - c_j) H (k - c_j)^T,   H = L L^T,
+ * with chol == NULL meaning H = I (plain nearest centroid, the bulk path).  Ties go to the
+ * lowest centroid index.  The minimiser is exact: a fp16 MFMA pass proposes candidates
+ * under a rigorous error bound and fp64 arithmetic decides every close call.
+ *
+ *   keys      [heads, n, d]  fp32 or bf16 (keys_dtype); d must be 128
+ *   idx       [heads, n_idx] int32 row indices in [0, n) to encode, or NULL for all rows
+ *             (then n_idx is ignored); only the listed rows of codes/dist are written;
+ *             entries outside [0, n) are skipped
+ *   codebook  [heads, c, d]  fp32 centroids in the original (un-transformed) space
+ *   chol      [heads, d, d]  fp32 lower-triangular L, or NULL
+ *   codes     [heads, n]     uint16 output; 1 <= c <= 65536
+ *   dist      [heads, n]     fp32 output (k - c_code) H (k - c_code)^T, or NULL
+ *   stats     device a2ats_encode_stats, or NULL: counters of how each key was decided
+ * Keys with an element of magnitude >= 65520 (outside fp16) are decided entirely in fp64.
+ * Returns without waiting.
+ */
+typedef struct a2ats_encode_stats {
+  uint32_t keys;        /* keys encoded */
+  uint32_t direct;      /* decided by the MFMA pass alone */
+  uint32_t reranked;    /* decided after an fp64 rerank of the leading candidates */
+  uint32_t rescanned;   /* decided by a second candidate pass over the codebook */
+  uint32_t full_scan;   /* decided by an fp64 scan of the whole codebook */
+  uint32_t reserved[3];
+} a2ats_encode_stats;
+
+size_t a2ats_encode_workspace(int64_t heads, int64_t n, int64_t d, int64_t c);
+int a2ats_encode(const void* keys, int keys_dtype, int64_t heads, int64_t n, int64_t d,
+                 const int32_t* idx, int64_t n_idx, const float* codebook, int64_t c,
+                 const float* chol, uint16_t* codes, float* dist, a2ats_encode_stats* stats,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * assign_cosine -- "veloxquant_mlx.quantizers.a2ats module", a2ats_query_aware_assignment:
+ *     score_j = beta * (-e_j / max_i e_i) + (1 - beta) * cos(q, c_j),  e_j = ||x - c_j||^2,
+ *     codes[h, r] = argmax_j score_j  (lowest index on ties).
+ * The error term is 0 when max_i e_i == 0; a zero-norm q or c_j has cosine 0.  beta = 1 is
+ * plain nearest centroid.  Computed in fp64.
+ *
+ *   x         [heads, n, d]   fp32 or bf16 (x_dtype)
+ *   query     [heads, nq, d]  same dtype as x; nq == 1 (one query per head) or nq == n
+ *   codebook  [heads, c, d]   fp32
+ *   codes     [heads, n]      uint16 output
+ * Requires 1 <= d <= 256 and 1 <= c <= 65536, beta in [0, 1].  No workspace.
+ */
+int a2ats_assign_cosine(const void* x, int x_dtype, int64_t heads, int64_t n, int64_t d,
+                        const void* query, int64_t nq, const float* codebook, int64_t c,
+                        double beta, uint16_t* codes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * select_retrieval -- "veloxquant_mlx.quantizers.a2ats module", a2ats_select_retrieval_set:
+ * per head, the n_r = a2ats_retrieval_count(n, fraction) keys with the largest cosine to
+ * the query form the retrieval set, the other n - n_r the bulk.  Equal scores keep the
+ * lower index first.  Both outputs are ascending and together cover 0..n-1 exactly once.
+ * A zero-norm key scores 0.  The ranking score is k.q / ||k|| in fp32 (||q|| is a per-head
+ * constant and does not change the order).
+ *
+ *   keys           [heads, n, d] fp32 or bf16; d must be 128
+ *   query          [heads, d]    same dtype as keys (the proxy query)
+ *   retrieval_idx  [heads, n_r]      int32 output
+ *   bulk_idx       [heads, n - n_r]  int32 output
+ * Requires n <= 2^31 - 1.
+ */
+size_t a2ats_select_retrieval_workspace(int64_t heads, int64_t n);
+int a2ats_select_retrieval(const void* keys, int keys_dtype, int64_t heads, int64_t n,
+                           int64_t d, const void* query, double fraction,
+                           int32_t* retrieval_idx, int32_t* bulk_idx, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * reconstruct -- "A2ATS-adapted -- Windowed RoPE + Query-Aware Retrieval VQ", How it works
+ * steps 3-4, with the far-token rule of the "paper fidelity" section (Eq. 11-12):
+ *   x = codebook[h, codes[b, h, t]]                      (the pre-RoPE key)
+ *   near  <=>  0 <= cur_pos - positions[b, t] < window:  RoPE(x, positions[b, t])
+ *   far, A2ATS_FAR_FIXED_OFFSET:                          RoPE(x, cur_pos - far_offset)
+ *   far, A2ATS_FAR_UNROTATED:                             x
+ * RoPE rotates the half-split pairs (i, i + d/2) by pos * rope_base^(-2i/d); angles, sines
+ * and the rotation are evaluated in fp64 and rounded once to out_dtype.
+ * window <= 0 makes every token far; window > cur_pos makes every valid token near.
+ *
+ *   codes      [batch, heads, n] uint16
+ *   positions  [batch, n]        int32 absolute positions, shared by the heads
+ *   codebook   [heads, c, d]     fp32; d must be 128
+ *   out        [batch, heads, n, d]  fp32 or bf16 (out_dtype)
+ * A token whose code is >= c or whose position is negative gets a row of NaN.
+ * Requires cur_pos >= 0 and rope_base > 0.
+ */
+size_t a2ats_reconstruct_workspace(int64_t d, int64_t cur_pos, int64_t window);
+int a2ats_reconstruct(const uint16_t* codes, const int32_t* positions, int64_t batch,
+                      int64_t heads, int64_t n, int64_t d, const float* codebook, int64_t c,
+                      int64_t cur_pos, int64_t window, int64_t far_offset, int far_mode,
+                      double rope_base, void* out, int out_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Kernel timing (diagnostics).  While enabled, every kernel the library launches is
+ * bracketed by HIP events recorded on its stream.  a2ats_profile_read waits for those
+ * events and writes one line per kernel name, "name<TAB>launches<TAB>total_ms\n", into
+ * buf (NUL-terminated, truncated to len); it returns the number of bytes needed.
+ * Not thread-safe; intended for benchmarks.
+ */
+int a2ats_profile_enable(int on);
+int a2ats_profile_reset(void);
+int64_t a2ats_profile_read(char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* A2ATS_H */

@@ -1,0 +1,243 @@
+"""A2ATS key-cache hot path on MI355X (gfx950): Python binding of liba2ats.so.
+
+Every function here only marshals arguments: it checks tensor placement, dtypes and shapes,
+allocates outputs and the workspace with torch on the same device, and calls the C ABI
+declared in include/a2ats.h on torch's current HIP stream.  All computation happens in the
+library's kernels.  If the library has not been built, the functions raise.
+
+Operations (see include/a2ats.h for the exact contracts):
+    calibrate(queries, ridge)            -> (H, L)
+    encode(keys, codebook, chol, ...)    -> codes [, dist]
+    assign_cosine(x, query, codebook, beta) -> codes
+    select_retrieval(keys, query, fraction) -> (retrieval_idx, bulk_idx)
+    reconstruct(codes, positions, codebook, cur_pos, window, ...) -> rotated keys
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liba2ats.so")
+
+F32, BF16 = 0, 1
+FAR_FIXED_OFFSET, FAR_UNROTATED = 0, 1
+HEAD_DIM = 128
+STATUS = {0: "ok", -1: "EINVAL", -2: "EDTYPE", -3: "EWORKSPACE", -4: "ENOTSPD", -5: "EHIP"}
+
+_lib = None
+
+
+class A2ATSError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (what, STATUS.get(status, "?"), status))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("liba2ats.so is not built (run __graft_entry__.build() or "
+                               "python kv_cache_vector_windowed_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, i32, sz, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
+        L.a2ats_strerror.argtypes, L.a2ats_strerror.restype = [i32], ctypes.c_char_p
+        L.a2ats_version.argtypes, L.a2ats_version.restype = [], i32
+        L.a2ats_retrieval_count.argtypes, L.a2ats_retrieval_count.restype = [i64, dbl], i64
+        L.a2ats_calibrate_workspace.argtypes, L.a2ats_calibrate_workspace.restype = [i64, i64, i64], sz
+        L.a2ats_calibrate.argtypes = [p, i64, i64, i64, dbl, p, p, p, sz, p]
+        L.a2ats_encode_workspace.argtypes, L.a2ats_encode_workspace.restype = [i64, i64, i64, i64], sz
+        L.a2ats_encode.argtypes = [p, i32, i64, i64, i64, p, i64, p, i64, p, p, p, p, p, sz, p]
+        L.a2ats_assign_cosine.argtypes = [p, i32, i64, i64, i64, p, i64, p, i64, dbl, p, p]
+        L.a2ats_select_retrieval_workspace.argtypes = [i64, i64]
+        L.a2ats_select_retrieval_workspace.restype = sz
+        L.a2ats_select_retrieval.argtypes = [p, i32, i64, i64, i64, p, dbl, p, p, p, sz, p]
+        L.a2ats_reconstruct_workspace.argtypes = [i64, i64, i64]
+        L.a2ats_reconstruct_workspace.restype = sz
+        L.a2ats_reconstruct.argtypes = [p, p, i64, i64, i64, i64, p, i64, i64, i64, i64, i32, dbl,
+                                        p, i32, p, sz, p]
+        L.a2ats_profile_enable.argtypes, L.a2ats_profile_enable.restype = [i32], i32
+        L.a2ats_profile_reset.argtypes, L.a2ats_profile_reset.restype = [], i32
+        L.a2ats_profile_read.argtypes, L.a2ats_profile_read.restype = [ctypes.c_char_p, sz], i64
+        for f in ("a2ats_calibrate", "a2ats_encode", "a2ats_assign_cosine",
+                  "a2ats_select_retrieval", "a2ats_reconstruct"):
+            getattr(L, f).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise A2ATSError(status, what)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("expected float32 or bfloat16, got %s" % t.dtype)
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns blocks aligned to at least 512 bytes
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def retrieval_count(n: int, fraction: float) -> int:
+    """ceil(fraction * n) in fp64; -1 for an invalid fraction."""
+    return int(lib().a2ats_retrieval_count(int(n), float(fraction)))
+
+
+def calibrate(queries: torch.Tensor, ridge: float = 1e-4):
+    """queries [heads, m, d] fp32 -> (H [heads, d, d], L [heads, d, d]) fp32.  Waits."""
+    _dev(queries, "queries")
+    if queries.dtype != torch.float32 or queries.dim() != 3:
+        raise ValueError("queries must be [heads, m, d] float32")
+    heads, m, d = queries.shape
+    h = torch.empty((heads, d, d), dtype=torch.float32, device=queries.device)
+    l = torch.empty_like(h)
+    ws = _workspace(lib().a2ats_calibrate_workspace(heads, m, d), queries.device)
+    _check(lib().a2ats_calibrate(_ptr(queries), heads, m, d, float(ridge), _ptr(h), _ptr(l),
+                                 _ptr(ws), ws.numel(), _stream(queries.device)), "calibrate")
+    return h, l
+
+
+def encode(keys: torch.Tensor, codebook: torch.Tensor, chol: torch.Tensor | None = None,
+           idx: torch.Tensor | None = None, codes: torch.Tensor | None = None,
+           want_dist: bool = False, stats: torch.Tensor | None = None):
+    """Nearest-centroid codes under H = L L^T (plain when chol is None).
+
+    keys [heads, n, d] fp32/bf16, codebook [heads, c, d] fp32, chol [heads, d, d] fp32,
+    idx [heads, n_idx] int32 rows to encode (others of `codes` untouched), codes [heads, n]
+    uint16 to write into (allocated when None).  Returns codes, or (codes, dist) with
+    want_dist.  stats: optional int32 tensor of 8 elements receiving a2ats_encode_stats.
+    """
+    _dev(keys, "keys")
+    _dev(codebook, "codebook")
+    heads, n, d = keys.shape
+    c = codebook.shape[1]
+    if codebook.dtype != torch.float32 or codebook.shape != (heads, c, d):
+        raise ValueError("codebook must be [heads, c, d] float32")
+    if chol is not None:
+        _dev(chol, "chol")
+        if chol.dtype != torch.float32 or chol.shape != (heads, d, d):
+            raise ValueError("chol must be [heads, d, d] float32")
+    n_idx = 0
+    if idx is not None:
+        _dev(idx, "idx")
+        if idx.dtype != torch.int32 or idx.dim() != 2 or idx.shape[0] != heads:
+            raise ValueError("idx must be [heads, n_idx] int32")
+        n_idx = idx.shape[1]
+    if codes is None:
+        codes = torch.zeros((heads, n), dtype=torch.uint16, device=keys.device)
+    else:
+        _dev(codes, "codes")
+    dist = torch.zeros((heads, n), dtype=torch.float32, device=keys.device) if want_dist else None
+    if stats is not None:
+        _dev(stats, "stats")
+    ws = _workspace(lib().a2ats_encode_workspace(heads, n, d, c), keys.device)
+    _check(lib().a2ats_encode(_ptr(keys), _dtype_code(keys), heads, n, d, _ptr(idx), n_idx,
+                              _ptr(codebook), c, _ptr(chol), _ptr(codes), _ptr(dist),
+                              _ptr(stats), _ptr(ws), ws.numel(), _stream(keys.device)), "encode")
+    return (codes, dist) if want_dist else codes
+
+
+def assign_cosine(x: torch.Tensor, query: torch.Tensor, codebook: torch.Tensor, beta: float):
+    """x [heads, n, d], query [heads, nq, d] (nq in {1, n}), codebook [heads, c, d] -> codes."""
+    _dev(x, "x")
+    _dev(query, "query")
+    _dev(codebook, "codebook")
+    heads, n, d = x.shape
+    if query.dtype != x.dtype or query.dim() != 3 or query.shape[0] != heads:
+        raise ValueError("query must be [heads, nq, d] in the dtype of x")
+    codes = torch.zeros((heads, n), dtype=torch.uint16, device=x.device)
+    _check(lib().a2ats_assign_cosine(_ptr(x), _dtype_code(x), heads, n, d, _ptr(query),
+                                     query.shape[1], _ptr(codebook), codebook.shape[1],
+                                     float(beta), _ptr(codes), _stream(x.device)), "assign_cosine")
+    return codes
+
+
+def select_retrieval(keys: torch.Tensor, query: torch.Tensor, fraction: float):
+    """keys [heads, n, d], query [heads, d] -> (retrieval_idx [heads, n_r], bulk [heads, n-n_r])."""
+    _dev(keys, "keys")
+    _dev(query, "query")
+    heads, n, d = keys.shape
+    if query.dtype != keys.dtype or query.shape != (heads, d):
+        raise ValueError("query must be [heads, d] in the dtype of keys")
+    n_r = retrieval_count(n, fraction)
+    if n_r < 0:
+        raise A2ATSError(-1, "select_retrieval")
+    ret = torch.empty((heads, n_r), dtype=torch.int32, device=keys.device)
+    bulk = torch.empty((heads, n - n_r), dtype=torch.int32, device=keys.device)
+    ws = _workspace(lib().a2ats_select_retrieval_workspace(heads, n), keys.device)
+    _check(lib().a2ats_select_retrieval(_ptr(keys), _dtype_code(keys), heads, n, d, _ptr(query),
+                                        float(fraction), _ptr(ret), _ptr(bulk), _ptr(ws),
+                                        ws.numel(), _stream(keys.device)), "select_retrieval")
+    return ret, bulk
+
+
+def reconstruct(codes: torch.Tensor, positions: torch.Tensor, codebook: torch.Tensor,
+                cur_pos: int, window: int, far_offset: int = 2048,
+                far_mode: int = FAR_FIXED_OFFSET, rope_base: float = 10000.0,
+                out_dtype: torch.dtype = torch.float32, out: torch.Tensor | None = None):
+    """codes [batch, heads, n] uint16, positions [batch, n] int32, codebook [heads, c, d]
+    -> out [batch, heads, n, d] (out_dtype)."""
+    _dev(codes, "codes")
+    _dev(positions, "positions")
+    _dev(codebook, "codebook")
+    batch, heads, n = codes.shape
+    c, d = codebook.shape[1], codebook.shape[2]
+    if positions.dtype != torch.int32 or positions.shape != (batch, n):
+        raise ValueError("positions must be [batch, n] int32")
+    if out is None:
+        out = torch.empty((batch, heads, n, d), dtype=out_dtype, device=codes.device)
+    else:
+        _dev(out, "out")
+    ws = _workspace(lib().a2ats_reconstruct_workspace(d, int(cur_pos), int(window)), codes.device)
+    _check(lib().a2ats_reconstruct(_ptr(codes), _ptr(positions), batch, heads, n, d,
+                                   _ptr(codebook), c, int(cur_pos), int(window), int(far_offset),
+                                   int(far_mode), float(rope_base), _ptr(out), _dtype_code(out),
+                                   _ptr(ws), ws.numel(), _stream(codes.device)), "reconstruct")
+    return out
+
+
+# ----------------------------------------------------------------- kernel timing
+def profile_enable(on: bool = True):
+    lib().a2ats_profile_enable(1 if on else 0)
+
+
+def profile_reset():
+    lib().a2ats_profile_reset()
+
+
+def profile_read() -> dict:
+    """{kernel name: (launches, total_ms)} for kernels launched while profiling was on."""
+    n = lib().a2ats_profile_read(None, 0)
+    buf = ctypes.create_string_buffer(int(n) + 16)
+    lib().a2ats_profile_read(buf, len(buf))
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, ms = line.split("\t")
+        out[name] = (int(cnt), float(ms))
+    return out

@@ -1,0 +1,115 @@
+// Shared host/device plumbing of the gfx950 library: status handling, workspace carving,
+// kernel launch with optional event timing, and small device helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+#include <cstring>
+
+#include "a2ats.h"
+
+namespace a2ats {
+
+// ------------------------------------------------------------------ host side
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Carves aligned sub-buffers from the caller's workspace; `base == nullptr` only sizes.
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    size_t off = used;
+    used = align_up(used + count * sizeof(T));
+    return base ? reinterpret_cast<T*>(base + off) : nullptr;
+  }
+};
+
+inline bool ws_ok(const void* ws, size_t have, size_t need) {
+  if (need == 0) return true;
+  if (!ws || have < need) return false;
+  return (reinterpret_cast<uintptr_t>(ws) % kAlign) == 0;
+}
+
+// Records start/stop events around a launch when profiling is on (see a2ats_profile_*).
+void profile_begin(const char* name, hipStream_t s, int* slot);
+void profile_end(int slot, hipStream_t s);
+
+template <typename K, typename... Args>
+inline int launch(const char* name, K kernel, dim3 grid, dim3 block, size_t shmem,
+                  hipStream_t s, Args... args) {
+  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return A2ATS_OK;
+  int slot = -1;
+  profile_begin(name, s, &slot);
+  hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+  hipError_t e = hipGetLastError();
+  profile_end(slot, s);
+  return e == hipSuccess ? A2ATS_OK : A2ATS_EHIP;
+}
+
+// Allows a kernel more than the default dynamic LDS (gfx950 has 160 KB per workgroup).
+template <typename K>
+inline int set_dynamic_lds(K kernel, size_t bytes) {
+  if (bytes <= 65536) return A2ATS_OK;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  return e == hipSuccess ? A2ATS_OK : A2ATS_EHIP;
+}
+
+#define A2ATS_TRY(expr)          \
+  do {                           \
+    int st_ = (expr);            \
+    if (st_ != A2ATS_OK) return st_; \
+  } while (0)
+
+// Number of workgroups for a 1-D launch, capped to keep the grid size in range.
+inline unsigned grid_for(int64_t items, int per_block, int64_t cap = (int64_t)1 << 30) {
+  int64_t g = (items + per_block - 1) / per_block;
+  if (g > cap) g = cap;
+  return (unsigned)(g < 0 ? 0 : g);
+}
+
+// ------------------------------------------------------------------ device side
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Loads element i of a key/query row stored as fp32 (dt == A2ATS_F32) or bf16.
+__device__ __forceinline__ float load_elem(const void* p, int dt, int64_t i) {
+  return dt == A2ATS_F32 ? static_cast<const float*>(p)[i]
+                         : bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+}
+
+// Round an fp64 value to bf16 (nearest, ties to even) directly, without passing through
+// fp32: keep 8 significant bits of the fp64 significand, then reinterpret.
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+  uint16_t s16 = (u >> 63) ? 0x8000 : 0;
+  uint64_t a = u & 0x7FFFFFFFFFFFFFFFull;
+  if (a > 0x7FF0000000000000ull) return s16 | 0x7FC0;  // NaN
+  double ad = __longlong_as_double(static_cast<long long>(a));
+  if (ad < 0x1p-126) {
+    // bf16 subnormal range: spacing 2^-133; round ad / 2^-133 to an integer, ties to even
+    double q = ad * 0x1p133;
+    double fl = floor(q);
+    double rem = q - fl;
+    uint32_t m = static_cast<uint32_t>(fl);
+    if (rem > 0.5 || (rem == 0.5 && (m & 1u))) m += 1;
+    return s16 | static_cast<uint16_t>(m);  // m == 128 is the smallest normal
+  }
+  // normal range: round the significand at fp64 bit 45 (52 - 7 stored bf16 bits)
+  uint64_t r = (a + 0x00000FFFFFFFFFFFull + ((a >> 45) & 1ull)) & ~0x00001FFFFFFFFFFFull;
+  double rd = __longlong_as_double(static_cast<long long>(r));
+  if (rd >= 0x1p128) return s16 | 0x7F80;  // overflow to infinity
+  float f = static_cast<float>(rd);         // exact: at most 8 significant bits
+  return s16 | static_cast<uint16_t>(__float_as_uint(f) >> 16);
+}
+
+}  // namespace a2ats

@@ -1,0 +1,451 @@
+// select_retrieval: per head, the ceil(f * n) keys with the largest cosine to the proxy
+// query form the retrieval set, the rest the bulk; both outputs ascending.
+// "veloxquant_mlx.quantizers.a2ats module", a2ats_select_retrieval_set.
+//
+// Ranking score: s = k.q / ||k|| in fp32 (||q|| is constant per head).  Each score is
+// mapped to an order-preserving 32-bit key u; the selection order is the 64-bit key
+// (u << 32) | (0xffffffff - index), so equal scores keep the lower index first and every
+// element has a distinct key.
+//
+// Kernels (4 launches, no host round trip):
+//   sel_init     per head: ||q|| and the binning scale; zeroes histograms and counters.
+//   sel_score    HBM-bound pass over the keys: writes u, builds a 4096-bin histogram of a
+//                monotone binning of s/||q|| in [-1, 1]; the last workgroup of each head
+//                (detected with a fenced atomic counter, no waiting) finds the bin b* that
+//                holds the n_r-th largest score.
+//   sel_collect  pass over u: counts keys above b* per block and appends the keys in b* to
+//                a candidate list; the last workgroup of each head radix-selects the exact
+//                n_r-th largest 64-bit key among the candidates and turns the per-block
+//                counts into output offsets.
+//   sel_scatter  pass over u: ordered compaction of the predicate key64 >= threshold into
+//                the retrieval and bulk index arrays.
+#include "common.hpp"
+
+namespace a2ats {
+namespace {
+
+constexpr int kD = A2ATS_HEAD_DIM;
+constexpr int kBins = 4096;
+constexpr int kScoreChunk = 1024;   // keys per sel_score workgroup
+constexpr int kBlock = 4096;        // scores per sel_collect / sel_scatter workgroup
+
+struct HeadInfo {
+  float inv_scale;       // 2048 / ||q||, or 0 when q == 0
+  int n_r;               // retrieval-set size
+  int bstar;             // bin holding the n_r-th largest score (kBins: nothing selected)
+  int count_above;       // keys in bins above bstar
+  int n_cand;            // keys in bin bstar (candidate list length)
+  unsigned done_score;   // workgroups of sel_score finished
+  unsigned done_collect; // workgroups of sel_collect finished
+  int pad;
+  unsigned long long thr; // 64-bit key of the n_r-th largest element
+};
+
+__device__ __forceinline__ unsigned order_key(float s) {
+  if (s == 0.0f) s = 0.0f;  // -0 and +0 rank equal
+  unsigned b = __float_as_uint(s);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(unsigned u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// Monotone non-decreasing in s: a positive scale, an add and floor all preserve order.
+__device__ __forceinline__ int bin_of(unsigned u, float inv_scale) {
+  float s = key_value(u);
+  float v = floorf(__fmaf_rn(s, inv_scale, 2048.0f));  // one rounding, identical everywhere
+  v = fminf(fmaxf(v, 0.0f), (float)(kBins - 1));
+  return (int)v;
+}
+
+__device__ __forceinline__ unsigned long long key64(unsigned u, int64_t idx) {
+  return ((unsigned long long)u << 32) | (unsigned long long)(0xFFFFFFFFu - (unsigned)idx);
+}
+
+__device__ __forceinline__ unsigned atomic_load_u32(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(256) void sel_init(const void* __restrict__ query, int dt, int64_t n,
+                                                double fraction, HeadInfo* __restrict__ info,
+                                                unsigned* __restrict__ hist,
+                                                unsigned* __restrict__ sel_extra, int nblk) {
+  const int head = blockIdx.x;
+  const int t = threadIdx.x;
+  __shared__ float red[4];
+  float v = 0.f;
+  if (t < kD) {
+    float x = load_elem(query, dt, (int64_t)head * kD + t);
+    v = x * x;
+  }
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((t & 63) == 0) red[t >> 6] = v;
+  __syncthreads();
+  for (int i = t; i < kBins; i += 256) hist[(int64_t)head * kBins + i] = 0u;
+  for (int i = t; i < nblk; i += 256) sel_extra[(int64_t)head * nblk + i] = 0u;
+  if (t == 0) {
+    float qn = sqrtf(red[0] + red[1] + red[2] + red[3]);
+    HeadInfo h;
+    h.inv_scale = qn > 0.f ? 2048.0f / qn : 0.f;
+    h.n_r = (int)ceil(fraction * (double)n);
+    h.bstar = kBins;
+    h.count_above = 0;
+    h.n_cand = 0;
+    h.done_score = 0u;
+    h.done_collect = 0u;
+    h.pad = 0;
+    h.thr = ~0ull;
+    info[head] = h;
+  }
+}
+
+// 16 lanes per key; each lane covers 8 consecutive elements of the 128.
+template <int DT>
+__global__ __launch_bounds__(256) void sel_score(const void* __restrict__ keys,
+                                                 const void* __restrict__ query, int64_t n,
+                                                 int wg_per_head, HeadInfo* __restrict__ info,
+                                                 unsigned* __restrict__ scores,
+                                                 unsigned* __restrict__ hist) {
+  const int head = blockIdx.x / wg_per_head;
+  const int wg = blockIdx.x % wg_per_head;
+  const int t = threadIdx.x;
+  const int sub = t & 15;
+  __shared__ unsigned lh[kBins];
+  __shared__ int is_last;
+  for (int i = t; i < kBins; i += 256) lh[i] = 0u;
+  float qv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qv[e] = load_elem(query, DT, (int64_t)head * kD + sub * 8 + e);
+  const float inv = info[head].inv_scale;
+  __syncthreads();
+  const int64_t k_begin = (int64_t)wg * kScoreChunk;
+  const int64_t k_end = k_begin + kScoreChunk < n ? k_begin + kScoreChunk : n;
+  const int64_t hoff = (int64_t)head * n;
+  for (int64_t k0 = k_begin; k0 < k_end; k0 += 16 * 4) {
+    float dot[4], nrm[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t key = k0 + u * 16 + (t >> 4);
+      dot[u] = 0.f;
+      nrm[u] = 0.f;
+      if (key < k_end) {
+        float x[8];
+        if (DT == A2ATS_BF16) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(
+              static_cast<const uint16_t*>(keys) + (hoff + key) * kD + sub * 8);
+          const unsigned w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[2 * e] = __uint_as_float(w[e] << 16);
+            x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+          }
+        } else {
+          const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(keys) +
+                                                            (hoff + key) * kD + sub * 8);
+          float4 a = p[0], b = p[1];
+          x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+          x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          dot[u] += x[e] * qv[e];
+          nrm[u] += x[e] * x[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        dot[u] += __shfl_xor(dot[u], o);
+        nrm[u] += __shfl_xor(nrm[u], o);
+      }
+      const int64_t key = k0 + u * 16 + (t >> 4);
+      if (sub == 0 && key < k_end) {
+        const float s = nrm[u] > 0.f ? dot[u] / sqrtf(nrm[u]) : 0.f;
+        const unsigned ukey = order_key(s);
+        scores[hoff + key] = ukey;
+        atomicAdd(&lh[bin_of(ukey, inv)], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = t; i < kBins; i += 256)
+    if (lh[i]) atomicAdd(&hist[(int64_t)head * kBins + i], lh[i]);
+  __threadfence();
+  __syncthreads();
+  if (t == 0) is_last = (atomicAdd(&info[head].done_score, 1u) == (unsigned)wg_per_head - 1);
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+  // Last workgroup of this head: locate the bin of the n_r-th largest score.
+  __shared__ unsigned part[256];
+  const int n_r = info[head].n_r;
+  unsigned s16 = 0;
+  // thread t owns bins [kBins - 16(t+1), kBins - 16t), i.e. descending ranges
+  for (int i = 0; i < 16; ++i) {
+    int b = kBins - 16 * (t + 1) + i;
+    unsigned c = atomic_load_u32(&hist[(int64_t)head * kBins + b]);
+    lh[b] = c;
+    s16 += c;
+  }
+  part[t] = s16;
+  __syncthreads();
+  if (t == 0) {
+    int bstar = kBins, above = 0;
+    if (n_r > 0) {
+      unsigned cum = 0;
+      for (int i = 0; i < 256 && bstar == kBins; ++i) {
+        if (cum + part[i] >= (unsigned)n_r) {
+          for (int b = kBins - 16 * i - 1; b >= kBins - 16 * (i + 1); --b) {
+            if (cum + lh[b] >= (unsigned)n_r) {
+              bstar = b;
+              above = (int)cum;
+              break;
+            }
+            cum += lh[b];
+          }
+        } else {
+          cum += part[i];
+        }
+      }
+    }
+    info[head].bstar = bstar;
+    info[head].count_above = above;
+  }
+}
+
+__global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ scores, int64_t n,
+                                                   int nblk, HeadInfo* __restrict__ info,
+                                                   unsigned* __restrict__ above_blk,
+                                                   unsigned long long* __restrict__ cand,
+                                                   unsigned* __restrict__ sel_extra) {
+  const int head = blockIdx.x / nblk;
+  const int blk = blockIdx.x % nblk;
+  const int t = threadIdx.x;
+  const int bstar = info[head].bstar;
+  const float inv = info[head].inv_scale;
+  const int64_t hoff = (int64_t)head * n;
+  const int64_t i_begin = (int64_t)blk * kBlock;
+  const int64_t i_end = i_begin + kBlock < n ? i_begin + kBlock : n;
+  unsigned above = 0;
+  for (int64_t i = i_begin + t; i < i_end; i += 256) {
+    const unsigned u = scores[hoff + i];
+    const int b = bin_of(u, inv);
+    if (b > bstar) above += 1;
+    if (b == bstar) {
+      unsigned slot = atomicAdd((unsigned*)&info[head].n_cand, 1u);
+      cand[hoff + slot] = key64(u, i);
+    }
+  }
+  __shared__ unsigned red[4];
+  __shared__ int is_last;
+  for (int o = 32; o > 0; o >>= 1) above += __shfl_xor(above, o);
+  if ((t & 63) == 0) red[t >> 6] = above;
+  __syncthreads();
+  if (t == 0) above_blk[(int64_t)head * nblk + blk] = red[0] + red[1] + red[2] + red[3];
+  __threadfence();
+  __syncthreads();
+  if (t == 0) is_last = (atomicAdd(&info[head].done_collect, 1u) == (unsigned)nblk - 1);
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+  // Last workgroup of this head: exact radix select of the r-th largest candidate key.
+  const int n_cand = (int)atomic_load_u32((const unsigned*)&info[head].n_cand);
+  const int r = info[head].n_r - info[head].count_above;  // 1-based rank inside bin b*
+  __shared__ unsigned dh[256];
+  __shared__ unsigned long long s_prefix;
+  __shared__ unsigned s_remaining;
+  unsigned long long prefix = 0ull, mask = 0ull;
+  if (t == 0) s_remaining = (unsigned)(r > 0 ? r : 0);
+  __syncthreads();
+  const unsigned long long* ch = cand + hoff;
+  if (r > 0) {
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      dh[t] = 0u;
+      __syncthreads();
+      for (int i = t; i < n_cand; i += 256) {
+        unsigned long long kv = __hip_atomic_load(&ch[i], __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        if ((kv & mask) == prefix) atomicAdd(&dh[(kv >> shift) & 0xFF], 1u);
+      }
+      __syncthreads();
+      if (t == 0) {
+        unsigned rem = s_remaining, cum = 0;
+        int dg = 0;
+        for (int g = 255; g >= 0; --g) {
+          if (cum + dh[g] >= rem) {
+            dg = g;
+            break;
+          }
+          cum += dh[g];
+        }
+        s_remaining = rem - cum;
+        s_prefix = prefix | ((unsigned long long)dg << shift);
+      }
+      __syncthreads();
+      prefix = s_prefix;
+      mask |= 0xFFull << shift;
+      __syncthreads();
+    }
+    if (t == 0) info[head].thr = prefix;
+  } else if (t == 0) {
+    info[head].thr = ~0ull;
+  }
+  __syncthreads();
+  // Selected candidates per block, then exclusive offsets over the blocks of this head.
+  const unsigned long long thr = (r > 0) ? prefix : ~0ull;
+  if (r > 0) {
+    for (int i = t; i < n_cand; i += 256) {
+      unsigned long long kv = __hip_atomic_load(&ch[i], __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+      if (kv >= thr) {
+        int64_t idx = (int64_t)(0xFFFFFFFFu - (unsigned)(kv & 0xFFFFFFFFull));
+        atomicAdd(&sel_extra[(int64_t)head * nblk + idx / kBlock], 1u);
+      }
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  if (t == 0) {
+    unsigned run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      unsigned cnt = atomic_load_u32(&above_blk[(int64_t)head * nblk + b]) +
+                     atomic_load_u32(&sel_extra[(int64_t)head * nblk + b]);
+      sel_extra[(int64_t)head * nblk + b] = run;  // becomes the exclusive offset
+      run += cnt;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void sel_scatter(const unsigned* __restrict__ scores, int64_t n,
+                                                   int nblk, const HeadInfo* __restrict__ info,
+                                                   const unsigned* __restrict__ offsets,
+                                                   int32_t* __restrict__ ret,
+                                                   int32_t* __restrict__ bulk) {
+  const int head = blockIdx.x / nblk;
+  const int blk = blockIdx.x % nblk;
+  const int t = threadIdx.x;
+  const int bstar = info[head].bstar;
+  const float inv = info[head].inv_scale;
+  const unsigned long long thr = info[head].thr;
+  const int n_r = info[head].n_r;
+  const int64_t hoff = (int64_t)head * n;
+  const int64_t i_begin = (int64_t)blk * kBlock;
+  constexpr int kPer = kBlock / 256;  // 16 consecutive elements per thread
+  const int64_t my0 = i_begin + (int64_t)t * kPer;
+  unsigned flags = 0;
+  int cnt = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int64_t i = my0 + k;
+    if (i < n) {
+      const unsigned u = scores[hoff + i];
+      const int b = bin_of(u, inv);
+      const bool sel = b > bstar || (b == bstar && key64(u, i) >= thr);
+      if (sel) {
+        flags |= 1u << k;
+        ++cnt;
+      }
+    }
+  }
+  // exclusive scan of cnt over the workgroup (thread order = index order)
+  __shared__ int wsum[4];
+  int incl = cnt;
+  const int lane = t & 63;
+  for (int o = 1; o < 64; o <<= 1) {
+    int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[t >> 6] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int w = 0; w < (t >> 6); ++w) wbase += wsum[w];
+  const int64_t sel_before = (int64_t)offsets[(int64_t)head * nblk + blk] + wbase + incl - cnt;
+  int64_t rpos = sel_before;
+  int64_t bpos = my0 - sel_before;  // non-selected before my0
+  int32_t* rh = ret + (int64_t)head * n_r;
+  int32_t* bh = bulk + (int64_t)head * (n - n_r);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int64_t i = my0 + k;
+    if (i < n) {
+      // bounds guards: the counts are consistent by construction, the guards keep any
+      // inconsistency a wrong answer instead of an out-of-bounds store
+      if (flags & (1u << k)) {
+        if (rpos < n_r) rh[rpos] = (int32_t)i;
+        ++rpos;
+      } else {
+        if (bpos < n - n_r) bh[bpos] = (int32_t)i;
+        ++bpos;
+      }
+    }
+  }
+}
+
+struct SelLayout {
+  HeadInfo* info;
+  unsigned* hist;
+  unsigned* scores;
+  unsigned long long* cand;
+  unsigned* above_blk;
+  unsigned* sel_extra;
+  size_t bytes;
+};
+
+SelLayout carve(void* ws, int64_t heads, int64_t n) {
+  const int64_t nblk = (n + kBlock - 1) / kBlock;
+  Carver c(ws);
+  SelLayout L;
+  L.info = c.take<HeadInfo>((size_t)heads);
+  L.hist = c.take<unsigned>((size_t)heads * kBins);
+  L.scores = c.take<unsigned>((size_t)heads * n);
+  L.cand = c.take<unsigned long long>((size_t)heads * n);
+  L.above_blk = c.take<unsigned>((size_t)heads * nblk);
+  L.sel_extra = c.take<unsigned>((size_t)heads * nblk);
+  L.bytes = c.used;
+  return L;
+}
+
+}  // namespace
+}  // namespace a2ats
+
+using namespace a2ats;
+
+extern "C" size_t a2ats_select_retrieval_workspace(int64_t heads, int64_t n) {
+  if (heads < 1 || n < 0) return 0;
+  return carve(nullptr, heads, n).bytes;
+}
+
+extern "C" int a2ats_select_retrieval(const void* keys, int keys_dtype, int64_t heads, int64_t n,
+                                      int64_t d, const void* query, double fraction,
+                                      int32_t* retrieval_idx, int32_t* bulk_idx, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (keys_dtype != A2ATS_F32 && keys_dtype != A2ATS_BF16) return A2ATS_EDTYPE;
+  if (d != kD || heads < 1 || n < 0 || n > 0x7FFFFFFF) return A2ATS_EINVAL;
+  const int64_t n_r = a2ats_retrieval_count(n, fraction);
+  if (n_r < 0) return A2ATS_EINVAL;
+  if (n == 0) return A2ATS_OK;
+  if (!keys || !query) return A2ATS_EINVAL;
+  if ((n_r > 0 && !retrieval_idx) || (n_r < n && !bulk_idx)) return A2ATS_EINVAL;
+  const int64_t wg_per_head = (n + kScoreChunk - 1) / kScoreChunk;
+  const int64_t nblk = (n + kBlock - 1) / kBlock;
+  if (heads * wg_per_head > 0x7FFFFFFF || heads > 65535) return A2ATS_EINVAL;
+  const size_t need = a2ats_select_retrieval_workspace(heads, n);
+  if (!ws_ok(workspace, workspace_bytes, need)) return A2ATS_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SelLayout L = carve(workspace, heads, n);
+  A2ATS_TRY(launch("select_init", sel_init, dim3((unsigned)heads), dim3(256), 0, s, query,
+                   keys_dtype, n, fraction, L.info, L.hist, L.sel_extra, (int)nblk));
+  if (keys_dtype == A2ATS_BF16)
+    A2ATS_TRY(launch("select_score", sel_score<A2ATS_BF16>, dim3((unsigned)(heads * wg_per_head)),
+                     dim3(256), 0, s, keys, query, n, (int)wg_per_head, L.info, L.scores, L.hist));
+  else
+    A2ATS_TRY(launch("select_score", sel_score<A2ATS_F32>, dim3((unsigned)(heads * wg_per_head)),
+                     dim3(256), 0, s, keys, query, n, (int)wg_per_head, L.info, L.scores, L.hist));
+  A2ATS_TRY(launch("select_collect", sel_collect, dim3((unsigned)(heads * nblk)), dim3(256), 0, s,
+                   L.scores, n, (int)nblk, L.info, L.above_blk, L.cand, L.sel_extra));
+  return launch("select_scatter", sel_scatter, dim3((unsigned)(heads * nblk)), dim3(256), 0, s,
+                L.scores, n, (int)nblk, L.info, L.sel_extra, retrieval_idx, bulk_idx);
+}

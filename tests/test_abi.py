@@ -1,0 +1,166 @@
+"""The C ABI: the library loads, exports every function include/a2ats.h declares, and every
+host-side validation path returns its status without touching a device (runs on CPU)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import kv_cache_vector_windowed_amd as kv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "a2ats.h")
+
+EINVAL, EDTYPE, EWORKSPACE = -1, -2, -3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(a2ats_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kv.LIB_PATH):
+        pytest.skip("library not built")
+    return kv.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) >= 15
+    out = subprocess.check_output(["nm", "-D", "--defined-only", kv.LIB_PATH], text=True)
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        getattr(L, n)
+
+
+def test_version_and_strerror(L):
+    assert L.a2ats_version() == 1
+    for st in (0, -1, -2, -3, -4, -5):
+        assert L.a2ats_strerror(st).decode() not in ("", "unknown status")
+    assert L.a2ats_strerror(42).decode() == "unknown status"
+
+
+@pytest.mark.parametrize("n,f,want", [(4096, 0.1, 410), (32768, 0.1, 3277), (131072, 0.05, 6554),
+                                      (10, 0.3, 3), (100, 0.07, 8), (1, 0.2, 1), (1, 0.0, 0),
+                                      (0, 0.5, 0), (5, 1.0, 5), (10, 1.5, -1), (10, -0.1, -1),
+                                      (-1, 0.5, -1)])
+def test_retrieval_count(L, n, f, want):
+    assert L.a2ats_retrieval_count(n, f) == want
+    assert L.a2ats_retrieval_count(10, math.nan) == -1
+
+
+FAKE = ctypes.c_void_p(4096)  # never dereferenced: every call below fails validation first
+
+
+def test_encode_validation(L):
+    ws_need = L.a2ats_encode_workspace(2, 100, 128, 50)
+    assert ws_need > 0
+    assert L.a2ats_encode_workspace(2, 100, 64, 50) == 0
+    args = dict(keys=FAKE, dt=1, heads=2, n=100, d=128, idx=None, n_idx=0, cb=FAKE, c=50,
+                chol=None, codes=FAKE, dist=None, stats=None, ws=FAKE, wsb=ws_need, s=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.a2ats_encode(a["keys"], a["dt"], a["heads"], a["n"], a["d"], a["idx"], a["n_idx"],
+                              a["cb"], a["c"], a["chol"], a["codes"], a["dist"], a["stats"],
+                              a["ws"], a["wsb"], a["s"])
+
+    assert call(dt=5) == EDTYPE
+    assert call(d=64) == EINVAL
+    assert call(d=127) == EINVAL
+    assert call(c=0) == EINVAL
+    assert call(c=65537) == EINVAL
+    assert call(heads=0) == EINVAL
+    assert call(n=-1) == EINVAL
+    assert call(idx=FAKE, n_idx=101) == EINVAL
+    assert call(idx=FAKE, n_idx=-1) == EINVAL
+    assert call(keys=None) == EINVAL
+    assert call(codes=None) == EINVAL
+    assert call(keys=ctypes.c_void_p(4098)) == EINVAL          # not 16-byte aligned
+    assert call(wsb=ws_need - 1) == EWORKSPACE
+    assert call(ws=None) == EWORKSPACE
+    assert call(ws=ctypes.c_void_p(4096 + 64)) == EWORKSPACE   # not 256-byte aligned
+    assert call(n=0) == 0                                       # nothing to do
+    assert call(idx=FAKE, n_idx=0) == 0
+
+
+def test_assign_cosine_validation(L):
+    def call(dt=0, heads=1, n=4, d=128, nq=1, c=8, beta=0.5, x=FAKE):
+        return L.a2ats_assign_cosine(x, dt, heads, n, d, FAKE, nq, FAKE, c, beta, FAKE, None)
+
+    assert call(dt=3) == EDTYPE
+    for beta in (-0.01, 1.01, math.nan):
+        assert call(beta=beta) == EINVAL
+    assert call(nq=2) == EINVAL
+    assert call(d=257) == EINVAL
+    assert call(c=0) == EINVAL
+    assert call(c=65537) == EINVAL
+    assert call(x=None) == EINVAL
+    assert call(n=0) == 0
+
+
+def test_select_validation(L):
+    need = L.a2ats_select_retrieval_workspace(2, 1000)
+    assert need > 0
+
+    def call(dt=1, heads=2, n=1000, d=128, f=0.1, ws=FAKE, wsb=need, keys=FAKE):
+        return L.a2ats_select_retrieval(keys, dt, heads, n, d, FAKE, f, FAKE, FAKE, ws, wsb, None)
+
+    assert call(dt=2) == EDTYPE
+    assert call(d=64) == EINVAL
+    assert call(f=1.5) == EINVAL
+    assert call(f=math.nan) == EINVAL
+    assert call(keys=None) == EINVAL
+    assert call(wsb=need - 1) == EWORKSPACE
+    assert call(n=0) == 0
+
+
+def test_reconstruct_validation(L):
+    need = L.a2ats_reconstruct_workspace(128, 16384, 256)
+    assert need >= (256 + 1) * 64 * 16
+    assert L.a2ats_reconstruct_workspace(128, 10, 1 << 40) >= 11 * 64 * 16  # rows capped at cur+1
+
+    def call(out_dt=0, d=128, cur=100, window=16, far_mode=0, base=10000.0, c=10, n=50,
+             wsb=None, codes=FAKE):
+        wsb = need if wsb is None else wsb
+        return L.a2ats_reconstruct(codes, FAKE, 1, 2, n, d, FAKE, c, cur, window, 2048, far_mode,
+                                   base, FAKE, out_dt, FAKE, wsb, None)
+
+    assert call(out_dt=7) == EDTYPE
+    assert call(d=64) == EINVAL
+    assert call(cur=-1) == EINVAL
+    assert call(far_mode=2) == EINVAL
+    assert call(base=0.0) == EINVAL
+    assert call(base=math.inf) == EINVAL
+    assert call(c=0) == EINVAL
+    assert call(codes=None) == EINVAL
+    assert call(wsb=0) == EWORKSPACE
+    assert call(n=0) == 0
+
+
+def test_calibrate_validation(L):
+    need = L.a2ats_calibrate_workspace(2, 100, 128)
+    assert need > 0 and L.a2ats_calibrate_workspace(2, 100, 129) == 0
+
+    def call(heads=2, m=100, d=128, ridge=1e-4, wsb=need, q=FAKE):
+        return L.a2ats_calibrate(q, heads, m, d, ridge, FAKE, FAKE, FAKE, wsb, None)
+
+    assert call(d=129) == EINVAL
+    assert call(m=0) == EINVAL
+    assert call(ridge=-1.0) == EINVAL
+    assert call(ridge=math.nan) == EINVAL
+    assert call(q=None) == EINVAL
+    assert call(wsb=need - 1) == EWORKSPACE
+
+
+def test_binding_fails_loudly_without_device_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        kv.calibrate(torch.zeros(1, 4, 128))

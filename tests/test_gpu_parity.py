@@ -1,0 +1,362 @@
+"""GPU parity: every call of the C ABI against the fp64 CPU oracle on seeded inputs.
+
+Small cases are compared element by element (several MFMA tiles, ragged tails); the
+workloads at full size are compared on sampled rows the oracle computes one by one.  All
+calls go through the C ABI (via the ctypes binding) on cuda:0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_vector_windowed_amd as kv
+import oracle
+from kv_cache_vector_windowed_amd import synth
+
+from parity import (DEV, bf16_to_np_bits, check_codes, check_dist, check_rotation, check_split,
+                    f32_to_dev, keys_to_dev, u16_to_dev, u16_to_np)
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def oracle_L(cfg, heads, m):
+    return oracle.calibrate(synth.queries(cfg, heads, m), 1e-4)[1]
+
+
+def z2_of(x, l):
+    x = np.asarray(x, np.float64)
+    return ((x @ l.astype(np.float64)) ** 2).sum(-1) if l is not None else (x ** 2).sum(-1)
+
+
+# ====================================================================== calibrate
+class TestCalibrate:
+    @pytest.mark.parametrize("name", ["tiny", "layer"])
+    def test_workload(self, name):
+        w = W[name]
+        q = synth.queries(w.cfg, w.heads, w.m)
+        H, L = kv.calibrate(f32_to_dev(q), 1e-4)
+        Ho, Lo = oracle.calibrate(q, 1e-4)
+        H, L = H.cpu().numpy(), L.cpu().numpy()
+        for h in range(w.heads):
+            assert np.abs(H[h] - Ho[h]).max() <= 1e-5 * np.abs(Ho[h]).max()
+            assert np.abs(L[h] - Lo[h]).max() <= 1e-5 * np.abs(Lo[h]).max()
+            assert np.all(np.triu(L[h], 1) == 0)
+
+    def test_small_odd_dimension(self):
+        q = synth.queries(100, 3, 77, d=5)
+        H, L = kv.calibrate(f32_to_dev(q), 0.25)
+        Ho, Lo = oracle.calibrate(q, 0.25)
+        np.testing.assert_allclose(H.cpu().numpy(), Ho, rtol=0, atol=1e-5 * np.abs(Ho).max())
+        np.testing.assert_allclose(L.cpu().numpy(), Lo, rtol=0, atol=1e-5 * np.abs(Lo).max())
+
+    def test_not_positive_definite(self):
+        q = synth.queries(101, 1, 64, d=8)
+        q[:, :, 3] = 0.0  # zero column, no ridge: exact zero pivot
+        with pytest.raises(kv.A2ATSError) as e:
+            kv.calibrate(f32_to_dev(q), 0.0)
+        assert e.value.status == -4
+
+
+# ====================================================================== encode
+def run_encode(name_or_w, n_sample=None, use_h=True, seed=0):
+    w = W[name_or_w] if isinstance(name_or_w, str) else name_or_w
+    keys = synth.keys(w.cfg, w.heads, w.n, w.key_dtype)
+    cb = synth.codebook(w.cfg, w.heads, w.c)
+    L = oracle_L(w.cfg, w.heads, w.m) if use_h else None
+    stats = torch.zeros(8, dtype=torch.int32, device=DEV)
+    codes, dist = kv.encode(keys_to_dev(keys), f32_to_dev(cb), f32_to_dev(L) if use_h else None,
+                            want_dist=True, stats=stats)
+    codes = u16_to_np(codes)
+    dist = dist.cpu().numpy()
+    rng = np.random.default_rng(seed)
+    ties = []
+    for h in range(w.heads):
+        rows = np.arange(w.n) if n_sample is None else np.sort(rng.choice(w.n, n_sample, replace=False))
+        x = keys.values[h][rows]
+        lh = L[h] if use_h else None
+        code, d1, d2 = oracle.assign_h(x, cb[h], lh)
+        tie, _ = check_codes(codes[h][rows], code, d1, d2, "%s head %d" % (w.name, h))
+        check_dist(dist[h][rows], d1, z2_of(x, lh), "%s head %d" % (w.name, h))
+        ties.append(tie)
+    st = stats.cpu().numpy()
+    assert st[0] == w.heads * w.n
+    assert st[1] + st[2] + st[3] + st[4] == st[0]
+    return float(np.mean(ties)), st
+
+
+class TestEncode:
+    @pytest.mark.parametrize("use_h", [False, True])
+    def test_tiny_all_rows(self, use_h):
+        tie, st = run_encode("tiny", use_h=use_h)
+        print("tiny use_h=%s tie rate %.2e stats %s" % (use_h, tie, st[:5]))
+
+    def test_ragged_shapes_and_index_subset(self):
+        w = synth.Workload("ragged", 110, 3, 1000, 100, "bf16", m=300)
+        keys = synth.keys(w.cfg, w.heads, w.n, "bf16")
+        cb = synth.codebook(w.cfg, w.heads, w.c)
+        L = oracle_L(w.cfg, w.heads, w.m)
+        rng = np.random.default_rng(3)
+        idx = np.stack([np.sort(rng.choice(w.n, 333, replace=False)) for _ in range(w.heads)]).astype(np.int32)
+        codes0 = u16_to_dev(np.full((w.heads, w.n), 0xFFFF, np.uint16))
+        out = kv.encode(keys_to_dev(keys), f32_to_dev(cb), f32_to_dev(L),
+                        idx=torch.from_numpy(idx).to(DEV), codes=codes0)
+        out = u16_to_np(out)
+        for h in range(w.heads):
+            code, d1, d2 = oracle.assign_h(keys.values[h][idx[h]], cb[h], L[h])
+            check_codes(out[h][idx[h]], code, d1, d2, "ragged head %d" % h)
+            untouched = np.setdiff1d(np.arange(w.n), idx[h])
+            assert np.all(out[h][untouched] == 0xFFFF)
+
+    def test_layer_sampled(self):
+        tie, st = run_encode("layer", n_sample=768)
+        print("layer tie rate %.2e stats %s" % (tie, st[:5]))
+
+    def test_encode_stress_sampled(self):
+        tie, st = run_encode("encode_stress", n_sample=192)
+        print("encode_stress tie rate %.2e stats %s" % (tie, st[:5]))
+
+    def test_single_centroid_and_duplicate_centroids(self):
+        keys = synth.keys(120, 2, 300, "f32")
+        cb1 = synth.codebook(120, 2, 1)
+        out = u16_to_np(kv.encode(keys_to_dev(keys), f32_to_dev(cb1), None))
+        assert np.all(out == 0)
+        cb = synth.codebook(121, 2, 40)
+        cb[:, 20] = cb[:, 5]  # exact duplicate rows: ties resolve to the lower index
+        cb[:, 39] = cb[:, 5]
+        L = oracle_L(121, 2, 256)
+        for chol in (None, L):
+            out = u16_to_np(kv.encode(keys_to_dev(keys), f32_to_dev(cb),
+                                      f32_to_dev(chol) if chol is not None else None))
+            assert not np.any(out == 20) and not np.any(out == 39)
+            for h in range(2):
+                code, d1, d2 = oracle.assign_h(keys.values[h], cb[h], None if chol is None else chol[h])
+                check_codes(out[h], code, d1, d2, "duplicates")
+
+    def test_keys_outside_fp16_range(self):
+        keys = synth.keys(122, 1, 200, "f32")
+        keys.values[0, ::7, 3] *= 1e4  # some elements beyond 65504
+        cb = synth.codebook(122, 1, 64) * 1e2
+        out, dist = kv.encode(keys_to_dev(keys), f32_to_dev(cb), None, want_dist=True)
+        code, d1, d2 = oracle.assign_h(keys.values[0], cb[0], None)
+        check_codes(u16_to_np(out)[0], code, d1, d2, "large keys")
+        check_dist(dist.cpu().numpy()[0], d1, z2_of(keys.values[0], None), "large keys")
+
+    def test_deterministic(self):
+        w = W["tiny"]
+        keys = keys_to_dev(synth.keys(w.cfg, 1, w.n, w.key_dtype))
+        cb = f32_to_dev(synth.codebook(w.cfg, 1, w.c))
+        L = f32_to_dev(oracle_L(w.cfg, 1, w.m))
+        a = kv.encode(keys, cb, L, want_dist=True)
+        b = kv.encode(keys, cb, L, want_dist=True)
+        assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+        assert torch.equal(a[1], b[1])
+
+
+# ====================================================================== cosine blend
+class TestAssignCosine:
+    @pytest.mark.parametrize("beta", [1.0, 0.7, 0.0])
+    def test_tiny_retrieval_rows(self, beta):
+        w = W["tiny"]
+        keys = synth.keys(w.cfg, 1, w.n, w.key_dtype)
+        cb = synth.codebook(w.cfg, 1, w.c)
+        nr = oracle.retrieval_count(w.n, w.fraction)
+        rows = np.arange(w.n - nr, w.n)  # any 410 rows; the proxy query is the last key
+        x = keys.values[:, rows]
+        q = keys.values[:, -1:]
+        out = u16_to_np(kv.assign_cosine(f32_to_dev(x), f32_to_dev(q), f32_to_dev(cb), beta))
+        code, s1, s2 = oracle.assign_cosine(x[0], q[0], cb[0], beta)
+        bad = (s1 - s2 > 1e-5) & (out[0] != code)
+        assert not bad.any(), np.nonzero(bad)[0][:5]
+
+    def test_decode_new_keys(self):
+        w = W["decode"]
+        x = synth.new_keys(w.cfg, w.heads, w.batch)  # [heads, 32 sequences, d]
+        cb = synth.codebook(w.cfg, w.heads, w.c)
+        beta = w.betas[0]
+        out = u16_to_np(kv.assign_cosine(f32_to_dev(x), f32_to_dev(x), f32_to_dev(cb), beta))
+        for h in range(w.heads):
+            code, s1, s2 = oracle.assign_cosine(x[h], x[h], cb[h], beta)
+            bad = (s1 - s2 > 1e-5) & (out[h] != code)
+            assert not bad.any()
+
+    def test_bf16_rows_and_beta_one_matches_plain_encode(self):
+        k = synth.keys(130, 2, 150, "bf16")
+        cb = synth.codebook(130, 2, 70)
+        xd = keys_to_dev(k)
+        out = kv.assign_cosine(xd, xd[:, -1:].contiguous(), f32_to_dev(cb), 1.0)
+        plain = kv.encode(xd, f32_to_dev(cb), None)
+        for h in range(2):
+            code, d1, d2 = oracle.assign_h(k.values[h], cb[h], None)
+            check_codes(u16_to_np(out)[h], code, d1, d2, "beta=1")
+            check_codes(u16_to_np(plain)[h], code, d1, d2, "plain")
+
+
+# ====================================================================== retrieval split
+def run_split(keys: synth.Keys, q: np.ndarray, f: float, what: str):
+    ret, bulk = kv.select_retrieval(keys_to_dev(keys), q_to_dev(q, keys.dtype), f)
+    ret, bulk = ret.cpu().numpy(), bulk.cpu().numpy()
+    heads, n, _ = keys.values.shape
+    band = 0
+    for h in range(heads):
+        ro, bo, cosv = oracle.select_retrieval(keys.values[h], q_exact(q, keys.dtype)[h], f)
+        band += check_split(ret[h], bulk[h], n, cosv, ro, "%s head %d" % (what, h))
+    return band
+
+
+def q_to_dev(q, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(synth.f32_to_bf16_bits(q).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return f32_to_dev(q)
+
+
+def q_exact(q, dtype):
+    return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(q)) if dtype == "bf16" else q
+
+
+class TestSelectRetrieval:
+    @pytest.mark.parametrize("name", ["tiny", "layer", "long_context"])
+    def test_workload(self, name):
+        w = W[name]
+        keys = synth.keys(w.cfg, w.heads, w.n, w.key_dtype)
+        q = keys.values[:, -1].copy()  # proxy query: the last key of each head
+        band = run_split(keys, q, w.fraction, name)
+        print("%s: %d indices in the tie band" % (name, band))
+
+    @pytest.mark.parametrize("f", [0.0, 1.0, 0.5, 0.07])
+    def test_fractions_ragged(self, f):
+        keys = synth.keys(140, 2, 5000, "bf16")
+        run_split(keys, keys.values[:, 17].copy(), f, "f=%g" % f)
+
+    def test_degenerate_inputs(self):
+        keys = synth.keys(141, 3, 4500, "f32")
+        keys.values[0, 100:200] = 0.0          # zero-norm keys score 0
+        keys.values[1] = keys.values[1, :1]    # every key identical: all ties, lowest indices win
+        q = keys.values[:, 3].copy()
+        q[2] = 0.0                             # zero query: every score 0
+        run_split(keys, q, 0.3, "degenerate")
+        ret, _ = kv.select_retrieval(keys_to_dev(keys), f32_to_dev(q), 0.3)
+        nr = oracle.retrieval_count(4500, 0.3)
+        assert np.array_equal(ret.cpu().numpy()[1], np.arange(nr))
+        assert np.array_equal(ret.cpu().numpy()[2], np.arange(nr))
+
+    def test_single_token(self):
+        keys = synth.keys(142, 1, 1, "bf16")
+        ret, bulk = kv.select_retrieval(keys_to_dev(keys), q_to_dev(keys.values[:, 0], "bf16"), 0.2)
+        assert ret.cpu().numpy().tolist() == [[0]] and bulk.shape == (1, 0)
+
+
+# ====================================================================== reconstruct
+def oracle_rows(codes, pos, cb, w_cur, window, far_b, far_mode):
+    out, _ = oracle.reconstruct(codes, pos, cb, w_cur, window, far_b, far_mode)
+    return out
+
+
+class TestReconstruct:
+    def test_tiny_fp32_all_tokens(self):
+        w = W["tiny"]
+        cb = synth.codebook(w.cfg, 1, w.c)
+        codes = synth.uniform_codes(w.cfg, (1, 1, w.n), w.c)
+        pos = np.arange(w.n, dtype=np.int32)[None]
+        out = kv.reconstruct(u16_to_dev(codes), torch.from_numpy(pos).to(DEV), f32_to_dev(cb),
+                             w.cur_pos, w.window).cpu().numpy()
+        ref = oracle_rows(codes[0, 0], pos[0], cb[0], w.cur_pos, w.window, w.far_b, 0)
+        err, n_big = check_rotation(out[0, 0], ref, cb[0][codes[0, 0]].astype(np.float64), "f32", "tiny")
+        print("tiny reconstruct max err %g, >1e-5: %d" % (err, n_big))
+
+    def test_decode_sampled(self):
+        w = W["decode"]
+        cb = synth.codebook(w.cfg, w.heads, w.c)
+        codes = synth.uniform_codes(w.cfg, (w.batch, w.heads, w.n), w.c)
+        pos = np.tile(np.arange(w.n, dtype=np.int32), (w.batch, 1))
+        out = kv.reconstruct(u16_to_dev(codes), torch.from_numpy(pos).to(DEV), f32_to_dev(cb),
+                             w.cur_pos, w.window)
+        rng = np.random.default_rng(5)
+        b = rng.integers(0, w.batch, 4000)
+        h = rng.integers(0, w.heads, 4000)
+        t = np.concatenate([rng.integers(0, w.n, 3000), rng.integers(w.n - w.window - 4, w.n, 1000)])
+        got = out[torch.from_numpy(b).to(DEV), torch.from_numpy(h).to(DEV),
+                  torch.from_numpy(t).to(DEV)].cpu().numpy()
+        for hh in range(w.heads):
+            m = h == hh
+            ref = oracle_rows(codes[b[m], hh, t[m]], pos[b[m], t[m]], cb[hh], w.cur_pos, w.window,
+                              w.far_b, 0)
+            check_rotation(got[m], ref, cb[hh][codes[b[m], hh, t[m]]].astype(np.float64), "f32",
+                           "decode head %d" % hh)
+
+    def test_long_context_bf16_sampled(self):
+        w = W["long_context"]
+        cb = synth.codebook(w.cfg, w.heads, w.c)
+        codes = synth.uniform_codes(w.cfg, (1, w.heads, w.n), w.c)
+        pos = np.arange(w.n, dtype=np.int32)[None]
+        out = kv.reconstruct(u16_to_dev(codes), torch.from_numpy(pos).to(DEV), f32_to_dev(cb),
+                             w.cur_pos, w.window, out_dtype=torch.bfloat16)
+        rng = np.random.default_rng(6)
+        t = np.concatenate([rng.integers(0, w.n, 3000), np.arange(w.n - w.window - 8, w.n)])
+        for hh in range(w.heads):
+            got = bf16_to_np_bits(out[0, hh, torch.from_numpy(t).to(DEV)])
+            ref = oracle_rows(codes[0, hh, t], pos[0, t], cb[hh], w.cur_pos, w.window, w.far_b, 0)
+            ref_bits = oracle.round_bf16(ref)
+            mism = (got != ref_bits).mean()
+            check_rotation(synth.bf16_bits_to_f32(got), ref, cb[hh][codes[0, hh, t]].astype(np.float64),
+                           "bf16", "long_context head %d" % hh)
+            assert mism < 1e-3, mism  # rounding once from fp64 on both sides
+
+    @pytest.mark.parametrize("window,far_mode,far_b", [(0, 0, 2048), (-5, 1, 2048), (10 ** 9, 0, 2048),
+                                                       (300, 1, 0), (300, 0, 77), (1, 0, 5000)])
+    def test_windows_and_modes(self, window, far_mode, far_b):
+        cb = synth.codebook(150, 2, 90)
+        codes = synth.uniform_codes(150, (2, 2, 1777), 90)
+        pos = np.tile(np.arange(1777, dtype=np.int32), (2, 1))
+        cur = 1800
+        out = kv.reconstruct(u16_to_dev(codes), torch.from_numpy(pos).to(DEV), f32_to_dev(cb), cur,
+                             window, far_offset=far_b, far_mode=far_mode).cpu().numpy()
+        for b in range(2):
+            for h in range(2):
+                ref = oracle_rows(codes[b, h], pos[b], cb[h], cur, window, far_b, far_mode)
+                check_rotation(out[b, h], ref, cb[h][codes[b, h]].astype(np.float64), "f32", "modes")
+
+    def test_invalid_code_or_position_is_nan_and_window_is_bitwise_exact(self):
+        cb = synth.codebook(151, 1, 50)
+        codes = synth.uniform_codes(151, (1, 1, 600), 50)
+        codes[0, 0, 7] = 50
+        pos = np.arange(600, dtype=np.int32)[None].copy()
+        pos[0, 9] = -3
+        out = kv.reconstruct(u16_to_dev(codes), torch.from_numpy(pos).to(DEV), f32_to_dev(cb), 599, 64)
+        o = out.cpu().numpy()[0, 0]
+        assert np.all(np.isnan(o[7])) and np.all(np.isnan(o[9])) and np.isfinite(o[10]).all()
+        exact = kv.reconstruct(u16_to_dev(codes), torch.from_numpy(pos).to(DEV), f32_to_dev(cb), 599,
+                               10 ** 6).cpu().numpy()[0, 0]
+        assert np.array_equal(o[536:], exact[536:])  # inside the window: identical to exact RoPE
+
+
+# ====================================================================== pipeline
+class TestPipeline:
+    @pytest.mark.parametrize("name", ["layer", "long_context"])
+    def test_split_encode_reconstruct(self, name):
+        w = W[name]
+        keys = synth.keys(w.cfg, w.heads, w.n, w.key_dtype)
+        cb = synth.codebook(w.cfg, w.heads, w.c)
+        q = synth.queries(w.cfg, w.heads, w.m)
+        kd, cbd = keys_to_dev(keys), f32_to_dev(cb)
+        H, L = kv.calibrate(f32_to_dev(q), 1e-4)
+        ret, bulk = kv.select_retrieval(kd, kd[:, -1].contiguous(), w.fraction)
+        codes = kv.encode(kd, cbd, None)
+        codes = kv.encode(kd, cbd, L, idx=ret, codes=codes)
+        out = kv.reconstruct(codes[None].contiguous(), torch.arange(w.n, dtype=torch.int32, device=DEV)[None],
+                             cbd, w.cur_pos, w.window, out_dtype=torch.bfloat16)
+        Lh = L.cpu().numpy()
+        codes_np = u16_to_np(codes)
+        ret_np = ret.cpu().numpy()
+        rng = np.random.default_rng(7)
+        for h in range(w.heads):
+            r = ret_np[h][rng.choice(ret_np.shape[1], 256, replace=False)]
+            code, d1, d2 = oracle.assign_h(keys.values[h][r], cb[h], Lh[h])
+            check_codes(codes_np[h][r], code, d1, d2, "%s retrieval rows" % name)
+            b = np.setdiff1d(rng.choice(w.n, 600, replace=False), ret_np[h])[:256]
+            code, d1, d2 = oracle.assign_h(keys.values[h][b], cb[h], None)
+            check_codes(codes_np[h][b], code, d1, d2, "%s bulk rows" % name)
+            t = np.concatenate([b, np.arange(w.n - 16, w.n)])
+            got = synth.bf16_bits_to_f32(bf16_to_np_bits(out[0, h, torch.from_numpy(t).to(DEV)]))
+            ref = oracle_rows(codes_np[h][t], t.astype(np.int32), cb[h], w.cur_pos, w.window, w.far_b, 0)
+            check_rotation(got, ref, cb[h][codes_np[h][t]].astype(np.float64), "bf16", name)
