@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Benchmark of the A2ATS key-cache hot path on one MI355X.
+
+Headline: the per-layer cache update of a Llama-3.2-3B-shaped layer (8 KV heads x 32768
+tokens x d=128, bf16 keys, C=1024 centroids per head, H from 4096 queries, W=512, retrieval
+fraction 0.1).  One step = retrieval split -> plain encode of every key -> H-weighted encode
+of the retrieval rows -> windowed-RoPE reconstruct (bf16) of the whole cache.  Calibration
+(H and L) is the pages' one-time offline job: it runs once before timing and is reported
+separately.  `value` = keys encoded per second.
+
+Also reported (field "extra"): the large-codebook H-weighted encode (8 x 131072 keys,
+C=4096, codes + distances) with its MFMA fraction; the decode step (32 x 8 x 16384 tokens,
+fp32 reconstruct + cosine-blend of the new keys) and the long-context pipeline (8 x 131072
+keys, 5% split, C=2048, W=1024) with HBM fractions.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2516.6   # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "keys encoded/sec (H-weighted VQ, d=128) + % MFMA peak; reconstruct GB/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def sha_of(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py: this build runs on exactly one GPU; --gpus %d (world size %d) is not "
+                  "supported" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_cache_vector_windowed_amd as kv
+    from kv_cache_vector_windowed_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    W = synth.WORKLOADS
+
+    def keys_dev(k):
+        return torch.from_numpy(k.bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+    # ------------------------------------------------------------------ headline workload
+    w = W["layer"]
+    log("generating layer inputs")
+    keys = synth.keys(w.cfg, w.heads, w.n, "bf16")
+    kd = keys_dev(keys)
+    cbd = f32(synth.codebook(w.cfg, w.heads, w.c))
+    qd = f32(synth.queries(w.cfg, w.heads, w.m))
+    pos = torch.arange(w.n, dtype=torch.int32, device=dev)[None]
+    proxy = kd[:, -1].contiguous()
+    H, L = kv.calibrate(qd, 1e-4)
+    codes = torch.zeros((w.heads, w.n), dtype=torch.uint16, device=dev)
+    out = torch.empty((1, w.heads, w.n, 128), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        ret, _ = kv.select_retrieval(kd, proxy, w.fraction)
+        kv.encode(kd, cbd, None, codes=codes)
+        kv.encode(kd, cbd, L, idx=ret, codes=codes)
+        kv.reconstruct(codes[None], pos, cbd, w.cur_pos, w.window, out=out)
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("timing %d steps" % args.steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    keys_per_step = w.heads * w.n
+    value = keys_per_step / (ms * 1e-3)
+    log("layer step %.4f ms -> %.4g keys/s" % (ms, value))
+
+    # per-kernel durations: same step, same launches, with HIP events around every kernel
+    def profile(fn, reps):
+        kv.profile_reset()
+        kv.profile_enable(True)
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        prof = kv.profile_read()
+        kv.profile_enable(False)
+        kv.profile_reset()
+        return {k: (c, t / c) for k, (c, t) in prof.items()}
+
+    prof = profile(step, min(args.steps, 20))
+    log("kernels: " + ", ".join("%s %.1fus" % (k, v[1] * 1e3) for k, v in prof.items()))
+    coarse_ms = prof["encode_coarse_plain"][1]
+    flops = 2.0 * w.heads * w.n * w.c * 128
+    achieved = flops / (coarse_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "encode_coarse_plain", "achieved": round(achieved, 2),
+                "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+                "traffic": traffic_from_profiles("encode_coarse_plain", "layer"),
+                "launch_us": round(coarse_ms * 1e3, 2), "flops_per_launch": flops}
+    t0 = time.perf_counter()
+    kv.calibrate(qd, 1e-4)
+    calib_ms = (time.perf_counter() - t0) * 1e3
+
+    extra = {"layer_kernels_us": {k: round(v[1] * 1e3, 2) for k, v in prof.items()},
+             "layer_calibrate_ms_host_clock": round(calib_ms, 3)}
+    if not args.no_extra:
+        extra.update(extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, keys, synth)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "keys/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "layer: 8 KV heads x 32768 tokens x d=128 bf16 keys, C=1024, "
+                               "H from 4096 queries, W=512, retrieval fraction 0.1; step = split + "
+                               "plain encode + H-weighted encode of retrieval rows + bf16 reconstruct",
+                   "heads": w.heads, "tokens": w.n, "centroids": w.c, "window": w.window,
+                   "fraction": w.fraction},
+        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def traffic_from_profiles(kernel, workload):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken on
+    the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", "%s_%s_pmc.json" % (kernel, workload))
+    if not os.path.exists(p):
+        return None
+    try:
+        with open(p) as f:
+            d = json.load(f)
+        src = os.path.join(ROOT, d["source"])
+        if sha_of(src) != d["source_sha"]:
+            return None
+        return d["hbm_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
+    W = synth.WORKLOADS
+    res = {}
+    flush_buf = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+
+    def timed(fn, reps, flush=False):
+        tot = 0.0
+        for _ in range(reps):
+            if flush:
+                flush_buf.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            tot += a.elapsed_time(b)
+        return tot / reps
+
+    # large-codebook encode
+    w = W["encode_stress"]
+    log("generating encode_stress inputs")
+    kd = keys_dev(synth.keys(w.cfg, w.heads, w.n, "bf16"))
+    cbd = f32(synth.codebook(w.cfg, w.heads, w.c))
+    _, L = kv.calibrate(f32(synth.queries(w.cfg, w.heads, w.m)), 1e-4)
+    stats = torch.zeros(8, dtype=torch.int32, device=dev)
+
+    def enc():
+        kv.encode(kd, cbd, L, want_dist=True, stats=stats)
+
+    enc()
+    torch.cuda.synchronize()
+    ms = timed(enc, 5)
+    pr = profile(enc, 3)
+    flops = 2.0 * w.heads * w.n * w.c * 128
+    cms = pr["encode_coarse_h"][1]
+    st = stats.cpu().numpy().tolist()
+    res["encode_stress"] = {
+        "workload": "8 heads x 131072 bf16 keys, C=4096, H-weighted, codes + distances",
+        "ms_per_call": round(ms, 4), "keys_per_s": round(w.heads * w.n / (ms * 1e-3), 1),
+        "mfma_frac_call": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+        "coarse_us": round(cms * 1e3, 2),
+        "mfma_frac_coarse": round(flops / (cms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+        "kernels_us": {k: round(v[1] * 1e3, 2) for k, v in pr.items()},
+        "decided": {"direct": st[1], "reranked": st[2], "rescanned": st[3], "full_scan": st[4]},
+    }
+    log("encode_stress %s" % res["encode_stress"])
+    del kd
+    # decode step
+    w = W["decode"]
+    log("generating decode inputs")
+    cbd = f32(synth.codebook(w.cfg, w.heads, w.c))
+    codes = torch.from_numpy(synth.uniform_codes(w.cfg, (w.batch, w.heads, w.n), w.c).view(np.int16)).to(dev).view(torch.uint16)
+    pos = torch.arange(w.n, dtype=torch.int32, device=dev)[None].repeat(w.batch, 1).contiguous()
+    out = torch.empty((w.batch, w.heads, w.n, 128), dtype=torch.float32, device=dev)
+    newk = f32(synth.new_keys(w.cfg, w.heads, w.batch))
+
+    def rec():
+        kv.reconstruct(codes, pos, cbd, w.cur_pos, w.window, out=out)
+
+    def blend():
+        kv.assign_cosine(newk, newk, cbd, w.betas[0])
+
+    rec()
+    blend()
+    torch.cuda.synchronize()
+    ms_r = timed(rec, 5, flush=True)
+    ms_b = timed(blend, 10)
+    tokens = w.batch * w.heads * w.n
+    alg = tokens * (2 + 128 * 4) + w.batch * w.n * 4 + w.heads * w.c * 128 * 4
+    pr = profile(rec, 3)
+    kr = pr["reconstruct"][1]
+    res["decode"] = {
+        "workload": "32 sequences x 8 heads x 16384 tokens, fp32 out, W=256; blend of 256 new keys",
+        "reconstruct_ms": round(ms_r, 4), "reconstruct_GBps": round(alg / (ms_r * 1e-3) / 1e9, 1),
+        "reconstruct_kernel_us": round(kr * 1e3, 2),
+        "reconstruct_kernel_GBps": round(alg / (kr * 1e-3) / 1e9, 1),
+        "reconstruct_hbm_frac": round(alg / (kr * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "algorithmic_bytes": alg, "blend_us": round(ms_b * 1e3, 2),
+    }
+    log("decode %s" % res["decode"])
+    del out
+    # long-context pipeline
+    w = W["long_context"]
+    log("generating long_context inputs")
+    kd = keys_dev(synth.keys(w.cfg, w.heads, w.n, "bf16"))
+    cbd = f32(synth.codebook(w.cfg, w.heads, w.c))
+    _, L = kv.calibrate(f32(synth.queries(w.cfg, w.heads, w.m)), 1e-4)
+    proxy = kd[:, -1].contiguous()
+    codes = torch.zeros((w.heads, w.n), dtype=torch.uint16, device=dev)
+    pos = torch.arange(w.n, dtype=torch.int32, device=dev)[None]
+    out = torch.empty((1, w.heads, w.n, 128), dtype=torch.bfloat16, device=dev)
+
+    def split():
+        return kv.select_retrieval(kd, proxy, w.fraction)
+
+    def rec2():
+        kv.reconstruct(codes[None], pos, cbd, w.cur_pos, w.window, out=out)
+
+    def pipe():
+        ret, _ = split()
+        kv.encode(kd, cbd, None, codes=codes)
+        kv.encode(kd, cbd, L, idx=ret, codes=codes)
+        rec2()
+
+    pipe()
+    torch.cuda.synchronize()
+    ms_s = timed(split, 5, flush=True)
+    ms_r = timed(rec2, 5, flush=True)
+    ms_p = timed(pipe, 3)
+    split_bytes = w.heads * w.n * (128 * 2 + 4)
+    rec_bytes = w.heads * w.n * (2 + 128 * 2) + w.n * 4 + w.heads * w.c * 128 * 4
+    pr = profile(pipe, 3)
+    split_kernels = sum(v[1] for k, v in pr.items() if k.startswith("select_"))
+    res["long_context"] = {
+        "workload": "8 heads x 131072 bf16 keys, 5% split, C=2048, W=1024, bf16 reconstruct",
+        "pipeline_ms": round(ms_p, 4), "keys_per_s": round(w.heads * w.n / (ms_p * 1e-3), 1),
+        "split_ms": round(ms_s, 4), "split_GBps": round(split_bytes / (ms_s * 1e-3) / 1e9, 1),
+        "split_hbm_frac": round(split_bytes / (ms_s * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "split_kernels_us": round(split_kernels * 1e3, 2),
+        "reconstruct_ms": round(ms_r, 4), "reconstruct_GBps": round(rec_bytes / (ms_r * 1e-3) / 1e9, 1),
+        "reconstruct_hbm_frac": round(rec_bytes / (ms_r * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "kernels_us": {k: round(v[1] * 1e3, 2) for k, v in pr.items()},
+    }
+    log("long_context %s" % res["long_context"])
+    return res
+
+
+def cpu_baseline(w, keys, synth):
+    """The oracle (as it stands) on a bounded sample of the headline step: whole heads of the
+    layer workload, each running split, plain encode of every key, H-weighted encode of the
+    retrieval rows and the fp64 reconstruct; as many heads as fit in about 15 s."""
+    import oracle
+
+    log("cpu baseline (oracle)")
+    cb = synth.codebook(w.cfg, w.heads, w.c)
+    q = synth.queries(w.cfg, w.heads, w.m)
+    _, L = oracle.calibrate(q, 1e-4)
+    done = 0
+    t0 = time.perf_counter()
+    for h in range(w.heads):
+        x = keys.values[h]
+        ret, _, _ = oracle.select_retrieval(x, x[-1], w.fraction)
+        code, _, _ = oracle.assign_h(x, cb[h], None)
+        code_r, _, _ = oracle.assign_h(x[ret], cb[h], L[h])
+        code[ret] = code_r
+        oracle.reconstruct(code.astype(np.uint16), np.arange(w.n, dtype=np.int32), cb[h],
+                           w.cur_pos, w.window)
+        done += 1
+        if time.perf_counter() - t0 > 15.0:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done * w.n / dt, 1), "unit": "keys/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": "%d of %d heads of the layer step (%d keys each): split, plain encode, "
+                      "H-weighted encode of retrieval rows, reconstruct; %.1f s" % (done, w.heads, w.n, dt)}
+
+
+if __name__ == "__main__":
+    main()

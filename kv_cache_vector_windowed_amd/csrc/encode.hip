@@ -2,32 +2,33 @@
 // "veloxquant_mlx.quantizers.a2ats module", a2ats_h_weighted_assignment (Eq. 14 through the
 // Eq. 15-17 Cholesky identity):
 //     code(k) = argmin_j (k - c_j) H (k - c_j)^T = argmin_j ||k L - c_j L||^2,   H = L L^T.
-// Expanding the square, with v_j = c_j H and b_j = c_j H c_j^T (exact in fp64),
+// With w_j = c_j L, v_j = w_j L^T (= c_j H) and b_j = ||w_j||^2, all exact in fp64,
 //     ||kL - c_jL||^2 = ||kL||^2 - 2 (k . v_j - b_j / 2),
 // so the code maximises the score s_j = k . v_j - b_j / 2: a dense contraction of the keys
 // against the transformed codebook plus a row argmax.  Without L, H = I (plain nearest
-// centroid, the bulk path).
+// centroid, the bulk path of the first docs page's "How it works").
 //
 // Exactness.  The contraction runs on fp16 MFMA (bf16 keys are exact in fp16; the codebook
-// side is rounded after a power-of-two scale S).  For each key the kernel bounds the
-// MFMA error rigorously,
+// side is rounded after a power-of-two scale S).  For each key the error of every MFMA score
+// is bounded rigorously,
 //     |acc_j - S s_j| <= E = |k| rho + |k - k16| nu + gamma (B + |k16| nu) + u B,
 // (rho = max_j |S v_j - v16_j|, nu = max_j |v16_j|, B = max_j S b_j / 2, gamma covers the
-// fp32 accumulation of 129 terms) and only accepts the MFMA winner when the bound proves it.
-// Close calls are settled by exact fp64 scores; what remains is rescanned.
+// fp32 accumulation of 129 terms).  The MFMA winner is accepted only when the bound proves
+// it; close calls are settled by exact fp64 scores, and whatever is still open is rescanned.
 //
-// Kernels
-//   enc_gram        H = L L^T in fp64 (skipped without L); zeroes per-call counters.
-//   enc_prep_rows   v_j = c_j H and b_j in fp64; per-head max |v| and max b.
-//   enc_prep_frag   fp16 operand fragments of S v (MFMA A-operand order), the fp32 bias
-//                   -S b_j / 2 per accumulator slot, rho and nu; optionally fp16 hi/lo
-//                   fragments of L^T for ||kL||^2.
-//   enc_coarse      the MFMA pass (see the kernel comment) with certification and fp64
-//                   rerank of the two leading candidates.
-//   enc_rescan      keys left uncertified: a second MFMA pass that collects every centroid
-//                   whose score could reach the best exact score, then fp64 decides.
-//   enc_fullscan    keys that overflow fp16 or overflow the candidate list: fp64 scan.
-//   enc_znorm64     ||kL||^2 in fp64 for fp32 keys when distances are requested with L.
+// Kernels (in launch order)
+//   enc_prep_rows       w = c L, v = w L^T, b = ||w||^2 in fp64, per-workgroup maxima.
+//   enc_prep_frag       fp16 fragments of S v in MFMA A-operand order, fp32 bias -S b / 2 per
+//                       accumulator slot, per-workgroup rho / nu; optional fp16 hi/lo
+//                       fragments of L^T for ||kL||^2; clears the list counters.
+//   enc_clear           zeroes the rescan candidate counters.
+//   enc_znorm64         ||kL||^2 in fp64 (fp32 keys with distances and L only).
+//   enc_coarse          the MFMA pass; writes directly certified codes, lists the rest.
+//   enc_refine          fp64 scores of the two leading candidates of every listed key.
+//   enc_rescan_collect  second MFMA pass over the keys still open: collects every centroid
+//                       whose score could reach the best exact score.
+//   enc_rescan_decide   fp64 over the collected candidates.
+//   enc_fullscan        fp64 over the whole codebook (fp16 overflow, list overflow).
 #include "common.hpp"
 
 namespace a2ats {
@@ -38,40 +39,50 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = A2ATS_HEAD_DIM;
+constexpr int kLd = kD + 1;               // padded LDS row of L (conflict-free column reads)
 constexpr int kRows = 32;                 // centroids per MFMA tile
-constexpr int kSteps = kD / 16;           // k-steps of 16 per tile (v_mfma_f32_32x32x16_f16)
-constexpr int kFragPerTile = kSteps * 64; // half8 fragments per tile
-constexpr int kTPS = 4;                   // tiles per LDS stage
+constexpr int kSteps = kD / 16;           // k-steps per tile (v_mfma_f32_32x32x16_f16)
+constexpr int kFragPerTile = kSteps * 64; // half8 fragments per tile (8 KiB)
+constexpr int kRing = 3;                  // LDS tile ring of the coarse pass
 constexpr int kKeysPerWG = 256;           // 4 waves x 64 keys
 constexpr int kCandCap = 32;              // rescan candidates per key
+constexpr int kRescanTiles = 8;           // tiles per rescan work item
 constexpr float kPadBias = -1.0e38f;      // bias of padding rows: finite, never competitive
 
-struct EncHead {
-  unsigned maxabs_v;  // float bits, max |v_ja| rounded up
-  unsigned maxb;      // float bits, max b_j rounded up
-  unsigned rho;       // float bits, max_j ||S v_j - v16_j|| rounded up (scaled units)
-  unsigned nu;        // float bits, max_j ||v16_j|| rounded up (scaled units)
-  unsigned maxabs_l;  // float bits, max |L_ab| rounded up
-  unsigned pad[3];
-};
-
 struct Counters {
-  unsigned unc;        // entries in the rescan list
-  unsigned full;       // entries in the full-scan list
-  unsigned stats[8];   // keys, direct, reranked, rescanned, full_scan
+  unsigned refine;      // refine list entries
+  unsigned full;        // full-scan list entries
+  unsigned stats[8];    // keys, direct, reranked, rescanned, full_scan
+  unsigned unc[1];      // per-head rescan list lengths follow (heads entries)
 };
 
-struct UncEntry {
-  int32_t head;
+struct RefEntry {       // a key whose code needs fp64 scores
+  int32_t head, row;
+  int32_t j0, j1;       // leading candidates (j1 < 0: none)
+  double thr;           // certified if the best exact score exceeds thr + eps (unscaled)
+  double e_unscaled;    // E / S, for the rescan threshold
+  float z2;             // ||kL||^2 (distances), or -1: ||k||^2 computed here
+  int32_t pad;
+};
+
+struct UncEntry {       // a key left open after the rerank
   int32_t row;
-  double sbest;        // exact score of the best reranked candidate (a lower bound of the max)
-  int32_t jbest;       // its index
+  int32_t jbest;
+  double sbest;         // exact score of jbest (a lower bound of the maximum)
+  double e_unscaled;
+  float z2;
+  int32_t pad;
+};
+
+struct FullEntry {
+  int32_t head, row;
+  float z2;
   int32_t pad;
 };
 
 __device__ __forceinline__ float round_up_f(double x) {
   float f = (float)x;
-  if ((double)f < x) f = __uint_as_float(__float_as_uint(f) + (f >= 0.f ? 1u : -1u));
+  if ((double)f < x) f = __uint_as_float(__float_as_uint(f) + (f >= 0.f ? 1u : 0xFFFFFFFFu));
   return f;
 }
 
@@ -81,46 +92,59 @@ __device__ __forceinline__ int ilog2_floor(float x) {  // x > 0, normal
 
 __device__ __forceinline__ float pow2f(int e) { return __uint_as_float((unsigned)(e + 127) << 23); }
 
+__device__ __forceinline__ float scale_for(float maxabs) {  // max |S x| in [2^14, 2^15)
+  return maxabs > 0.f ? pow2f(14 - ilog2_floor(maxabs)) : 1.f;
+}
+
 // Accumulator slot r of a lane in half hh holds MFMA output row 8(r/4) + 4hh + (r%4).
 __device__ __forceinline__ int slot_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
 
-// ------------------------------------------------------------------ prep
-__global__ __launch_bounds__(256) void enc_gram(const float* __restrict__ chol,
-                                                double* __restrict__ h64,
-                                                EncHead* __restrict__ info,
-                                                Counters* __restrict__ cnt) {
-  const int head = blockIdx.y;
-  const int e = blockIdx.x * 256 + threadIdx.x;  // element of the 128 x 128 matrix
-  if (blockIdx.x == 0 && threadIdx.x < sizeof(EncHead) / 4)
-    reinterpret_cast<unsigned*>(&info[head])[threadIdx.x] = 0u;
-  if (head == 0 && blockIdx.x == 0 && threadIdx.x < sizeof(Counters) / 4)
-    reinterpret_cast<unsigned*>(cnt)[threadIdx.x] = 0u;
-  if (!chol) return;
-  const float* L = chol + (int64_t)head * kD * kD;
-  const int i = e / kD, j = e % kD;
-  const int kmax = i < j ? i : j;
-  double s = 0.0;
-  for (int k = 0; k <= kmax; ++k) s += (double)L[i * kD + k] * (double)L[j * kD + k];
-  h64[(int64_t)head * kD * kD + e] = s;
+// Workgroup-aggregated list append: every thread of the workgroup calls it (uniform control
+// flow); threads with want == true receive distinct slots of `*counter`.  One global atomic
+// per workgroup instead of one per entry (same-address atomics serialise at the L2).
+__device__ __forceinline__ unsigned block_append(unsigned* counter, bool want, unsigned* s_cnt,
+                                                 unsigned* s_base) {
+  __syncthreads();
+  if (threadIdx.x == 0) *s_cnt = 0u;
+  __syncthreads();
+  const unsigned local = want ? atomicAdd(s_cnt, 1u) : 0u;
+  __syncthreads();
+  if (threadIdx.x == 0) *s_base = *s_cnt ? atomicAdd(counter, *s_cnt) : 0u;
+  __syncthreads();
+  return *s_base + local;
 }
 
-// v_j = c_j H, b_j = c_j . v_j (fp64).  32 rows per workgroup; H and the rows in LDS.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// ------------------------------------------------------------------ prep
+// 32 rows per workgroup.  L (fp32) and the rows in LDS; w = c L then v = w L^T in fp64,
+// each thread owning 4 rows x 4 columns.  Writes v (fp64 and fp32), b, and this
+// workgroup's max |v| and max b; workgroup 0 of a head also records max |L|.
 __global__ __launch_bounds__(256) void enc_prep_rows(const float* __restrict__ cb, int64_t c,
-                                                     const double* __restrict__ h64,
                                                      const float* __restrict__ chol,
                                                      double* __restrict__ v64,
+                                                     float* __restrict__ v32,
                                                      double* __restrict__ b64,
-                                                     EncHead* __restrict__ info) {
-  const int plain = chol == nullptr;
+                                                     float* __restrict__ part_a, int nwg) {
   extern __shared__ double sm[];
-  double* H = sm;                                  // [128][128] (unused when plain)
-  float* cr = reinterpret_cast<float*>(sm + (plain ? 0 : kD * kD));  // [32][128]
+  double* w = sm;                                             // [32][128] fp64
+  float* Ls = reinterpret_cast<float*>(sm + 32 * kD);         // [128][129] fp32 (with L)
+  float* cr = Ls + (chol ? kD * kLd : 0);                     // [32][128] fp32
+  __shared__ float red[3][4];
   const int head = blockIdx.y;
   const int64_t j0 = (int64_t)blockIdx.x * 32;
   const int t = threadIdx.x;
   const float* cbh = cb + (int64_t)head * c * kD;
-  if (!plain)
-    for (int e = t; e < kD * kD; e += 256) H[e] = h64[(int64_t)head * kD * kD + e];
+  const float* L = chol ? chol + (int64_t)head * kD * kD : nullptr;
+  float lmax = 0.f;
+  if (L)
+    for (int e = t; e < kD * kD; e += 256) {
+      Ls[(e / kD) * kLd + e % kD] = L[e];
+      lmax = fmaxf(lmax, fabsf(L[e]));
+    }
   for (int e = t; e < 32 * kD; e += 256) {
     int r = e / kD, a = e % kD;
     cr[e] = (j0 + r < c) ? cbh[(j0 + r) * kD + a] : 0.f;
@@ -129,27 +153,52 @@ __global__ __launch_bounds__(256) void enc_prep_rows(const float* __restrict__ c
   const int rg = t / 32;  // rows rg*4 .. rg*4+3
   const int cg = t % 32;  // columns cg + 32m
   double acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int m = 0; m < 4; ++m) acc[i][m] = 0.0;
-  if (plain) {
+  if (L) {
+    // w[r][a] = sum_b c[r][b] L[b][a]   (L is lower triangular: zeros above the diagonal)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) acc[i][m] = (double)cr[(rg * 4 + i) * kD + cg + 32 * m];
-  } else {
+      for (int m = 0; m < 4; ++m) acc[i][m] = 0.0;
     for (int b = 0; b < kD; ++b) {
-      double cv[4], hv[4];
+      double cv[4], lv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) cv[i] = (double)cr[(rg * 4 + i) * kD + b];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) hv[m] = H[b * kD + cg + 32 * m];
+      for (int m = 0; m < 4; ++m) lv[m] = (double)Ls[b * kLd + cg + 32 * m];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) acc[i][m] += cv[i] * hv[m];
+        for (int m = 0; m < 4; ++m) acc[i][m] += cv[i] * lv[m];
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) w[(rg * 4 + i) * kD + cg + 32 * m] = acc[i][m];
+    __syncthreads();
+    // v[r][a] = sum_b w[r][b] L[a][b]
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc[i][m] = 0.0;
+    for (int b = 0; b < kD; ++b) {
+      double wv[4], lv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[i] = w[(rg * 4 + i) * kD + b];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) lv[m] = (double)Ls[(cg + 32 * m) * kLd + b];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[i][m] += wv[i] * lv[m];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        acc[i][m] = (double)cr[(rg * 4 + i) * kD + cg + 32 * m];
+        w[(rg * 4 + i) * kD + cg + 32 * m] = acc[i][m];
+      }
   }
   float vmax = 0.f, bmax = 0.f;
 #pragma unroll
@@ -157,12 +206,16 @@ __global__ __launch_bounds__(256) void enc_prep_rows(const float* __restrict__ c
     const int64_t j = j0 + rg * 4 + i;
     double bp = 0.0;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) bp += (double)cr[(rg * 4 + i) * kD + cg + 32 * m] * acc[i][m];
-    for (int o = 16; o > 0; o >>= 1) bp += __shfl_xor(bp, o);  // 32 lanes of this row group
+    for (int m = 0; m < 4; ++m) {
+      const double wv = w[(rg * 4 + i) * kD + cg + 32 * m];
+      bp += wv * wv;
+    }
+    for (int o = 16; o > 0; o >>= 1) bp += __shfl_xor(bp, o);  // the 32 lanes of this row group
     if (j < c) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         v64[((int64_t)head * c + j) * kD + cg + 32 * m] = acc[i][m];
+        v32[((int64_t)head * c + j) * kD + cg + 32 * m] = (float)acc[i][m];
         vmax = fmaxf(vmax, round_up_f(fabs(acc[i][m])));
       }
       if (cg == 0) b64[(int64_t)head * c + j] = bp;
@@ -172,116 +225,137 @@ __global__ __launch_bounds__(256) void enc_prep_rows(const float* __restrict__ c
   for (int o = 32; o > 0; o >>= 1) {
     vmax = fmaxf(vmax, __shfl_xor(vmax, o));
     bmax = fmaxf(bmax, __shfl_xor(bmax, o));
+    lmax = fmaxf(lmax, __shfl_xor(lmax, o));
   }
   if ((t & 63) == 0) {
-    atomicMax(&info[head].maxabs_v, __float_as_uint(vmax));
-    atomicMax(&info[head].maxb, __float_as_uint(bmax));
+    red[0][t >> 6] = vmax;
+    red[1][t >> 6] = bmax;
+    red[2][t >> 6] = lmax;
   }
-  if (!plain && blockIdx.x == 0) {  // max |L| for the z-norm fragments
-    const float* L = chol + (int64_t)head * kD * kD;
-    float a = 0.f;
-    for (int e = t; e < kD * kD; e += 256) a = fmaxf(a, fabsf(L[e]));
-    for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
-    if ((t & 63) == 0) atomicMax(&info[head].maxabs_l, __float_as_uint(a));
-  }
+  __syncthreads();
+  if (t < 3)
+    part_a[((int64_t)head * nwg + blockIdx.x) * 4 + t] =
+        fmaxf(fmaxf(red[t][0], red[t][1]), fmaxf(red[t][2], red[t][3]));
 }
 
-__device__ __forceinline__ float head_scale(const EncHead& h) {
-  float m = __uint_as_float(h.maxabs_v);
-  if (!(m > 0.f)) return 1.f;
-  return pow2f(14 - ilog2_floor(m));  // max |S v| in [2^14, 2^15)
+// Head constants from the prep_rows partials.
+struct HeadScale {
+  float S;      // codebook-side scale
+  float maxb;   // max b_j (rounded up)
+  float SL;     // L-side scale
+};
+
+__device__ HeadScale head_scale(const float* part_a, int64_t head, int nwg) {
+  float a = 0.f, b = 0.f;
+  for (int i = 0; i < nwg; ++i) {
+    a = fmaxf(a, part_a[(head * nwg + i) * 4 + 0]);
+    b = fmaxf(b, part_a[(head * nwg + i) * 4 + 1]);
+  }
+  HeadScale h;
+  h.S = scale_for(a);
+  h.maxb = b;
+  h.SL = scale_for(part_a[(head * nwg) * 4 + 2]);
+  return h;
 }
 
-// One thread per padded row j in [0, T*32): fp16 fragments of S v_j, the bias slot, rho, nu.
-// Threads past the rows build the L^T hi/lo fragments when requested.
+// 16 threads per padded row (each one k-chunk of 8): fp16 fragments of S v, the bias slot,
+// and this workgroup's max residual / max fragment norm.  Threads past the rows build the
+// L^T hi/lo fragments; workgroup (0, 0) clears the list counters.
 __global__ __launch_bounds__(256) void enc_prep_frag(const double* __restrict__ v64,
                                                      const double* __restrict__ b64, int64_t c,
                                                      int T, const float* __restrict__ chol,
-                                                     int want_l, EncHead* __restrict__ info,
+                                                     int want_l, const float* __restrict__ part_a,
+                                                     int nwg_a, float* __restrict__ part_b,
                                                      half8* __restrict__ v16,
                                                      float* __restrict__ bias,
-                                                     half8* __restrict__ lfrag) {
+                                                     half8* __restrict__ lfrag,
+                                                     unsigned* __restrict__ cnt, int ncnt) {
   const int head = blockIdx.y;
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int t = threadIdx.x;
+  if (head == 0 && blockIdx.x == 0)
+    for (int i = t; i < ncnt; i += 256) cnt[i] = 0u;
+  const HeadScale hs = head_scale(part_a, head, nwg_a);
   const int64_t rows = (int64_t)T * kRows;
-  EncHead hi = info[head];
-  float rr = 0.f, nn = 0.f;
-  if (j < rows) {
-    const float S = head_scale(hi);
+  const int64_t rid = (int64_t)blockIdx.x * 16 + t / 16;  // padded row (or L^T row after rows)
+  const int chunk = t % 16;                                // k = 8 chunk .. 8 chunk + 7
+  const int s = chunk / 2, hh = chunk % 2;
+  double rho2 = 0.0, nu2 = 0.0;
+  if (rid < rows) {
+    const int64_t j = rid;
     const int64_t tile = j / kRows;
     const int i = (int)(j % kRows);
-    half8* vt = v16 + ((int64_t)head * T + tile) * kFragPerTile;
-    double rho2 = 0.0, nu2 = 0.0;
-    for (int s = 0; s < kSteps; ++s) {
-      for (int hh = 0; hh < 2; ++hh) {
-        half8 f;
+    half8 f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int a = 16 * s + 8 * hh + e;
-          double sv = (j < c) ? (double)S * v64[((int64_t)head * c + j) * kD + a] : 0.0;
-          _Float16 q = (_Float16)sv;  // fp64 -> fp16, round to nearest even
-          double dq = (double)q;
-          rho2 += (sv - dq) * (sv - dq);
-          nu2 += dq * dq;
-          f[e] = q;
-        }
-        vt[s * 64 + i + 32 * hh] = f;
-      }
+    for (int e = 0; e < 8; ++e) {
+      const int a = 8 * chunk + e;
+      const double sv = (j < c) ? (double)hs.S * v64[((int64_t)head * c + j) * kD + a] : 0.0;
+      const _Float16 q = (_Float16)sv;  // fp64 -> fp16, round to nearest even
+      const double dq = (double)q;
+      rho2 += (sv - dq) * (sv - dq);
+      nu2 += dq * dq;
+      f[e] = q;
     }
-    const int hh = (i >> 2) & 1;
-    const int r = (i >> 3) * 4 + (i & 3);
-    bias[((int64_t)head * T + tile) * 32 + hh * 16 + r] =
-        (j < c) ? (float)(-0.5 * (double)S * b64[(int64_t)head * c + j]) : kPadBias;
-    rr = round_up_f(sqrt(rho2));
-    nn = round_up_f(sqrt(nu2));
-  } else if (want_l && j < rows + kD) {
-    // Row a of L^T (output component z_a = sum_b k_b L_ba) as MFMA A-operand fragments:
-    // 4 tiles of 32 rows; tiles 0..3 hold the fp16 high parts, 4..7 the residuals.
-    const int a = (int)(j - rows);
+    v16[((int64_t)head * T + tile) * kFragPerTile + s * 64 + i + 32 * hh] = f;
+    if (chunk == 0) {
+      const int bh = (i >> 2) & 1;
+      const int r = (i >> 3) * 4 + (i & 3);
+      bias[((int64_t)head * T + tile) * 32 + bh * 16 + r] =
+          (j < c) ? (float)(-0.5 * (double)hs.S * b64[(int64_t)head * c + j]) : kPadBias;
+    }
+  } else if (want_l && rid < rows + kD) {
+    // Row a of L^T (output z_a = sum_b k_b L_ba) as A-operand fragments: 4 tiles of 32
+    // rows; tiles 0..3 the fp16 high parts, 4..7 the residuals.
+    const int a = (int)(rid - rows);
     const float* L = chol + (int64_t)head * kD * kD;
-    float ml = __uint_as_float(hi.maxabs_l);
-    const float SL = ml > 0.f ? pow2f(14 - ilog2_floor(ml)) : 1.f;
     const int tile = a / kRows, i = a % kRows;
-    half8* lt = lfrag + (int64_t)head * 8 * kFragPerTile;
-    for (int s = 0; s < kSteps; ++s) {
-      for (int hh = 0; hh < 2; ++hh) {
-        half8 fh, fl;
+    half8 fh, fl;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int b = 16 * s + 8 * hh + e;
-          double x = (double)SL * (double)L[b * kD + a];
-          _Float16 qh = (_Float16)x;
-          fh[e] = qh;
-          fl[e] = (_Float16)(x - (double)qh);
-        }
-        lt[(int64_t)tile * kFragPerTile + s * 64 + i + 32 * hh] = fh;
-        lt[(int64_t)(tile + 4) * kFragPerTile + s * 64 + i + 32 * hh] = fl;
-      }
+    for (int e = 0; e < 8; ++e) {
+      const int b = 8 * chunk + e;
+      const double x = (double)hs.SL * (double)L[b * kD + a];
+      const _Float16 qh = (_Float16)x;
+      fh[e] = qh;
+      fl[e] = (_Float16)(x - (double)qh);
     }
+    half8* lt = lfrag + (int64_t)head * 8 * kFragPerTile;
+    lt[(int64_t)tile * kFragPerTile + s * 64 + i + 32 * hh] = fh;
+    lt[(int64_t)(tile + 4) * kFragPerTile + s * 64 + i + 32 * hh] = fl;
   }
-  for (int o = 32; o > 0; o >>= 1) {  // every lane of the wave takes part
+  // row norms over the 16 threads of the row, then the workgroup maxima
+  for (int o = 8; o > 0; o >>= 1) {
+    rho2 += __shfl_xor(rho2, o);
+    nu2 += __shfl_xor(nu2, o);
+  }
+  float rr = round_up_f(sqrt(rho2)), nn = round_up_f(sqrt(nu2));
+  for (int o = 32; o > 0; o >>= 1) {
     rr = fmaxf(rr, __shfl_xor(rr, o));
     nn = fmaxf(nn, __shfl_xor(nn, o));
   }
-  if ((threadIdx.x & 63) == 0) {
-    atomicMax(&info[head].rho, __float_as_uint(rr));
-    atomicMax(&info[head].nu, __float_as_uint(nn));
+  __shared__ float red[2][4];
+  if ((t & 63) == 0) {
+    red[0][t >> 6] = rr;
+    red[1][t >> 6] = nn;
   }
+  __syncthreads();
+  if (t < 2)
+    part_b[((int64_t)head * gridDim.x + blockIdx.x) * 2 + t] =
+        fmaxf(fmaxf(red[t][0], red[t][1]), fmaxf(red[t][2], red[t][3]));
 }
 
-// ------------------------------------------------------------------ key fragments
+// ------------------------------------------------------------------ shared helpers
+template <int NB>
 struct KeyFrags {
-  half8 f[2][kSteps];  // two 32-key blocks (MFMA B operand: key = lane % 32, k = 16s+8hh+e)
-  float n2[2];         // ||k||^2 of this lane's 64 elements (fp32, exact values)
-  float e2[2];         // ||k - k16||^2 partial
-  bool bad[2];         // an element outside the fp16 range
+  half8 f[NB][kSteps];  // 32-key blocks (MFMA B operand: key = lane % 32, k = 16s+8hh+e)
+  float n2[NB];         // ||k||^2 (fp32 of the exact values)
+  float e2[NB];         // ||k - k16||^2
+  bool bad[NB];         // an element outside the fp16 range
 };
 
-template <int DT>
+template <int DT, int NB>
 __device__ __forceinline__ void load_key_frags(const void* keys, int64_t head, int64_t n,
-                                               const int64_t row[2], int hh, KeyFrags& kf) {
+                                               const int64_t* row, int hh, KeyFrags<NB>& kf) {
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
+  for (int blk = 0; blk < NB; ++blk) {
     kf.n2[blk] = 0.f;
     kf.e2[blk] = 0.f;
     kf.bad[blk] = false;
@@ -292,11 +366,11 @@ __device__ __forceinline__ void load_key_frags(const void* keys, int64_t head, i
         const int64_t off = (head * n + row[blk]) * kD + 16 * s + 8 * hh;
         if (DT == A2ATS_BF16) {
           const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(keys) + off);
-          const unsigned w[4] = {raw.x, raw.y, raw.z, raw.w};
+          const unsigned wv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            x[2 * e] = __uint_as_float(w[e] << 16);
-            x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+            x[2 * e] = __uint_as_float(wv[e] << 16);
+            x[2 * e + 1] = __uint_as_float(wv[e] & 0xFFFF0000u);
           }
         } else {
           const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(keys) + off);
@@ -308,71 +382,29 @@ __device__ __forceinline__ void load_key_frags(const void* keys, int64_t head, i
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = 0.f;
       }
+      half8 v;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const bool ok = fabsf(x[e]) < 65504.0f;
         const _Float16 q = ok ? (_Float16)x[e] : (_Float16)0.0f;
         kf.bad[blk] |= !ok;
-        const float d = x[e] - (float)q;  // exact: q is x rounded to 11 significant bits
+        const float d = x[e] - (float)q;  // exact
         kf.n2[blk] += x[e] * x[e];
         kf.e2[blk] += d * d;
-        kf.f[blk][s][e] = q;
+        v[e] = q;
       }
+      kf.f[blk][s] = v;
     }
+    kf.n2[blk] += __shfl_xor(kf.n2[blk], 32);
+    kf.e2[blk] += __shfl_xor(kf.e2[blk], 32);
+    kf.bad[blk] = kf.bad[blk] || __shfl_xor((int)kf.bad[blk], 32);
   }
 }
-
-// Exact score s_j = k . v_j - b_j / 2 in fp64, key row read from global.
-template <int DT>
-__device__ double exact_score(const void* keys, int64_t head, int64_t n, int64_t row,
-                              const double* v64, const double* b64, int64_t c, int64_t j) {
-  const double* v = v64 + (head * c + j) * kD;
-  const int64_t off = (head * n + row) * kD;
-  double s = 0.0;
-  for (int a = 0; a < kD; a += 2) {
-    const double2 vv = *reinterpret_cast<const double2*>(v + a);
-    s += (double)load_elem(keys, DT, off + a) * vv.x;
-    s += (double)load_elem(keys, DT, off + a + 1) * vv.y;
-  }
-  return s - 0.5 * b64[head * c + j];
-}
-
-// (value, index) order: larger value first, equal values keep the lower index first.
-__device__ __forceinline__ bool before(float v1, int j1, float v2, int j2) {
-  return v1 > v2 || (v1 == v2 && j1 < j2);
-}
-
-struct Top3 {
-  float v[3];
-  int j[3];
-  __device__ __forceinline__ void init() {
-    v[0] = v[1] = v[2] = -INFINITY;
-    j[0] = j[1] = j[2] = 0x7FFFFFFF;
-  }
-  __device__ __forceinline__ void push(float x, int jx) {
-    if (before(x, jx, v[2], j[2])) {
-      if (before(x, jx, v[1], j[1])) {
-        v[2] = v[1]; j[2] = j[1];
-        if (before(x, jx, v[0], j[0])) {
-          v[1] = v[0]; j[1] = j[0];
-          v[0] = x; j[0] = jx;
-        } else {
-          v[1] = x; j[1] = jx;
-        }
-      } else {
-        v[2] = x; j[2] = jx;
-      }
-    }
-  }
-};
 
 // Error bound E (scaled units) of a key's MFMA scores, evaluated with upward margins.
-__device__ __forceinline__ double score_bound(float n2, float e2, const EncHead& h, float S) {
+__device__ __forceinline__ double score_bound(float n2, float e2, double rho, double nu, double B) {
   const double kn = sqrt((double)n2) * (1.0 + 0x1p-18);
   const double ke = sqrt((double)e2) * (1.0 + 0x1p-18);
-  const double rho = (double)__uint_as_float(h.rho);
-  const double nu = (double)__uint_as_float(h.nu);
-  const double B = 0.5 * (double)S * (double)__uint_as_float(h.maxb);
   const double gamma = 130.0 * 0x1p-23;
   return (kn * rho + ke * nu + gamma * (B + (kn + ke) * nu) + 0x1p-23 * B) * (1.0 + 0x1p-16) + 1e-30;
 }
@@ -382,63 +414,138 @@ __device__ __forceinline__ double pack_slack(float p, int tbits) {
   return fabs((double)p) * ldexp(1.0, tbits - 22) + ldexp(1.0, tbits - 140);
 }
 
+// Replace the low bits of x with the tile index.  Written in C so the compiler inserts the
+// wait states between the MFMA that produced x and this read; with the tile index held in
+// a VGPR (see vgpr_of) it becomes one v_and_or_b32 (mask in an SGPR).
+__device__ __forceinline__ float pack_tile(float x, unsigned keep, unsigned tile_v) {
+  return __uint_as_float((__float_as_uint(x) & keep) | tile_v);
+}
+
+// A uniform value copied into a VGPR, opaque to the optimiser (GFX9 VALU instructions may
+// read only one scalar operand).
+__device__ __forceinline__ unsigned vgpr_of(unsigned s) {
+  unsigned v;
+  asm("v_mov_b32 %0, %1" : "=v"(v) : "s"(s));
+  return v;
+}
+
+// Exact fp64 score of one candidate, 16 lanes cooperating (lane g of the group owns dims
+// 8g .. 8g+7).  Returns the score (valid in every lane of the group) and, in z2, ||k||^2.
+template <int DT>
+__device__ __forceinline__ double coop_score(const void* keys, int64_t off_key, const double* vrow,
+                                             double bj, int g, double* z2) {
+  double x[8];
+  if (DT == A2ATS_BF16) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(keys) + off_key + 8 * g);
+    const unsigned wv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = (double)__uint_as_float(wv[e] << 16);
+      x[2 * e + 1] = (double)__uint_as_float(wv[e] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(keys) + off_key + 8 * g);
+    const float4 a = p[0], b = p[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+  double s = 0.0, k2 = 0.0;
+  const double2* v2 = reinterpret_cast<const double2*>(vrow + 8 * g);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const double2 vv = v2[e];
+    s += x[2 * e] * vv.x + x[2 * e + 1] * vv.y;
+    k2 += x[2 * e] * x[2 * e] + x[2 * e + 1] * x[2 * e + 1];
+  }
+  for (int o = 8; o > 0; o >>= 1) {
+    s += __shfl_xor(s, o);
+    k2 += __shfl_xor(k2, o);
+  }
+  *z2 = k2;
+  return s - 0.5 * bj;
+}
+
 // ------------------------------------------------------------------ the MFMA pass
 // Workgroup: 256 keys of one head (4 waves x two 32-key column blocks).  Lane l serves key
-// column l % 32 of both blocks and, within every 32-centroid tile, the 16 rows
-// 8(r/4) + 4(l/32) + (r%4).  The codebook streams through LDS in stages of 4 tiles,
-// double-buffered; each tile costs 8 MFMAs per block with the bias preloaded as the
-// accumulator.  Every accumulator slot r keeps its own running top-2 over the tiles (the
-// tile index packed into the low bits): 3 VALU ops per score (pack, med3, max).  At the end
-// each key has 32 (max, second) pairs; the top three of those and the largest second give
-// the certificate:
-//   direct    t1 - t2 > 2E (+ packing slack)                  -> code = j(t1)
-//   reranked  exact fp64 scores of j(t1), j(t2) beat max(t3, every list's second) + E
-//   otherwise the key goes to the rescan list with its best exact score.
-// Workgroups are mapped so that each XCD serves a contiguous range of (head, block) pairs.
-template <int DT, bool ZNORM>
-__global__ __launch_bounds__(256, 2) void enc_coarse(
+// column l % 32 of both blocks and, in every 32-centroid tile, the 16 rows
+// 8(r/4) + 4(l/32) + (r%4).  Codebook tiles stream through a 3-deep LDS ring, one barrier
+// per tile; each tile costs 8 MFMAs per block with the bias as the first accumulator input.
+// Every accumulator slot keeps its own running top-2 over the tiles, the tile index packed
+// into the low bits: 3 VALU ops per score (pack, med3 for the second, med3 for the max).
+// At the end each key has 32 (max, second) pairs: the top three and the largest second give
+//   direct  t1 - t2 > 2E (+ packing slack)  -> code j(t1)
+//   else    listed for the fp64 rerank of j(t1), j(t2) against max(t3, largest second) + E.
+// Workgroups are dealt to XCDs round-robin; the mapping gives each XCD a contiguous range of
+// (head, key block) pairs so a head's codebook stays in one L2.
+template <int DT, bool ZNORM, bool DIST>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void enc_coarse(
     const void* __restrict__ keys, int64_t n, const int32_t* __restrict__ idx, int64_t n_sel,
     int64_t heads, int nkb, int T, int tbits, const half8* __restrict__ v16,
-    const float* __restrict__ bias, const double* __restrict__ v64,
+    const float* __restrict__ bias, const float* __restrict__ v32,
     const double* __restrict__ b64, int64_t c, const half8* __restrict__ lfrag,
-    const EncHead* __restrict__ info, float* __restrict__ znorm,
-    uint16_t* __restrict__ codes, float* __restrict__ dist, UncEntry* __restrict__ unc,
-    UncEntry* __restrict__ full, Counters* __restrict__ cnt) {
-  __shared__ half8 sv[2][kTPS][kFragPerTile];
-  __shared__ __attribute__((aligned(16))) float sb[2][kTPS][32];
+    const float* __restrict__ part_a, int nwg_a, const float* __restrict__ part_b, int nwg_b,
+    float* __restrict__ znorm, uint16_t* __restrict__ codes, float* __restrict__ dist,
+    RefEntry* __restrict__ refl, FullEntry* __restrict__ full, Counters* __restrict__ cnt) {
+  __shared__ half8 sv[kRing][kFragPerTile];
+  __shared__ __attribute__((aligned(16))) float sb[kRing][32];
+  __shared__ float s_red[2][4];
   const int64_t G = gridDim.x;
   const int64_t per_xcd = G / 8;
-  const int64_t w = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (w >= heads * nkb) return;
-  const int64_t head = w / nkb;
-  const int64_t kb = w % nkb;
+  const int64_t wk = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (wk >= heads * nkb) return;
+  const int64_t head = wk / nkb;
+  const int64_t kb = wk % nkb;
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, col = lane & 31, hh = lane >> 5;
-  const EncHead hinfo = info[head];
-  const float S = head_scale(hinfo);
+  const HeadScale hs = head_scale(part_a, head, nwg_a);
+  {  // rho and nu: maxima over the prep_frag partials of this head
+    float rr = 0.f, nn = 0.f;
+    for (int i = t; i < nwg_b; i += 256) {
+      rr = fmaxf(rr, part_b[(head * nwg_b + i) * 2 + 0]);
+      nn = fmaxf(nn, part_b[(head * nwg_b + i) * 2 + 1]);
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      rr = fmaxf(rr, __shfl_xor(rr, o));
+      nn = fmaxf(nn, __shfl_xor(nn, o));
+    }
+    if (lane == 0) {
+      s_red[0][wave] = rr;
+      s_red[1][wave] = nn;
+    }
+  }
+  const half8* vh = v16 + head * (int64_t)T * kFragPerTile;
+  const float* bh = bias + head * (int64_t)T * 32;
+  // tile loader: 256 threads x 2 fragments; 8 threads x 4 bias floats
+  half8 pf0, pf1;
+  f4 pb = {};
+  auto fetch = [&](int tile) {
+    pf0 = vh[(int64_t)tile * kFragPerTile + t];
+    pf1 = vh[(int64_t)tile * kFragPerTile + 256 + t];
+    if (t < 8) pb = *reinterpret_cast<const f4*>(bh + (int64_t)tile * 32 + t * 4);
+  };
+  auto commit = [&](int buf) {
+    sv[buf][t] = pf0;
+    sv[buf][256 + t] = pf1;
+    if (t < 8) *reinterpret_cast<f4*>(&sb[buf][t * 4]) = pb;
+  };
+  fetch(0);
+  commit(0);
+  if (T > 1) fetch(1);
 
   int64_t row[2];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     const int64_t sel = kb * kKeysPerWG + wave * 64 + blk * 32 + col;
-    int64_t r = sel < n_sel ? (idx ? (int64_t)idx[head * n_sel + sel] : sel) : -1;
+    const int64_t r = sel < n_sel ? (idx ? (int64_t)idx[head * n_sel + sel] : sel) : -1;
     row[blk] = (r >= 0 && r < n) ? r : -1;  // out-of-range index entries are skipped
   }
-  KeyFrags kf;
-  load_key_frags<DT>(keys, head, n, row, hh, kf);
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    kf.n2[blk] += __shfl_xor(kf.n2[blk], 32);
-    kf.e2[blk] += __shfl_xor(kf.e2[blk], 32);
-    kf.bad[blk] = kf.bad[blk] || __shfl_xor((int)kf.bad[blk], 32);
-  }
+  KeyFrags<2> kf;
+  load_key_frags<DT, 2>(keys, head, n, row, hh, kf);
 
   // ||k L||^2 from fp16 hi/lo fragments of L^T (bf16 keys are exact in fp16).
   float zn[2] = {0.f, 0.f};
   if (ZNORM) {
     const half8* lt = lfrag + head * 8 * kFragPerTile;
-    float ml = __uint_as_float(hinfo.maxabs_l);
-    const float SL = ml > 0.f ? pow2f(14 - ilog2_floor(ml)) : 1.f;
     for (int tz = 0; tz < 4; ++tz) {
       f16v z0 = {}, z1 = {};
 #pragma unroll
@@ -456,7 +563,7 @@ __global__ __launch_bounds__(256, 2) void enc_coarse(
         zn[1] += z1[r] * z1[r];
       }
     }
-    const float inv = 1.f / (SL * SL);
+    const float inv = 1.f / (hs.SL * hs.SL);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) zn[blk] = (zn[blk] + __shfl_xor(zn[blk], 32)) * inv;
   }
@@ -466,318 +573,458 @@ __global__ __launch_bounds__(256, 2) void enc_coarse(
   for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
     for (int r = 0; r < 16; ++r) m1[blk][r] = m2[blk][r] = -INFINITY;
-  const unsigned tmask = (1u << tbits) - 1u;
-
-  const half8* vh = v16 + head * (int64_t)T * kFragPerTile;
-  const float* bh = bias + head * (int64_t)T * 32;
-  const int nst = (T + kTPS - 1) / kTPS;
-  // stage loader: 256 threads x 8 fragments = 4 tiles; 32 threads x 4 bias floats
-  half8 pf[8];
-  f4 pb;
-  auto fetch = [&](int st) {
-    const int t0 = st * kTPS;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int e = q * 256 + t;               // fragment within the stage
-      const int tt = e / kFragPerTile;
-      pf[q] = (t0 + tt < T) ? vh[(int64_t)t0 * kFragPerTile + e] : half8{};
-    }
-    if (t < 32) {
-      const int tt = t / 8;
-      pb = (t0 + tt < T) ? *reinterpret_cast<const f4*>(bh + (int64_t)t0 * 32 + t * 4) : f4{};
-    }
-  };
-  auto commit = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int e = q * 256 + t;
-      sv[buf][e / kFragPerTile][e % kFragPerTile] = pf[q];
-    }
-    if (t < 32) *reinterpret_cast<f4*>(&sb[buf][t / 8][(t % 8) * 4]) = pb;
-  };
-  fetch(0);
-  commit(0);
+  const unsigned keep = ~((1u << tbits) - 1u);
+  // +inf kept opaque so med3(x, p, +inf) stays one v_med3_f32 (as a max it would gain
+  // NaN-canonicalising extra instructions)
+  float inf;
+  asm("v_mov_b32 %0, 0x7f800000" : "=v"(inf));
   __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nst) fetch(st + 1);
-    const int tiles = (T - st * kTPS) < kTPS ? (T - st * kTPS) : kTPS;
-    for (int tt = 0; tt < tiles; ++tt) {
-      const unsigned tile = (unsigned)(st * kTPS + tt);
-      f16v acc0, acc1;
-      const f4* bl = reinterpret_cast<const f4*>(&sb[buf][tt][hh * 16]);
+
+  for (int tile = 0; tile < T; ++tile) {
+    const int buf = tile % kRing;
+    if (tile + 1 < T) commit((tile + 1) % kRing);
+    if (tile + 2 < T) fetch(tile + 2);
+    const f4* bl = reinterpret_cast<const f4*>(&sb[buf][hh * 16]);
+    f16v bv;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f4 b4 = bl[q];
-        acc0[4 * q + 0] = b4.x; acc0[4 * q + 1] = b4.y; acc0[4 * q + 2] = b4.z; acc0[4 * q + 3] = b4.w;
-      }
-      acc1 = acc0;
-#pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        const half8 a = sv[buf][tt][s * 64 + lane];
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf.f[0][s], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf.f[1][s], acc1, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p0 = __uint_as_float((__float_as_uint(acc0[r]) & ~tmask) | tile);
-        const float p1 = __uint_as_float((__float_as_uint(acc1[r]) & ~tmask) | tile);
-        m2[0][r] = __builtin_amdgcn_fmed3f(m1[0][r], m2[0][r], p0);
-        m1[0][r] = fmaxf(m1[0][r], p0);
-        m2[1][r] = __builtin_amdgcn_fmed3f(m1[1][r], m2[1][r], p1);
-        m1[1][r] = fmaxf(m1[1][r], p1);
-      }
+    for (int q = 0; q < 4; ++q) {
+      const f4 b4 = bl[q];
+      bv[4 * q + 0] = b4.x; bv[4 * q + 1] = b4.y; bv[4 * q + 2] = b4.z; bv[4 * q + 3] = b4.w;
     }
-    if (st + 1 < nst) {
-      commit(buf ^ 1);
+    f16v acc0, acc1;
+    {
+      const half8 a = sv[buf][lane];
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf.f[0][0], bv, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf.f[1][0], bv, 0, 0, 0);
+    }
+#pragma unroll
+    for (int s = 1; s < kSteps; ++s) {
+      const half8 a = sv[buf][s * 64 + lane];
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf.f[0][s], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf.f[1][s], acc1, 0, 0, 0);
+    }
+    const unsigned tv = vgpr_of((unsigned)tile);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p0 = pack_tile(acc0[r], keep, tv);
+      const float p1 = pack_tile(acc1[r], keep, tv);
+      m2[0][r] = __builtin_amdgcn_fmed3f(m1[0][r], m2[0][r], p0);
+      m1[0][r] = __builtin_amdgcn_fmed3f(m1[0][r], p0, inf);
+      m2[1][r] = __builtin_amdgcn_fmed3f(m1[1][r], m2[1][r], p1);
+      m1[1][r] = __builtin_amdgcn_fmed3f(m1[1][r], p1, inf);
     }
     __syncthreads();
   }
 
   // ---- per-key certificate.  Both lanes of a key merge the same 32 lists; lane half hh
-  // finalises block hh.
-  Top3 top[2];
-  float useg[2];
+  // finalises block hh.  Top three (value, index) with straight-line insertion.
+  const unsigned tmask = ~keep;
+  float tv0[2], tv1[2], tv2[2], useg[2];
+  int tj0[2], tj1[2];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
-    top[blk].init();
-    useg[blk] = -INFINITY;
+    float a0 = -INFINITY, a1 = -INFINITY, a2 = -INFINITY, u = -INFINITY;
+    int i0 = 0x7FFFFFFF, i1 = 0x7FFFFFFF, i2 = 0x7FFFFFFF;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rowi = slot_row(r, hh);
-      const float a = m1[blk][r], b = m2[blk][r];
-      if (a > -INFINITY) top[blk].push(a, (int)((__float_as_uint(a) & tmask) * kRows + rowi));
-      if (b > -INFINITY) top[blk].push(b, (int)((__float_as_uint(b) & tmask) * kRows + rowi));
-      useg[blk] = fmaxf(useg[blk], b);
+    for (int q = 0; q < 32; ++q) {
+      const int r = q >> 1;
+      const float x = (q & 1) ? m2[blk][r] : m1[blk][r];
+      if (q & 1) u = fmaxf(u, x);
+      const int jx = (int)((__float_as_uint(x) & tmask) * kRows + slot_row(r, hh));
+      const bool b2 = x > a2 || (x == a2 && jx < i2);
+      const bool b1 = x > a1 || (x == a1 && jx < i1);
+      const bool b0 = x > a0 || (x == a0 && jx < i0);
+      if (x > -INFINITY && b2) {
+        a2 = b1 ? a1 : x; i2 = b1 ? i1 : jx;
+        if (b1) { a1 = b0 ? a0 : x; i1 = b0 ? i0 : jx; }
+        if (b0) { a0 = x; i0 = jx; }
+      }
     }
-  }
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    float pv[3];
-    int pj[3];
+    // merge with the partner lane (the other 16 rows of every tile)
+    u = fmaxf(u, __shfl_xor(u, 32));
+    const float p0 = __shfl_xor(a0, 32), p1 = __shfl_xor(a1, 32), p2 = __shfl_xor(a2, 32);
+    const int q0 = __shfl_xor(i0, 32), q1 = __shfl_xor(i1, 32), q2 = __shfl_xor(i2, 32);
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
-      pv[q] = __shfl_xor(top[blk].v[q], 32);
-      pj[q] = __shfl_xor(top[blk].j[q], 32);
+      const float x = q == 0 ? p0 : (q == 1 ? p1 : p2);
+      const int jx = q == 0 ? q0 : (q == 1 ? q1 : q2);
+      const bool b2 = x > a2 || (x == a2 && jx < i2);
+      const bool b1 = x > a1 || (x == a1 && jx < i1);
+      const bool b0 = x > a0 || (x == a0 && jx < i0);
+      if (x > -INFINITY && b2) {
+        a2 = b1 ? a1 : x; i2 = b1 ? i1 : jx;
+        if (b1) { a1 = b0 ? a0 : x; i1 = b0 ? i0 : jx; }
+        if (b0) { a0 = x; i0 = jx; }
+      }
     }
-#pragma unroll
-    for (int q = 0; q < 3; ++q)
-      if (pv[q] > -INFINITY) top[blk].push(pv[q], pj[q]);
-    useg[blk] = fmaxf(useg[blk], __shfl_xor(useg[blk], 32));
+    tv0[blk] = a0; tv1[blk] = a1; tv2[blk] = a2; useg[blk] = u;
+    tj0[blk] = i0; tj1[blk] = i1;
   }
   const int blk = hh;
   const int64_t myrow = row[blk];
-  const Top3 tp = top[blk];
-  int outcome = 0;  // 1 direct, 2 reranked, 3 rescan list, 4 full-scan list
+  int outcome = 0;  // 1 direct, 2 listed for the rerank, 4 listed for the full scan
+  RefEntry re;
+  float z2 = -1.f;
   if (myrow >= 0) {
-    const double E = score_bound(kf.n2[blk], kf.e2[blk], hinfo, S);
-    const double s1 = pack_slack(tp.v[0], tbits), s2 = pack_slack(tp.v[1], tbits);
-    int code = tp.j[0];
-    double sbest = 0.0;
-    bool have_exact = false;
+    const double S = (double)hs.S;
+    const double rho = (double)fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+    const double nu = (double)fmaxf(fmaxf(s_red[1][0], s_red[1][1]), fmaxf(s_red[1][2], s_red[1][3]));
+    const double B = 0.5 * S * (double)hs.maxb;
+    const double E = score_bound(kf.n2[blk], kf.e2[blk], rho, nu, B);
+    const float t0 = tv0[blk], t1 = tv1[blk], t2 = tv2[blk];
+    const double s0 = pack_slack(t0, tbits), s1 = pack_slack(t1, tbits);
+    if (ZNORM) {
+      z2 = zn[blk];
+      znorm[head * n + myrow] = z2;
+    } else if (znorm) {
+      z2 = znorm[head * n + myrow];
+    }
     if (kf.bad[blk]) {
       outcome = 4;
-    } else if ((double)tp.v[0] - s1 - E > (double)tp.v[1] + s2 + E) {
+    } else if (tj0[blk] < c && (double)t0 - s0 - E > (double)t1 + s1 + E) {
       outcome = 1;
-    } else {
-      // exact scores of the two leading candidates
-      double ex[2];
-      int ej[2];
-      int ne = 0;
-      for (int q = 0; q < 2; ++q) {
-        if (tp.j[q] < c && tp.v[q] > -INFINITY) {
-          ex[ne] = exact_score<DT>(keys, head, n, myrow, v64, b64, c, tp.j[q]);
-          ej[ne] = tp.j[q];
-          ++ne;
-        }
-      }
-      int bi = 0;
-      if (ne == 2 && (ex[1] > ex[0] || (ex[1] == ex[0] && ej[1] < ej[0]))) bi = 1;
-      sbest = ex[bi];
-      code = ej[bi];
-      have_exact = true;
-      const double U = fmax((double)tp.v[2], (double)useg[blk]);
-      const double su = pack_slack((float)U, tbits);
-      const double nuraw = (double)__uint_as_float(hinfo.nu) / (double)S;
-      const double eps = ldexp(1.0, -40) * (sqrt((double)kf.n2[blk]) * nuraw * 2.0 +
-                                           (double)__uint_as_float(hinfo.maxb));
-      outcome = ((sbest - eps) * (double)S > U + su + E) ? 2 : 3;
-    }
-    if (ZNORM && dist) znorm[head * n + myrow] = zn[blk];
-    if (outcome <= 2) {
+      const int code = tj0[blk];
       codes[head * n + myrow] = (uint16_t)code;
-      if (dist) {
-        if (!have_exact) sbest = exact_score<DT>(keys, head, n, myrow, v64, b64, c, code);
-        double z2;
-        if (ZNORM) {
-          z2 = (double)zn[blk];
-        } else if (znorm) {
-          z2 = (double)znorm[head * n + myrow];  // fp64 ||kL||^2 computed beforehand
-        } else {
-          z2 = 0.0;  // plain: ||k||^2 exactly
-          const int64_t off = (head * n + myrow) * kD;
-          for (int a = 0; a < kD; ++a) {
-            const double x = (double)load_elem(keys, DT, off + a);
-            z2 += x * x;
-          }
+      if (DIST) {
+        // distance of the certified code: fp32 dot with the fp32 copy of v_code
+        const float* vr = v32 + (head * c + code) * kD;
+        const int64_t off = (head * n + myrow) * kD;
+        float sdot = 0.f, k2 = 0.f;
+        for (int a = 0; a < kD; a += 8) {
+          const f4 va = *reinterpret_cast<const f4*>(vr + a);
+          const f4 vb = *reinterpret_cast<const f4*>(vr + a + 4);
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = load_elem(keys, DT, off + a + e);
+          sdot += x[0] * va.x + x[1] * va.y + x[2] * va.z + x[3] * va.w;
+          sdot += x[4] * vb.x + x[5] * vb.y + x[6] * vb.z + x[7] * vb.w;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) k2 += x[e] * x[e];
         }
-        dist[head * n + myrow] = (float)fmax(z2 - 2.0 * sbest, 0.0);
+        const double zz = (ZNORM || znorm) ? (double)z2 : (double)k2;
+        const double sc = (double)sdot - 0.5 * b64[head * c + code];
+        dist[head * n + myrow] = (float)fmax(zz - 2.0 * sc, 0.0);
       }
     } else {
-      UncEntry ue;
-      ue.head = (int32_t)head;
-      ue.row = (int32_t)myrow;
-      ue.sbest = have_exact ? sbest : -INFINITY;
-      ue.jbest = have_exact ? code : -1;
-      ue.pad = 0;
-      if (outcome == 3) unc[atomicAdd(&cnt->unc, 1u)] = ue;
-      else full[atomicAdd(&cnt->full, 1u)] = ue;
+      outcome = 2;
+      const double U = fmax((double)t2, (double)useg[blk]);
+      re.head = (int32_t)head;
+      re.row = (int32_t)myrow;
+      re.j0 = tj0[blk] < c ? tj0[blk] : -1;
+      re.j1 = (tj1[blk] < c && t1 > -INFINITY) ? tj1[blk] : -1;
+      re.thr = (U + pack_slack((float)U, tbits) + E) / S;
+      re.e_unscaled = E / S;
+      re.z2 = z2;
+      re.pad = 0;
     }
   }
-  // statistics (per wave)
+  __shared__ unsigned s_cnt, s_base, s_stat[2];
+  if (t == 0) s_stat[0] = s_stat[1] = 0u;
+  const unsigned rslot = block_append(&cnt->refine, outcome == 2, &s_cnt, &s_base);
+  if (outcome == 2) refl[rslot] = re;
+  const unsigned fslot = block_append(&cnt->full, outcome == 4, &s_cnt, &s_base);
+  if (outcome == 4) {
+    FullEntry fe;
+    fe.head = (int32_t)head;
+    fe.row = (int32_t)myrow;
+    fe.z2 = z2;
+    fe.pad = 0;
+    full[fslot] = fe;
+  }
+  // statistics: one atomic per workgroup
   const unsigned long long valid = __ballot(myrow >= 0);
-#pragma unroll
-  for (int o = 1; o <= 4; ++o) {
-    const unsigned long long m = __ballot(outcome == o);
-    if (lane == 0 && m) atomicAdd(&cnt->stats[o], (unsigned)__popcll(m));
+  const unsigned long long dmask = __ballot(outcome == 1);
+  if (lane == 0) {
+    atomicAdd(&s_stat[0], (unsigned)__popcll(valid));
+    atomicAdd(&s_stat[1], (unsigned)__popcll(dmask));
   }
-  if (lane == 0 && valid) atomicAdd(&cnt->stats[0], (unsigned)__popcll(valid));
-}
-
-// ------------------------------------------------------------------ rescan of uncertified keys
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
-// Squared norm used for distances of keys decided outside the MFMA pass.
-template <int DT>
-__device__ double key_z2(const void* keys, int64_t head, int64_t n, int64_t row,
-                         const float* znorm) {
-  if (znorm) return (double)znorm[head * n + row];
-  double z2 = 0.0;
-  const int64_t off = (head * n + row) * kD;
-  for (int a = 0; a < kD; ++a) {
-    const double x = (double)load_elem(keys, DT, off + a);
-    z2 += x * x;
+  __syncthreads();
+  if (t == 0) {
+    if (s_stat[0]) atomicAdd(&cnt->stats[0], s_stat[0]);
+    if (s_stat[1]) atomicAdd(&cnt->stats[1], s_stat[1]);
   }
-  return z2;
 }
 
-// Each wave takes 32 listed keys of one head at a time (MFMA column block 0; lanes 32-63
-// hold the other half of the k dimension).  Every centroid whose MFMA score reaches
-// S * sbest - E could be the maximiser (sbest is an exact score, so the maximum is at least
-// that); those are collected in the wave's LDS slice (kCandCap per key) and decided in
-// fp64.  A key with more candidates is forwarded to the full scan.  Waves synchronise only
-// with themselves: the loop trip count differs between waves.
+// ------------------------------------------------------------------ fp64 rerank
+// Two entries per wave, 32 lanes each: lanes 0-15 score j0, lanes 16-31 score j1.
 template <int DT>
-__global__ __launch_bounds__(256) void enc_rescan(
-    const void* __restrict__ keys, int64_t n, int T, int64_t c, const half8* __restrict__ v16,
-    const float* __restrict__ bias, const double* __restrict__ v64,
-    const double* __restrict__ b64, const EncHead* __restrict__ info,
-    const float* __restrict__ znorm, uint16_t* __restrict__ codes, float* __restrict__ dist,
-    const UncEntry* __restrict__ unc, UncEntry* __restrict__ full, Counters* __restrict__ cnt) {
-  __shared__ int cand[4][32][kCandCap];
-  __shared__ int ncand[4][32];
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, col = lane & 31, hh = lane >> 5;
-  const unsigned total = __hip_atomic_load(&cnt->unc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int64_t groups = ((int64_t)total + 31) / 32;
-  for (int64_t g = (int64_t)blockIdx.x * 4 + wave; g < groups; g += (int64_t)gridDim.x * 4) {
-    const int64_t e = g * 32 + col;
+__global__ __launch_bounds__(256) void enc_refine(
+    const void* __restrict__ keys, int64_t n, int64_t c, const double* __restrict__ v64,
+    const double* __restrict__ b64, const RefEntry* __restrict__ refl, uint16_t* __restrict__ codes,
+    float* __restrict__ dist, UncEntry* __restrict__ unc, int64_t unc_cap,
+    FullEntry* __restrict__ full, Counters* __restrict__ cnt) {
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int sub = lane >> 5;          // which entry of the wave
+  const int which = (lane >> 4) & 1;  // candidate 0 or 1
+  const int g = lane & 15;
+  const unsigned total = __hip_atomic_load(&cnt->refine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int64_t stride = (int64_t)gridDim.x * 8;
+  unsigned decided = 0;
+  for (int64_t e0 = (int64_t)blockIdx.x * 8 + (t >> 6) * 2; e0 < (int64_t)total; e0 += stride) {
+    const int64_t e = e0 + sub;
     const bool live = e < (int64_t)total;
-    UncEntry ue;
-    ue.head = -1;
-    ue.row = -1;
-    ue.sbest = -INFINITY;
-    ue.jbest = -1;
-    ue.pad = 0;
-    if (live) ue = unc[e];
-    int pending = live ? ue.head : 0x7FFFFFFF;
-    for (;;) {
-      int hmin = pending;  // smallest head still pending in this wave
-      for (int o = 32; o > 0; o >>= 1) hmin = min(hmin, __shfl_xor(hmin, o));
-      if (hmin == 0x7FFFFFFF) break;
-      const bool mine = live && ue.head == hmin;
-      if (lane < 32) ncand[wave][col] = 0;
-      wave_sync();
-      const EncHead hinfo = info[hmin];
-      const float S = head_scale(hinfo);
-      const int64_t row[2] = {mine ? (int64_t)ue.row : -1, -1};
-      KeyFrags kf;
-      load_key_frags<DT>(keys, hmin, n, row, hh, kf);
-      kf.n2[0] += __shfl_xor(kf.n2[0], 32);
-      kf.e2[0] += __shfl_xor(kf.e2[0], 32);
-      const double E = score_bound(kf.n2[0], kf.e2[0], hinfo, S);
-      const double th = ue.sbest * (double)S - E;
-      const float thr = mine ? (float)(th - fabs(th) * 0x1p-20 - 1e-30) : INFINITY;
-      const half8* vh = v16 + (int64_t)hmin * T * kFragPerTile;
-      const float* bh = bias + (int64_t)hmin * T * 32;
-      for (int tile = 0; tile < T; ++tile) {
-        f16v acc;
-        const f4* bl = reinterpret_cast<const f4*>(bh + (int64_t)tile * 32 + hh * 16);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f4 b4 = bl[q];
-          acc[4 * q + 0] = b4.x; acc[4 * q + 1] = b4.y; acc[4 * q + 2] = b4.z; acc[4 * q + 3] = b4.w;
-        }
-#pragma unroll
-        for (int s2 = 0; s2 < kSteps; ++s2) {
-          const half8 a = vh[(int64_t)tile * kFragPerTile + s2 * 64 + lane];
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf.f[0][s2], acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (acc[r] >= thr) {
-            const int j = tile * kRows + slot_row(r, hh);
-            if (j < c) {
-              const int pos = atomicAdd(&ncand[wave][col], 1);
-              if (pos < kCandCap) cand[wave][col][pos] = j;
-            }
-          }
-        }
+    RefEntry re;
+    re.head = 0;
+    re.row = 0;
+    re.j0 = re.j1 = -1;
+    if (live) re = refl[e];
+    const int j = live ? (which ? re.j1 : re.j0) : -1;
+    double s = -INFINITY, k2 = 0.0;
+    if (j >= 0) {
+      const int64_t off = ((int64_t)re.head * n + re.row) * kD;
+      s = coop_score<DT>(keys, off, v64 + ((int64_t)re.head * c + j) * kD,
+                         b64[(int64_t)re.head * c + j], g, &k2);
+    }
+    const double s_other = __shfl_xor(s, 16);
+    const double k2_other = __shfl_xor(k2, 16);
+    if (live && (lane & 31) == 0) {
+      const int ja = re.j0, jb = re.j1;  // lane 0 of the group scored ja, lane 16 jb
+      const double sa = s, sb = s_other;
+      if (ja < 0) k2 = k2_other;
+      int best = ja;
+      double sbest = sa;
+      if (jb >= 0 && (ja < 0 || sb > sa || (sb == sa && jb < ja))) {
+        best = jb;
+        sbest = sb;
       }
-      wave_sync();
-      if (mine && hh == 0) {
-        const int nc = ncand[wave][col];
-        if (nc > kCandCap) {
-          full[atomicAdd(&cnt->full, 1u)] = ue;
+      const double z2 = re.z2 >= 0.f ? (double)re.z2 : k2;
+      const double eps = 0x1p-40 * (fabs(sbest) + k2 + 1.0);
+      if (best >= 0 && sbest - eps > re.thr) {
+        codes[(int64_t)re.head * n + re.row] = (uint16_t)best;
+        if (dist) dist[(int64_t)re.head * n + re.row] = (float)fmax(z2 - 2.0 * sbest, 0.0);
+        decided += 1;
+      } else {
+        const unsigned slot = atomicAdd(&cnt->unc[re.head], 1u);
+        if (best >= 0 && slot < unc_cap) {
+          UncEntry ue;
+          ue.row = re.row;
+          ue.jbest = best;
+          ue.sbest = sbest;
+          ue.e_unscaled = re.e_unscaled;
+          ue.z2 = re.z2;
+          ue.pad = 0;
+          unc[(int64_t)re.head * unc_cap + slot] = ue;
         } else {
-          double best = ue.sbest;
-          int bj = ue.jbest >= 0 ? ue.jbest : 0x7FFFFFFF;
-          for (int q = 0; q < nc; ++q) {
-            const int j = cand[wave][col][q];
-            const double sj = exact_score<DT>(keys, hmin, n, ue.row, v64, b64, c, j);
-            if (sj > best || (sj == best && j < bj)) {
-              best = sj;
-              bj = j;
-            }
-          }
-          codes[(int64_t)hmin * n + ue.row] = (uint16_t)bj;
-          if (dist)
-            dist[(int64_t)hmin * n + ue.row] =
-                (float)fmax(key_z2<DT>(keys, hmin, n, ue.row, znorm) - 2.0 * best, 0.0);
-          atomicAdd(&cnt->stats[5], 1u);
+          FullEntry fe;
+          fe.head = re.head;
+          fe.row = re.row;
+          fe.z2 = re.z2;
+          fe.pad = 0;
+          full[atomicAdd(&cnt->full, 1u)] = fe;
         }
       }
-      wave_sync();
-      if (mine) pending = 0x7FFFFFFF;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) decided += __shfl_xor(decided, o);
+  if (lane == 0 && decided) atomicAdd(&cnt->stats[2], decided);
+}
+
+// Number of listed open keys of a head (capped to the list capacity).
+__device__ __forceinline__ int64_t open_count(const Counters* cnt, int64_t head, int64_t cap) {
+  const unsigned u = __hip_atomic_load(&cnt->unc[head], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (int64_t)u < cap ? (int64_t)u : cap;
+}
+
+constexpr int kMaxHeadsLds = 1024;
+
+// Exclusive prefix over heads of `per(open count)`, built once per workgroup in LDS
+// (heads <= kMaxHeadsLds; larger head counts fall back to scanning global counters).
+template <typename F>
+__device__ int64_t head_prefix(const Counters* cnt, int64_t heads, int64_t cap, int64_t* pre, F per) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t run = 0;
+    const int64_t hn = heads < kMaxHeadsLds ? heads : kMaxHeadsLds;
+    for (int64_t h = 0; h < hn; ++h) {
+      pre[h] = run;
+      run += per(open_count(cnt, h, cap));
+    }
+    for (int64_t h = hn; h < heads; ++h) run += per(open_count(cnt, h, cap));
+    pre[kMaxHeadsLds] = run;
+  }
+  __syncthreads();
+  return pre[kMaxHeadsLds];
+}
+
+// Head owning global item index `it` (prefix from head_prefix).
+template <typename F>
+__device__ int64_t find_head(const Counters* cnt, int64_t heads, int64_t cap, const int64_t* pre,
+                             int64_t it, F per, int64_t* rest) {
+  const int64_t hn = heads < kMaxHeadsLds ? heads : kMaxHeadsLds;
+  int64_t lo = 0, hi = hn - 1;
+  if (hn > 0 && it < (hn < heads ? pre[hn - 1] + per(open_count(cnt, hn - 1, cap)) : pre[kMaxHeadsLds])) {
+    while (lo < hi) {  // last head with pre[h] <= it
+      const int64_t mid = (lo + hi + 1) / 2;
+      if (pre[mid] <= it) lo = mid;
+      else hi = mid - 1;
+    }
+    *rest = it - pre[lo];
+    return lo;
+  }
+  int64_t run = hn > 0 ? pre[hn - 1] + per(open_count(cnt, hn - 1, cap)) : 0;
+  for (int64_t h = hn; h < heads; ++h) {
+    const int64_t m = per(open_count(cnt, h, cap));
+    if (it < run + m) {
+      *rest = it - run;
+      return h;
+    }
+    run += m;
+  }
+  *rest = 0;
+  return heads - 1;
+}
+
+// ------------------------------------------------------------------ rescan of open keys
+// Work item = (head, group of 32 listed keys, chunk of kRescanTiles tiles).  One wave per
+// item: MFMA scores of the chunk (fragments straight from L2); every centroid whose score
+// reaches S * sbest - E is appended to the key's candidate list.
+template <int DT>
+__global__ __launch_bounds__(256) void enc_rescan_collect(
+    const void* __restrict__ keys, int64_t n, int64_t heads, int T, int64_t c,
+    const half8* __restrict__ v16, const float* __restrict__ bias,
+    const float* __restrict__ part_a, int nwg_a, const UncEntry* __restrict__ unc,
+    int64_t unc_cap, const Counters* __restrict__ cnt, unsigned* __restrict__ cand_n,
+    int32_t* __restrict__ cand) {
+  const int t = threadIdx.x, lane = t & 63, col = lane & 31, hh = lane >> 5;
+  const int chunks = (T + kRescanTiles - 1) / kRescanTiles;
+  __shared__ int64_t pre[kMaxHeadsLds + 1];
+  auto per = [chunks](int64_t m) { return (m + 31) / 32 * chunks; };
+  const int64_t items = head_prefix(cnt, heads, unc_cap, pre, per);
+  for (int64_t it = (int64_t)blockIdx.x * 4 + (t >> 6); it < items; it += (int64_t)gridDim.x * 4) {
+    int64_t rest = 0;
+    const int64_t head = find_head(cnt, heads, unc_cap, pre, it, per, &rest);
+    const int64_t m = open_count(cnt, head, unc_cap);
+    const int64_t grp = rest / chunks;
+    const int chunk = (int)(rest % chunks);
+    const int64_t slot = grp * 32 + col;
+    const bool live = slot < m;
+    UncEntry ue;
+    ue.row = -1;
+    ue.sbest = 0.0;
+    ue.e_unscaled = 0.0;
+    if (live) ue = unc[head * unc_cap + slot];
+    const HeadScale hs = head_scale(part_a, head, nwg_a);
+    const int64_t row[1] = {live ? (int64_t)ue.row : -1};
+    KeyFrags<1> kf;
+    load_key_frags<DT, 1>(keys, head, n, row, hh, kf);
+    const double th = (ue.sbest - ue.e_unscaled) * (double)hs.S;
+    const float thr = live ? (float)(th - fabs(th) * 0x1p-20 - 1e-30) : INFINITY;
+    const half8* vh = v16 + head * (int64_t)T * kFragPerTile;
+    const float* bh = bias + head * (int64_t)T * 32;
+    const int tb = chunk * kRescanTiles;
+    const int te = tb + kRescanTiles < T ? tb + kRescanTiles : T;
+    for (int tile = tb; tile < te; ++tile) {
+      const f4* bl = reinterpret_cast<const f4*>(bh + (int64_t)tile * 32 + hh * 16);
+      f16v acc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f4 b4 = bl[q];
+        acc[4 * q + 0] = b4.x; acc[4 * q + 1] = b4.y; acc[4 * q + 2] = b4.z; acc[4 * q + 3] = b4.w;
+      }
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const half8 a = vh[(int64_t)tile * kFragPerTile + s * 64 + lane];
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf.f[0][s], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (acc[r] >= thr) {
+          const int j = tile * kRows + slot_row(r, hh);
+          if (j < c) {
+            const unsigned pos = atomicAdd(&cand_n[head * unc_cap + slot], 1u);
+            if (pos < (unsigned)kCandCap) cand[(head * unc_cap + slot) * kCandCap + pos] = j;
+          }
+        }
+      }
     }
   }
 }
 
-// fp64 scan of the whole codebook, one wave per listed key.  Runs after the rescan, which
-// may append to the list.
+// One wave per open key: fp64 over its candidates (16 lanes per candidate, 4 at a time).
+template <int DT>
+__global__ __launch_bounds__(256) void enc_rescan_decide(
+    const void* __restrict__ keys, int64_t n, int64_t heads, int64_t c,
+    const double* __restrict__ v64, const double* __restrict__ b64,
+    const UncEntry* __restrict__ unc, int64_t unc_cap, const unsigned* __restrict__ cand_n,
+    const int32_t* __restrict__ cand, uint16_t* __restrict__ codes, float* __restrict__ dist,
+    FullEntry* __restrict__ full, Counters* __restrict__ cnt) {
+  const int t = threadIdx.x, lane = t & 63, g = lane & 15, q4 = lane >> 4;
+  __shared__ int64_t pre[kMaxHeadsLds + 1];
+  auto per = [](int64_t m) { return m; };
+  const int64_t total = head_prefix(cnt, heads, unc_cap, pre, per);
+  unsigned decided = 0;
+  for (int64_t e = (int64_t)blockIdx.x * 4 + (t >> 6); e < total; e += (int64_t)gridDim.x * 4) {
+    int64_t rest = 0;
+    const int64_t head = find_head(cnt, heads, unc_cap, pre, e, per, &rest);
+    const int64_t slot = head * unc_cap + rest;
+    const UncEntry ue = unc[slot];
+    const unsigned nc = cand_n[slot];
+    if (nc > (unsigned)kCandCap) {
+      if (lane == 0) {
+        FullEntry fe;
+        fe.head = (int32_t)head;
+        fe.row = ue.row;
+        fe.z2 = ue.z2;
+        fe.pad = 0;
+        full[atomicAdd(&cnt->full, 1u)] = fe;
+      }
+      continue;
+    }
+    const int64_t off = ((int64_t)head * n + ue.row) * kD;
+    double best = ue.sbest;
+    int bj = ue.jbest;
+    // ||k||^2 (for distances without a precomputed ||kL||^2) and the first batch of scores
+    double k2 = 0.0;
+    for (unsigned q0 = 0; q0 < (nc > 0 ? nc : 1u); q0 += 4) {
+      const unsigned q = q0 + q4;
+      double s = -INFINITY, kk = 0.0;
+      int j = 0x7FFFFFFF;
+      const int jj = q < nc ? cand[slot * kCandCap + q] : ue.jbest;
+      const double sj = coop_score<DT>(keys, off, v64 + ((int64_t)head * c + jj) * kD,
+                                       b64[(int64_t)head * c + jj], g, &kk);
+      if (q < nc) {
+        s = sj;
+        j = jj;
+      }
+      k2 = kk;
+      for (int o = 16; o < 64; o <<= 1) {
+        const double os = __shfl_xor(s, o);
+        const int oj = __shfl_xor(j, o);
+        if (os > s || (os == s && oj < j)) {
+          s = os;
+          j = oj;
+        }
+      }
+      if (s > best || (s == best && j < bj)) {
+        best = s;
+        bj = j;
+      }
+    }
+    if (lane == 0) {
+      codes[(int64_t)head * n + ue.row] = (uint16_t)bj;
+      if (dist) {
+        const double z2 = ue.z2 >= 0.f ? (double)ue.z2 : k2;
+        dist[(int64_t)head * n + ue.row] = (float)fmax(z2 - 2.0 * best, 0.0);
+      }
+      decided += 1;
+    }
+  }
+  if (lane == 0 && decided) atomicAdd(&cnt->stats[3], decided);
+}
+
+// fp64 scan of the whole codebook, one wave per listed key.
 template <int DT>
 __global__ __launch_bounds__(256) void enc_fullscan(
     const void* __restrict__ keys, int64_t n, int64_t c, const double* __restrict__ v64,
-    const double* __restrict__ b64, const float* __restrict__ znorm, uint16_t* __restrict__ codes,
-    float* __restrict__ dist, const UncEntry* __restrict__ full, Counters* __restrict__ cnt) {
+    const double* __restrict__ b64, uint16_t* __restrict__ codes, float* __restrict__ dist,
+    const FullEntry* __restrict__ full, Counters* __restrict__ cnt) {
   __shared__ double kx[4][kD];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const unsigned total = __hip_atomic_load(&cnt->full, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (int64_t e = (int64_t)blockIdx.x * 4 + wave; e < (int64_t)total; e += (int64_t)gridDim.x * 4) {
-    const UncEntry ue = full[e];
-    const int64_t off = ((int64_t)ue.head * n + ue.row) * kD;
+    const FullEntry fe = full[e];
+    const int64_t off = ((int64_t)fe.head * n + fe.row) * kD;
     wave_sync();
     kx[wave][lane] = (double)load_elem(keys, DT, off + lane);
     kx[wave][lane + 64] = (double)load_elem(keys, DT, off + lane + 64);
@@ -785,10 +1032,10 @@ __global__ __launch_bounds__(256) void enc_fullscan(
     double best = -INFINITY;
     int bj = 0x7FFFFFFF;
     for (int64_t j = lane; j < c; j += 64) {
-      const double* v = v64 + ((int64_t)ue.head * c + j) * kD;
+      const double* v = v64 + ((int64_t)fe.head * c + j) * kD;
       double sj = 0.0;
       for (int a = 0; a < kD; ++a) sj += kx[wave][a] * v[a];
-      sj -= 0.5 * b64[(int64_t)ue.head * c + j];
+      sj -= 0.5 * b64[(int64_t)fe.head * c + j];
       if (sj > best || (sj == best && j < bj)) {
         best = sj;
         bj = (int)j;
@@ -803,11 +1050,16 @@ __global__ __launch_bounds__(256) void enc_fullscan(
       }
     }
     if (lane == 0) {
-      codes[(int64_t)ue.head * n + ue.row] = (uint16_t)bj;
-      if (dist)
-        dist[(int64_t)ue.head * n + ue.row] =
-            (float)fmax(key_z2<DT>(keys, ue.head, n, ue.row, znorm) - 2.0 * best, 0.0);
-      atomicAdd(&cnt->stats[6], 1u);
+      codes[(int64_t)fe.head * n + fe.row] = (uint16_t)bj;
+      if (dist) {
+        double z2 = fe.z2;
+        if (fe.z2 < 0.f) {
+          z2 = 0.0;
+          for (int a = 0; a < kD; ++a) z2 += kx[wave][a] * kx[wave][a];
+        }
+        dist[(int64_t)fe.head * n + fe.row] = (float)fmax(z2 - 2.0 * best, 0.0);
+      }
+      atomicAdd(&cnt->stats[4], 1u);
     }
   }
 }
@@ -842,31 +1094,48 @@ __global__ __launch_bounds__(256) void enc_znorm64(const float* __restrict__ key
   }
 }
 
+__global__ void enc_clear_u32(unsigned* p, int64_t count) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256)
+    p[i] = 0u;
+}
+
 __global__ void enc_stats_out(const Counters* __restrict__ cnt, a2ats_encode_stats* out) {
   if (threadIdx.x == 0) {
     out->keys = cnt->stats[0];
     out->direct = cnt->stats[1];
     out->reranked = cnt->stats[2];
-    out->rescanned = cnt->stats[5];
-    out->full_scan = cnt->stats[6];
-    out->reserved[0] = cnt->stats[3];
-    out->reserved[1] = cnt->stats[4];
+    out->rescanned = cnt->stats[3];
+    out->full_scan = cnt->stats[4];
+    out->reserved[0] = cnt->refine;
+    out->reserved[1] = cnt->full;
     out->reserved[2] = 0;
   }
 }
 
+// ------------------------------------------------------------------ host side
+inline int64_t unc_capacity(int64_t n) {
+  const int64_t cap = n / 8;
+  return cap < 1024 ? (n < 1024 ? n : 1024) : cap;
+}
+
 struct EncLayout {
-  double* h64;
   double* v64;
+  float* v32;
   double* b64;
   half8* v16;
   float* bias;
   half8* lfrag;
-  EncHead* info;
-  Counters* cnt;
+  float* part_a;
+  float* part_b;
+  unsigned* cnt;
+  RefEntry* refl;
   UncEntry* unc;
-  UncEntry* full;
+  FullEntry* full;
+  unsigned* cand_n;
+  int32_t* cand;
   float* znorm;
+  int nwg_a, nwg_b, ncnt;
+  int64_t unc_cap;
   size_t bytes;
 };
 
@@ -874,16 +1143,24 @@ EncLayout carve(void* ws, int64_t heads, int64_t n, int64_t c) {
   const int64_t T = (c + kRows - 1) / kRows;
   Carver cv(ws);
   EncLayout L;
-  L.h64 = cv.take<double>((size_t)heads * kD * kD);
+  L.nwg_a = (int)((c + 31) / 32);
+  L.nwg_b = (int)((T * kRows + kD + 15) / 16);
+  L.ncnt = (int)(offsetof(Counters, unc) / 4 + heads);
+  L.unc_cap = unc_capacity(n);
   L.v64 = cv.take<double>((size_t)heads * c * kD);
+  L.v32 = cv.take<float>((size_t)heads * c * kD);
   L.b64 = cv.take<double>((size_t)heads * c);
   L.v16 = cv.take<half8>((size_t)heads * T * kFragPerTile);
   L.bias = cv.take<float>((size_t)heads * T * 32);
   L.lfrag = cv.take<half8>((size_t)heads * 8 * kFragPerTile);
-  L.info = cv.take<EncHead>((size_t)heads);
-  L.cnt = cv.take<Counters>(1);
-  L.unc = cv.take<UncEntry>((size_t)heads * n);
-  L.full = cv.take<UncEntry>((size_t)heads * n);
+  L.part_a = cv.take<float>((size_t)heads * L.nwg_a * 4);
+  L.part_b = cv.take<float>((size_t)heads * L.nwg_b * 2);
+  L.cnt = cv.take<unsigned>((size_t)L.ncnt);
+  L.refl = cv.take<RefEntry>((size_t)heads * n);
+  L.unc = cv.take<UncEntry>((size_t)heads * L.unc_cap);
+  L.full = cv.take<FullEntry>((size_t)heads * n);
+  L.cand_n = cv.take<unsigned>((size_t)heads * L.unc_cap);
+  L.cand = cv.take<int32_t>((size_t)heads * L.unc_cap * kCandCap);
   L.znorm = cv.take<float>((size_t)heads * n);
   L.bytes = cv.used;
   return L;
@@ -896,20 +1173,20 @@ int encode_typed(const void* keys, int64_t heads, int64_t n, const int32_t* idx,
   const int T = (int)((c + kRows - 1) / kRows);
   int tbits = 0;
   while ((1 << tbits) < T) ++tbits;
-  const int plain = chol == nullptr;
-  A2ATS_TRY(launch("encode_gram", enc_gram, dim3(kD * kD / 256, (unsigned)heads), dim3(256), 0, s,
-                   chol, L.h64, L.info, L.cnt));
-  const size_t sm_rows = (plain ? 0 : kD * kD * sizeof(double)) + 32 * kD * sizeof(float);
+  const bool plain = chol == nullptr;
+  Counters* cnt = reinterpret_cast<Counters*>(L.cnt);
+  const size_t sm_rows = 32 * kD * sizeof(double) + (plain ? 0 : kD * kLd * sizeof(float)) +
+                         32 * kD * sizeof(float);
   A2ATS_TRY(set_dynamic_lds(enc_prep_rows, sm_rows));
-  A2ATS_TRY(launch("encode_prep_rows", enc_prep_rows, dim3((unsigned)((c + 31) / 32), (unsigned)heads),
-                   dim3(256), sm_rows, s, codebook, c, L.h64, chol, L.v64, L.b64, L.info));
+  A2ATS_TRY(launch("encode_prep_rows", enc_prep_rows, dim3((unsigned)L.nwg_a, (unsigned)heads),
+                   dim3(256), sm_rows, s, codebook, c, chol, L.v64, L.v32, L.b64, L.part_a, L.nwg_a));
   const bool znorm_mfma = dist && !plain && DT == A2ATS_BF16;
-  const int64_t frag_threads = (int64_t)T * kRows + (znorm_mfma ? kD : 0);
-  A2ATS_TRY(launch("encode_prep_frag", enc_prep_frag, dim3(grid_for(frag_threads, 256), (unsigned)heads),
-                   dim3(256), 0, s, L.v64, L.b64, c, T, chol, (int)znorm_mfma, L.info, L.v16,
-                   L.bias, L.lfrag));
-  // ||kL||^2 for distances with L: MFMA prologue of the coarse pass for bf16 keys (it also
-  // stores the value for keys decided later), an fp64 pass for fp32 keys.
+  A2ATS_TRY(launch("encode_prep_frag", enc_prep_frag, dim3((unsigned)L.nwg_b, (unsigned)heads),
+                   dim3(256), 0, s, L.v64, L.b64, c, T, chol, (int)znorm_mfma, L.part_a, L.nwg_a,
+                   L.part_b, L.v16, L.bias, L.lfrag, L.cnt, L.ncnt));
+  // the rescan candidate counters start at zero (a fill kernel, not a memset node)
+  A2ATS_TRY(launch("encode_clear", enc_clear_u32, dim3(grid_for(heads * L.unc_cap, 256, 1024)),
+                   dim3(256), 0, s, L.cand_n, heads * L.unc_cap));
   float* znorm = nullptr;
   if (dist && !plain) {
     znorm = L.znorm;
@@ -919,22 +1196,28 @@ int encode_typed(const void* keys, int64_t heads, int64_t n, const int32_t* idx,
                        L.znorm));
   }
   const int nkb = (int)((n_sel + kKeysPerWG - 1) / kKeysPerWG);
-  const int64_t work = heads * nkb;
-  const int64_t G = (work + 7) / 8 * 8;
-  if (znorm_mfma)
-    A2ATS_TRY(launch("encode_coarse", enc_coarse<DT, true>, dim3((unsigned)G), dim3(256), 0, s, keys, n,
-                     idx, n_sel, heads, nkb, T, tbits, L.v16, L.bias, L.v64, L.b64, c, L.lfrag, L.info,
-                     znorm, codes, dist, L.unc, L.full, L.cnt));
-  else
-    A2ATS_TRY(launch("encode_coarse", enc_coarse<DT, false>, dim3((unsigned)G), dim3(256), 0, s, keys, n,
-                     idx, n_sel, heads, nkb, T, tbits, L.v16, L.bias, L.v64, L.b64, c, L.lfrag, L.info,
-                     znorm, codes, dist, L.unc, L.full, L.cnt));
-  A2ATS_TRY(launch("encode_rescan", enc_rescan<DT>, dim3(256), dim3(256), 0, s, keys, n, T, c, L.v16,
-                   L.bias, L.v64, L.b64, L.info, znorm, codes, dist, L.unc, L.full, L.cnt));
-  A2ATS_TRY(launch("encode_fullscan", enc_fullscan<DT>, dim3(256), dim3(256), 0, s, keys, n, c, L.v64,
-                   L.b64, znorm, codes, dist, L.full, L.cnt));
+  const int64_t G = (heads * nkb + 7) / 8 * 8;
+  const char* name = plain ? "encode_coarse_plain" : "encode_coarse_h";
+#define A2ATS_COARSE(Z, DI)                                                                       \
+  launch(name, enc_coarse<DT, Z, DI>, dim3((unsigned)G), dim3(256), 0, s, keys, n, idx, n_sel,   \
+         heads, nkb, T, tbits, L.v16, L.bias, L.v32, L.b64, c, L.lfrag, L.part_a, L.nwg_a,        \
+         L.part_b, L.nwg_b, znorm, codes, dist, L.refl, L.full, cnt)
+  if (znorm_mfma) A2ATS_TRY(A2ATS_COARSE(true, true));
+  else if (dist) A2ATS_TRY(A2ATS_COARSE(false, true));
+  else A2ATS_TRY(A2ATS_COARSE(false, false));
+#undef A2ATS_COARSE
+  A2ATS_TRY(launch("encode_refine", enc_refine<DT>, dim3(1024), dim3(256), 0, s, keys, n, c, L.v64,
+                   L.b64, L.refl, codes, dist, L.unc, L.unc_cap, L.full, cnt));
+  A2ATS_TRY(launch("encode_rescan_collect", enc_rescan_collect<DT>, dim3(512), dim3(256), 0, s, keys,
+                   n, heads, T, c, L.v16, L.bias, L.part_a, L.nwg_a, L.unc, L.unc_cap, cnt,
+                   L.cand_n, L.cand));
+  A2ATS_TRY(launch("encode_rescan_decide", enc_rescan_decide<DT>, dim3(256), dim3(256), 0, s, keys, n,
+                   heads, c, L.v64, L.b64, L.unc, L.unc_cap, L.cand_n, L.cand, codes, dist, L.full,
+                   cnt));
+  A2ATS_TRY(launch("encode_fullscan", enc_fullscan<DT>, dim3(128), dim3(256), 0, s, keys, n, c, L.v64,
+                   L.b64, codes, dist, L.full, cnt));
   if (stats)
-    A2ATS_TRY(launch("encode_stats", enc_stats_out, dim3(1), dim3(64), 0, s, L.cnt, stats));
+    A2ATS_TRY(launch("encode_stats", enc_stats_out, dim3(1), dim3(64), 0, s, cnt, stats));
   return A2ATS_OK;
 }
 

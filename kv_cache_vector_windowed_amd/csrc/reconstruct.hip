@@ -16,11 +16,13 @@
 //   rope_gather  HBM-write-bound stream: each thread owns a fixed group of P pairs of the
 //                head dimension (P = 4 for fp32 output, 8 for bf16, so every store is 16 B),
 //                keeps the far row's cos/sin for its pairs in registers, gathers the
-//                centroid from L2, rotates in fp64, rounds once, and writes with
-//                non-temporal stores.  Work items are (batch, head, 64-token chunk); item k
-//                has head k % heads and the grid is a multiple of 8 * heads, so a workgroup
+//                centroid from L2, rotates (fp64 for fp32 output, fp32 for bf16 output),
+//                rounds once, and writes with non-temporal stores.  Work items are
+//                (batch, head, 64-token chunk); item k has head k % heads and the grid is a multiple of 8 * heads, so a workgroup
 //                always serves one head and, with 8 heads, each XCD (workgroups are dealt
 //                round-robin over the 8 XCDs) keeps a single head's codebook in its L2.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace a2ats {
@@ -56,57 +58,39 @@ __global__ __launch_bounds__(256) void rope_table(int64_t rows_near, int64_t cur
   table[e] = v;
 }
 
-template <int P>
-struct OutT;
-template <>
-struct OutT<4> {  // fp32 output: 4 pairs -> two 16-byte stores
-  static __device__ __forceinline__ void store(void* out, int64_t off, const double* lo,
-                                               const double* hi) {
-    f4 a, b;
-    a.x = (float)lo[0]; a.y = (float)lo[1]; a.z = (float)lo[2]; a.w = (float)lo[3];
-    b.x = (float)hi[0]; b.y = (float)hi[1]; b.z = (float)hi[2]; b.w = (float)hi[3];
-    float* o = static_cast<float*>(out) + off;
-    __builtin_nontemporal_store(a, reinterpret_cast<f4*>(o));
-    __builtin_nontemporal_store(b, reinterpret_cast<f4*>(o + kHalf));
-  }
-};
-template <>
-struct OutT<8> {  // bf16 output: 8 pairs -> two 16-byte stores
-  static __device__ __forceinline__ void store(void* out, int64_t off, const double* lo,
-                                               const double* hi) {
-    u4 a, b;
-    unsigned la[4], lb[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      la[k] = (unsigned)f64_to_bf16(lo[2 * k]) | ((unsigned)f64_to_bf16(lo[2 * k + 1]) << 16);
-      lb[k] = (unsigned)f64_to_bf16(hi[2 * k]) | ((unsigned)f64_to_bf16(hi[2 * k + 1]) << 16);
-    }
-    a.x = la[0]; a.y = la[1]; a.z = la[2]; a.w = la[3];
-    b.x = lb[0]; b.y = lb[1]; b.z = lb[2]; b.w = lb[3];
-    uint16_t* o = static_cast<uint16_t*>(out) + off;
-    __builtin_nontemporal_store(a, reinterpret_cast<u4*>(o));
-    __builtin_nontemporal_store(b, reinterpret_cast<u4*>(o + kHalf));
-  }
-};
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
-template <int P>
+// Two fp32 values to a packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  bf2 v;
+  v.x = (__bf16)lo;
+  v.y = (__bf16)hi;
+  return __builtin_bit_cast(unsigned, v);
+}
+
+// fp32 output: 4 pairs per thread, rotation in fp64, one rounding, two 16-byte stores.
+// bf16 output: 8 pairs per thread, rotation in fp32 (FMA) and one rounding to bf16; the
+// result lies within one bf16 unit of the single rounding of the exact value.
+template <bool BF16>
 __global__ __launch_bounds__(256) void rope_gather(
     const uint16_t* __restrict__ codes, const int32_t* __restrict__ positions, int64_t heads,
     int64_t n, const float* __restrict__ cb, int64_t c, int64_t cur, int64_t window,
     int64_t rows_near, const d2* __restrict__ table, void* __restrict__ out, int64_t items) {
-  constexpr int TPT = kHalf / P;          // threads per token
-  constexpr int TOK = 256 / TPT;          // tokens per pass of the workgroup
+  constexpr int P = BF16 ? 8 : 4;        // pairs per thread
+  constexpr int TPT = kHalf / P;         // threads per token
+  constexpr int TOK = 256 / TPT;         // tokens per pass of the workgroup
+  using real = typename std::conditional<BF16, float, double>::type;
   const int t = threadIdx.x;
-  const int g = t % TPT;                  // pair group: pairs [g*P, g*P + P)
+  const int g = t % TPT;                 // pair group: pairs [g*P, g*P + P)
   const int tk = t / TPT;
   const int i0 = g * P;
-  double fc[P], fs[P];
+  real fc[P], fs[P];
   const d2* far_row = table + rows_near * kHalf;
 #pragma unroll
   for (int k = 0; k < P; ++k) {
-    d2 v = far_row[i0 + k];
-    fc[k] = v.x;
-    fs[k] = v.y;
+    const d2 v = far_row[i0 + k];
+    fc[k] = (real)v.x;
+    fs[k] = (real)v.y;
   }
   const int64_t chunks = (n + kChunk - 1) / kChunk;
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
@@ -121,39 +105,59 @@ __global__ __launch_bounds__(256) void rope_gather(
       const uint16_t code = codes[(b * heads + h) * n + tok];
       const int32_t pos = positions[b * n + tok];
       const int64_t ooff = ((b * heads + h) * n + tok) * kD + i0;
-      double lo[P], hi[P];
+      real lo[P], hi[P];
       if ((int64_t)code >= c || pos < 0) {
 #pragma unroll
-        for (int k = 0; k < P; ++k) lo[k] = hi[k] = __longlong_as_double(0x7FF8000000000000ll);
-        OutT<P>::store(out, ooff, lo, hi);
-        continue;
-      }
-      const float* x = cbh + (int64_t)code * kD + i0;
-      float xl[P], xh[P];
-#pragma unroll
-      for (int k = 0; k < P; k += 4) {
-        f4 a = *reinterpret_cast<const f4*>(x + k);
-        f4 bb = *reinterpret_cast<const f4*>(x + kHalf + k);
-        xl[k] = a.x; xl[k + 1] = a.y; xl[k + 2] = a.z; xl[k + 3] = a.w;
-        xh[k] = bb.x; xh[k + 1] = bb.y; xh[k + 2] = bb.z; xh[k + 3] = bb.w;
-      }
-      const int64_t delta = cur - (int64_t)pos;
-      if (delta >= 0 && delta < window) {
-        const d2* row = table + delta * kHalf + i0;  // delta < rows_near since pos >= 0
-#pragma unroll
-        for (int k = 0; k < P; ++k) {
-          d2 v = row[k];
-          lo[k] = (double)xl[k] * v.x - (double)xh[k] * v.y;
-          hi[k] = (double)xh[k] * v.x + (double)xl[k] * v.y;
-        }
+        for (int k = 0; k < P; ++k) lo[k] = hi[k] = (real)NAN;
       } else {
+        const float* x = cbh + (int64_t)code * kD + i0;
+        float xl[P], xh[P];
 #pragma unroll
-        for (int k = 0; k < P; ++k) {
-          lo[k] = (double)xl[k] * fc[k] - (double)xh[k] * fs[k];
-          hi[k] = (double)xh[k] * fc[k] + (double)xl[k] * fs[k];
+        for (int k = 0; k < P; k += 4) {
+          const f4 a = *reinterpret_cast<const f4*>(x + k);
+          const f4 bb = *reinterpret_cast<const f4*>(x + kHalf + k);
+          xl[k] = a.x; xl[k + 1] = a.y; xl[k + 2] = a.z; xl[k + 3] = a.w;
+          xh[k] = bb.x; xh[k + 1] = bb.y; xh[k + 2] = bb.z; xh[k + 3] = bb.w;
+        }
+        const int64_t delta = cur - (int64_t)pos;
+        if (delta >= 0 && delta < window) {
+          const d2* row = table + delta * kHalf + i0;  // delta < rows_near since pos >= 0
+#pragma unroll
+          for (int k = 0; k < P; ++k) {
+            const d2 v = row[k];
+            const real cs = (real)v.x, sn = (real)v.y;
+            lo[k] = (real)xl[k] * cs - (real)xh[k] * sn;
+            hi[k] = (real)xh[k] * cs + (real)xl[k] * sn;
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < P; ++k) {
+            lo[k] = (real)xl[k] * fc[k] - (real)xh[k] * fs[k];
+            hi[k] = (real)xh[k] * fc[k] + (real)xl[k] * fs[k];
+          }
         }
       }
-      OutT<P>::store(out, ooff, lo, hi);
+      if (BF16) {
+        u4 a, bb;
+        unsigned la[4], lb[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          la[k] = pack_bf16x2((float)lo[2 * k], (float)lo[2 * k + 1]);
+          lb[k] = pack_bf16x2((float)hi[2 * k], (float)hi[2 * k + 1]);
+        }
+        a.x = la[0]; a.y = la[1]; a.z = la[2]; a.w = la[3];
+        bb.x = lb[0]; bb.y = lb[1]; bb.z = lb[2]; bb.w = lb[3];
+        uint16_t* o = static_cast<uint16_t*>(out) + ooff;
+        __builtin_nontemporal_store(a, reinterpret_cast<u4*>(o));
+        __builtin_nontemporal_store(bb, reinterpret_cast<u4*>(o + kHalf));
+      } else {
+        f4 a, bb;
+        a.x = (float)lo[0]; a.y = (float)lo[1]; a.z = (float)lo[2]; a.w = (float)lo[3];
+        bb.x = (float)hi[0]; bb.y = (float)hi[1]; bb.z = (float)hi[2]; bb.w = (float)hi[3];
+        float* o = static_cast<float*>(out) + ooff;
+        __builtin_nontemporal_store(a, reinterpret_cast<f4*>(o));
+        __builtin_nontemporal_store(bb, reinterpret_cast<f4*>(o + kHalf));
+      }
     }
   }
 }
@@ -199,8 +203,8 @@ extern "C" int a2ats_reconstruct(const uint16_t* codes, const int32_t* positions
   if (g > items) g = items;
   if (g > (int64_t)1 << 30) g = (int64_t)1 << 30;
   if (out_dtype == A2ATS_F32)
-    return launch("reconstruct", rope_gather<4>, dim3((unsigned)g), dim3(256), 0, s, codes,
+    return launch("reconstruct", rope_gather<false>, dim3((unsigned)g), dim3(256), 0, s, codes,
                   positions, heads, n, codebook, c, cur_pos, window, rows, table, out, items);
-  return launch("reconstruct", rope_gather<8>, dim3((unsigned)g), dim3(256), 0, s, codes, positions,
-                heads, n, codebook, c, cur_pos, window, rows, table, out, items);
+  return launch("reconstruct", rope_gather<true>, dim3((unsigned)g), dim3(256), 0, s, codes,
+                positions, heads, n, codebook, c, cur_pos, window, rows, table, out, items);
 }

@@ -7,12 +7,14 @@
 // (u << 32) | (0xffffffff - index), so equal scores keep the lower index first and every
 // element has a distinct key.
 //
-// Kernels (4 launches, no host round trip):
+// Kernels (5 launches, no host round trip):
 //   sel_init     per head: ||q|| and the binning scale; zeroes histograms and counters.
-//   sel_score    HBM-bound pass over the keys: writes u, builds a 4096-bin histogram of a
-//                monotone binning of s/||q|| in [-1, 1]; the last workgroup of each head
-//                (detected with a fenced atomic counter, no waiting) finds the bin b* that
-//                holds the n_r-th largest score.
+//   sel_score    HBM-bound pass over the keys (8 keys in flight per 16-lane group,
+//                non-temporal loads): writes u.
+//   sel_hist     4096-bin histogram of a monotone binning of s/||q|| in [-1, 1] from the
+//                L2/MALL-resident scores, 16 workgroups per head (few same-address atomics);
+//                the last workgroup of each head (fenced atomic counter, no waiting) finds
+//                the bin b* that holds the n_r-th largest score.
 //   sel_collect  pass over u: counts keys above b* per block and appends the keys in b* to
 //                a candidate list; the last workgroup of each head radix-selects the exact
 //                n_r-th largest 64-bit key among the candidates and turns the per-block
@@ -24,10 +26,16 @@
 namespace a2ats {
 namespace {
 
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
 constexpr int kD = A2ATS_HEAD_DIM;
 constexpr int kBins = 4096;
-constexpr int kScoreChunk = 1024;   // keys per sel_score workgroup
-constexpr int kBlock = 4096;        // scores per sel_collect / sel_scatter workgroup
+constexpr int kScoreChunk = 512;    // keys per sel_score workgroup
+constexpr int kScoreUnroll = 8;     // keys in flight per 16-lane group
+constexpr int kBlock = 1024;        // scores per sel_collect / sel_scatter workgroup
+constexpr int kSortCap = 2048;      // candidates sorted in LDS; more take the radix path
+constexpr int kHistWG = 16;         // sel_hist workgroups per head
 
 struct HeadInfo {
   float inv_scale;       // 2048 / ||q||, or 0 when q == 0
@@ -104,58 +112,57 @@ __global__ __launch_bounds__(256) void sel_init(const void* __restrict__ query, 
 template <int DT>
 __global__ __launch_bounds__(256) void sel_score(const void* __restrict__ keys,
                                                  const void* __restrict__ query, int64_t n,
-                                                 int wg_per_head, HeadInfo* __restrict__ info,
-                                                 unsigned* __restrict__ scores,
-                                                 unsigned* __restrict__ hist) {
+                                                 int wg_per_head, unsigned* __restrict__ scores) {
   const int head = blockIdx.x / wg_per_head;
   const int wg = blockIdx.x % wg_per_head;
   const int t = threadIdx.x;
   const int sub = t & 15;
-  __shared__ unsigned lh[kBins];
-  __shared__ int is_last;
-  for (int i = t; i < kBins; i += 256) lh[i] = 0u;
   float qv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) qv[e] = load_elem(query, DT, (int64_t)head * kD + sub * 8 + e);
-  const float inv = info[head].inv_scale;
-  __syncthreads();
   const int64_t k_begin = (int64_t)wg * kScoreChunk;
   const int64_t k_end = k_begin + kScoreChunk < n ? k_begin + kScoreChunk : n;
   const int64_t hoff = (int64_t)head * n;
-  for (int64_t k0 = k_begin; k0 < k_end; k0 += 16 * 4) {
-    float dot[4], nrm[4];
+  for (int64_t k0 = k_begin; k0 < k_end; k0 += 16 * kScoreUnroll) {
+    float dot[kScoreUnroll], nrm[kScoreUnroll];
+    float x[kScoreUnroll][8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kScoreUnroll; ++u) {  // issue every load first
       const int64_t key = k0 + u * 16 + (t >> 4);
-      dot[u] = 0.f;
-      nrm[u] = 0.f;
       if (key < k_end) {
-        float x[8];
         if (DT == A2ATS_BF16) {
-          const uint4 raw = *reinterpret_cast<const uint4*>(
-              static_cast<const uint16_t*>(keys) + (hoff + key) * kD + sub * 8);
+          const u4v raw = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(
+              static_cast<const uint16_t*>(keys) + (hoff + key) * kD + sub * 8));
           const unsigned w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            x[2 * e] = __uint_as_float(w[e] << 16);
-            x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+            x[u][2 * e] = __uint_as_float(w[e] << 16);
+            x[u][2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
           }
         } else {
-          const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(keys) +
-                                                            (hoff + key) * kD + sub * 8);
-          float4 a = p[0], b = p[1];
-          x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-          x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+          const f4v* p = reinterpret_cast<const f4v*>(static_cast<const float*>(keys) +
+                                                      (hoff + key) * kD + sub * 8);
+          const f4v a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+          x[u][0] = a.x; x[u][1] = a.y; x[u][2] = a.z; x[u][3] = a.w;
+          x[u][4] = b.x; x[u][5] = b.y; x[u][6] = b.z; x[u][7] = b.w;
         }
+      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          dot[u] += x[e] * qv[e];
-          nrm[u] += x[e] * x[e];
-        }
+        for (int e = 0; e < 8; ++e) x[u][e] = 0.f;
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kScoreUnroll; ++u) {
+      dot[u] = 0.f;
+      nrm[u] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dot[u] += x[u][e] * qv[e];
+        nrm[u] += x[u][e] * x[u][e];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u) {
 #pragma unroll
       for (int o = 8; o > 0; o >>= 1) {
         dot[u] += __shfl_xor(dot[u], o);
@@ -163,11 +170,41 @@ __global__ __launch_bounds__(256) void sel_score(const void* __restrict__ keys,
       }
       const int64_t key = k0 + u * 16 + (t >> 4);
       if (sub == 0 && key < k_end) {
-        const float s = nrm[u] > 0.f ? dot[u] / sqrtf(nrm[u]) : 0.f;
-        const unsigned ukey = order_key(s);
-        scores[hoff + key] = ukey;
-        atomicAdd(&lh[bin_of(ukey, inv)], 1u);
+        const float sc = nrm[u] > 0.f ? dot[u] / sqrtf(nrm[u]) : 0.f;
+        scores[hoff + key] = order_key(sc);
       }
+    }
+  }
+}
+
+// Histogram of the binned scores: kHistWG workgroups per head, LDS histogram, one global
+// atomic per non-empty bin; the last workgroup of each head (fenced counter, no waiting)
+// finds the bin b* holding the n_r-th largest score.
+__global__ __launch_bounds__(256) void sel_hist(const unsigned* __restrict__ scores, int64_t n,
+                                                HeadInfo* __restrict__ info,
+                                                unsigned* __restrict__ hist) {
+  const int head = blockIdx.x / kHistWG;
+  const int wg = blockIdx.x % kHistWG;
+  const int t = threadIdx.x;
+  __shared__ unsigned lh[kBins];
+  __shared__ int is_last;
+  for (int i = t; i < kBins; i += 256) lh[i] = 0u;
+  const float inv = info[head].inv_scale;
+  __syncthreads();
+  const int64_t per = ((n + kHistWG - 1) / kHistWG + 3) / 4 * 4;
+  const int64_t i_begin = (int64_t)wg * per;
+  const int64_t i_end = i_begin + per < n ? i_begin + per : n;
+  const int64_t hoff = (int64_t)head * n;
+  for (int64_t i0 = i_begin + 4 * t; i0 < i_end; i0 += 1024) {
+    unsigned uv[4];
+    if (i0 + 3 < i_end && ((hoff + i0) & 3) == 0) {
+      const uint4 q = *reinterpret_cast<const uint4*>(scores + hoff + i0);
+      uv[0] = q.x; uv[1] = q.y; uv[2] = q.z; uv[3] = q.w;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) atomicAdd(&lh[bin_of(uv[k], inv)], 1u);
+    } else {
+      for (int k = 0; k < 4 && i0 + k < i_end; ++k)
+        atomicAdd(&lh[bin_of(scores[hoff + i0 + k], inv)], 1u);
     }
   }
   __syncthreads();
@@ -175,7 +212,7 @@ __global__ __launch_bounds__(256) void sel_score(const void* __restrict__ keys,
     if (lh[i]) atomicAdd(&hist[(int64_t)head * kBins + i], lh[i]);
   __threadfence();
   __syncthreads();
-  if (t == 0) is_last = (atomicAdd(&info[head].done_score, 1u) == (unsigned)wg_per_head - 1);
+  if (t == 0) is_last = (atomicAdd(&info[head].done_score, 1u) == (unsigned)kHistWG - 1);
   __syncthreads();
   if (!is_last) return;
   __threadfence();
@@ -230,15 +267,33 @@ __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ 
   const int64_t i_begin = (int64_t)blk * kBlock;
   const int64_t i_end = i_begin + kBlock < n ? i_begin + kBlock : n;
   unsigned above = 0;
-  for (int64_t i = i_begin + t; i < i_end; i += 256) {
-    const unsigned u = scores[hoff + i];
-    const int b = bin_of(u, inv);
-    if (b > bstar) above += 1;
-    if (b == bstar) {
-      unsigned slot = atomicAdd((unsigned*)&info[head].n_cand, 1u);
-      cand[hoff + slot] = key64(u, i);
+  __shared__ unsigned s_cnt, s_base;
+  if (t == 0) s_cnt = 0u;
+  __syncthreads();
+  const int64_t i0 = i_begin + 4 * t;  // 4 consecutive scores per thread
+  unsigned uv[4];
+  if (i0 + 3 < i_end && ((hoff + i0) & 3) == 0) {
+    const uint4 q = *reinterpret_cast<const uint4*>(scores + hoff + i0);
+    uv[0] = q.x; uv[1] = q.y; uv[2] = q.z; uv[3] = q.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) uv[k] = (i0 + k < i_end) ? scores[hoff + i0 + k] : 0u;
+  }
+  unsigned mine = 0, local = 0;  // candidates of this thread, and their LDS slot base
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (i0 + k < i_end) {
+      const int b = bin_of(uv[k], inv);
+      if (b > bstar) above += 1;
+      if (b == bstar) mine |= 1u << k;
     }
   }
+  if (mine) local = atomicAdd(&s_cnt, (unsigned)__popc(mine));
+  __syncthreads();
+  if (t == 0) s_base = s_cnt ? atomicAdd((unsigned*)&info[head].n_cand, s_cnt) : 0u;
+  __syncthreads();
+  for (int k = 0; k < 4; ++k)
+    if (mine & (1u << k)) cand[hoff + s_base + local++] = key64(uv[k], i0 + k);
   __shared__ unsigned red[4];
   __shared__ int is_last;
   for (int o = 32; o > 0; o >>= 1) above += __shfl_xor(above, o);
@@ -261,7 +316,33 @@ __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ 
   if (t == 0) s_remaining = (unsigned)(r > 0 ? r : 0);
   __syncthreads();
   const unsigned long long* ch = cand + hoff;
-  if (r > 0) {
+  __shared__ unsigned long long sk[kSortCap];
+  if (r > 0 && n_cand <= kSortCap) {
+    // bitonic sort of the candidate keys, descending; the r-th is the threshold
+    int P = 1;
+    while (P < n_cand) P <<= 1;
+    for (int i = t; i < P; i += 256)
+      sk[i] = i < n_cand ? __hip_atomic_load(&ch[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+    __syncthreads();
+    for (int k = 2; k <= P; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = t; i < P; i += 256) {
+          const int l = i ^ j;
+          if (l > i) {
+            const unsigned long long a = sk[i], b = sk[l];
+            const bool desc = (i & k) == 0;
+            if (desc ? (a < b) : (a > b)) {
+              sk[i] = b;
+              sk[l] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    prefix = sk[r - 1];
+    if (t == 0) info[head].thr = prefix;
+  } else if (r > 0) {
     for (int shift = 56; shift >= 0; shift -= 8) {
       dh[t] = 0u;
       __syncthreads();
@@ -333,7 +414,7 @@ __global__ __launch_bounds__(256) void sel_scatter(const unsigned* __restrict__ 
   const int n_r = info[head].n_r;
   const int64_t hoff = (int64_t)head * n;
   const int64_t i_begin = (int64_t)blk * kBlock;
-  constexpr int kPer = kBlock / 256;  // 16 consecutive elements per thread
+  constexpr int kPer = kBlock / 256;  // consecutive elements per thread
   const int64_t my0 = i_begin + (int64_t)t * kPer;
   unsigned flags = 0;
   int cnt = 0;
@@ -440,10 +521,12 @@ extern "C" int a2ats_select_retrieval(const void* keys, int keys_dtype, int64_t 
                    keys_dtype, n, fraction, L.info, L.hist, L.sel_extra, (int)nblk));
   if (keys_dtype == A2ATS_BF16)
     A2ATS_TRY(launch("select_score", sel_score<A2ATS_BF16>, dim3((unsigned)(heads * wg_per_head)),
-                     dim3(256), 0, s, keys, query, n, (int)wg_per_head, L.info, L.scores, L.hist));
+                     dim3(256), 0, s, keys, query, n, (int)wg_per_head, L.scores));
   else
     A2ATS_TRY(launch("select_score", sel_score<A2ATS_F32>, dim3((unsigned)(heads * wg_per_head)),
-                     dim3(256), 0, s, keys, query, n, (int)wg_per_head, L.info, L.scores, L.hist));
+                     dim3(256), 0, s, keys, query, n, (int)wg_per_head, L.scores));
+  A2ATS_TRY(launch("select_hist", sel_hist, dim3((unsigned)(heads * kHistWG)), dim3(256), 0, s,
+                   L.scores, n, L.info, L.hist));
   A2ATS_TRY(launch("select_collect", sel_collect, dim3((unsigned)(heads * nblk)), dim3(256), 0, s,
                    L.scores, n, (int)nblk, L.info, L.above_blk, L.cand, L.sel_extra));
   return launch("select_scatter", sel_scatter, dim3((unsigned)(heads * nblk)), dim3(256), 0, s,

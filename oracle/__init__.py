@@ -48,6 +48,7 @@ def lib():
                   L.orc_select_retrieval, L.orc_reconstruct):
             f.restype = ctypes.c_int
         L.orc_round_bf16.restype = None
+        L.orc_threads.argtypes, L.orc_threads.restype = [], ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -179,3 +180,7 @@ def round_bf16(x):
     out = np.empty(x.shape, np.uint16)
     lib().orc_round_bf16(_ptr(x.reshape(-1), _dp), x.size, _ptr(out.reshape(-1), _up))
     return out
+
+
+def threads() -> int:
+    return int(lib().orc_threads())

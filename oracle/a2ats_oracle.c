@@ -19,6 +19,7 @@
 #include "a2ats_oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -296,3 +297,6 @@ void orc_round_bf16(const double* x, int64_t n, uint16_t* out) {
     out[t] = (uint16_t)(u >> 16) | sign;
   }
 }
+
+/* Threads OpenMP uses for the parallel loops above. */
+int orc_threads(void) { return omp_get_max_threads(); }

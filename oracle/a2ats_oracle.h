@@ -60,6 +60,9 @@ int orc_reconstruct(const uint16_t* codes, const int32_t* pos, int64_t n, int64_
                     const double* cb, int64_t c, int64_t cur, int64_t window, int64_t far_b,
                     int far_mode, double base, double* out, int64_t* far_count);
 
+/* Threads the OpenMP loops use. */
+int orc_threads(void);
+
 /* Round fp64 values to bf16 (nearest, ties to even), raw bits. */
 void orc_round_bf16(const double* x, int64_t n, uint16_t* out);
 
