@@ -112,4 +112,11 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
   return s16 | static_cast<uint16_t>(__float_as_uint(f) >> 16);
 }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations, then
+// s_barrier.  Unlike __syncthreads() it does not wait for outstanding global loads, so a
+// prefetch issued before it stays in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace a2ats

@@ -43,17 +43,18 @@ constexpr int kLd = kD + 1;               // padded LDS row of L (conflict-free 
 constexpr int kRows = 32;                 // centroids per MFMA tile
 constexpr int kSteps = kD / 16;           // k-steps per tile (v_mfma_f32_32x32x16_f16)
 constexpr int kFragPerTile = kSteps * 64; // half8 fragments per tile (8 KiB)
-constexpr int kRing = 3;                  // LDS tile ring of the coarse pass
+constexpr int kTPS = 4;                   // tiles per LDS stage of the coarse pass
 constexpr int kKeysPerWG = 256;           // 4 waves x 64 keys
 constexpr int kCandCap = 32;              // rescan candidates per key
 constexpr int kRescanTiles = 8;           // tiles per rescan work item
 constexpr float kPadBias = -1.0e38f;      // bias of padding rows: finite, never competitive
 
 struct Counters {
-  unsigned refine;      // refine list entries
-  unsigned full;        // full-scan list entries
-  unsigned stats[8];    // keys, direct, reranked, rescanned, full_scan
-  unsigned unc[1];      // per-head rescan list lengths follow (heads entries)
+  unsigned refine_x[8][16];  // refine list entries per XCD region (counters 64 B apart)
+  unsigned stat_x[8][16];    // keys and direct decisions per XCD (when statistics are asked)
+  unsigned full;             // full-scan list entries
+  unsigned stats[8];         // [2] reranked, [3] rescanned, [4] full scan
+  unsigned unc[1];           // per-head rescan list lengths follow (heads entries)
 };
 
 struct RefEntry {       // a key whose code needs fp64 scores
@@ -421,6 +422,19 @@ __device__ __forceinline__ float pack_tile(float x, unsigned keep, unsigned tile
   return __uint_as_float((__float_as_uint(x) & keep) | tile_v);
 }
 
+// Largest of three with IEEE-754 maximum semantics (one v_maximum3_f32; the operands are
+// never NaN, and unlike fmaxf it needs no canonicalising of integer-packed inputs).
+__device__ __forceinline__ float fmax3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+// Element h of a two-element register array without dynamic indexing (which would move
+// the array, and everything that shares its storage, to scratch memory).
+template <class T>
+__device__ __forceinline__ T sel2(const T (&a)[2], int h) {
+  return h ? a[1] : a[0];
+}
+
 // A uniform value copied into a VGPR, opaque to the optimiser (GFX9 VALU instructions may
 // read only one scalar operand).
 __device__ __forceinline__ unsigned vgpr_of(unsigned s) {
@@ -468,13 +482,15 @@ __device__ __forceinline__ double coop_score(const void* keys, int64_t off_key, 
 // ------------------------------------------------------------------ the MFMA pass
 // Workgroup: 256 keys of one head (4 waves x two 32-key column blocks).  Lane l serves key
 // column l % 32 of both blocks and, in every 32-centroid tile, the 16 rows
-// 8(r/4) + 4(l/32) + (r%4).  Codebook tiles stream through a 3-deep LDS ring, one barrier
-// per tile; each tile costs 8 MFMAs per block with the bias as the first accumulator input.
-// Every accumulator slot keeps its own running top-2 over the tiles, the tile index packed
-// into the low bits: 3 VALU ops per score (pack, med3 for the second, med3 for the max).
-// At the end each key has 32 (max, second) pairs: the top three and the largest second give
-//   direct  t1 - t2 > 2E (+ packing slack)  -> code j(t1)
-//   else    listed for the fp64 rerank of j(t1), j(t2) against max(t3, largest second) + E.
+// 8(r/4) + 4(l/32) + (r%4).  Codebook tiles stream through LDS in double-buffered stages of
+// four tiles, loads issued a stage ahead, one LDS-only barrier per stage; each tile costs 8
+// MFMAs per block with the bias as the first accumulator input, and its VALU fold overlaps
+// the next tile's MFMAs.
+// Each lane keeps 8 slot maxima per block (a slot pairs two of its rows), the tile index and
+// row parity packed into the low bits, plus one value U bounding every score that is not a
+// slot maximum.  At the end each key has 16 slot maxima and U:
+//   direct  t1 - max(t2, U) > 2E (+ packing slack)  -> code j(t1)
+//   else    listed for the fp64 rerank of j(t1), j(t2) against max(t3, U) + E.
 // Workgroups are dealt to XCDs round-robin; the mapping gives each XCD a contiguous range of
 // (head, key block) pairs so a head's codebook stays in one L2.
 template <int DT, bool ZNORM, bool DIST>
@@ -485,9 +501,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const double* __restrict__ b64, int64_t c, const half8* __restrict__ lfrag,
     const float* __restrict__ part_a, int nwg_a, const float* __restrict__ part_b, int nwg_b,
     float* __restrict__ znorm, uint16_t* __restrict__ codes, float* __restrict__ dist,
-    RefEntry* __restrict__ refl, FullEntry* __restrict__ full, Counters* __restrict__ cnt) {
-  __shared__ half8 sv[kRing][kFragPerTile];
-  __shared__ __attribute__((aligned(16))) float sb[kRing][32];
+    RefEntry* __restrict__ refl, FullEntry* __restrict__ full, Counters* __restrict__ cnt,
+    int want_stats) {
+  __shared__ half8 sv[2][kTPS][kFragPerTile];
+  __shared__ __attribute__((aligned(16))) float sb[2][kTPS][32];
   __shared__ float s_red[2][4];
   const int64_t G = gridDim.x;
   const int64_t per_xcd = G / 8;
@@ -515,22 +532,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   const half8* vh = v16 + head * (int64_t)T * kFragPerTile;
   const float* bh = bias + head * (int64_t)T * 32;
-  // tile loader: 256 threads x 2 fragments; 8 threads x 4 bias floats
-  half8 pf0, pf1;
+  // stage loader: a stage is kTPS tiles (32 KiB of fragments, 512 B of bias); 256 threads x
+  // 8 fragments, 32 threads x 4 bias floats.  Loads for stage s+2 are issued when stage s+1
+  // is committed, so each load has a whole stage of MFMA work to arrive.
+  const int nst = (T + kTPS - 1) / kTPS;
+  half8 pf[kTPS][2];
   f4 pb = {};
-  auto fetch = [&](int tile) {
-    pf0 = vh[(int64_t)tile * kFragPerTile + t];
-    pf1 = vh[(int64_t)tile * kFragPerTile + 256 + t];
-    if (t < 8) pb = *reinterpret_cast<const f4*>(bh + (int64_t)tile * 32 + t * 4);
+  auto fetch = [&](int st) {
+    const half8* src = vh + (int64_t)st * kTPS * kFragPerTile;
+#pragma unroll
+    for (int q = 0; q < kTPS; ++q) {
+      pf[q][0] = src[q * kFragPerTile + t];
+      pf[q][1] = src[q * kFragPerTile + 256 + t];
+    }
+    if (t < 8 * kTPS) pb = *reinterpret_cast<const f4*>(bh + (int64_t)st * kTPS * 32 + t * 4);
   };
   auto commit = [&](int buf) {
-    sv[buf][t] = pf0;
-    sv[buf][256 + t] = pf1;
-    if (t < 8) *reinterpret_cast<f4*>(&sb[buf][t * 4]) = pb;
+#pragma unroll
+    for (int q = 0; q < kTPS; ++q) {
+      sv[buf][q][t] = pf[q][0];
+      sv[buf][q][256 + t] = pf[q][1];
+    }
+    if (t < 8 * kTPS) *reinterpret_cast<f4*>(&sb[buf][t / 8][(t % 8) * 4]) = pb;
   };
   fetch(0);
   commit(0);
-  if (T > 1) fetch(1);
+  if (nst > 1) fetch(1);
 
   int64_t row[2];
 #pragma unroll
@@ -568,100 +595,139 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int blk = 0; blk < 2; ++blk) zn[blk] = (zn[blk] + __shfl_xor(zn[blk], 32)) * inv;
   }
 
-  float m1[2][16], m2[2][16];
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) m1[blk][r] = m2[blk][r] = -INFINITY;
-  const unsigned keep = ~((1u << tbits) - 1u);
-  // +inf kept opaque so med3(x, p, +inf) stays one v_med3_f32 (as a max it would gain
-  // NaN-canonicalising extra instructions)
-  float inf;
-  asm("v_mov_b32 %0, 0x7f800000" : "=v"(inf));
-  __syncthreads();
-
-  for (int tile = 0; tile < T; ++tile) {
-    const int buf = tile % kRing;
-    if (tile + 1 < T) commit((tile + 1) % kRing);
-    if (tile + 2 < T) fetch(tile + 2);
-    const f4* bl = reinterpret_cast<const f4*>(&sb[buf][hh * 16]);
-    f16v bv;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f4 b4 = bl[q];
-      bv[4 * q + 0] = b4.x; bv[4 * q + 1] = b4.y; bv[4 * q + 2] = b4.z; bv[4 * q + 3] = b4.w;
-    }
-    f16v acc0, acc1;
-    {
-      const half8 a = sv[buf][lane];
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf.f[0][0], bv, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf.f[1][0], bv, 0, 0, 0);
-    }
-#pragma unroll
-    for (int s = 1; s < kSteps; ++s) {
-      const half8 a = sv[buf][s * 64 + lane];
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf.f[0][s], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf.f[1][s], acc1, 0, 0, 0);
-    }
-    const unsigned tv = vgpr_of((unsigned)tile);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p0 = pack_tile(acc0[r], keep, tv);
-      const float p1 = pack_tile(acc1[r], keep, tv);
-      m2[0][r] = __builtin_amdgcn_fmed3f(m1[0][r], m2[0][r], p0);
-      m1[0][r] = __builtin_amdgcn_fmed3f(m1[0][r], p0, inf);
-      m2[1][r] = __builtin_amdgcn_fmed3f(m1[1][r], m2[1][r], p1);
-      m1[1][r] = __builtin_amdgcn_fmed3f(m1[1][r], p1, inf);
-    }
-    __syncthreads();
-  }
-
-  // ---- per-key certificate.  Both lanes of a key merge the same 32 lists; lane half hh
-  // finalises block hh.  Top three (value, index) with straight-line insertion.
-  const unsigned tmask = ~keep;
-  float tv0[2], tv1[2], tv2[2], useg[2];
-  int tj0[2], tj1[2];
+  // Per lane and 32-key block: 8 slot maxima (slot i = the lane's tile rows of registers 2i
+  // and 2i+1, over all tiles), each packed with (tile << 1 | register parity) in its low
+  // bits, and one running value U at least as large as every score that is not a slot
+  // maximum.  Per pair of scores: two packs, a med3 (the middle of slot max and the pair,
+  // which is the largest value the slot drops) and a max3; U absorbs two dropped values per
+  // max3: 2.25 VALU ops per score.
+  float m1[2][8], U[2];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
-    float a0 = -INFINITY, a1 = -INFINITY, a2 = -INFINITY, u = -INFINITY;
-    int i0 = 0x7FFFFFFF, i1 = 0x7FFFFFFF, i2 = 0x7FFFFFFF;
+    U[blk] = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
-      const int r = q >> 1;
-      const float x = (q & 1) ? m2[blk][r] : m1[blk][r];
-      if (q & 1) u = fmaxf(u, x);
-      const int jx = (int)((__float_as_uint(x) & tmask) * kRows + slot_row(r, hh));
-      const bool b2 = x > a2 || (x == a2 && jx < i2);
-      const bool b1 = x > a1 || (x == a1 && jx < i1);
-      const bool b0 = x > a0 || (x == a0 && jx < i0);
-      if (x > -INFINITY && b2) {
-        a2 = b1 ? a1 : x; i2 = b1 ? i1 : jx;
-        if (b1) { a1 = b0 ? a0 : x; i1 = b0 ? i0 : jx; }
-        if (b0) { a0 = x; i0 = jx; }
-      }
-    }
-    // merge with the partner lane (the other 16 rows of every tile)
-    u = fmaxf(u, __shfl_xor(u, 32));
-    const float p0 = __shfl_xor(a0, 32), p1 = __shfl_xor(a1, 32), p2 = __shfl_xor(a2, 32);
-    const int q0 = __shfl_xor(i0, 32), q1 = __shfl_xor(i1, 32), q2 = __shfl_xor(i2, 32);
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const float x = q == 0 ? p0 : (q == 1 ? p1 : p2);
-      const int jx = q == 0 ? q0 : (q == 1 ? q1 : q2);
-      const bool b2 = x > a2 || (x == a2 && jx < i2);
-      const bool b1 = x > a1 || (x == a1 && jx < i1);
-      const bool b0 = x > a0 || (x == a0 && jx < i0);
-      if (x > -INFINITY && b2) {
-        a2 = b1 ? a1 : x; i2 = b1 ? i1 : jx;
-        if (b1) { a1 = b0 ? a0 : x; i1 = b0 ? i0 : jx; }
-        if (b0) { a0 = x; i0 = jx; }
-      }
-    }
-    tv0[blk] = a0; tv1[blk] = a1; tv2[blk] = a2; useg[blk] = u;
-    tj0[blk] = i0; tj1[blk] = i1;
+    for (int i = 0; i < 8; ++i) m1[blk][i] = -INFINITY;
   }
-  const int blk = hh;
-  const int64_t myrow = row[blk];
+  const unsigned keep = ~((1u << tbits) - 1u);
+  __syncthreads();
+
+  // Fold pair i (registers 2i, 2i+1) of one tile's scores into the slot maxima and U.
+  float dr[2][8];
+  auto fold_pair = [&](const f16v& a0, const f16v& a1, int i, unsigned te, unsigned to) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const f16v& acc = blk ? a1 : a0;
+      const float p = pack_tile(acc[2 * i], keep, te);
+      const float q = pack_tile(acc[2 * i + 1], keep, to);
+      dr[blk][i] = __builtin_amdgcn_fmed3f(m1[blk][i], p, q);
+      m1[blk][i] = fmax3(m1[blk][i], p, q);
+      if (i & 1) U[blk] = fmax3(U[blk], dr[blk][i - 1], dr[blk][i]);
+    }
+    // an empty use pins the fold here (it would otherwise sink to the end of the stage,
+    // keeping every tile's accumulators live at once)
+    asm volatile("" ::"v"(m1[0][i]), "v"(m1[1][i]));
+    if (i & 1) asm volatile("" ::"v"(U[0]), "v"(U[1]));
+  };
+  auto load_bias = [&](int buf, int q) {
+    const f4* bl = reinterpret_cast<const f4*>(&sb[buf][q][hh * 16]);
+    f16v bv;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f4 b4 = bl[k];
+      bv[4 * k + 0] = b4.x; bv[4 * k + 1] = b4.y; bv[4 * k + 2] = b4.z; bv[4 * k + 3] = b4.w;
+    }
+    return bv;
+  };
+
+  // Software pipeline: tile q of a stage runs its 8 MFMA steps into (a0, a1) while the VALU
+  // folds the previous tile (p0, p1) one register pair per step; scheduling barriers keep
+  // that interleave.  Fragments are read from LDS kAhead steps before their MFMAs, the bias
+  // of the next tile two steps before it starts.  Stages always hold kTPS tiles (tiles past
+  // the codebook carry the padding bias), so the accumulator pairs x and y simply
+  // alternate; y starts as a fold-neutral stand-in for the tile before the first.
+  constexpr int kAhead = 3;
+  constexpr int kStageSteps = kTPS * kSteps;
+  f16v x0, x1, y0, y1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) y0[r] = y1[r] = kPadBias;
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    const int base = st * kTPS;
+    half8 fr[kStageSteps];
+#pragma unroll
+    for (int g = 0; g < kAhead; ++g) fr[g] = sv[buf][g / kSteps][(g % kSteps) * 64 + lane];
+    f16v bv = load_bias(buf, 0);
+#pragma unroll
+    for (int q = 0; q < kTPS; ++q) {
+      f16v& a0 = (q & 1) ? y0 : x0;
+      f16v& a1 = (q & 1) ? y1 : x1;
+      const f16v& p0 = (q & 1) ? x0 : y0;
+      const f16v& p1 = (q & 1) ? x1 : y1;
+      const int ptile = base + q - 1 < 0 ? 0 : base + q - 1;
+      const unsigned te = vgpr_of((unsigned)ptile << 1);
+      const unsigned to = te | 1u;
+      f16v bn;
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const int g = q * kSteps + s;
+        if (g + kAhead < kStageSteps)
+          fr[g + kAhead] = sv[buf][(g + kAhead) / kSteps][((g + kAhead) % kSteps) * 64 + lane];
+        if (s == kSteps - 2 && q + 1 < kTPS) bn = load_bias(buf, q + 1);
+        a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[g], kf.f[0][s], s == 0 ? bv : a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[g], kf.f[1][s], s == 0 ? bv : a1, 0, 0, 0);
+        fold_pair(p0, p1, s, te, to);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      bv = bn;
+    }
+    if (st + 1 < nst) commit(buf ^ 1);
+    if (st + 2 < nst) fetch(st + 2);
+    lds_barrier();
+  }
+  {
+    const unsigned te = vgpr_of((unsigned)(nst * kTPS - 1) << 1);
+    const unsigned to = te | 1u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fold_pair(y0, y1, i, te, to);
+  }
+  __syncthreads();
+
+  // ---- per-key certificate.  Lane (col, hh) finalises key col of block hh: it keeps its own
+  // 8 slot maxima of that block and takes the partner lane's 8 (the other 16 rows).
+  const unsigned tmask = ~keep;
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = hh ? m1[1][i] : m1[0][i];
+    v[8 + i] = __shfl_xor(hh ? m1[0][i] : m1[1][i], 32);
+  }
+  const float um = fmaxf(hh ? U[1] : U[0], __shfl_xor(hh ? U[0] : U[1], 32));
+  // top three values: a0 >= a1 >= a2 (med3 insertion, three ops per value)
+  float a0 = -INFINITY, a1 = -INFINITY, a2 = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float n2 = __builtin_amdgcn_fmed3f(a1, a2, v[i]);
+    const float n1 = __builtin_amdgcn_fmed3f(a0, a1, v[i]);
+    a0 = __builtin_elementwise_maximum(a0, v[i]);
+    a1 = n1;
+    a2 = n2;
+  }
+  // the slots holding a0 and (another) a1.  Equal packed values break ties arbitrarily: they
+  // never certify directly, and the rerank and rescan resolve them exactly.
+  int i0 = 0, i1 = 0;
+#pragma unroll
+  for (int i = 15; i >= 0; --i) i0 = v[i] == a0 ? i : i0;
+#pragma unroll
+  for (int i = 15; i >= 0; --i) i1 = (v[i] == a1 && i != i0) ? i : i1;
+  // centroid index of slot i: tile and parity from the packed bits, row from the slot
+  auto jdec = [&](float x, int i) {
+    const unsigned low = __float_as_uint(x) & tmask;
+    const int h = i < 8 ? hh : 1 - hh;
+    const int ii = i & 7;
+    return (int)(low >> 1) * kRows + 8 * (ii >> 1) + 4 * h + 2 * (ii & 1) + (int)(low & 1u);
+  };
+  const int j0 = jdec(a0, i0), j1 = jdec(a1, i1);
+  const int64_t myrow = hh ? row[1] : row[0];
   int outcome = 0;  // 1 direct, 2 listed for the rerank, 4 listed for the full scan
   RefEntry re;
   float z2 = -1.f;
@@ -670,24 +736,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const double rho = (double)fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
     const double nu = (double)fmaxf(fmaxf(s_red[1][0], s_red[1][1]), fmaxf(s_red[1][2], s_red[1][3]));
     const double B = 0.5 * S * (double)hs.maxb;
-    const double E = score_bound(kf.n2[blk], kf.e2[blk], rho, nu, B);
-    const float t0 = tv0[blk], t1 = tv1[blk], t2 = tv2[blk];
-    const double s0 = pack_slack(t0, tbits), s1 = pack_slack(t1, tbits);
+    const double E = score_bound(hh ? kf.n2[1] : kf.n2[0], hh ? kf.e2[1] : kf.e2[0], rho, nu, B);
+    const float t1u = fmaxf(a1, um);  // bound on every score but the best
+    const double s0 = pack_slack(a0, tbits), s1 = pack_slack(t1u, tbits);
     if (ZNORM) {
-      z2 = zn[blk];
+      z2 = hh ? zn[1] : zn[0];
       znorm[head * n + myrow] = z2;
     } else if (znorm) {
       z2 = znorm[head * n + myrow];
     }
-    if (kf.bad[blk]) {
+    if (hh ? kf.bad[1] : kf.bad[0]) {
       outcome = 4;
-    } else if (tj0[blk] < c && (double)t0 - s0 - E > (double)t1 + s1 + E) {
+    } else if (j0 < c && (double)a0 - s0 - E > (double)t1u + s1 + E) {
       outcome = 1;
-      const int code = tj0[blk];
-      codes[head * n + myrow] = (uint16_t)code;
+      codes[head * n + myrow] = (uint16_t)j0;
       if (DIST) {
         // distance of the certified code: fp32 dot with the fp32 copy of v_code
-        const float* vr = v32 + (head * c + code) * kD;
+        const float* vr = v32 + (head * c + j0) * kD;
         const int64_t off = (head * n + myrow) * kD;
         float sdot = 0.f, k2 = 0.f;
         for (int a = 0; a < kD; a += 8) {
@@ -702,26 +767,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int e = 0; e < 8; ++e) k2 += x[e] * x[e];
         }
         const double zz = (ZNORM || znorm) ? (double)z2 : (double)k2;
-        const double sc = (double)sdot - 0.5 * b64[head * c + code];
+        const double sc = (double)sdot - 0.5 * b64[head * c + j0];
         dist[head * n + myrow] = (float)fmax(zz - 2.0 * sc, 0.0);
       }
     } else {
       outcome = 2;
-      const double U = fmax((double)t2, (double)useg[blk]);
+      const double Ub = fmax((double)a2, (double)um);
       re.head = (int32_t)head;
       re.row = (int32_t)myrow;
-      re.j0 = tj0[blk] < c ? tj0[blk] : -1;
-      re.j1 = (tj1[blk] < c && t1 > -INFINITY) ? tj1[blk] : -1;
-      re.thr = (U + pack_slack((float)U, tbits) + E) / S;
+      re.j0 = j0 < c ? j0 : -1;
+      re.j1 = j1 < c ? j1 : -1;
+      re.thr = (Ub + pack_slack((float)Ub, tbits) + E) / S;
       re.e_unscaled = E / S;
       re.z2 = z2;
       re.pad = 0;
     }
   }
+  // Rerank entries go to this XCD's region of the list (a counter per XCD keeps the
+  // global atomics off one address), one atomic per workgroup; full-scan entries (rare)
+  // share one counter.
   __shared__ unsigned s_cnt, s_base, s_stat[2];
-  if (t == 0) s_stat[0] = s_stat[1] = 0u;
-  const unsigned rslot = block_append(&cnt->refine, outcome == 2, &s_cnt, &s_base);
-  if (outcome == 2) refl[rslot] = re;
+  const unsigned xcd = blockIdx.x % 8;
+  const unsigned rslot = block_append(&cnt->refine_x[xcd][0], outcome == 2, &s_cnt, &s_base);
+  if (outcome == 2) refl[(int64_t)xcd * per_xcd * kKeysPerWG + rslot] = re;
   const unsigned fslot = block_append(&cnt->full, outcome == 4, &s_cnt, &s_base);
   if (outcome == 4) {
     FullEntry fe;
@@ -731,17 +799,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     fe.pad = 0;
     full[fslot] = fe;
   }
-  // statistics: one atomic per workgroup
-  const unsigned long long valid = __ballot(myrow >= 0);
-  const unsigned long long dmask = __ballot(outcome == 1);
-  if (lane == 0) {
-    atomicAdd(&s_stat[0], (unsigned)__popcll(valid));
-    atomicAdd(&s_stat[1], (unsigned)__popcll(dmask));
-  }
-  __syncthreads();
-  if (t == 0) {
-    if (s_stat[0]) atomicAdd(&cnt->stats[0], s_stat[0]);
-    if (s_stat[1]) atomicAdd(&cnt->stats[1], s_stat[1]);
+  if (want_stats) {  // keys and direct decisions, per XCD
+    if (t == 0) s_stat[0] = s_stat[1] = 0u;
+    __syncthreads();
+    const unsigned long long valid = __ballot(myrow >= 0);
+    const unsigned long long dmask = __ballot(outcome == 1);
+    if (lane == 0) {
+      atomicAdd(&s_stat[0], (unsigned)__popcll(valid));
+      atomicAdd(&s_stat[1], (unsigned)__popcll(dmask));
+    }
+    __syncthreads();
+    if (t == 0) {
+      if (s_stat[0]) atomicAdd(&cnt->stat_x[xcd][0], s_stat[0]);
+      if (s_stat[1]) atomicAdd(&cnt->stat_x[xcd][1], s_stat[1]);
+    }
   }
 }
 
@@ -752,13 +823,19 @@ __global__ __launch_bounds__(256) void enc_refine(
     const void* __restrict__ keys, int64_t n, int64_t c, const double* __restrict__ v64,
     const double* __restrict__ b64, const RefEntry* __restrict__ refl, uint16_t* __restrict__ codes,
     float* __restrict__ dist, UncEntry* __restrict__ unc, int64_t unc_cap,
-    FullEntry* __restrict__ full, Counters* __restrict__ cnt) {
+    FullEntry* __restrict__ full, Counters* __restrict__ cnt, int64_t region) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int sub = lane >> 5;          // which entry of the wave
   const int which = (lane >> 4) & 1;  // candidate 0 or 1
   const int g = lane & 15;
-  const unsigned total = __hip_atomic_load(&cnt->refine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the list is 8 regions of `region` entries, region x holding cnt->refine_x[x][0]
+  unsigned rc[8], total = 0u;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    rc[x] = cnt->refine_x[x][0];
+    total += rc[x];
+  }
   const int64_t stride = (int64_t)gridDim.x * 8;
   unsigned decided = 0;
   for (int64_t e0 = (int64_t)blockIdx.x * 8 + (t >> 6) * 2; e0 < (int64_t)total; e0 += stride) {
@@ -768,7 +845,17 @@ __global__ __launch_bounds__(256) void enc_refine(
     re.head = 0;
     re.row = 0;
     re.j0 = re.j1 = -1;
-    if (live) re = refl[e];
+    if (live) {
+      int x = 0;
+      unsigned off = (unsigned)e;
+#pragma unroll
+      for (int y = 0; y < 7; ++y) {
+        const bool on = x == y && off >= rc[y];
+        off = on ? off - rc[y] : off;
+        x = on ? y + 1 : x;
+      }
+      re = refl[(int64_t)x * region + off];
+    }
     const int j = live ? (which ? re.j1 : re.j0) : -1;
     double s = -INFINITY, k2 = 0.0;
     if (j >= 0) {
@@ -1101,12 +1188,18 @@ __global__ void enc_clear_u32(unsigned* p, int64_t count) {
 
 __global__ void enc_stats_out(const Counters* __restrict__ cnt, a2ats_encode_stats* out) {
   if (threadIdx.x == 0) {
-    out->keys = cnt->stats[0];
-    out->direct = cnt->stats[1];
+    unsigned keys = 0, direct = 0, listed = 0;
+    for (int x = 0; x < 8; ++x) {
+      keys += cnt->stat_x[x][0];
+      direct += cnt->stat_x[x][1];
+      listed += cnt->refine_x[x][0];
+    }
+    out->keys = keys;
+    out->direct = direct;
     out->reranked = cnt->stats[2];
     out->rescanned = cnt->stats[3];
     out->full_scan = cnt->stats[4];
-    out->reserved[0] = cnt->refine;
+    out->reserved[0] = listed;
     out->reserved[1] = cnt->full;
     out->reserved[2] = 0;
   }
@@ -1116,6 +1209,12 @@ __global__ void enc_stats_out(const Counters* __restrict__ cnt, a2ats_encode_sta
 inline int64_t unc_capacity(int64_t n) {
   const int64_t cap = n / 8;
   return cap < 1024 ? (n < 1024 ? n : 1024) : cap;
+}
+
+// Coarse-pass workgroups per XCD for n keys a head (the grid is a multiple of 8); each XCD
+// appends its rerank entries to a region of refine_regions * kKeysPerWG entries.
+inline int64_t refine_regions(int64_t heads, int64_t n) {
+  return (heads * ((n + kKeysPerWG - 1) / kKeysPerWG) + 7) / 8;
 }
 
 struct EncLayout {
@@ -1139,8 +1238,12 @@ struct EncLayout {
   size_t bytes;
 };
 
+// Codebook tiles of 32 centroids, padded to whole coarse-pass stages; the padding tiles hold
+// zero fragments and the padding bias.
+int64_t tiles_of(int64_t c) { return ((c + kRows - 1) / kRows + kTPS - 1) / kTPS * kTPS; }
+
 EncLayout carve(void* ws, int64_t heads, int64_t n, int64_t c) {
-  const int64_t T = (c + kRows - 1) / kRows;
+  const int64_t T = tiles_of(c);
   Carver cv(ws);
   EncLayout L;
   L.nwg_a = (int)((c + 31) / 32);
@@ -1156,7 +1259,7 @@ EncLayout carve(void* ws, int64_t heads, int64_t n, int64_t c) {
   L.part_a = cv.take<float>((size_t)heads * L.nwg_a * 4);
   L.part_b = cv.take<float>((size_t)heads * L.nwg_b * 2);
   L.cnt = cv.take<unsigned>((size_t)L.ncnt);
-  L.refl = cv.take<RefEntry>((size_t)heads * n);
+  L.refl = cv.take<RefEntry>((size_t)refine_regions(heads, n) * 8 * kKeysPerWG);
   L.unc = cv.take<UncEntry>((size_t)heads * L.unc_cap);
   L.full = cv.take<FullEntry>((size_t)heads * n);
   L.cand_n = cv.take<unsigned>((size_t)heads * L.unc_cap);
@@ -1170,9 +1273,10 @@ template <int DT>
 int encode_typed(const void* keys, int64_t heads, int64_t n, const int32_t* idx, int64_t n_sel,
                  const float* codebook, int64_t c, const float* chol, uint16_t* codes,
                  float* dist, a2ats_encode_stats* stats, const EncLayout& L, hipStream_t s) {
-  const int T = (int)((c + kRows - 1) / kRows);
-  int tbits = 0;
-  while ((1 << tbits) < T) ++tbits;
+  const int T = (int)tiles_of(c);
+  // packed into the low bits of the coarse pass: (tile << 1 | parity)
+  int tbits = 1;
+  while ((1 << (tbits - 1)) < T) ++tbits;
   const bool plain = chol == nullptr;
   Counters* cnt = reinterpret_cast<Counters*>(L.cnt);
   const size_t sm_rows = 32 * kD * sizeof(double) + (plain ? 0 : kD * kLd * sizeof(float)) +
@@ -1201,13 +1305,14 @@ int encode_typed(const void* keys, int64_t heads, int64_t n, const int32_t* idx,
 #define A2ATS_COARSE(Z, DI)                                                                       \
   launch(name, enc_coarse<DT, Z, DI>, dim3((unsigned)G), dim3(256), 0, s, keys, n, idx, n_sel,   \
          heads, nkb, T, tbits, L.v16, L.bias, L.v32, L.b64, c, L.lfrag, L.part_a, L.nwg_a,        \
-         L.part_b, L.nwg_b, znorm, codes, dist, L.refl, L.full, cnt)
+         L.part_b, L.nwg_b, znorm, codes, dist, L.refl, L.full, cnt, stats ? 1 : 0)
   if (znorm_mfma) A2ATS_TRY(A2ATS_COARSE(true, true));
   else if (dist) A2ATS_TRY(A2ATS_COARSE(false, true));
   else A2ATS_TRY(A2ATS_COARSE(false, false));
 #undef A2ATS_COARSE
   A2ATS_TRY(launch("encode_refine", enc_refine<DT>, dim3(1024), dim3(256), 0, s, keys, n, c, L.v64,
-                   L.b64, L.refl, codes, dist, L.unc, L.unc_cap, L.full, cnt));
+                   L.b64, L.refl, codes, dist, L.unc, L.unc_cap, L.full, cnt,
+                   (int64_t)(G / 8) * kKeysPerWG));
   A2ATS_TRY(launch("encode_rescan_collect", enc_rescan_collect<DT>, dim3(512), dim3(256), 0, s, keys,
                    n, heads, T, c, L.v16, L.bias, L.part_a, L.nwg_a, L.unc, L.unc_cap, cnt,
                    L.cand_n, L.cand));

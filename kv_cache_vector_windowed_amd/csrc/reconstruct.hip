@@ -71,6 +71,8 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
 // fp32 output: 4 pairs per thread, rotation in fp64, one rounding, two 16-byte stores.
 // bf16 output: 8 pairs per thread, rotation in fp32 (FMA) and one rounding to bf16; the
 // result lies within one bf16 unit of the single rounding of the exact value.
+// Each thread handles U tokens of a 64-token chunk at once: all code / position loads, then
+// all centroid loads, then the rotations and stores, so the dependent loads overlap.
 template <bool BF16>
 __global__ __launch_bounds__(256) void rope_gather(
     const uint16_t* __restrict__ codes, const int32_t* __restrict__ positions, int64_t heads,
@@ -79,6 +81,7 @@ __global__ __launch_bounds__(256) void rope_gather(
   constexpr int P = BF16 ? 8 : 4;        // pairs per thread
   constexpr int TPT = kHalf / P;         // threads per token
   constexpr int TOK = 256 / TPT;         // tokens per pass of the workgroup
+  constexpr int U = kChunk / TOK;        // tokens per thread per chunk
   using real = typename std::conditional<BF16, float, double>::type;
   const int t = threadIdx.x;
   const int g = t % TPT;                 // pair group: pairs [g*P, g*P + P)
@@ -99,54 +102,68 @@ __global__ __launch_bounds__(256) void rope_gather(
     const int64_t b = rest / chunks;
     const int64_t t0 = (rest % chunks) * kChunk;
     const float* cbh = cb + h * c * kD;
-    for (int base = 0; base < kChunk; base += TOK) {
-      const int64_t tok = t0 + base + tk;
-      if (tok >= n) break;
-      const uint16_t code = codes[(b * heads + h) * n + tok];
-      const int32_t pos = positions[b * n + tok];
-      const int64_t ooff = ((b * heads + h) * n + tok) * kD + i0;
+    int64_t tok[U];
+    int code[U], pos[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      tok[u] = t0 + u * TOK + tk;
+      code[u] = 0;
+      pos[u] = -1;
+      if (tok[u] < n) {
+        code[u] = codes[(b * heads + h) * n + tok[u]];
+        pos[u] = positions[b * n + tok[u]];
+      }
+    }
+    float xl[U][P], xh[U][P];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = tok[u] < n && code[u] < c && pos[u] >= 0;
+      const float* x = cbh + (int64_t)(ok ? code[u] : 0) * kD + i0;
+#pragma unroll
+      for (int k = 0; k < P; k += 4) {
+        const f4 a = *reinterpret_cast<const f4*>(x + k);
+        const f4 bb = *reinterpret_cast<const f4*>(x + kHalf + k);
+        xl[u][k] = a.x; xl[u][k + 1] = a.y; xl[u][k + 2] = a.z; xl[u][k + 3] = a.w;
+        xh[u][k] = bb.x; xh[u][k + 1] = bb.y; xh[u][k + 2] = bb.z; xh[u][k + 3] = bb.w;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (tok[u] >= n) continue;
+      const int64_t ooff = ((b * heads + h) * n + tok[u]) * kD + i0;
       real lo[P], hi[P];
-      if ((int64_t)code >= c || pos < 0) {
+      if ((int64_t)code[u] >= c || pos[u] < 0) {
 #pragma unroll
         for (int k = 0; k < P; ++k) lo[k] = hi[k] = (real)NAN;
       } else {
-        const float* x = cbh + (int64_t)code * kD + i0;
-        float xl[P], xh[P];
-#pragma unroll
-        for (int k = 0; k < P; k += 4) {
-          const f4 a = *reinterpret_cast<const f4*>(x + k);
-          const f4 bb = *reinterpret_cast<const f4*>(x + kHalf + k);
-          xl[k] = a.x; xl[k + 1] = a.y; xl[k + 2] = a.z; xl[k + 3] = a.w;
-          xh[k] = bb.x; xh[k + 1] = bb.y; xh[k + 2] = bb.z; xh[k + 3] = bb.w;
-        }
-        const int64_t delta = cur - (int64_t)pos;
+        const int64_t delta = cur - (int64_t)pos[u];
         if (delta >= 0 && delta < window) {
           const d2* row = table + delta * kHalf + i0;  // delta < rows_near since pos >= 0
 #pragma unroll
           for (int k = 0; k < P; ++k) {
             const d2 v = row[k];
             const real cs = (real)v.x, sn = (real)v.y;
-            lo[k] = (real)xl[k] * cs - (real)xh[k] * sn;
-            hi[k] = (real)xh[k] * cs + (real)xl[k] * sn;
+            lo[k] = (real)xl[u][k] * cs - (real)xh[u][k] * sn;
+            hi[k] = (real)xh[u][k] * cs + (real)xl[u][k] * sn;
           }
         } else {
 #pragma unroll
           for (int k = 0; k < P; ++k) {
-            lo[k] = (real)xl[k] * fc[k] - (real)xh[k] * fs[k];
-            hi[k] = (real)xh[k] * fc[k] + (real)xl[k] * fs[k];
+            lo[k] = (real)xl[u][k] * fc[k] - (real)xh[u][k] * fs[k];
+            hi[k] = (real)xh[u][k] * fc[k] + (real)xl[u][k] * fs[k];
           }
         }
       }
       if (BF16) {
         u4 a, bb;
-        unsigned la[4], lb[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          la[k] = pack_bf16x2((float)lo[2 * k], (float)lo[2 * k + 1]);
-          lb[k] = pack_bf16x2((float)hi[2 * k], (float)hi[2 * k + 1]);
-        }
-        a.x = la[0]; a.y = la[1]; a.z = la[2]; a.w = la[3];
-        bb.x = lb[0]; bb.y = lb[1]; bb.z = lb[2]; bb.w = lb[3];
+        a.x = pack_bf16x2((float)lo[0], (float)lo[1]);
+        a.y = pack_bf16x2((float)lo[2], (float)lo[3]);
+        a.z = pack_bf16x2((float)lo[4], (float)lo[5]);
+        a.w = pack_bf16x2((float)lo[6], (float)lo[7]);
+        bb.x = pack_bf16x2((float)hi[0], (float)hi[1]);
+        bb.y = pack_bf16x2((float)hi[2], (float)hi[3]);
+        bb.z = pack_bf16x2((float)hi[4], (float)hi[5]);
+        bb.w = pack_bf16x2((float)hi[6], (float)hi[7]);
         uint16_t* o = static_cast<uint16_t*>(out) + ooff;
         __builtin_nontemporal_store(a, reinterpret_cast<u4*>(o));
         __builtin_nontemporal_store(bb, reinterpret_cast<u4*>(o + kHalf));

@@ -221,9 +221,9 @@ __global__ __launch_bounds__(256) void sel_hist(const unsigned* __restrict__ sco
   const int n_r = info[head].n_r;
   unsigned s16 = 0;
   // thread t owns bins [kBins - 16(t+1), kBins - 16t), i.e. descending ranges
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 16; ++i) {  // plain loads: the fence above made the atomics visible
     int b = kBins - 16 * (t + 1) + i;
-    unsigned c = atomic_load_u32(&hist[(int64_t)head * kBins + b]);
+    unsigned c = hist[(int64_t)head * kBins + b];
     lh[b] = c;
     s16 += c;
   }
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ 
   if (!is_last) return;
   __threadfence();
   // Last workgroup of this head: exact radix select of the r-th largest candidate key.
-  const int n_cand = (int)atomic_load_u32((const unsigned*)&info[head].n_cand);
+  const int n_cand = (int)info[head].n_cand;  // visible after the acquire fence above
   const int r = info[head].n_r - info[head].count_above;  // 1-based rank inside bin b*
   __shared__ unsigned dh[256];
   __shared__ unsigned long long s_prefix;
@@ -321,8 +321,7 @@ __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ 
     // bitonic sort of the candidate keys, descending; the r-th is the threshold
     int P = 1;
     while (P < n_cand) P <<= 1;
-    for (int i = t; i < P; i += 256)
-      sk[i] = i < n_cand ? __hip_atomic_load(&ch[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+    for (int i = t; i < P; i += 256) sk[i] = i < n_cand ? ch[i] : 0ull;
     __syncthreads();
     for (int k = 2; k <= P; k <<= 1) {
       for (int j = k >> 1; j > 0; j >>= 1) {
@@ -347,8 +346,7 @@ __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ 
       dh[t] = 0u;
       __syncthreads();
       for (int i = t; i < n_cand; i += 256) {
-        unsigned long long kv = __hip_atomic_load(&ch[i], __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long kv = ch[i];
         if ((kv & mask) == prefix) atomicAdd(&dh[(kv >> shift) & 0xFF], 1u);
       }
       __syncthreads();
@@ -379,8 +377,7 @@ __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ 
   const unsigned long long thr = (r > 0) ? prefix : ~0ull;
   if (r > 0) {
     for (int i = t; i < n_cand; i += 256) {
-      unsigned long long kv = __hip_atomic_load(&ch[i], __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned long long kv = ch[i];
       if (kv >= thr) {
         int64_t idx = (int64_t)(0xFFFFFFFFu - (unsigned)(kv & 0xFFFFFFFFull));
         atomicAdd(&sel_extra[(int64_t)head * nblk + idx / kBlock], 1u);
@@ -389,14 +386,30 @@ __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ 
   }
   __threadfence();
   __syncthreads();
-  if (t == 0) {
-    unsigned run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      unsigned cnt = atomic_load_u32(&above_blk[(int64_t)head * nblk + b]) +
-                     atomic_load_u32(&sel_extra[(int64_t)head * nblk + b]);
-      sel_extra[(int64_t)head * nblk + b] = run;  // becomes the exclusive offset
-      run += cnt;
+  // exclusive offsets over the blocks: counts loaded in parallel (atomic loads for the
+  // counters this workgroup just incremented), then a serial prefix in LDS, 256 at a time
+  __shared__ unsigned cbuf[256];
+  __shared__ unsigned s_run;
+  if (t == 0) s_run = 0u;
+  for (int b0 = 0; b0 < nblk; b0 += 256) {
+    const int b = b0 + t;
+    if (b < nblk)
+      cbuf[t] = above_blk[(int64_t)head * nblk + b] +
+                atomic_load_u32(&sel_extra[(int64_t)head * nblk + b]);
+    __syncthreads();
+    if (t == 0) {
+      unsigned run = s_run;
+      const int m = nblk - b0 < 256 ? nblk - b0 : 256;
+      for (int k = 0; k < m; ++k) {
+        const unsigned cnt = cbuf[k];
+        cbuf[k] = run;
+        run += cnt;
+      }
+      s_run = run;
     }
+    __syncthreads();
+    if (b < nblk) sel_extra[(int64_t)head * nblk + b] = cbuf[t];  // the exclusive offset
+    __syncthreads();
   }
 }
 
