@@ -100,6 +100,7 @@ __global__ __launch_bounds__(256) void cal_cholesky(const float* __restrict__ h,
   const int head = blockIdx.x;
   const int t = threadIdx.x;
   const float* hh = h + (int64_t)head * d * d;
+#pragma unroll 8
   for (int e = t; e < d * d; e += 256) {
     int i = e / d, k = e % d;
     A[i * ld + k] = (double)hh[e];

@@ -17,7 +17,8 @@
 // it; close calls are settled by exact fp64 scores, and whatever is still open is rescanned.
 //
 // Kernels (in launch order)
-//   enc_prep_rows       w = c L, v = w L^T, b = ||w||^2 in fp64, per-workgroup maxima.
+//   enc_prep_gram       M = L L^T in fp64 (H-weighted only).
+//   enc_prep_rows       v = c M, b = v . c in fp64 (fp64 MFMA), per-workgroup maxima.
 //   enc_prep_frag       fp16 fragments of S v in MFMA A-operand order, fp32 bias -S b / 2 per
 //                       accumulator slot, per-workgroup rho / nu; optional fp16 hi/lo
 //                       fragments of L^T for ||kL||^2; clears the list counters.
@@ -51,9 +52,9 @@ constexpr float kPadBias = -1.0e38f;      // bias of padding rows: finite, never
 
 struct Counters {
   unsigned refine_x[8][16];  // refine list entries per XCD region (counters 64 B apart)
-  unsigned stat_x[8][16];    // keys and direct decisions per XCD (when statistics are asked)
+  unsigned stat_x[8][16];    // keys, direct decisions, reranks per XCD (statistics only)
   unsigned full;             // full-scan list entries
-  unsigned stats[8];         // [2] reranked, [3] rescanned, [4] full scan
+  unsigned stats[8];         // [3] rescanned, [4] full scan
   unsigned unc[1];           // per-head rescan list lengths follow (heads entries)
 };
 
@@ -121,122 +122,142 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // ------------------------------------------------------------------ prep
-// 32 rows per workgroup.  L (fp32) and the rows in LDS; w = c L then v = w L^T in fp64,
-// each thread owning 4 rows x 4 columns.  Writes v (fp64 and fp32), b, and this
-// workgroup's max |v| and max b; workgroup 0 of a head also records max |L|.
+typedef double d4 __attribute__((ext_vector_type(4)));
+
+// M = L L^T (fp64, symmetric) of one head, 8 rows of M per workgroup; workgroup 0 of a head
+// also records max |L| in the head's first prep_rows partial.
+__global__ __launch_bounds__(256) void enc_prep_gram(const float* __restrict__ chol,
+                                                     double* __restrict__ gram,
+                                                     float* __restrict__ part_a, int nwg) {
+  __shared__ float Ls[kD * kLd];
+  __shared__ float red[4];
+  const int head = blockIdx.y, rb = blockIdx.x, t = threadIdx.x;
+  const float* L = chol + (int64_t)head * kD * kD;
+  float lmax = 0.f;
+#pragma unroll 16
+  for (int e = t; e < kD * kD; e += 256) {
+    const float x = L[e];
+    Ls[(e / kD) * kLd + e % kD] = x;
+    lmax = fmaxf(lmax, fabsf(x));
+  }
+  __syncthreads();
+  const int bcol = t % kD;          // column b of M
+  const int a0 = rb * 8 + (t / kD) * 4;  // rows a0 .. a0+3
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int k = 0; k < kD; ++k) {
+    const double lb = (double)Ls[bcol * kLd + k];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += (double)Ls[(a0 + i) * kLd + k] * lb;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) gram[((int64_t)head * kD + a0 + i) * kD + bcol] = acc[i];
+  if (rb == 0) {
+    for (int o = 32; o > 0; o >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, o));
+    if ((t & 63) == 0) red[t >> 6] = lmax;
+    __syncthreads();
+    if (t == 0) part_a[((int64_t)head * nwg) * 4 + 2] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  }
+}
+
+// 32 codebook rows per workgroup: v = c M (fp64 MFMA, M = L L^T; v = c without L) and
+// b = v . c (= ||c L||^2), written as fp64 and fp32, plus this workgroup's max |v| and
+// max b.  Wave w computes columns 32w .. 32w+31 as 2 x 2 tiles of 16 x 16.
 __global__ __launch_bounds__(256) void enc_prep_rows(const float* __restrict__ cb, int64_t c,
-                                                     const float* __restrict__ chol,
+                                                     const double* __restrict__ gram,
                                                      double* __restrict__ v64,
                                                      float* __restrict__ v32,
                                                      double* __restrict__ b64,
                                                      float* __restrict__ part_a, int nwg) {
-  extern __shared__ double sm[];
-  double* w = sm;                                             // [32][128] fp64
-  float* Ls = reinterpret_cast<float*>(sm + 32 * kD);         // [128][129] fp32 (with L)
-  float* cr = Ls + (chol ? kD * kLd : 0);                     // [32][128] fp32
-  __shared__ float red[3][4];
+  __shared__ float cr[32 * kD];
+  __shared__ double bsum[4][32];
+  __shared__ float red[2][4];
   const int head = blockIdx.y;
   const int64_t j0 = (int64_t)blockIdx.x * 32;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const float* cbh = cb + (int64_t)head * c * kD;
-  const float* L = chol ? chol + (int64_t)head * kD * kD : nullptr;
-  float lmax = 0.f;
-  if (L)
-    for (int e = t; e < kD * kD; e += 256) {
-      Ls[(e / kD) * kLd + e % kD] = L[e];
-      lmax = fmaxf(lmax, fabsf(L[e]));
-    }
+#pragma unroll
   for (int e = t; e < 32 * kD; e += 256) {
-    int r = e / kD, a = e % kD;
+    const int r = e / kD, a = e % kD;
     cr[e] = (j0 + r < c) ? cbh[(j0 + r) * kD + a] : 0.f;
   }
   __syncthreads();
-  const int rg = t / 32;  // rows rg*4 .. rg*4+3
-  const int cg = t % 32;  // columns cg + 32m
-  double acc[4][4];
-  if (L) {
-    // w[r][a] = sum_b c[r][b] L[b][a]   (L is lower triangular: zeros above the diagonal)
+  // acc[rt][ct][r]: row 16 rt + 4 r + lane / 16, column 32 wave + 16 ct + lane % 16
+  d4 acc[2][2];
+  if (gram) {
+    const double* M = gram + (int64_t)head * kD * kD;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) acc[i][m] = 0.0;
-    for (int b = 0; b < kD; ++b) {
-      double cv[4], lv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) cv[i] = (double)cr[(rg * 4 + i) * kD + b];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) lv[m] = (double)Ls[b * kLd + cg + 32 * m];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc[i][m] += cv[i] * lv[m];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) w[(rg * 4 + i) * kD + cg + 32 * m] = acc[i][m];
-    __syncthreads();
-    // v[r][a] = sum_b w[r][b] L[a][b]
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) acc[i][m] = 0.0;
-    for (int b = 0; b < kD; ++b) {
-      double wv[4], lv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wv[i] = w[(rg * 4 + i) * kD + b];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) lv[m] = (double)Ls[(cg + 32 * m) * kLd + b];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc[i][m] += wv[i] * lv[m];
+      for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = d4{0.0, 0.0, 0.0, 0.0};
+    const int li = lane % 16, lk = lane / 16;
+    for (int k0 = 0; k0 < kD; k0 += 4) {
+      const double a0 = (double)cr[li * kD + k0 + lk];
+      const double a1 = (double)cr[(16 + li) * kD + k0 + lk];
+      const double b0 = M[(k0 + lk) * kD + 32 * wave + li];
+      const double b1 = M[(k0 + lk) * kD + 32 * wave + 16 + li];
+      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        acc[i][m] = (double)cr[(rg * 4 + i) * kD + cg + 32 * m];
-        w[(rg * 4 + i) * kD + cg + 32 * m] = acc[i][m];
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[rt][ct][r] = (double)cr[(16 * rt + 4 * r + lane / 16) * kD + 32 * wave + 16 * ct + lane % 16];
+  }
+  float vmax = 0.f;
+  double bp[2][4];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * rt + 4 * r + lane / 16;
+      const int64_t j = j0 + row;
+      double p = 0.0;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const int col = 32 * wave + 16 * ct + lane % 16;
+        const double x = acc[rt][ct][r];
+        p += x * (double)cr[row * kD + col];
+        if (j < c) {
+          v64[((int64_t)head * c + j) * kD + col] = x;
+          v32[((int64_t)head * c + j) * kD + col] = (float)x;
+          vmax = fmaxf(vmax, round_up_f(fabs(x)));
+        }
       }
-  }
-  float vmax = 0.f, bmax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t j = j0 + rg * 4 + i;
-    double bp = 0.0;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const double wv = w[(rg * 4 + i) * kD + cg + 32 * m];
-      bp += wv * wv;
+      bp[rt][r] = p;
     }
-    for (int o = 16; o > 0; o >>= 1) bp += __shfl_xor(bp, o);  // the 32 lanes of this row group
-    if (j < c) {
+  // b: sum over the 16 lanes of a row, then over the four waves
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        v64[((int64_t)head * c + j) * kD + cg + 32 * m] = acc[i][m];
-        v32[((int64_t)head * c + j) * kD + cg + 32 * m] = (float)acc[i][m];
-        vmax = fmaxf(vmax, round_up_f(fabs(acc[i][m])));
-      }
-      if (cg == 0) b64[(int64_t)head * c + j] = bp;
-      bmax = fmaxf(bmax, round_up_f(bp));
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      double p = bp[rt][r];
+      for (int o = 8; o > 0; o >>= 1) p += __shfl_xor(p, o);
+      if (lane % 16 == 0) bsum[wave][16 * rt + 4 * r + lane / 16] = p;
     }
-  }
-  for (int o = 32; o > 0; o >>= 1) {
-    vmax = fmaxf(vmax, __shfl_xor(vmax, o));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, o));
-    lmax = fmaxf(lmax, __shfl_xor(lmax, o));
-  }
-  if ((t & 63) == 0) {
-    red[0][t >> 6] = vmax;
-    red[1][t >> 6] = bmax;
-    red[2][t >> 6] = lmax;
-  }
+  for (int o = 32; o > 0; o >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, o));
+  if (lane == 0) red[0][wave] = vmax;
   __syncthreads();
-  if (t < 3)
-    part_a[((int64_t)head * nwg + blockIdx.x) * 4 + t] =
-        fmaxf(fmaxf(red[t][0], red[t][1]), fmaxf(red[t][2], red[t][3]));
+  float bmax = 0.f;
+  if (t < 32) {
+    const double bj = ((bsum[0][t] + bsum[1][t]) + bsum[2][t]) + bsum[3][t];
+    if (j0 + t < c) {
+      b64[(int64_t)head * c + j0 + t] = bj;
+      bmax = round_up_f(bj);
+    }
+    for (int o = 16; o > 0; o >>= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, o));
+  }
+  if (t == 0) {
+    float* pa = part_a + ((int64_t)head * nwg + blockIdx.x) * 4;
+    pa[0] = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    pa[1] = bmax;
+    if (!gram) pa[2] = 0.f;  // no L: max |L| unused
+  }
 }
 
 // Head constants from the prep_rows partials.
@@ -246,11 +267,30 @@ struct HeadScale {
   float SL;     // L-side scale
 };
 
-__device__ HeadScale head_scale(const float* part_a, int64_t head, int nwg) {
+// Scales of one head from the prep_rows partial maxima; every thread of the workgroup calls
+// it (a workgroup reduction).
+__device__ HeadScale head_scale_wg(const float* part_a, int64_t head, int nwg) {
+  __shared__ float red[2][4];
+  const int t = threadIdx.x;
   float a = 0.f, b = 0.f;
-  for (int i = 0; i < nwg; ++i) {
+  for (int i = t; i < nwg; i += blockDim.x) {
     a = fmaxf(a, part_a[(head * nwg + i) * 4 + 0]);
     b = fmaxf(b, part_a[(head * nwg + i) * 4 + 1]);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    a = fmaxf(a, __shfl_xor(a, o));
+    b = fmaxf(b, __shfl_xor(b, o));
+  }
+  __syncthreads();
+  if ((t & 63) == 0) {
+    red[0][t >> 6] = a;
+    red[1][t >> 6] = b;
+  }
+  __syncthreads();
+  const int nw = (int)(blockDim.x + 63) / 64;
+  for (int w = 0; w < nw; ++w) {
+    a = fmaxf(a, red[0][w]);
+    b = fmaxf(b, red[1][w]);
   }
   HeadScale h;
   h.S = scale_for(a);
@@ -270,12 +310,14 @@ __global__ __launch_bounds__(256) void enc_prep_frag(const double* __restrict__ 
                                                      half8* __restrict__ v16,
                                                      float* __restrict__ bias,
                                                      half8* __restrict__ lfrag,
-                                                     unsigned* __restrict__ cnt, int ncnt) {
+                                                     unsigned* __restrict__ cnt, int ncnt,
+                                                     HeadScale* __restrict__ hsc) {
   const int head = blockIdx.y;
   const int t = threadIdx.x;
   if (head == 0 && blockIdx.x == 0)
     for (int i = t; i < ncnt; i += 256) cnt[i] = 0u;
-  const HeadScale hs = head_scale(part_a, head, nwg_a);
+  const HeadScale hs = head_scale_wg(part_a, head, nwg_a);
+  if (blockIdx.x == 0 && t == 0) hsc[head] = hs;  // for the later passes
   const int64_t rows = (int64_t)T * kRows;
   const int64_t rid = (int64_t)blockIdx.x * 16 + t / 16;  // padded row (or L^T row after rows)
   const int chunk = t % 16;                                // k = 8 chunk .. 8 chunk + 7
@@ -499,7 +541,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int64_t heads, int nkb, int T, int tbits, const half8* __restrict__ v16,
     const float* __restrict__ bias, const float* __restrict__ v32,
     const double* __restrict__ b64, int64_t c, const half8* __restrict__ lfrag,
-    const float* __restrict__ part_a, int nwg_a, const float* __restrict__ part_b, int nwg_b,
+    const HeadScale* __restrict__ hsc, const float* __restrict__ part_b, int nwg_b,
     float* __restrict__ znorm, uint16_t* __restrict__ codes, float* __restrict__ dist,
     RefEntry* __restrict__ refl, FullEntry* __restrict__ full, Counters* __restrict__ cnt,
     int want_stats) {
@@ -514,7 +556,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t kb = wk % nkb;
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, col = lane & 31, hh = lane >> 5;
-  const HeadScale hs = head_scale(part_a, head, nwg_a);
+  const HeadScale hs = hsc[head];
   {  // rho and nu: maxima over the prep_frag partials of this head
     float rr = 0.f, nn = 0.f;
     for (int i = t; i < nwg_b; i += 256) {
@@ -817,57 +859,113 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ------------------------------------------------------------------ fp64 rerank
-// Two entries per wave, 32 lanes each: lanes 0-15 score j0, lanes 16-31 score j1.
+// Exact fp64 score of one candidate, 8 lanes cooperating (lane g of the group owns dims
+// 16g .. 16g+15).  Returns the score (valid in every lane of the group) and, in z2, ||k||^2.
+template <int DT, typename VT>
+__device__ __forceinline__ double coop_score8(const void* keys, int64_t off_key, const VT* vrow,
+                                              double bj, int g, double* z2) {
+  double x[16];
+  if (DT == A2ATS_BF16) {
+    const uint4* kp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(keys) + off_key + 16 * g);
+    const uint4 r0 = kp[0], r1 = kp[1];
+    const unsigned wv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[2 * e] = (double)__uint_as_float(wv[e] << 16);
+      x[2 * e + 1] = (double)__uint_as_float(wv[e] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* kp = reinterpret_cast<const float4*>(static_cast<const float*>(keys) + off_key + 16 * g);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 a = kp[q];
+      x[4 * q] = a.x; x[4 * q + 1] = a.y; x[4 * q + 2] = a.z; x[4 * q + 3] = a.w;
+    }
+  }
+  double v[16];
+  if (sizeof(VT) == 8) {
+    const double2* v2 = reinterpret_cast<const double2*>(vrow + 16 * g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double2 vv = v2[e];
+      v[2 * e] = vv.x;
+      v[2 * e + 1] = vv.y;
+    }
+  } else {
+    const float4* v4 = reinterpret_cast<const float4*>(vrow + 16 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float4 vv = v4[e];
+      v[4 * e] = vv.x; v[4 * e + 1] = vv.y; v[4 * e + 2] = vv.z; v[4 * e + 3] = vv.w;
+    }
+  }
+  double s = 0.0, k2 = 0.0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    s += x[e] * v[e];
+    k2 += x[e] * x[e];
+  }
+  for (int o = 4; o > 0; o >>= 1) {
+    s += __shfl_xor(s, o);
+    k2 += __shfl_xor(k2, o);
+  }
+  *z2 = k2;
+  return s - 0.5 * bj;
+}
+
+// Four entries per wave, 16 lanes each: lanes 0-7 of a group score j0, lanes 8-15 j1.  The
+// workgroups on XCD x take the entries of list region x (listed by the coarse pass on that
+// XCD, so the heads whose rows they read are the ones cached in that XCD's L2).  Without L
+// the rows are the fp32 codebook itself (v = c exactly), half the bytes of the fp64 copy.
 template <int DT>
 __global__ __launch_bounds__(256) void enc_refine(
     const void* __restrict__ keys, int64_t n, int64_t c, const double* __restrict__ v64,
+    const float* __restrict__ v32, int plain,
     const double* __restrict__ b64, const RefEntry* __restrict__ refl, uint16_t* __restrict__ codes,
     float* __restrict__ dist, UncEntry* __restrict__ unc, int64_t unc_cap,
-    FullEntry* __restrict__ full, Counters* __restrict__ cnt, int64_t region) {
+    FullEntry* __restrict__ full, Counters* __restrict__ cnt, int64_t region, int want_stats) {
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int sub = lane >> 5;          // which entry of the wave
-  const int which = (lane >> 4) & 1;  // candidate 0 or 1
-  const int g = lane & 15;
+  const int sub = lane >> 4;          // which entry of the wave
+  const int which = (lane >> 3) & 1;  // candidate 0 or 1
+  const int g = lane & 7;
   // the list is 8 regions of `region` entries, region x holding cnt->refine_x[x][0]
-  unsigned rc[8], total = 0u;
-#pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    rc[x] = cnt->refine_x[x][0];
-    total += rc[x];
-  }
-  const int64_t stride = (int64_t)gridDim.x * 8;
+  const int xcd = blockIdx.x % 8;
+  const unsigned total = cnt->refine_x[xcd][0];
+  const RefEntry* reg = refl + (int64_t)xcd * region;
+  const int64_t stride = (int64_t)(gridDim.x / 8) * 16;
   unsigned decided = 0;
-  for (int64_t e0 = (int64_t)blockIdx.x * 8 + (t >> 6) * 2; e0 < (int64_t)total; e0 += stride) {
+  for (int64_t e0 = (int64_t)(blockIdx.x / 8) * 16 + (t >> 6) * 4; e0 < (int64_t)total; e0 += stride) {
     const int64_t e = e0 + sub;
     const bool live = e < (int64_t)total;
-    RefEntry re;
-    re.head = 0;
-    re.row = 0;
-    re.j0 = re.j1 = -1;
+    const RefEntry* rp = reg + (live ? e : 0);
+    int32_t head = 0, row = 0, ja = -1, jb = -1;
+    double thr = 0.0;
+    float rz2 = -1.f;
     if (live) {
-      int x = 0;
-      unsigned off = (unsigned)e;
-#pragma unroll
-      for (int y = 0; y < 7; ++y) {
-        const bool on = x == y && off >= rc[y];
-        off = on ? off - rc[y] : off;
-        x = on ? y + 1 : x;
+      const int2 hr = *reinterpret_cast<const int2*>(&rp->head);
+      const int2 jj = *reinterpret_cast<const int2*>(&rp->j0);
+      head = hr.x;
+      row = hr.y;
+      ja = jj.x;
+      jb = jj.y;
+      if ((lane & 15) == 0) {
+        thr = rp->thr;
+        rz2 = rp->z2;
       }
-      re = refl[(int64_t)x * region + off];
     }
-    const int j = live ? (which ? re.j1 : re.j0) : -1;
+    const int j = which ? jb : ja;
     double s = -INFINITY, k2 = 0.0;
     if (j >= 0) {
-      const int64_t off = ((int64_t)re.head * n + re.row) * kD;
-      s = coop_score<DT>(keys, off, v64 + ((int64_t)re.head * c + j) * kD,
-                         b64[(int64_t)re.head * c + j], g, &k2);
+      const int64_t off = ((int64_t)head * n + row) * kD;
+      const int64_t vo = ((int64_t)head * c + j) * kD;
+      s = plain ? coop_score8<DT>(keys, off, v32 + vo, b64[(int64_t)head * c + j], g, &k2)
+                : coop_score8<DT>(keys, off, v64 + vo, b64[(int64_t)head * c + j], g, &k2);
     }
-    const double s_other = __shfl_xor(s, 16);
-    const double k2_other = __shfl_xor(k2, 16);
-    if (live && (lane & 31) == 0) {
-      const int ja = re.j0, jb = re.j1;  // lane 0 of the group scored ja, lane 16 jb
-      const double sa = s, sb = s_other;
+    const double s_other = __shfl_xor(s, 8);
+    const double k2_other = __shfl_xor(k2, 8);
+    if (live && (lane & 15) == 0) {
+      const double sa = s, sb = s_other;  // lane 0 of the group scored ja, lane 8 jb
       if (ja < 0) k2 = k2_other;
       int best = ja;
       double sbest = sa;
@@ -875,36 +973,43 @@ __global__ __launch_bounds__(256) void enc_refine(
         best = jb;
         sbest = sb;
       }
-      const double z2 = re.z2 >= 0.f ? (double)re.z2 : k2;
+      const double z2 = rz2 >= 0.f ? (double)rz2 : k2;
       const double eps = 0x1p-40 * (fabs(sbest) + k2 + 1.0);
-      if (best >= 0 && sbest - eps > re.thr) {
-        codes[(int64_t)re.head * n + re.row] = (uint16_t)best;
-        if (dist) dist[(int64_t)re.head * n + re.row] = (float)fmax(z2 - 2.0 * sbest, 0.0);
+      if (best >= 0 && sbest - eps > thr) {
+        codes[(int64_t)head * n + row] = (uint16_t)best;
+        if (dist) dist[(int64_t)head * n + row] = (float)fmax(z2 - 2.0 * sbest, 0.0);
         decided += 1;
       } else {
-        const unsigned slot = atomicAdd(&cnt->unc[re.head], 1u);
+        const unsigned slot = atomicAdd(&cnt->unc[head], 1u);
         if (best >= 0 && slot < unc_cap) {
           UncEntry ue;
-          ue.row = re.row;
+          ue.row = row;
           ue.jbest = best;
           ue.sbest = sbest;
-          ue.e_unscaled = re.e_unscaled;
-          ue.z2 = re.z2;
+          ue.e_unscaled = rp->e_unscaled;
+          ue.z2 = rz2;
           ue.pad = 0;
-          unc[(int64_t)re.head * unc_cap + slot] = ue;
+          unc[(int64_t)head * unc_cap + slot] = ue;
         } else {
           FullEntry fe;
-          fe.head = re.head;
-          fe.row = re.row;
-          fe.z2 = re.z2;
+          fe.head = head;
+          fe.row = row;
+          fe.z2 = rz2;
           fe.pad = 0;
           full[atomicAdd(&cnt->full, 1u)] = fe;
         }
       }
     }
   }
-  for (int o = 32; o > 0; o >>= 1) decided += __shfl_xor(decided, o);
-  if (lane == 0 && decided) atomicAdd(&cnt->stats[2], decided);
+  if (want_stats) {  // one atomic per workgroup, per-XCD counter
+    __shared__ unsigned s_dec;
+    if (t == 0) s_dec = 0u;
+    __syncthreads();
+    for (int o = 32; o > 0; o >>= 1) decided += __shfl_xor(decided, o);
+    if (lane == 0 && decided) atomicAdd(&s_dec, decided);
+    __syncthreads();
+    if (t == 0 && s_dec) atomicAdd(&cnt->stat_x[xcd][2], s_dec);
+  }
 }
 
 // Number of listed open keys of a head (capped to the list capacity).
@@ -970,7 +1075,7 @@ template <int DT>
 __global__ __launch_bounds__(256) void enc_rescan_collect(
     const void* __restrict__ keys, int64_t n, int64_t heads, int T, int64_t c,
     const half8* __restrict__ v16, const float* __restrict__ bias,
-    const float* __restrict__ part_a, int nwg_a, const UncEntry* __restrict__ unc,
+    const HeadScale* __restrict__ hsc, const UncEntry* __restrict__ unc,
     int64_t unc_cap, const Counters* __restrict__ cnt, unsigned* __restrict__ cand_n,
     int32_t* __restrict__ cand) {
   const int t = threadIdx.x, lane = t & 63, col = lane & 31, hh = lane >> 5;
@@ -991,7 +1096,7 @@ __global__ __launch_bounds__(256) void enc_rescan_collect(
     ue.sbest = 0.0;
     ue.e_unscaled = 0.0;
     if (live) ue = unc[head * unc_cap + slot];
-    const HeadScale hs = head_scale(part_a, head, nwg_a);
+    const HeadScale hs = hsc[head];
     const int64_t row[1] = {live ? (int64_t)ue.row : -1};
     KeyFrags<1> kf;
     load_key_frags<DT, 1>(keys, head, n, row, hh, kf);
@@ -1196,7 +1301,9 @@ __global__ void enc_stats_out(const Counters* __restrict__ cnt, a2ats_encode_sta
     }
     out->keys = keys;
     out->direct = direct;
-    out->reranked = cnt->stats[2];
+    unsigned reranked = 0;
+    for (int x = 0; x < 8; ++x) reranked += cnt->stat_x[x][2];
+    out->reranked = reranked;
     out->rescanned = cnt->stats[3];
     out->full_scan = cnt->stats[4];
     out->reserved[0] = listed;
@@ -1233,6 +1340,8 @@ struct EncLayout {
   unsigned* cand_n;
   int32_t* cand;
   float* znorm;
+  HeadScale* hsc;
+  double* gram;
   int nwg_a, nwg_b, ncnt;
   int64_t unc_cap;
   size_t bytes;
@@ -1258,6 +1367,8 @@ EncLayout carve(void* ws, int64_t heads, int64_t n, int64_t c) {
   L.lfrag = cv.take<half8>((size_t)heads * 8 * kFragPerTile);
   L.part_a = cv.take<float>((size_t)heads * L.nwg_a * 4);
   L.part_b = cv.take<float>((size_t)heads * L.nwg_b * 2);
+  L.hsc = cv.take<HeadScale>((size_t)heads);
+  L.gram = cv.take<double>((size_t)heads * kD * kD);
   L.cnt = cv.take<unsigned>((size_t)L.ncnt);
   L.refl = cv.take<RefEntry>((size_t)refine_regions(heads, n) * 8 * kKeysPerWG);
   L.unc = cv.take<UncEntry>((size_t)heads * L.unc_cap);
@@ -1279,15 +1390,16 @@ int encode_typed(const void* keys, int64_t heads, int64_t n, const int32_t* idx,
   while ((1 << (tbits - 1)) < T) ++tbits;
   const bool plain = chol == nullptr;
   Counters* cnt = reinterpret_cast<Counters*>(L.cnt);
-  const size_t sm_rows = 32 * kD * sizeof(double) + (plain ? 0 : kD * kLd * sizeof(float)) +
-                         32 * kD * sizeof(float);
-  A2ATS_TRY(set_dynamic_lds(enc_prep_rows, sm_rows));
+  if (!plain)
+    A2ATS_TRY(launch("encode_prep_gram", enc_prep_gram, dim3(kD / 8, (unsigned)heads), dim3(256), 0, s,
+                     chol, L.gram, L.part_a, L.nwg_a));
   A2ATS_TRY(launch("encode_prep_rows", enc_prep_rows, dim3((unsigned)L.nwg_a, (unsigned)heads),
-                   dim3(256), sm_rows, s, codebook, c, chol, L.v64, L.v32, L.b64, L.part_a, L.nwg_a));
+                   dim3(256), 0, s, codebook, c, plain ? nullptr : L.gram, L.v64, L.v32, L.b64,
+                   L.part_a, L.nwg_a));
   const bool znorm_mfma = dist && !plain && DT == A2ATS_BF16;
   A2ATS_TRY(launch("encode_prep_frag", enc_prep_frag, dim3((unsigned)L.nwg_b, (unsigned)heads),
                    dim3(256), 0, s, L.v64, L.b64, c, T, chol, (int)znorm_mfma, L.part_a, L.nwg_a,
-                   L.part_b, L.v16, L.bias, L.lfrag, L.cnt, L.ncnt));
+                   L.part_b, L.v16, L.bias, L.lfrag, L.cnt, L.ncnt, L.hsc));
   // the rescan candidate counters start at zero (a fill kernel, not a memset node)
   A2ATS_TRY(launch("encode_clear", enc_clear_u32, dim3(grid_for(heads * L.unc_cap, 256, 1024)),
                    dim3(256), 0, s, L.cand_n, heads * L.unc_cap));
@@ -1304,17 +1416,21 @@ int encode_typed(const void* keys, int64_t heads, int64_t n, const int32_t* idx,
   const char* name = plain ? "encode_coarse_plain" : "encode_coarse_h";
 #define A2ATS_COARSE(Z, DI)                                                                       \
   launch(name, enc_coarse<DT, Z, DI>, dim3((unsigned)G), dim3(256), 0, s, keys, n, idx, n_sel,   \
-         heads, nkb, T, tbits, L.v16, L.bias, L.v32, L.b64, c, L.lfrag, L.part_a, L.nwg_a,        \
+         heads, nkb, T, tbits, L.v16, L.bias, L.v32, L.b64, c, L.lfrag, L.hsc,                    \
          L.part_b, L.nwg_b, znorm, codes, dist, L.refl, L.full, cnt, stats ? 1 : 0)
   if (znorm_mfma) A2ATS_TRY(A2ATS_COARSE(true, true));
   else if (dist) A2ATS_TRY(A2ATS_COARSE(false, true));
   else A2ATS_TRY(A2ATS_COARSE(false, false));
 #undef A2ATS_COARSE
-  A2ATS_TRY(launch("encode_refine", enc_refine<DT>, dim3(1024), dim3(256), 0, s, keys, n, c, L.v64,
+  // up to 16 entries per workgroup and pass; at most one entry per key
+  const unsigned rblocks =
+      (unsigned)std::min<int64_t>(2048, std::max<int64_t>(8, (heads * n_sel + 127) / 128 * 8));
+  A2ATS_TRY(launch("encode_refine", enc_refine<DT>, dim3(rblocks), dim3(256), 0, s, keys, n, c, L.v64,
+                   L.v32, plain ? 1 : 0,
                    L.b64, L.refl, codes, dist, L.unc, L.unc_cap, L.full, cnt,
-                   (int64_t)(G / 8) * kKeysPerWG));
+                   (int64_t)(G / 8) * kKeysPerWG, stats ? 1 : 0));
   A2ATS_TRY(launch("encode_rescan_collect", enc_rescan_collect<DT>, dim3(512), dim3(256), 0, s, keys,
-                   n, heads, T, c, L.v16, L.bias, L.part_a, L.nwg_a, L.unc, L.unc_cap, cnt,
+                   n, heads, T, c, L.v16, L.bias, L.hsc, L.unc, L.unc_cap, cnt,
                    L.cand_n, L.cand));
   A2ATS_TRY(launch("encode_rescan_decide", enc_rescan_decide<DT>, dim3(256), dim3(256), 0, s, keys, n,
                    heads, c, L.v64, L.b64, L.unc, L.unc_cap, L.cand_n, L.cand, codes, dist, L.full,
