@@ -21,8 +21,8 @@
 //   enc_prep_rows       v = c M, b = v . c in fp64 (fp64 MFMA), per-workgroup maxima.
 //   enc_prep_frag       fp16 fragments of S v in MFMA A-operand order, fp32 bias -S b / 2 per
 //                       accumulator slot, per-workgroup rho / nu; optional fp16 hi/lo
-//                       fragments of L^T for ||kL||^2; clears the list counters.
-//   enc_clear           zeroes the rescan candidate counters.
+//                       fragments of L^T for ||kL||^2; clears the list and candidate
+//                       counters.
 //   enc_znorm64         ||kL||^2 in fp64 (fp32 keys with distances and L only).
 //   enc_coarse          the MFMA pass; writes directly certified codes, lists the rest.
 //   enc_refine          fp64 scores of the two leading candidates of every listed key.
@@ -47,7 +47,7 @@ constexpr int kFragPerTile = kSteps * 64; // half8 fragments per tile (8 KiB)
 constexpr int kTPS = 4;                   // tiles per LDS stage of the coarse pass
 constexpr int kKeysPerWG = 256;           // 4 waves x 64 keys
 constexpr int kCandCap = 32;              // rescan candidates per key
-constexpr int kRescanTiles = 8;           // tiles per rescan work item
+constexpr int kRescanTiles = 2;           // tiles per rescan work item
 constexpr float kPadBias = -1.0e38f;      // bias of padding rows: finite, never competitive
 
 struct Counters {
@@ -311,11 +311,17 @@ __global__ __launch_bounds__(256) void enc_prep_frag(const double* __restrict__ 
                                                      float* __restrict__ bias,
                                                      half8* __restrict__ lfrag,
                                                      unsigned* __restrict__ cnt, int ncnt,
-                                                     HeadScale* __restrict__ hsc) {
+                                                     HeadScale* __restrict__ hsc,
+                                                     unsigned* __restrict__ cand_n, int64_t ncand) {
   const int head = blockIdx.y;
   const int t = threadIdx.x;
   if (head == 0 && blockIdx.x == 0)
     for (int i = t; i < ncnt; i += 256) cnt[i] = 0u;
+  {  // the rescan candidate counters start at zero
+    const int64_t stride = (int64_t)gridDim.x * gridDim.y * 256;
+    for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 256 + t; i < ncand; i += stride)
+      cand_n[i] = 0u;
+  }
   const HeadScale hs = head_scale_wg(part_a, head, nwg_a);
   if (blockIdx.x == 0 && t == 0) hsc[head] = hs;  // for the later passes
   const int64_t rows = (int64_t)T * kRows;
@@ -1104,25 +1110,30 @@ __global__ __launch_bounds__(256) void enc_rescan_collect(
     const float thr = live ? (float)(th - fabs(th) * 0x1p-20 - 1e-30) : INFINITY;
     const half8* vh = v16 + head * (int64_t)T * kFragPerTile;
     const float* bh = bias + head * (int64_t)T * 32;
-    const int tb = chunk * kRescanTiles;
-    const int te = tb + kRescanTiles < T ? tb + kRescanTiles : T;
-    for (int tile = tb; tile < te; ++tile) {
-      const f4* bl = reinterpret_cast<const f4*>(bh + (int64_t)tile * 32 + hh * 16);
-      f16v acc;
+    const int tb = chunk * kRescanTiles;  // T is a multiple of kRescanTiles
+    half8 fa[kRescanTiles][kSteps];
+    f16v acc[kRescanTiles];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f4 b4 = bl[q];
-        acc[4 * q + 0] = b4.x; acc[4 * q + 1] = b4.y; acc[4 * q + 2] = b4.z; acc[4 * q + 3] = b4.w;
+    for (int q = 0; q < kRescanTiles; ++q) {
+      const int64_t tile = tb + q;
+      const f4* bl = reinterpret_cast<const f4*>(bh + tile * 32 + hh * 16);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f4 b4 = bl[k];
+        acc[q][4 * k + 0] = b4.x; acc[q][4 * k + 1] = b4.y; acc[q][4 * k + 2] = b4.z; acc[q][4 * k + 3] = b4.w;
       }
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        const half8 a = vh[(int64_t)tile * kFragPerTile + s * 64 + lane];
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf.f[0][s], acc, 0, 0, 0);
-      }
+      for (int st = 0; st < kSteps; ++st) fa[q][st] = vh[tile * kFragPerTile + st * 64 + lane];
+    }
+#pragma unroll
+    for (int q = 0; q < kRescanTiles; ++q) {
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st)
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[q][st], kf.f[0][st], acc[q], 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        if (acc[r] >= thr) {
-          const int j = tile * kRows + slot_row(r, hh);
+        if (acc[q][r] >= thr) {
+          const int j = (tb + q) * kRows + slot_row(r, hh);
           if (j < c) {
             const unsigned pos = atomicAdd(&cand_n[head * unc_cap + slot], 1u);
             if (pos < (unsigned)kCandCap) cand[(head * unc_cap + slot) * kCandCap + pos] = j;
@@ -1133,15 +1144,16 @@ __global__ __launch_bounds__(256) void enc_rescan_collect(
   }
 }
 
-// One wave per open key: fp64 over its candidates (16 lanes per candidate, 4 at a time).
+// One wave per open key: fp64 over its candidates (8 lanes per candidate, 8 at a time).
 template <int DT>
 __global__ __launch_bounds__(256) void enc_rescan_decide(
     const void* __restrict__ keys, int64_t n, int64_t heads, int64_t c,
-    const double* __restrict__ v64, const double* __restrict__ b64,
+    const double* __restrict__ v64, const float* __restrict__ v32, int plain,
+    const double* __restrict__ b64,
     const UncEntry* __restrict__ unc, int64_t unc_cap, const unsigned* __restrict__ cand_n,
     const int32_t* __restrict__ cand, uint16_t* __restrict__ codes, float* __restrict__ dist,
     FullEntry* __restrict__ full, Counters* __restrict__ cnt) {
-  const int t = threadIdx.x, lane = t & 63, g = lane & 15, q4 = lane >> 4;
+  const int t = threadIdx.x, lane = t & 63, g = lane & 7, q8 = lane >> 3;
   __shared__ int64_t pre[kMaxHeadsLds + 1];
   auto per = [](int64_t m) { return m; };
   const int64_t total = head_prefix(cnt, heads, unc_cap, pre, per);
@@ -1166,21 +1178,23 @@ __global__ __launch_bounds__(256) void enc_rescan_decide(
     const int64_t off = ((int64_t)head * n + ue.row) * kD;
     double best = ue.sbest;
     int bj = ue.jbest;
-    // ||k||^2 (for distances without a precomputed ||kL||^2) and the first batch of scores
+    // ||k||^2 (for distances without a precomputed ||kL||^2) comes with the first batch
     double k2 = 0.0;
-    for (unsigned q0 = 0; q0 < (nc > 0 ? nc : 1u); q0 += 4) {
-      const unsigned q = q0 + q4;
+    for (unsigned q0 = 0; q0 < (nc > 0 ? nc : 1u); q0 += 8) {
+      const unsigned q = q0 + q8;
       double s = -INFINITY, kk = 0.0;
       int j = 0x7FFFFFFF;
       const int jj = q < nc ? cand[slot * kCandCap + q] : ue.jbest;
-      const double sj = coop_score<DT>(keys, off, v64 + ((int64_t)head * c + jj) * kD,
-                                       b64[(int64_t)head * c + jj], g, &kk);
+      const int64_t vo = ((int64_t)head * c + jj) * kD;
+      const double bjj = b64[(int64_t)head * c + jj];
+      const double sj = plain ? coop_score8<DT>(keys, off, v32 + vo, bjj, g, &kk)
+                              : coop_score8<DT>(keys, off, v64 + vo, bjj, g, &kk);
       if (q < nc) {
         s = sj;
         j = jj;
       }
       k2 = kk;
-      for (int o = 16; o < 64; o <<= 1) {
+      for (int o = 8; o < 64; o <<= 1) {
         const double os = __shfl_xor(s, o);
         const int oj = __shfl_xor(j, o);
         if (os > s || (os == s && oj < j)) {
@@ -1284,11 +1298,6 @@ __global__ __launch_bounds__(256) void enc_znorm64(const float* __restrict__ key
     for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
     if (lane == 0) znorm[head * n + row] = (float)part;
   }
-}
-
-__global__ void enc_clear_u32(unsigned* p, int64_t count) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256)
-    p[i] = 0u;
 }
 
 __global__ void enc_stats_out(const Counters* __restrict__ cnt, a2ats_encode_stats* out) {
@@ -1399,10 +1408,8 @@ int encode_typed(const void* keys, int64_t heads, int64_t n, const int32_t* idx,
   const bool znorm_mfma = dist && !plain && DT == A2ATS_BF16;
   A2ATS_TRY(launch("encode_prep_frag", enc_prep_frag, dim3((unsigned)L.nwg_b, (unsigned)heads),
                    dim3(256), 0, s, L.v64, L.b64, c, T, chol, (int)znorm_mfma, L.part_a, L.nwg_a,
-                   L.part_b, L.v16, L.bias, L.lfrag, L.cnt, L.ncnt, L.hsc));
-  // the rescan candidate counters start at zero (a fill kernel, not a memset node)
-  A2ATS_TRY(launch("encode_clear", enc_clear_u32, dim3(grid_for(heads * L.unc_cap, 256, 1024)),
-                   dim3(256), 0, s, L.cand_n, heads * L.unc_cap));
+                   L.part_b, L.v16, L.bias, L.lfrag, L.cnt, L.ncnt, L.hsc, L.cand_n,
+                   heads * L.unc_cap));
   float* znorm = nullptr;
   if (dist && !plain) {
     znorm = L.znorm;
@@ -1433,7 +1440,7 @@ int encode_typed(const void* keys, int64_t heads, int64_t n, const int32_t* idx,
                    n, heads, T, c, L.v16, L.bias, L.hsc, L.unc, L.unc_cap, cnt,
                    L.cand_n, L.cand));
   A2ATS_TRY(launch("encode_rescan_decide", enc_rescan_decide<DT>, dim3(256), dim3(256), 0, s, keys, n,
-                   heads, c, L.v64, L.b64, L.unc, L.unc_cap, L.cand_n, L.cand, codes, dist, L.full,
+                   heads, c, L.v64, L.v32, plain ? 1 : 0, L.b64, L.unc, L.unc_cap, L.cand_n, L.cand, codes, dist, L.full,
                    cnt));
   A2ATS_TRY(launch("encode_fullscan", enc_fullscan<DT>, dim3(128), dim3(256), 0, s, keys, n, c, L.v64,
                    L.b64, codes, dist, L.full, cnt));

@@ -9,16 +9,17 @@
 //
 // Kernels (5 launches, no host round trip):
 //   sel_init     per head: ||q|| and the binning scale; zeroes histograms and counters.
-//   sel_score    HBM-bound pass over the keys (8 keys in flight per 16-lane group,
-//                non-temporal loads): writes u.
-//   sel_hist     4096-bin histogram of a monotone binning of s/||q|| in [-1, 1] from the
-//                L2/MALL-resident scores, 16 workgroups per head (few same-address atomics);
-//                the last workgroup of each head (fenced atomic counter, no waiting) finds
-//                the bin b* that holds the n_r-th largest score.
+//   sel_score    HBM-bound pass over the keys (8 lanes per key, 4 keys in flight per lane
+//                group): writes u.
+//   sel_hist     1024-bin histogram of a monotone binning of s/||q|| in [-1, 1] from the
+//                L2/MALL-resident scores (LDS histograms, one global atomic per non-empty
+//                bin and workgroup); the last workgroup of each head (fenced atomic counter,
+//                no waiting) finds, with a parallel prefix sum, the bin b* that holds the
+//                n_r-th largest score.
 //   sel_collect  pass over u: counts keys above b* per block and appends the keys in b* to
-//                a candidate list; the last workgroup of each head radix-selects the exact
-//                n_r-th largest 64-bit key among the candidates and turns the per-block
-//                counts into output offsets.
+//                a candidate list; the last workgroup of each head selects the exact n_r-th
+//                largest 64-bit key among the candidates and turns the per-block counts
+//                into output offsets (parallel prefix sum).
 //   sel_scatter  pass over u: ordered compaction of the predicate key64 >= threshold into
 //                the retrieval and bulk index arrays.
 #include "common.hpp"
@@ -30,20 +31,21 @@ typedef unsigned u4v __attribute__((ext_vector_type(4)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr int kD = A2ATS_HEAD_DIM;
-constexpr int kBins = 4096;
+constexpr int kBins = 1024;
+constexpr float kHalfBins = 512.0f;
+constexpr int kHistScores = 4096;   // scores per sel_hist workgroup (at most 64 per head)
 constexpr int kScoreChunk = 512;    // keys per sel_score workgroup
-constexpr int kScoreUnroll = 8;     // keys in flight per 16-lane group
+constexpr int kScoreUnroll = 4;     // keys in flight per 8-lane group
 constexpr int kBlock = 1024;        // scores per sel_collect / sel_scatter workgroup
-constexpr int kSortCap = 2048;      // candidates sorted in LDS; more take the radix path
-constexpr int kHistWG = 16;         // sel_hist workgroups per head
+constexpr int kSortCap = 4096;      // candidates sorted in LDS; more take the radix path
 
 struct HeadInfo {
-  float inv_scale;       // 2048 / ||q||, or 0 when q == 0
+  float inv_scale;       // (kBins / 2) / ||q||, or 0 when q == 0
   int n_r;               // retrieval-set size
   int bstar;             // bin holding the n_r-th largest score (kBins: nothing selected)
   int count_above;       // keys in bins above bstar
   int n_cand;            // keys in bin bstar (candidate list length)
-  unsigned done_score;   // workgroups of sel_score finished
+  unsigned done_score;   // workgroups of sel_hist finished
   unsigned done_collect; // workgroups of sel_collect finished
   int pad;
   unsigned long long thr; // 64-bit key of the n_r-th largest element
@@ -62,7 +64,7 @@ __device__ __forceinline__ float key_value(unsigned u) {
 // Monotone non-decreasing in s: a positive scale, an add and floor all preserve order.
 __device__ __forceinline__ int bin_of(unsigned u, float inv_scale) {
   float s = key_value(u);
-  float v = floorf(__fmaf_rn(s, inv_scale, 2048.0f));  // one rounding, identical everywhere
+  float v = floorf(__fmaf_rn(s, inv_scale, kHalfBins));  // one rounding, identical everywhere
   v = fminf(fmaxf(v, 0.0f), (float)(kBins - 1));
   return (int)v;
 }
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(256) void sel_init(const void* __restrict__ query, 
   if (t == 0) {
     float qn = sqrtf(red[0] + red[1] + red[2] + red[3]);
     HeadInfo h;
-    h.inv_scale = qn > 0.f ? 2048.0f / qn : 0.f;
+    h.inv_scale = qn > 0.f ? kHalfBins / qn : 0.f;
     h.n_r = (int)ceil(fraction * (double)n);
     h.bstar = kBins;
     h.count_above = 0;
@@ -108,7 +110,30 @@ __global__ __launch_bounds__(256) void sel_init(const void* __restrict__ query, 
   }
 }
 
-// 16 lanes per key; each lane covers 8 consecutive elements of the 128.
+// Exclusive prefix sum over the 256 threads of a workgroup (thread order); returns the sum of
+// the threads before this one and, in *total, the workgroup sum.
+__device__ __forceinline__ unsigned block_exclusive_scan(unsigned v, unsigned* total) {
+  __shared__ unsigned wsum[4];
+  const int t = threadIdx.x, lane = t & 63;
+  unsigned incl = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned u = __shfl_up(incl, o);
+    if (lane >= o) incl += u;
+  }
+  __syncthreads();
+  if (lane == 63) wsum[t >> 6] = incl;
+  __syncthreads();
+  unsigned before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    before += w < (t >> 6) ? wsum[w] : 0u;
+    all += wsum[w];
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+// 8 lanes per key; each lane covers 16 consecutive elements of the 128.
 template <int DT>
 __global__ __launch_bounds__(256) void sel_score(const void* __restrict__ keys,
                                                  const void* __restrict__ query, int64_t n,
@@ -116,92 +141,93 @@ __global__ __launch_bounds__(256) void sel_score(const void* __restrict__ keys,
   const int head = blockIdx.x / wg_per_head;
   const int wg = blockIdx.x % wg_per_head;
   const int t = threadIdx.x;
-  const int sub = t & 15;
-  float qv[8];
+  const int sub = t & 7;
+  float qv[16];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) qv[e] = load_elem(query, DT, (int64_t)head * kD + sub * 8 + e);
+  for (int e = 0; e < 16; ++e) qv[e] = load_elem(query, DT, (int64_t)head * kD + sub * 16 + e);
   const int64_t k_begin = (int64_t)wg * kScoreChunk;
   const int64_t k_end = k_begin + kScoreChunk < n ? k_begin + kScoreChunk : n;
   const int64_t hoff = (int64_t)head * n;
-  for (int64_t k0 = k_begin; k0 < k_end; k0 += 16 * kScoreUnroll) {
-    float dot[kScoreUnroll], nrm[kScoreUnroll];
-    float x[kScoreUnroll][8];
+  for (int64_t k0 = k_begin; k0 < k_end; k0 += 32 * kScoreUnroll) {
+    float x[kScoreUnroll][16];
 #pragma unroll
     for (int u = 0; u < kScoreUnroll; ++u) {  // issue every load first
-      const int64_t key = k0 + u * 16 + (t >> 4);
+      const int64_t key = k0 + u * 32 + (t >> 3);
       if (key < k_end) {
         if (DT == A2ATS_BF16) {
-          const u4v raw = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(
-              static_cast<const uint16_t*>(keys) + (hoff + key) * kD + sub * 8));
-          const unsigned w[4] = {raw.x, raw.y, raw.z, raw.w};
+          const u4v* p = reinterpret_cast<const u4v*>(static_cast<const uint16_t*>(keys) +
+                                                      (hoff + key) * kD + sub * 16);
+          const u4v r0 = p[0], r1 = p[1];
+          const unsigned w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+          for (int e = 0; e < 8; ++e) {
             x[u][2 * e] = __uint_as_float(w[e] << 16);
             x[u][2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
           }
         } else {
           const f4v* p = reinterpret_cast<const f4v*>(static_cast<const float*>(keys) +
-                                                      (hoff + key) * kD + sub * 8);
-          const f4v a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
-          x[u][0] = a.x; x[u][1] = a.y; x[u][2] = a.z; x[u][3] = a.w;
-          x[u][4] = b.x; x[u][5] = b.y; x[u][6] = b.z; x[u][7] = b.w;
+                                                      (hoff + key) * kD + sub * 16);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f4v a = p[q];
+            x[u][4 * q] = a.x; x[u][4 * q + 1] = a.y; x[u][4 * q + 2] = a.z; x[u][4 * q + 3] = a.w;
+          }
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[u][e] = 0.f;
+        for (int e = 0; e < 16; ++e) x[u][e] = 0.f;
       }
     }
 #pragma unroll
     for (int u = 0; u < kScoreUnroll; ++u) {
-      dot[u] = 0.f;
-      nrm[u] = 0.f;
+      float dot = 0.f, nrm = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        dot[u] += x[u][e] * qv[e];
-        nrm[u] += x[u][e] * x[u][e];
+      for (int e = 0; e < 16; ++e) {
+        dot += x[u][e] * qv[e];
+        nrm += x[u][e] * x[u][e];
       }
-    }
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) {
-        dot[u] += __shfl_xor(dot[u], o);
-        nrm[u] += __shfl_xor(nrm[u], o);
+      for (int o = 4; o > 0; o >>= 1) {
+        dot += __shfl_xor(dot, o);
+        nrm += __shfl_xor(nrm, o);
       }
-      const int64_t key = k0 + u * 16 + (t >> 4);
+      const int64_t key = k0 + u * 32 + (t >> 3);
       if (sub == 0 && key < k_end) {
-        const float sc = nrm[u] > 0.f ? dot[u] / sqrtf(nrm[u]) : 0.f;
+        const float sc = nrm > 0.f ? dot / sqrtf(nrm) : 0.f;
         scores[hoff + key] = order_key(sc);
       }
     }
   }
 }
 
-// Histogram of the binned scores: kHistWG workgroups per head, LDS histogram, one global
-// atomic per non-empty bin; the last workgroup of each head (fenced counter, no waiting)
-// finds the bin b* holding the n_r-th largest score.
+// Histogram of the binned scores from the L2/MALL-resident score array: kHistScores
+// scores per workgroup into an LDS histogram, one global atomic per non-empty bin (the
+// scores of a head fall into a few hundred bins); the last workgroup of each head (fenced
+// counter, no waiting) finds, with a parallel prefix sum, the bin b* holding the n_r-th
+// largest score.
 __global__ __launch_bounds__(256) void sel_hist(const unsigned* __restrict__ scores, int64_t n,
-                                                HeadInfo* __restrict__ info,
+                                                int wg_per_head, HeadInfo* __restrict__ info,
                                                 unsigned* __restrict__ hist) {
-  const int head = blockIdx.x / kHistWG;
-  const int wg = blockIdx.x % kHistWG;
+  const int head = blockIdx.x / wg_per_head;
+  const int wg = blockIdx.x % wg_per_head;
   const int t = threadIdx.x;
   __shared__ unsigned lh[kBins];
   __shared__ int is_last;
   for (int i = t; i < kBins; i += 256) lh[i] = 0u;
   const float inv = info[head].inv_scale;
+  unsigned* hh = hist + (int64_t)head * kBins;
   __syncthreads();
-  const int64_t per = ((n + kHistWG - 1) / kHistWG + 3) / 4 * 4;
+  const int64_t per = ((n + wg_per_head - 1) / wg_per_head + 3) / 4 * 4;
   const int64_t i_begin = (int64_t)wg * per;
   const int64_t i_end = i_begin + per < n ? i_begin + per : n;
   const int64_t hoff = (int64_t)head * n;
   for (int64_t i0 = i_begin + 4 * t; i0 < i_end; i0 += 1024) {
-    unsigned uv[4];
     if (i0 + 3 < i_end && ((hoff + i0) & 3) == 0) {
       const uint4 q = *reinterpret_cast<const uint4*>(scores + hoff + i0);
-      uv[0] = q.x; uv[1] = q.y; uv[2] = q.z; uv[3] = q.w;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) atomicAdd(&lh[bin_of(uv[k], inv)], 1u);
+      atomicAdd(&lh[bin_of(q.x, inv)], 1u);
+      atomicAdd(&lh[bin_of(q.y, inv)], 1u);
+      atomicAdd(&lh[bin_of(q.z, inv)], 1u);
+      atomicAdd(&lh[bin_of(q.w, inv)], 1u);
     } else {
       for (int k = 0; k < 4 && i0 + k < i_end; ++k)
         atomicAdd(&lh[bin_of(scores[hoff + i0 + k], inv)], 1u);
@@ -209,47 +235,30 @@ __global__ __launch_bounds__(256) void sel_hist(const unsigned* __restrict__ sco
   }
   __syncthreads();
   for (int i = t; i < kBins; i += 256)
-    if (lh[i]) atomicAdd(&hist[(int64_t)head * kBins + i], lh[i]);
+    if (lh[i]) atomicAdd(&hh[i], lh[i]);
   __threadfence();
   __syncthreads();
-  if (t == 0) is_last = (atomicAdd(&info[head].done_score, 1u) == (unsigned)kHistWG - 1);
+  if (t == 0) is_last = (atomicAdd(&info[head].done_score, 1u) == (unsigned)wg_per_head - 1);
   __syncthreads();
   if (!is_last) return;
   __threadfence();
-  // Last workgroup of this head: locate the bin of the n_r-th largest score.
-  __shared__ unsigned part[256];
+  // Last workgroup of this head: thread t owns the 4 bins kBins-4(t+1) .. kBins-4t-1, taken
+  // in descending order; a prefix sum over the threads finds the bin of the n_r-th largest.
   const int n_r = info[head].n_r;
-  unsigned s16 = 0;
-  // thread t owns bins [kBins - 16(t+1), kBins - 16t), i.e. descending ranges
-  for (int i = 0; i < 16; ++i) {  // plain loads: the fence above made the atomics visible
-    int b = kBins - 16 * (t + 1) + i;
-    unsigned c = hist[(int64_t)head * kBins + b];
-    lh[b] = c;
-    s16 += c;
-  }
-  part[t] = s16;
-  __syncthreads();
-  if (t == 0) {
-    int bstar = kBins, above = 0;
-    if (n_r > 0) {
-      unsigned cum = 0;
-      for (int i = 0; i < 256 && bstar == kBins; ++i) {
-        if (cum + part[i] >= (unsigned)n_r) {
-          for (int b = kBins - 16 * i - 1; b >= kBins - 16 * (i + 1); --b) {
-            if (cum + lh[b] >= (unsigned)n_r) {
-              bstar = b;
-              above = (int)cum;
-              break;
-            }
-            cum += lh[b];
-          }
-        } else {
-          cum += part[i];
-        }
+  const uint4 v = *reinterpret_cast<const uint4*>(hh + kBins - 4 * (t + 1));  // plain load: fenced
+  const unsigned c4[4] = {v.w, v.z, v.y, v.x};
+  const unsigned s4 = c4[0] + c4[1] + c4[2] + c4[3];
+  unsigned total;
+  unsigned cum = block_exclusive_scan(s4, &total);
+  if (n_r > 0 && cum < (unsigned)n_r && cum + s4 >= (unsigned)n_r) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (cum < (unsigned)n_r && cum + c4[i] >= (unsigned)n_r) {
+        info[head].bstar = kBins - 1 - 4 * t - i;
+        info[head].count_above = (int)cum;
       }
+      cum += c4[i];
     }
-    info[head].bstar = bstar;
-    info[head].count_above = above;
   }
 }
 
@@ -350,18 +359,15 @@ __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ 
         if ((kv & mask) == prefix) atomicAdd(&dh[(kv >> shift) & 0xFF], 1u);
       }
       __syncthreads();
-      if (t == 0) {
-        unsigned rem = s_remaining, cum = 0;
-        int dg = 0;
-        for (int g = 255; g >= 0; --g) {
-          if (cum + dh[g] >= rem) {
-            dg = g;
-            break;
-          }
-          cum += dh[g];
+      {  // digit holding the rem-th largest: thread t takes digit 255 - t (descending)
+        const unsigned rem = s_remaining;
+        const unsigned cdg = dh[255 - t];
+        unsigned all;
+        const unsigned cum = block_exclusive_scan(cdg, &all);
+        if (cum < rem && cum + cdg >= rem) {
+          s_remaining = rem - cum;
+          s_prefix = prefix | ((unsigned long long)(255 - t) << shift);
         }
-        s_remaining = rem - cum;
-        s_prefix = prefix | ((unsigned long long)dg << shift);
       }
       __syncthreads();
       prefix = s_prefix;
@@ -386,30 +392,18 @@ __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ 
   }
   __threadfence();
   __syncthreads();
-  // exclusive offsets over the blocks: counts loaded in parallel (atomic loads for the
-  // counters this workgroup just incremented), then a serial prefix in LDS, 256 at a time
-  __shared__ unsigned cbuf[256];
-  __shared__ unsigned s_run;
-  if (t == 0) s_run = 0u;
+  // exclusive offsets over the blocks, 256 at a time (atomic loads for the counters this
+  // workgroup just incremented)
+  unsigned run = 0;
   for (int b0 = 0; b0 < nblk; b0 += 256) {
     const int b = b0 + t;
-    if (b < nblk)
-      cbuf[t] = above_blk[(int64_t)head * nblk + b] +
-                atomic_load_u32(&sel_extra[(int64_t)head * nblk + b]);
-    __syncthreads();
-    if (t == 0) {
-      unsigned run = s_run;
-      const int m = nblk - b0 < 256 ? nblk - b0 : 256;
-      for (int k = 0; k < m; ++k) {
-        const unsigned cnt = cbuf[k];
-        cbuf[k] = run;
-        run += cnt;
-      }
-      s_run = run;
-    }
-    __syncthreads();
-    if (b < nblk) sel_extra[(int64_t)head * nblk + b] = cbuf[t];  // the exclusive offset
-    __syncthreads();
+    const unsigned cntb = b < nblk ? above_blk[(int64_t)head * nblk + b] +
+                                         atomic_load_u32(&sel_extra[(int64_t)head * nblk + b])
+                                   : 0u;
+    unsigned chunk;
+    const unsigned ex = block_exclusive_scan(cntb, &chunk);
+    if (b < nblk) sel_extra[(int64_t)head * nblk + b] = run + ex;  // the exclusive offset
+    run += chunk;
   }
 }
 
@@ -538,8 +532,9 @@ extern "C" int a2ats_select_retrieval(const void* keys, int keys_dtype, int64_t 
   else
     A2ATS_TRY(launch("select_score", sel_score<A2ATS_F32>, dim3((unsigned)(heads * wg_per_head)),
                      dim3(256), 0, s, keys, query, n, (int)wg_per_head, L.scores));
-  A2ATS_TRY(launch("select_hist", sel_hist, dim3((unsigned)(heads * kHistWG)), dim3(256), 0, s,
-                   L.scores, n, L.info, L.hist));
+  const int64_t hist_wg = std::min<int64_t>(64, std::max<int64_t>(1, (n + kHistScores - 1) / kHistScores));
+  A2ATS_TRY(launch("select_hist", sel_hist, dim3((unsigned)(heads * hist_wg)), dim3(256), 0, s,
+                   L.scores, n, (int)hist_wg, L.info, L.hist));
   A2ATS_TRY(launch("select_collect", sel_collect, dim3((unsigned)(heads * nblk)), dim3(256), 0, s,
                    L.scores, n, (int)nblk, L.info, L.above_blk, L.cand, L.sel_extra));
   return launch("select_scatter", sel_scatter, dim3((unsigned)(heads * nblk)), dim3(256), 0, s,
