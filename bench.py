@@ -48,7 +48,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="run 3 layer steps and a 256 MiB reference copy, for rocprofv3 --pmc")
+    ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) of "
+                         "--pmc-probe into profiles/encode_coarse_plain_layer_pmc.{json,md}")
     args = ap.parse_args()
+    if args.pmc_summarize:
+        pmc_summarize(*args.pmc_summarize)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         if int(os.environ.get("RANK", "0")) == 0:
@@ -88,6 +96,21 @@ def main():
         kv.encode(kd, cbd, None, codes=codes)
         kv.encode(kd, cbd, L, idx=ret, codes=codes)
         kv.reconstruct(codes[None], pos, cbd, w.cur_pos, w.window, out=out)
+
+    if args.pmc_probe:
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        src = torch.ones(COPY_REF_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)  # reads and writes COPY_REF_BYTES: the counter scale
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_probe": "done", "copy_ref_bytes": COPY_REF_BYTES}), flush=True)
+        return
 
     log("warmup %d" % args.warmup)
     for _ in range(args.warmup):
@@ -152,6 +175,76 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+COPY_REF_BYTES = 256 * 2 ** 20
+COARSE_SOURCE = "kv_cache_vector_windowed_amd/csrc/encode.hip"
+
+
+def _pmc_rows(d, counter):
+    """{dispatch id: (kernel name, grid size, value summed over instances)} for one counter."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % d)
+    out = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = (f, r["Dispatch_Id"])
+                name, grid, v = out.get(k, (r["Kernel_Name"], int(r["Grid_Size"]), 0.0))
+                out[k] = (name, grid, v + float(r["Counter_Value"]))
+    return out
+
+
+def pmc_summarize(fetch_dir, write_dir):
+    """HBM bytes per launch of the plain coarse encode pass on the layer workload: FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads for a
+    reference elementwise kernel that reads and writes COPY_REF_BYTES."""
+    layer_grid = 8 * (32768 // 256) * 256  # workgroups x 256 threads
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _pmc_rows(d, counter)
+        coarse = sorted(v for n, g, v in rows.values() if "enc_coarse" in n and "Lb0ELb0E" in n
+                        and g == layer_grid)
+        ref = sorted(v for n, g, v in rows.values() if "neg" in n)
+        if not coarse or not ref:
+            raise SystemExit("%s: missing dispatches (coarse %d, reference %d)" % (counter, len(coarse), len(ref)))
+        kib = coarse[len(coarse) // 2]
+        ref_kib = ref[len(ref) // 2]
+        scale = (COPY_REF_BYTES / 1024.0) / ref_kib
+        res[counter] = {"kib_per_dispatch": kib, "reference_kib": ref_kib, "scale": scale,
+                        "bytes": kib * 1024.0 * scale}
+    total = res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"]
+    # bf16 keys, fp16 codebook fragments, fp32 bias, uint16 codes
+    algorithmic = 8 * 32768 * 128 * 2 + 8 * 1024 * 128 * 2 + 8 * 1024 * 4 + 8 * 32768 * 2
+    cmd = ["cd /tmp && export TMPDIR=/tmp",
+           "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/gpurun_out/pmc_fetch -o p -- "
+           "python <repo>/bench.py --pmc-probe",
+           "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/gpurun_out/pmc_write -o p -- "
+           "python <repo>/bench.py --pmc-probe",
+           "python bench.py --pmc-summarize gpurun_out/pmc_fetch gpurun_out/pmc_write"]
+    d = {"kernel": "encode_coarse_plain", "workload": "layer", "source": COARSE_SOURCE,
+         "source_sha": sha_of(os.path.join(ROOT, COARSE_SOURCE)),
+         "hbm_bytes_per_launch": round(total), "algorithmic_bytes_per_launch": algorithmic,
+         "counters": res, "commands": cmd}
+    base = os.path.join(ROOT, "profiles", "encode_coarse_plain_layer_pmc")
+    with open(base + ".json", "w") as f:
+        json.dump(d, f, indent=1)
+    with open(base + ".md", "w") as f:
+        f.write("# encode_coarse_plain, layer workload: HBM traffic per launch\n\n")
+        f.write("Commands:\n\n```\n%s\n```\n\n" % "\n".join(cmd))
+        f.write("| counter | KiB / dispatch | reference KiB (%d MiB read + write) | scale | bytes |\n"
+                "|---|---|---|---|---|\n" % (COPY_REF_BYTES >> 20))
+        for k, v in res.items():
+            f.write("| %s | %.0f | %.0f | %.4f | %.4g |\n" % (k, v["kib_per_dispatch"], v["reference_kib"],
+                                                         v["scale"], v["bytes"]))
+        f.write("\nTotal %.4g bytes per launch; algorithmic %.4g (keys, fp16 codebook, bias, codes); "
+                "source %s @ %s\n" % (total, algorithmic, COARSE_SOURCE, d["source_sha"]))
+    print(json.dumps(d))
 
 
 def traffic_from_profiles(kernel, workload):
