@@ -7,7 +7,7 @@
 // (u << 32) | (0xffffffff - index), so equal scores keep the lower index first and every
 // element has a distinct key.
 //
-// Kernels (5 launches, no host round trip):
+// Kernels (6 launches, no host round trip, no workgroup waits for another):
 //   sel_init     per head: ||q|| and the binning scale; zeroes histograms and counters.
 //   sel_score    HBM-bound pass over the keys (8 lanes per key, 4 keys in flight per lane
 //                group): writes u.
@@ -16,10 +16,11 @@
 //                bin and workgroup); the last workgroup of each head (fenced atomic counter,
 //                no waiting) finds, with a parallel prefix sum, the bin b* that holds the
 //                n_r-th largest score.
-//   sel_collect  pass over u: counts keys above b* per block and appends the keys in b* to
-//                a candidate list; the last workgroup of each head selects the exact n_r-th
-//                largest 64-bit key among the candidates and turns the per-block counts
-//                into output offsets (parallel prefix sum).
+//   sel_collect  pass over u: per block of 1024 scores, the count above b* and the keys in
+//                b* (into the block's own region of the candidate array).
+//   sel_thresh   one workgroup per head: the exact n_r-th largest 64-bit key among the
+//                candidates, the selected candidates per block, and every block's output
+//                offset (parallel prefix sums).
 //   sel_scatter  pass over u: ordered compaction of the predicate key64 >= threshold into
 //                the retrieval and bulk index arrays.
 #include "common.hpp"
@@ -33,7 +34,7 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 constexpr int kD = A2ATS_HEAD_DIM;
 constexpr int kBins = 1024;
 constexpr float kHalfBins = 512.0f;
-constexpr int kHistScores = 4096;   // scores per sel_hist workgroup (at most 64 per head)
+constexpr int kHistScores = 16384;  // scores per sel_hist workgroup (at most 64 per head)
 constexpr int kScoreChunk = 512;    // keys per sel_score workgroup
 constexpr int kScoreUnroll = 4;     // keys in flight per 8-lane group
 constexpr int kBlock = 1024;        // scores per sel_collect / sel_scatter workgroup
@@ -44,9 +45,9 @@ struct HeadInfo {
   int n_r;               // retrieval-set size
   int bstar;             // bin holding the n_r-th largest score (kBins: nothing selected)
   int count_above;       // keys in bins above bstar
-  int n_cand;            // keys in bin bstar (candidate list length)
+  int n_cand;            // unused
   unsigned done_score;   // workgroups of sel_hist finished
-  unsigned done_collect; // workgroups of sel_collect finished
+  unsigned done_collect; // unused
   int pad;
   unsigned long long thr; // 64-bit key of the n_r-th largest element
 };
@@ -262,11 +263,13 @@ __global__ __launch_bounds__(256) void sel_hist(const unsigned* __restrict__ sco
   }
 }
 
+// Per block of kBlock scores: the count above b* and the keys in b*, appended to the
+// block's own region of the candidate array (no global atomics).
 __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ scores, int64_t n,
-                                                   int nblk, HeadInfo* __restrict__ info,
+                                                   int nblk, const HeadInfo* __restrict__ info,
                                                    unsigned* __restrict__ above_blk,
-                                                   unsigned long long* __restrict__ cand,
-                                                   unsigned* __restrict__ sel_extra) {
+                                                   unsigned* __restrict__ cand_blk,
+                                                   unsigned long long* __restrict__ cand) {
   const int head = blockIdx.x / nblk;
   const int blk = blockIdx.x % nblk;
   const int t = threadIdx.x;
@@ -276,7 +279,8 @@ __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ 
   const int64_t i_begin = (int64_t)blk * kBlock;
   const int64_t i_end = i_begin + kBlock < n ? i_begin + kBlock : n;
   unsigned above = 0;
-  __shared__ unsigned s_cnt, s_base;
+  __shared__ unsigned s_cnt;
+  __shared__ unsigned red[4];
   if (t == 0) s_cnt = 0u;
   __syncthreads();
   const int64_t i0 = i_begin + 4 * t;  // 4 consecutive scores per thread
@@ -288,7 +292,7 @@ __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ 
 #pragma unroll
     for (int k = 0; k < 4; ++k) uv[k] = (i0 + k < i_end) ? scores[hoff + i0 + k] : 0u;
   }
-  unsigned mine = 0, local = 0;  // candidates of this thread, and their LDS slot base
+  unsigned mine = 0, local = 0;  // candidates of this thread, and their slot base
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     if (i0 + k < i_end) {
@@ -298,39 +302,54 @@ __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ 
     }
   }
   if (mine) local = atomicAdd(&s_cnt, (unsigned)__popc(mine));
-  __syncthreads();
-  if (t == 0) s_base = s_cnt ? atomicAdd((unsigned*)&info[head].n_cand, s_cnt) : 0u;
-  __syncthreads();
   for (int k = 0; k < 4; ++k)
-    if (mine & (1u << k)) cand[hoff + s_base + local++] = key64(uv[k], i0 + k);
-  __shared__ unsigned red[4];
-  __shared__ int is_last;
+    if (mine & (1u << k)) cand[hoff + i_begin + local++] = key64(uv[k], i0 + k);
   for (int o = 32; o > 0; o >>= 1) above += __shfl_xor(above, o);
   if ((t & 63) == 0) red[t >> 6] = above;
   __syncthreads();
-  if (t == 0) above_blk[(int64_t)head * nblk + blk] = red[0] + red[1] + red[2] + red[3];
-  __threadfence();
-  __syncthreads();
-  if (t == 0) is_last = (atomicAdd(&info[head].done_collect, 1u) == (unsigned)nblk - 1);
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  // Last workgroup of this head: exact radix select of the r-th largest candidate key.
-  const int n_cand = (int)info[head].n_cand;  // visible after the acquire fence above
+  if (t == 0) {
+    above_blk[(int64_t)head * nblk + blk] = red[0] + red[1] + red[2] + red[3];
+    cand_blk[(int64_t)head * nblk + blk] = s_cnt;
+  }
+}
+
+// One workgroup per head: the exact n_r-th largest 64-bit key among the candidates of bin
+// b* (LDS bitonic sort, radix select beyond kSortCap), the selected candidates per block,
+// and the exclusive output offset of every block (parallel prefix sums).
+__global__ __launch_bounds__(256) void sel_thresh(int64_t n, int nblk, HeadInfo* __restrict__ info,
+                                                  const unsigned* __restrict__ above_blk,
+                                                  const unsigned* __restrict__ cand_blk,
+                                                  const unsigned long long* __restrict__ cand,
+                                                  unsigned* __restrict__ sel_extra) {
+  const int head = blockIdx.x;
+  const int t = threadIdx.x;
+  const int64_t hoff = (int64_t)head * n;
   const int r = info[head].n_r - info[head].count_above;  // 1-based rank inside bin b*
+  __shared__ unsigned long long sk[kSortCap];
+  // candidate count, and (when they fit) the candidates packed into LDS in block order
+  unsigned n_cand = 0;
+  for (int b0 = 0; b0 < nblk; b0 += 256) {
+    const int b = b0 + t;
+    const unsigned cb = b < nblk ? cand_blk[(int64_t)head * nblk + b] : 0u;
+    unsigned chunk;
+    const unsigned ex = block_exclusive_scan(cb, &chunk);
+    if (n_cand + ex + cb <= (unsigned)kSortCap)
+      for (unsigned i = 0; i < cb; ++i) sk[n_cand + ex + i] = cand[hoff + (int64_t)b * kBlock + i];
+    n_cand += chunk;
+  }
+  __syncthreads();
   __shared__ unsigned dh[256];
   __shared__ unsigned long long s_prefix;
   __shared__ unsigned s_remaining;
   unsigned long long prefix = 0ull, mask = 0ull;
   if (t == 0) s_remaining = (unsigned)(r > 0 ? r : 0);
   __syncthreads();
-  const unsigned long long* ch = cand + hoff;
-  __shared__ unsigned long long sk[kSortCap];
-  if (r > 0 && n_cand <= kSortCap) {
+  const bool fits = n_cand <= (unsigned)kSortCap;
+  if (r > 0 && fits) {
     // bitonic sort of the candidate keys, descending; the r-th is the threshold
     int P = 1;
-    while (P < n_cand) P <<= 1;
-    for (int i = t; i < P; i += 256) sk[i] = i < n_cand ? ch[i] : 0ull;
+    while (P < (int)n_cand) P <<= 1;
+    for (int i = (int)n_cand + t; i < P; i += 256) sk[i] = 0ull;
     __syncthreads();
     for (int k = 2; k <= P; k <<= 1) {
       for (int j = k >> 1; j > 0; j >>= 1) {
@@ -349,14 +368,17 @@ __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ 
       }
     }
     prefix = sk[r - 1];
-    if (t == 0) info[head].thr = prefix;
   } else if (r > 0) {
+    // radix select over the per-block candidate regions, 8 bits at a time
     for (int shift = 56; shift >= 0; shift -= 8) {
       dh[t] = 0u;
       __syncthreads();
-      for (int i = t; i < n_cand; i += 256) {
-        const unsigned long long kv = ch[i];
-        if ((kv & mask) == prefix) atomicAdd(&dh[(kv >> shift) & 0xFF], 1u);
+      for (int b = t; b < nblk; b += 256) {
+        const unsigned cb = cand_blk[(int64_t)head * nblk + b];
+        for (unsigned i = 0; i < cb; ++i) {
+          const unsigned long long kv = cand[hoff + (int64_t)b * kBlock + i];
+          if ((kv & mask) == prefix) atomicAdd(&dh[(kv >> shift) & 0xFF], 1u);
+        }
       }
       __syncthreads();
       {  // digit holding the rem-th largest: thread t takes digit 255 - t (descending)
@@ -374,19 +396,25 @@ __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ 
       mask |= 0xFFull << shift;
       __syncthreads();
     }
-    if (t == 0) info[head].thr = prefix;
-  } else if (t == 0) {
-    info[head].thr = ~0ull;
   }
-  __syncthreads();
-  // Selected candidates per block, then exclusive offsets over the blocks of this head.
-  const unsigned long long thr = (r > 0) ? prefix : ~0ull;
+  const unsigned long long thr = r > 0 ? prefix : ~0ull;
+  if (t == 0) info[head].thr = thr;
+  // selected candidates per block
   if (r > 0) {
-    for (int i = t; i < n_cand; i += 256) {
-      const unsigned long long kv = ch[i];
-      if (kv >= thr) {
-        int64_t idx = (int64_t)(0xFFFFFFFFu - (unsigned)(kv & 0xFFFFFFFFull));
-        atomicAdd(&sel_extra[(int64_t)head * nblk + idx / kBlock], 1u);
+    if (fits) {
+      for (int i = t; i < (int)n_cand; i += 256) {
+        const unsigned long long kv = sk[i];
+        if (kv >= thr) {
+          const int64_t idx = (int64_t)(0xFFFFFFFFu - (unsigned)(kv & 0xFFFFFFFFull));
+          atomicAdd(&sel_extra[(int64_t)head * nblk + idx / kBlock], 1u);
+        }
+      }
+    } else {
+      for (int b = t; b < nblk; b += 256) {
+        const unsigned cb = cand_blk[(int64_t)head * nblk + b];
+        unsigned sel = 0;
+        for (unsigned i = 0; i < cb; ++i) sel += cand[hoff + (int64_t)b * kBlock + i] >= thr ? 1u : 0u;
+        if (sel) atomicAdd(&sel_extra[(int64_t)head * nblk + b], sel);
       }
     }
   }
@@ -478,6 +506,7 @@ struct SelLayout {
   unsigned* scores;
   unsigned long long* cand;
   unsigned* above_blk;
+  unsigned* cand_blk;
   unsigned* sel_extra;
   size_t bytes;
 };
@@ -491,6 +520,7 @@ SelLayout carve(void* ws, int64_t heads, int64_t n) {
   L.scores = c.take<unsigned>((size_t)heads * n);
   L.cand = c.take<unsigned long long>((size_t)heads * n);
   L.above_blk = c.take<unsigned>((size_t)heads * nblk);
+  L.cand_blk = c.take<unsigned>((size_t)heads * nblk);
   L.sel_extra = c.take<unsigned>((size_t)heads * nblk);
   L.bytes = c.used;
   return L;
@@ -536,7 +566,9 @@ extern "C" int a2ats_select_retrieval(const void* keys, int keys_dtype, int64_t 
   A2ATS_TRY(launch("select_hist", sel_hist, dim3((unsigned)(heads * hist_wg)), dim3(256), 0, s,
                    L.scores, n, (int)hist_wg, L.info, L.hist));
   A2ATS_TRY(launch("select_collect", sel_collect, dim3((unsigned)(heads * nblk)), dim3(256), 0, s,
-                   L.scores, n, (int)nblk, L.info, L.above_blk, L.cand, L.sel_extra));
+                   L.scores, n, (int)nblk, L.info, L.above_blk, L.cand_blk, L.cand));
+  A2ATS_TRY(launch("select_thresh", sel_thresh, dim3((unsigned)heads), dim3(256), 0, s, n, (int)nblk,
+                   L.info, L.above_blk, L.cand_blk, L.cand, L.sel_extra));
   return launch("select_scatter", sel_scatter, dim3((unsigned)(heads * nblk)), dim3(256), 0, s,
                 L.scores, n, (int)nblk, L.info, L.sel_extra, retrieval_idx, bulk_idx);
 }
