@@ -122,6 +122,32 @@ int a2ats_encode(const void* keys, int keys_dtype, int64_t heads, int64_t n, int
                  const float* chol, uint16_t* codes, float* dist, a2ats_encode_stats* stats,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* encode in two calls -- the same computation as a2ats_encode, split at the boundary between
+ * its codebook side and its key side, so that the codebook side (which depends on the
+ * codebook and L only) can run once for several key sets, or on another stream while the
+ * keys are still being produced.
+ *
+ * a2ats_encode_prepare writes the prepared codebook (fp64 rows v = c L L^T, b = ||c L||^2,
+ * the fp16 MFMA fragments, the bias and the per-head scales) into a workspace of
+ * a2ats_encode_workspace(heads, n, d, c) bytes; n is the largest key count the workspace will
+ * serve.  codebook and chol as for a2ats_encode (chol NULL: plain nearest centroid).
+ *
+ * a2ats_encode_prepared encodes keys with a workspace that a2ats_encode_prepare filled for the
+ * same heads, n, c and chol-or-NULL; the other arguments are as for a2ats_encode.  It does not
+ * read the codebook or L again (chol only selects the H-weighted rule, and with fp32 keys and
+ * dist != NULL it is read for ||k L||^2).  Any number of runs may follow one prepare; each run
+ * resets its own counters.  Runs on one workspace must be ordered on one stream (they share
+ * the list buffers); the prepared part must not be written between prepare and the runs.
+ * Both return without waiting; errors as for a2ats_encode.
+ */
+int a2ats_encode_prepare(const float* codebook, int64_t c, const float* chol, int64_t heads,
+                         int64_t n, int64_t d, void* workspace, size_t workspace_bytes,
+                         void* stream);
+int a2ats_encode_prepared(const void* keys, int keys_dtype, int64_t heads, int64_t n, int64_t d,
+                          const int32_t* idx, int64_t n_idx, int64_t c, const float* chol,
+                          uint16_t* codes, float* dist, a2ats_encode_stats* stats,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------------------
  * assign_cosine -- "veloxquant_mlx.quantizers.a2ats module", a2ats_query_aware_assignment:
  *     score_j = beta * (-e_j / max_i e_i) + (1 - beta) * cos(q, c_j),  e_j = ||x - c_j||^2,

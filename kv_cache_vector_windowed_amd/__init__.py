@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.a2ats_calibrate.argtypes = [p, i64, i64, i64, dbl, p, p, p, sz, p]
         L.a2ats_encode_workspace.argtypes, L.a2ats_encode_workspace.restype = [i64, i64, i64, i64], sz
         L.a2ats_encode.argtypes = [p, i32, i64, i64, i64, p, i64, p, i64, p, p, p, p, p, sz, p]
+        L.a2ats_encode_prepare.argtypes = [p, i64, p, i64, i64, i64, p, sz, p]
+        L.a2ats_encode_prepared.argtypes = [p, i32, i64, i64, i64, p, i64, i64, p, p, p, p, p, sz, p]
         L.a2ats_assign_cosine.argtypes = [p, i32, i64, i64, i64, p, i64, p, i64, dbl, p, p]
         L.a2ats_select_retrieval_workspace.argtypes = [i64, i64]
         L.a2ats_select_retrieval_workspace.restype = sz
@@ -63,7 +65,8 @@ def lib() -> ctypes.CDLL:
         L.a2ats_profile_enable.argtypes, L.a2ats_profile_enable.restype = [i32], i32
         L.a2ats_profile_reset.argtypes, L.a2ats_profile_reset.restype = [], i32
         L.a2ats_profile_read.argtypes, L.a2ats_profile_read.restype = [ctypes.c_char_p, sz], i64
-        for f in ("a2ats_calibrate", "a2ats_encode", "a2ats_assign_cosine",
+        for f in ("a2ats_calibrate", "a2ats_encode", "a2ats_encode_prepare", "a2ats_encode_prepared",
+                  "a2ats_assign_cosine",
                   "a2ats_select_retrieval", "a2ats_reconstruct"):
             getattr(L, f).restype = i32
         _lib = L
@@ -160,6 +163,68 @@ def encode(keys: torch.Tensor, codebook: torch.Tensor, chol: torch.Tensor | None
     _check(lib().a2ats_encode(_ptr(keys), _dtype_code(keys), heads, n, d, _ptr(idx), n_idx,
                               _ptr(codebook), c, _ptr(chol), _ptr(codes), _ptr(dist),
                               _ptr(stats), _ptr(ws), ws.numel(), _stream(keys.device)), "encode")
+    return (codes, dist) if want_dist else codes
+
+
+class PreparedCodebook:
+    """A codebook (and optional L) prepared for encoding `n` keys per head: the workspace of
+    a2ats_encode_prepare, reused by every encode_prepared call.  Keep the object alive while
+    work that uses it is queued on any stream."""
+
+    def __init__(self, codebook: torch.Tensor, chol: torch.Tensor | None, n: int):
+        _dev(codebook, "codebook")
+        heads, c, d = codebook.shape
+        self.heads, self.c, self.d, self.n = heads, c, d, int(n)
+        self.ws = _workspace(lib().a2ats_encode_workspace(heads, self.n, d, c), codebook.device)
+        self.prepare(codebook, chol)
+
+    def prepare(self, codebook: torch.Tensor, chol: torch.Tensor | None):
+        """(Re)run the codebook side into this workspace, on the current stream."""
+        _dev(codebook, "codebook")
+        if codebook.dtype != torch.float32 or codebook.shape != (self.heads, self.c, self.d):
+            raise ValueError("codebook must be [%d, %d, %d] float32" % (self.heads, self.c, self.d))
+        if chol is not None:
+            _dev(chol, "chol")
+            if chol.dtype != torch.float32 or chol.shape != (self.heads, self.d, self.d):
+                raise ValueError("chol must be [heads, d, d] float32")
+        self.chol = chol
+        _check(lib().a2ats_encode_prepare(_ptr(codebook), self.c, _ptr(chol), self.heads, self.n,
+                                          self.d, _ptr(self.ws), self.ws.numel(),
+                                          _stream(codebook.device)), "encode_prepare")
+        return self
+
+
+def encode_prepare(codebook: torch.Tensor, chol: torch.Tensor | None, n: int) -> PreparedCodebook:
+    """Codebook side of encode (depends on codebook and L only), on the current stream."""
+    return PreparedCodebook(codebook, chol, n)
+
+
+def encode_prepared(keys: torch.Tensor, prep: PreparedCodebook, idx: torch.Tensor | None = None,
+                    codes: torch.Tensor | None = None, want_dist: bool = False,
+                    stats: torch.Tensor | None = None):
+    """Key side of encode with a prepared codebook (keys [heads, n, d], n == prep.n); the
+    other arguments and the result as for encode()."""
+    _dev(keys, "keys")
+    heads, n, d = keys.shape
+    if (heads, n, d) != (prep.heads, prep.n, prep.d):
+        raise ValueError("keys must be [%d, %d, %d]" % (prep.heads, prep.n, prep.d))
+    n_idx = 0
+    if idx is not None:
+        _dev(idx, "idx")
+        if idx.dtype != torch.int32 or idx.dim() != 2 or idx.shape[0] != heads:
+            raise ValueError("idx must be [heads, n_idx] int32")
+        n_idx = idx.shape[1]
+    if codes is None:
+        codes = torch.zeros((heads, n), dtype=torch.uint16, device=keys.device)
+    else:
+        _dev(codes, "codes")
+    dist = torch.zeros((heads, n), dtype=torch.float32, device=keys.device) if want_dist else None
+    if stats is not None:
+        _dev(stats, "stats")
+    _check(lib().a2ats_encode_prepared(_ptr(keys), _dtype_code(keys), heads, n, d, _ptr(idx), n_idx,
+                                       prep.c, _ptr(prep.chol), _ptr(codes), _ptr(dist),
+                                       _ptr(stats), _ptr(prep.ws), prep.ws.numel(),
+                                       _stream(keys.device)), "encode_prepared")
     return (codes, dist) if want_dist else codes
 
 

@@ -24,12 +24,13 @@
 //                       fragments of L^T for ||kL||^2; clears the list and candidate
 //                       counters.
 //   enc_znorm64         ||kL||^2 in fp64 (fp32 keys with distances and L only).
-//   enc_coarse          the MFMA pass; writes directly certified codes, lists the rest.
-//   enc_refine          fp64 scores of the two leading candidates of every listed key.
+//   enc_coarse          the MFMA pass; writes directly certified codes; in its tail, fp64
+//                       scores of the two leading candidates of the other keys settle most
+//                       of them and list the rest for the rescan.
 //   enc_rescan_collect  second MFMA pass over the keys still open: collects every centroid
 //                       whose score could reach the best exact score.
-//   enc_rescan_decide   fp64 over the collected candidates.
-//   enc_fullscan        fp64 over the whole codebook (fp16 overflow, list overflow).
+//   enc_rescan_decide   fp64 over the collected candidates; fp64 over the whole codebook for
+//                       the keys listed for it (fp16 overflow, list overflow).
 #include "common.hpp"
 
 namespace a2ats {
@@ -51,7 +52,6 @@ constexpr int kRescanTiles = 2;           // tiles per rescan work item
 constexpr float kPadBias = -1.0e38f;      // bias of padding rows: finite, never competitive
 
 struct Counters {
-  unsigned refine_x[8][16];  // refine list entries per XCD region (counters 64 B apart)
   unsigned stat_x[8][16];    // keys, direct decisions, reranks per XCD (statistics only)
   unsigned full;             // full-scan list entries
   unsigned stats[8];         // [3] rescanned, [4] full scan
@@ -310,18 +310,9 @@ __global__ __launch_bounds__(256) void enc_prep_frag(const double* __restrict__ 
                                                      half8* __restrict__ v16,
                                                      float* __restrict__ bias,
                                                      half8* __restrict__ lfrag,
-                                                     unsigned* __restrict__ cnt, int ncnt,
-                                                     HeadScale* __restrict__ hsc,
-                                                     unsigned* __restrict__ cand_n, int64_t ncand) {
+                                                     HeadScale* __restrict__ hsc) {
   const int head = blockIdx.y;
   const int t = threadIdx.x;
-  if (head == 0 && blockIdx.x == 0)
-    for (int i = t; i < ncnt; i += 256) cnt[i] = 0u;
-  {  // the rescan candidate counters start at zero
-    const int64_t stride = (int64_t)gridDim.x * gridDim.y * 256;
-    for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 256 + t; i < ncand; i += stride)
-      cand_n[i] = 0u;
-  }
   const HeadScale hs = head_scale_wg(part_a, head, nwg_a);
   if (blockIdx.x == 0 && t == 0) hsc[head] = hs;  // for the later passes
   const int64_t rows = (int64_t)T * kRows;
@@ -527,6 +518,191 @@ __device__ __forceinline__ double coop_score(const void* keys, int64_t off_key, 
   return s - 0.5 * bj;
 }
 
+// ------------------------------------------------------------------ fp64 rerank
+// Exact fp64 score of one candidate, G lanes cooperating (lane g of the group owns dims
+// (128/G)g .. (128/G)(g+1)-1).  Returns the score (valid in every lane of the group) and, in
+// z2, ||k||^2.
+template <int DT, int G, typename VT>
+__device__ __forceinline__ double coop_score_g(const void* keys, int64_t off_key, const VT* vrow,
+                                               double bj, int g, double* z2) {
+  constexpr int DIM = kD / G;
+  double x[DIM];
+  if (DT == A2ATS_BF16) {
+    const uint4* kp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(keys) + off_key + DIM * g);
+#pragma unroll
+    for (int q = 0; q < DIM / 8; ++q) {
+      const uint4 r = kp[q];
+      const unsigned wv[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * q + 2 * e] = (double)__uint_as_float(wv[e] << 16);
+        x[8 * q + 2 * e + 1] = (double)__uint_as_float(wv[e] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const float4* kp = reinterpret_cast<const float4*>(static_cast<const float*>(keys) + off_key + DIM * g);
+#pragma unroll
+    for (int q = 0; q < DIM / 4; ++q) {
+      const float4 a = kp[q];
+      x[4 * q] = a.x; x[4 * q + 1] = a.y; x[4 * q + 2] = a.z; x[4 * q + 3] = a.w;
+    }
+  }
+  double v[DIM];
+  if (sizeof(VT) == 8) {
+    const double2* v2 = reinterpret_cast<const double2*>(vrow + DIM * g);
+#pragma unroll
+    for (int e = 0; e < DIM / 2; ++e) {
+      const double2 vv = v2[e];
+      v[2 * e] = vv.x;
+      v[2 * e + 1] = vv.y;
+    }
+  } else {
+    const float4* v4 = reinterpret_cast<const float4*>(vrow + DIM * g);
+#pragma unroll
+    for (int e = 0; e < DIM / 4; ++e) {
+      const float4 vv = v4[e];
+      v[4 * e] = vv.x; v[4 * e + 1] = vv.y; v[4 * e + 2] = vv.z; v[4 * e + 3] = vv.w;
+    }
+  }
+  double s = 0.0, k2 = 0.0;
+#pragma unroll
+  for (int e = 0; e < DIM; ++e) {
+    s += x[e] * v[e];
+    k2 += x[e] * x[e];
+  }
+  for (int o = G / 2; o > 0; o >>= 1) {
+    s += __shfl_xor(s, o);
+    k2 += __shfl_xor(k2, o);
+  }
+  *z2 = k2;
+  return s - 0.5 * bj;
+}
+
+template <int DT, typename VT>
+__device__ __forceinline__ double coop_score8(const void* keys, int64_t off_key, const VT* vrow,
+                                              double bj, int g, double* z2) {
+  return coop_score_g<DT, 8, VT>(keys, off_key, vrow, bj, g, z2);
+}
+
+// fp64 rerank of one listed key per 16-lane group (lanes 0-7 score j0, lanes 8-15 j1):
+// certified when the better exact score beats re.thr, else handed to the rescan (or, when
+// its list is full, the full scan).  Without L the rows are the fp32 codebook itself (v = c
+// exactly), half the bytes of the fp64 copy.  Returns 1 in the group's first lane when the
+// key was decided here.
+template <int DT>
+__device__ __forceinline__ unsigned rerank_group(
+    bool live, const RefEntry& re, const void* keys, int64_t n, int64_t c,
+    const double* v64, const float* v32, bool plain, const double* b64, uint16_t* codes,
+    float* dist, UncEntry* unc, int64_t unc_cap, FullEntry* full, Counters* cnt, int lane) {
+  const int which = (lane >> 3) & 1;  // candidate 0 or 1
+  const int g = lane & 7;
+  const int32_t head = live ? re.head : 0, row = live ? re.row : 0;
+  const int32_t ja = live ? re.j0 : -1, jb = live ? re.j1 : -1;
+  const int j = which ? jb : ja;
+  double s = -INFINITY, k2 = 0.0;
+  if (j >= 0) {
+    const int64_t off = ((int64_t)head * n + row) * kD;
+    const int64_t vo = ((int64_t)head * c + j) * kD;
+    s = plain ? coop_score8<DT>(keys, off, v32 + vo, b64[(int64_t)head * c + j], g, &k2)
+              : coop_score8<DT>(keys, off, v64 + vo, b64[(int64_t)head * c + j], g, &k2);
+  }
+  const double s_other = __shfl_xor(s, 8);
+  const double k2_other = __shfl_xor(k2, 8);
+  unsigned decided = 0;
+  if (live && (lane & 15) == 0) {
+    const double sa = s, sb = s_other;  // lane 0 of the group scored ja, lane 8 jb
+    if (ja < 0) k2 = k2_other;
+    int best = ja;
+    double sbest = sa;
+    if (jb >= 0 && (ja < 0 || sb > sa || (sb == sa && jb < ja))) {
+      best = jb;
+      sbest = sb;
+    }
+    const double z2 = re.z2 >= 0.f ? (double)re.z2 : k2;
+    const double eps = 0x1p-40 * (fabs(sbest) + k2 + 1.0);
+    if (best >= 0 && sbest - eps > re.thr) {
+      codes[(int64_t)head * n + row] = (uint16_t)best;
+      if (dist) dist[(int64_t)head * n + row] = (float)fmax(z2 - 2.0 * sbest, 0.0);
+      decided = 1;
+    } else {
+      const unsigned slot = atomicAdd(&cnt->unc[head], 1u);
+      if (best >= 0 && slot < unc_cap) {
+        UncEntry ue;
+        ue.row = row;
+        ue.jbest = best;
+        ue.sbest = sbest;
+        ue.e_unscaled = re.e_unscaled;
+        ue.z2 = re.z2;
+        ue.pad = 0;
+        unc[(int64_t)head * unc_cap + slot] = ue;
+      } else {
+        FullEntry fe;
+        fe.head = head;
+        fe.row = row;
+        fe.z2 = re.z2;
+        fe.pad = 0;
+        full[atomicAdd(&cnt->full, 1u)] = fe;
+      }
+    }
+  }
+  return decided;
+}
+
+// Number of listed open keys of a head (capped to the list capacity).
+__device__ __forceinline__ int64_t open_count(const Counters* cnt, int64_t head, int64_t cap) {
+  const unsigned u = __hip_atomic_load(&cnt->unc[head], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (int64_t)u < cap ? (int64_t)u : cap;
+}
+
+constexpr int kMaxHeadsLds = 1024;
+
+// Exclusive prefix over heads of `per(open count)`, built once per workgroup in LDS
+// (heads <= kMaxHeadsLds; larger head counts fall back to scanning global counters).
+template <typename F>
+__device__ int64_t head_prefix(const Counters* cnt, int64_t heads, int64_t cap, int64_t* pre, F per) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t run = 0;
+    const int64_t hn = heads < kMaxHeadsLds ? heads : kMaxHeadsLds;
+    for (int64_t h = 0; h < hn; ++h) {
+      pre[h] = run;
+      run += per(open_count(cnt, h, cap));
+    }
+    for (int64_t h = hn; h < heads; ++h) run += per(open_count(cnt, h, cap));
+    pre[kMaxHeadsLds] = run;
+  }
+  __syncthreads();
+  return pre[kMaxHeadsLds];
+}
+
+// Head owning global item index `it` (prefix from head_prefix).
+template <typename F>
+__device__ int64_t find_head(const Counters* cnt, int64_t heads, int64_t cap, const int64_t* pre,
+                             int64_t it, F per, int64_t* rest) {
+  const int64_t hn = heads < kMaxHeadsLds ? heads : kMaxHeadsLds;
+  int64_t lo = 0, hi = hn - 1;
+  if (hn > 0 && it < (hn < heads ? pre[hn - 1] + per(open_count(cnt, hn - 1, cap)) : pre[kMaxHeadsLds])) {
+    while (lo < hi) {  // last head with pre[h] <= it
+      const int64_t mid = (lo + hi + 1) / 2;
+      if (pre[mid] <= it) lo = mid;
+      else hi = mid - 1;
+    }
+    *rest = it - pre[lo];
+    return lo;
+  }
+  int64_t run = hn > 0 ? pre[hn - 1] + per(open_count(cnt, hn - 1, cap)) : 0;
+  for (int64_t h = hn; h < heads; ++h) {
+    const int64_t m = per(open_count(cnt, h, cap));
+    if (it < run + m) {
+      *rest = it - run;
+      return h;
+    }
+    run += m;
+  }
+  *rest = 0;
+  return heads - 1;
+}
+
 // ------------------------------------------------------------------ the MFMA pass
 // Workgroup: 256 keys of one head (4 waves x two 32-key column blocks).  Lane l serves key
 // column l % 32 of both blocks and, in every 32-centroid tile, the 16 rows
@@ -549,8 +725,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const double* __restrict__ b64, int64_t c, const half8* __restrict__ lfrag,
     const HeadScale* __restrict__ hsc, const float* __restrict__ part_b, int nwg_b,
     float* __restrict__ znorm, uint16_t* __restrict__ codes, float* __restrict__ dist,
-    RefEntry* __restrict__ refl, FullEntry* __restrict__ full, Counters* __restrict__ cnt,
-    int want_stats) {
+    const double* __restrict__ v64, UncEntry* __restrict__ unc, int64_t unc_cap,
+    FullEntry* __restrict__ full, Counters* __restrict__ cnt, int want_stats) {
   __shared__ half8 sv[2][kTPS][kFragPerTile];
   __shared__ __attribute__((aligned(16))) float sb[2][kTPS][32];
   __shared__ float s_red[2][4];
@@ -831,13 +1007,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       re.pad = 0;
     }
   }
-  // Rerank entries go to this XCD's region of the list (a counter per XCD keeps the
-  // global atomics off one address), one atomic per workgroup; full-scan entries (rare)
-  // share one counter.
-  __shared__ unsigned s_cnt, s_base, s_stat[2];
+  // Rerank entries stay in LDS (in the stage buffers, free after the loop) and are settled
+  // here, 4 per wave and pass; full-scan entries (rare) go to the global list.
+  RefEntry* s_ref = reinterpret_cast<RefEntry*>(&sv[0][0][0]);
+  static_assert(sizeof(RefEntry) * kKeysPerWG <= sizeof(sv), "rerank list fits the stage buffers");
+  __shared__ unsigned s_cnt, s_base, s_stat[3], s_nref;
   const unsigned xcd = blockIdx.x % 8;
-  const unsigned rslot = block_append(&cnt->refine_x[xcd][0], outcome == 2, &s_cnt, &s_base);
-  if (outcome == 2) refl[(int64_t)xcd * per_xcd * kKeysPerWG + rslot] = re;
+  if (t == 0) s_nref = 0u;
+  __syncthreads();
+  {
+    const unsigned long long m = __ballot(outcome == 2);
+    unsigned base = 0u;
+    if (lane == 0 && m) base = atomicAdd(&s_nref, (unsigned)__popcll(m));
+    base = __shfl(base, 0);
+    if (outcome == 2) s_ref[base + (unsigned)__popcll(m & ((1ull << lane) - 1ull))] = re;
+  }
+  __syncthreads();
+  const unsigned nref = s_nref;
+  unsigned reranked = 0;
+  for (unsigned e0 = (unsigned)wave * 4u; e0 < nref; e0 += 16u) {
+    const unsigned e = e0 + (unsigned)(lane >> 4);
+    const bool live = e < nref;
+    RefEntry rl;
+    if (live) rl = s_ref[e];
+    reranked += rerank_group<DT>(live, rl, keys, n, c, v64, v32, v64 == nullptr, b64, codes,
+                                 dist, unc, unc_cap, full, cnt, lane);
+  }
   const unsigned fslot = block_append(&cnt->full, outcome == 4, &s_cnt, &s_base);
   if (outcome == 4) {
     FullEntry fe;
@@ -847,230 +1042,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     fe.pad = 0;
     full[fslot] = fe;
   }
-  if (want_stats) {  // keys and direct decisions, per XCD
-    if (t == 0) s_stat[0] = s_stat[1] = 0u;
+  if (want_stats) {  // keys, direct decisions and reranks, per XCD
+    if (t == 0) s_stat[0] = s_stat[1] = s_stat[2] = 0u;
     __syncthreads();
     const unsigned long long valid = __ballot(myrow >= 0);
     const unsigned long long dmask = __ballot(outcome == 1);
+    for (int o = 32; o > 0; o >>= 1) reranked += __shfl_xor(reranked, o);
     if (lane == 0) {
       atomicAdd(&s_stat[0], (unsigned)__popcll(valid));
       atomicAdd(&s_stat[1], (unsigned)__popcll(dmask));
+      atomicAdd(&s_stat[2], reranked);
     }
     __syncthreads();
     if (t == 0) {
       if (s_stat[0]) atomicAdd(&cnt->stat_x[xcd][0], s_stat[0]);
       if (s_stat[1]) atomicAdd(&cnt->stat_x[xcd][1], s_stat[1]);
+      if (s_stat[2]) atomicAdd(&cnt->stat_x[xcd][2], s_stat[2]);
     }
   }
-}
-
-// ------------------------------------------------------------------ fp64 rerank
-// Exact fp64 score of one candidate, 8 lanes cooperating (lane g of the group owns dims
-// 16g .. 16g+15).  Returns the score (valid in every lane of the group) and, in z2, ||k||^2.
-template <int DT, typename VT>
-__device__ __forceinline__ double coop_score8(const void* keys, int64_t off_key, const VT* vrow,
-                                              double bj, int g, double* z2) {
-  double x[16];
-  if (DT == A2ATS_BF16) {
-    const uint4* kp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(keys) + off_key + 16 * g);
-    const uint4 r0 = kp[0], r1 = kp[1];
-    const unsigned wv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      x[2 * e] = (double)__uint_as_float(wv[e] << 16);
-      x[2 * e + 1] = (double)__uint_as_float(wv[e] & 0xFFFF0000u);
-    }
-  } else {
-    const float4* kp = reinterpret_cast<const float4*>(static_cast<const float*>(keys) + off_key + 16 * g);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 a = kp[q];
-      x[4 * q] = a.x; x[4 * q + 1] = a.y; x[4 * q + 2] = a.z; x[4 * q + 3] = a.w;
-    }
-  }
-  double v[16];
-  if (sizeof(VT) == 8) {
-    const double2* v2 = reinterpret_cast<const double2*>(vrow + 16 * g);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const double2 vv = v2[e];
-      v[2 * e] = vv.x;
-      v[2 * e + 1] = vv.y;
-    }
-  } else {
-    const float4* v4 = reinterpret_cast<const float4*>(vrow + 16 * g);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float4 vv = v4[e];
-      v[4 * e] = vv.x; v[4 * e + 1] = vv.y; v[4 * e + 2] = vv.z; v[4 * e + 3] = vv.w;
-    }
-  }
-  double s = 0.0, k2 = 0.0;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    s += x[e] * v[e];
-    k2 += x[e] * x[e];
-  }
-  for (int o = 4; o > 0; o >>= 1) {
-    s += __shfl_xor(s, o);
-    k2 += __shfl_xor(k2, o);
-  }
-  *z2 = k2;
-  return s - 0.5 * bj;
-}
-
-// Four entries per wave, 16 lanes each: lanes 0-7 of a group score j0, lanes 8-15 j1.  The
-// workgroups on XCD x take the entries of list region x (listed by the coarse pass on that
-// XCD, so the heads whose rows they read are the ones cached in that XCD's L2).  Without L
-// the rows are the fp32 codebook itself (v = c exactly), half the bytes of the fp64 copy.
-template <int DT>
-__global__ __launch_bounds__(256) void enc_refine(
-    const void* __restrict__ keys, int64_t n, int64_t c, const double* __restrict__ v64,
-    const float* __restrict__ v32, int plain,
-    const double* __restrict__ b64, const RefEntry* __restrict__ refl, uint16_t* __restrict__ codes,
-    float* __restrict__ dist, UncEntry* __restrict__ unc, int64_t unc_cap,
-    FullEntry* __restrict__ full, Counters* __restrict__ cnt, int64_t region, int want_stats) {
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int sub = lane >> 4;          // which entry of the wave
-  const int which = (lane >> 3) & 1;  // candidate 0 or 1
-  const int g = lane & 7;
-  // the list is 8 regions of `region` entries, region x holding cnt->refine_x[x][0]
-  const int xcd = blockIdx.x % 8;
-  const unsigned total = cnt->refine_x[xcd][0];
-  const RefEntry* reg = refl + (int64_t)xcd * region;
-  const int64_t stride = (int64_t)(gridDim.x / 8) * 16;
-  unsigned decided = 0;
-  for (int64_t e0 = (int64_t)(blockIdx.x / 8) * 16 + (t >> 6) * 4; e0 < (int64_t)total; e0 += stride) {
-    const int64_t e = e0 + sub;
-    const bool live = e < (int64_t)total;
-    const RefEntry* rp = reg + (live ? e : 0);
-    int32_t head = 0, row = 0, ja = -1, jb = -1;
-    double thr = 0.0;
-    float rz2 = -1.f;
-    if (live) {
-      const int2 hr = *reinterpret_cast<const int2*>(&rp->head);
-      const int2 jj = *reinterpret_cast<const int2*>(&rp->j0);
-      head = hr.x;
-      row = hr.y;
-      ja = jj.x;
-      jb = jj.y;
-      if ((lane & 15) == 0) {
-        thr = rp->thr;
-        rz2 = rp->z2;
-      }
-    }
-    const int j = which ? jb : ja;
-    double s = -INFINITY, k2 = 0.0;
-    if (j >= 0) {
-      const int64_t off = ((int64_t)head * n + row) * kD;
-      const int64_t vo = ((int64_t)head * c + j) * kD;
-      s = plain ? coop_score8<DT>(keys, off, v32 + vo, b64[(int64_t)head * c + j], g, &k2)
-                : coop_score8<DT>(keys, off, v64 + vo, b64[(int64_t)head * c + j], g, &k2);
-    }
-    const double s_other = __shfl_xor(s, 8);
-    const double k2_other = __shfl_xor(k2, 8);
-    if (live && (lane & 15) == 0) {
-      const double sa = s, sb = s_other;  // lane 0 of the group scored ja, lane 8 jb
-      if (ja < 0) k2 = k2_other;
-      int best = ja;
-      double sbest = sa;
-      if (jb >= 0 && (ja < 0 || sb > sa || (sb == sa && jb < ja))) {
-        best = jb;
-        sbest = sb;
-      }
-      const double z2 = rz2 >= 0.f ? (double)rz2 : k2;
-      const double eps = 0x1p-40 * (fabs(sbest) + k2 + 1.0);
-      if (best >= 0 && sbest - eps > thr) {
-        codes[(int64_t)head * n + row] = (uint16_t)best;
-        if (dist) dist[(int64_t)head * n + row] = (float)fmax(z2 - 2.0 * sbest, 0.0);
-        decided += 1;
-      } else {
-        const unsigned slot = atomicAdd(&cnt->unc[head], 1u);
-        if (best >= 0 && slot < unc_cap) {
-          UncEntry ue;
-          ue.row = row;
-          ue.jbest = best;
-          ue.sbest = sbest;
-          ue.e_unscaled = rp->e_unscaled;
-          ue.z2 = rz2;
-          ue.pad = 0;
-          unc[(int64_t)head * unc_cap + slot] = ue;
-        } else {
-          FullEntry fe;
-          fe.head = head;
-          fe.row = row;
-          fe.z2 = rz2;
-          fe.pad = 0;
-          full[atomicAdd(&cnt->full, 1u)] = fe;
-        }
-      }
-    }
-  }
-  if (want_stats) {  // one atomic per workgroup, per-XCD counter
-    __shared__ unsigned s_dec;
-    if (t == 0) s_dec = 0u;
-    __syncthreads();
-    for (int o = 32; o > 0; o >>= 1) decided += __shfl_xor(decided, o);
-    if (lane == 0 && decided) atomicAdd(&s_dec, decided);
-    __syncthreads();
-    if (t == 0 && s_dec) atomicAdd(&cnt->stat_x[xcd][2], s_dec);
-  }
-}
-
-// Number of listed open keys of a head (capped to the list capacity).
-__device__ __forceinline__ int64_t open_count(const Counters* cnt, int64_t head, int64_t cap) {
-  const unsigned u = __hip_atomic_load(&cnt->unc[head], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return (int64_t)u < cap ? (int64_t)u : cap;
-}
-
-constexpr int kMaxHeadsLds = 1024;
-
-// Exclusive prefix over heads of `per(open count)`, built once per workgroup in LDS
-// (heads <= kMaxHeadsLds; larger head counts fall back to scanning global counters).
-template <typename F>
-__device__ int64_t head_prefix(const Counters* cnt, int64_t heads, int64_t cap, int64_t* pre, F per) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t run = 0;
-    const int64_t hn = heads < kMaxHeadsLds ? heads : kMaxHeadsLds;
-    for (int64_t h = 0; h < hn; ++h) {
-      pre[h] = run;
-      run += per(open_count(cnt, h, cap));
-    }
-    for (int64_t h = hn; h < heads; ++h) run += per(open_count(cnt, h, cap));
-    pre[kMaxHeadsLds] = run;
-  }
-  __syncthreads();
-  return pre[kMaxHeadsLds];
-}
-
-// Head owning global item index `it` (prefix from head_prefix).
-template <typename F>
-__device__ int64_t find_head(const Counters* cnt, int64_t heads, int64_t cap, const int64_t* pre,
-                             int64_t it, F per, int64_t* rest) {
-  const int64_t hn = heads < kMaxHeadsLds ? heads : kMaxHeadsLds;
-  int64_t lo = 0, hi = hn - 1;
-  if (hn > 0 && it < (hn < heads ? pre[hn - 1] + per(open_count(cnt, hn - 1, cap)) : pre[kMaxHeadsLds])) {
-    while (lo < hi) {  // last head with pre[h] <= it
-      const int64_t mid = (lo + hi + 1) / 2;
-      if (pre[mid] <= it) lo = mid;
-      else hi = mid - 1;
-    }
-    *rest = it - pre[lo];
-    return lo;
-  }
-  int64_t run = hn > 0 ? pre[hn - 1] + per(open_count(cnt, hn - 1, cap)) : 0;
-  for (int64_t h = hn; h < heads; ++h) {
-    const int64_t m = per(open_count(cnt, h, cap));
-    if (it < run + m) {
-      *rest = it - run;
-      return h;
-    }
-    run += m;
-  }
-  *rest = 0;
-  return heads - 1;
 }
 
 // ------------------------------------------------------------------ rescan of open keys
@@ -1144,7 +1133,52 @@ __global__ __launch_bounds__(256) void enc_rescan_collect(
   }
 }
 
-// One wave per open key: fp64 over its candidates (8 lanes per candidate, 8 at a time).
+// fp64 scan of the whole codebook for one key by one wave (kx: this wave's LDS row of 128).
+template <int DT>
+__device__ void full_scan_wave(const void* keys, int64_t n, int64_t c, const double* v64,
+                               const double* b64, int64_t head, int64_t row, float z2f,
+                               uint16_t* codes, float* dist, double* kx, int lane) {
+  const int64_t off = (head * n + row) * kD;
+  wave_sync();
+  kx[lane] = (double)load_elem(keys, DT, off + lane);
+  kx[lane + 64] = (double)load_elem(keys, DT, off + lane + 64);
+  wave_sync();
+  double best = -INFINITY;
+  int bj = 0x7FFFFFFF;
+  for (int64_t j = lane; j < c; j += 64) {
+    const double* v = v64 + (head * c + j) * kD;
+    double sj = 0.0;
+    for (int a = 0; a < kD; ++a) sj += kx[a] * v[a];
+    sj -= 0.5 * b64[head * c + j];
+    if (sj > best || (sj == best && j < bj)) {
+      best = sj;
+      bj = (int)j;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const double ob = __shfl_xor(best, o);
+    const int oj = __shfl_xor(bj, o);
+    if (ob > best || (ob == best && oj < bj)) {
+      best = ob;
+      bj = oj;
+    }
+  }
+  if (lane == 0) {
+    codes[head * n + row] = (uint16_t)bj;
+    if (dist) {
+      double z2 = z2f;
+      if (z2f < 0.f) {
+        z2 = 0.0;
+        for (int a = 0; a < kD; ++a) z2 += kx[a] * kx[a];
+      }
+      dist[head * n + row] = (float)fmax(z2 - 2.0 * best, 0.0);
+    }
+  }
+}
+
+// One wave per open key: fp64 over its candidates (8 lanes per candidate, 8 at a time); a key
+// whose candidate list overflowed gets the full scan at once.  Then the keys the coarse pass
+// listed for the full scan (fp16-range keys, rescan list overflow).
 template <int DT>
 __global__ __launch_bounds__(256) void enc_rescan_decide(
     const void* __restrict__ keys, int64_t n, int64_t heads, int64_t c,
@@ -1155,9 +1189,10 @@ __global__ __launch_bounds__(256) void enc_rescan_decide(
     FullEntry* __restrict__ full, Counters* __restrict__ cnt) {
   const int t = threadIdx.x, lane = t & 63, g = lane & 7, q8 = lane >> 3;
   __shared__ int64_t pre[kMaxHeadsLds + 1];
+  __shared__ double kx[4][kD];
   auto per = [](int64_t m) { return m; };
   const int64_t total = head_prefix(cnt, heads, unc_cap, pre, per);
-  unsigned decided = 0;
+  unsigned decided = 0, full_scans = 0;
   for (int64_t e = (int64_t)blockIdx.x * 4 + (t >> 6); e < total; e += (int64_t)gridDim.x * 4) {
     int64_t rest = 0;
     const int64_t head = find_head(cnt, heads, unc_cap, pre, e, per, &rest);
@@ -1165,14 +1200,8 @@ __global__ __launch_bounds__(256) void enc_rescan_decide(
     const UncEntry ue = unc[slot];
     const unsigned nc = cand_n[slot];
     if (nc > (unsigned)kCandCap) {
-      if (lane == 0) {
-        FullEntry fe;
-        fe.head = (int32_t)head;
-        fe.row = ue.row;
-        fe.z2 = ue.z2;
-        fe.pad = 0;
-        full[atomicAdd(&cnt->full, 1u)] = fe;
-      }
+      full_scan_wave<DT>(keys, n, c, v64, b64, head, ue.row, ue.z2, codes, dist, kx[t >> 6], lane);
+      if (lane == 0) full_scans += 1;
       continue;
     }
     const int64_t off = ((int64_t)head * n + ue.row) * kD;
@@ -1216,59 +1245,16 @@ __global__ __launch_bounds__(256) void enc_rescan_decide(
       decided += 1;
     }
   }
+  const unsigned nfull = __hip_atomic_load(&cnt->full, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int64_t e = (int64_t)blockIdx.x * 4 + (t >> 6); e < (int64_t)nfull; e += (int64_t)gridDim.x * 4) {
+    const FullEntry fe = full[e];
+    full_scan_wave<DT>(keys, n, c, v64, b64, fe.head, fe.row, fe.z2, codes, dist, kx[t >> 6], lane);
+    if (lane == 0) full_scans += 1;
+  }
   if (lane == 0 && decided) atomicAdd(&cnt->stats[3], decided);
+  if (lane == 0 && full_scans) atomicAdd(&cnt->stats[4], full_scans);
 }
 
-// fp64 scan of the whole codebook, one wave per listed key.
-template <int DT>
-__global__ __launch_bounds__(256) void enc_fullscan(
-    const void* __restrict__ keys, int64_t n, int64_t c, const double* __restrict__ v64,
-    const double* __restrict__ b64, uint16_t* __restrict__ codes, float* __restrict__ dist,
-    const FullEntry* __restrict__ full, Counters* __restrict__ cnt) {
-  __shared__ double kx[4][kD];
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  const unsigned total = __hip_atomic_load(&cnt->full, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (int64_t e = (int64_t)blockIdx.x * 4 + wave; e < (int64_t)total; e += (int64_t)gridDim.x * 4) {
-    const FullEntry fe = full[e];
-    const int64_t off = ((int64_t)fe.head * n + fe.row) * kD;
-    wave_sync();
-    kx[wave][lane] = (double)load_elem(keys, DT, off + lane);
-    kx[wave][lane + 64] = (double)load_elem(keys, DT, off + lane + 64);
-    wave_sync();
-    double best = -INFINITY;
-    int bj = 0x7FFFFFFF;
-    for (int64_t j = lane; j < c; j += 64) {
-      const double* v = v64 + ((int64_t)fe.head * c + j) * kD;
-      double sj = 0.0;
-      for (int a = 0; a < kD; ++a) sj += kx[wave][a] * v[a];
-      sj -= 0.5 * b64[(int64_t)fe.head * c + j];
-      if (sj > best || (sj == best && j < bj)) {
-        best = sj;
-        bj = (int)j;
-      }
-    }
-    for (int o = 32; o > 0; o >>= 1) {
-      const double ob = __shfl_xor(best, o);
-      const int oj = __shfl_xor(bj, o);
-      if (ob > best || (ob == best && oj < bj)) {
-        best = ob;
-        bj = oj;
-      }
-    }
-    if (lane == 0) {
-      codes[(int64_t)fe.head * n + fe.row] = (uint16_t)bj;
-      if (dist) {
-        double z2 = fe.z2;
-        if (fe.z2 < 0.f) {
-          z2 = 0.0;
-          for (int a = 0; a < kD; ++a) z2 += kx[wave][a] * kx[wave][a];
-        }
-        dist[(int64_t)fe.head * n + fe.row] = (float)fmax(z2 - 2.0 * best, 0.0);
-      }
-      atomicAdd(&cnt->stats[4], 1u);
-    }
-  }
-}
 
 // ||k L||^2 in fp64, one wave per selected key (fp32 keys with distances and L).
 __global__ __launch_bounds__(256) void enc_znorm64(const float* __restrict__ keys, int64_t n,
@@ -1300,13 +1286,21 @@ __global__ __launch_bounds__(256) void enc_znorm64(const float* __restrict__ key
   }
 }
 
+// The run's list and candidate counters start at zero (a fill kernel, not a memset node).
+__global__ void enc_clear(unsigned* __restrict__ cnt, int ncnt, unsigned* __restrict__ cand_n,
+                          int64_t ncand) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t k = i; k < ncnt; k += stride) cnt[k] = 0u;
+  for (int64_t k = i; k < ncand; k += stride) cand_n[k] = 0u;
+}
+
 __global__ void enc_stats_out(const Counters* __restrict__ cnt, a2ats_encode_stats* out) {
   if (threadIdx.x == 0) {
-    unsigned keys = 0, direct = 0, listed = 0;
+    unsigned keys = 0, direct = 0;
     for (int x = 0; x < 8; ++x) {
       keys += cnt->stat_x[x][0];
       direct += cnt->stat_x[x][1];
-      listed += cnt->refine_x[x][0];
     }
     out->keys = keys;
     out->direct = direct;
@@ -1315,7 +1309,7 @@ __global__ void enc_stats_out(const Counters* __restrict__ cnt, a2ats_encode_sta
     out->reranked = reranked;
     out->rescanned = cnt->stats[3];
     out->full_scan = cnt->stats[4];
-    out->reserved[0] = listed;
+    out->reserved[0] = 0;
     out->reserved[1] = cnt->full;
     out->reserved[2] = 0;
   }
@@ -1325,12 +1319,6 @@ __global__ void enc_stats_out(const Counters* __restrict__ cnt, a2ats_encode_sta
 inline int64_t unc_capacity(int64_t n) {
   const int64_t cap = n / 8;
   return cap < 1024 ? (n < 1024 ? n : 1024) : cap;
-}
-
-// Coarse-pass workgroups per XCD for n keys a head (the grid is a multiple of 8); each XCD
-// appends its rerank entries to a region of refine_regions * kKeysPerWG entries.
-inline int64_t refine_regions(int64_t heads, int64_t n) {
-  return (heads * ((n + kKeysPerWG - 1) / kKeysPerWG) + 7) / 8;
 }
 
 struct EncLayout {
@@ -1343,7 +1331,6 @@ struct EncLayout {
   float* part_a;
   float* part_b;
   unsigned* cnt;
-  RefEntry* refl;
   UncEntry* unc;
   FullEntry* full;
   unsigned* cand_n;
@@ -1379,7 +1366,6 @@ EncLayout carve(void* ws, int64_t heads, int64_t n, int64_t c) {
   L.hsc = cv.take<HeadScale>((size_t)heads);
   L.gram = cv.take<double>((size_t)heads * kD * kD);
   L.cnt = cv.take<unsigned>((size_t)L.ncnt);
-  L.refl = cv.take<RefEntry>((size_t)refine_regions(heads, n) * 8 * kKeysPerWG);
   L.unc = cv.take<UncEntry>((size_t)heads * L.unc_cap);
   L.full = cv.take<FullEntry>((size_t)heads * n);
   L.cand_n = cv.take<unsigned>((size_t)heads * L.unc_cap);
@@ -1389,27 +1375,38 @@ EncLayout carve(void* ws, int64_t heads, int64_t n, int64_t c) {
   return L;
 }
 
-template <int DT>
-int encode_typed(const void* keys, int64_t heads, int64_t n, const int32_t* idx, int64_t n_sel,
-                 const float* codebook, int64_t c, const float* chol, uint16_t* codes,
-                 float* dist, a2ats_encode_stats* stats, const EncLayout& L, hipStream_t s) {
+// Codebook-side preparation: M = L L^T (with L), v, b, the fp16 fragments, the bias and the
+// per-head scales.  Depends on the codebook and L only.
+int encode_prepare(int64_t heads, const float* codebook, int64_t c, const float* chol,
+                   const EncLayout& L, hipStream_t s) {
   const int T = (int)tiles_of(c);
-  // packed into the low bits of the coarse pass: (tile << 1 | parity)
-  int tbits = 1;
-  while ((1 << (tbits - 1)) < T) ++tbits;
   const bool plain = chol == nullptr;
-  Counters* cnt = reinterpret_cast<Counters*>(L.cnt);
   if (!plain)
     A2ATS_TRY(launch("encode_prep_gram", enc_prep_gram, dim3(kD / 8, (unsigned)heads), dim3(256), 0, s,
                      chol, L.gram, L.part_a, L.nwg_a));
   A2ATS_TRY(launch("encode_prep_rows", enc_prep_rows, dim3((unsigned)L.nwg_a, (unsigned)heads),
                    dim3(256), 0, s, codebook, c, plain ? nullptr : L.gram, L.v64, L.v32, L.b64,
                    L.part_a, L.nwg_a));
+  return launch("encode_prep_frag", enc_prep_frag, dim3((unsigned)L.nwg_b, (unsigned)heads),
+                dim3(256), 0, s, L.v64, L.b64, c, T, chol, (int)!plain, L.part_a, L.nwg_a,
+                L.part_b, L.v16, L.bias, L.lfrag, L.hsc);
+}
+
+// Key-side pass over a prepared workspace.
+template <int DT>
+int encode_run(const void* keys, int64_t heads, int64_t n, const int32_t* idx, int64_t n_sel,
+               int64_t c, const float* chol, uint16_t* codes, float* dist,
+               a2ats_encode_stats* stats, const EncLayout& L, hipStream_t s) {
+  const int T = (int)tiles_of(c);
+  // packed into the low bits of the coarse pass: (tile << 1 | parity)
+  int tbits = 1;
+  while ((1 << (tbits - 1)) < T) ++tbits;
+  const bool plain = chol == nullptr;
+  Counters* cnt = reinterpret_cast<Counters*>(L.cnt);
+  const int64_t ncand = heads * L.unc_cap;
+  A2ATS_TRY(launch("encode_clear", enc_clear, dim3(grid_for(std::max<int64_t>(ncand, L.ncnt), 256, 1024)),
+                   dim3(256), 0, s, L.cnt, L.ncnt, L.cand_n, ncand));
   const bool znorm_mfma = dist && !plain && DT == A2ATS_BF16;
-  A2ATS_TRY(launch("encode_prep_frag", enc_prep_frag, dim3((unsigned)L.nwg_b, (unsigned)heads),
-                   dim3(256), 0, s, L.v64, L.b64, c, T, chol, (int)znorm_mfma, L.part_a, L.nwg_a,
-                   L.part_b, L.v16, L.bias, L.lfrag, L.cnt, L.ncnt, L.hsc, L.cand_n,
-                   heads * L.unc_cap));
   float* znorm = nullptr;
   if (dist && !plain) {
     znorm = L.znorm;
@@ -1424,26 +1421,18 @@ int encode_typed(const void* keys, int64_t heads, int64_t n, const int32_t* idx,
 #define A2ATS_COARSE(Z, DI)                                                                       \
   launch(name, enc_coarse<DT, Z, DI>, dim3((unsigned)G), dim3(256), 0, s, keys, n, idx, n_sel,   \
          heads, nkb, T, tbits, L.v16, L.bias, L.v32, L.b64, c, L.lfrag, L.hsc,                    \
-         L.part_b, L.nwg_b, znorm, codes, dist, L.refl, L.full, cnt, stats ? 1 : 0)
+         L.part_b, L.nwg_b, znorm, codes, dist, plain ? nullptr : L.v64, L.unc, L.unc_cap, L.full,   \
+         cnt, stats ? 1 : 0)
   if (znorm_mfma) A2ATS_TRY(A2ATS_COARSE(true, true));
   else if (dist) A2ATS_TRY(A2ATS_COARSE(false, true));
   else A2ATS_TRY(A2ATS_COARSE(false, false));
 #undef A2ATS_COARSE
-  // up to 16 entries per workgroup and pass; at most one entry per key
-  const unsigned rblocks =
-      (unsigned)std::min<int64_t>(2048, std::max<int64_t>(8, (heads * n_sel + 127) / 128 * 8));
-  A2ATS_TRY(launch("encode_refine", enc_refine<DT>, dim3(rblocks), dim3(256), 0, s, keys, n, c, L.v64,
-                   L.v32, plain ? 1 : 0,
-                   L.b64, L.refl, codes, dist, L.unc, L.unc_cap, L.full, cnt,
-                   (int64_t)(G / 8) * kKeysPerWG, stats ? 1 : 0));
   A2ATS_TRY(launch("encode_rescan_collect", enc_rescan_collect<DT>, dim3(512), dim3(256), 0, s, keys,
                    n, heads, T, c, L.v16, L.bias, L.hsc, L.unc, L.unc_cap, cnt,
                    L.cand_n, L.cand));
   A2ATS_TRY(launch("encode_rescan_decide", enc_rescan_decide<DT>, dim3(256), dim3(256), 0, s, keys, n,
                    heads, c, L.v64, L.v32, plain ? 1 : 0, L.b64, L.unc, L.unc_cap, L.cand_n, L.cand, codes, dist, L.full,
                    cnt));
-  A2ATS_TRY(launch("encode_fullscan", enc_fullscan<DT>, dim3(128), dim3(256), 0, s, keys, n, c, L.v64,
-                   L.b64, codes, dist, L.full, cnt));
   if (stats)
     A2ATS_TRY(launch("encode_stats", enc_stats_out, dim3(1), dim3(64), 0, s, cnt, stats));
   return A2ATS_OK;
@@ -1459,26 +1448,68 @@ extern "C" size_t a2ats_encode_workspace(int64_t heads, int64_t n, int64_t d, in
   return carve(nullptr, heads, n, c).bytes;
 }
 
+static int encode_check_keys(const void* keys, int keys_dtype, int64_t heads, int64_t n, int64_t d,
+                             const int32_t* idx, int64_t n_idx, int64_t c, uint16_t* codes,
+                             int64_t* n_sel) {
+  if (keys_dtype != A2ATS_F32 && keys_dtype != A2ATS_BF16) return A2ATS_EDTYPE;
+  if (d != kD || heads < 1 || n < 0 || c < 1 || c > 65536) return A2ATS_EINVAL;
+  if (n > 0x7FFFFFFF || heads > 65535) return A2ATS_EINVAL;
+  *n_sel = idx ? n_idx : n;
+  if (*n_sel < 0 || *n_sel > n) return A2ATS_EINVAL;
+  if (*n_sel == 0) return A2ATS_OK;
+  if (!keys || !codes) return A2ATS_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(keys) & 15) != 0) return A2ATS_EINVAL;
+  return A2ATS_OK;
+}
+
+static int encode_dispatch(const void* keys, int keys_dtype, int64_t heads, int64_t n,
+                           const int32_t* idx, int64_t n_sel, int64_t c, const float* chol,
+                           uint16_t* codes, float* dist, a2ats_encode_stats* stats,
+                           const EncLayout& L, hipStream_t s) {
+  if (keys_dtype == A2ATS_BF16)
+    return encode_run<A2ATS_BF16>(keys, heads, n, idx, n_sel, c, chol, codes, dist, stats, L, s);
+  return encode_run<A2ATS_F32>(keys, heads, n, idx, n_sel, c, chol, codes, dist, stats, L, s);
+}
+
 extern "C" int a2ats_encode(const void* keys, int keys_dtype, int64_t heads, int64_t n, int64_t d,
                             const int32_t* idx, int64_t n_idx, const float* codebook, int64_t c,
                             const float* chol, uint16_t* codes, float* dist,
                             a2ats_encode_stats* stats, void* workspace, size_t workspace_bytes,
                             void* stream) {
-  if (keys_dtype != A2ATS_F32 && keys_dtype != A2ATS_BF16) return A2ATS_EDTYPE;
-  if (d != kD || heads < 1 || n < 0 || c < 1 || c > 65536) return A2ATS_EINVAL;
-  if (n > 0x7FFFFFFF || heads > 65535) return A2ATS_EINVAL;
-  const int64_t n_sel = idx ? n_idx : n;
-  if (n_sel < 0 || n_sel > n) return A2ATS_EINVAL;
+  int64_t n_sel = 0;
+  A2ATS_TRY(encode_check_keys(keys, keys_dtype, heads, n, d, idx, n_idx, c, codes, &n_sel));
   if (n_sel == 0) return A2ATS_OK;
-  if (!keys || !codebook || !codes) return A2ATS_EINVAL;
-  if ((reinterpret_cast<uintptr_t>(keys) & 15) != 0) return A2ATS_EINVAL;
+  if (!codebook) return A2ATS_EINVAL;
   const size_t need = a2ats_encode_workspace(heads, n, d, c);
   if (!ws_ok(workspace, workspace_bytes, need)) return A2ATS_EWORKSPACE;
   EncLayout L = carve(workspace, heads, n, c);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (keys_dtype == A2ATS_BF16)
-    return encode_typed<A2ATS_BF16>(keys, heads, n, idx, n_sel, codebook, c, chol, codes, dist,
-                                    stats, L, s);
-  return encode_typed<A2ATS_F32>(keys, heads, n, idx, n_sel, codebook, c, chol, codes, dist, stats,
-                                 L, s);
+  A2ATS_TRY(encode_prepare(heads, codebook, c, chol, L, s));
+  return encode_dispatch(keys, keys_dtype, heads, n, idx, n_sel, c, chol, codes, dist, stats, L, s);
+}
+
+extern "C" int a2ats_encode_prepare(const float* codebook, int64_t c, const float* chol,
+                                    int64_t heads, int64_t n, int64_t d, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (d != kD || heads < 1 || heads > 65535 || n < 0 || n > 0x7FFFFFFF || c < 1 || c > 65536)
+    return A2ATS_EINVAL;
+  if (!codebook) return A2ATS_EINVAL;
+  const size_t need = a2ats_encode_workspace(heads, n, d, c);
+  if (!ws_ok(workspace, workspace_bytes, need)) return A2ATS_EWORKSPACE;
+  return encode_prepare(heads, codebook, c, chol, carve(workspace, heads, n, c),
+                        static_cast<hipStream_t>(stream));
+}
+
+extern "C" int a2ats_encode_prepared(const void* keys, int keys_dtype, int64_t heads, int64_t n,
+                                     int64_t d, const int32_t* idx, int64_t n_idx, int64_t c,
+                                     const float* chol, uint16_t* codes, float* dist,
+                                     a2ats_encode_stats* stats, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  int64_t n_sel = 0;
+  A2ATS_TRY(encode_check_keys(keys, keys_dtype, heads, n, d, idx, n_idx, c, codes, &n_sel));
+  if (n_sel == 0) return A2ATS_OK;
+  const size_t need = a2ats_encode_workspace(heads, n, d, c);
+  if (!ws_ok(workspace, workspace_bytes, need)) return A2ATS_EWORKSPACE;
+  return encode_dispatch(keys, keys_dtype, heads, n, idx, n_sel, c, chol, codes, dist, stats,
+                         carve(workspace, heads, n, c), static_cast<hipStream_t>(stream));
 }

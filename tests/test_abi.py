@@ -91,6 +91,36 @@ def test_encode_validation(L):
     assert call(idx=FAKE, n_idx=0) == 0
 
 
+def test_encode_prepare_validation(L):
+    ws_need = L.a2ats_encode_workspace(2, 100, 128, 50)
+
+    def prep(cb=FAKE, c=50, heads=2, n=100, d=128, wsb=ws_need):
+        return L.a2ats_encode_prepare(cb, c, None, heads, n, d, FAKE, wsb, None)
+
+    assert prep(cb=None) == EINVAL
+    assert prep(c=0) == EINVAL
+    assert prep(c=65537) == EINVAL
+    assert prep(d=64) == EINVAL
+    assert prep(heads=0) == EINVAL
+    assert prep(n=-1) == EINVAL
+    assert prep(wsb=ws_need - 1) == EWORKSPACE
+
+    def run(keys=FAKE, dt=1, n=100, d=128, idx=None, n_idx=0, c=50, codes=FAKE, wsb=ws_need):
+        return L.a2ats_encode_prepared(keys, dt, 2, n, d, idx, n_idx, c, None, codes, None, None,
+                                       FAKE, wsb, None)
+
+    assert run(dt=5) == EDTYPE
+    assert run(d=64) == EINVAL
+    assert run(c=0) == EINVAL
+    assert run(idx=FAKE, n_idx=101) == EINVAL
+    assert run(keys=None) == EINVAL
+    assert run(codes=None) == EINVAL
+    assert run(keys=ctypes.c_void_p(4098)) == EINVAL
+    assert run(wsb=ws_need - 1) == EWORKSPACE
+    assert run(n=0) == 0                   # nothing to encode: no launch
+    assert run(idx=FAKE, n_idx=0) == 0
+
+
 def test_assign_cosine_validation(L):
     def call(dt=0, heads=1, n=4, d=128, nq=1, c=8, beta=0.5, x=FAKE):
         return L.a2ats_assign_cosine(x, dt, heads, n, d, FAKE, nq, FAKE, c, beta, FAKE, None)

@@ -142,6 +142,24 @@ class TestEncode:
         check_codes(u16_to_np(out)[0], code, d1, d2, "large keys")
         check_dist(dist.cpu().numpy()[0], d1, z2_of(keys.values[0], None), "large keys")
 
+    @pytest.mark.parametrize("use_h", [False, True])
+    def test_prepared_runs_match_one_shot(self, use_h):
+        # one prepare, two runs (all rows, then a subset of other keys): each equals encode()
+        w = synth.Workload("prepared", 120, 2, 1500, 300, "bf16", m=400)
+        cb = f32_to_dev(synth.codebook(w.cfg, w.heads, w.c))
+        L = f32_to_dev(oracle_L(w.cfg, w.heads, w.m)) if use_h else None
+        prep = kv.encode_prepare(cb, L, w.n)
+        k1 = keys_to_dev(synth.keys(w.cfg, w.heads, w.n, "bf16"))
+        k2 = keys_to_dev(synth.keys(w.cfg + 1, w.heads, w.n, "bf16"))
+        rng = np.random.default_rng(5)
+        idx = torch.from_numpy(np.stack([np.sort(rng.choice(w.n, 700, replace=False))
+                                         for _ in range(w.heads)]).astype(np.int32)).to(DEV)
+        for keys, ix in ((k1, None), (k2, idx)):
+            a = kv.encode_prepared(keys, prep, idx=ix, want_dist=True)
+            b = kv.encode(keys, cb, L, idx=ix, want_dist=True)
+            assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+            assert torch.equal(a[1], b[1])
+
     def test_deterministic(self):
         w = W["tiny"]
         keys = keys_to_dev(synth.keys(w.cfg, 1, w.n, w.key_dtype))
@@ -332,6 +350,38 @@ class TestReconstruct:
 
 # ====================================================================== pipeline
 class TestPipeline:
+    def test_two_streams_prepared_equals_sequential(self):
+        # the benchmark's step: prepares and the H-weighted encode on a second stream
+        w = W["layer"]
+        keys = synth.keys(w.cfg, w.heads, w.n, w.key_dtype)
+        kd, cbd = keys_to_dev(keys), f32_to_dev(synth.codebook(w.cfg, w.heads, w.c))
+        H, L = kv.calibrate(f32_to_dev(synth.queries(w.cfg, w.heads, w.m)), 1e-4)
+        proxy = kd[:, -1].contiguous()
+        ret, bulk = kv.select_retrieval(kd, proxy, w.fraction)
+        seq = kv.encode(kd, cbd, None)
+        seq = kv.encode(kd, cbd, L, idx=ret, codes=seq)
+        aux = torch.cuda.Stream(device=DEV)
+        main = torch.cuda.current_stream(DEV)
+        codes = torch.zeros((w.heads, w.n), dtype=torch.uint16, device=DEV)
+        for _ in range(3):  # repeated steps reuse nothing but the tensors above
+            aux.wait_event(main.record_event())
+            with torch.cuda.stream(aux):
+                pp = kv.encode_prepare(cbd, None, w.n)
+                ph = kv.encode_prepare(cbd, L, w.n)
+                prep_done = aux.record_event()
+            r2, b2 = kv.select_retrieval(kd, proxy, w.fraction)
+            split_done = main.record_event()
+            main.wait_event(prep_done)
+            kv.encode_prepared(kd, pp, idx=b2, codes=codes)
+            aux.wait_event(split_done)
+            with torch.cuda.stream(aux):
+                kv.encode_prepared(kd, ph, idx=r2, codes=codes)
+            main.wait_event(aux.record_event())
+            torch.cuda.synchronize()
+            assert torch.equal(codes.view(torch.int16), seq.view(torch.int16))
+            del pp, ph
+
+
     @pytest.mark.parametrize("name", ["layer", "long_context"])
     def test_split_encode_reconstruct(self, name):
         w = W[name]
