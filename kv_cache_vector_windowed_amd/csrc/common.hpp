@@ -115,6 +115,18 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
 // Workgroup barrier that orders LDS only: waits for this wave's LDS operations, then
 // s_barrier.  Unlike __syncthreads() it does not wait for outstanding global loads, so a
 // prefetch issued before it stays in flight across the barrier.
+// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4): the LDS address
+// is the wave-uniform ldst plus 16 x the lane index.  Completion is counted by vmcnt.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, void* ldst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                   (__attribute__((address_space(3))) void*)ldst, 16, 0, 0);
+}
+
+// Barrier after this wave's LDS loads (direct and DS) have completed.
+__device__ __forceinline__ void lds_dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }

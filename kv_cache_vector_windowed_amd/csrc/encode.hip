@@ -727,8 +727,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float* __restrict__ znorm, uint16_t* __restrict__ codes, float* __restrict__ dist,
     const double* __restrict__ v64, UncEntry* __restrict__ unc, int64_t unc_cap,
     FullEntry* __restrict__ full, Counters* __restrict__ cnt, int want_stats) {
-  __shared__ half8 sv[2][kTPS][kFragPerTile];
-  __shared__ __attribute__((aligned(16))) float sb[2][kTPS][32];
+  // two stage buffers as separate arrays: the compiler then sees that the loads streaming
+  // into one buffer cannot alias the LDS reads of the other, and does not wait for them
+  __shared__ half8 sv0[kTPS][kFragPerTile], sv1[kTPS][kFragPerTile];
+  __shared__ __attribute__((aligned(16))) float sb0[kTPS][32], sb1[kTPS][32];
   __shared__ float s_red[2][4];
   const int64_t G = gridDim.x;
   const int64_t per_xcd = G / 8;
@@ -756,32 +758,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   const half8* vh = v16 + head * (int64_t)T * kFragPerTile;
   const float* bh = bias + head * (int64_t)T * 32;
-  // stage loader: a stage is kTPS tiles (32 KiB of fragments, 512 B of bias); 256 threads x
-  // 8 fragments, 32 threads x 4 bias floats.  Loads for stage s+2 are issued when stage s+1
-  // is committed, so each load has a whole stage of MFMA work to arrive.
+  // stage loader: a stage is kTPS tiles (32 KiB of fragments, 512 B of bias), loaded straight
+  // into LDS (global_load_lds_dwordx4: lane l of a wave writes 16 B at the wave's LDS base +
+  // 16 l); 256 threads x 8 fragments, 32 threads x 4 bias floats.  Stage s+1 is loaded while
+  // stage s is computed: its loads go out at the start of stage s, right after the barrier
+  // that freed its buffer, so no load is in flight across the loop's back edge.
   const int nst = (T + kTPS - 1) / kTPS;
-  half8 pf[kTPS][2];
-  f4 pb = {};
-  auto fetch = [&](int st) {
+  auto load_stage = [&](int st, half8 (&svb)[kTPS][kFragPerTile], float (&sbb)[kTPS][32]) {
     const half8* src = vh + (int64_t)st * kTPS * kFragPerTile;
 #pragma unroll
     for (int q = 0; q < kTPS; ++q) {
-      pf[q][0] = src[q * kFragPerTile + t];
-      pf[q][1] = src[q * kFragPerTile + 256 + t];
+      lds_dma16(src + q * kFragPerTile + t, &svb[q][wave * 64]);
+      lds_dma16(src + q * kFragPerTile + 256 + t, &svb[q][256 + wave * 64]);
     }
-    if (t < 8 * kTPS) pb = *reinterpret_cast<const f4*>(bh + (int64_t)st * kTPS * 32 + t * 4);
+    if (t < 8 * kTPS) lds_dma16(bh + (int64_t)st * kTPS * 32 + t * 4, &sbb[0][0]);
   };
-  auto commit = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < kTPS; ++q) {
-      sv[buf][q][t] = pf[q][0];
-      sv[buf][q][256 + t] = pf[q][1];
-    }
-    if (t < 8 * kTPS) *reinterpret_cast<f4*>(&sb[buf][t / 8][(t % 8) * 4]) = pb;
-  };
-  fetch(0);
-  commit(0);
-  if (nst > 1) fetch(1);
+  load_stage(0, sv0, sb0);
 
   int64_t row[2];
 #pragma unroll
@@ -833,7 +825,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = 0; i < 8; ++i) m1[blk][i] = -INFINITY;
   }
   const unsigned keep = ~((1u << tbits) - 1u);
-  __syncthreads();
+  lds_dma_barrier();  // stage 0 in LDS, s_red visible
 
   // Fold pair i (registers 2i, 2i+1) of one tile's scores into the slot maxima and U.
   float dr[2][8];
@@ -852,8 +844,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     asm volatile("" ::"v"(m1[0][i]), "v"(m1[1][i]));
     if (i & 1) asm volatile("" ::"v"(U[0]), "v"(U[1]));
   };
-  auto load_bias = [&](int buf, int q) {
-    const f4* bl = reinterpret_cast<const f4*>(&sb[buf][q][hh * 16]);
+  auto load_bias = [&](float (&sbb)[kTPS][32], int q) {
+    const f4* bl = reinterpret_cast<const f4*>(&sbb[q][hh * 16]);
     f16v bv;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -874,13 +866,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   f16v x0, x1, y0, y1;
 #pragma unroll
   for (int r = 0; r < 16; ++r) y0[r] = y1[r] = kPadBias;
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
+  auto stage = [&](int st, half8 (&svb)[kTPS][kFragPerTile], float (&sbb)[kTPS][32],
+                   half8 (&svn)[kTPS][kFragPerTile], float (&sbn)[kTPS][32]) {
     const int base = st * kTPS;
     half8 fr[kStageSteps];
 #pragma unroll
-    for (int g = 0; g < kAhead; ++g) fr[g] = sv[buf][g / kSteps][(g % kSteps) * 64 + lane];
-    f16v bv = load_bias(buf, 0);
+    for (int g = 0; g < kAhead; ++g) fr[g] = svb[g / kSteps][(g % kSteps) * 64 + lane];
+    f16v bv = load_bias(sbb, 0);
+    if (st + 1 < nst) load_stage(st + 1, svn, sbn);
 #pragma unroll
     for (int q = 0; q < kTPS; ++q) {
       f16v& a0 = (q & 1) ? y0 : x0;
@@ -895,8 +888,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int s = 0; s < kSteps; ++s) {
         const int g = q * kSteps + s;
         if (g + kAhead < kStageSteps)
-          fr[g + kAhead] = sv[buf][(g + kAhead) / kSteps][((g + kAhead) % kSteps) * 64 + lane];
-        if (s == kSteps - 2 && q + 1 < kTPS) bn = load_bias(buf, q + 1);
+          fr[g + kAhead] = svb[(g + kAhead) / kSteps][((g + kAhead) % kSteps) * 64 + lane];
+        if (s == kSteps - 2 && q + 1 < kTPS) bn = load_bias(sbb, q + 1);
         a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[g], kf.f[0][s], s == 0 ? bv : a0, 0, 0, 0);
         a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[g], kf.f[1][s], s == 0 ? bv : a1, 0, 0, 0);
         fold_pair(p0, p1, s, te, to);
@@ -904,9 +897,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       bv = bn;
     }
-    if (st + 1 < nst) commit(buf ^ 1);
-    if (st + 2 < nst) fetch(st + 2);
-    lds_barrier();
+    lds_dma_barrier();  // this wave's loads of stage st+1 landed; this buffer free everywhere
+  };
+  for (int st = 0; st < nst; st += 2) {
+    stage(st, sv0, sb0, sv1, sb1);
+    if (st + 1 < nst) stage(st + 1, sv1, sb1, sv0, sb0);
   }
   {
     const unsigned te = vgpr_of((unsigned)(nst * kTPS - 1) << 1);
@@ -1009,8 +1004,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   // Rerank entries stay in LDS (in the stage buffers, free after the loop) and are settled
   // here, 4 per wave and pass; full-scan entries (rare) go to the global list.
-  RefEntry* s_ref = reinterpret_cast<RefEntry*>(&sv[0][0][0]);
-  static_assert(sizeof(RefEntry) * kKeysPerWG <= sizeof(sv), "rerank list fits the stage buffers");
+  RefEntry* s_ref = reinterpret_cast<RefEntry*>(&sv0[0][0]);
+  static_assert(sizeof(RefEntry) * kKeysPerWG <= sizeof(sv0), "rerank list fits a stage buffer");
   __shared__ unsigned s_cnt, s_base, s_stat[3], s_nref;
   const unsigned xcd = blockIdx.x % 8;
   if (t == 0) s_nref = 0u;
