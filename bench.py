@@ -301,20 +301,31 @@ def traffic_from_profiles(kernel, workload):
 def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
     W = synth.WORKLOADS
     res = {}
-    flush_buf = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device=dev)
+    flush_buf = torch.empty(2 ** 28, dtype=torch.float32, device=dev)  # 1 GiB
 
     def timed(fn, reps, flush=False):
-        tot = 0.0
-        for _ in range(reps):
-            if flush:
-                flush_buf.fill_(1)
+        """ms per call of fn, calls issued back to back on the stream so the host's issue time
+        overlaps the GPU's work.  With flush, a read of a 1 GiB buffer (which evicts the
+        256 MB last-level cache with clean lines) precedes every call, and the same number of
+        reads timed alone is subtracted."""
+        def run(with_fn):
+            torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            fn()
+            for _ in range(reps):
+                if flush:
+                    flush_buf.sum()
+                if with_fn:
+                    fn()
             b.record()
             torch.cuda.synchronize()
-            tot += a.elapsed_time(b)
-        return tot / reps
+            return a.elapsed_time(b)
+
+        fn()
+        t = run(True)
+        if flush:
+            t -= run(False)
+        return t / reps
 
     # large-codebook encode
     w = W["encode_stress"]
@@ -372,6 +383,7 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
     res["decode"] = {
         "workload": "32 sequences x 8 heads x 16384 tokens, fp32 out, W=256; blend of 256 new keys",
         "reconstruct_ms": round(ms_r, 4), "reconstruct_GBps": round(alg / (ms_r * 1e-3) / 1e9, 1),
+        "reconstruct_call_hbm_frac": round(alg / (ms_r * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "reconstruct_kernel_us": round(kr * 1e3, 2),
         "reconstruct_kernel_GBps": round(alg / (kr * 1e-3) / 1e9, 1),
         "reconstruct_hbm_frac": round(alg / (kr * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -419,22 +431,23 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
 
     pipe()
     torch.cuda.synchronize()
-    ms_s = timed(split, 5, flush=True)
-    ms_r = timed(rec2, 5, flush=True)
-    ms_p = timed(pipe, 3)
+    ms_s = timed(split, 10, flush=True)
+    ms_r = timed(rec2, 10, flush=True)
+    ms_p = timed(pipe, 5)
     split_bytes = w.heads * w.n * (128 * 2 + 4)
     rec_bytes = w.heads * w.n * (2 + 128 * 2) + w.n * 4 + w.heads * w.c * 128 * 4
-    pr = profile(pipe, 3)
-    split_kernels = sum(v[1] for k, v in pr.items() if k.startswith("select_"))
+    pr_s = profile(split, 5)
+    pr_r = profile(rec2, 5)
     res["long_context"] = {
         "workload": "8 heads x 131072 bf16 keys, 5% split, C=2048, W=1024, bf16 reconstruct",
         "pipeline_ms": round(ms_p, 4), "keys_per_s": round(w.heads * w.n / (ms_p * 1e-3), 1),
         "split_ms": round(ms_s, 4), "split_GBps": round(split_bytes / (ms_s * 1e-3) / 1e9, 1),
         "split_hbm_frac": round(split_bytes / (ms_s * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "split_kernels_us": round(split_kernels * 1e3, 2),
+        "split_kernels_us": {k: round(v[1] * 1e3, 2) for k, v in pr_s.items()},
         "reconstruct_ms": round(ms_r, 4), "reconstruct_GBps": round(rec_bytes / (ms_r * 1e-3) / 1e9, 1),
         "reconstruct_hbm_frac": round(rec_bytes / (ms_r * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "kernels_us": {k: round(v[1] * 1e3, 2) for k, v in pr.items()},
+        "reconstruct_kernels_us": {k: round(v[1] * 1e3, 2) for k, v in pr_r.items()},
+        "pipeline_kernels_us": {k: round(v[1] * 1e3, 2) for k, v in profile(pipe, 3).items()},
     }
     log("long_context %s" % res["long_context"])
     return res

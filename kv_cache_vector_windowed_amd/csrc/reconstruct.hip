@@ -15,12 +15,13 @@
 //                keys stay unrotated).
 //   rope_gather  HBM-write-bound stream: each thread owns a fixed group of P pairs of the
 //                head dimension (P = 4 for fp32 output, 8 for bf16, so every store is 16 B),
-//                keeps the far row's cos/sin for its pairs in registers, gathers the
-//                centroid from L2, rotates (fp64 for fp32 output, fp32 for bf16 output),
-//                rounds once, and writes with non-temporal stores.  Work items are
-//                (batch, head, 64-token chunk); item k has head k % heads and the grid is a multiple of 8 * heads, so a workgroup
-//                always serves one head and, with 8 heads, each XCD (workgroups are dealt
-//                round-robin over the 8 XCDs) keeps a single head's codebook in its L2.
+//                takes the far row's cos/sin for its pairs from a copy the workgroup stages
+//                in LDS, gathers the centroid from L2, rotates (fp64 for fp32 output, fp32
+//                for bf16 output), rounds once, and writes with non-temporal stores.  Work
+//                items are (batch, head, 64-token chunk); item k has head k % heads and the
+//                grid is a multiple of 8 * heads, so a workgroup always serves one head and,
+//                with 8 heads, each XCD (workgroups are dealt round-robin over the 8 XCDs)
+//                keeps a single head's codebook in its L2.
 #include <type_traits>
 
 #include "common.hpp"
@@ -34,7 +35,15 @@ typedef double d2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = A2ATS_HEAD_DIM;
 constexpr int kHalf = kD / 2;
-constexpr int kChunk = 64;  // tokens per work item
+constexpr int kChunkF32 = 64;   // tokens per work item, fp32 output
+constexpr int kChunkBf16 = 64;  // tokens per work item, bf16 output
+// Work items per workgroup (the grid is rounded to a multiple of 8 * heads and is at least
+// kGridMin).  Few items per workgroup measure best: a later item's loads would wait, in
+// order, behind the earlier item's stores (one vector memory counter), while the far
+// rotation a workgroup stages in LDS is still shared by 64-128 tokens.
+constexpr int kItemsPerWgF32 = 1;
+constexpr int kItemsPerWgBf16 = 2;
+constexpr int kGridMin = 256;
 
 __global__ __launch_bounds__(256) void rope_table(int64_t rows_near, int64_t cur, int64_t far_pos,
                                                   int far_identity, double base, int d,
@@ -69,10 +78,13 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
 }
 
 // fp32 output: 4 pairs per thread, rotation in fp64, one rounding, two 16-byte stores.
-// bf16 output: 8 pairs per thread, rotation in fp32 (FMA) and one rounding to bf16; the
-// result lies within one bf16 unit of the single rounding of the exact value.
-// Each thread handles U tokens of a 64-token chunk at once: all code / position loads, then
-// all centroid loads, then the rotations and stores, so the dependent loads overlap.
+// bf16 output: 8 pairs per thread, rotation in fp32 and one rounding to bf16; the result lies
+// within one bf16 unit of the single rounding of the exact value.  Both rotations are written
+// as one product and one fused multiply-add, so the rounding steps do not depend on how the
+// compiler contracts the expression.
+// Each thread handles U tokens of a chunk at once.  The codes and positions of the
+// workgroup's next chunk are fetched before the current chunk's centroids are gathered,
+// rotated and stored, so the dependent loads of one chunk overlap the work of the previous.
 template <bool BF16>
 __global__ __launch_bounds__(256) void rope_gather(
     const uint16_t* __restrict__ codes, const int32_t* __restrict__ positions, int64_t heads,
@@ -81,43 +93,56 @@ __global__ __launch_bounds__(256) void rope_gather(
   constexpr int P = BF16 ? 8 : 4;        // pairs per thread
   constexpr int TPT = kHalf / P;         // threads per token
   constexpr int TOK = 256 / TPT;         // tokens per pass of the workgroup
-  constexpr int U = kChunk / TOK;        // tokens per thread per chunk
+  constexpr int CH = BF16 ? kChunkBf16 : kChunkF32;
+  constexpr int U = CH / TOK;            // tokens per thread per chunk
   using real = typename std::conditional<BF16, float, double>::type;
   const int t = threadIdx.x;
   const int g = t % TPT;                 // pair group: pairs [g*P, g*P + P)
   const int tk = t / TPT;
   const int i0 = g * P;
+  // the far rotation, read once per workgroup (one 16-byte load per pair) and shared in LDS
+  __shared__ d2 s_far[kHalf];
+  if (t < kHalf) s_far[t] = table[rows_near * kHalf + t];
+  __syncthreads();
   real fc[P], fs[P];
-  const d2* far_row = table + rows_near * kHalf;
 #pragma unroll
   for (int k = 0; k < P; ++k) {
-    const d2 v = far_row[i0 + k];
+    const d2 v = s_far[i0 + k];
     fc[k] = (real)v.x;
     fs[k] = (real)v.y;
   }
-  const int64_t chunks = (n + kChunk - 1) / kChunk;
-  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+  const int64_t chunks = (n + CH - 1) / CH;
+  int code[U], pos[U];
+  auto fetch = [&](int64_t item, int* cd, int* ps) {
     const int64_t h = item % heads;
     const int64_t rest = item / heads;
     const int64_t b = rest / chunks;
-    const int64_t t0 = (rest % chunks) * kChunk;
-    const float* cbh = cb + h * c * kD;
-    int64_t tok[U];
-    int code[U], pos[U];
+    const int64_t t0 = (rest % chunks) * CH;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      tok[u] = t0 + u * TOK + tk;
-      code[u] = 0;
-      pos[u] = -1;
-      if (tok[u] < n) {
-        code[u] = codes[(b * heads + h) * n + tok[u]];
-        pos[u] = positions[b * n + tok[u]];
+      const int64_t tok = t0 + u * TOK + tk;
+      cd[u] = 0;
+      ps[u] = -1;
+      if (item < items && tok < n) {
+        cd[u] = codes[(b * heads + h) * n + tok];
+        ps[u] = positions[b * n + tok];
       }
     }
+  };
+  fetch(blockIdx.x, code, pos);
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    int ncode[U], npos[U];
+    fetch(item + gridDim.x, ncode, npos);
+    const int64_t h = item % heads;
+    const int64_t rest = item / heads;
+    const int64_t b = rest / chunks;
+    const int64_t t0 = (rest % chunks) * CH;
+    const float* cbh = cb + h * c * kD;
     float xl[U][P], xh[U][P];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool ok = tok[u] < n && code[u] < c && pos[u] >= 0;
+      const int64_t tok = t0 + u * TOK + tk;
+      const bool ok = tok < n && code[u] < c && pos[u] >= 0;
       const float* x = cbh + (int64_t)(ok ? code[u] : 0) * kD + i0;
 #pragma unroll
       for (int k = 0; k < P; k += 4) {
@@ -129,8 +154,9 @@ __global__ __launch_bounds__(256) void rope_gather(
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (tok[u] >= n) continue;
-      const int64_t ooff = ((b * heads + h) * n + tok[u]) * kD + i0;
+      const int64_t tok = t0 + u * TOK + tk;
+      if (tok >= n) continue;
+      const int64_t ooff = ((b * heads + h) * n + tok) * kD + i0;
       real lo[P], hi[P];
       if ((int64_t)code[u] >= c || pos[u] < 0) {
 #pragma unroll
@@ -143,14 +169,14 @@ __global__ __launch_bounds__(256) void rope_gather(
           for (int k = 0; k < P; ++k) {
             const d2 v = row[k];
             const real cs = (real)v.x, sn = (real)v.y;
-            lo[k] = (real)xl[u][k] * cs - (real)xh[u][k] * sn;
-            hi[k] = (real)xh[u][k] * cs + (real)xl[u][k] * sn;
+            lo[k] = fma((real)xl[u][k], cs, -((real)xh[u][k] * sn));
+            hi[k] = fma((real)xh[u][k], cs, (real)xl[u][k] * sn);
           }
         } else {
 #pragma unroll
           for (int k = 0; k < P; ++k) {
-            lo[k] = (real)xl[u][k] * fc[k] - (real)xh[u][k] * fs[k];
-            hi[k] = (real)xh[u][k] * fc[k] + (real)xl[u][k] * fs[k];
+            lo[k] = fma((real)xl[u][k], fc[k], -((real)xh[u][k] * fs[k]));
+            hi[k] = fma((real)xh[u][k], fc[k], (real)xl[u][k] * fs[k]);
           }
         }
       }
@@ -175,6 +201,11 @@ __global__ __launch_bounds__(256) void rope_gather(
         __builtin_nontemporal_store(a, reinterpret_cast<f4*>(o));
         __builtin_nontemporal_store(bb, reinterpret_cast<f4*>(o + kHalf));
       }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      code[u] = ncode[u];
+      pos[u] = npos[u];
     }
   }
 }
@@ -213,10 +244,13 @@ extern "C" int a2ats_reconstruct(const uint16_t* codes, const int32_t* positions
   A2ATS_TRY(launch("rope_table", rope_table, dim3(grid_for((rows + 1) * kHalf, 256)), dim3(256), 0,
                    s, rows, cur_pos, cur_pos - far_offset, (int)(far_mode == A2ATS_FAR_UNROTATED),
                    rope_base, (int)kD, table));
-  const int64_t items = batch * heads * ((n + kChunk - 1) / kChunk);
+  const int64_t chunk = out_dtype == A2ATS_F32 ? kChunkF32 : kChunkBf16;
+  const int64_t items = batch * heads * ((n + chunk - 1) / chunk);
   // A multiple of 8 * heads workgroups, enough to fill the chip several times over.
   int64_t per = 8 * heads;
-  int64_t g = (2048 + per - 1) / per * per;
+  int64_t g = items / (out_dtype == A2ATS_F32 ? kItemsPerWgF32 : kItemsPerWgBf16);
+  if (g < kGridMin) g = kGridMin;
+  g = (g + per - 1) / per * per;
   if (g > items) g = items;
   if (g > (int64_t)1 << 30) g = (int64_t)1 << 30;
   if (out_dtype == A2ATS_F32)

@@ -7,20 +7,19 @@
 // (u << 32) | (0xffffffff - index), so equal scores keep the lower index first and every
 // element has a distinct key.
 //
-// Kernels (6 launches, no host round trip, no workgroup waits for another):
-//   sel_init     per head: ||q|| and the binning scale; zeroes histograms and counters.
-//   sel_score    HBM-bound pass over the keys (8 lanes per key, 4 keys in flight per lane
-//                group): writes u.
-//   sel_hist     1024-bin histogram of a monotone binning of s/||q|| in [-1, 1] from the
-//                L2/MALL-resident scores (LDS histograms, one global atomic per non-empty
-//                bin and workgroup); the last workgroup of each head (fenced atomic counter,
-//                no waiting) finds, with a parallel prefix sum, the bin b* that holds the
-//                n_r-th largest score.
+// Kernels (5 launches, no host round trip, no workgroup waits for another, no global atomics):
+//   sel_score    HBM-bound pass over the keys (8 lanes per key, 8 keys in flight per lane
+//                group): writes u, and the workgroup's 1024-bin histogram of a monotone
+//                binning of s/||q|| in [-1, 1] (LDS counts, written out whole; at most 64
+//                workgroups per head).
+//   sel_bstar    one workgroup per head: sums the partial histograms and finds, with a
+//                parallel prefix sum, the bin b* that holds the n_r-th largest score.
 //   sel_collect  pass over u: per block of 1024 scores, the count above b* and the keys in
 //                b* (into the block's own region of the candidate array).
 //   sel_thresh   one workgroup per head: the exact n_r-th largest 64-bit key among the
-//                candidates, the selected candidates per block, and every block's output
-//                offset (parallel prefix sums).
+//                candidates (gathered into LDS in parallel, bitonic sort; radix select when
+//                they do not fit), the selected count of every block from the block-ordered
+//                copy, and every block's output offset (parallel prefix sums).
 //   sel_scatter  pass over u: ordered compaction of the predicate key64 >= threshold into
 //                the retrieval and bulk index arrays.
 #include "common.hpp"
@@ -34,21 +33,20 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 constexpr int kD = A2ATS_HEAD_DIM;
 constexpr int kBins = 1024;
 constexpr float kHalfBins = 512.0f;
-constexpr int kHistScores = 16384;  // scores per sel_hist workgroup (at most 64 per head)
-constexpr int kScoreChunk = 512;    // keys per sel_score workgroup
+constexpr int kScoreWgPerHead = 64; // at most this many sel_score workgroups (partial histograms) per head
+constexpr int kScoreMinKeys = 512;  // and at least this many keys per workgroup
 constexpr int kScoreUnroll = 4;     // keys in flight per 8-lane group
+constexpr int kScoreThreads = 512;  // sel_score workgroup size
 constexpr int kBlock = 1024;        // scores per sel_collect / sel_scatter workgroup
 constexpr int kSortCap = 4096;      // candidates sorted in LDS; more take the radix path
+constexpr int kOffCap = 4096;       // blocks whose candidate offsets fit in LDS (n <= 4M)
+constexpr int kRankCap = 512;       // up to this many candidates: rank counting instead of a sort
 
 struct HeadInfo {
-  float inv_scale;       // (kBins / 2) / ||q||, or 0 when q == 0
-  int n_r;               // retrieval-set size
-  int bstar;             // bin holding the n_r-th largest score (kBins: nothing selected)
-  int count_above;       // keys in bins above bstar
-  int n_cand;            // unused
-  unsigned done_score;   // workgroups of sel_hist finished
-  unsigned done_collect; // unused
-  int pad;
+  float inv_scale;        // (kBins / 2) / ||q||, or 0 when q == 0
+  int n_r;                // retrieval-set size
+  int bstar;              // bin holding the n_r-th largest score (kBins: nothing selected)
+  int count_above;        // keys in bins above bstar
   unsigned long long thr; // 64-bit key of the n_r-th largest element
 };
 
@@ -74,47 +72,12 @@ __device__ __forceinline__ unsigned long long key64(unsigned u, int64_t idx) {
   return ((unsigned long long)u << 32) | (unsigned long long)(0xFFFFFFFFu - (unsigned)idx);
 }
 
-__device__ __forceinline__ unsigned atomic_load_u32(const unsigned* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__global__ __launch_bounds__(256) void sel_init(const void* __restrict__ query, int dt, int64_t n,
-                                                double fraction, HeadInfo* __restrict__ info,
-                                                unsigned* __restrict__ hist,
-                                                unsigned* __restrict__ sel_extra, int nblk) {
-  const int head = blockIdx.x;
-  const int t = threadIdx.x;
-  __shared__ float red[4];
-  float v = 0.f;
-  if (t < kD) {
-    float x = load_elem(query, dt, (int64_t)head * kD + t);
-    v = x * x;
-  }
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  if ((t & 63) == 0) red[t >> 6] = v;
-  __syncthreads();
-  for (int i = t; i < kBins; i += 256) hist[(int64_t)head * kBins + i] = 0u;
-  for (int i = t; i < nblk; i += 256) sel_extra[(int64_t)head * nblk + i] = 0u;
-  if (t == 0) {
-    float qn = sqrtf(red[0] + red[1] + red[2] + red[3]);
-    HeadInfo h;
-    h.inv_scale = qn > 0.f ? kHalfBins / qn : 0.f;
-    h.n_r = (int)ceil(fraction * (double)n);
-    h.bstar = kBins;
-    h.count_above = 0;
-    h.n_cand = 0;
-    h.done_score = 0u;
-    h.done_collect = 0u;
-    h.pad = 0;
-    h.thr = ~0ull;
-    info[head] = h;
-  }
-}
-
-// Exclusive prefix sum over the 256 threads of a workgroup (thread order); returns the sum of
-// the threads before this one and, in *total, the workgroup sum.
+// Exclusive prefix sum over the NT threads of a workgroup (thread order); returns the sum of
+// the threads before this one and, in *total, the workgroup sum.  Every thread must call it.
+template <int NT = 256>
 __device__ __forceinline__ unsigned block_exclusive_scan(unsigned v, unsigned* total) {
-  __shared__ unsigned wsum[4];
+  constexpr int kW = NT / 64;
+  __shared__ unsigned wsum[kW];
   const int t = threadIdx.x, lane = t & 63;
   unsigned incl = v;
   for (int o = 1; o < 64; o <<= 1) {
@@ -126,7 +89,7 @@ __device__ __forceinline__ unsigned block_exclusive_scan(unsigned v, unsigned* t
   __syncthreads();
   unsigned before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < kW; ++w) {
     before += w < (t >> 6) ? wsum[w] : 0u;
     all += wsum[w];
   }
@@ -134,128 +97,152 @@ __device__ __forceinline__ unsigned block_exclusive_scan(unsigned v, unsigned* t
   return before + incl - v;
 }
 
-// 8 lanes per key; each lane covers 16 consecutive elements of the 128.
+// 8 lanes per key; each lane covers 16 consecutive elements of the 128.  Workgroup wg of a
+// head scores keys [wg * per_wg, (wg + 1) * per_wg) and writes their histogram (all kBins
+// counts) to part[head][wg].  ||q|| is formed identically in every workgroup (the same
+// sums in the same order), and workgroup 0 of the head publishes the binning scale.  The
+// raw key words are held until every load of a round is issued (bf16: 8 registers a key
+// per lane), so that kScoreUnroll keys per lane group are in flight.
 template <int DT>
-__global__ __launch_bounds__(256) void sel_score(const void* __restrict__ keys,
-                                                 const void* __restrict__ query, int64_t n,
-                                                 int wg_per_head, unsigned* __restrict__ scores) {
+__global__ __launch_bounds__(kScoreThreads) void sel_score(const void* __restrict__ keys,
+                                                           const void* __restrict__ query,
+                                                           int64_t n, int wg_per_head,
+                                                           int64_t per_wg,
+                                                           unsigned* __restrict__ scores,
+                                                           unsigned* __restrict__ part,
+                                                           HeadInfo* __restrict__ info) {
+  constexpr int kKeysPerRound = kScoreThreads / 8;
+  constexpr int kWords = DT == A2ATS_BF16 ? 2 : 4;  // 16-byte words per lane and key
   const int head = blockIdx.x / wg_per_head;
   const int wg = blockIdx.x % wg_per_head;
   const int t = threadIdx.x;
   const int sub = t & 7;
+  __shared__ unsigned lh[kBins];
+  for (int i = t; i < kBins; i += kScoreThreads) lh[i] = 0u;
   float qv[16];
+  float qq = 0.f;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) qv[e] = load_elem(query, DT, (int64_t)head * kD + sub * 16 + e);
-  const int64_t k_begin = (int64_t)wg * kScoreChunk;
-  const int64_t k_end = k_begin + kScoreChunk < n ? k_begin + kScoreChunk : n;
+  for (int e = 0; e < 16; ++e) {
+    qv[e] = load_elem(query, DT, (int64_t)head * kD + sub * 16 + e);
+    qq += qv[e] * qv[e];
+  }
+  // butterfly sums are commutative pairwise, so every lane ends with the same value
+#pragma unroll
+  for (int o = 4; o > 0; o >>= 1) qq += __shfl_xor(qq, o);
+  const float qn = sqrtf(qq);
+  const float inv = qn > 0.f ? kHalfBins / qn : 0.f;
+  if (wg == 0 && t == 0) info[head].inv_scale = inv;
+  __syncthreads();
+  const int64_t k_begin = (int64_t)wg * per_wg;
+  const int64_t k_end = k_begin + per_wg < n ? k_begin + per_wg : n;
   const int64_t hoff = (int64_t)head * n;
-  for (int64_t k0 = k_begin; k0 < k_end; k0 += 32 * kScoreUnroll) {
-    float x[kScoreUnroll][16];
+  const char* kbase = static_cast<const char*>(keys) + sub * 16 * (DT == A2ATS_BF16 ? 2 : 4);
+  constexpr int kRowBytes = kD * (DT == A2ATS_BF16 ? 2 : 4);
+  for (int64_t k0 = k_begin; k0 < k_end; k0 += kKeysPerRound * kScoreUnroll) {
+    u4v raw[kScoreUnroll][kWords];
 #pragma unroll
     for (int u = 0; u < kScoreUnroll; ++u) {  // issue every load first
-      const int64_t key = k0 + u * 32 + (t >> 3);
-      if (key < k_end) {
-        if (DT == A2ATS_BF16) {
-          const u4v* p = reinterpret_cast<const u4v*>(static_cast<const uint16_t*>(keys) +
-                                                      (hoff + key) * kD + sub * 16);
-          const u4v r0 = p[0], r1 = p[1];
-          const unsigned w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+      const int64_t key = k0 + u * kKeysPerRound + (t >> 3);
+      const u4v* p = reinterpret_cast<const u4v*>(kbase + (hoff + key) * kRowBytes);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            x[u][2 * e] = __uint_as_float(w[e] << 16);
-            x[u][2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-          }
-        } else {
-          const f4v* p = reinterpret_cast<const f4v*>(static_cast<const float*>(keys) +
-                                                      (hoff + key) * kD + sub * 16);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f4v a = p[q];
-            x[u][4 * q] = a.x; x[u][4 * q + 1] = a.y; x[u][4 * q + 2] = a.z; x[u][4 * q + 3] = a.w;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) x[u][e] = 0.f;
-      }
+      for (int q = 0; q < kWords; ++q) raw[u][q] = key < k_end ? p[q] : u4v{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < kScoreUnroll; ++u) {
+      float x[16];
+#pragma unroll
+      for (int q = 0; q < kWords; ++q) {
+        const unsigned w[4] = {raw[u][q].x, raw[u][q].y, raw[u][q].z, raw[u][q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (DT == A2ATS_BF16) {
+            x[8 * q + 2 * e] = __uint_as_float(w[e] << 16);
+            x[8 * q + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+          } else {
+            x[4 * q + e] = __uint_as_float(w[e]);
+          }
+        }
+      }
       float dot = 0.f, nrm = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        dot += x[u][e] * qv[e];
-        nrm += x[u][e] * x[u][e];
+        dot += x[e] * qv[e];
+        nrm += x[e] * x[e];
       }
 #pragma unroll
       for (int o = 4; o > 0; o >>= 1) {
         dot += __shfl_xor(dot, o);
         nrm += __shfl_xor(nrm, o);
       }
-      const int64_t key = k0 + u * 32 + (t >> 3);
+      const int64_t key = k0 + u * kKeysPerRound + (t >> 3);
       if (sub == 0 && key < k_end) {
         const float sc = nrm > 0.f ? dot / sqrtf(nrm) : 0.f;
-        scores[hoff + key] = order_key(sc);
+        const unsigned uk = order_key(sc);
+        scores[hoff + key] = uk;
+        atomicAdd(&lh[bin_of(uk, inv)], 1u);
       }
     }
   }
+  __syncthreads();
+  uint4* dst = reinterpret_cast<uint4*>(part + ((int64_t)head * wg_per_head + wg) * kBins);
+  const uint4* src = reinterpret_cast<const uint4*>(lh);
+  for (int i = t; i < kBins / 4; i += kScoreThreads) dst[i] = src[i];
 }
 
-// Histogram of the binned scores from the L2/MALL-resident score array: kHistScores
-// scores per workgroup into an LDS histogram, one global atomic per non-empty bin (the
-// scores of a head fall into a few hundred bins); the last workgroup of each head (fenced
-// counter, no waiting) finds, with a parallel prefix sum, the bin b* holding the n_r-th
-// largest score.
-__global__ __launch_bounds__(256) void sel_hist(const unsigned* __restrict__ scores, int64_t n,
-                                                int wg_per_head, HeadInfo* __restrict__ info,
-                                                unsigned* __restrict__ hist) {
-  const int head = blockIdx.x / wg_per_head;
-  const int wg = blockIdx.x % wg_per_head;
+// One workgroup of 1024 threads per head: total histogram over the sel_score partials, then
+// b*.  Thread t sums the 4 bins kBins-4(q+1) .. kBins-4q-1 (q = t % 256, taken in
+// descending order) over the partials w = t / 256 (mod 4), all its loads in flight at once;
+// the four groups meet in LDS and a prefix sum over the quads finds the bin of the n_r-th
+// largest.
+constexpr int kBstarThreads = 1024;
+__global__ __launch_bounds__(kBstarThreads) void sel_bstar(const unsigned* __restrict__ part,
+                                                           int wg_per_head, int64_t n_r,
+                                                           HeadInfo* __restrict__ info) {
+  constexpr int kGroups = kBstarThreads / (kBins / 4);
+  constexpr int kPerGroup = kScoreWgPerHead / kGroups;
+  const int head = blockIdx.x;
   const int t = threadIdx.x;
-  __shared__ unsigned lh[kBins];
-  __shared__ int is_last;
-  for (int i = t; i < kBins; i += 256) lh[i] = 0u;
-  const float inv = info[head].inv_scale;
-  unsigned* hh = hist + (int64_t)head * kBins;
+  const int q = t % (kBins / 4), g = t / (kBins / 4);
+  const uint4* p = reinterpret_cast<const uint4*>(part + (int64_t)head * wg_per_head * kBins) +
+                   (kBins / 4 - 1 - q);
+  uint4 v[kPerGroup];
+#pragma unroll
+  for (int k = 0; k < kPerGroup; ++k) {
+    const int w = g + kGroups * k;
+    v[k] = w < wg_per_head ? p[(int64_t)w * (kBins / 4)] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int k = 0; k < kPerGroup; ++k) {
+    acc.x += v[k].x; acc.y += v[k].y; acc.z += v[k].z; acc.w += v[k].w;
+  }
+  __shared__ uint4 s_acc[kGroups - 1][kBins / 4];
+  if (g > 0) s_acc[g - 1][q] = acc;
   __syncthreads();
-  const int64_t per = ((n + wg_per_head - 1) / wg_per_head + 3) / 4 * 4;
-  const int64_t i_begin = (int64_t)wg * per;
-  const int64_t i_end = i_begin + per < n ? i_begin + per : n;
-  const int64_t hoff = (int64_t)head * n;
-  for (int64_t i0 = i_begin + 4 * t; i0 < i_end; i0 += 1024) {
-    if (i0 + 3 < i_end && ((hoff + i0) & 3) == 0) {
-      const uint4 q = *reinterpret_cast<const uint4*>(scores + hoff + i0);
-      atomicAdd(&lh[bin_of(q.x, inv)], 1u);
-      atomicAdd(&lh[bin_of(q.y, inv)], 1u);
-      atomicAdd(&lh[bin_of(q.z, inv)], 1u);
-      atomicAdd(&lh[bin_of(q.w, inv)], 1u);
-    } else {
-      for (int k = 0; k < 4 && i0 + k < i_end; ++k)
-        atomicAdd(&lh[bin_of(scores[hoff + i0 + k], inv)], 1u);
+  if (g == 0) {
+#pragma unroll
+    for (int k = 0; k < kGroups - 1; ++k) {
+      const uint4 o = s_acc[k][q];
+      acc.x += o.x; acc.y += o.y; acc.z += o.z; acc.w += o.w;
     }
   }
-  __syncthreads();
-  for (int i = t; i < kBins; i += 256)
-    if (lh[i]) atomicAdd(&hh[i], lh[i]);
-  __threadfence();
-  __syncthreads();
-  if (t == 0) is_last = (atomicAdd(&info[head].done_score, 1u) == (unsigned)wg_per_head - 1);
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  // Last workgroup of this head: thread t owns the 4 bins kBins-4(t+1) .. kBins-4t-1, taken
-  // in descending order; a prefix sum over the threads finds the bin of the n_r-th largest.
-  const int n_r = info[head].n_r;
-  const uint4 v = *reinterpret_cast<const uint4*>(hh + kBins - 4 * (t + 1));  // plain load: fenced
-  const unsigned c4[4] = {v.w, v.z, v.y, v.x};
-  const unsigned s4 = c4[0] + c4[1] + c4[2] + c4[3];
+  const unsigned c4[4] = {acc.w, acc.z, acc.y, acc.x};
+  const unsigned s4 = g == 0 ? c4[0] + c4[1] + c4[2] + c4[3] : 0u;
   unsigned total;
-  unsigned cum = block_exclusive_scan(s4, &total);
-  if (n_r > 0 && cum < (unsigned)n_r && cum + s4 >= (unsigned)n_r) {
+  unsigned cum = block_exclusive_scan<kBstarThreads>(s4, &total);
+  if (t == 0) {
+    info[head].n_r = (int)n_r;
+    info[head].thr = ~0ull;
+    if (n_r == 0) {
+      info[head].bstar = kBins;
+      info[head].count_above = 0;
+    }
+  }
+  if (g == 0 && n_r > 0 && cum < (unsigned)n_r && cum + s4 >= (unsigned)n_r) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (cum < (unsigned)n_r && cum + c4[i] >= (unsigned)n_r) {
-        info[head].bstar = kBins - 1 - 4 * t - i;
+        info[head].bstar = kBins - 1 - 4 * q - i;
         info[head].count_above = (int)cum;
       }
       cum += c4[i];
@@ -314,48 +301,98 @@ __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ 
 }
 
 // One workgroup per head: the exact n_r-th largest 64-bit key among the candidates of bin
-// b* (LDS bitonic sort, radix select beyond kSortCap), the selected candidates per block,
-// and the exclusive output offset of every block (parallel prefix sums).
+// b*, the selected candidates per block, and the exclusive output offset of every block.
+// When the candidates fit (at most kSortCap of them, at most kOffCap blocks) they are
+// gathered into LDS in parallel (each thread finds the block of its slot by binary search
+// over the block offsets), kept in block order in `su` and sorted descending (bitonic) in
+// `sk`; otherwise a radix select runs over the candidate regions in global memory.
 __global__ __launch_bounds__(256) void sel_thresh(int64_t n, int nblk, HeadInfo* __restrict__ info,
                                                   const unsigned* __restrict__ above_blk,
                                                   const unsigned* __restrict__ cand_blk,
                                                   const unsigned long long* __restrict__ cand,
-                                                  unsigned* __restrict__ sel_extra) {
+                                                  unsigned* __restrict__ blk_off) {
   const int head = blockIdx.x;
   const int t = threadIdx.x;
   const int64_t hoff = (int64_t)head * n;
+  const int64_t cbase = (int64_t)head * nblk;
+  // the first 256 blocks' above-b* counts are fetched up front, beside the head's record
+  const unsigned above0 = t < nblk ? above_blk[cbase + t] : 0u;
   const int r = info[head].n_r - info[head].count_above;  // 1-based rank inside bin b*
   __shared__ unsigned long long sk[kSortCap];
-  // candidate count, and (when they fit) the candidates packed into LDS in block order
+  __shared__ unsigned long long su[kSortCap];
+  __shared__ unsigned s_off[kOffCap + 1];
+  // candidate count and per-block candidate offsets
   unsigned n_cand = 0;
   for (int b0 = 0; b0 < nblk; b0 += 256) {
     const int b = b0 + t;
-    const unsigned cb = b < nblk ? cand_blk[(int64_t)head * nblk + b] : 0u;
+    const unsigned cb = b < nblk ? cand_blk[cbase + b] : 0u;
     unsigned chunk;
     const unsigned ex = block_exclusive_scan(cb, &chunk);
-    if (n_cand + ex + cb <= (unsigned)kSortCap)
-      for (unsigned i = 0; i < cb; ++i) sk[n_cand + ex + i] = cand[hoff + (int64_t)b * kBlock + i];
+    if (b < nblk && b < kOffCap) s_off[b] = n_cand + ex;
     n_cand += chunk;
   }
+  if (t == 0 && nblk <= kOffCap) s_off[nblk] = n_cand;
   __syncthreads();
+  const bool fits = n_cand <= (unsigned)kSortCap && nblk <= kOffCap;
   __shared__ unsigned dh[256];
   __shared__ unsigned long long s_prefix;
   __shared__ unsigned s_remaining;
   unsigned long long prefix = 0ull, mask = 0ull;
   if (t == 0) s_remaining = (unsigned)(r > 0 ? r : 0);
-  __syncthreads();
-  const bool fits = n_cand <= (unsigned)kSortCap;
   if (r > 0 && fits) {
-    // bitonic sort of the candidate keys, descending; the r-th is the threshold
-    int P = 1;
-    while (P < (int)n_cand) P <<= 1;
-    for (int i = (int)n_cand + t; i < P; i += 256) sk[i] = 0ull;
-    __syncthreads();
-    for (int k = 2; k <= P; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = t; i < P; i += 256) {
-          const int l = i ^ j;
-          if (l > i) {
+    const bool by_rank = n_cand <= (unsigned)kRankCap;
+    for (int j = t; j < (int)n_cand; j += 256) {
+      int lo = 0, hi = nblk - 1;  // the last block whose offset is <= j holds slot j
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_off[mid] <= (unsigned)j) lo = mid;
+        else hi = mid - 1;
+      }
+      const unsigned long long v = cand[hoff + (int64_t)lo * kBlock + (j - (int)s_off[lo])];
+      su[j] = v;
+      if (!by_rank) sk[j] = v;
+    }
+    if (by_rank) {
+      // few candidates: each one counts the larger keys (all distinct); rank r - 1 is it
+      __syncthreads();
+      constexpr int J = kRankCap / 256;
+      unsigned long long mine[J];
+      unsigned rank[J];
+#pragma unroll
+      for (int k = 0; k < J; ++k) {
+        const int j = t + 256 * k;
+        mine[k] = j < (int)n_cand ? su[j] : ~0ull;
+        rank[k] = 0u;
+      }
+      // 8 independent LDS reads per round (slots past n_cand hold 0, which counts nothing)
+      const int n_pad = ((int)n_cand + 7) & ~7;
+      for (int i = (int)n_cand + t; i < n_pad; i += 256) su[i] = 0ull;
+      __syncthreads();
+      for (int i = 0; i < n_pad; i += 8) {
+        unsigned long long x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = su[i + e];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int k = 0; k < J; ++k) rank[k] += x[e] > mine[k] ? 1u : 0u;
+      }
+#pragma unroll
+      for (int k = 0; k < J; ++k)
+        if (t + 256 * k < (int)n_cand && rank[k] == (unsigned)(r - 1)) s_prefix = mine[k];
+      __syncthreads();
+      prefix = s_prefix;
+    } else {
+      int P = 1;
+      while (P < (int)n_cand) P <<= 1;
+      for (int i = (int)n_cand + t; i < P; i += 256) sk[i] = 0ull;
+      __syncthreads();
+      // bitonic sort, descending; every thread takes whole compare-exchange pairs
+      for (int k = 2; k <= P; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+          for (int q = t; q < P / 2; q += 256) {
+            const int i = (q / j) * 2 * j + (q % j);
+            const int l = i + j;
             const unsigned long long a = sk[i], b = sk[l];
             const bool desc = (i & k) == 0;
             if (desc ? (a < b) : (a > b)) {
@@ -363,18 +400,19 @@ __global__ __launch_bounds__(256) void sel_thresh(int64_t n, int nblk, HeadInfo*
               sk[l] = a;
             }
           }
+          __syncthreads();
         }
-        __syncthreads();
       }
+      prefix = sk[r - 1];
     }
-    prefix = sk[r - 1];
   } else if (r > 0) {
+    __syncthreads();
     // radix select over the per-block candidate regions, 8 bits at a time
     for (int shift = 56; shift >= 0; shift -= 8) {
       dh[t] = 0u;
       __syncthreads();
       for (int b = t; b < nblk; b += 256) {
-        const unsigned cb = cand_blk[(int64_t)head * nblk + b];
+        const unsigned cb = cand_blk[cbase + b];
         for (unsigned i = 0; i < cb; ++i) {
           const unsigned long long kv = cand[hoff + (int64_t)b * kBlock + i];
           if ((kv & mask) == prefix) atomicAdd(&dh[(kv >> shift) & 0xFF], 1u);
@@ -399,38 +437,24 @@ __global__ __launch_bounds__(256) void sel_thresh(int64_t n, int nblk, HeadInfo*
   }
   const unsigned long long thr = r > 0 ? prefix : ~0ull;
   if (t == 0) info[head].thr = thr;
-  // selected candidates per block
-  if (r > 0) {
-    if (fits) {
-      for (int i = t; i < (int)n_cand; i += 256) {
-        const unsigned long long kv = sk[i];
-        if (kv >= thr) {
-          const int64_t idx = (int64_t)(0xFFFFFFFFu - (unsigned)(kv & 0xFFFFFFFFull));
-          atomicAdd(&sel_extra[(int64_t)head * nblk + idx / kBlock], 1u);
-        }
-      }
-    } else {
-      for (int b = t; b < nblk; b += 256) {
-        const unsigned cb = cand_blk[(int64_t)head * nblk + b];
-        unsigned sel = 0;
-        for (unsigned i = 0; i < cb; ++i) sel += cand[hoff + (int64_t)b * kBlock + i] >= thr ? 1u : 0u;
-        if (sel) atomicAdd(&sel_extra[(int64_t)head * nblk + b], sel);
-      }
-    }
-  }
-  __threadfence();
-  __syncthreads();
-  // exclusive offsets over the blocks, 256 at a time (atomic loads for the counters this
-  // workgroup just incremented)
+  // per block: keys above b* plus its selected candidates, then exclusive offsets
   unsigned run = 0;
   for (int b0 = 0; b0 < nblk; b0 += 256) {
     const int b = b0 + t;
-    const unsigned cntb = b < nblk ? above_blk[(int64_t)head * nblk + b] +
-                                         atomic_load_u32(&sel_extra[(int64_t)head * nblk + b])
-                                   : 0u;
+    unsigned cnt = 0;
+    if (b < nblk) {
+      cnt = b0 == 0 ? above0 : above_blk[cbase + b];
+      if (r > 0 && fits) {
+        for (unsigned i = s_off[b]; i < s_off[b + 1]; ++i) cnt += su[i] >= thr ? 1u : 0u;
+      } else if (r > 0) {
+        const unsigned cb = cand_blk[cbase + b];
+        for (unsigned i = 0; i < cb; ++i)
+          cnt += cand[hoff + (int64_t)b * kBlock + i] >= thr ? 1u : 0u;
+      }
+    }
     unsigned chunk;
-    const unsigned ex = block_exclusive_scan(cntb, &chunk);
-    if (b < nblk) sel_extra[(int64_t)head * nblk + b] = run + ex;  // the exclusive offset
+    const unsigned ex = block_exclusive_scan(cnt, &chunk);
+    if (b < nblk) blk_off[cbase + b] = run + ex;
     run += chunk;
   }
 }
@@ -502,26 +526,37 @@ __global__ __launch_bounds__(256) void sel_scatter(const unsigned* __restrict__ 
 
 struct SelLayout {
   HeadInfo* info;
-  unsigned* hist;
+  unsigned* part;
   unsigned* scores;
   unsigned long long* cand;
   unsigned* above_blk;
   unsigned* cand_blk;
-  unsigned* sel_extra;
+  unsigned* blk_off;
   size_t bytes;
 };
+
+// sel_score workgroups per head and keys per workgroup
+inline void score_split(int64_t n, int64_t* wg_per_head, int64_t* per_wg) {
+  int64_t w = (n + kScoreMinKeys - 1) / kScoreMinKeys;
+  if (w > kScoreWgPerHead) w = kScoreWgPerHead;
+  if (w < 1) w = 1;
+  *wg_per_head = w;
+  *per_wg = (n + w - 1) / w;
+}
 
 SelLayout carve(void* ws, int64_t heads, int64_t n) {
   const int64_t nblk = (n + kBlock - 1) / kBlock;
   Carver c(ws);
   SelLayout L;
   L.info = c.take<HeadInfo>((size_t)heads);
-  L.hist = c.take<unsigned>((size_t)heads * kBins);
+  int64_t wgph, per;
+  score_split(n, &wgph, &per);
+  L.part = c.take<unsigned>((size_t)(heads * wgph * kBins));
   L.scores = c.take<unsigned>((size_t)heads * n);
   L.cand = c.take<unsigned long long>((size_t)heads * n);
   L.above_blk = c.take<unsigned>((size_t)heads * nblk);
   L.cand_blk = c.take<unsigned>((size_t)heads * nblk);
-  L.sel_extra = c.take<unsigned>((size_t)heads * nblk);
+  L.blk_off = c.take<unsigned>((size_t)heads * nblk);
   L.bytes = c.used;
   return L;
 }
@@ -547,28 +582,28 @@ extern "C" int a2ats_select_retrieval(const void* keys, int keys_dtype, int64_t 
   if (n == 0) return A2ATS_OK;
   if (!keys || !query) return A2ATS_EINVAL;
   if ((n_r > 0 && !retrieval_idx) || (n_r < n && !bulk_idx)) return A2ATS_EINVAL;
-  const int64_t wg_per_head = (n + kScoreChunk - 1) / kScoreChunk;
+  int64_t wg_per_head, per_wg;
+  score_split(n, &wg_per_head, &per_wg);
   const int64_t nblk = (n + kBlock - 1) / kBlock;
-  if (heads * wg_per_head > 0x7FFFFFFF || heads > 65535) return A2ATS_EINVAL;
+  if (heads * nblk > 0x7FFFFFFF || heads > 65535) return A2ATS_EINVAL;
   const size_t need = a2ats_select_retrieval_workspace(heads, n);
   if (!ws_ok(workspace, workspace_bytes, need)) return A2ATS_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   SelLayout L = carve(workspace, heads, n);
-  A2ATS_TRY(launch("select_init", sel_init, dim3((unsigned)heads), dim3(256), 0, s, query,
-                   keys_dtype, n, fraction, L.info, L.hist, L.sel_extra, (int)nblk));
   if (keys_dtype == A2ATS_BF16)
     A2ATS_TRY(launch("select_score", sel_score<A2ATS_BF16>, dim3((unsigned)(heads * wg_per_head)),
-                     dim3(256), 0, s, keys, query, n, (int)wg_per_head, L.scores));
+                     dim3(kScoreThreads), 0, s, keys, query, n, (int)wg_per_head, per_wg, L.scores, L.part,
+                     L.info));
   else
     A2ATS_TRY(launch("select_score", sel_score<A2ATS_F32>, dim3((unsigned)(heads * wg_per_head)),
-                     dim3(256), 0, s, keys, query, n, (int)wg_per_head, L.scores));
-  const int64_t hist_wg = std::min<int64_t>(64, std::max<int64_t>(1, (n + kHistScores - 1) / kHistScores));
-  A2ATS_TRY(launch("select_hist", sel_hist, dim3((unsigned)(heads * hist_wg)), dim3(256), 0, s,
-                   L.scores, n, (int)hist_wg, L.info, L.hist));
+                     dim3(kScoreThreads), 0, s, keys, query, n, (int)wg_per_head, per_wg, L.scores, L.part,
+                     L.info));
+  A2ATS_TRY(launch("select_bstar", sel_bstar, dim3((unsigned)heads), dim3(kBstarThreads), 0, s, L.part,
+                   (int)wg_per_head, n_r, L.info));
   A2ATS_TRY(launch("select_collect", sel_collect, dim3((unsigned)(heads * nblk)), dim3(256), 0, s,
                    L.scores, n, (int)nblk, L.info, L.above_blk, L.cand_blk, L.cand));
   A2ATS_TRY(launch("select_thresh", sel_thresh, dim3((unsigned)heads), dim3(256), 0, s, n, (int)nblk,
-                   L.info, L.above_blk, L.cand_blk, L.cand, L.sel_extra));
+                   L.info, L.above_blk, L.cand_blk, L.cand, L.blk_off));
   return launch("select_scatter", sel_scatter, dim3((unsigned)(heads * nblk)), dim3(256), 0, s,
-                L.scores, n, (int)nblk, L.info, L.sel_extra, retrieval_idx, bulk_idx);
+                L.scores, n, (int)nblk, L.info, L.blk_off, retrieval_idx, bulk_idx);
 }
