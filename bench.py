@@ -106,11 +106,11 @@ def main():
         aux.wait_event(main_s.record_event())
         with torch.cuda.stream(aux):
             prep_plain.prepare(cbd, None)
+            plain_ready = aux.record_event()
             prep_h.prepare(cbd, L)
-            prep_done = aux.record_event()
         ret, bulk = kv.select_retrieval(kd, proxy, w.fraction)
         split_done = main_s.record_event()
-        main_s.wait_event(prep_done)
+        main_s.wait_event(plain_ready)
         kv.encode_prepared(kd, prep_plain, idx=bulk, codes=codes)
         aux.wait_event(split_done)
         with torch.cuda.stream(aux):
@@ -417,11 +417,11 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
         aux.wait_event(main_s.record_event())
         with torch.cuda.stream(aux):
             prep_plain.prepare(cbd, None)
+            plain_ready = aux.record_event()
             prep_h.prepare(cbd, L)
-            prep_done = aux.record_event()
         ret, bulk = split()
         split_done = main_s.record_event()
-        main_s.wait_event(prep_done)
+        main_s.wait_event(plain_ready)
         kv.encode_prepared(kd, prep_plain, idx=bulk, codes=codes)
         aux.wait_event(split_done)
         with torch.cuda.stream(aux):

@@ -43,9 +43,10 @@ def lib():
         L.orc_select_retrieval.argtypes = [_dp, _i64, _i64, _dp, ctypes.c_double, _ip, _ip, _dp]
         L.orc_reconstruct.argtypes = [_up, _ip, _i64, _i64, _dp, _i64, _i64, _i64, _i64,
                                       ctypes.c_int, ctypes.c_double, _dp, _lp]
+        L.orc_rope_at.argtypes = [_dp, _i64, _i64, ctypes.c_double, ctypes.c_double, _dp]
         L.orc_round_bf16.argtypes = [_dp, _i64, _up]
         for f in (L.orc_second_moment, L.orc_cholesky, L.orc_assign_h, L.orc_assign_cosine,
-                  L.orc_select_retrieval, L.orc_reconstruct):
+                  L.orc_select_retrieval, L.orc_reconstruct, L.orc_rope_at):
             f.restype = ctypes.c_int
         L.orc_round_bf16.restype = None
         L.orc_threads.argtypes, L.orc_threads.restype = [], ctypes.c_int
@@ -172,6 +173,16 @@ def reconstruct(codes, positions, cb, cur, window, far_b=2048, far_mode=FAR_FIXE
                                  int(cur), int(window), int(far_b), int(far_mode), float(base),
                                  _ptr(out, _dp), _ptr(far, _lp)))
     return out, int(far[0])
+
+
+def rope_at(x, position, base=10000.0):
+    """Rows of x [rows, d] rotated as tokens at `position` (the query-side R_b of Eq. 11 when
+    position = b) -> fp64 [rows, d]."""
+    x = _f64(x)
+    rows, d = x.shape
+    out = np.empty((rows, d))
+    _check(lib().orc_rope_at(_ptr(x, _dp), rows, d, float(position), float(base), _ptr(out, _dp)))
+    return out
 
 
 def round_bf16(x):

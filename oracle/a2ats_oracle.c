@@ -269,6 +269,32 @@ int orc_reconstruct(const uint16_t* codes, const int32_t* pos, int64_t n, int64_
   return ORC_OK;
 }
 
+/* ------------------------------------------------------------------ query-side far rotation */
+
+/* The query-side half of Eq. 11: [DOC2] "paper fidelity" keeps far keys unrotated (Eq. 12)
+ * and puts the constant far rotation R_b on the query, so the far attention logit is
+ * (q R_b) . k; [LOG] adds this half as a2ats_apply_far_query_rope.  Each row of x is
+ * rotated as a token at position `position` (= b): the same half-split pairs and RoFormer
+ * frequencies as orc_reconstruct, in fp64. */
+int orc_rope_at(const double* x, int64_t rows, int64_t d, double position, double base,
+                double* out) {
+  if (rows < 0 || d <= 0 || (d % 2) != 0 || !(base > 0.0)) return ORC_EINVAL;
+  const int64_t half = d / 2;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const double* q = x + r * d;
+    double* o = out + r * d;
+    for (int64_t i = 0; i < half; ++i) {
+      double theta = pow(base, -2.0 * (double)i / (double)d);
+      double phi = position * theta;
+      double cs = cos(phi), sn = sin(phi);
+      o[i] = q[i] * cs - q[i + half] * sn;
+      o[i + half] = q[i + half] * cs + q[i] * sn;
+    }
+  }
+  return ORC_OK;
+}
+
 /* ------------------------------------------------------------------ output rounding */
 
 /* Nearest bf16 (8 significant bits, fp32 exponent range), ties to even, computed from

@@ -60,6 +60,11 @@ int orc_reconstruct(const uint16_t* codes, const int32_t* pos, int64_t n, int64_
                     const double* cb, int64_t c, int64_t cur, int64_t window, int64_t far_b,
                     int far_mode, double base, double* out, int64_t* far_count);
 
+/* Query-side far rotation (Eq. 11, R_b on the query): every row of x [rows, d] rotated as a
+ * token at `position`, same pairs and frequencies as orc_reconstruct. */
+int orc_rope_at(const double* x, int64_t rows, int64_t d, double position, double base,
+                double* out);
+
 /* Threads the OpenMP loops use. */
 int orc_threads(void);
 

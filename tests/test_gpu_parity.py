@@ -367,11 +367,11 @@ class TestPipeline:
             aux.wait_event(main.record_event())
             with torch.cuda.stream(aux):
                 pp = kv.encode_prepare(cbd, None, w.n)
+                plain_ready = aux.record_event()
                 ph = kv.encode_prepare(cbd, L, w.n)
-                prep_done = aux.record_event()
             r2, b2 = kv.select_retrieval(kd, proxy, w.fraction)
             split_done = main.record_event()
-            main.wait_event(prep_done)
+            main.wait_event(plain_ready)
             kv.encode_prepared(kd, pp, idx=b2, codes=codes)
             aux.wait_event(split_done)
             with torch.cuda.stream(aux):

@@ -407,6 +407,65 @@ class TestReconstruct:
         assert np.all(np.isfinite(out[0])) and np.all(np.isnan(out[1])) and np.all(np.isnan(out[2]))
 
 
+class TestFarQueryRope:
+    """The query-side half of Eq. 11: q R_b, every row rotated as a token at position b."""
+
+    def test_complex_form(self):
+        rng = np.random.default_rng(21)
+        x = rng.standard_normal((7, 128)) * 2
+        for b in (0, 1, 64, 2048, 131071):
+            # the angle b * theta carries a rounding of about b * 2^-53 radians on both sides
+            tol = 1e-13 + 4 * b * 2.0 ** -53 * np.abs(x).max()
+            np.testing.assert_allclose(oracle.rope_at(x, b), rope_complex(x, b), rtol=0, atol=tol)
+
+    def test_hand_values(self):
+        # the reconstruct fixture rotates one vector at its own position: the same rotation
+        for case in golden("rope_values.json")["cases"]:
+            out = oracle.rope_at(np.array([case["x"]]), case["pos"], base=case["base"])
+            np.testing.assert_allclose(out[0], case["out"], atol=1e-15)
+
+    def test_position_zero_identity_and_group_property(self):
+        rng = np.random.default_rng(22)
+        x = rng.standard_normal((4, 64))
+        np.testing.assert_array_equal(oracle.rope_at(x, 0), x)
+        two = oracle.rope_at(oracle.rope_at(x, 300), 1748)
+        np.testing.assert_allclose(two, oracle.rope_at(x, 2048), atol=1e-12)
+        back = oracle.rope_at(oracle.rope_at(x, 2048), -2048)
+        np.testing.assert_allclose(back, x, atol=1e-12)
+
+    def test_wrong_pairing_is_caught(self):
+        # planted mistake: interleaved pairs (2i, 2i+1) instead of half-split (i, i + d/2)
+        rng = np.random.default_rng(23)
+        x = rng.standard_normal((3, 16))
+        h = 8
+        theta = 10000.0 ** (-2.0 * np.arange(h) / 16)
+        z = (x[:, 0::2] + 1j * x[:, 1::2]) * np.exp(1j * 5.0 * theta)
+        wrong = np.empty_like(x)
+        wrong[:, 0::2], wrong[:, 1::2] = z.real, z.imag
+        out = oracle.rope_at(x, 5)
+        assert np.abs(out - wrong).max() > 0.1
+        np.testing.assert_allclose(out, rope_complex(x, 5), atol=1e-13)
+
+    def test_eq11_with_unrotated_far_keys(self):
+        # (q R_b) . k for unrotated far keys (FAR_UNROTATED) equals the fixed-offset form
+        # RoPE(q, cur) . RoPE(k, cur - b), and depends on b only, not on the window
+        rng = np.random.default_rng(24)
+        d, cur, b = 128, 40000, 2048
+        cb = rng.standard_normal((9, d))
+        q = rng.standard_normal((1, d))
+        codes = np.arange(9, dtype=np.uint16)
+        pos = np.arange(9, dtype=np.int32)
+        qb = oracle.rope_at(q, b)[0]
+        qcur = oracle.rope_at(q, cur)[0]
+        for w in (1, 4, 9):
+            unrot, far = oracle.reconstruct(codes, pos, cb, cur=cur, window=w,
+                                            far_mode=oracle.FAR_UNROTATED)
+            fixed, _ = oracle.reconstruct(codes, pos, cb, cur=cur, window=w, far_b=b)
+            assert far == 9
+            np.testing.assert_allclose(unrot @ qb, fixed @ qcur, rtol=1e-10, atol=1e-9)
+            np.testing.assert_allclose(unrot @ qb, cb @ qb, rtol=0, atol=0)
+
+
 # ============================================================ bf16 rounding
 class TestRoundBf16:
     def test_hand_values(self):
