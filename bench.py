@@ -301,13 +301,16 @@ def traffic_from_profiles(kernel, workload):
 def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
     W = synth.WORKLOADS
     res = {}
-    flush_buf = torch.empty(2 ** 28, dtype=torch.float32, device=dev)  # 1 GiB
+    flush_buf = torch.ones(2 ** 28, dtype=torch.float32, device=dev)  # 1 GiB, finite values
 
     def timed(fn, reps, flush=False):
         """ms per call of fn, calls issued back to back on the stream so the host's issue time
         overlaps the GPU's work.  With flush, a read of a 1 GiB buffer (which evicts the
         256 MB last-level cache with clean lines) precedes every call, and the same number of
-        reads timed alone is subtracted."""
+        reads timed alone is subtracted.  A kernel that follows a large streaming kernel runs
+        measurably slower than in a back-to-back steady state on this GPU (the gap does not
+        come from cache contents: it appears after a read of 256 MB as after a write of the
+        kernel's own output), so both figures are reported."""
         def run(with_fn):
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -375,6 +378,7 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
     blend()
     torch.cuda.synchronize()
     ms_r = timed(rec, 5, flush=True)
+    ms_r_steady = timed(rec, 10)
     ms_b = timed(blend, 10)
     tokens = w.batch * w.heads * w.n
     alg = tokens * (2 + 128 * 4) + w.batch * w.n * 4 + w.heads * w.c * 128 * 4
@@ -384,12 +388,50 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
         "workload": "32 sequences x 8 heads x 16384 tokens, fp32 out, W=256; blend of 256 new keys",
         "reconstruct_ms": round(ms_r, 4), "reconstruct_GBps": round(alg / (ms_r * 1e-3) / 1e9, 1),
         "reconstruct_call_hbm_frac": round(alg / (ms_r * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "reconstruct_steady_ms": round(ms_r_steady, 4),
+        "reconstruct_steady_hbm_frac": round(alg / (ms_r_steady * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "reconstruct_kernel_us": round(kr * 1e3, 2),
         "reconstruct_kernel_GBps": round(alg / (kr * 1e-3) / 1e9, 1),
         "reconstruct_hbm_frac": round(alg / (kr * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "algorithmic_bytes": alg, "blend_us": round(ms_b * 1e3, 2),
     }
     log("decode %s" % res["decode"])
+    # Far keys left unrotated (Eq. 12) with R_b on the query (Eq. 11): a decode step then
+    # rewrites only the rows that cross the window edge plus the appended token, and rotates
+    # the step's queries once.  Same cache; step from cur - 1 to cur, the last token new.
+    cur = w.cur_pos
+    kv.reconstruct(codes, pos, cbd, cur - 1, w.window, far_mode=kv.FAR_UNROTATED, out=out)
+
+    def upd():
+        kv.reconstruct_update(codes, pos, cbd, w.n - 1, cur - 1, cur, w.window, out)
+
+    def full_unrot():
+        kv.reconstruct(codes, pos, cbd, cur, w.window, far_mode=kv.FAR_UNROTATED, out=out)
+
+    qh = 24  # query heads of the 8-KV-head layer (grouped-query attention, 3 per KV head)
+    qd = torch.randn((w.batch, qh, 128), dtype=torch.float32, device=dev)
+    qo = torch.empty_like(qd)
+
+    def qrope():
+        kv.far_query_rope(qd, 2048, out=qo)
+
+    upd()
+    torch.cuda.synchronize()
+    ms_u = timed(upd, 20)
+    ms_fu = timed(full_unrot, 5)
+    ms_q = timed(qrope, 20)
+    pr_u = profile(upd, 5)
+    rows_step = w.batch * w.heads * 2  # the token leaving the window and the appended token
+    res["decode_unrotated"] = {
+        "workload": "same cache, far keys unrotated; one decode step (cur-1 -> cur, one token "
+                    "appended per sequence); queries 32 x 24 heads",
+        "update_us": round(ms_u * 1e3, 2), "update_kernel_us": round(pr_u["reconstruct_update"][1] * 1e3, 2),
+        "rows_written": rows_step, "full_reconstruct_us": round(ms_fu * 1e3, 2),
+        "speedup_vs_full": round(ms_fu / ms_u, 1),
+        "update_bytes": w.batch * w.n * 4 + rows_step * (2 + 512),
+        "far_query_rope_us": round(ms_q * 1e3, 2),
+    }
+    log("decode_unrotated %s" % res["decode_unrotated"])
     del out
     # long-context pipeline
     w = W["long_context"]
@@ -433,6 +475,8 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
     torch.cuda.synchronize()
     ms_s = timed(split, 10, flush=True)
     ms_r = timed(rec2, 10, flush=True)
+    ms_s_steady = timed(split, 20)
+    ms_r_steady = timed(rec2, 20)
     ms_p = timed(pipe, 5)
     split_bytes = w.heads * w.n * (128 * 2 + 4)
     rec_bytes = w.heads * w.n * (2 + 128 * 2) + w.n * 4 + w.heads * w.c * 128 * 4
@@ -443,9 +487,13 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
         "pipeline_ms": round(ms_p, 4), "keys_per_s": round(w.heads * w.n / (ms_p * 1e-3), 1),
         "split_ms": round(ms_s, 4), "split_GBps": round(split_bytes / (ms_s * 1e-3) / 1e9, 1),
         "split_hbm_frac": round(split_bytes / (ms_s * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "split_steady_ms": round(ms_s_steady, 4),
+        "split_steady_hbm_frac": round(split_bytes / (ms_s_steady * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "split_kernels_us": {k: round(v[1] * 1e3, 2) for k, v in pr_s.items()},
         "reconstruct_ms": round(ms_r, 4), "reconstruct_GBps": round(rec_bytes / (ms_r * 1e-3) / 1e9, 1),
         "reconstruct_hbm_frac": round(rec_bytes / (ms_r * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "reconstruct_steady_ms": round(ms_r_steady, 4),
+        "reconstruct_steady_hbm_frac": round(rec_bytes / (ms_r_steady * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "reconstruct_kernels_us": {k: round(v[1] * 1e3, 2) for k, v in pr_r.items()},
         "pipeline_kernels_us": {k: round(v[1] * 1e3, 2) for k, v in profile(pipe, 3).items()},
     }

@@ -1,13 +1,15 @@
 /* a2ats.h -- C ABI of the A2ATS key-cache hot path on gfx950 (MI355X).
  *
- * Five operations of the A2ATS method ("A2ATS: Retrieval-Based KV Cache Reduction via
+ * The operations of the A2ATS method ("A2ATS: Retrieval-Based KV Cache Reduction via
  * Windowed Rotary Position Embedding and Query-Aware Vector Quantization", as adapted and
  * documented by the "A2ATS-adapted" VeloxQuant-MLX pages):
  *   calibrate          H = E[q^T q] + ridge I and its Cholesky factor L
  *   encode             H-weighted (or plain) nearest-centroid codes, uint16
  *   assign_cosine      the cosine-blend assignment of the decode path
  *   select_retrieval   top-fraction cosine split of token indices
- *   reconstruct        centroid gather + windowed RoPE
+ *   reconstruct        centroid gather + windowed RoPE (and its incremental update for far
+ *                      keys left unrotated)
+ *   far_query_rope     the query-side far rotation R_b of Eq. 11
  *
  * Conventions shared by every call:
  *  - All array pointers are DEVICE pointers owned by the caller, row-major, contiguous,
@@ -209,6 +211,40 @@ int a2ats_reconstruct(const uint16_t* codes, const int32_t* positions, int64_t b
                       int64_t cur_pos, int64_t window, int64_t far_offset, int far_mode,
                       double rope_base, void* out, int out_dtype, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* reconstruct_update -- the decode-time use of far keys left unrotated ("A2ATS-adapted"
+ * docs, "paper fidelity" section, Eq. 12: far keys are returned as the centroid itself).  With
+ * A2ATS_FAR_UNROTATED a row depends on cur_pos only through the token's near/far status, so
+ * advancing the decode position rewrites only the tokens that crossed the window edge:
+ * given `out` holding a2ats_reconstruct(..., cur_prev, window, A2ATS_FAR_UNROTATED) of the
+ * first n_prev tokens (same codes, positions, codebook and rope_base), this call makes `out`
+ * equal, bit for bit, to a2ats_reconstruct(..., cur_pos, window, A2ATS_FAR_UNROTATED) of all
+ * n tokens.  It writes exactly the rows of tokens t >= n_prev (appended since) and of tokens
+ * t < n_prev with positions[b, t] >= 0 whose status (0 <= cur - pos < window) differs
+ * between cur_prev and cur_pos; every other row is left untouched.  Arguments as for
+ * a2ats_reconstruct; requires 0 <= n_prev <= n, cur_prev >= 0, cur_pos >= 0.  No workspace.
+ * The far keys' position (R_b) then belongs on the query: see a2ats_far_query_rope.
+ */
+int a2ats_reconstruct_update(const uint16_t* codes, const int32_t* positions, int64_t batch,
+                             int64_t heads, int64_t n, int64_t d, const float* codebook,
+                             int64_t c, int64_t n_prev, int64_t cur_prev, int64_t cur_pos,
+                             int64_t window, double rope_base, void* out, int out_dtype,
+                             void* stream);
+
+/* far_query_rope -- the query-side half of Eq. 11 ("A2ATS-adapted" docs, "paper fidelity"
+ * section; a2ats_apply_far_query_rope of the changelog entry "A2ATS-adapted paper-fidelity
+ * fixes"): every row of q is rotated as a token at position far_offset (= b), so that
+ * (q R_b) . k is the far-token logit against keys left unrotated.  With the same far_offset,
+ * RoPE(q, cur) . RoPE(k, cur - b) = RoPE(q, b) . k, which is what A2ATS_FAR_FIXED_OFFSET
+ * bakes into the keys instead.  Same pairs (i, i + d/2) and frequencies as reconstruct;
+ * rotation in fp64, one rounding to out_dtype.
+ *
+ *   q    [rows, d]  fp32 or bf16 (q_dtype), d must be 128
+ *   out  [rows, d]  fp32 or bf16 (out_dtype); may be q itself when the dtypes agree, and may
+ *                   not overlap q otherwise (A2ATS_EINVAL)
+ */
+int a2ats_far_query_rope(const void* q, int q_dtype, int64_t rows, int64_t d, int64_t far_offset,
+                         double rope_base, void* out, int out_dtype, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * Kernel timing (diagnostics).  While enabled, every kernel the library launches is

@@ -62,12 +62,16 @@ def lib() -> ctypes.CDLL:
         L.a2ats_reconstruct_workspace.restype = sz
         L.a2ats_reconstruct.argtypes = [p, p, i64, i64, i64, i64, p, i64, i64, i64, i64, i32, dbl,
                                         p, i32, p, sz, p]
+        L.a2ats_reconstruct_update.argtypes = [p, p, i64, i64, i64, i64, p, i64, i64, i64, i64,
+                                               i64, dbl, p, i32, p]
+        L.a2ats_far_query_rope.argtypes = [p, i32, i64, i64, i64, dbl, p, i32, p]
         L.a2ats_profile_enable.argtypes, L.a2ats_profile_enable.restype = [i32], i32
         L.a2ats_profile_reset.argtypes, L.a2ats_profile_reset.restype = [], i32
         L.a2ats_profile_read.argtypes, L.a2ats_profile_read.restype = [ctypes.c_char_p, sz], i64
         for f in ("a2ats_calibrate", "a2ats_encode", "a2ats_encode_prepare", "a2ats_encode_prepared",
                   "a2ats_assign_cosine",
-                  "a2ats_select_retrieval", "a2ats_reconstruct"):
+                  "a2ats_select_retrieval", "a2ats_reconstruct", "a2ats_reconstruct_update",
+                  "a2ats_far_query_rope"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -284,6 +288,50 @@ def reconstruct(codes: torch.Tensor, positions: torch.Tensor, codebook: torch.Te
                                    _ptr(codebook), c, int(cur_pos), int(window), int(far_offset),
                                    int(far_mode), float(rope_base), _ptr(out), _dtype_code(out),
                                    _ptr(ws), ws.numel(), _stream(codes.device)), "reconstruct")
+    return out
+
+
+def reconstruct_update(codes: torch.Tensor, positions: torch.Tensor, codebook: torch.Tensor,
+                       n_prev: int, cur_prev: int, cur_pos: int, window: int, out: torch.Tensor,
+                       rope_base: float = 10000.0):
+    """Advance `out` (a FAR_UNROTATED reconstruct of the first n_prev tokens at cur_prev) to
+    the FAR_UNROTATED reconstruct of all n tokens at cur_pos, rewriting only the rows that
+    change.  codes [batch, heads, n] uint16, positions [batch, n] int32, out [batch, heads,
+    n, d] fp32 or bf16."""
+    _dev(codes, "codes")
+    _dev(positions, "positions")
+    _dev(codebook, "codebook")
+    _dev(out, "out")
+    batch, heads, n = codes.shape
+    c, d = codebook.shape[1], codebook.shape[2]
+    if positions.dtype != torch.int32 or positions.shape != (batch, n):
+        raise ValueError("positions must be [batch, n] int32")
+    if out.shape != (batch, heads, n, d):
+        raise ValueError("out must be [batch, heads, n, d]")
+    _check(lib().a2ats_reconstruct_update(_ptr(codes), _ptr(positions), batch, heads, n, d,
+                                          _ptr(codebook), c, int(n_prev), int(cur_prev),
+                                          int(cur_pos), int(window), float(rope_base), _ptr(out),
+                                          _dtype_code(out), _stream(codes.device)),
+           "reconstruct_update")
+    return out
+
+
+def far_query_rope(q: torch.Tensor, far_offset: int = 2048, rope_base: float = 10000.0,
+                   out: torch.Tensor | None = None, out_dtype: torch.dtype | None = None):
+    """q [..., d] -> q R_b: every row rotated as a token at position far_offset (Eq. 11's
+    query-side far rotation).  out may be q itself."""
+    _dev(q, "q")
+    d = q.shape[-1]
+    rows = q.numel() // d if d else 0
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    else:
+        _dev(out, "out")
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    _check(lib().a2ats_far_query_rope(_ptr(q), _dtype_code(q), rows, d, int(far_offset),
+                                      float(rope_base), _ptr(out), _dtype_code(out),
+                                      _stream(q.device)), "far_query_rope")
     return out
 
 

@@ -45,6 +45,18 @@ constexpr int kItemsPerWgF32 = 1;
 constexpr int kItemsPerWgBf16 = 2;
 constexpr int kGridMin = 256;
 
+// (cos, sin) of the rotation of pair i at position p: angle p * base^(-2i/d), fp64.  The
+// table, the incremental update and the query-side rotation all take their angles from here,
+// so equal positions give bitwise equal rotations in every kernel.
+__device__ __forceinline__ d2 rope_cs(double p, int i, int d, double base) {
+  const double theta = pow(base, -2.0 * (double)i / (double)d);
+  const double phi = p * theta;
+  d2 v;
+  v.x = cos(phi);
+  v.y = sin(phi);
+  return v;
+}
+
 __global__ __launch_bounds__(256) void rope_table(int64_t rows_near, int64_t cur, int64_t far_pos,
                                                   int far_identity, double base, int d,
                                                   d2* __restrict__ table) {
@@ -58,11 +70,7 @@ __global__ __launch_bounds__(256) void rope_table(int64_t rows_near, int64_t cur
     v.x = 1.0;
     v.y = 0.0;
   } else {
-    const double p = (r == rows_near) ? (double)far_pos : (double)(cur - r);
-    const double theta = pow(base, -2.0 * (double)i / (double)d);
-    const double phi = p * theta;
-    v.x = cos(phi);
-    v.y = sin(phi);
+    v = rope_cs((r == rows_near) ? (double)far_pos : (double)(cur - r), i, d, base);
   }
   table[e] = v;
 }
@@ -75,6 +83,66 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
   v.x = (__bf16)lo;
   v.y = (__bf16)hi;
   return __builtin_bit_cast(unsigned, v);
+}
+
+__device__ __forceinline__ bool in_window(int64_t cur, int64_t pos, int64_t window) {
+  const int64_t delta = cur - pos;
+  return delta >= 0 && delta < window;
+}
+
+// The rotation of P pairs, (lo, hi) = (xl c - xh s, xh c + xl s), as one product and one
+// fused multiply-add each; every kernel that writes reconstructed rows uses it.
+template <typename real, int P>
+__device__ __forceinline__ void rotate_pairs(const float (&xl)[P], const float (&xh)[P],
+                                             const real (&cs)[P], const real (&sn)[P],
+                                             real (&lo)[P], real (&hi)[P]) {
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    lo[k] = fma((real)xl[k], cs[k], -((real)xh[k] * sn[k]));
+    hi[k] = fma((real)xh[k], cs[k], (real)xl[k] * sn[k]);
+  }
+}
+
+// P pairs of one row, rounded once, as two 16-byte non-temporal stores (low half at pair
+// i0, high half at i0 + d/2).
+template <bool BF16, typename real, int P>
+__device__ __forceinline__ void store_pairs(void* out, int64_t ooff, const real (&lo)[P],
+                                            const real (&hi)[P]) {
+  if constexpr (BF16) {
+    static_assert(P == 8, "bf16 rows: 8 pairs per thread");
+    u4 a, bb;
+    a.x = pack_bf16x2((float)lo[0], (float)lo[1]);
+    a.y = pack_bf16x2((float)lo[2], (float)lo[3]);
+    a.z = pack_bf16x2((float)lo[4], (float)lo[5]);
+    a.w = pack_bf16x2((float)lo[6], (float)lo[7]);
+    bb.x = pack_bf16x2((float)hi[0], (float)hi[1]);
+    bb.y = pack_bf16x2((float)hi[2], (float)hi[3]);
+    bb.z = pack_bf16x2((float)hi[4], (float)hi[5]);
+    bb.w = pack_bf16x2((float)hi[6], (float)hi[7]);
+    uint16_t* o = static_cast<uint16_t*>(out) + ooff;
+    __builtin_nontemporal_store(a, reinterpret_cast<u4*>(o));
+    __builtin_nontemporal_store(bb, reinterpret_cast<u4*>(o + kHalf));
+  } else {
+    static_assert(P == 4, "fp32 rows: 4 pairs per thread");
+    f4 a, bb;
+    a.x = (float)lo[0]; a.y = (float)lo[1]; a.z = (float)lo[2]; a.w = (float)lo[3];
+    bb.x = (float)hi[0]; bb.y = (float)hi[1]; bb.z = (float)hi[2]; bb.w = (float)hi[3];
+    float* o = static_cast<float*>(out) + ooff;
+    __builtin_nontemporal_store(a, reinterpret_cast<f4*>(o));
+    __builtin_nontemporal_store(bb, reinterpret_cast<f4*>(o + kHalf));
+  }
+}
+
+// Centroid halves of P pairs starting at pair i0 (row x of the codebook).
+template <int P>
+__device__ __forceinline__ void load_pairs(const float* x, float (&xl)[P], float (&xh)[P]) {
+#pragma unroll
+  for (int k = 0; k < P; k += 4) {
+    const f4 a = *reinterpret_cast<const f4*>(x + k);
+    const f4 bb = *reinterpret_cast<const f4*>(x + kHalf + k);
+    xl[k] = a.x; xl[k + 1] = a.y; xl[k + 2] = a.z; xl[k + 3] = a.w;
+    xh[k] = bb.x; xh[k + 1] = bb.y; xh[k + 2] = bb.z; xh[k + 3] = bb.w;
+  }
 }
 
 // fp32 output: 4 pairs per thread, rotation in fp64, one rounding, two 16-byte stores.
@@ -143,14 +211,7 @@ __global__ __launch_bounds__(256) void rope_gather(
     for (int u = 0; u < U; ++u) {
       const int64_t tok = t0 + u * TOK + tk;
       const bool ok = tok < n && code[u] < c && pos[u] >= 0;
-      const float* x = cbh + (int64_t)(ok ? code[u] : 0) * kD + i0;
-#pragma unroll
-      for (int k = 0; k < P; k += 4) {
-        const f4 a = *reinterpret_cast<const f4*>(x + k);
-        const f4 bb = *reinterpret_cast<const f4*>(x + kHalf + k);
-        xl[u][k] = a.x; xl[u][k + 1] = a.y; xl[u][k + 2] = a.z; xl[u][k + 3] = a.w;
-        xh[u][k] = bb.x; xh[u][k + 1] = bb.y; xh[u][k + 2] = bb.z; xh[u][k + 3] = bb.w;
-      }
+      load_pairs<P>(cbh + (int64_t)(ok ? code[u] : 0) * kD + i0, xl[u], xh[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -162,50 +223,141 @@ __global__ __launch_bounds__(256) void rope_gather(
 #pragma unroll
         for (int k = 0; k < P; ++k) lo[k] = hi[k] = (real)NAN;
       } else {
+        real cs[P], sn[P];
         const int64_t delta = cur - (int64_t)pos[u];
-        if (delta >= 0 && delta < window) {
+        if (in_window(cur, pos[u], window)) {
           const d2* row = table + delta * kHalf + i0;  // delta < rows_near since pos >= 0
 #pragma unroll
           for (int k = 0; k < P; ++k) {
             const d2 v = row[k];
-            const real cs = (real)v.x, sn = (real)v.y;
-            lo[k] = fma((real)xl[u][k], cs, -((real)xh[u][k] * sn));
-            hi[k] = fma((real)xh[u][k], cs, (real)xl[u][k] * sn);
+            cs[k] = (real)v.x;
+            sn[k] = (real)v.y;
           }
         } else {
 #pragma unroll
           for (int k = 0; k < P; ++k) {
-            lo[k] = fma((real)xl[u][k], fc[k], -((real)xh[u][k] * fs[k]));
-            hi[k] = fma((real)xh[u][k], fc[k], (real)xl[u][k] * fs[k]);
+            cs[k] = fc[k];
+            sn[k] = fs[k];
           }
         }
+        rotate_pairs<real, P>(xl[u], xh[u], cs, sn, lo, hi);
       }
-      if (BF16) {
-        u4 a, bb;
-        a.x = pack_bf16x2((float)lo[0], (float)lo[1]);
-        a.y = pack_bf16x2((float)lo[2], (float)lo[3]);
-        a.z = pack_bf16x2((float)lo[4], (float)lo[5]);
-        a.w = pack_bf16x2((float)lo[6], (float)lo[7]);
-        bb.x = pack_bf16x2((float)hi[0], (float)hi[1]);
-        bb.y = pack_bf16x2((float)hi[2], (float)hi[3]);
-        bb.z = pack_bf16x2((float)hi[4], (float)hi[5]);
-        bb.w = pack_bf16x2((float)hi[6], (float)hi[7]);
-        uint16_t* o = static_cast<uint16_t*>(out) + ooff;
-        __builtin_nontemporal_store(a, reinterpret_cast<u4*>(o));
-        __builtin_nontemporal_store(bb, reinterpret_cast<u4*>(o + kHalf));
-      } else {
-        f4 a, bb;
-        a.x = (float)lo[0]; a.y = (float)lo[1]; a.z = (float)lo[2]; a.w = (float)lo[3];
-        bb.x = (float)hi[0]; bb.y = (float)hi[1]; bb.z = (float)hi[2]; bb.w = (float)hi[3];
-        float* o = static_cast<float*>(out) + ooff;
-        __builtin_nontemporal_store(a, reinterpret_cast<f4*>(o));
-        __builtin_nontemporal_store(bb, reinterpret_cast<f4*>(o + kHalf));
-      }
+      store_pairs<BF16, real, P>(out, ooff, lo, hi);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       code[u] = ncode[u];
       pos[u] = npos[u];
+    }
+  }
+}
+
+// Incremental update for far keys left unrotated (Eq. 12): a token's reconstructed row then
+// depends on the current position only through its near/far status, so moving from cur_prev
+// to cur rewrites only the tokens whose status changed, plus the tokens appended since
+// (index >= n_prev).  Work item = (sequence, 256 tokens): each thread tests one token, the
+// changed ones are listed in LDS, and the workgroup then writes their rows for every head
+// with the gather's own arithmetic (near: the rotation at the token's position from
+// rope_cs; far: identity), so the rows are bitwise those of a full reconstruct at cur.
+template <bool BF16>
+__global__ __launch_bounds__(256) void rope_update(
+    const uint16_t* __restrict__ codes, const int32_t* __restrict__ positions, int64_t heads,
+    int64_t n, const float* __restrict__ cb, int64_t c, int64_t n_prev, int64_t cur_prev,
+    int64_t cur, int64_t window, double base, void* __restrict__ out, int64_t chunks) {
+  constexpr int P = BF16 ? 8 : 4;
+  constexpr int TPT = kHalf / P;
+  constexpr int TOK = 256 / TPT;
+  using real = typename std::conditional<BF16, float, double>::type;
+  __shared__ int s_tok[256];
+  __shared__ int s_pos[256];
+  __shared__ unsigned s_n;
+  const int t = threadIdx.x, lane = t & 63;
+  const int64_t b = blockIdx.x / chunks;
+  const int64_t t0 = (blockIdx.x % chunks) * 256;
+  if (t == 0) s_n = 0u;
+  __syncthreads();
+  const int64_t tok = t0 + t;
+  bool changed = false;
+  int p = -1;
+  if (tok < n) {
+    p = positions[b * n + tok];
+    changed = tok >= n_prev ||
+              (p >= 0 && in_window(cur_prev, p, window) != in_window(cur, p, window));
+  }
+  const unsigned long long m = __ballot(changed);
+  unsigned wbase = 0u;
+  if (lane == 0 && m) wbase = atomicAdd(&s_n, (unsigned)__popcll(m));
+  wbase = __shfl(wbase, 0);
+  if (changed) {
+    const unsigned slot = wbase + (unsigned)__popcll(m & ((1ull << lane) - 1ull));
+    s_tok[slot] = t;
+    s_pos[slot] = p;
+  }
+  __syncthreads();
+  const int cnt = (int)s_n;
+  if (cnt == 0) return;
+  const int g = t % TPT, tk = t / TPT;
+  const int i0 = g * P;
+  for (int64_t h = 0; h < heads; ++h) {
+    const float* cbh = cb + h * c * kD;
+    for (int e = tk; e < cnt; e += TOK) {
+      const int64_t row = t0 + s_tok[e];
+      const int pp = s_pos[e];
+      const int code = codes[(b * heads + h) * n + row];
+      const int64_t ooff = ((b * heads + h) * n + row) * kD + i0;
+      real lo[P], hi[P];
+      if ((int64_t)code >= c || pp < 0) {
+#pragma unroll
+        for (int k = 0; k < P; ++k) lo[k] = hi[k] = (real)NAN;
+      } else {
+        float xl[P], xh[P];
+        load_pairs<P>(cbh + (int64_t)code * kD + i0, xl, xh);
+        real cs[P], sn[P];
+        if (in_window(cur, pp, window)) {
+#pragma unroll
+          for (int k = 0; k < P; ++k) {
+            const d2 v = rope_cs((double)pp, i0 + k, kD, base);
+            cs[k] = (real)v.x;
+            sn[k] = (real)v.y;
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < P; ++k) {
+            cs[k] = (real)1.0;
+            sn[k] = (real)0.0;
+          }
+        }
+        rotate_pairs<real, P>(xl, xh, cs, sn, lo, hi);
+      }
+      store_pairs<BF16, real, P>(out, ooff, lo, hi);
+    }
+  }
+}
+
+// The query-side half of Eq. 11: every row rotated as a token at position b, in fp64, then
+// rounded once to the output type.  The 64 (cos, sin) pairs are formed once per workgroup in
+// LDS; thread t handles pair t % 64 of rows t / 64, t / 64 + 4, ...  Each thread reads both
+// elements of its pair before writing them, so the output may be the input itself.
+template <int DIN, int DOUT>
+__global__ __launch_bounds__(256) void rope_query(const void* __restrict__ q, int64_t rows,
+                                                  double position, double base, void* out) {
+  __shared__ d2 s_cs[kHalf];
+  const int t = threadIdx.x;
+  if (t < kHalf) s_cs[t] = rope_cs(position, t, kD, base);
+  __syncthreads();
+  const int i = t % kHalf;
+  const d2 v = s_cs[i];
+  for (int64_t r = (int64_t)blockIdx.x * 4 + t / kHalf; r < rows; r += (int64_t)gridDim.x * 4) {
+    const double xl = (double)load_elem(q, DIN, r * kD + i);
+    const double xh = (double)load_elem(q, DIN, r * kD + kHalf + i);
+    const double lo = fma(xl, v.x, -(xh * v.y));
+    const double hi = fma(xh, v.x, xl * v.y);
+    if (DOUT == A2ATS_F32) {
+      static_cast<float*>(out)[r * kD + i] = (float)lo;
+      static_cast<float*>(out)[r * kD + kHalf + i] = (float)hi;
+    } else {
+      static_cast<uint16_t*>(out)[r * kD + i] = f64_to_bf16(lo);
+      static_cast<uint16_t*>(out)[r * kD + kHalf + i] = f64_to_bf16(hi);
     }
   }
 }
@@ -258,4 +410,57 @@ extern "C" int a2ats_reconstruct(const uint16_t* codes, const int32_t* positions
                   positions, heads, n, codebook, c, cur_pos, window, rows, table, out, items);
   return launch("reconstruct", rope_gather<true>, dim3((unsigned)g), dim3(256), 0, s, codes,
                 positions, heads, n, codebook, c, cur_pos, window, rows, table, out, items);
+}
+
+extern "C" int a2ats_reconstruct_update(const uint16_t* codes, const int32_t* positions,
+                                        int64_t batch, int64_t heads, int64_t n, int64_t d,
+                                        const float* codebook, int64_t c, int64_t n_prev,
+                                        int64_t cur_prev, int64_t cur_pos, int64_t window,
+                                        double rope_base, void* out, int out_dtype, void* stream) {
+  if (out_dtype != A2ATS_F32 && out_dtype != A2ATS_BF16) return A2ATS_EDTYPE;
+  if (d != kD || batch < 1 || heads < 1 || n < 0 || c < 1 || c > 65536) return A2ATS_EINVAL;
+  if (n_prev < 0 || n_prev > n || cur_prev < 0 || cur_pos < 0) return A2ATS_EINVAL;
+  if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return A2ATS_EINVAL;
+  if (n == 0) return A2ATS_OK;
+  if (!codes || !positions || !codebook || !out) return A2ATS_EINVAL;
+  const int64_t chunks = (n + 255) / 256;
+  if (batch * chunks > 0x7FFFFFFF) return A2ATS_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (out_dtype == A2ATS_F32)
+    return launch("reconstruct_update", rope_update<false>, dim3((unsigned)(batch * chunks)),
+                  dim3(256), 0, s, codes, positions, heads, n, codebook, c, n_prev, cur_prev,
+                  cur_pos, window, rope_base, out, chunks);
+  return launch("reconstruct_update", rope_update<true>, dim3((unsigned)(batch * chunks)),
+                dim3(256), 0, s, codes, positions, heads, n, codebook, c, n_prev, cur_prev,
+                cur_pos, window, rope_base, out, chunks);
+}
+
+extern "C" int a2ats_far_query_rope(const void* q, int q_dtype, int64_t rows, int64_t d,
+                                    int64_t far_offset, double rope_base, void* out,
+                                    int out_dtype, void* stream) {
+  if ((q_dtype != A2ATS_F32 && q_dtype != A2ATS_BF16) ||
+      (out_dtype != A2ATS_F32 && out_dtype != A2ATS_BF16))
+    return A2ATS_EDTYPE;
+  if (d != kD || rows < 0) return A2ATS_EINVAL;
+  if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return A2ATS_EINVAL;
+  if (rows == 0) return A2ATS_OK;
+  if (!q || !out) return A2ATS_EINVAL;
+  // the output may be the input itself (same dtype), but may not overlap it otherwise
+  const size_t in_bytes = (size_t)rows * kD * (q_dtype == A2ATS_F32 ? 4 : 2);
+  const size_t out_bytes = (size_t)rows * kD * (out_dtype == A2ATS_F32 ? 4 : 2);
+  const char* qa = static_cast<const char*>(q);
+  const char* oa = static_cast<const char*>(out);
+  const bool overlap = qa < oa + out_bytes && oa < qa + in_bytes;
+  if (overlap && (qa != oa || q_dtype != out_dtype)) return A2ATS_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int64_t g = (rows + 3) / 4;
+  if (g > 1024) g = 1024;
+  const double pos = (double)far_offset;
+#define A2ATS_QROPE(I, O)                                                                        \
+  launch("far_query_rope", rope_query<I, O>, dim3((unsigned)g), dim3(256), 0, s, q, rows, pos, \
+         rope_base, out)
+  if (q_dtype == A2ATS_F32)
+    return out_dtype == A2ATS_F32 ? A2ATS_QROPE(A2ATS_F32, A2ATS_F32) : A2ATS_QROPE(A2ATS_F32, A2ATS_BF16);
+  return out_dtype == A2ATS_F32 ? A2ATS_QROPE(A2ATS_BF16, A2ATS_F32) : A2ATS_QROPE(A2ATS_BF16, A2ATS_BF16);
+#undef A2ATS_QROPE
 }

@@ -175,6 +175,40 @@ def test_reconstruct_validation(L):
     assert call(n=0) == 0
 
 
+def test_reconstruct_update_validation(L):
+    def call(out_dt=0, d=128, n=50, n_prev=40, cur_prev=99, cur=100, base=10000.0, c=10,
+             codes=FAKE):
+        return L.a2ats_reconstruct_update(codes, FAKE, 1, 2, n, d, FAKE, c, n_prev, cur_prev, cur,
+                                          16, base, FAKE, out_dt, None)
+
+    assert call(out_dt=3) == EDTYPE
+    assert call(d=256) == EINVAL
+    assert call(n_prev=-1) == EINVAL
+    assert call(n_prev=51) == EINVAL
+    assert call(cur_prev=-1) == EINVAL
+    assert call(cur=-2) == EINVAL
+    assert call(base=-1.0) == EINVAL
+    assert call(c=65537) == EINVAL
+    assert call(codes=None) == EINVAL
+    assert call(n=0, n_prev=0) == 0
+
+
+def test_far_query_rope_validation(L):
+    def call(q=FAKE, qdt=0, rows=4, d=128, base=10000.0, out=ctypes.c_void_p(1 << 20), odt=0):
+        return L.a2ats_far_query_rope(q, qdt, rows, d, 2048, base, out, odt, None)
+
+    assert call(qdt=2) == EDTYPE
+    assert call(odt=5) == EDTYPE
+    assert call(d=64) == EINVAL
+    assert call(rows=-1) == EINVAL
+    assert call(base=math.nan) == EINVAL
+    assert call(q=None) == EINVAL
+    assert call(rows=0) == 0
+    # partial overlap, or the same buffer with another dtype, is refused before any launch
+    assert call(out=ctypes.c_void_p(4096 + 256)) == EINVAL
+    assert call(out=FAKE, odt=1) == EINVAL
+
+
 def test_calibrate_validation(L):
     need = L.a2ats_calibrate_workspace(2, 100, 128)
     assert need > 0 and L.a2ats_calibrate_workspace(2, 100, 129) == 0

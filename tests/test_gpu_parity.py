@@ -349,6 +349,160 @@ class TestReconstruct:
 
 
 # ====================================================================== pipeline
+# ====================================================================== far keys unrotated
+def ulp(v, dtype):
+    """Spacing of the output format at |v| (fp32: 24 significant bits, bf16: 8)."""
+    bits = 24 if dtype == "f32" else 8
+    a = np.maximum(np.abs(np.asarray(v, np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - (bits - 1))
+
+
+def widen(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+class TestFarQueryRope:
+    @pytest.mark.parametrize("rows,b", [(1, 2048), (3, 0), (1000, 2048), (777, 131071), (64, -5)])
+    @pytest.mark.parametrize("dt_in,dt_out", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16"),
+                                              ("bf16", "f32")])
+    def test_matches_oracle(self, rows, b, dt_in, dt_out):
+        rng = np.random.default_rng(rows + 7 * abs(b))
+        x = (rng.standard_normal((rows, 128)) * 3).astype(np.float32)
+        if dt_in == "bf16":
+            x = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(x))
+        xd = torch.from_numpy(x).to(DEV)
+        if dt_in == "bf16":
+            xd = xd.to(torch.bfloat16)  # exact: x is already on the bf16 grid
+        odt = torch.float32 if dt_out == "f32" else torch.bfloat16
+        got = widen(kv.far_query_rope(xd, b, out_dtype=odt))
+        ref = oracle.rope_at(x.astype(np.float64), b)
+        # fp64 rotation rounded once: within one unit of the output format, and exact
+        # (nearest) for nearly every element
+        err = np.abs(got - ref)
+        assert np.all(err <= ulp(ref, dt_out)), err.max()
+        if dt_out == "bf16":
+            exact = (synth.f32_to_bf16_bits(got.astype(np.float32)) == oracle.round_bf16(ref)).mean()
+        else:
+            exact = (got == ref.astype(np.float32).astype(np.float64)).mean()
+        assert exact > 0.999, exact
+
+    def test_in_place_and_batched_shape(self):
+        rng = np.random.default_rng(3)
+        x = (rng.standard_normal((2, 24, 5, 128))).astype(np.float32)
+        xd = torch.from_numpy(x).to(DEV)
+        want = kv.far_query_rope(xd.clone(), 2048)
+        kv.far_query_rope(xd, 2048, out=xd)
+        assert torch.equal(xd, want)
+        ref = oracle.rope_at(x.reshape(-1, 128).astype(np.float64), 2048).reshape(x.shape)
+        assert np.abs(xd.cpu().numpy() - ref).max() <= 2.0 ** -22 * np.abs(ref).max()
+
+    def test_eq11_logits_against_fixed_offset_keys(self):
+        # logits of one query against far keys: (q R_b) . k with unrotated keys (GPU) equal
+        # RoPE(q, cur) . RoPE(k, cur - b), the fixed-offset form (oracle, fp64)
+        w = W["decode"]
+        cb = synth.codebook(w.cfg, 1, w.c)[0]
+        rng = np.random.default_rng(11)
+        n, cur, win, b = 4000, 5000, 256, 2048
+        codes = rng.integers(0, w.c, n).astype(np.uint16)
+        pos = np.arange(n, dtype=np.int32)
+        q = rng.standard_normal((1, 128)).astype(np.float32)
+        keys = kv.reconstruct(u16_to_dev(codes[None, None]), torch.from_numpy(pos[None]).to(DEV),
+                              f32_to_dev(cb[None]), cur, win, far_mode=kv.FAR_UNROTATED)
+        qb = kv.far_query_rope(torch.from_numpy(q).to(DEV), b)
+        logits = (keys[0, 0].double() @ qb[0].double()).cpu().numpy()
+        fixed, far = oracle.reconstruct(codes, pos, cb, cur, win, far_b=b)
+        assert far == n
+        ref = fixed @ oracle.rope_at(q.astype(np.float64), cur)[0]
+        scale = np.abs(cb[codes]).sum(1) * np.abs(q).sum()
+        assert np.all(np.abs(logits - ref) <= 1e-6 * scale)
+
+
+class TestReconstructUpdate:
+    @staticmethod
+    def setup_case(batch, heads, n, c, seed, out_dtype):
+        rng = np.random.default_rng(seed)
+        cb = (rng.standard_normal((heads, c, 128)) * 2).astype(np.float32)
+        codes = rng.integers(0, c, (batch, heads, n)).astype(np.uint16)
+        pos = np.tile(np.arange(n, dtype=np.int32), (batch, 1))
+        return (u16_to_dev(codes), torch.from_numpy(pos).to(DEV), f32_to_dev(cb),
+                torch.float32 if out_dtype == "f32" else torch.bfloat16, codes, pos, cb)
+
+    @staticmethod
+    def full(codes, pos, cb, cur, win, odt):
+        return kv.reconstruct(codes, pos, cb, cur, win, far_mode=kv.FAR_UNROTATED, out_dtype=odt)
+
+    @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+    @pytest.mark.parametrize("win", [64, 1, 0, -3, 100000])
+    def test_steps_match_full_reconstruct(self, out_dtype, win):
+        batch, heads, n, c = 2, 3, 3000, 70
+        cd, pd, cbd, odt, codes, pos, cb = self.setup_case(batch, heads, n, c, 5, out_dtype)
+        # decode steps: one token appended per step, the window slides by one; rows of
+        # tokens not yet appended hold a sentinel until their first update writes them
+        n_prev, cur = n - 10, n - 11
+        out = self.full(cd, pd, cbd, cur, win, odt)
+        out[:, :, n_prev:] = 7.0
+        for step in range(10):
+            kv.reconstruct_update(cd, pd, cbd, n_prev, cur, cur + 1, win, out)
+            n_prev, cur = n_prev + 1, cur + 1
+            assert torch.equal(out, self.full(cd, pd, cbd, cur, win, odt)), step
+        # a jump of many positions at once
+        kv.reconstruct_update(cd, pd, cbd, n, cur, cur + 150, win, out)
+        assert torch.equal(out, self.full(cd, pd, cbd, cur + 150, win, odt))
+
+    @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+    def test_writes_only_changed_rows(self, out_dtype):
+        batch, heads, n, c, win = 2, 2, 1500, 40, 100
+        cd, pd, cbd, odt, codes, pos, cb = self.setup_case(batch, heads, n, c, 6, out_dtype)
+        cur0, cur1, n_prev = 1200, 1260, 1490
+        out = self.full(cd, pd, cbd, cur0, win, odt)
+        # sentinels: one row whose status is unchanged (must survive), rows that crossed the
+        # window edge and appended rows (must be rewritten)
+        keep_t, cross_t, leave_t = 500, 1230, 1120
+        out[:, :, keep_t] = 3.0
+        out[:, :, cross_t] = 3.0   # far at cur0 (1230 > 1200: not yet seen), near at cur1
+        out[:, :, leave_t] = 3.0   # near at cur0 (delta 80), far at cur1 (delta 140)
+        out[:, :, n_prev:] = 3.0
+        kv.reconstruct_update(cd, pd, cbd, n_prev, cur0, cur1, win, out)
+        ref = self.full(cd, pd, cbd, cur1, win, odt)
+        assert torch.all(out[:, :, keep_t] == 3.0)
+        out[:, :, keep_t] = ref[:, :, keep_t]
+        assert torch.equal(out, ref)
+
+    def test_backwards_invalid_codes_and_positions(self):
+        batch, heads, n, c, win = 1, 2, 800, 30, 50
+        cd, pd, cbd, odt, codes, pos, cb = self.setup_case(batch, heads, n, c, 7, "f32")
+        pos[0, 10] = -4
+        codes[0, 1, 700] = 31  # >= c
+        pd = torch.from_numpy(pos).to(DEV)
+        cd = u16_to_dev(codes)
+        out = self.full(cd, pd, cbd, 790, win, odt)
+        kv.reconstruct_update(cd, pd, cbd, n, 790, 720, win, out)  # moving back in time
+        ref = self.full(cd, pd, cbd, 720, win, odt)
+        assert torch.equal(torch.nan_to_num(out, nan=-9.0), torch.nan_to_num(ref, nan=-9.0))
+        assert torch.isnan(out[0, 1, 700]).all() and torch.isnan(out[0, :, 10]).all()
+
+    def test_decode_shape_step_against_oracle(self):
+        # the decode workload: 32 sequences x 8 heads x 16384 tokens, fp32, W=256; one step
+        w = W["decode"]
+        cb = synth.codebook(w.cfg, w.heads, w.c)
+        codes = synth.uniform_codes(w.cfg, (w.batch, w.heads, w.n), w.c)
+        pos = np.tile(np.arange(w.n, dtype=np.int32), (w.batch, 1))
+        cd, pd, cbd = u16_to_dev(codes), torch.from_numpy(pos).to(DEV), f32_to_dev(cb)
+        cur = w.n - 1
+        out = kv.reconstruct(cd, pd, cbd, cur - 1, w.window, far_mode=kv.FAR_UNROTATED)
+        kv.reconstruct_update(cd, pd, cbd, w.n - 1, cur - 1, cur, w.window, out)
+        full = kv.reconstruct(cd, pd, cbd, cur, w.window, far_mode=kv.FAR_UNROTATED)
+        assert torch.equal(out, full)
+        # the rows the step changed, against the oracle
+        for t in (cur - w.window, w.n - 1, cur - w.window + 1, 0):
+            for hh in (0, 5):
+                got = out[:, hh, t].cpu().numpy()
+                ref, _ = oracle.reconstruct(codes[:, hh, t], pos[:, t], cb[hh], cur, w.window,
+                                            far_mode=oracle.FAR_UNROTATED)
+                check_rotation(got, ref, cb[hh][codes[:, hh, t]].astype(np.float64), "f32",
+                               "decode step token %d head %d" % (t, hh))
+
+
 class TestPipeline:
     def test_two_streams_prepared_equals_sequential(self):
         # the benchmark's step: prepares and the H-weighted encode on a second stream
