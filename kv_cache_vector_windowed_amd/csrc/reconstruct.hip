@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256) void rope_gather(
 // to cur rewrites only the tokens whose status changed, plus the tokens appended since
 // (index >= n_prev).  Work item = (sequence, 256 tokens): each thread tests one token, the
 // changed ones are listed in LDS, and the workgroup then writes their rows for every head
-// with the gather's own arithmetic (near: the rotation at the token's position from
+// (all (head, token) rows spread over the workgroup at once) with the gather's own arithmetic (near: the rotation at the token's position from
 // rope_cs; far: identity), so the rows are bitwise those of a full reconstruct at cur.
 template <bool BF16>
 __global__ __launch_bounds__(256) void rope_update(
@@ -298,39 +298,41 @@ __global__ __launch_bounds__(256) void rope_update(
   if (cnt == 0) return;
   const int g = t % TPT, tk = t / TPT;
   const int i0 = g * P;
-  for (int64_t h = 0; h < heads; ++h) {
+  // (head, listed token) pairs, all heads at once, so every row's loads are in flight together
+  const int64_t rows_total = heads * (int64_t)cnt;
+  for (int64_t e2 = tk; e2 < rows_total; e2 += TOK) {
+    const int64_t h = e2 / cnt;
+    const int e = (int)(e2 % cnt);
     const float* cbh = cb + h * c * kD;
-    for (int e = tk; e < cnt; e += TOK) {
-      const int64_t row = t0 + s_tok[e];
-      const int pp = s_pos[e];
-      const int code = codes[(b * heads + h) * n + row];
-      const int64_t ooff = ((b * heads + h) * n + row) * kD + i0;
-      real lo[P], hi[P];
-      if ((int64_t)code >= c || pp < 0) {
+    const int64_t row = t0 + s_tok[e];
+    const int pp = s_pos[e];
+    const int code = codes[(b * heads + h) * n + row];
+    const int64_t ooff = ((b * heads + h) * n + row) * kD + i0;
+    real lo[P], hi[P];
+    if ((int64_t)code >= c || pp < 0) {
 #pragma unroll
-        for (int k = 0; k < P; ++k) lo[k] = hi[k] = (real)NAN;
-      } else {
-        float xl[P], xh[P];
-        load_pairs<P>(cbh + (int64_t)code * kD + i0, xl, xh);
-        real cs[P], sn[P];
-        if (in_window(cur, pp, window)) {
+      for (int k = 0; k < P; ++k) lo[k] = hi[k] = (real)NAN;
+    } else {
+      float xl[P], xh[P];
+      load_pairs<P>(cbh + (int64_t)code * kD + i0, xl, xh);
+      real cs[P], sn[P];
+      if (in_window(cur, pp, window)) {
 #pragma unroll
-          for (int k = 0; k < P; ++k) {
-            const d2 v = rope_cs((double)pp, i0 + k, kD, base);
-            cs[k] = (real)v.x;
-            sn[k] = (real)v.y;
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < P; ++k) {
-            cs[k] = (real)1.0;
-            sn[k] = (real)0.0;
-          }
+        for (int k = 0; k < P; ++k) {
+          const d2 v = rope_cs((double)pp, i0 + k, kD, base);
+          cs[k] = (real)v.x;
+          sn[k] = (real)v.y;
         }
-        rotate_pairs<real, P>(xl, xh, cs, sn, lo, hi);
+      } else {
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+          cs[k] = (real)1.0;
+          sn[k] = (real)0.0;
+        }
       }
-      store_pairs<BF16, real, P>(out, ooff, lo, hi);
+      rotate_pairs<real, P>(xl, xh, cs, sn, lo, hi);
     }
+    store_pairs<BF16, real, P>(out, ooff, lo, hi);
   }
 }
 
