@@ -48,7 +48,7 @@ constexpr int kFragPerTile = kSteps * 64; // half8 fragments per tile (8 KiB)
 constexpr int kTPS = 4;                   // tiles per LDS stage of the coarse pass
 constexpr int kKeysPerWG = 256;           // 4 waves x 64 keys
 constexpr int kCandCap = 32;              // rescan candidates per key
-constexpr int kRescanTiles = 2;           // tiles per rescan work item
+constexpr int kDecideWgs = 256;           // workgroups of the rescan decide pass (a multiple of 8)
 constexpr float kPadBias = -1.0e38f;      // bias of padding rows: finite, never competitive
 
 struct Counters {
@@ -656,51 +656,81 @@ __device__ __forceinline__ int64_t open_count(const Counters* cnt, int64_t head,
 
 constexpr int kMaxHeadsLds = 1024;
 
-// Exclusive prefix over heads of `per(open count)`, built once per workgroup in LDS
-// (heads <= kMaxHeadsLds; larger head counts fall back to scanning global counters).
+// The heads a workgroup of the rescan kernels serves (all of them: binding heads to XCDs
+// measured slower, the heads' open counts differ too much) and its rank among the
+// workgroups serving them.
+struct HeadSet {
+  int64_t count;
+  int64_t rank, ranks;
+  __device__ int64_t head(int64_t v) const { return v; }
+};
+
+__device__ __forceinline__ HeadSet all_heads(int64_t heads) {
+  HeadSet hs;
+  hs.count = heads;
+  hs.rank = blockIdx.x;
+  hs.ranks = gridDim.x;
+  return hs;
+}
+
+// Exclusive prefix over the set's heads of `per(open count)`, built once per workgroup in
+// LDS (up to kMaxHeadsLds heads; beyond that the global counters are scanned).  The first
+// wave reads 64 heads' counters at once and scans them with shuffles.
 template <typename F>
-__device__ int64_t head_prefix(const Counters* cnt, int64_t heads, int64_t cap, int64_t* pre, F per) {
+__device__ int64_t head_prefix(const Counters* cnt, const HeadSet& hs, int64_t cap, int64_t* pre,
+                               F per) {
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int64_t hn = hs.count < kMaxHeadsLds ? hs.count : kMaxHeadsLds;
     int64_t run = 0;
-    const int64_t hn = heads < kMaxHeadsLds ? heads : kMaxHeadsLds;
-    for (int64_t h = 0; h < hn; ++h) {
-      pre[h] = run;
-      run += per(open_count(cnt, h, cap));
+    for (int64_t h0 = 0; h0 < hn; h0 += 64) {
+      const int64_t h = h0 + lane;
+      const int64_t v = h < hn ? per(open_count(cnt, hs.head(h), cap)) : 0;
+      int64_t incl = v;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int64_t u = __shfl_up(incl, o);
+        if (lane >= o) incl += u;
+      }
+      if (h < hn) pre[h] = run + incl - v;
+      run += __shfl(incl, 63);
     }
-    for (int64_t h = hn; h < heads; ++h) run += per(open_count(cnt, h, cap));
-    pre[kMaxHeadsLds] = run;
+    if (lane == 0) {
+      for (int64_t h = hn; h < hs.count; ++h) run += per(open_count(cnt, hs.head(h), cap));
+      pre[kMaxHeadsLds] = run;
+    }
   }
   __syncthreads();
   return pre[kMaxHeadsLds];
 }
 
-// Head owning global item index `it` (prefix from head_prefix).
+// Head (real index) owning item `it` of the set (prefix from head_prefix).
 template <typename F>
-__device__ int64_t find_head(const Counters* cnt, int64_t heads, int64_t cap, const int64_t* pre,
+__device__ int64_t find_head(const Counters* cnt, const HeadSet& hs, int64_t cap, const int64_t* pre,
                              int64_t it, F per, int64_t* rest) {
-  const int64_t hn = heads < kMaxHeadsLds ? heads : kMaxHeadsLds;
+  const int64_t hn = hs.count < kMaxHeadsLds ? hs.count : kMaxHeadsLds;
   int64_t lo = 0, hi = hn - 1;
-  if (hn > 0 && it < (hn < heads ? pre[hn - 1] + per(open_count(cnt, hn - 1, cap)) : pre[kMaxHeadsLds])) {
+  if (hn > 0 && it < (hn < hs.count ? pre[hn - 1] + per(open_count(cnt, hs.head(hn - 1), cap))
+                                    : pre[kMaxHeadsLds])) {
     while (lo < hi) {  // last head with pre[h] <= it
       const int64_t mid = (lo + hi + 1) / 2;
       if (pre[mid] <= it) lo = mid;
       else hi = mid - 1;
     }
     *rest = it - pre[lo];
-    return lo;
+    return hs.head(lo);
   }
-  int64_t run = hn > 0 ? pre[hn - 1] + per(open_count(cnt, hn - 1, cap)) : 0;
-  for (int64_t h = hn; h < heads; ++h) {
-    const int64_t m = per(open_count(cnt, h, cap));
+  int64_t run = hn > 0 ? pre[hn - 1] + per(open_count(cnt, hs.head(hn - 1), cap)) : 0;
+  for (int64_t h = hn; h < hs.count; ++h) {
+    const int64_t m = per(open_count(cnt, hs.head(h), cap));
     if (it < run + m) {
       *rest = it - run;
-      return h;
+      return hs.head(h);
     }
     run += m;
   }
   *rest = 0;
-  return heads - 1;
+  return hs.head(hs.count - 1);
 }
 
 // ------------------------------------------------------------------ the MFMA pass
@@ -1058,9 +1088,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ------------------------------------------------------------------ rescan of open keys
-// Work item = (head, group of 32 listed keys, chunk of kRescanTiles tiles).  One wave per
-// item: MFMA scores of the chunk (fragments straight from L2); every centroid whose score
-// reaches S * sbest - E is appended to the key's candidate list.
+// Work item = (head, group of 32 listed keys, chunk of tiles).  One wave per item: the keys
+// are loaded once, then the chunk's tiles are scored on MFMA (fragments straight from L2,
+// the next tile's fragments and bias loaded while the current tile runs); every centroid
+// whose score reaches S * sbest - E is appended to the key's candidate list.  The chunk
+// length adapts to the number of groups: about two items per wave of the grid (short
+// chunks when few keys are open, long ones when many are).
 template <int DT>
 __global__ __launch_bounds__(256) void enc_rescan_collect(
     const void* __restrict__ keys, int64_t n, int64_t heads, int T, int64_t c,
@@ -1069,17 +1102,24 @@ __global__ __launch_bounds__(256) void enc_rescan_collect(
     int64_t unc_cap, const Counters* __restrict__ cnt, unsigned* __restrict__ cand_n,
     int32_t* __restrict__ cand) {
   const int t = threadIdx.x, lane = t & 63, col = lane & 31, hh = lane >> 5;
-  const int chunks = (T + kRescanTiles - 1) / kRescanTiles;
+  const HeadSet hsx = all_heads(heads);
   __shared__ int64_t pre[kMaxHeadsLds + 1];
-  auto per = [chunks](int64_t m) { return (m + 31) / 32 * chunks; };
-  const int64_t items = head_prefix(cnt, heads, unc_cap, pre, per);
-  for (int64_t it = (int64_t)blockIdx.x * 4 + (t >> 6); it < items; it += (int64_t)gridDim.x * 4) {
+  auto groups = [](int64_t m) { return (m + 31) / 32; };
+  const int64_t ngroups = head_prefix(cnt, hsx, unc_cap, pre, groups);
+  const int64_t waves = hsx.ranks * 4;
+  int64_t chunks = ngroups > 0 ? (2 * waves + ngroups - 1) / ngroups : 1;
+  if (chunks > T / 2) chunks = T / 2;
+  if (chunks < 1) chunks = 1;
+  int tpi = (int)((T + chunks - 1) / chunks);
+  tpi = (tpi + 1) & ~1;  // whole tile pairs (T is a multiple of kTPS)
+  chunks = (T + tpi - 1) / tpi;
+  const int64_t items = ngroups * chunks;
+  for (int64_t it = hsx.rank * 4 + (t >> 6); it < items; it += hsx.ranks * 4) {
     int64_t rest = 0;
-    const int64_t head = find_head(cnt, heads, unc_cap, pre, it, per, &rest);
+    const int64_t head = find_head(cnt, hsx, unc_cap, pre, it / chunks, groups, &rest);
+    const int chunk = (int)(it % chunks);
     const int64_t m = open_count(cnt, head, unc_cap);
-    const int64_t grp = rest / chunks;
-    const int chunk = (int)(rest % chunks);
-    const int64_t slot = grp * 32 + col;
+    const int64_t slot = rest * 32 + col;
     const bool live = slot < m;
     UncEntry ue;
     ue.row = -1;
@@ -1094,36 +1134,41 @@ __global__ __launch_bounds__(256) void enc_rescan_collect(
     const float thr = live ? (float)(th - fabs(th) * 0x1p-20 - 1e-30) : INFINITY;
     const half8* vh = v16 + head * (int64_t)T * kFragPerTile;
     const float* bh = bias + head * (int64_t)T * 32;
-    const int tb = chunk * kRescanTiles;  // T is a multiple of kRescanTiles
-    half8 fa[kRescanTiles][kSteps];
-    f16v acc[kRescanTiles];
-#pragma unroll
-    for (int q = 0; q < kRescanTiles; ++q) {
-      const int64_t tile = tb + q;
-      const f4* bl = reinterpret_cast<const f4*>(bh + tile * 32 + hh * 16);
+    const int tb = chunk * tpi;
+    const int nt = T - tb < tpi ? T - tb : tpi;  // even
+    auto load_tile = [&](int tile, half8 (&fa)[kSteps], f16v& acc) {
+      const f4* bl = reinterpret_cast<const f4*>(bh + (int64_t)tile * 32 + hh * 16);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const f4 b4 = bl[k];
-        acc[q][4 * k + 0] = b4.x; acc[q][4 * k + 1] = b4.y; acc[q][4 * k + 2] = b4.z; acc[q][4 * k + 3] = b4.w;
+        acc[4 * k + 0] = b4.x; acc[4 * k + 1] = b4.y; acc[4 * k + 2] = b4.z; acc[4 * k + 3] = b4.w;
       }
 #pragma unroll
-      for (int st = 0; st < kSteps; ++st) fa[q][st] = vh[tile * kFragPerTile + st * 64 + lane];
-    }
-#pragma unroll
-    for (int q = 0; q < kRescanTiles; ++q) {
+      for (int st = 0; st < kSteps; ++st) fa[st] = vh[(int64_t)tile * kFragPerTile + st * 64 + lane];
+    };
+    auto score_tile = [&](int tile, const half8 (&fa)[kSteps], f16v& acc) {
 #pragma unroll
       for (int st = 0; st < kSteps; ++st)
-        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[q][st], kf.f[0][st], acc[q], 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[st], kf.f[0][st], acc, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        if (acc[q][r] >= thr) {
-          const int j = (tb + q) * kRows + slot_row(r, hh);
+        if (acc[r] >= thr) {
+          const int j = tile * kRows + slot_row(r, hh);
           if (j < c) {
             const unsigned pos = atomicAdd(&cand_n[head * unc_cap + slot], 1u);
             if (pos < (unsigned)kCandCap) cand[(head * unc_cap + slot) * kCandCap + pos] = j;
           }
         }
       }
+    };
+    half8 fa0[kSteps], fa1[kSteps];
+    f16v acc0, acc1;
+    load_tile(tb, fa0, acc0);
+    for (int q = 0; q < nt; q += 2) {
+      load_tile(tb + q + 1, fa1, acc1);
+      score_tile(tb + q, fa0, acc0);
+      if (q + 2 < nt) load_tile(tb + q + 2, fa0, acc0);
+      score_tile(tb + q + 1, fa1, acc1);
     }
   }
 }
@@ -1171,9 +1216,11 @@ __device__ void full_scan_wave(const void* keys, int64_t n, int64_t c, const dou
   }
 }
 
-// One wave per open key: fp64 over its candidates (8 lanes per candidate, 8 at a time); a key
-// whose candidate list overflowed gets the full scan at once.  Then the keys the coarse pass
-// listed for the full scan (fp16-range keys, rescan list overflow).
+// One wave per open key: fp64 over its candidates (4 lanes per candidate, 16 at a time); a
+// key whose candidate list overflowed gets the full scan at once.  Then the keys the coarse
+// pass listed for the full scan (fp16-range keys, rescan list overflow).  Decision counts
+// are gathered per workgroup and added once, and only when statistics were asked for (a
+// same-address atomic per wave would serialise at the end of the pass).
 template <int DT>
 __global__ __launch_bounds__(256) void enc_rescan_decide(
     const void* __restrict__ keys, int64_t n, int64_t heads, int64_t c,
@@ -1181,16 +1228,17 @@ __global__ __launch_bounds__(256) void enc_rescan_decide(
     const double* __restrict__ b64,
     const UncEntry* __restrict__ unc, int64_t unc_cap, const unsigned* __restrict__ cand_n,
     const int32_t* __restrict__ cand, uint16_t* __restrict__ codes, float* __restrict__ dist,
-    FullEntry* __restrict__ full, Counters* __restrict__ cnt) {
-  const int t = threadIdx.x, lane = t & 63, g = lane & 7, q8 = lane >> 3;
+    FullEntry* __restrict__ full, Counters* __restrict__ cnt, int want_stats) {
+  const int t = threadIdx.x, lane = t & 63, g = lane & 3, q16 = lane >> 2;
+  const HeadSet hsx = all_heads(heads);
   __shared__ int64_t pre[kMaxHeadsLds + 1];
   __shared__ double kx[4][kD];
   auto per = [](int64_t m) { return m; };
-  const int64_t total = head_prefix(cnt, heads, unc_cap, pre, per);
+  const int64_t total = head_prefix(cnt, hsx, unc_cap, pre, per);
   unsigned decided = 0, full_scans = 0;
-  for (int64_t e = (int64_t)blockIdx.x * 4 + (t >> 6); e < total; e += (int64_t)gridDim.x * 4) {
+  for (int64_t e = hsx.rank * 4 + (t >> 6); e < total; e += hsx.ranks * 4) {
     int64_t rest = 0;
-    const int64_t head = find_head(cnt, heads, unc_cap, pre, e, per, &rest);
+    const int64_t head = find_head(cnt, hsx, unc_cap, pre, e, per, &rest);
     const int64_t slot = head * unc_cap + rest;
     const UncEntry ue = unc[slot];
     const unsigned nc = cand_n[slot];
@@ -1204,21 +1252,21 @@ __global__ __launch_bounds__(256) void enc_rescan_decide(
     int bj = ue.jbest;
     // ||k||^2 (for distances without a precomputed ||kL||^2) comes with the first batch
     double k2 = 0.0;
-    for (unsigned q0 = 0; q0 < (nc > 0 ? nc : 1u); q0 += 8) {
-      const unsigned q = q0 + q8;
+    for (unsigned q0 = 0; q0 < (nc > 0 ? nc : 1u); q0 += 16) {
+      const unsigned q = q0 + q16;
       double s = -INFINITY, kk = 0.0;
       int j = 0x7FFFFFFF;
       const int jj = q < nc ? cand[slot * kCandCap + q] : ue.jbest;
       const int64_t vo = ((int64_t)head * c + jj) * kD;
       const double bjj = b64[(int64_t)head * c + jj];
-      const double sj = plain ? coop_score8<DT>(keys, off, v32 + vo, bjj, g, &kk)
-                              : coop_score8<DT>(keys, off, v64 + vo, bjj, g, &kk);
+      const double sj = plain ? coop_score_g<DT, 4>(keys, off, v32 + vo, bjj, g, &kk)
+                              : coop_score_g<DT, 4>(keys, off, v64 + vo, bjj, g, &kk);
       if (q < nc) {
         s = sj;
         j = jj;
       }
       k2 = kk;
-      for (int o = 8; o < 64; o <<= 1) {
+      for (int o = 4; o < 64; o <<= 1) {
         const double os = __shfl_xor(s, o);
         const int oj = __shfl_xor(j, o);
         if (os > s || (os == s && oj < j)) {
@@ -1246,8 +1294,16 @@ __global__ __launch_bounds__(256) void enc_rescan_decide(
     full_scan_wave<DT>(keys, n, c, v64, b64, fe.head, fe.row, fe.z2, codes, dist, kx[t >> 6], lane);
     if (lane == 0) full_scans += 1;
   }
-  if (lane == 0 && decided) atomicAdd(&cnt->stats[3], decided);
-  if (lane == 0 && full_scans) atomicAdd(&cnt->stats[4], full_scans);
+  if (want_stats) {
+    __shared__ unsigned s_dec, s_full;
+    if (t == 0) s_dec = s_full = 0u;
+    __syncthreads();
+    if (lane == 0 && decided) atomicAdd(&s_dec, decided);
+    if (lane == 0 && full_scans) atomicAdd(&s_full, full_scans);
+    __syncthreads();
+    if (t == 0 && s_dec) atomicAdd(&cnt->stats[3], s_dec);
+    if (t == 0 && s_full) atomicAdd(&cnt->stats[4], s_full);
+  }
 }
 
 
@@ -1425,9 +1481,9 @@ int encode_run(const void* keys, int64_t heads, int64_t n, const int32_t* idx, i
   A2ATS_TRY(launch("encode_rescan_collect", enc_rescan_collect<DT>, dim3(512), dim3(256), 0, s, keys,
                    n, heads, T, c, L.v16, L.bias, L.hsc, L.unc, L.unc_cap, cnt,
                    L.cand_n, L.cand));
-  A2ATS_TRY(launch("encode_rescan_decide", enc_rescan_decide<DT>, dim3(256), dim3(256), 0, s, keys, n,
+  A2ATS_TRY(launch("encode_rescan_decide", enc_rescan_decide<DT>, dim3(kDecideWgs), dim3(256), 0, s, keys, n,
                    heads, c, L.v64, L.v32, plain ? 1 : 0, L.b64, L.unc, L.unc_cap, L.cand_n, L.cand, codes, dist, L.full,
-                   cnt));
+                   cnt, stats ? 1 : 0));
   if (stats)
     A2ATS_TRY(launch("encode_stats", enc_stats_out, dim3(1), dim3(64), 0, s, cnt, stats));
   return A2ATS_OK;
