@@ -302,6 +302,8 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
     W = synth.WORKLOADS
     res = {}
     flush_buf = torch.ones(2 ** 28, dtype=torch.float32, device=dev)  # 1 GiB, finite values
+    flush_buf.sum()  # the first reduction launch carries a one-time setup cost of ~20 ms
+    torch.cuda.synchronize()
 
     def timed(fn, reps, flush=False):
         """ms per call of fn, calls issued back to back on the stream so the host's issue time
