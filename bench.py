@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_MFMA_TFLOPS = 2516.6   # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (256 CU x 2.4 GHz x 256 flop/clk with FMA)
 METRIC = "keys encoded/sec (H-weighted VQ, d=128) + % MFMA peak; reconstruct GB/s"
 
 
@@ -500,6 +501,81 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
         "pipeline_kernels_us": {k: round(v[1] * 1e3, 2) for k, v in profile(pipe, 3).items()},
     }
     log("long_context %s" % res["long_context"])
+    del kd, codes, out
+    # The pages' default configuration: sub-vector codes (sub_dim 8, one shared 256-entry
+    # codebook), keys of the layer shape: split, plain codes for the bulk rows, cosine-blend
+    # (beta 0.5; no H) or H-weighted codes for the retrieval rows; values plain; bf16 keys
+    # reconstructed with W = 128, values gathered without rotation.
+    w = W["pq_layer"]
+    log("generating pq_layer inputs")
+    kd = keys_dev(synth.keys(w.cfg, w.heads, w.n, "bf16"))
+    vd = keys_dev(synth.keys(w.cfg, w.heads, w.n, "bf16", stream=8))  # value rows
+    cbk = f32(synth.pq_codebook(w.cfg, w.heads, w.c, 8))
+    cbv = f32(synth.pq_codebook(w.cfg + 100, w.heads, w.c, 8))
+    qs = synth.queries(w.cfg, w.heads, w.m)
+    _, lq = kv.calibrate(f32(qs.reshape(1, -1, 8)), 1e-4)
+    lq = lq[0].contiguous()
+    proxy = kd[:, -1].contiguous()
+    ret, bulk = kv.select_retrieval(kd, proxy, w.fraction)
+    kc = torch.zeros((w.heads, w.n, 16), dtype=torch.uint8, device=dev)
+    vc = torch.zeros((w.heads, w.n, 16), dtype=torch.uint8, device=dev)
+    pos = torch.arange(w.n, dtype=torch.int32, device=dev)[None]
+    kout = torch.empty((1, w.heads, w.n, 128), dtype=torch.bfloat16, device=dev)
+    vout = torch.empty_like(kout)
+
+    def enc_plain_all():
+        kv.pq_encode(kd, cbk, 8, codes=kc)
+
+    def enc_blend():
+        kv.pq_encode(kd, cbk, 8, query=proxy[:, None], beta=w.betas[0], idx=ret, codes=kc)
+
+    def enc_h():
+        kv.pq_encode(kd, cbk, 8, chol=lq, idx=ret, codes=kc)
+
+    def enc_values():
+        kv.pq_encode(vd, cbv, 8, codes=vc)
+
+    def rec_keys():
+        kv.pq_reconstruct(kc[None], pos, cbk, w.cur_pos, w.window, out=kout)
+
+    def rec_values():
+        kv.pq_reconstruct(vc[None], pos, cbv, w.cur_pos, 0, far_mode=kv.FAR_UNROTATED, out=vout)
+
+    def step():  # split, keys (bulk plain + retrieval blend), values, both reconstructions
+        r, b = kv.select_retrieval(kd, proxy, w.fraction)
+        kv.pq_encode(kd, cbk, 8, idx=b, codes=kc)
+        kv.pq_encode(kd, cbk, 8, query=proxy[:, None], beta=w.betas[0], idx=r, codes=kc)
+        enc_values()
+        rec_keys()
+        rec_values()
+
+    for f in (enc_plain_all, enc_blend, enc_h, enc_values, rec_keys, rec_values, step):
+        f()
+    torch.cuda.synchronize()
+    t_plain = timed(enc_plain_all, 10)
+    t_blend = timed(enc_blend, 5)
+    t_h = timed(enc_h, 10)
+    t_rk = timed(rec_keys, 10)
+    t_rv = timed(rec_values, 10)
+    t_step = timed(step, 5)
+    subvecs = w.heads * w.n * 16
+    flops_plain = 2.0 * subvecs * w.c * 8  # the sub-vector contraction, 2 k sub_dim per sub-vector
+    acc = kv.pq_accounting(w.n, w.heads, 128, 8, 8)
+    res["pq_layer"] = {
+        "workload": "8 heads x 32768 bf16 keys and values, sub_dim 8, one 256-entry codebook, "
+                    "retrieval fraction 0.2 (beta 0.5 blend or H-weighted), bf16 W=128 keys, "
+                    "values unrotated",
+        "step_ms": round(t_step, 4), "keys_per_s": round(w.heads * w.n / (t_step * 1e-3), 1),
+        "encode_plain_all_us": round(t_plain * 1e3, 2),
+        "encode_plain_alu_frac": round(flops_plain / (t_plain * 1e-3) / 1e12 / PEAK_FP32_VALU_TFLOPS, 4),
+        "encode_blend_retrieval_us": round(t_blend * 1e3, 2),
+        "encode_h_retrieval_us": round(t_h * 1e3, 2),
+        "reconstruct_keys_us": round(t_rk * 1e3, 2),
+        "reconstruct_keys_hbm_frac": round(w.heads * w.n * (16 + 256) / (t_rk * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "reconstruct_values_us": round(t_rv * 1e3, 2),
+        "accounting": acc,
+    }
+    log("pq_layer %s" % res["pq_layer"])
     return res
 
 

@@ -10,6 +10,7 @@
  *   reconstruct        centroid gather + windowed RoPE (and its incremental update for far
  *                      keys left unrotated)
  *   far_query_rope     the query-side far rotation R_b of Eq. 11
+ *   pq_*               the sub-vector (product) codes of the pages' default configuration
  *
  * Conventions shared by every call:
  *  - All array pointers are DEVICE pointers owned by the caller, row-major, contiguous,
@@ -245,6 +246,55 @@ int a2ats_reconstruct_update(const uint16_t* codes, const int32_t* positions, in
  */
 int a2ats_far_query_rope(const void* q, int q_dtype, int64_t rows, int64_t d, int64_t far_offset,
                          double rope_base, void* out, int out_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Sub-vector (product) VQ -- the pages' default configuration ("A2ATS-adapted" docs,
+ * "Configuration reference" and "What you get with the defaults"; the calibration example in
+ * "How it works" trains one codebook on the pooled sub-vectors of every head).  A head vector
+ * of d = 128 numbers is cut into d / sub_dim sub-vectors, each coded by one byte against a
+ * single shared codebook [k, sub_dim] (k = 2^bits <= 256).  sub_dim is 4 or 8 (the table's
+ * rows).
+ *
+ * pq_encode: for every selected row of x [heads, n, d] (idx as for a2ats_encode) and every
+ * sub-space s, codes[h, row, s] (uint8, [heads, n, d / sub_dim]) =
+ *   chol != NULL   argmin_j (x_s - c_j) H (x_s - c_j)^T, H = L L^T, chol = L [sub_dim,
+ *                  sub_dim] fp32 lower-triangular (one H for every sub-space, from the
+ *                  query sub-vectors: a2ats_calibrate with d = sub_dim on the queries viewed
+ *                  as [m * d / sub_dim, sub_dim])     -- a2ats_h_weighted_assignment
+ *   chol == NULL, query != NULL
+ *                  argmax_j beta (-e_j / max_i e_i) + (1 - beta) cos(q_s, c_j), q_s the same
+ *                  slice of query [heads, nq, d] (nq 1 or n, dtype of x), rules as for
+ *                  a2ats_assign_cosine            -- a2ats_query_aware_assignment
+ *   both NULL      argmin_j ||x_s - c_j||^2 (bulk rows; values)
+ * Ties go to the lowest index; the decision is exact (fp32 scan under a proven error bound,
+ * fp64 for close calls; the blend entirely in fp64).  No workspace; returns without waiting.
+ */
+int a2ats_pq_encode(const void* x, int x_dtype, int64_t heads, int64_t n, int64_t d,
+                    int64_t sub_dim, const int32_t* idx, int64_t n_idx, const float* codebook,
+                    int64_t k, const float* chol, const void* query, int64_t nq, double beta,
+                    uint8_t* codes, void* stream);
+
+/* pq_reconstruct: as a2ats_reconstruct, with x = the concatenation of the token's sub-centroids
+ * codebook[codes[b, h, t, s]] (codes uint8 [batch, heads, n, d / sub_dim]).  The value path of
+ * the pages (values are never rotated) is this call with window <= 0 and A2ATS_FAR_UNROTATED:
+ * a plain gather.  A token with any code >= k, or a negative position, gets a row of NaN.
+ * Workspace: a2ats_reconstruct_workspace(d, cur_pos, window) bytes.
+ */
+int a2ats_pq_reconstruct(const uint8_t* codes, const int32_t* positions, int64_t batch,
+                         int64_t heads, int64_t n, int64_t d, int64_t sub_dim,
+                         const float* codebook, int64_t k, int64_t cur_pos, int64_t window,
+                         int64_t far_offset, int far_mode, double rope_base, void* out,
+                         int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* pq_accounting (host only): what the settings alone decide ("What you get with the
+ * defaults"): bits / sub_dim bits per number, 16 / that as the ratio against fp16, a table of
+ * 2^bits x sub_dim fp16 entries; for `tokens` tokens of `heads` heads, the packed code bytes
+ * and the fp16 bytes of the same keys.  Any output pointer may be NULL.  Returns A2ATS_EINVAL
+ * unless d % sub_dim == 0 and 1 <= bits <= 16.
+ */
+int a2ats_pq_accounting(int64_t tokens, int64_t heads, int64_t d, int64_t sub_dim, int bits,
+                        double* bits_per_number, double* ratio_vs_fp16, int64_t* table_bytes,
+                        int64_t* compressed_bytes, int64_t* fp16_bytes);
 
 /* ---------------------------------------------------------------------------------------
  * Kernel timing (diagnostics).  While enabled, every kernel the library launches is

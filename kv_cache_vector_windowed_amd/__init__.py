@@ -65,13 +65,18 @@ def lib() -> ctypes.CDLL:
         L.a2ats_reconstruct_update.argtypes = [p, p, i64, i64, i64, i64, p, i64, i64, i64, i64,
                                                i64, dbl, p, i32, p]
         L.a2ats_far_query_rope.argtypes = [p, i32, i64, i64, i64, dbl, p, i32, p]
+        L.a2ats_pq_encode.argtypes = [p, i32, i64, i64, i64, i64, p, i64, p, i64, p, p, i64, dbl, p, p]
+        L.a2ats_pq_reconstruct.argtypes = [p, p, i64, i64, i64, i64, i64, p, i64, i64, i64, i64, i32,
+                                           dbl, p, i32, p, sz, p]
+        L.a2ats_pq_accounting.argtypes = [i64, i64, i64, i64, i32, p, p, p, p, p]
+        L.a2ats_pq_accounting.restype = i32
         L.a2ats_profile_enable.argtypes, L.a2ats_profile_enable.restype = [i32], i32
         L.a2ats_profile_reset.argtypes, L.a2ats_profile_reset.restype = [], i32
         L.a2ats_profile_read.argtypes, L.a2ats_profile_read.restype = [ctypes.c_char_p, sz], i64
         for f in ("a2ats_calibrate", "a2ats_encode", "a2ats_encode_prepare", "a2ats_encode_prepared",
                   "a2ats_assign_cosine",
                   "a2ats_select_retrieval", "a2ats_reconstruct", "a2ats_reconstruct_update",
-                  "a2ats_far_query_rope"):
+                  "a2ats_far_query_rope", "a2ats_pq_encode", "a2ats_pq_reconstruct"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -333,6 +338,76 @@ def far_query_rope(q: torch.Tensor, far_offset: int = 2048, rope_base: float = 1
                                       float(rope_base), _ptr(out), _dtype_code(out),
                                       _stream(q.device)), "far_query_rope")
     return out
+
+
+def pq_encode(x: torch.Tensor, codebook: torch.Tensor, sub_dim: int = 8,
+              chol: torch.Tensor | None = None, query: torch.Tensor | None = None,
+              beta: float = 0.5, idx: torch.Tensor | None = None,
+              codes: torch.Tensor | None = None):
+    """Sub-vector codes: x [heads, n, d] (fp32/bf16), codebook [k, sub_dim] fp32 shared by
+    every sub-space and head, chol [sub_dim, sub_dim] (H-weighted) or query [heads, nq, d]
+    (cosine blend) or neither (plain) -> codes [heads, n, d // sub_dim] uint8 (only the idx
+    rows are written when idx is given)."""
+    _dev(x, "x")
+    _dev(codebook, "codebook")
+    heads, n, d = x.shape
+    k = codebook.shape[0]
+    if codebook.shape[1] != sub_dim:
+        raise ValueError("codebook must be [k, sub_dim]")
+    if codes is None:
+        codes = torch.zeros((heads, n, d // sub_dim), dtype=torch.uint8, device=x.device)
+    n_idx = 0
+    if idx is not None:
+        _dev(idx, "idx")
+        if idx.dtype != torch.int32 or idx.dim() != 2 or idx.shape[0] != heads:
+            raise ValueError("idx must be [heads, n_idx] int32")
+        n_idx = idx.shape[1]
+    nq = 0
+    if query is not None:
+        _dev(query, "query")
+        nq = query.shape[1]
+    _check(lib().a2ats_pq_encode(_ptr(x), _dtype_code(x), heads, n, d, sub_dim, _ptr(idx), n_idx,
+                                 _ptr(codebook), k, _ptr(chol), _ptr(query), nq, float(beta),
+                                 _ptr(codes), _stream(x.device)), "pq_encode")
+    return codes
+
+
+def pq_reconstruct(codes: torch.Tensor, positions: torch.Tensor, codebook: torch.Tensor,
+                   cur_pos: int, window: int, far_offset: int = 2048,
+                   far_mode: int = FAR_FIXED_OFFSET, rope_base: float = 10000.0,
+                   out_dtype: torch.dtype = torch.float32, out: torch.Tensor | None = None):
+    """codes [batch, heads, n, m] uint8, positions [batch, n] int32, codebook [k, sub_dim]
+    -> out [batch, heads, n, m * sub_dim].  Values: window=0, far_mode=FAR_UNROTATED."""
+    _dev(codes, "codes")
+    _dev(positions, "positions")
+    _dev(codebook, "codebook")
+    batch, heads, n, m = codes.shape
+    k, sub = codebook.shape
+    d = m * sub
+    if positions.dtype != torch.int32 or positions.shape != (batch, n):
+        raise ValueError("positions must be [batch, n] int32")
+    if out is None:
+        out = torch.empty((batch, heads, n, d), dtype=out_dtype, device=codes.device)
+    else:
+        _dev(out, "out")
+    ws = _workspace(lib().a2ats_reconstruct_workspace(d, int(cur_pos), int(window)), codes.device)
+    _check(lib().a2ats_pq_reconstruct(_ptr(codes), _ptr(positions), batch, heads, n, d, sub,
+                                      _ptr(codebook), k, int(cur_pos), int(window), int(far_offset),
+                                      int(far_mode), float(rope_base), _ptr(out), _dtype_code(out),
+                                      _ptr(ws), ws.numel(), _stream(codes.device)), "pq_reconstruct")
+    return out
+
+
+def pq_accounting(tokens: int, heads: int, d: int = 128, sub_dim: int = 8, bits: int = 8) -> dict:
+    """The compression the settings decide: bits per number, ratio against fp16, table bytes,
+    packed code bytes and fp16 bytes for `tokens` tokens of `heads` heads (host only)."""
+    bpn, ratio = ctypes.c_double(), ctypes.c_double()
+    table, comp, fp16 = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().a2ats_pq_accounting(tokens, heads, d, sub_dim, bits, ctypes.byref(bpn),
+                                     ctypes.byref(ratio), ctypes.byref(table), ctypes.byref(comp),
+                                     ctypes.byref(fp16)), "pq_accounting")
+    return {"bits_per_number": bpn.value, "ratio_vs_fp16": ratio.value, "table_bytes": table.value,
+            "compressed_bytes": comp.value, "fp16_bytes": fp16.value}
 
 
 # ----------------------------------------------------------------- kernel timing

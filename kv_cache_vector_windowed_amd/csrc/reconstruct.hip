@@ -252,6 +252,119 @@ __global__ __launch_bounds__(256) void rope_gather(
   }
 }
 
+// Sub-vector (product) codes: a token's key is the concatenation of d / SUB sub-centroids
+// of one shared codebook [k, SUB] ("A2ATS-adapted" docs, "What you get with the
+// defaults").  Same work items, grid and arithmetic as rope_gather; each thread reads the
+// token's whole code row (d / SUB bytes), takes for each 4-dimension group of its pairs the
+// sub-centroid slice that covers it, and rotates and stores exactly as rope_gather does.  A
+// token with any code >= k, or a negative position, gets a row of NaN.
+template <bool BF16, int SUB>
+__global__ __launch_bounds__(256) void pq_gather(
+    const uint8_t* __restrict__ codes, const int32_t* __restrict__ positions, int64_t heads,
+    int64_t n, const float* __restrict__ cb, int64_t k, int64_t cur, int64_t window,
+    int64_t rows_near, const d2* __restrict__ table, void* __restrict__ out, int64_t items) {
+  constexpr int P = BF16 ? 8 : 4;
+  constexpr int TPT = kHalf / P;
+  constexpr int TOK = 256 / TPT;
+  constexpr int CH = BF16 ? kChunkBf16 : kChunkF32;
+  constexpr int U = CH / TOK;
+  constexpr int M = kD / SUB;   // codes per token
+  constexpr int NW = M / 4;     // 32-bit words of a code row (4 for SUB 8, 8 for SUB 4)
+  static_assert(SUB % 4 == 0 && M % 16 == 0, "code rows of whole 16-byte vectors");
+  using real = typename std::conditional<BF16, float, double>::type;
+  const int t = threadIdx.x;
+  const int g = t % TPT;
+  const int tk = t / TPT;
+  const int i0 = g * P;
+  __shared__ d2 s_far[kHalf];
+  if (t < kHalf) s_far[t] = table[rows_near * kHalf + t];
+  __syncthreads();
+  real fc[P], fs[P];
+#pragma unroll
+  for (int kk = 0; kk < P; ++kk) {
+    const d2 v = s_far[i0 + kk];
+    fc[kk] = (real)v.x;
+    fs[kk] = (real)v.y;
+  }
+  const int64_t chunks = (n + CH - 1) / CH;
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    const int64_t h = item % heads;
+    const int64_t rest = item / heads;
+    const int64_t b = rest / chunks;
+    const int64_t t0 = (rest % chunks) * CH;
+    unsigned cw[U][NW];
+    int pos[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t tok = t0 + u * TOK + tk;
+      pos[u] = -1;
+#pragma unroll
+      for (int q = 0; q < NW; ++q) cw[u][q] = 0u;
+      if (tok < n) {
+        const uint4* cr = reinterpret_cast<const uint4*>(codes + ((b * heads + h) * n + tok) * M);
+#pragma unroll
+        for (int q = 0; q < NW / 4; ++q) {
+          const uint4 v = cr[q];
+          cw[u][4 * q] = v.x; cw[u][4 * q + 1] = v.y; cw[u][4 * q + 2] = v.z; cw[u][4 * q + 3] = v.w;
+        }
+        pos[u] = positions[b * n + tok];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t tok = t0 + u * TOK + tk;
+      if (tok >= n) continue;
+      bool ok = pos[u] >= 0;
+#pragma unroll
+      for (int q = 0; q < NW; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ok = ok && (int64_t)((cw[u][q] >> (8 * e)) & 0xFFu) < k;
+      // the code of sub-space sidx (a runtime byte of the row held in registers)
+      auto code_of = [&](int sidx) {
+        unsigned w = 0u;
+#pragma unroll
+        for (int q = 0; q < NW; ++q) w = (sidx >> 2) == q ? cw[u][q] : w;
+        return (int64_t)((w >> (8 * (sidx & 3))) & 0xFFu);
+      };
+      float xl[P], xh[P];
+#pragma unroll
+      for (int kk = 0; kk < P; kk += 4) {
+        const int dl = i0 + kk, dh = kHalf + i0 + kk;
+        const int64_t cl = ok ? code_of(dl / SUB) : 0, chh = ok ? code_of(dh / SUB) : 0;
+        const f4 a = *reinterpret_cast<const f4*>(cb + cl * SUB + dl % SUB);
+        const f4 bb = *reinterpret_cast<const f4*>(cb + chh * SUB + dh % SUB);
+        xl[kk] = a.x; xl[kk + 1] = a.y; xl[kk + 2] = a.z; xl[kk + 3] = a.w;
+        xh[kk] = bb.x; xh[kk + 1] = bb.y; xh[kk + 2] = bb.z; xh[kk + 3] = bb.w;
+      }
+      const int64_t ooff = ((b * heads + h) * n + tok) * kD + i0;
+      real lo[P], hi[P];
+      if (!ok) {
+#pragma unroll
+        for (int kk = 0; kk < P; ++kk) lo[kk] = hi[kk] = (real)NAN;
+      } else {
+        real cs[P], sn[P];
+        if (in_window(cur, pos[u], window)) {
+          const d2* row = table + (cur - (int64_t)pos[u]) * kHalf + i0;
+#pragma unroll
+          for (int kk = 0; kk < P; ++kk) {
+            const d2 v = row[kk];
+            cs[kk] = (real)v.x;
+            sn[kk] = (real)v.y;
+          }
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < P; ++kk) {
+            cs[kk] = fc[kk];
+            sn[kk] = fs[kk];
+          }
+        }
+        rotate_pairs<real, P>(xl, xh, cs, sn, lo, hi);
+      }
+      store_pairs<BF16, real, P>(out, ooff, lo, hi);
+    }
+  }
+}
+
 // Incremental update for far keys left unrotated (Eq. 12): a token's reconstructed row then
 // depends on the current position only through its near/far status, so moving from cur_prev
 // to cur rewrites only the tokens whose status changed, plus the tokens appended since
@@ -465,4 +578,42 @@ extern "C" int a2ats_far_query_rope(const void* q, int q_dtype, int64_t rows, in
     return out_dtype == A2ATS_F32 ? A2ATS_QROPE(A2ATS_F32, A2ATS_F32) : A2ATS_QROPE(A2ATS_F32, A2ATS_BF16);
   return out_dtype == A2ATS_F32 ? A2ATS_QROPE(A2ATS_BF16, A2ATS_F32) : A2ATS_QROPE(A2ATS_BF16, A2ATS_BF16);
 #undef A2ATS_QROPE
+}
+
+extern "C" int a2ats_pq_reconstruct(const uint8_t* codes, const int32_t* positions, int64_t batch,
+                                    int64_t heads, int64_t n, int64_t d, int64_t sub_dim,
+                                    const float* codebook, int64_t k, int64_t cur_pos,
+                                    int64_t window, int64_t far_offset, int far_mode,
+                                    double rope_base, void* out, int out_dtype, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (out_dtype != A2ATS_F32 && out_dtype != A2ATS_BF16) return A2ATS_EDTYPE;
+  if (d != kD || batch < 1 || heads < 1 || n < 0 || k < 1 || k > 256) return A2ATS_EINVAL;
+  if (sub_dim != 4 && sub_dim != 8) return A2ATS_EINVAL;
+  if (cur_pos < 0 || !(rope_base > 0.0) || !std::isfinite(rope_base)) return A2ATS_EINVAL;
+  if (far_mode != A2ATS_FAR_FIXED_OFFSET && far_mode != A2ATS_FAR_UNROTATED) return A2ATS_EINVAL;
+  if (n == 0) return A2ATS_OK;
+  if (!codes || !positions || !codebook || !out) return A2ATS_EINVAL;
+  const int64_t rows = near_rows(cur_pos, window);
+  const size_t need = a2ats_reconstruct_workspace(d, cur_pos, window);
+  if (!ws_ok(workspace, workspace_bytes, need)) return A2ATS_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  d2* table = static_cast<d2*>(workspace);
+  A2ATS_TRY(launch("rope_table", rope_table, dim3(grid_for((rows + 1) * kHalf, 256)), dim3(256), 0,
+                   s, rows, cur_pos, cur_pos - far_offset, (int)(far_mode == A2ATS_FAR_UNROTATED),
+                   rope_base, (int)kD, table));
+  const int64_t chunk = out_dtype == A2ATS_F32 ? kChunkF32 : kChunkBf16;
+  const int64_t items = batch * heads * ((n + chunk - 1) / chunk);
+  int64_t per = 8 * heads;
+  int64_t g = items / (out_dtype == A2ATS_F32 ? kItemsPerWgF32 : kItemsPerWgBf16);
+  if (g < kGridMin) g = kGridMin;
+  g = (g + per - 1) / per * per;
+  if (g > items) g = items;
+  if (g > (int64_t)1 << 30) g = (int64_t)1 << 30;
+#define A2ATS_PQG(B, S)                                                                          \
+  launch("pq_reconstruct", pq_gather<B, S>, dim3((unsigned)g), dim3(256), 0, s, codes, positions, \
+         heads, n, codebook, k, cur_pos, window, rows, table, out, items)
+  if (out_dtype == A2ATS_F32)
+    return sub_dim == 8 ? A2ATS_PQG(false, 8) : A2ATS_PQG(false, 4);
+  return sub_dim == 8 ? A2ATS_PQG(true, 8) : A2ATS_PQG(true, 4);
+#undef A2ATS_PQG
 }

@@ -12,7 +12,8 @@ Recipe (stated once, used everywhere):
   ``s`` and the outlier channels come from stream 0.
 * ``draw(n, stream)`` returns ``n`` fp32 rows of that distribution from the
   given stream.  Keys use stream 1, the codebook stream 2 (the first ``C`` rows
-  of a separate seeded draw), decode-time new keys stream 6.
+  of a separate seeded draw), decode-time new keys stream 6, value rows stream 8;
+  the shared sub-vector codebook picks (stream 7) from pooled stream-2 sub-vectors.
 * Calibration queries are ``G @ A.T`` with ``A ~ N(0, 1/d)`` (stream 3) and
   ``G ~ N(0, 1)`` of shape ``[M, d]`` (stream 4), i.e. Gaussian with the
   non-diagonal covariance ``A A^T``.
@@ -107,6 +108,17 @@ def uniform_codes(cfg: int, shape, c: int) -> np.ndarray:
     return rng(cfg, 0, 5).integers(0, c, size=shape).astype(np.uint16)
 
 
+def pq_codebook(cfg: int, heads: int, k: int, sub_dim: int, d: int = D) -> np.ndarray:
+    """[k, sub_dim] fp32 shared sub-vector codebook: k sub-vectors picked (stream 7) from the
+    pooled sub-vectors of a separate seeded draw (stream 2) of every head, standing in for the
+    pages' codebook trained on pooled calibration keys."""
+    per = (k + heads - 1) // heads
+    pool = np.concatenate([draw(cfg, h, per, 2, d).reshape(-1, sub_dim) for h in range(heads)])
+    pick = rng(cfg, 0, 7).choice(pool.shape[0], size=k, replace=False)
+    return np.ascontiguousarray(pool[pick])
+
+
+
 # --------------------------------------------------------------------------- workloads
 @dataclasses.dataclass(frozen=True)
 class Workload:
@@ -144,4 +156,9 @@ WORKLOADS = {
     # Long-context pipeline: 8 x 131072 bf16, 5% retrieval split, C = 2048, W = 1024.
     "long_context": Workload("long_context", 4, 8, 131072, 2048, "bf16", m=4096, window=1024,
                              cur_pos=131071, fraction=0.05),
+    # The pages' default configuration on the layer shape: sub-vector codes (sub_dim 8, one
+    # shared codebook of 2^8 entries), W = 128, retrieval fraction 0.2, beta 0.5; keys and
+    # values, 8 heads x 32768 bf16 tokens.  c is the codebook size k.
+    "pq_layer": Workload("pq_layer", 5, 8, 32768, 256, "bf16", m=4096, window=128,
+                         cur_pos=32767, fraction=0.2, betas=(0.5,)),
 }

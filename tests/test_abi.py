@@ -1,6 +1,7 @@
 """The C ABI: the library loads, exports every function include/a2ats.h declares, and every
 host-side validation path returns its status without touching a device (runs on CPU)."""
 import ctypes
+import json
 import math
 import os
 import re
@@ -207,6 +208,47 @@ def test_far_query_rope_validation(L):
     # partial overlap, or the same buffer with another dtype, is refused before any launch
     assert call(out=ctypes.c_void_p(4096 + 256)) == EINVAL
     assert call(out=FAKE, odt=1) == EINVAL
+
+
+def test_pq_accounting_matches_pages_table(L):
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pq_compression.json")))
+    for case in g["cases"]:
+        r = kv.pq_accounting(4096, 8, 128, case["sub_dim"], case["bits"])
+        assert r["bits_per_number"] == case["bits_per_number"]
+        assert r["ratio_vs_fp16"] == case["smaller_by"]
+        assert r["table_bytes"] == case["table_kb"] * 1024
+        assert r["fp16_bytes"] == 4096 * 8 * 128 * 2
+        assert r["compressed_bytes"] * case["smaller_by"] == r["fp16_bytes"]
+    assert L.a2ats_pq_accounting(10, 1, 128, 12, 8, None, None, None, None, None) == EINVAL
+    assert L.a2ats_pq_accounting(10, 1, 128, 8, 0, None, None, None, None, None) == EINVAL
+
+
+def test_pq_validation(L):
+    def enc(dt=1, d=128, sub=8, k=256, n=10, beta=0.5, nq=1, q=None, chol=None, x=FAKE):
+        return L.a2ats_pq_encode(x, dt, 2, n, d, sub, None, 0, FAKE, k, chol, q, nq, beta, FAKE,
+                                 None)
+
+    assert enc(dt=9) == EDTYPE
+    assert enc(d=64) == EINVAL
+    assert enc(sub=16) == EINVAL
+    assert enc(k=257) == EINVAL
+    assert enc(k=0) == EINVAL
+    assert enc(q=FAKE, beta=1.5) == EINVAL
+    assert enc(q=FAKE, nq=3) == EINVAL
+    assert enc(x=None) == EINVAL
+    assert enc(n=0) == 0
+
+    def rec(odt=0, sub=8, k=256, n=10, wsb=1 << 20, mode=0, cur=5):
+        return L.a2ats_pq_reconstruct(FAKE, FAKE, 1, 2, n, 128, sub, FAKE, k, cur, 4, 2048, mode,
+                                      10000.0, FAKE, odt, FAKE, wsb, None)
+
+    assert rec(odt=4) == EDTYPE
+    assert rec(sub=2) == EINVAL
+    assert rec(k=300) == EINVAL
+    assert rec(mode=3) == EINVAL
+    assert rec(cur=-1) == EINVAL
+    assert rec(wsb=0) == EWORKSPACE
+    assert rec(n=0) == 0
 
 
 def test_calibrate_validation(L):

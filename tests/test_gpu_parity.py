@@ -503,6 +503,115 @@ class TestReconstructUpdate:
                                "decode step token %d head %d" % (t, hh))
 
 
+# ====================================================================== sub-vector codes
+def sub_rows(x, sub):
+    """[.., n, d] -> [.. * n * d/sub, sub] (row-major: sub-spaces of a row consecutive)."""
+    return np.ascontiguousarray(x.reshape(-1, sub))
+
+
+class TestPQ:
+    @staticmethod
+    def inputs(n, sub, k, dtype, seed):
+        keys = synth.keys(200 + seed, 2, n, dtype)
+        cb = synth.pq_codebook(200 + seed, 2, k, sub)
+        q = synth.queries(200 + seed, 2, 512)
+        l = oracle.cholesky(oracle.second_moment(sub_rows(q, sub), 1e-4))
+        return keys, cb, l
+
+    @pytest.mark.parametrize("sub,k", [(8, 256), (4, 256), (8, 16)])
+    @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+    @pytest.mark.parametrize("mode", ["plain", "h"])
+    def test_encode_matches_oracle(self, sub, k, dtype, mode):
+        keys, cb, l = self.inputs(700, sub, k, dtype, 1)
+        lt = f32_to_dev(l.astype(np.float32)) if mode == "h" else None
+        got = kv.pq_encode(keys_to_dev(keys), f32_to_dev(cb), sub, chol=lt).cpu().numpy()
+        # the oracle sees the same fp32 factor the kernel does
+        lref = l.astype(np.float32).astype(np.float64) if mode == "h" else None
+        code, d1, d2 = oracle.assign_h(sub_rows(keys.values, sub), cb, lref)
+        check_codes(got.reshape(-1).astype(np.int64), code, d1, d2, "pq %s sub %d k %d" % (mode, sub, k))
+
+    @pytest.mark.parametrize("sub", [8, 4])
+    @pytest.mark.parametrize("beta", [0.5, 1.0, 0.0])
+    def test_blend_matches_oracle(self, sub, beta):
+        keys, cb, _ = self.inputs(300, sub, 256, "bf16", 2)
+        xd = keys_to_dev(keys)
+        got = kv.pq_encode(xd, f32_to_dev(cb), sub, query=xd[:, -1:].contiguous(), beta=beta)
+        got = got.cpu().numpy()
+        m = 128 // sub
+        for h in range(2):
+            x = keys.values[h]
+            for s_ in range(m):
+                sl = slice(s_ * sub, (s_ + 1) * sub)
+                code, s1, s2 = oracle.assign_cosine(x[:, sl], x[-1, sl], cb, beta)
+                bad = (s1 - s2 > 1e-5) & (got[h, :, s_] != code)
+                assert not bad.any(), (h, s_, np.nonzero(bad)[0][:5])
+
+    def test_idx_rows_only_and_layer_shape_sampled(self):
+        w = W["pq_layer"]
+        keys = synth.keys(w.cfg, w.heads, w.n, w.key_dtype)
+        cb = synth.pq_codebook(w.cfg, w.heads, w.c, 8)
+        q = synth.queries(w.cfg, w.heads, w.m)
+        hq, lq = kv.calibrate(f32_to_dev(sub_rows(q, 8)[None]), 1e-4)  # one 8x8 H, pooled
+        kd = keys_to_dev(keys)
+        ret, bulk = kv.select_retrieval(kd, kd[:, -1].contiguous(), w.fraction)
+        codes = torch.full((w.heads, w.n, 16), 255, dtype=torch.uint8, device=DEV)
+        kv.pq_encode(kd, f32_to_dev(cb), 8, idx=bulk, codes=codes)
+        kv.pq_encode(kd, f32_to_dev(cb), 8, chol=lq[0], idx=ret, codes=codes)
+        got = codes.cpu().numpy()
+        ret, bulk = ret.cpu().numpy(), bulk.cpu().numpy()
+        lref = lq[0].cpu().numpy().astype(np.float64)
+        rng = np.random.default_rng(3)
+        for h in range(w.heads):
+            for rows, lf in ((rng.choice(ret[h], 300, replace=False), lref),
+                             (rng.choice(bulk[h], 300, replace=False), None)):
+                code, d1, d2 = oracle.assign_h(sub_rows(keys.values[h, rows], 8), cb, lf)
+                check_codes(got[h, rows].reshape(-1).astype(np.int64), code, d1, d2, "head %d" % h)
+        # a row selected by neither list keeps its initial bytes: every row is in one list
+        assert (got != 255).any(axis=2).all()
+
+    @pytest.mark.parametrize("sub", [8, 4])
+    @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+    def test_reconstruct_matches_oracle(self, sub, out_dtype):
+        rng = np.random.default_rng(9)
+        batch, heads, n, k, m = 2, 3, 1100, 200, 128 // sub
+        cb = synth.pq_codebook(210, 2, k, sub)
+        codes = rng.integers(0, k, (batch, heads, n, m)).astype(np.uint8)
+        pos = np.tile(np.arange(n, dtype=np.int32), (batch, 1))
+        cur, win, b = n - 1, 100, 2048
+        odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+        out = kv.pq_reconstruct(torch.from_numpy(codes).to(DEV), torch.from_numpy(pos).to(DEV),
+                                f32_to_dev(cb), cur, win, b, out_dtype=odt)
+        for bb in range(batch):
+            for h in range(heads):
+                full = cb[codes[bb, h]].reshape(n, 128).astype(np.float64)  # concatenated
+                ref, _ = oracle.reconstruct(np.arange(n, dtype=np.uint16), pos[bb], full, cur,
+                                            win, b)
+                if out_dtype == "f32":
+                    check_rotation(out[bb, h].cpu().numpy(), ref, full, "f32", "pq %d %d" % (bb, h))
+                else:
+                    gotb = bf16_to_np_bits(out[bb, h])
+                    mism = (gotb != oracle.round_bf16(ref)).mean()
+                    assert mism < 0.01, mism
+                    check_rotation(out[bb, h].float().cpu().numpy(), ref, full, "bf16", "pq")
+
+    def test_values_are_a_plain_gather_and_invalid_codes_nan(self):
+        rng = np.random.default_rng(10)
+        n, k = 500, 64
+        cb = synth.pq_codebook(211, 1, k, 8)
+        codes = rng.integers(0, k, (1, 2, n, 16)).astype(np.uint8)
+        codes[0, 1, 7, 3] = 200  # >= k
+        pos = np.arange(n, dtype=np.int32)[None].copy()
+        pos[0, 9] = -1
+        out = kv.pq_reconstruct(torch.from_numpy(codes).to(DEV), torch.from_numpy(pos).to(DEV),
+                                f32_to_dev(cb), n - 1, 0, far_mode=kv.FAR_UNROTATED).cpu().numpy()
+        want = cb[np.minimum(codes, k - 1)].reshape(1, 2, n, 128)
+        ok = np.ones((1, 2, n), bool)
+        ok[0, 1, 7] = False
+        ok[0, :, 9] = False
+        assert np.array_equal(out[ok], want[ok])
+        assert np.isnan(out[~ok]).all()
+
+
 class TestPipeline:
     def test_two_streams_prepared_equals_sequential(self):
         # the benchmark's step: prepares and the H-weighted encode on a second stream

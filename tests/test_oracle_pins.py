@@ -466,6 +466,33 @@ class TestFarQueryRope:
             np.testing.assert_allclose(unrot @ qb, cb @ qb, rtol=0, atol=0)
 
 
+class TestSubVectorComposition:
+    """The sub-vector codes of the pages' default configuration are the per-sub-space
+    assignments of orc_assign_h; with one H per sub-space (block-diagonal over the whole
+    vector) that equals the whole-vector H-weighted argmin over the product codebook."""
+
+    def test_block_diagonal_product_codebook_brute_force(self):
+        rng = np.random.default_rng(31)
+        sub, m, k = 2, 2, 3
+        cb = rng.standard_normal((k, sub))
+        l = random_spd_l(rng, sub, cond=5.0)
+        x = rng.standard_normal((40, sub * m)) * 1.5
+        per = [oracle.assign_h(x[:, s * sub:(s + 1) * sub], cb, l)[0] for s in range(m)]
+        # the product codebook: every pair of sub-centroids, the block-diagonal factor
+        combos = [(a, b) for a in range(k) for b in range(k)]
+        full = np.array([np.concatenate([cb[a], cb[b]]) for a, b in combos])
+        lb = np.zeros((sub * m, sub * m))
+        for s in range(m):
+            lb[s * sub:(s + 1) * sub, s * sub:(s + 1) * sub] = l
+        code, d1, d2 = oracle.assign_h(x, full, lb)
+        h = lb @ lb.T
+        for r in range(x.shape[0]):
+            q = [(x[r] - f) @ h @ (x[r] - f) for f in full]  # direct quadratic forms
+            assert int(np.argmin(q)) == code[r]
+            if d2[r] - d1[r] > 1e-9 * d1[r]:
+                assert combos[code[r]] == (per[0][r], per[1][r])
+
+
 # ============================================================ bf16 rounding
 class TestRoundBf16:
     def test_hand_values(self):
