@@ -44,9 +44,12 @@ def lib():
         L.orc_reconstruct.argtypes = [_up, _ip, _i64, _i64, _dp, _i64, _i64, _i64, _i64,
                                       ctypes.c_int, ctypes.c_double, _dp, _lp]
         L.orc_rope_at.argtypes = [_dp, _i64, _i64, ctypes.c_double, ctypes.c_double, _dp]
+        L.orc_kmeans_update.argtypes = [_dp, _i64, _i64, _ip, _i64, _dp, _dp, _lp]
+        L.orc_kmeans.argtypes = [_dp, _i64, _i64, _i64, _dp, ctypes.c_int, _dp, _ip]
         L.orc_round_bf16.argtypes = [_dp, _i64, _up]
         for f in (L.orc_second_moment, L.orc_cholesky, L.orc_assign_h, L.orc_assign_cosine,
-                  L.orc_select_retrieval, L.orc_reconstruct, L.orc_rope_at):
+                  L.orc_select_retrieval, L.orc_reconstruct, L.orc_rope_at,
+                  L.orc_kmeans_update, L.orc_kmeans):
             f.restype = ctypes.c_int
         L.orc_round_bf16.restype = None
         L.orc_threads.argtypes, L.orc_threads.restype = [], ctypes.c_int
@@ -183,6 +186,33 @@ def rope_at(x, position, base=10000.0):
     out = np.empty((rows, d))
     _check(lib().orc_rope_at(_ptr(x, _dp), rows, d, float(position), float(base), _ptr(out, _dp)))
     return out
+
+
+def kmeans_update(x, code, cb):
+    """x [n,d], code [n] (int), cb [k,d] -> (new cb fp64 [k,d], counts int64 [k])."""
+    x = _f64(x)
+    cb = _f64(cb)
+    code = np.ascontiguousarray(code, dtype=np.int32)
+    n, d = x.shape
+    k = cb.shape[0]
+    out = np.empty((k, d))
+    cnt = np.empty(k, np.int64)
+    _check(lib().orc_kmeans_update(_ptr(x, _dp), n, d, _ptr(code, _ip), k, _ptr(cb, _dp),
+                                   _ptr(out, _dp), _ptr(cnt, _lp)))
+    return out, cnt
+
+
+def kmeans(x, cb, l=None, iters=5):
+    """Lloyd's iterations from cb (H-weighted with l) -> (cb fp64 [k,d], final code [n])."""
+    x = _f64(x)
+    cb = _f64(cb).copy()
+    n, d = x.shape
+    k = cb.shape[0]
+    lf = _f64(l) if l is not None else None
+    code = np.empty(n, np.int32)
+    _check(lib().orc_kmeans(_ptr(x, _dp), n, d, k, _ptr(lf, _dp), int(iters), _ptr(cb, _dp),
+                            _ptr(code, _ip)))
+    return cb, code
 
 
 def round_bf16(x):

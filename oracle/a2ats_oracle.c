@@ -295,6 +295,57 @@ int orc_rope_at(const double* x, int64_t rows, int64_t d, double position, doubl
   return ORC_OK;
 }
 
+/* ------------------------------------------------------------------ codebook training */
+
+/* The update step of k-means in z-space ([API] a2ats_cholesky_factor: Eq. 16-18 make the
+ * H-weighted objective a plain Euclidean one on z = xL, so conventional k-means applies).
+ * The Euclidean k-means update in z-space is the mean of the cluster's z rows; since
+ * z = xL is linear and L is invertible, mapping that mean back (w L^-1) gives the mean of
+ * the cluster's x rows: the original-space centroid is the plain member mean, with or
+ * without H.  Members are summed in ascending row order in fp64, then divided by the count;
+ * a cluster with no member keeps its previous centroid.  counts (optional) gets the sizes. */
+int orc_kmeans_update(const double* x, int64_t n, int64_t d, const int32_t* code, int64_t k,
+                      const double* cb_in, double* cb_out, int64_t* counts) {
+  if (n < 0 || d <= 0 || k <= 0) return ORC_EINVAL;
+  double* sum = (double*)calloc((size_t)(k * d), sizeof(double));
+  int64_t* cnt = (int64_t*)calloc((size_t)k, sizeof(int64_t));
+  if (!sum || !cnt) { free(sum); free(cnt); return ORC_EINVAL; }
+  for (int64_t t = 0; t < n; ++t) {
+    const int64_t j = code[t];
+    if (j < 0 || j >= k) continue;
+    cnt[j] += 1;
+    for (int64_t a = 0; a < d; ++a) sum[j * d + a] += x[t * d + a];
+  }
+  for (int64_t j = 0; j < k; ++j) {
+    for (int64_t a = 0; a < d; ++a)
+      cb_out[j * d + a] = cnt[j] > 0 ? sum[j * d + a] / (double)cnt[j] : cb_in[j * d + a];
+    if (counts) counts[j] = cnt[j];
+  }
+  free(sum);
+  free(cnt);
+  return ORC_OK;
+}
+
+/* Lloyd's iteration with the H-weighted assignment: `iters` rounds of (orc_assign_h with L,
+ * or plain without, then orc_kmeans_update), cb updated in place, then the final assignment
+ * into code.  Each round's new centroids are rounded to fp32 before the next assignment, as
+ * a codebook stored in fp32 would be. */
+int orc_kmeans(const double* x, int64_t n, int64_t d, int64_t k, const double* l, int iters,
+               double* cb, int32_t* code) {
+  if (n < 0 || d <= 0 || k <= 0 || iters < 0) return ORC_EINVAL;
+  double* nxt = (double*)malloc(sizeof(double) * (size_t)(k * d));
+  if (!nxt) return ORC_EINVAL;
+  int st = ORC_OK;
+  for (int it = 0; it < iters && st == ORC_OK; ++it) {
+    st = orc_assign_h(x, n, d, cb, k, l, code, NULL, NULL);
+    if (st == ORC_OK) st = orc_kmeans_update(x, n, d, code, k, cb, nxt, NULL);
+    for (int64_t e = 0; e < k * d; ++e) cb[e] = (double)(float)nxt[e];
+  }
+  if (st == ORC_OK) st = orc_assign_h(x, n, d, cb, k, l, code, NULL, NULL);
+  free(nxt);
+  return st;
+}
+
 /* ------------------------------------------------------------------ output rounding */
 
 /* Nearest bf16 (8 significant bits, fp32 exponent range), ties to even, computed from

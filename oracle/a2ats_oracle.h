@@ -65,6 +65,16 @@ int orc_reconstruct(const uint16_t* codes, const int32_t* pos, int64_t n, int64_
 int orc_rope_at(const double* x, int64_t rows, int64_t d, double position, double base,
                 double* out);
 
+/* k-means update: each cluster's centroid becomes the fp64 mean of its member rows (ascending
+ * row order), an empty cluster keeps cb_in's row; counts (optional) receives the sizes. */
+int orc_kmeans_update(const double* x, int64_t n, int64_t d, const int32_t* code, int64_t k,
+                      const double* cb_in, double* cb_out, int64_t* counts);
+
+/* Lloyd's iterations with the H-weighted (L) or plain (L == NULL) assignment; cb in place,
+ * rounded to fp32 after each update; code receives the final assignment. */
+int orc_kmeans(const double* x, int64_t n, int64_t d, int64_t k, const double* l, int iters,
+               double* cb, int32_t* code);
+
 /* Threads the OpenMP loops use. */
 int orc_threads(void);
 

@@ -493,6 +493,84 @@ class TestSubVectorComposition:
                 assert combos[code[r]] == (per[0][r], per[1][r])
 
 
+class TestKmeans:
+    """Codebook training ([API] a2ats_cholesky_factor: Eq. 16-18 turn the H-weighted
+    objective into k-means on z = xL)."""
+
+    def test_update_is_the_member_mean_library_groupby(self):
+        rng = np.random.default_rng(41)
+        x = rng.standard_normal((300, 6)) * 3
+        code = rng.integers(0, 9, 300)
+        code[code == 4] = 5  # cluster 4 empty: keeps its old centroid
+        cb = rng.standard_normal((9, 6))
+        out, cnt = oracle.kmeans_update(x, code, cb)
+        sums = np.zeros((9, 6))
+        np.add.at(sums, code, x)  # numpy's unbuffered scatter-add as the reference
+        cnts = np.bincount(code, minlength=9)
+        assert np.array_equal(cnt, cnts)
+        for j in range(9):
+            want = cb[j] if cnts[j] == 0 else sums[j] / cnts[j]
+            np.testing.assert_allclose(out[j], want, rtol=1e-14, atol=1e-15)
+        assert np.array_equal(out[4], cb[4])
+
+    def test_hand_case_two_clusters(self):
+        x = np.array([[0.0, 0.0], [0.0, 2.0], [10.0, 0.0], [12.0, 0.0]])
+        cb, code = oracle.kmeans(x, np.array([[1.0, 1.0], [9.0, 0.0]]), iters=3)
+        assert code.tolist() == [0, 0, 1, 1]
+        np.testing.assert_array_equal(cb, [[0.0, 1.0], [11.0, 0.0]])
+
+    def test_h_weighted_equals_plain_kmeans_in_z_space(self):
+        # Eq. 16-18: H-weighted k-means on x from C0 is plain k-means on z = xL from W0 = C0 L,
+        # with the centroids related by W = C L after every round
+        rng = np.random.default_rng(42)
+        d, k = 8, 6
+        l = random_spd_l(rng, d, cond=8.0)
+        x = rng.standard_normal((400, d)) * np.linspace(0.5, 3.0, d)
+        c0 = x[rng.choice(400, k, replace=False)].copy()
+        ch = c0.copy()
+        wz = c0 @ l
+        for _ in range(4):  # one round at a time, without the fp32 rounding of orc_kmeans
+            code_h, _, _ = oracle.assign_h(x, ch, l)
+            code_z, _, _ = oracle.assign_h(x @ l, wz, None)
+            assert np.array_equal(code_h, code_z)
+            ch, _ = oracle.kmeans_update(x, code_h, ch)
+            wz, _ = oracle.kmeans_update(x @ l, code_z, wz)
+            np.testing.assert_allclose(ch @ l, wz, rtol=1e-10, atol=1e-10)
+
+    def test_objective_never_increases(self):
+        rng = np.random.default_rng(43)
+        d, k = 8, 16
+        l = random_spd_l(rng, d, cond=10.0)
+        x = rng.standard_normal((600, d)) * 2
+        cb = x[:k].copy()
+        h = l @ l.T
+        prev = np.inf
+        for it in range(6):
+            code, d1, _ = oracle.assign_h(x, cb, l)
+            obj = d1.sum()
+            assert obj <= prev * (1 + 1e-12)
+            prev = obj
+            cb, _ = oracle.kmeans_update(x, code, cb)
+        # the assignment's distance is the H-weighted quadratic form
+        r = x[0] - cb[code[0]]
+        code0, d10, _ = oracle.assign_h(x[:1], cb, l)
+        np.testing.assert_allclose(d10[0], (x[0] - cb[code0[0]]) @ h @ (x[0] - cb[code0[0]]),
+                                   rtol=1e-12)
+
+    def test_wrong_update_is_caught(self):
+        # planted mistake: averaging in z-space without mapping back (keeping W as C) moves
+        # the centroids away from the member means
+        rng = np.random.default_rng(44)
+        d = 4
+        l = random_spd_l(rng, d, cond=6.0)
+        x = rng.standard_normal((100, d))
+        code = rng.integers(0, 3, 100)
+        good, _ = oracle.kmeans_update(x, code, np.zeros((3, d)))
+        wrong, _ = oracle.kmeans_update(x @ l, code, np.zeros((3, d)))
+        assert np.abs(good - wrong).max() > 0.1
+        np.testing.assert_allclose(good @ l, wrong, rtol=1e-12, atol=1e-12)
+
+
 # ============================================================ bf16 rounding
 class TestRoundBf16:
     def test_hand_values(self):
