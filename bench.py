@@ -576,6 +576,40 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
         "accounting": acc,
     }
     log("pq_layer %s" % res["pq_layer"])
+    # Codebook training (Lloyd rounds on the device, H-weighted assignment): whole-vector
+    # codebooks of the layer workload (8 x 32768 bf16 keys, k = 1024), and the pages' shared
+    # sub-vector codebook (k = 256, sub_dim 8) over the same keys pooled as 4.2M sub-vectors.
+    wl = W["layer"]
+    kl = keys_dev(synth.keys(wl.cfg, wl.heads, wl.n, "bf16"))
+    _, ll = kv.calibrate(f32(synth.queries(wl.cfg, wl.heads, wl.m)), 1e-4)
+    cb_init = kl[:, ::wl.n // wl.c][:, :wl.c].float().contiguous()
+    cbw = cb_init.clone()
+    sub_x = kd.reshape(-1, 8)
+    cbs_init = sub_x[:: sub_x.shape[0] // 256][:256].float().contiguous()
+    cbs = cbs_init.clone()
+
+    def train_whole():
+        cbw.copy_(cb_init)
+        kv.kmeans(kl, cbw, ll, iters=5)
+
+    def train_sub():
+        cbs.copy_(cbs_init)
+        kv.kmeans(sub_x, cbs, lq, iters=5)
+
+    train_whole()
+    train_sub()
+    torch.cuda.synchronize()
+    t_w = timed(train_whole, 3)
+    t_s = timed(train_sub, 3)
+    pr_w = profile(train_whole, 1)
+    res["kmeans"] = {
+        "workload": "5 Lloyd rounds + final assignment, H-weighted: 8 heads x 32768 bf16 keys with "
+                    "k=1024 per head; 4.2M pooled sub-vectors (sub_dim 8) with one k=256 codebook",
+        "whole_ms_per_round": round(t_w / 6, 4),
+        "sub_ms_per_round": round(t_s / 6, 4),
+        "whole_update_us": round(sum(v[1] for kk, v in pr_w.items() if kk.startswith("kmeans_")) * 1e3, 2),
+    }
+    log("kmeans %s" % res["kmeans"])
     return res
 
 

@@ -11,6 +11,7 @@
  *                      keys left unrotated)
  *   far_query_rope     the query-side far rotation R_b of Eq. 11
  *   pq_*               the sub-vector (product) codes of the pages' default configuration
+ *   kmeans*            codebook training: Lloyd's k-means with the H-weighted assignment
  *
  * Conventions shared by every call:
  *  - All array pointers are DEVICE pointers owned by the caller, row-major, contiguous,
@@ -295,6 +296,41 @@ int a2ats_pq_reconstruct(const uint8_t* codes, const int32_t* positions, int64_t
 int a2ats_pq_accounting(int64_t tokens, int64_t heads, int64_t d, int64_t sub_dim, int bits,
                         double* bits_per_number, double* ratio_vs_fp16, int64_t* table_bytes,
                         int64_t* compressed_bytes, int64_t* fp16_bytes);
+
+/* ---------------------------------------------------------------------------------------
+ * Codebook training -- "veloxquant_mlx.quantizers.a2ats module", a2ats_cholesky_factor:
+ * Eq. 16-18 map the H-weighted objective to plain k-means on z = xL.  The z-space update
+ * (the cluster mean of z) mapped back through L^-1 is the cluster mean of x, so Lloyd's
+ * iteration here alternates the exact H-weighted (or plain) assignment with the member mean.
+ *
+ * kmeans_update: codebook_out[h, j] = fp64 mean of the rows x[h, r] with codes[h, r] == j,
+ * rounded once to fp32; a code with no member keeps codebook_in[h, j]; codes >= k are
+ * ignored.  counts (optional) [heads, k] int32 receives the cluster sizes.
+ *   x         [heads, n, d] fp32 or bf16, d in {4, 8, 16, 32, 64, 128}
+ *   codes     [heads, n] uint16 (codes_bytes 2) or uint8 (codes_bytes 1, k <= 256)
+ *   codebook  [heads, k] x d fp32, 1 <= k <= 4096; codebook_out may be codebook_in
+ * Deterministic: the members are grouped by a stable sort and summed in a fixed order (no
+ * floating-point atomics).  Workspace: a2ats_kmeans_update_workspace(heads, n, k) bytes.
+ */
+size_t a2ats_kmeans_update_workspace(int64_t heads, int64_t n, int64_t k);
+int a2ats_kmeans_update(const void* x, int x_dtype, int64_t heads, int64_t n, int64_t d,
+                        const void* codes, int codes_bytes, int64_t k, const float* codebook_in,
+                        float* codebook_out, int32_t* counts, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* kmeans: `iters` Lloyd rounds on the device from the initial codebook (updated in place),
+ * then the final assignment into codes.  chol (optional) is L for the H-weighted assignment.
+ *   d = 128   x [heads, n, 128], per-head codebooks [heads, k, 128] and L [heads, 128, 128]
+ *             (a2ats_encode); codes uint16 [heads, n]
+ *   d = 4, 8  one codebook [k, d] (k <= 256) over the pooled sub-vectors x [n, d] (heads must
+ *             be 1, n a multiple of 128 / d), L [d, d] (a2ats_pq_encode); codes uint8 [n] --
+ *             the pages' calibration trains this codebook on the keys viewed as [-1, sub_dim]
+ * Workspace: a2ats_kmeans_workspace(heads, n, d, k) bytes.  Returns without waiting.
+ */
+size_t a2ats_kmeans_workspace(int64_t heads, int64_t n, int64_t d, int64_t k);
+int a2ats_kmeans(const void* x, int x_dtype, int64_t heads, int64_t n, int64_t d, int64_t k,
+                 const float* chol, int iters, float* codebook, void* codes, void* workspace,
+                 size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * Kernel timing (diagnostics).  While enabled, every kernel the library launches is

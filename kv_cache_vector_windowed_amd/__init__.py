@@ -70,13 +70,20 @@ def lib() -> ctypes.CDLL:
                                            dbl, p, i32, p, sz, p]
         L.a2ats_pq_accounting.argtypes = [i64, i64, i64, i64, i32, p, p, p, p, p]
         L.a2ats_pq_accounting.restype = i32
+        L.a2ats_kmeans_update_workspace.argtypes = [i64, i64, i64]
+        L.a2ats_kmeans_update_workspace.restype = sz
+        L.a2ats_kmeans_update.argtypes = [p, i32, i64, i64, i64, p, i32, i64, p, p, p, p, sz, p]
+        L.a2ats_kmeans_workspace.argtypes = [i64, i64, i64, i64]
+        L.a2ats_kmeans_workspace.restype = sz
+        L.a2ats_kmeans.argtypes = [p, i32, i64, i64, i64, i64, p, i32, p, p, p, sz, p]
         L.a2ats_profile_enable.argtypes, L.a2ats_profile_enable.restype = [i32], i32
         L.a2ats_profile_reset.argtypes, L.a2ats_profile_reset.restype = [], i32
         L.a2ats_profile_read.argtypes, L.a2ats_profile_read.restype = [ctypes.c_char_p, sz], i64
         for f in ("a2ats_calibrate", "a2ats_encode", "a2ats_encode_prepare", "a2ats_encode_prepared",
                   "a2ats_assign_cosine",
                   "a2ats_select_retrieval", "a2ats_reconstruct", "a2ats_reconstruct_update",
-                  "a2ats_far_query_rope", "a2ats_pq_encode", "a2ats_pq_reconstruct"):
+                  "a2ats_far_query_rope", "a2ats_pq_encode", "a2ats_pq_reconstruct",
+                  "a2ats_kmeans_update", "a2ats_kmeans"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -408,6 +415,47 @@ def pq_accounting(tokens: int, heads: int, d: int = 128, sub_dim: int = 8, bits:
                                      ctypes.byref(fp16)), "pq_accounting")
     return {"bits_per_number": bpn.value, "ratio_vs_fp16": ratio.value, "table_bytes": table.value,
             "compressed_bytes": comp.value, "fp16_bytes": fp16.value}
+
+
+def kmeans_update(x: torch.Tensor, codes: torch.Tensor, codebook: torch.Tensor,
+                  out: torch.Tensor | None = None, want_counts: bool = False):
+    """x [heads, n, d], codes [heads, n] uint16 or uint8, codebook [heads, k, d] fp32 ->
+    new codebook (cluster member means; empty clusters unchanged) [, counts int32]."""
+    _dev(x, "x")
+    _dev(codes, "codes")
+    _dev(codebook, "codebook")
+    heads, n, d = x.shape
+    k = codebook.shape[-2]
+    if out is None:
+        out = torch.empty_like(codebook)
+    counts = torch.empty((heads, k), dtype=torch.int32, device=x.device) if want_counts else None
+    cbytes = 2 if codes.dtype == torch.uint16 else 1
+    ws = _workspace(lib().a2ats_kmeans_update_workspace(heads, n, k), x.device)
+    _check(lib().a2ats_kmeans_update(_ptr(x), _dtype_code(x), heads, n, d, _ptr(codes), cbytes, k,
+                                     _ptr(codebook), _ptr(out), _ptr(counts), _ptr(ws), ws.numel(),
+                                     _stream(x.device)), "kmeans_update")
+    return (out, counts) if want_counts else out
+
+
+def kmeans(x: torch.Tensor, codebook: torch.Tensor, chol: torch.Tensor | None = None,
+           iters: int = 10):
+    """Lloyd's k-means from `codebook` (updated in place).  x [heads, n, 128] with codebook
+    [heads, k, 128] (codes uint16 [heads, n]), or pooled sub-vectors x [n, d] (d 4 or 8) with
+    one codebook [k, d] (codes uint8 [n]).  Returns (codebook, codes)."""
+    _dev(x, "x")
+    _dev(codebook, "codebook")
+    if x.dim() == 2:
+        heads, (n, d) = 1, x.shape
+        codes = torch.empty(n, dtype=torch.uint8, device=x.device)
+    else:
+        heads, n, d = x.shape
+        codes = torch.empty((heads, n), dtype=torch.uint16, device=x.device)
+    k = codebook.shape[-2]
+    ws = _workspace(lib().a2ats_kmeans_workspace(heads, n, d, k), x.device)
+    _check(lib().a2ats_kmeans(_ptr(x), _dtype_code(x), heads, n, d, k, _ptr(chol), int(iters),
+                              _ptr(codebook), _ptr(codes), _ptr(ws), ws.numel(), _stream(x.device)),
+           "kmeans")
+    return codebook, codes
 
 
 # ----------------------------------------------------------------- kernel timing

@@ -251,6 +251,34 @@ def test_pq_validation(L):
     assert rec(n=0) == 0
 
 
+def test_kmeans_validation(L):
+    need = L.a2ats_kmeans_update_workspace(2, 1000, 64)
+    assert need > 0
+
+    def upd(dt=0, d=128, cb=2, k=64, n=1000, wsb=None, x=FAKE):
+        wsb = need if wsb is None else wsb
+        return L.a2ats_kmeans_update(x, dt, 2, n, d, FAKE, cb, k, FAKE, FAKE, None, FAKE, wsb, None)
+
+    assert upd(dt=5) == EDTYPE
+    assert upd(cb=4) == EDTYPE
+    assert upd(d=12) == EINVAL
+    assert upd(k=5000) == EINVAL
+    assert upd(cb=1, k=300) == EINVAL
+    assert upd(x=None) == EINVAL
+    assert upd(wsb=16) == EWORKSPACE
+
+    def km(d=128, heads=1, n=1024, k=64, iters=3, wsb=1 << 30):
+        return L.a2ats_kmeans(FAKE, 0, heads, n, d, k, None, iters, FAKE, FAKE, FAKE, wsb, None)
+
+    assert km(d=16) == EINVAL          # the driver trains whole vectors or 4/8 sub-vectors
+    assert km(d=8, heads=2) == EINVAL  # one shared sub-vector codebook
+    assert km(d=8, n=1000) == EINVAL   # 1000 sub-vectors do not fill whole 128-wide rows
+    assert km(d=8, k=512) == EINVAL
+    assert km(iters=-1) == EINVAL
+    assert km(wsb=8) == EWORKSPACE
+    assert km(n=0) == 0
+
+
 def test_calibrate_validation(L):
     need = L.a2ats_calibrate_workspace(2, 100, 128)
     assert need > 0 and L.a2ats_calibrate_workspace(2, 100, 129) == 0

@@ -612,6 +612,86 @@ class TestPQ:
         assert np.isnan(out[~ok]).all()
 
 
+# ====================================================================== codebook training
+def f32_ulp(v):
+    return np.spacing(np.abs(np.asarray(v, np.float32))).astype(np.float64)
+
+
+class TestKmeans:
+    @pytest.mark.parametrize("d,dtype", [(128, "bf16"), (128, "f32"), (8, "f32"), (4, "bf16")])
+    def test_update_matches_oracle(self, d, dtype):
+        rng = np.random.default_rng(50 + d)
+        heads, n, k = 2, 3072, 64
+        keys = synth.keys(60 + d, heads, n * d // 128, dtype)
+        x = keys.values.reshape(heads, n, d)
+        codes = rng.integers(0, k + 3, (heads, n))  # k .. k+2: ignored
+        codes[codes == 7] = 8                       # cluster 7 empty in both heads
+        cb = rng.standard_normal((heads, k, d)).astype(np.float32)
+        xd = torch.from_numpy(x).to(DEV)
+        if dtype == "bf16":
+            xd = xd.to(torch.bfloat16)  # exact: the values are on the bf16 grid
+        ct = torch.uint16 if d == 128 else torch.uint8
+        cd = torch.from_numpy(codes.astype(np.uint16 if d == 128 else np.uint8)).to(DEV)
+        out, cnt = kv.kmeans_update(xd, cd, f32_to_dev(cb), want_counts=True)
+        out, cnt = out.cpu().numpy(), cnt.cpu().numpy()
+        for h in range(heads):
+            ref, rc = oracle.kmeans_update(x[h], codes[h], cb[h])
+            assert np.array_equal(cnt[h], rc)
+            ref32 = ref.astype(np.float32)
+            if d == 128:  # members summed in ascending row order, as the oracle does
+                assert np.array_equal(out[h], ref32)
+            else:         # interleaved member subsets: within one fp32 unit
+                assert np.all(np.abs(out[h] - ref32) <= f32_ulp(ref32))
+            assert np.array_equal(out[h, 7], cb[h, 7])
+
+    def test_update_is_deterministic(self):
+        keys = synth.keys(70, 2, 5000, "bf16")
+        xd = keys_to_dev(keys)
+        codes = torch.from_numpy(np.random.default_rng(1).integers(0, 300, (2, 5000)).astype(np.uint16)).to(DEV)
+        cb = f32_to_dev(np.zeros((2, 300, 128), np.float32))
+        a = kv.kmeans_update(xd, codes, cb)
+        b = kv.kmeans_update(xd, codes, cb)
+        assert torch.equal(a, b)
+
+    @pytest.mark.parametrize("use_h", [True, False])
+    def test_lloyd_whole_vectors_matches_oracle(self, use_h):
+        w = W["layer"]
+        heads, n, k = 2, 4096, 64
+        keys = synth.keys(w.cfg, heads, n, "bf16")
+        cb0 = keys.values[:, ::n // k][:, :k].copy()  # k spread rows as the initial codebook
+        lt = None
+        if use_h:
+            _, lt = kv.calibrate(f32_to_dev(synth.queries(w.cfg, heads, 1024)), 1e-4)
+        cbd = f32_to_dev(cb0)
+        cbd, codes = kv.kmeans(keys_to_dev(keys), cbd, lt, iters=4)
+        got_cb, got_code = cbd.cpu().numpy(), codes.cpu().numpy()
+        for h in range(heads):
+            lref = lt[h].cpu().numpy().astype(np.float64) if use_h else None
+            ref_cb, ref_code = oracle.kmeans(keys.values[h], cb0[h], lref, iters=4)
+            assert np.array_equal(got_code[h], ref_code)
+            assert np.array_equal(got_cb[h], ref_cb.astype(np.float32))
+
+    def test_lloyd_pooled_sub_vectors(self):
+        w = W["pq_layer"]
+        keys = synth.keys(w.cfg, 1, 2048, "f32")
+        x = np.ascontiguousarray(keys.values[0].reshape(-1, 8))  # the pages' reshape(-1, sub_dim)
+        cb0 = x[::x.shape[0] // 256][:256].copy()
+        q = synth.queries(w.cfg, 1, 512)
+        _, lt = kv.calibrate(f32_to_dev(np.ascontiguousarray(q.reshape(1, -1, 8))), 1e-4)
+        cbd, codes = kv.kmeans(f32_to_dev(x), f32_to_dev(cb0), lt[0].contiguous(), iters=2)
+        lref = lt[0].cpu().numpy().astype(np.float64)
+        ref_cb, ref_code = oracle.kmeans(x, cb0, lref, iters=2)
+        got_code = codes.cpu().numpy()
+        # updates agree within one fp32 unit (interleaved sums), so near-ties may flip a few
+        # assignments; the codebooks stay within a tight relative band
+        assert (got_code == ref_code).mean() > 0.999
+        np.testing.assert_allclose(cbd.cpu().numpy(), ref_cb, rtol=1e-3, atol=1e-3)
+        # the H-weighted objective of the trained codebook is no worse than the initial one
+        _, d_init, _ = oracle.assign_h(x, cb0, lref)
+        _, d_fin, _ = oracle.assign_h(x, cbd.cpu().numpy(), lref)
+        assert d_fin.sum() < d_init.sum()
+
+
 class TestPipeline:
     def test_two_streams_prepared_equals_sequential(self):
         # the benchmark's step: prepares and the H-weighted encode on a second stream
