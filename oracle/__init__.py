@@ -46,10 +46,11 @@ def lib():
         L.orc_rope_at.argtypes = [_dp, _i64, _i64, ctypes.c_double, ctypes.c_double, _dp]
         L.orc_kmeans_update.argtypes = [_dp, _i64, _i64, _ip, _i64, _dp, _dp, _lp]
         L.orc_kmeans.argtypes = [_dp, _i64, _i64, _i64, _dp, ctypes.c_int, _dp, _ip]
+        L.orc_topk_codes.argtypes = [_dp, _i64, _up, _i64, _dp, _i64, _i64, _ip, _dp]
         L.orc_round_bf16.argtypes = [_dp, _i64, _up]
         for f in (L.orc_second_moment, L.orc_cholesky, L.orc_assign_h, L.orc_assign_cosine,
                   L.orc_select_retrieval, L.orc_reconstruct, L.orc_rope_at,
-                  L.orc_kmeans_update, L.orc_kmeans):
+                  L.orc_kmeans_update, L.orc_kmeans, L.orc_topk_codes):
             f.restype = ctypes.c_int
         L.orc_round_bf16.restype = None
         L.orc_threads.argtypes, L.orc_threads.restype = [], ctypes.c_int
@@ -213,6 +214,21 @@ def kmeans(x, cb, l=None, iters=5):
     _check(lib().orc_kmeans(_ptr(x, _dp), n, d, k, _ptr(lf, _dp), int(iters), _ptr(cb, _dp),
                             _ptr(code, _ip)))
     return cb, code
+
+
+def topk_codes(qb, codes, cb, k):
+    """qb [d] (= q R_b), codes [n] uint16, cb [c,d], k -> (idx int32 [k] ascending,
+    score fp64 [k])."""
+    qb = _f64(qb).reshape(-1)
+    codes = np.ascontiguousarray(codes, dtype=np.uint16)
+    cb = _f64(cb)
+    n = codes.shape[0]
+    c, d = cb.shape
+    idx = np.empty(k, np.int32)
+    sc = np.empty(k)
+    _check(lib().orc_topk_codes(_ptr(qb, _dp), d, _ptr(codes, _up), n, _ptr(cb, _dp), c, int(k),
+                                _ptr(idx, _ip), _ptr(sc, _dp)))
+    return idx, sc
 
 
 def round_bf16(x):

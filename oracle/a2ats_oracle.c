@@ -346,6 +346,54 @@ int orc_kmeans(const double* x, int64_t n, int64_t d, int64_t k, const double* l
   return st;
 }
 
+/* ------------------------------------------------------------------ top-K over codes */
+
+static int orc_cmp_score_desc(const void* a, const void* b) {
+  const orc_scored* x = (const orc_scored*)a;
+  const orc_scored* y = (const orc_scored*)b;
+  if (x->cosv > y->cosv) return -1;
+  if (x->cosv < y->cosv) return 1;
+  return (x->idx > y->idx) - (x->idx < y->idx);
+}
+
+/* [ABS] A2ATS approximates attention scores with the quantised keys to retrieve the top-K
+ * tokens.  With far keys unrotated (Eq. 12) and R_b on the query (Eq. 11), the approximate
+ * logit of token t is (q R_b) . c_{code_t}: one table of C values per query, gathered by
+ * code.  qb is q R_b.  The table entries are the fp64 dot products (each product, then the
+ * running sum, in dimension order) rounded once to fp32.  A token whose code is >= C scores
+ * -inf.  The K tokens with the largest scores (equal scores: lower index first) are returned
+ * in ascending index order with their scores. */
+int orc_topk_codes(const double* qb, int64_t d, const uint16_t* codes, int64_t n,
+                   const double* cb, int64_t c, int64_t k, int32_t* idx, double* score) {
+  if (d <= 0 || n < 0 || c <= 0 || k < 0 || k > n) return ORC_EINVAL;
+  double* lut = (double*)malloc(sizeof(double) * (size_t)c);
+  orc_scored* s = (orc_scored*)malloc(sizeof(orc_scored) * (size_t)(n > 0 ? n : 1));
+  if (!lut || !s) { free(lut); free(s); return ORC_EINVAL; }
+  for (int64_t j = 0; j < c; ++j) {
+    double acc = 0.0;
+    for (int64_t a = 0; a < d; ++a) acc += qb[a] * cb[j * d + a];
+    lut[j] = (double)(float)acc;
+  }
+  for (int64_t t = 0; t < n; ++t) {
+    s[t].cosv = codes[t] < c ? lut[codes[t]] : -INFINITY;  /* the record's score field */
+    s[t].idx = (int32_t)t;
+  }
+  qsort(s, (size_t)n, sizeof(orc_scored), orc_cmp_score_desc);
+  /* the first k, back in index order */
+  int32_t* pick = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
+  if (!pick) { free(lut); free(s); return ORC_EINVAL; }
+  for (int64_t i = 0; i < k; ++i) pick[i] = s[i].idx;
+  qsort(pick, (size_t)k, sizeof(int32_t), orc_cmp_i32);
+  for (int64_t i = 0; i < k; ++i) {
+    idx[i] = pick[i];
+    if (score) score[i] = codes[pick[i]] < c ? lut[codes[pick[i]]] : -INFINITY;
+  }
+  free(pick);
+  free(lut);
+  free(s);
+  return ORC_OK;
+}
+
 /* ------------------------------------------------------------------ output rounding */
 
 /* Nearest bf16 (8 significant bits, fp32 exponent range), ties to even, computed from

@@ -75,6 +75,12 @@ int orc_kmeans_update(const double* x, int64_t n, int64_t d, const int32_t* code
 int orc_kmeans(const double* x, int64_t n, int64_t d, int64_t k, const double* l, int iters,
                double* cb, int32_t* code);
 
+/* Approximate-score top-K over codes: table lut_j = fl32(qb . c_j) (fp64 products and sum in
+ * dimension order), score_t = lut[codes[t]] (-inf for codes >= c); the k largest (equal
+ * scores: lower index first) in ascending index order, with their scores. */
+int orc_topk_codes(const double* qb, int64_t d, const uint16_t* codes, int64_t n,
+                   const double* cb, int64_t c, int64_t k, int32_t* idx, double* score);
+
 /* Threads the OpenMP loops use. */
 int orc_threads(void);
 

@@ -571,6 +571,51 @@ class TestKmeans:
         np.testing.assert_allclose(good @ l, wrong, rtol=1e-12, atol=1e-12)
 
 
+class TestTopkCodes:
+    """[ABS] top-K retrieval by approximate attention scores over the quantised keys."""
+
+    def test_scores_are_the_far_logits_of_unrotated_keys(self):
+        # the table score of token t is the Eq. 11 logit (q R_b) . k_t for its unrotated
+        # quantised key (Eq. 12), here taken from orc_reconstruct and orc_rope_at
+        rng = np.random.default_rng(51)
+        d, c, n, b = 128, 40, 300, 2048
+        cb = rng.standard_normal((c, d))
+        codes = rng.integers(0, c, n).astype(np.uint16)
+        q = rng.standard_normal((1, d))
+        qb = oracle.rope_at(q, b)[0]
+        idx, sc = oracle.topk_codes(qb, codes, cb, n)  # k = n: every token, index order
+        assert np.array_equal(idx, np.arange(n))
+        keys, _ = oracle.reconstruct(codes, np.arange(n, dtype=np.int32), cb, cur=n - 1,
+                                     window=0, far_mode=oracle.FAR_UNROTATED)
+        logit = keys @ qb
+        np.testing.assert_allclose(sc, logit, rtol=2.0 ** -23, atol=1e-12)
+        # and the fixed-offset form of the same logit
+        fixed, _ = oracle.reconstruct(codes, np.arange(n, dtype=np.int32), cb, cur=n - 1,
+                                      window=0, far_b=b)
+        np.testing.assert_allclose(sc, fixed @ oracle.rope_at(q, n - 1)[0], rtol=1e-6, atol=1e-6)
+
+    def test_selection_against_a_stable_library_sort(self):
+        rng = np.random.default_rng(52)
+        d, c, n = 16, 12, 500  # few centroids: many equal scores, ties by index
+        cb = rng.standard_normal((c, d))
+        codes = rng.integers(0, c + 2, n).astype(np.uint16)  # c, c+1: invalid, score -inf
+        qb = rng.standard_normal(d)
+        lut = (cb @ qb).astype(np.float32).astype(np.float64)
+        score = np.where(codes < c, lut[np.minimum(codes, c - 1)], -np.inf)
+        order = np.lexsort((np.arange(n), -score))  # score descending, then index ascending
+        for k in (0, 1, 37, 250, 499, 500):
+            idx, sc = oracle.topk_codes(qb, codes, cb, k)
+            assert np.array_equal(idx, np.sort(order[:k]))
+            assert np.array_equal(sc, score[idx])
+
+    def test_hand_case(self):
+        cb = np.array([[1.0, 0.0], [0.0, 1.0], [-1.0, 0.0]])
+        codes = np.array([2, 0, 1, 0, 2, 1], np.uint16)
+        idx, sc = oracle.topk_codes(np.array([3.0, 1.0]), codes, cb, 3)
+        # table (3, 1, -3): the two code-0 tokens (1, 3) and the first code-1 token (2)
+        assert idx.tolist() == [1, 2, 3] and sc.tolist() == [3.0, 1.0, 3.0]
+
+
 # ============================================================ bf16 rounding
 class TestRoundBf16:
     def test_hand_values(self):
