@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 PEAK_MFMA_TFLOPS = 2516.6   # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (256 CU x 2.4 GHz x 256 flop/clk with FMA)
+PEAK_FP64_TFLOPS = 78.6        # MI355X fp64 vector (an FMA counted as two operations)
 METRIC = "keys encoded/sec (H-weighted VQ, d=128) + % MFMA peak; reconstruct GB/s"
 
 
@@ -436,6 +437,39 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
     }
     log("decode_unrotated %s" % res["decode_unrotated"])
     del out
+    # Top-K retrieval over the same codes: rotate the step's queries by R_b, score every token
+    # through the per-query table (q R_b) . c_j gathered by code, keep the best 10%.
+    wt = W["topk_decode"]
+    kt = int(np.ceil(wt.fraction * wt.n))
+    qt = torch.from_numpy(np.ascontiguousarray(
+        synth.queries(wt.cfg, wt.q_heads, wt.batch).transpose(1, 0, 2))).to(dev)
+    qtb = torch.empty_like(qt)
+    t_idx = torch.empty((wt.batch, wt.q_heads, kt), dtype=torch.int32, device=dev)
+
+    def topk_step():
+        kv.far_query_rope(qt, wt.far_b, out=qtb)
+        kv.topk_codes(qtb, codes, cbd, kt)
+
+    topk_step()
+    torch.cuda.synchronize()
+    ms_t = timed(topk_step, 20)
+    ms_tf = timed(topk_step, 5, flush=True)
+    pr_t = profile(topk_step, 5)
+    kt_us = pr_t["topk_codes"][1] * 1e3
+    t_bytes = (wt.batch * wt.heads * wt.n * 2 + wt.heads * wt.c * 128 * 4
+               + wt.batch * wt.q_heads * (128 * 4 + kt * 8))
+    t_flops = 2.0 * wt.batch * wt.q_heads * wt.c * 128  # fp64 table: one mul + one add a term
+    res["topk_decode"] = {
+        "workload": "32 sequences x 24 query heads over 8 key heads x 16384 codes, C=1024, "
+                    "k=%d (10%%); far query rotation + table + top-K" % kt,
+        "step_us": round(ms_t * 1e3, 2), "step_flushed_us": round(ms_tf * 1e3, 2),
+        "topk_kernel_us": round(kt_us, 2),
+        "far_query_rope_us": round(pr_t["far_query_rope"][1] * 1e3, 2),
+        "algorithmic_bytes": t_bytes, "kernel_GBps": round(t_bytes / (kt_us * 1e-6) / 1e9, 1),
+        "table_fp64_ops": t_flops,
+        "table_fp64_frac": round(t_flops / (kt_us * 1e-6) / 1e12 / (PEAK_FP64_TFLOPS / 2), 4),
+    }
+    log("topk_decode %s" % res["topk_decode"])
     # long-context pipeline
     w = W["long_context"]
     log("generating long_context inputs")

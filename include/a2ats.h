@@ -333,6 +333,30 @@ int a2ats_kmeans(const void* x, int x_dtype, int64_t heads, int64_t n, int64_t d
                  size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Approximate attention-score top-K over codes -- the A2ATS paper page ("Abstract (arXiv)")
+ * retrieves the tokens with the top-K attention scores approximated from the quantised keys.
+ * With far keys unrotated, the far logit of token t is (q R_b) . c_{code_t} ("A2ATS-adapted"
+ * docs, "paper fidelity" section, Eq. 11-12), so one table of C values per query, gathered by
+ * code, scores every token.
+ *
+ * topk_codes: for every sequence b and query head h (key/value head h / (hq / hkv)):
+ *   lut_j     = fp32( sum_a qb[b, h, a] * codebook[kvh, j, a] ), the products formed in fp64
+ *               and added in dimension order, rounded to fp32 once
+ *   score_t   = lut[codes[b, kvh, t]], or -inf for a code >= c
+ *   idx[b, h] = the k tokens with the largest scores (equal scores: lower index first; -0 and
+ *               +0 are equal), in ascending index order; score[b, h] (optional) their scores
+ *   qb        [batch, hq, d] fp32 or bf16 (q_dtype): the query already rotated by R_b
+ *               (a2ats_far_query_rope)
+ *   codes     [batch, hkv, n] uint16; codebook [hkv, c, d] fp32, 1 <= c <= 4096, d = 128
+ *   idx       [batch, hq, k] int32; score [batch, hq, k] fp32 or NULL; 0 <= k <= n
+ * hq must be a multiple of hkv.  Nothing is written when n or k is 0.  No workspace; one
+ * workgroup reads the codes and the codebook once for up to four query heads of a group.
+ */
+int a2ats_topk_codes(const void* qb, int q_dtype, int64_t batch, int64_t hq, int64_t hkv,
+                     int64_t d, const uint16_t* codes, int64_t n, const float* codebook,
+                     int64_t c, int64_t k, int32_t* idx, float* score, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Kernel timing (diagnostics).  While enabled, every kernel the library launches is
  * bracketed by HIP events recorded on its stream.  a2ats_profile_read waits for those
  * events and writes one line per kernel name, "name<TAB>launches<TAB>total_ms\n", into

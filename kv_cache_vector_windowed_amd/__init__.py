@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         L.a2ats_kmeans_workspace.argtypes = [i64, i64, i64, i64]
         L.a2ats_kmeans_workspace.restype = sz
         L.a2ats_kmeans.argtypes = [p, i32, i64, i64, i64, i64, p, i32, p, p, p, sz, p]
+        L.a2ats_topk_codes.argtypes = [p, i32, i64, i64, i64, i64, p, i64, p, i64, i64, p, p, p]
         L.a2ats_profile_enable.argtypes, L.a2ats_profile_enable.restype = [i32], i32
         L.a2ats_profile_reset.argtypes, L.a2ats_profile_reset.restype = [], i32
         L.a2ats_profile_read.argtypes, L.a2ats_profile_read.restype = [ctypes.c_char_p, sz], i64
@@ -83,7 +84,7 @@ def lib() -> ctypes.CDLL:
                   "a2ats_assign_cosine",
                   "a2ats_select_retrieval", "a2ats_reconstruct", "a2ats_reconstruct_update",
                   "a2ats_far_query_rope", "a2ats_pq_encode", "a2ats_pq_reconstruct",
-                  "a2ats_kmeans_update", "a2ats_kmeans"):
+                  "a2ats_kmeans_update", "a2ats_kmeans", "a2ats_topk_codes"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -456,6 +457,31 @@ def kmeans(x: torch.Tensor, codebook: torch.Tensor, chol: torch.Tensor | None = 
                               _ptr(codebook), _ptr(codes), _ptr(ws), ws.numel(), _stream(x.device)),
            "kmeans")
     return codebook, codes
+
+
+def topk_codes(qb: torch.Tensor, codes: torch.Tensor, codebook: torch.Tensor, k: int,
+               want_scores: bool = True):
+    """Top-k tokens by the approximate score (q R_b) . c_code.  qb [batch, hq, d] (fp32/bf16,
+    already rotated by far_query_rope), codes [batch, hkv, n] uint16, codebook [hkv, c, d]
+    fp32 -> idx [batch, hq, k] int32 ascending (and scores [batch, hq, k] fp32)."""
+    _dev(qb, "qb")
+    _dev(codes, "codes")
+    _dev(codebook, "codebook")
+    if qb.dim() != 3 or codes.dim() != 3 or codebook.dim() != 3:
+        raise ValueError("qb [batch, hq, d], codes [batch, hkv, n], codebook [hkv, c, d]")
+    if codes.dtype != torch.uint16 or codebook.dtype != torch.float32:
+        raise ValueError("codes must be uint16 and codebook fp32")
+    batch, hq, d = qb.shape
+    _, hkv, n = codes.shape
+    c = codebook.shape[1]
+    if codes.shape[0] != batch or codebook.shape[0] != hkv or codebook.shape[2] != d:
+        raise ValueError("qb, codes and codebook shapes disagree")
+    idx = torch.empty((batch, hq, k), dtype=torch.int32, device=qb.device)
+    sc = torch.empty((batch, hq, k), dtype=torch.float32, device=qb.device) if want_scores else None
+    _check(lib().a2ats_topk_codes(_ptr(qb), _dtype_code(qb), batch, hq, hkv, d, _ptr(codes), n,
+                                  _ptr(codebook), c, int(k), _ptr(idx), _ptr(sc),
+                                  _stream(qb.device)), "topk_codes")
+    return (idx, sc) if want_scores else idx
 
 
 # ----------------------------------------------------------------- kernel timing

@@ -138,6 +138,7 @@ class Workload:
     rope_base: float = 10000.0
     dist: bool = False
     d: int = D
+    q_heads: int = 0         # query heads per sequence sharing the key heads (0: heads)
 
 
 WORKLOADS = {
@@ -156,6 +157,10 @@ WORKLOADS = {
     # Long-context pipeline: 8 x 131072 bf16, 5% retrieval split, C = 2048, W = 1024.
     "long_context": Workload("long_context", 4, 8, 131072, 2048, "bf16", m=4096, window=1024,
                              cur_pos=131071, fraction=0.05),
+    # Top-K retrieval over codes on the decode shape: 32 sequences x 24 query heads over 8 key
+    # heads (Llama-3.2-3B grouping) x 16384 codes uniform over C = 1024; k = 10% of the tokens.
+    "topk_decode": Workload("topk_decode", 2, 8, 16384, 1024, "f32", fraction=0.1, batch=32,
+                            q_heads=24),
     # The pages' default configuration on the layer shape: sub-vector codes (sub_dim 8, one
     # shared codebook of 2^8 entries), W = 128, retrieval fraction 0.2, beta 0.5; keys and
     # values, 8 heads x 32768 bf16 tokens.  c is the codebook size k.

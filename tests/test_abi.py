@@ -279,6 +279,25 @@ def test_kmeans_validation(L):
     assert km(n=0) == 0
 
 
+def test_topk_codes_validation(L):
+    def call(qdt=0, batch=2, hq=6, hkv=2, d=128, n=64, c=16, k=8, qb=FAKE, idx=FAKE):
+        return L.a2ats_topk_codes(qb, qdt, batch, hq, hkv, d, FAKE, n, FAKE, c, k, idx, None,
+                                  None)
+
+    assert call(qdt=2) == EDTYPE
+    assert call(d=64) == EINVAL
+    assert call(hq=5) == EINVAL          # hq not a multiple of hkv
+    assert call(batch=0) == EINVAL
+    assert call(c=0) == EINVAL
+    assert call(c=4097) == EINVAL
+    assert call(k=65) == EINVAL          # k > n
+    assert call(k=-1) == EINVAL
+    assert call(qb=None) == EINVAL
+    assert call(idx=None) == EINVAL
+    assert call(k=0) == 0                # nothing to select: no launch
+    assert call(n=0, k=0) == 0
+
+
 def test_calibrate_validation(L):
     need = L.a2ats_calibrate_workspace(2, 100, 128)
     assert need > 0 and L.a2ats_calibrate_workspace(2, 100, 129) == 0

@@ -753,3 +753,93 @@ class TestPipeline:
             got = synth.bf16_bits_to_f32(bf16_to_np_bits(out[0, h, torch.from_numpy(t).to(DEV)]))
             ref = oracle_rows(codes_np[h][t], t.astype(np.int32), cb[h], w.cur_pos, w.window, w.far_b, 0)
             check_rotation(got, ref, cb[h][codes_np[h][t]].astype(np.float64), "bf16", name)
+
+
+# --------------------------------------------------------------------------- top-K over codes
+def topk_case(qb, codes, cb, k, qdt="f32"):
+    """GPU top-K of qb [batch, hq, 128] fp32 (on the bf16 grid when qdt is bf16) against the
+    oracle row by row: indices bit-exact, scores bit-exact (as values: -0 == +0)."""
+    batch, hq, _ = qb.shape
+    hkv = codes.shape[1]
+    qd = torch.from_numpy(np.ascontiguousarray(qb)).to(DEV)
+    if qdt == "bf16":
+        qd = qd.to(torch.bfloat16)  # exact: qb is already on the bf16 grid
+    idx, sc = kv.topk_codes(qd, u16_to_dev(codes), f32_to_dev(cb), k)
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy().astype(np.float64)
+    g = hq // hkv
+    for b in range(batch):
+        for h in range(hq):
+            ri, rs = oracle.topk_codes(qb[b, h].astype(np.float64), codes[b, h // g], cb[h // g], k)
+            assert np.array_equal(idx[b, h], ri), (b, h, np.flatnonzero(idx[b, h] != ri)[:5])
+            assert np.array_equal(sc[b, h], rs), (b, h)
+    return idx, sc
+
+
+def bf16_grid(x):
+    return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(np.asarray(x, np.float32)))
+
+
+class TestTopkCodes:
+    # (batch, hq, hkv, n, c, k): every group size the kernel templates on (1..4), groups split
+    # over workgroups (8 = 4 + 4, 5 = 4 + 1 partial), ragged token counts, partial codebook
+    # tiles, several tiles (c = 4096), and rows too long for LDS (n > 32768)
+    @pytest.mark.parametrize("batch,hq,hkv,n,c,k", [
+        (2, 6, 2, 3000, 256, 300), (1, 3, 3, 1000, 1000, 1), (3, 4, 2, 4097, 1024, 4097),
+        (1, 8, 2, 5000, 300, 777), (2, 4, 1, 2048, 4096, 1500), (1, 5, 1, 999, 64, 100),
+        (1, 2, 1, 40000, 1024, 4000), (1, 1, 1, 1, 1, 1), (2, 2, 2, 65, 7, 64)])
+    @pytest.mark.parametrize("qdt", ["f32", "bf16"])
+    def test_matches_oracle(self, batch, hq, hkv, n, c, k, qdt):
+        rng = np.random.default_rng(batch * 1000 + hq * 100 + n + c)
+        cb = (rng.standard_normal((hkv, c, 128)) * 2).astype(np.float32)
+        codes = rng.integers(0, c, (batch, hkv, n)).astype(np.uint16)
+        qb = rng.standard_normal((batch, hq, 128)).astype(np.float32)
+        if qdt == "bf16":
+            qb = bf16_grid(qb)
+        topk_case(qb, codes, cb, k, qdt)
+
+    @pytest.mark.parametrize("k", [1, 37, 500, 1999, 2000])
+    def test_ties_invalid_codes_and_signed_zero(self, k):
+        # a codebook of four values (one repeated) over 2000 tokens: the cut falls inside runs
+        # of equal scores; codes >= c score -inf; a zero query ties every valid token at 0
+        rng = np.random.default_rng(k)
+        base = rng.standard_normal((3, 128)).astype(np.float32)
+        cb = np.stack([base[0], base[1], base[0], base[2]])[None]  # entries 0 and 2 equal
+        codes = rng.integers(0, 6, (1, 1, 2000)).astype(np.uint16)  # 4, 5 are invalid
+        qb = np.stack([rng.standard_normal(128), np.zeros(128), -np.zeros(128)])[None]
+        qb = qb.astype(np.float32)
+        idx, sc = topk_case(qb, codes, cb, k)
+        # the zero queries take the lowest-indexed valid tokens, then invalid ones at -inf
+        valid = np.flatnonzero(codes[0, 0] < 4)
+        want = np.sort(np.concatenate([valid, np.flatnonzero(codes[0, 0] >= 4)])[:k])
+        assert np.array_equal(idx[0, 1], want) and np.array_equal(idx[0, 2], want)
+
+    def test_decode_shape(self):
+        # 32 sequences x 24 query heads over 8 key heads, 16384 uniform codes, C = 1024,
+        # k = 10%: every row checked (qb = oracle's q R_b rounded to fp32)
+        w = W["topk_decode"]
+        cb = synth.codebook(w.cfg, w.heads, w.c)
+        codes = synth.uniform_codes(w.cfg, (w.batch, w.heads, w.n), w.c)
+        q = synth.queries(w.cfg, w.q_heads, w.batch).transpose(1, 0, 2)
+        qb = oracle.rope_at(q.reshape(-1, 128).astype(np.float64), w.far_b)
+        qb = qb.astype(np.float32).reshape(q.shape)
+        topk_case(qb, codes, cb, int(np.ceil(w.fraction * w.n)))
+
+    def test_after_far_query_rope(self):
+        # the composed decode path: GPU far rotation of the raw query, then top-K; the
+        # oracle's rotation agrees to one fp32 unit, so the picked sets agree up to near-ties
+        w = W["topk_decode"]
+        batch, n, c, k = 4, 4096, w.c, 400
+        cb = synth.codebook(w.cfg, w.heads, c)
+        codes = synth.uniform_codes(w.cfg, (batch, w.heads, n), c)
+        q = np.ascontiguousarray(synth.queries(w.cfg, w.q_heads, batch).transpose(1, 0, 2))
+        qb = kv.far_query_rope(torch.from_numpy(q).to(DEV), w.far_b)
+        idx = kv.topk_codes(qb, u16_to_dev(codes), f32_to_dev(cb), k, want_scores=False).cpu().numpy()
+        qr = oracle.rope_at(q.reshape(-1, 128).astype(np.float64), w.far_b).reshape(q.shape)
+        g = w.q_heads // w.heads
+        for b in range(batch):
+            for h in range(w.q_heads):
+                s = cb[h // g].astype(np.float64)[codes[b, h // g]] @ qr[b, h]
+                kth = np.sort(s)[::-1][k - 1]
+                slack = 1e-5 * np.abs(cb[h // g]).sum(1).max() * np.abs(qr[b, h]).max()
+                assert np.all(s[idx[b, h]] >= kth - slack)
+                assert np.all(np.diff(idx[b, h]) > 0)
