@@ -338,41 +338,43 @@ __global__ __launch_bounds__(kTkThreads) void topk_codes_rows(
     eq_take[g] = et < 0 ? 0 : (et > mine ? mine : et);
     eq_seen[g] = 0;
   }
+  auto below = [](unsigned long long m) {  // set bits of m in the lanes below this one
+    return (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+  };
+  const unsigned ku = (unsigned)k;
   for (int64_t base = w0; base < w1; base += 256) {
     unsigned cc[4], v[4];
     step(base, cc, v);
+    const unsigned vor = v[0] | v[1] | v[2] | v[3];
 #pragma unroll
     for (int g = 0; g < GN; ++g) {
       if (g >= gv) break;
-      bool take[4], eq[4];
-      bool any_eq = false;
+      bool take[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        take[e] = (v[e] >> (2 * g)) & 1u;
-        eq[e] = (v[e] >> (2 * g + 1)) & 1u;
-        any_eq |= eq[e];
-      }
-      if (__ballot(any_eq)) {  // tokens at T_g: the first eq_take of this wave's range
+      for (int e = 0; e < 4; ++e) take[e] = (v[e] >> (2 * g)) & 1u;
+      if (__ballot((vor >> (2 * g + 1)) & 1u)) {  // tokens at T_g: the first eq_take of the range
         int seen = eq_seen[g];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const unsigned long long m = __ballot(eq[e]);
-          take[e] = take[e] || (eq[e] && seen + __popcll(m & lt) < eq_take[g]);
+          const bool eq = (v[e] >> (2 * g + 1)) & 1u;
+          const unsigned long long m = __ballot(eq);
+          take[e] = take[e] || (eq && seen + below(m) < eq_take[g]);
           seen += __popcll(m);
         }
         eq_seen[g] = seen;
       }
       int32_t* orow = idx + (row0 + g) * k;
       float* srow = score ? score + (row0 + g) * k : nullptr;
-      float sv[4];
+      float sv[4];  // read ahead: one LDS wait for the four stores
 #pragma unroll
       for (int e = 0; e < 4; ++e) sv[e] = lut[g][cc[e]];
       int o = out[g];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const unsigned long long m = __ballot(take[e]);
-        const int pos = o + __popcll(m & lt);
-        if (take[e] && pos < k) {  // the bound turns any inconsistency into a wrong answer
+        const unsigned pos = (unsigned)(o + below(m));
+        if (take[e] && pos < ku) {  // the bound turns any inconsistency into a wrong answer
           orow[pos] = (int32_t)(base + 64 * e + lane);
           if (srow) srow[pos] = sv[e];
         }

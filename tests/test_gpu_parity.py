@@ -644,6 +644,27 @@ class TestKmeans:
                 assert np.all(np.abs(out[h] - ref32) <= f32_ulp(ref32))
             assert np.array_equal(out[h, 7], cb[h, 7])
 
+    def test_update_layer_shape(self):
+        # the codebook-training update at the layer workload's size (8 heads x 32768 bf16
+        # keys, k = 1024 per head; uniform codes: ~32 members a cluster, so every sum runs in
+        # ascending row order and the result is bitwise the oracle's), plus a large cluster
+        # (more than 256 members: segmented sums, within one fp32 unit)
+        w = W["layer"]
+        keys = synth.keys(w.cfg, w.heads, w.n, "bf16")
+        codes = synth.uniform_codes(w.cfg, (w.heads, w.n), w.c).astype(np.int64)
+        codes[:, :4000] = 5  # cluster 5: 4000+ members in every head
+        cb = synth.codebook(w.cfg, w.heads, w.c)
+        out, cnt = kv.kmeans_update(keys_to_dev(keys), torch.from_numpy(codes.astype(np.uint16)).to(DEV),
+                                    f32_to_dev(cb), want_counts=True)
+        out, cnt = out.cpu().numpy(), cnt.cpu().numpy()
+        for h in range(w.heads):
+            ref, rc = oracle.kmeans_update(keys.values[h], codes[h], cb[h])
+            assert np.array_equal(cnt[h], rc)
+            ref32 = ref.astype(np.float32)
+            small = rc <= 256
+            assert np.array_equal(out[h][small], ref32[small])
+            assert np.all(np.abs(out[h] - ref32) <= f32_ulp(ref32))
+
     def test_update_is_deterministic(self):
         keys = synth.keys(70, 2, 5000, "bf16")
         xd = keys_to_dev(keys)
