@@ -163,11 +163,15 @@ int a2ats_encode_prepared(const void* keys, int keys_dtype, int64_t heads, int64
  *   query     [heads, nq, d]  same dtype as x; nq == 1 (one query per head) or nq == n
  *   codebook  [heads, c, d]   fp32
  *   codes     [heads, n]      uint16 output
- * Requires 1 <= d <= 256 and 1 <= c <= 65536, beta in [0, 1].  No workspace.
+ * Requires 1 <= d <= 256 and 1 <= c <= 65536, beta in [0, 1].  Workspace:
+ * a2ats_assign_cosine_workspace(heads, n, c) bytes (per-centroid errors and cosine numerators
+ * of a batch of rows, at most 128 MiB; larger inputs run in several batches).
  */
+size_t a2ats_assign_cosine_workspace(int64_t heads, int64_t n, int64_t c);
 int a2ats_assign_cosine(const void* x, int x_dtype, int64_t heads, int64_t n, int64_t d,
                         const void* query, int64_t nq, const float* codebook, int64_t c,
-                        double beta, uint16_t* codes, void* stream);
+                        double beta, uint16_t* codes, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * select_retrieval -- "veloxquant_mlx.quantizers.a2ats module", a2ats_select_retrieval_set:

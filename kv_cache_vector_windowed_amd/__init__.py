@@ -54,7 +54,9 @@ def lib() -> ctypes.CDLL:
         L.a2ats_encode.argtypes = [p, i32, i64, i64, i64, p, i64, p, i64, p, p, p, p, p, sz, p]
         L.a2ats_encode_prepare.argtypes = [p, i64, p, i64, i64, i64, p, sz, p]
         L.a2ats_encode_prepared.argtypes = [p, i32, i64, i64, i64, p, i64, i64, p, p, p, p, p, sz, p]
-        L.a2ats_assign_cosine.argtypes = [p, i32, i64, i64, i64, p, i64, p, i64, dbl, p, p]
+        L.a2ats_assign_cosine_workspace.argtypes = [i64, i64, i64]
+        L.a2ats_assign_cosine_workspace.restype = sz
+        L.a2ats_assign_cosine.argtypes = [p, i32, i64, i64, i64, p, i64, p, i64, dbl, p, p, sz, p]
         L.a2ats_select_retrieval_workspace.argtypes = [i64, i64]
         L.a2ats_select_retrieval_workspace.restype = sz
         L.a2ats_select_retrieval.argtypes = [p, i32, i64, i64, i64, p, dbl, p, p, p, sz, p]
@@ -254,9 +256,11 @@ def assign_cosine(x: torch.Tensor, query: torch.Tensor, codebook: torch.Tensor, 
     if query.dtype != x.dtype or query.dim() != 3 or query.shape[0] != heads:
         raise ValueError("query must be [heads, nq, d] in the dtype of x")
     codes = torch.zeros((heads, n), dtype=torch.uint16, device=x.device)
+    ws = _workspace(lib().a2ats_assign_cosine_workspace(heads, n, codebook.shape[1]), x.device)
     _check(lib().a2ats_assign_cosine(_ptr(x), _dtype_code(x), heads, n, d, _ptr(query),
                                      query.shape[1], _ptr(codebook), codebook.shape[1],
-                                     float(beta), _ptr(codes), _stream(x.device)), "assign_cosine")
+                                     float(beta), _ptr(codes), _ptr(ws), ws.numel(),
+                                     _stream(x.device)), "assign_cosine")
     return codes
 
 

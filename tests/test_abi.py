@@ -123,8 +123,16 @@ def test_encode_prepare_validation(L):
 
 
 def test_assign_cosine_validation(L):
-    def call(dt=0, heads=1, n=4, d=128, nq=1, c=8, beta=0.5, x=FAKE):
-        return L.a2ats_assign_cosine(x, dt, heads, n, d, FAKE, nq, FAKE, c, beta, FAKE, None)
+    def call(dt=0, heads=1, n=4, d=128, nq=1, c=8, beta=0.5, x=FAKE, ws=FAKE, wsb=1 << 30):
+        return L.a2ats_assign_cosine(x, dt, heads, n, d, FAKE, nq, FAKE, c, beta, FAKE, ws, wsb,
+                                     None)
+
+    need = L.a2ats_assign_cosine_workspace(1, 4, 8)
+    assert need >= 2 * 4 * 8 * 8
+    # a large input is batched: the workspace stays bounded
+    assert L.a2ats_assign_cosine_workspace(8, 32768, 1024) <= 2 * (64 << 20) + 4096
+    assert call(ws=None, wsb=0) == EWORKSPACE
+    assert call(wsb=need - 1) == EWORKSPACE
 
     assert call(dt=3) == EDTYPE
     for beta in (-0.01, 1.01, math.nan):
