@@ -257,11 +257,11 @@ def pmc_summarize(fetch_dir, write_dir):
     # bf16 keys, fp16 codebook fragments, fp32 bias, int32 row indices, uint16 codes
     algorithmic = 8 * n_bulk * (128 * 2 + 4 + 2) + 8 * 1024 * (128 * 2 + 4)
     cmd = ["cd /tmp && export TMPDIR=/tmp",
-           "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/gpurun_out/pmc_fetch -o p -- "
-           "python <repo>/bench.py --pmc-probe",
-           "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/gpurun_out/pmc_write -o p -- "
-           "python <repo>/bench.py --pmc-probe",
-           "python bench.py --pmc-summarize gpurun_out/pmc_fetch gpurun_out/pmc_write"]
+           "rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o p -- "
+           "python <repo>/bench.py --pmc-probe" % fetch_dir,
+           "rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o p -- "
+           "python <repo>/bench.py --pmc-probe" % write_dir,
+           "python bench.py --pmc-summarize %s %s" % (fetch_dir, write_dir)]
     d = {"kernel": "encode_coarse_plain", "workload": "layer", "source": COARSE_SOURCE,
          "source_sha": sha_of(os.path.join(ROOT, COARSE_SOURCE)),
          "hbm_bytes_per_launch": round(total), "algorithmic_bytes_per_launch": algorithmic,

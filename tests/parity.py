@@ -1,6 +1,6 @@
 """Helpers shared by the GPU parity tests: device transfer and the comparison rules.
 
-Comparison rules (the oracle is fp64; see the design doc for the derivations):
+Comparison rules (the oracle is fp64; each bound covers the GPU path's own rounding):
   codes      bit-exact wherever the oracle's (d2 - d1) / d1 > 1e-5; the rest is the tie band
   distances  |gpu - d1| <= 1e-4 d1 + 1e-6 ||z||^2
   blend      bit-exact wherever the oracle's best-minus-second score > 1e-5

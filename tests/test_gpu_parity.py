@@ -198,6 +198,29 @@ class TestAssignCosine:
             bad = (s1 - s2 > 1e-5) & (out[h] != code)
             assert not bad.any()
 
+    @pytest.mark.parametrize("heads,n,d,c,nq,dtype", [
+        (3, 7, 100, 300, "n", "f32"),     # partial slices, row blocks and centroid tiles
+        (2, 33, 8, 9, "1", "bf16"),       # one short slice, tiny codebook
+        (1, 2, 256, 1, "n", "f32"),       # the largest d, a single centroid
+        (1, 100, 8, 65536, "1", "f32")])  # several workspace batches
+    def test_shapes_and_batches(self, heads, n, d, c, nq, dtype):
+        rng = np.random.default_rng(heads * 7 + n + d + c)
+        x = rng.standard_normal((heads, n, d)).astype(np.float32)
+        q = rng.standard_normal((heads, n if nq == "n" else 1, d)).astype(np.float32)
+        if dtype == "bf16":
+            x, q = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(x)), synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(q))
+        cb = rng.standard_normal((heads, c, d)).astype(np.float32)
+        xd, qd = torch.from_numpy(x).to(DEV), torch.from_numpy(q).to(DEV)
+        if dtype == "bf16":
+            xd, qd = xd.to(torch.bfloat16), qd.to(torch.bfloat16)  # exact: on the bf16 grid
+        if c == 65536:
+            assert kv.lib().a2ats_assign_cosine_workspace(heads, n, c) < 2 * heads * n * c * 8
+        out = u16_to_np(kv.assign_cosine(xd, qd, f32_to_dev(cb), 0.6))
+        for h in range(heads):
+            code, s1, s2 = oracle.assign_cosine(x[h], q[h] if nq == "n" else q[h, 0], cb[h], 0.6)
+            bad = (s1 - s2 > 1e-5) & (out[h] != code)
+            assert not bad.any(), (h, np.nonzero(bad)[0][:5])
+
     def test_bf16_rows_and_beta_one_matches_plain_encode(self):
         k = synth.keys(130, 2, 150, "bf16")
         cb = synth.codebook(130, 2, 70)
