@@ -105,6 +105,7 @@ def main():
     prep_h = kv.encode_prepare(cbd, L, w.n)
 
     def step():
+        main_s = torch.cuda.current_stream(dev)  # the capturing stream inside a graph capture
         aux.wait_event(main_s.record_event())
         with torch.cuda.stream(aux):
             prep_plain.prepare(cbd, None)
@@ -146,10 +147,38 @@ def main():
         step()
     e1.record()
     torch.cuda.synchronize()
+    ms_eager = e0.elapsed_time(e1) / args.steps
+    log("layer step, launched one by one: %.4f ms" % ms_eager)
+    # The same step captured once in a HIP graph (the launches of both streams, replayed as
+    # one): the timed steps are K replays.  A replay must reproduce the eager step's codes
+    # and keys bit for bit.
+    ref_codes, ref_out = codes.clone(), out.view(torch.int16).clone()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(main_s)
+    with torch.cuda.stream(side):
+        step()
+    main_s.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    codes.fill_(0)
+    graph.replay()
+    torch.cuda.synchronize()
+    if not (torch.equal(codes, ref_codes) and torch.equal(out.view(torch.int16), ref_out)):
+        raise SystemExit("graph replay differs from the eager step")
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     keys_per_step = w.heads * w.n
     value = keys_per_step / (ms * 1e-3)
-    log("layer step %.4f ms -> %.4g keys/s" % (ms, value))
+    log("layer step %.4f ms (graph replay) -> %.4g keys/s" % (ms, value))
 
     # per-kernel durations: same step, same launches, with HIP events around every kernel
     def profile(fn, reps):
@@ -185,7 +214,8 @@ def main():
     kv.calibrate(qd, 1e-4)
     calib_ms = (time.perf_counter() - t0) * 1e3
 
-    extra = {"layer_kernels_us": {k: round(v[1] * 1e3, 2) for k, v in prof.items()},
+    extra = {"layer_step_ms_eager": round(ms_eager, 5),
+             "layer_kernels_us": {k: round(v[1] * 1e3, 2) for k, v in prof.items()},
              "layer_calibrate_ms_host_clock": round(calib_ms, 3)}
     if not args.no_extra:
         extra.update(extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile))

@@ -768,6 +768,60 @@ class TestPipeline:
             assert torch.equal(codes.view(torch.int16), seq.view(torch.int16))
             del pp, ph
 
+    def test_graph_replays_match_eager(self):
+        # the benchmark's step captured in a HIP graph: every replay, with eager work and
+        # synchronisations between replays, gives the eager step's codes and keys bit for bit
+        w = W["layer"]
+        keys = synth.keys(w.cfg, w.heads, w.n, w.key_dtype)
+        kd, cbd = keys_to_dev(keys), f32_to_dev(synth.codebook(w.cfg, w.heads, w.c))
+        H, L = kv.calibrate(f32_to_dev(synth.queries(w.cfg, w.heads, w.m)), 1e-4)
+        proxy = kd[:, -1].contiguous()
+        pos = torch.arange(w.n, dtype=torch.int32, device=DEV)[None]
+        codes = torch.zeros((w.heads, w.n), dtype=torch.uint16, device=DEV)
+        out = torch.empty((1, w.heads, w.n, 128), dtype=torch.bfloat16, device=DEV)
+        aux = torch.cuda.Stream(device=DEV)
+        pp, ph = kv.encode_prepare(cbd, None, w.n), kv.encode_prepare(cbd, L, w.n)
+
+        def step():
+            main = torch.cuda.current_stream(DEV)
+            aux.wait_event(main.record_event())
+            with torch.cuda.stream(aux):
+                pp.prepare(cbd, None)
+                plain_ready = aux.record_event()
+                ph.prepare(cbd, L)
+            ret, bulk = kv.select_retrieval(kd, proxy, w.fraction)
+            split_done = main.record_event()
+            main.wait_event(plain_ready)
+            kv.encode_prepared(kd, pp, idx=bulk, codes=codes)
+            aux.wait_event(split_done)
+            with torch.cuda.stream(aux):
+                kv.encode_prepared(kd, ph, idx=ret, codes=codes)
+            main.wait_event(aux.record_event())
+            kv.reconstruct(codes[None], pos, cbd, w.cur_pos, w.window, out=out)
+
+        step()
+        torch.cuda.synchronize()
+        ref_codes, ref_out = codes.clone(), out.view(torch.int16).clone()
+        side = torch.cuda.Stream(device=DEV)
+        side.wait_stream(torch.cuda.current_stream(DEV))
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream(DEV).wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(4):
+            codes.fill_(7)
+            out.fill_(1.0)
+            step()  # eager work between replays
+            torch.cuda.synchronize()
+            codes.fill_(7)
+            out.fill_(1.0)
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(codes, ref_codes)
+            assert torch.equal(out.view(torch.int16), ref_out)
 
     @pytest.mark.parametrize("name", ["layer", "long_context"])
     def test_split_encode_reconstruct(self, name):
