@@ -39,6 +39,7 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __fp16 h2rtz __attribute__((ext_vector_type(2)));
 
 constexpr int kD = A2ATS_HEAD_DIM;
 constexpr int kLd = kD + 1;               // padded LDS row of L (conflict-free column reads)
@@ -391,53 +392,109 @@ struct KeyFrags {
   bool bad[NB];         // an element outside the fp16 range
 };
 
+// Converts one step (8 elements) of a key to fp16 and accumulates its norm terms.
+__device__ __forceinline__ void key_step(const float (&x)[8], half8& v, float& n2, float& e2,
+                                         bool& bad) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const bool ok = fabsf(x[e]) < 65504.0f;
+    const _Float16 q = ok ? (_Float16)x[e] : (_Float16)0.0f;
+    bad |= !ok;
+    const float d = x[e] - (float)q;  // exact
+    n2 += x[e] * x[e];
+    e2 += d * d;
+    v[e] = q;
+  }
+}
+
+// Every load is issued without a branch before any of them is used (a skipped key reads row 0
+// of its head and is zeroed afterwards): the lane's loads are then in flight together instead
+// of costing one memory round trip each.  bf16 keys: all blocks' loads at once (4 VGPRs per
+// step); f32 keys: one block at a time.
 template <int DT, int NB>
 __device__ __forceinline__ void load_key_frags(const void* keys, int64_t head, int64_t n,
                                                const int64_t* row, int hh, KeyFrags<NB>& kf) {
+  if constexpr (DT == A2ATS_BF16) {
+    // bf16 -> fp16 is exact for 2^-14 <= |x| <= 65280 (and zero); such a key needs none of
+    // key_step's per-element work: two fp16 conversions per instruction (toward zero, exact
+    // here), ||k||^2 from fp16 dot products (the products are exact), and one running
+    // maximum and minimum of the 15-bit magnitudes (two per instruction) to find the rare
+    // key that is not.  Beyond 65280 (bf16's next value is 65536) a key is outside the fp16
+    // range (scanned in fp64 instead); below 2^-14 its fp16 value is |q| <= |x| with
+    // |x - q| < 2^-24, so at most 64 such elements in a lane add less than 64 * 2^-28 to
+    // ||k||^2 and to ||k - k16||^2, the bounds added below.
+    uint4 raw[NB][kSteps];
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const int64_t off = (head * n + (row[blk] >= 0 ? row[blk] : 0)) * kD + 8 * hh;
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s)
+        raw[blk][s] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(keys) + off + 16 * s);
+    }
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const unsigned live = row[blk] >= 0 ? 0xFFFFFFFFu : 0u;
+      float n2 = 0.f;
+      unsigned mx = 0u, mn = 0xFFFFFFFFu;  // per 16-bit half: max |x| bits, min |x| bits - 1
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const unsigned wv[4] = {raw[blk][s].x & live, raw[blk][s].y & live, raw[blk][s].z & live,
+                                raw[blk][s].w & live};
+        unsigned qw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const h2rtz q2 = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(wv[e] << 16),
+                                                       __uint_as_float(wv[e] & 0xFFFF0000u));
+          n2 = __builtin_amdgcn_fdot2(q2, q2, n2, false);
+          qw[e] = __builtin_bit_cast(unsigned, q2);
+          // packed 16-bit integer ops (the same in vector-of-u16 C lets the register allocator
+          // spill around the MFMA loop); m - 1 wraps for a zero, which drops out of the minimum
+          const unsigned m = wv[e] & 0x7FFF7FFFu;
+          unsigned m1;
+          asm("v_pk_sub_u16 %0, %1, 1 op_sel_hi:[1,0]" : "=v"(m1) : "v"(m));
+          asm("v_pk_max_u16 %0, %1, %2" : "=v"(mx) : "v"(mx), "v"(m));
+          asm("v_pk_min_u16 %0, %1, %2" : "=v"(mn) : "v"(mn), "v"(m1));
+        }
+        kf.f[blk][s] = __builtin_bit_cast(half8, (uint4){qw[0], qw[1], qw[2], qw[3]});
+      }
+      const bool tiny = (mn & 0xFFFFu) < 0x387Fu || (mn >> 16) < 0x387Fu;  // 0 < |x| < 2^-14
+      kf.bad[blk] = (mx & 0xFFFFu) > 0x477Fu || (mx >> 16) > 0x477Fu;
+      kf.n2[blk] = tiny ? n2 + 0x1p-22f : n2;
+      kf.e2[blk] = tiny ? 0x1p-22f : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const int64_t off = (head * n + (row[blk] >= 0 ? row[blk] : 0)) * kD + 8 * hh;
+      float4 raw[kSteps][2];
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(keys) + off + 16 * s);
+        raw[s][0] = p[0];
+        raw[s][1] = p[1];
+      }
+      const bool live = row[blk] >= 0;
+      kf.n2[blk] = 0.f;
+      kf.e2[blk] = 0.f;
+      kf.bad[blk] = false;
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const float4 a = raw[s][0], b = raw[s][1];
+        float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = live ? x[e] : 0.f;
+        key_step(x, kf.f[blk][s], kf.n2[blk], kf.e2[blk], kf.bad[blk]);
+      }
+    }
+  }
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
-    kf.n2[blk] = 0.f;
-    kf.e2[blk] = 0.f;
-    kf.bad[blk] = false;
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      float x[8];
-      if (row[blk] >= 0) {
-        const int64_t off = (head * n + row[blk]) * kD + 16 * s + 8 * hh;
-        if (DT == A2ATS_BF16) {
-          const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(keys) + off);
-          const unsigned wv[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[2 * e] = __uint_as_float(wv[e] << 16);
-            x[2 * e + 1] = __uint_as_float(wv[e] & 0xFFFF0000u);
-          }
-        } else {
-          const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(keys) + off);
-          const float4 a = p[0], b = p[1];
-          x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-          x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.f;
-      }
-      half8 v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bool ok = fabsf(x[e]) < 65504.0f;
-        const _Float16 q = ok ? (_Float16)x[e] : (_Float16)0.0f;
-        kf.bad[blk] |= !ok;
-        const float d = x[e] - (float)q;  // exact
-        kf.n2[blk] += x[e] * x[e];
-        kf.e2[blk] += d * d;
-        v[e] = q;
-      }
-      kf.f[blk][s] = v;
-    }
     kf.n2[blk] += __shfl_xor(kf.n2[blk], 32);
     kf.e2[blk] += __shfl_xor(kf.e2[blk], 32);
-    kf.bad[blk] = kf.bad[blk] || __shfl_xor((int)kf.bad[blk], 32);
+    // the shuffle runs in every lane (under a short-circuit it would skip the lanes that
+    // already know, and their partners would read nothing from them)
+    const int partner_bad = __shfl_xor((int)kf.bad[blk], 32);
+    kf.bad[blk] = kf.bad[blk] || partner_bad != 0;
   }
 }
 
@@ -771,21 +828,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, col = lane & 31, hh = lane >> 5;
   const HeadScale hs = hsc[head];
-  {  // rho and nu: maxima over the prep_frag partials of this head
-    float rr = 0.f, nn = 0.f;
-    for (int i = t; i < nwg_b; i += 256) {
-      rr = fmaxf(rr, part_b[(head * nwg_b + i) * 2 + 0]);
-      nn = fmaxf(nn, part_b[(head * nwg_b + i) * 2 + 1]);
-    }
-    for (int o = 32; o > 0; o >>= 1) {
-      rr = fmaxf(rr, __shfl_xor(rr, o));
-      nn = fmaxf(nn, __shfl_xor(nn, o));
-    }
-    if (lane == 0) {
-      s_red[0][wave] = rr;
-      s_red[1][wave] = nn;
-    }
+  // Every prologue load is issued before any result is needed, so they share one memory round
+  // trip: the first partials of rho and nu (clamped rather than skipped: a repeated entry
+  // leaves a maximum unchanged), the rows (a key past the end reads the last entry and is then
+  // dropped), the first codebook stage and the keys.
+  const int ib = t < nwg_b ? t : nwg_b - 1;
+  const float rr0 = part_b[(head * nwg_b + ib) * 2 + 0];
+  const float nn0 = part_b[(head * nwg_b + ib) * 2 + 1];
+  int64_t row[2], sel[2], sc[2];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    sel[blk] = kb * kKeysPerWG + wave * 64 + blk * 32 + col;
+    sc[blk] = sel[blk] < n_sel ? sel[blk] : n_sel - 1;
+    row[blk] = sc[blk];
   }
+  if (idx) {
+    row[0] = (int64_t)idx[head * n_sel + sc[0]];
+    row[1] = (int64_t)idx[head * n_sel + sc[1]];
+  }
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)  // out-of-range index entries are skipped
+    row[blk] = (sel[blk] < n_sel && row[blk] >= 0 && row[blk] < n) ? row[blk] : -1;
   const half8* vh = v16 + head * (int64_t)T * kFragPerTile;
   const float* bh = bias + head * (int64_t)T * 32;
   // stage loader: a stage is kTPS tiles (32 KiB of fragments, 512 B of bias), loaded straight
@@ -805,15 +868,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   load_stage(0, sv0, sb0);
 
-  int64_t row[2];
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    const int64_t sel = kb * kKeysPerWG + wave * 64 + blk * 32 + col;
-    const int64_t r = sel < n_sel ? (idx ? (int64_t)idx[head * n_sel + sel] : sel) : -1;
-    row[blk] = (r >= 0 && r < n) ? r : -1;  // out-of-range index entries are skipped
-  }
   KeyFrags<2> kf;
   load_key_frags<DT, 2>(keys, head, n, row, hh, kf);
+  {  // rho and nu: maxima over the prep_frag partials of this head
+    float rr = fmaxf(0.f, rr0), nn = fmaxf(0.f, nn0);
+    for (int i = t + 256; i < nwg_b; i += 256) {
+      rr = fmaxf(rr, part_b[(head * nwg_b + i) * 2 + 0]);
+      nn = fmaxf(nn, part_b[(head * nwg_b + i) * 2 + 1]);
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      rr = fmaxf(rr, __shfl_xor(rr, o));
+      nn = fmaxf(nn, __shfl_xor(nn, o));
+    }
+    if (lane == 0) {
+      s_red[0][wave] = rr;
+      s_red[1][wave] = nn;
+    }
+  }
 
   // ||k L||^2 from fp16 hi/lo fragments of L^T (bf16 keys are exact in fp16).
   float zn[2] = {0.f, 0.f};
@@ -996,6 +1067,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     if (hh ? kf.bad[1] : kf.bad[0]) {
       outcome = 4;
+      if (ZNORM) z2 = -2.f;  // the fp16 fragments do not hold this key: ||kL||^2 in the scan
     } else if (j0 < c && (double)a0 - s0 - E > (double)t1u + s1 + E) {
       outcome = 1;
       codes[head * n + myrow] = (uint16_t)j0;
@@ -1174,10 +1246,12 @@ __global__ __launch_bounds__(256) void enc_rescan_collect(
 }
 
 // fp64 scan of the whole codebook for one key by one wave (kx: this wave's LDS row of 128).
+// z2f: ||kL||^2 for the distance, -1 for ||k||^2 (no L), -2 for ||kL||^2 computed here in
+// fp64 from chol (a bf16 key outside the fp16 range, whose fp16 fragments do not hold it).
 template <int DT>
 __device__ void full_scan_wave(const void* keys, int64_t n, int64_t c, const double* v64,
-                               const double* b64, int64_t head, int64_t row, float z2f,
-                               uint16_t* codes, float* dist, double* kx, int lane) {
+                               const double* b64, const float* chol, int64_t head, int64_t row,
+                               float z2f, uint16_t* codes, float* dist, double* kx, int lane) {
   const int64_t off = (head * n + row) * kD;
   wave_sync();
   kx[lane] = (double)load_elem(keys, DT, off + lane);
@@ -1203,11 +1277,21 @@ __device__ void full_scan_wave(const void* keys, int64_t n, int64_t c, const dou
       bj = oj;
     }
   }
+  double zl = 0.0;
+  if (dist && z2f < -1.5f) {  // one key per wave: uniform
+    const float* L = chol + head * kD * kD;
+    for (int a = lane; a < kD; a += 64) {
+      double z = 0.0;
+      for (int b = a; b < kD; ++b) z += kx[b] * (double)L[b * kD + a];  // L lower
+      zl += z * z;
+    }
+    for (int o = 32; o > 0; o >>= 1) zl += __shfl_xor(zl, o);
+  }
   if (lane == 0) {
     codes[head * n + row] = (uint16_t)bj;
     if (dist) {
-      double z2 = z2f;
-      if (z2f < 0.f) {
+      double z2 = z2f < -1.5f ? zl : (double)z2f;
+      if (z2f < 0.f && z2f > -1.5f) {
         z2 = 0.0;
         for (int a = 0; a < kD; ++a) z2 += kx[a] * kx[a];
       }
@@ -1228,7 +1312,8 @@ __global__ __launch_bounds__(256) void enc_rescan_decide(
     const double* __restrict__ b64,
     const UncEntry* __restrict__ unc, int64_t unc_cap, const unsigned* __restrict__ cand_n,
     const int32_t* __restrict__ cand, uint16_t* __restrict__ codes, float* __restrict__ dist,
-    FullEntry* __restrict__ full, Counters* __restrict__ cnt, int want_stats) {
+    FullEntry* __restrict__ full, Counters* __restrict__ cnt, int want_stats,
+    const float* __restrict__ chol) {
   const int t = threadIdx.x, lane = t & 63, g = lane & 3, q16 = lane >> 2;
   const HeadSet hsx = all_heads(heads);
   __shared__ int64_t pre[kMaxHeadsLds + 1];
@@ -1243,7 +1328,8 @@ __global__ __launch_bounds__(256) void enc_rescan_decide(
     const UncEntry ue = unc[slot];
     const unsigned nc = cand_n[slot];
     if (nc > (unsigned)kCandCap) {
-      full_scan_wave<DT>(keys, n, c, v64, b64, head, ue.row, ue.z2, codes, dist, kx[t >> 6], lane);
+      full_scan_wave<DT>(keys, n, c, v64, b64, chol, head, ue.row, ue.z2, codes, dist, kx[t >> 6],
+                         lane);
       if (lane == 0) full_scans += 1;
       continue;
     }
@@ -1291,7 +1377,8 @@ __global__ __launch_bounds__(256) void enc_rescan_decide(
   const unsigned nfull = __hip_atomic_load(&cnt->full, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (int64_t e = (int64_t)blockIdx.x * 4 + (t >> 6); e < (int64_t)nfull; e += (int64_t)gridDim.x * 4) {
     const FullEntry fe = full[e];
-    full_scan_wave<DT>(keys, n, c, v64, b64, fe.head, fe.row, fe.z2, codes, dist, kx[t >> 6], lane);
+    full_scan_wave<DT>(keys, n, c, v64, b64, chol, fe.head, fe.row, fe.z2, codes, dist, kx[t >> 6],
+                       lane);
     if (lane == 0) full_scans += 1;
   }
   if (want_stats) {
@@ -1483,7 +1570,7 @@ int encode_run(const void* keys, int64_t heads, int64_t n, const int32_t* idx, i
                    L.cand_n, L.cand));
   A2ATS_TRY(launch("encode_rescan_decide", enc_rescan_decide<DT>, dim3(kDecideWgs), dim3(256), 0, s, keys, n,
                    heads, c, L.v64, L.v32, plain ? 1 : 0, L.b64, L.unc, L.unc_cap, L.cand_n, L.cand, codes, dist, L.full,
-                   cnt, stats ? 1 : 0));
+                   cnt, stats ? 1 : 0, chol));
   if (stats)
     A2ATS_TRY(launch("encode_stats", enc_stats_out, dim3(1), dim3(64), 0, s, cnt, stats));
   return A2ATS_OK;

@@ -135,12 +135,37 @@ class TestEncode:
 
     def test_keys_outside_fp16_range(self):
         keys = synth.keys(122, 1, 200, "f32")
-        keys.values[0, ::7, 3] *= 1e4  # some elements beyond 65504
+        keys.values[0, ::7, 3] *= 1e4  # some elements beyond 65504 (first half of a lane pair)
+        keys.values[0, 2::9, 12] *= 1e4  # and in the second half
         cb = synth.codebook(122, 1, 64) * 1e2
         out, dist = kv.encode(keys_to_dev(keys), f32_to_dev(cb), None, want_dist=True)
         code, d1, d2 = oracle.assign_h(keys.values[0], cb[0], None)
         check_codes(u16_to_np(out)[0], code, d1, d2, "large keys")
         check_dist(dist.cpu().numpy()[0], d1, z2_of(keys.values[0], None), "large keys")
+
+    @pytest.mark.parametrize("use_h", [False, True])
+    def test_bf16_keys_outside_fp16_normal_range(self, use_h):
+        # bf16 elements beyond fp16's range, below its normal range (down to bf16's own
+        # subnormals) and exact zeros, spread over several 32-key blocks and both lane halves
+        w = synth.Workload("bf16edge", 123, 2, 700, 96, "bf16", m=300)
+        vals = synth.keys(w.cfg, w.heads, w.n, "f32").values.astype(np.float32)
+        vals[:, ::11, 5] *= 1e5          # beyond 65504
+        vals[:, 3::13, 70] *= 1e-6       # below 2^-14
+        vals[:, 5::17, 100] = 3e-39      # bf16 subnormal
+        vals[:, 7::19, :] *= 1e-7        # whole keys below 2^-14
+        vals[:, 9::23, 64:] = 0.0        # zero halves
+        vals[:, 1::29, 2] = -vals[:, 1::29, 2] * 1e-6
+        bits = synth.f32_to_bf16_bits(vals)
+        keys = synth.Keys(synth.bf16_bits_to_f32(bits), "bf16", bits)
+        cb = synth.codebook(w.cfg, w.heads, w.c)
+        L = oracle_L(w.cfg, w.heads, w.m) if use_h else None
+        out, dist = kv.encode(keys_to_dev(keys), f32_to_dev(cb),
+                              f32_to_dev(L) if use_h else None, want_dist=True)
+        out, dist = u16_to_np(out), dist.cpu().numpy()
+        for h in range(w.heads):
+            code, d1, d2 = oracle.assign_h(keys.values[h], cb[h], None if L is None else L[h])
+            check_codes(out[h], code, d1, d2, "bf16 edge head %d" % h)
+            check_dist(dist[h], d1, z2_of(keys.values[h], None if L is None else L[h]), "bf16 edge")
 
     @pytest.mark.parametrize("use_h", [False, True])
     def test_prepared_runs_match_one_shot(self, use_h):
