@@ -112,14 +112,24 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
   return s16 | static_cast<uint16_t>(__float_as_uint(f) >> 16);
 }
 
-// Workgroup barrier that orders LDS only: waits for this wave's LDS operations, then
-// s_barrier.  Unlike __syncthreads() it does not wait for outstanding global loads, so a
-// prefetch issued before it stays in flight across the barrier.
 // 16 bytes from global memory straight into LDS (global_load_lds_dwordx4): the LDS address
-// is the wave-uniform ldst plus 16 x the lane index.  Completion is counted by vmcnt.
-__device__ __forceinline__ void lds_dma16(const void* gsrc, void* ldst) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
-                                   (__attribute__((address_space(3))) void*)ldst, 16, 0, 0);
+// is the wave-uniform lds (in M0) plus 16 x the lane index.  Completion is counted by vmcnt.
+// Written as inline assembly rather than the compiler builtin: while a builtin copy is in
+// flight the compiler waits for all outstanding LDS reads (lgkmcnt(0)) before using any of
+// them, which exposes the full LDS latency at every use in a loop that streams the next
+// stage while reading the current one.  The compiler does not track this copy: the caller
+// reads the destination only after lds_dma_barrier() (vmcnt(0)), and the "memory" clobber
+// keeps the compiler from moving LDS accesses across it.
+// `lds` is an LDS byte offset (lds_offset()), equal in every lane.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, unsigned lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// LDS byte offset of a __shared__ object (a constant for a named array).
+__device__ __forceinline__ unsigned lds_offset(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 // Barrier after this wave's LDS loads (direct and DS) have completed.
@@ -127,6 +137,9 @@ __device__ __forceinline__ void lds_dma_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations, then
+// s_barrier.  Unlike __syncthreads() it does not wait for outstanding global loads, so a
+// prefetch issued before it stays in flight across the barrier.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }

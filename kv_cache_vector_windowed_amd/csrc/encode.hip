@@ -857,16 +857,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // stage s is computed: its loads go out at the start of stage s, right after the barrier
   // that freed its buffer, so no load is in flight across the loop's back edge.
   const int nst = (T + kTPS - 1) / kTPS;
-  auto load_stage = [&](int st, half8 (&svb)[kTPS][kFragPerTile], float (&sbb)[kTPS][32]) {
+  const unsigned lds_sv[2] = {lds_offset(&sv0[0][0]), lds_offset(&sv1[0][0])};
+  const unsigned lds_sb[2] = {lds_offset(&sb0[0][0]), lds_offset(&sb1[0][0])};
+  auto load_stage = [&](int st, int buf) {
     const half8* src = vh + (int64_t)st * kTPS * kFragPerTile;
+    const unsigned dst = lds_sv[buf] + (unsigned)(wave * 64 * sizeof(half8));
 #pragma unroll
     for (int q = 0; q < kTPS; ++q) {
-      lds_dma16(src + q * kFragPerTile + t, &svb[q][wave * 64]);
-      lds_dma16(src + q * kFragPerTile + 256 + t, &svb[q][256 + wave * 64]);
+      lds_dma16(src + q * kFragPerTile + t, dst + q * kFragPerTile * sizeof(half8));
+      lds_dma16(src + q * kFragPerTile + 256 + t, dst + (q * kFragPerTile + 256) * sizeof(half8));
     }
-    if (t < 8 * kTPS) lds_dma16(bh + (int64_t)st * kTPS * 32 + t * 4, &sbb[0][0]);
+    if (t < 8 * kTPS) lds_dma16(bh + (int64_t)st * kTPS * 32 + t * 4, lds_sb[buf]);
   };
-  load_stage(0, sv0, sb0);
+  load_stage(0, 0);
 
   KeyFrags<2> kf;
   load_key_frags<DT, 2>(keys, head, n, row, hh, kf);
@@ -967,14 +970,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   f16v x0, x1, y0, y1;
 #pragma unroll
   for (int r = 0; r < 16; ++r) y0[r] = y1[r] = kPadBias;
-  auto stage = [&](int st, half8 (&svb)[kTPS][kFragPerTile], float (&sbb)[kTPS][32],
-                   half8 (&svn)[kTPS][kFragPerTile], float (&sbn)[kTPS][32]) {
+  auto stage = [&](int st, half8 (&svb)[kTPS][kFragPerTile], float (&sbb)[kTPS][32], int nbuf) {
     const int base = st * kTPS;
     half8 fr[kStageSteps];
 #pragma unroll
     for (int g = 0; g < kAhead; ++g) fr[g] = svb[g / kSteps][(g % kSteps) * 64 + lane];
     f16v bv = load_bias(sbb, 0);
-    if (st + 1 < nst) load_stage(st + 1, svn, sbn);
+    if (st + 1 < nst) load_stage(st + 1, nbuf);
 #pragma unroll
     for (int q = 0; q < kTPS; ++q) {
       f16v& a0 = (q & 1) ? y0 : x0;
@@ -1001,8 +1003,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     lds_dma_barrier();  // this wave's loads of stage st+1 landed; this buffer free everywhere
   };
   for (int st = 0; st < nst; st += 2) {
-    stage(st, sv0, sb0, sv1, sb1);
-    if (st + 1 < nst) stage(st + 1, sv1, sb1, sv0, sb0);
+    stage(st, sv0, sb0, 1);
+    if (st + 1 < nst) stage(st + 1, sv1, sb1, 0);
   }
   {
     const unsigned te = vgpr_of((unsigned)(nst * kTPS - 1) << 1);
