@@ -635,24 +635,18 @@ __device__ __forceinline__ double coop_score_g(const void* keys, int64_t off_key
   return s - 0.5 * bj;
 }
 
-template <int DT, typename VT>
-__device__ __forceinline__ double coop_score8(const void* keys, int64_t off_key, const VT* vrow,
-                                              double bj, int g, double* z2) {
-  return coop_score_g<DT, 8, VT>(keys, off_key, vrow, bj, g, z2);
-}
-
-// fp64 rerank of one listed key per 16-lane group (lanes 0-7 score j0, lanes 8-15 j1):
+// fp64 rerank of one listed key per group of 2G lanes (the first G score j0, the next G j1):
 // certified when the better exact score beats re.thr, else handed to the rescan (or, when
 // its list is full, the full scan).  Without L the rows are the fp32 codebook itself (v = c
 // exactly), half the bytes of the fp64 copy.  Returns 1 in the group's first lane when the
 // key was decided here.
-template <int DT>
+template <int DT, int G>
 __device__ __forceinline__ unsigned rerank_group(
     bool live, const RefEntry& re, const void* keys, int64_t n, int64_t c,
     const double* v64, const float* v32, bool plain, const double* b64, uint16_t* codes,
     float* dist, UncEntry* unc, int64_t unc_cap, FullEntry* full, Counters* cnt, int lane) {
-  const int which = (lane >> 3) & 1;  // candidate 0 or 1
-  const int g = lane & 7;
+  const int which = (lane / G) & 1;  // candidate 0 or 1
+  const int g = lane % G;
   const int32_t head = live ? re.head : 0, row = live ? re.row : 0;
   const int32_t ja = live ? re.j0 : -1, jb = live ? re.j1 : -1;
   const int j = which ? jb : ja;
@@ -660,14 +654,14 @@ __device__ __forceinline__ unsigned rerank_group(
   if (j >= 0) {
     const int64_t off = ((int64_t)head * n + row) * kD;
     const int64_t vo = ((int64_t)head * c + j) * kD;
-    s = plain ? coop_score8<DT>(keys, off, v32 + vo, b64[(int64_t)head * c + j], g, &k2)
-              : coop_score8<DT>(keys, off, v64 + vo, b64[(int64_t)head * c + j], g, &k2);
+    s = plain ? coop_score_g<DT, G>(keys, off, v32 + vo, b64[(int64_t)head * c + j], g, &k2)
+              : coop_score_g<DT, G>(keys, off, v64 + vo, b64[(int64_t)head * c + j], g, &k2);
   }
-  const double s_other = __shfl_xor(s, 8);
-  const double k2_other = __shfl_xor(k2, 8);
+  const double s_other = __shfl_xor(s, G);
+  const double k2_other = __shfl_xor(k2, G);
   unsigned decided = 0;
-  if (live && (lane & 15) == 0) {
-    const double sa = s, sb = s_other;  // lane 0 of the group scored ja, lane 8 jb
+  if (live && lane % (2 * G) == 0) {
+    const double sa = s, sb = s_other;  // the group's first lane scored ja, lane G jb
     if (ja < 0) k2 = k2_other;
     int best = ja;
     double sbest = sa;
@@ -1107,7 +1101,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
   // Rerank entries stay in LDS (in the stage buffers, free after the loop) and are settled
-  // here, 4 per wave and pass; full-scan entries (rare) go to the global list.
+  // here, 8 per wave and pass; full-scan entries (rare) go to the global list.
   RefEntry* s_ref = reinterpret_cast<RefEntry*>(&sv0[0][0]);
   static_assert(sizeof(RefEntry) * kKeysPerWG <= sizeof(sv0), "rerank list fits a stage buffer");
   __shared__ unsigned s_cnt, s_base, s_stat[3], s_nref;
@@ -1124,13 +1118,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __syncthreads();
   const unsigned nref = s_nref;
   unsigned reranked = 0;
-  for (unsigned e0 = (unsigned)wave * 4u; e0 < nref; e0 += 16u) {
-    const unsigned e = e0 + (unsigned)(lane >> 4);
+  constexpr int kRrG = 4;                  // lanes per candidate: 8 keys per wave and pass
+  constexpr unsigned kRrKeys = 64 / (2 * kRrG);
+  for (unsigned e0 = (unsigned)wave * kRrKeys; e0 < nref; e0 += 4u * kRrKeys) {
+    const unsigned e = e0 + (unsigned)lane / (2 * kRrG);
     const bool live = e < nref;
     RefEntry rl;
     if (live) rl = s_ref[e];
-    reranked += rerank_group<DT>(live, rl, keys, n, c, v64, v32, v64 == nullptr, b64, codes,
-                                 dist, unc, unc_cap, full, cnt, lane);
+    reranked += rerank_group<DT, kRrG>(live, rl, keys, n, c, v64, v32, v64 == nullptr, b64,
+                                       codes, dist, unc, unc_cap, full, cnt, lane);
   }
   const unsigned fslot = block_append(&cnt->full, outcome == 4, &s_cnt, &s_base);
   if (outcome == 4) {
