@@ -108,7 +108,7 @@ int a2ats_calibrate(const float* queries, int64_t heads, int64_t m, int64_t d, d
  *   codes     [heads, n]     uint16 output; 1 <= c <= 65536
  *   dist      [heads, n]     fp32 output (k - c_code) H (k - c_code)^T, or NULL
  *   stats     device a2ats_encode_stats, or NULL: counters of how each key was decided
- * Keys with an element of magnitude >= 65520 (outside fp16) are decided entirely in fp64.
+ * Keys with an element of magnitude >= 65504 (outside fp16) are decided entirely in fp64.
  * Returns without waiting.
  */
 typedef struct a2ats_encode_stats {
@@ -139,10 +139,12 @@ int a2ats_encode(const void* keys, int keys_dtype, int64_t heads, int64_t n, int
  * a2ats_encode_prepared encodes keys with a workspace that a2ats_encode_prepare filled for the
  * same heads, n, c and chol-or-NULL; the other arguments are as for a2ats_encode.  It does not
  * read the codebook or L again (chol only selects the H-weighted rule, and with fp32 keys and
- * dist != NULL it is read for ||k L||^2).  Any number of runs may follow one prepare; each run
- * resets its own counters.  Runs on one workspace must be ordered on one stream (they share
- * the list buffers); the prepared part must not be written between prepare and the runs.
- * Both return without waiting; errors as for a2ats_encode.
+ * dist != NULL it is read for ||k L||^2).  Any number of runs may follow one prepare:
+ * a2ats_encode_prepare also clears the run state kept in the workspace (list lengths,
+ * decision counters), and every run leaves it cleared when its last kernel ends.  Runs on one
+ * workspace must be ordered on one stream (they share that state and the list buffers); the
+ * workspace must not be written between prepare and the runs; after a run that returned an
+ * error, prepare again.  Both return without waiting; errors as for a2ats_encode.
  */
 int a2ats_encode_prepare(const float* codebook, int64_t c, const float* chol, int64_t heads,
                          int64_t n, int64_t d, void* workspace, size_t workspace_bytes,

@@ -56,6 +56,7 @@ struct Counters {
   unsigned stat_x[8][16];    // keys, direct decisions, reranks per XCD (statistics only)
   unsigned full;             // full-scan list entries
   unsigned stats[8];         // [3] rescanned, [4] full scan
+  unsigned done;             // rescan-decide workgroups finished (the last one clears the run state)
   unsigned unc[1];           // per-head rescan list lengths follow (heads entries)
 };
 
@@ -1308,10 +1309,10 @@ __global__ __launch_bounds__(256) void enc_rescan_decide(
     const void* __restrict__ keys, int64_t n, int64_t heads, int64_t c,
     const double* __restrict__ v64, const float* __restrict__ v32, int plain,
     const double* __restrict__ b64,
-    const UncEntry* __restrict__ unc, int64_t unc_cap, const unsigned* __restrict__ cand_n,
+    const UncEntry* __restrict__ unc, int64_t unc_cap, unsigned* __restrict__ cand_n,
     const int32_t* __restrict__ cand, uint16_t* __restrict__ codes, float* __restrict__ dist,
     FullEntry* __restrict__ full, Counters* __restrict__ cnt, int want_stats,
-    const float* __restrict__ chol) {
+    const float* __restrict__ chol, int clear_words) {
   const int t = threadIdx.x, lane = t & 63, g = lane & 3, q16 = lane >> 2;
   const HeadSet hsx = all_heads(heads);
   __shared__ int64_t pre[kMaxHeadsLds + 1];
@@ -1325,6 +1326,7 @@ __global__ __launch_bounds__(256) void enc_rescan_decide(
     const int64_t slot = head * unc_cap + rest;
     const UncEntry ue = unc[slot];
     const unsigned nc = cand_n[slot];
+    if (lane == 0) cand_n[slot] = 0u;  // left cleared for the next run
     if (nc > (unsigned)kCandCap) {
       full_scan_wave<DT>(keys, n, c, v64, b64, chol, head, ue.row, ue.z2, codes, dist, kx[t >> 6],
                          lane);
@@ -1389,6 +1391,20 @@ __global__ __launch_bounds__(256) void enc_rescan_decide(
     if (t == 0 && s_dec) atomicAdd(&cnt->stats[3], s_dec);
     if (t == 0 && s_full) atomicAdd(&cnt->stats[4], s_full);
   }
+  if (clear_words > 0) {  // the last workgroup to finish leaves the run counters cleared
+    __shared__ unsigned s_last;
+    __syncthreads();
+    if (t == 0) {
+      __threadfence();
+      s_last = atomicAdd(&cnt->done, 1u) == gridDim.x - 1u;
+    }
+    __syncthreads();
+    if (s_last) {
+      __threadfence();
+      unsigned* w = reinterpret_cast<unsigned*>(cnt);
+      for (int i = t; i < clear_words; i += 256) w[i] = 0u;
+    }
+  }
 }
 
 
@@ -1422,7 +1438,9 @@ __global__ __launch_bounds__(256) void enc_znorm64(const float* __restrict__ key
   }
 }
 
-// The run's list and candidate counters start at zero (a fill kernel, not a memset node).
+// The run state (list lengths, decision counters, candidate counts) starts at zero: cleared
+// when the codebook side is prepared (a fill kernel, not a memset node), and left cleared by
+// the last kernel of every run.
 __global__ void enc_clear(unsigned* __restrict__ cnt, int ncnt, unsigned* __restrict__ cand_n,
                           int64_t ncand) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1431,7 +1449,8 @@ __global__ void enc_clear(unsigned* __restrict__ cnt, int ncnt, unsigned* __rest
   for (int64_t k = i; k < ncand; k += stride) cand_n[k] = 0u;
 }
 
-__global__ void enc_stats_out(const Counters* __restrict__ cnt, a2ats_encode_stats* out) {
+// Copies the run's decision counts out, then leaves the run counters cleared.
+__global__ void enc_stats_out(Counters* __restrict__ cnt, a2ats_encode_stats* out, int clear_words) {
   if (threadIdx.x == 0) {
     unsigned keys = 0, direct = 0;
     for (int x = 0; x < 8; ++x) {
@@ -1449,6 +1468,9 @@ __global__ void enc_stats_out(const Counters* __restrict__ cnt, a2ats_encode_sta
     out->reserved[1] = cnt->full;
     out->reserved[2] = 0;
   }
+  __syncthreads();
+  unsigned* w = reinterpret_cast<unsigned*>(cnt);
+  for (int i = threadIdx.x; i < clear_words; i += blockDim.x) w[i] = 0u;
 }
 
 // ------------------------------------------------------------------ host side
@@ -1517,6 +1539,9 @@ int encode_prepare(int64_t heads, const float* codebook, int64_t c, const float*
                    const EncLayout& L, hipStream_t s) {
   const int T = (int)tiles_of(c);
   const bool plain = chol == nullptr;
+  const int64_t ncand = heads * L.unc_cap;
+  A2ATS_TRY(launch("encode_clear", enc_clear, dim3(grid_for(std::max<int64_t>(ncand, L.ncnt), 256, 1024)),
+                   dim3(256), 0, s, L.cnt, L.ncnt, L.cand_n, ncand));
   if (!plain)
     A2ATS_TRY(launch("encode_prep_gram", enc_prep_gram, dim3(kD / 8, (unsigned)heads), dim3(256), 0, s,
                      chol, L.gram, L.part_a, L.nwg_a));
@@ -1539,9 +1564,6 @@ int encode_run(const void* keys, int64_t heads, int64_t n, const int32_t* idx, i
   while ((1 << (tbits - 1)) < T) ++tbits;
   const bool plain = chol == nullptr;
   Counters* cnt = reinterpret_cast<Counters*>(L.cnt);
-  const int64_t ncand = heads * L.unc_cap;
-  A2ATS_TRY(launch("encode_clear", enc_clear, dim3(grid_for(std::max<int64_t>(ncand, L.ncnt), 256, 1024)),
-                   dim3(256), 0, s, L.cnt, L.ncnt, L.cand_n, ncand));
   const bool znorm_mfma = dist && !plain && DT == A2ATS_BF16;
   float* znorm = nullptr;
   if (dist && !plain) {
@@ -1568,9 +1590,9 @@ int encode_run(const void* keys, int64_t heads, int64_t n, const int32_t* idx, i
                    L.cand_n, L.cand));
   A2ATS_TRY(launch("encode_rescan_decide", enc_rescan_decide<DT>, dim3(kDecideWgs), dim3(256), 0, s, keys, n,
                    heads, c, L.v64, L.v32, plain ? 1 : 0, L.b64, L.unc, L.unc_cap, L.cand_n, L.cand, codes, dist, L.full,
-                   cnt, stats ? 1 : 0, chol));
+                   cnt, stats ? 1 : 0, chol, stats ? 0 : L.ncnt));
   if (stats)
-    A2ATS_TRY(launch("encode_stats", enc_stats_out, dim3(1), dim3(64), 0, s, cnt, stats));
+    A2ATS_TRY(launch("encode_stats", enc_stats_out, dim3(1), dim3(64), 0, s, cnt, stats, L.ncnt));
   return A2ATS_OK;
 }
 

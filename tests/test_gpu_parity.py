@@ -185,6 +185,31 @@ class TestEncode:
             assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
             assert torch.equal(a[1], b[1])
 
+    @pytest.mark.parametrize("use_h", [False, True])
+    def test_prepared_runs_leave_state_clear(self, use_h):
+        # one prepare, then runs with and without statistics, all keys and subsets: every run
+        # starts from the state the previous one left (cleared), so each equals a one-shot call
+        w = synth.Workload("prepared_runs", 124, 2, 1500, 300, "bf16", m=400)
+        cb = f32_to_dev(synth.codebook(w.cfg, w.heads, w.c))
+        L = f32_to_dev(oracle_L(w.cfg, w.heads, w.m)) if use_h else None
+        prep = kv.encode_prepare(cb, L, w.n)
+        k1 = keys_to_dev(synth.keys(w.cfg, w.heads, w.n, "bf16"))
+        k2 = keys_to_dev(synth.keys(w.cfg + 1, w.heads, w.n, "bf16"))
+        rng = np.random.default_rng(7)
+        idx = torch.from_numpy(np.stack([np.sort(rng.choice(w.n, 600, replace=False))
+                                         for _ in range(w.heads)]).astype(np.int32)).to(DEV)
+        for keys, ix, with_stats in ((k1, None, True), (k2, idx, False), (k1, None, False),
+                                     (k2, idx, True), (k2, None, True)):
+            sa = torch.zeros(8, dtype=torch.int32, device=DEV) if with_stats else None
+            sb = torch.zeros(8, dtype=torch.int32, device=DEV) if with_stats else None
+            a = kv.encode_prepared(keys, prep, idx=ix, want_dist=True, stats=sa)
+            b = kv.encode(keys, cb, L, idx=ix, want_dist=True, stats=sb)
+            assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+            assert torch.equal(a[1], b[1])
+            if with_stats:
+                assert torch.equal(sa, sb)
+                assert int(sa[0]) == (w.heads * w.n if ix is None else ix.numel())
+
     def test_deterministic(self):
         w = W["tiny"]
         keys = keys_to_dev(synth.keys(w.cfg, 1, w.n, w.key_dtype))
