@@ -331,6 +331,30 @@ class TestSelectRetrieval:
         assert np.array_equal(ret.cpu().numpy()[1], np.arange(nr))
         assert np.array_equal(ret.cpu().numpy()[2], np.arange(nr))
 
+    @pytest.mark.parametrize("n", [20000, 40000])
+    def test_many_candidates_in_one_bin(self, n):
+        # 2500 keys that are power-of-two multiples of one key: the same cosine to a query
+        # along that key, the largest of all, so the cut falls inside one tie group of
+        # 2500 (a sort of the bin's candidates on one path, a radix select on the other)
+        keys = synth.keys(143, 1, n, "f32")
+        k0 = keys.values[0, 0].copy()
+        keys.values[0, :2500] = k0[None, :] * (2.0 ** (np.arange(2500) % 8 - 4))[:, None]
+        f = 1000.0 / n
+        run_split(keys, k0[None, :].copy(), f, "tie group n=%d" % n)
+        ret, _ = kv.select_retrieval(keys_to_dev(keys), f32_to_dev(k0[None, :].copy()), f)
+        nr = oracle.retrieval_count(n, f)
+        assert np.array_equal(ret.cpu().numpy()[0], np.arange(nr))
+
+    def test_degenerate_long(self):
+        # every key identical beyond the one-workgroup size: all ties, lowest indices win
+        keys = synth.keys(144, 1, 40000, "f32")
+        keys.values[0] = keys.values[0, :1]
+        q = keys.values[:, 5].copy()
+        ret, bulk = kv.select_retrieval(keys_to_dev(keys), f32_to_dev(q), 0.3)
+        nr = oracle.retrieval_count(40000, 0.3)
+        assert np.array_equal(ret.cpu().numpy()[0], np.arange(nr))
+        assert np.array_equal(bulk.cpu().numpy()[0], np.arange(nr, 40000))
+
     def test_single_token(self):
         keys = synth.keys(142, 1, 1, "bf16")
         ret, bulk = kv.select_retrieval(keys_to_dev(keys), q_to_dev(keys.values[:, 0], "bf16"), 0.2)
