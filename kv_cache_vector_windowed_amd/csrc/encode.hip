@@ -56,7 +56,8 @@ struct Counters {
   unsigned stat_x[8][16];    // keys, direct decisions, reranks per XCD (statistics only)
   unsigned full;             // full-scan list entries
   unsigned stats[8];         // [3] rescanned, [4] full scan
-  unsigned done;             // rescan-decide workgroups finished (the last one clears the run state)
+  unsigned done_grp[8][64];  // rescan-decide workgroups finished, per group blockIdx % 8 (256 B apart)
+  unsigned done;             // groups finished (the last workgroup clears the run state)
   unsigned unc[1];           // per-head rescan list lengths follow (heads entries)
 };
 
@@ -1392,17 +1393,27 @@ __global__ __launch_bounds__(256) void enc_rescan_decide(
     if (t == 0 && s_full) atomicAdd(&cnt->stats[4], s_full);
   }
   if (clear_words > 0) {  // the last workgroup to finish leaves the run counters cleared
+    // Without statistics this pass changes no counter; it only reads them, and every read
+    // has returned (its value was used) before the workgroup takes its ticket, so no
+    // device-scope fence is needed (one costs an L2 write-back per workgroup); the clearing
+    // stores are device-scope atomics, visible to every XCD.  Tickets are taken in two
+    // levels, per group of workgroups (blockIdx % 8) and then per group: same-address
+    // device-scope atomics serialise at the memory side, 256 of them on one address cost
+    // about 6 us.
     __shared__ unsigned s_last;
     __syncthreads();
     if (t == 0) {
-      __threadfence();
-      s_last = atomicAdd(&cnt->done, 1u) == gridDim.x - 1u;
+      const unsigned grp = blockIdx.x % 8u;
+      const unsigned members = gridDim.x / 8u + (grp < gridDim.x % 8u ? 1u : 0u);
+      const bool last_of_grp = atomicAdd(&cnt->done_grp[grp][0], 1u) == members - 1u;
+      const unsigned groups = gridDim.x < 8u ? gridDim.x : 8u;
+      s_last = last_of_grp && atomicAdd(&cnt->done, 1u) == groups - 1u;
     }
     __syncthreads();
     if (s_last) {
-      __threadfence();
       unsigned* w = reinterpret_cast<unsigned*>(cnt);
-      for (int i = t; i < clear_words; i += 256) w[i] = 0u;
+      for (int i = t; i < clear_words; i += 256)
+        __hip_atomic_store(&w[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
