@@ -637,6 +637,17 @@ __device__ __forceinline__ double coop_score_g(const void* keys, int64_t off_key
   return s - 0.5 * bj;
 }
 
+// Lists a key for the fp64 scan of the whole codebook.
+__device__ __forceinline__ void full_append(FullEntry* full, Counters* cnt, int32_t head,
+                                            int32_t row, float z2) {
+  FullEntry fe;
+  fe.head = head;
+  fe.row = row;
+  fe.z2 = z2;
+  fe.pad = 0;
+  full[atomicAdd(&cnt->full, 1u)] = fe;
+}
+
 // fp64 rerank of one listed key per group of 2G lanes (the first G score j0, the next G j1):
 // certified when the better exact score beats re.thr, else handed to the rescan (or, when
 // its list is full, the full scan).  Without L the rows are the fp32 codebook itself (v = c
@@ -662,11 +673,12 @@ __device__ __forceinline__ unsigned rerank_group(
   const double s_other = __shfl_xor(s, G);
   const double k2_other = __shfl_xor(k2, G);
   unsigned decided = 0;
+  bool listed = false;  // this group's key joins the rescan list
+  int best = ja;
+  double sbest = s;
   if (live && lane % (2 * G) == 0) {
     const double sa = s, sb = s_other;  // the group's first lane scored ja, lane G jb
     if (ja < 0) k2 = k2_other;
-    int best = ja;
-    double sbest = sa;
     if (jb >= 0 && (ja < 0 || sb > sa || (sb == sa && jb < ja))) {
       best = jb;
       sbest = sb;
@@ -677,9 +689,26 @@ __device__ __forceinline__ unsigned rerank_group(
       codes[(int64_t)head * n + row] = (uint16_t)best;
       if (dist) dist[(int64_t)head * n + row] = (float)fmax(z2 - 2.0 * sbest, 0.0);
       decided = 1;
+    } else if (best >= 0) {
+      listed = true;
     } else {
-      const unsigned slot = atomicAdd(&cnt->unc[head], 1u);
-      if (best >= 0 && slot < unc_cap) {
+      full_append(full, cnt, head, row, re.z2);
+    }
+  }
+  // One list append per wave: the live entries of a wave are keys of one head (a workgroup
+  // serves one head's key block), and device-scope atomics on one address serialise at the
+  // memory side.
+  const unsigned long long m = __ballot(listed);
+  if (m) {  // wave-uniform
+    const int first = __builtin_ctzll(m);
+    const int32_t h0 = __shfl(head, first);
+    unsigned base = 0u;
+    if (lane == first) base = atomicAdd(&cnt->unc[h0], (unsigned)__popcll(m));
+    base = __shfl(base, first);
+    if (listed) {
+      const unsigned slot = base + (unsigned)__builtin_amdgcn_mbcnt_hi(
+                                       (unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+      if (slot < unc_cap) {
         UncEntry ue;
         ue.row = row;
         ue.jbest = best;
@@ -689,12 +718,7 @@ __device__ __forceinline__ unsigned rerank_group(
         ue.pad = 0;
         unc[(int64_t)head * unc_cap + slot] = ue;
       } else {
-        FullEntry fe;
-        fe.head = head;
-        fe.row = row;
-        fe.z2 = re.z2;
-        fe.pad = 0;
-        full[atomicAdd(&cnt->full, 1u)] = fe;
+        full_append(full, cnt, head, row, re.z2);
       }
     }
   }
