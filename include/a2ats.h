@@ -176,6 +176,23 @@ int a2ats_assign_cosine(const void* x, int x_dtype, int64_t heads, int64_t n, in
                         void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * merge_codes -- the last step of the encode pipeline in "A2ATS-adapted -- Windowed RoPE +
+ * Query-Aware Retrieval VQ", How it works: every key first takes its plain code, and the
+ * keys of the retrieval set then take the query-aware (H-weighted or blended) code.  With
+ * both passes run over separate code arrays (so that they can run at the same time), this
+ * writes the second array's codes at the retrieval indices into the first:
+ *     codes[h, idx[h, i]] = src[h, idx[h, i]]   for i < n_idx
+ *
+ *   src    [heads, n]      uint16 codes of the query-aware pass (only the listed rows read)
+ *   idx    [heads, n_idx]  int32 row indices; entries outside [0, n) are skipped
+ *   codes  [heads, n]      uint16, updated in place at the listed rows only
+ * Requires 0 <= n_idx <= n <= 2^31 - 1; src and codes may be the same array (no change).
+ * Returns without waiting.
+ */
+int a2ats_merge_codes(const uint16_t* src, const int32_t* idx, int64_t heads, int64_t n,
+                      int64_t n_idx, uint16_t* codes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * select_retrieval -- "veloxquant_mlx.quantizers.a2ats module", a2ats_select_retrieval_set:
  * per head, the n_r = a2ats_retrieval_count(n, fraction) keys with the largest cosine to
  * the query form the retrieval set, the other n - n_r the bulk.  Equal scores keep the

@@ -54,6 +54,7 @@ def lib() -> ctypes.CDLL:
         L.a2ats_encode.argtypes = [p, i32, i64, i64, i64, p, i64, p, i64, p, p, p, p, p, sz, p]
         L.a2ats_encode_prepare.argtypes = [p, i64, p, i64, i64, i64, p, sz, p]
         L.a2ats_encode_prepared.argtypes = [p, i32, i64, i64, i64, p, i64, i64, p, p, p, p, p, sz, p]
+        L.a2ats_merge_codes.argtypes = [p, p, i64, i64, i64, p, p]
         L.a2ats_assign_cosine_workspace.argtypes = [i64, i64, i64]
         L.a2ats_assign_cosine_workspace.restype = sz
         L.a2ats_assign_cosine.argtypes = [p, i32, i64, i64, i64, p, i64, p, i64, dbl, p, p, sz, p]
@@ -261,6 +262,22 @@ def assign_cosine(x: torch.Tensor, query: torch.Tensor, codebook: torch.Tensor, 
                                      query.shape[1], _ptr(codebook), codebook.shape[1],
                                      float(beta), _ptr(codes), _ptr(ws), ws.numel(),
                                      _stream(x.device)), "assign_cosine")
+    return codes
+
+
+def merge_codes(codes: torch.Tensor, src: torch.Tensor, idx: torch.Tensor) -> torch.Tensor:
+    """codes [heads, n] uint16 (updated in place), src [heads, n] uint16, idx [heads, n_idx]
+    int32: codes[h, idx[h, i]] = src[h, idx[h, i]].  Returns codes."""
+    _dev(codes, "codes")
+    _dev(src, "src")
+    _dev(idx, "idx")
+    if codes.dtype != torch.uint16 or src.dtype != torch.uint16 or idx.dtype != torch.int32:
+        raise ValueError("codes and src must be uint16, idx int32")
+    if codes.dim() != 2 or src.shape != codes.shape or idx.dim() != 2 or idx.shape[0] != codes.shape[0]:
+        raise ValueError("codes, src [heads, n] and idx [heads, n_idx]")
+    heads, n = codes.shape
+    _check(lib().a2ats_merge_codes(_ptr(src), _ptr(idx), heads, n, idx.shape[1], _ptr(codes),
+                                   _stream(codes.device)), "merge_codes")
     return codes
 
 

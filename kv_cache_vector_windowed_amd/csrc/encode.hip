@@ -1681,6 +1681,31 @@ extern "C" int a2ats_encode(const void* keys, int keys_dtype, int64_t heads, int
   return encode_dispatch(keys, keys_dtype, heads, n, idx, n_sel, c, chol, codes, dist, stats, L, s);
 }
 
+// codes[h, idx[h, i]] = src[h, idx[h, i]]: the retrieval keys take the query-aware codes.
+__global__ __launch_bounds__(256) void enc_merge(const uint16_t* __restrict__ src,
+                                                 const int32_t* __restrict__ idx, int64_t heads,
+                                                 int64_t n, int64_t n_idx,
+                                                 uint16_t* __restrict__ codes) {
+  const int64_t total = heads * n_idx;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * 256) {
+    const int64_t h = e / n_idx;
+    const int64_t r = idx[e];
+    if (r >= 0 && r < n) codes[h * n + r] = src[h * n + r];
+  }
+}
+
+extern "C" int a2ats_merge_codes(const uint16_t* src, const int32_t* idx, int64_t heads,
+                                 int64_t n, int64_t n_idx, uint16_t* codes, void* stream) {
+  if (heads < 1 || heads > 65535 || n < 0 || n > 0x7FFFFFFF || n_idx < 0 || n_idx > n)
+    return A2ATS_EINVAL;
+  if (n_idx == 0) return A2ATS_OK;
+  if (!src || !idx || !codes) return A2ATS_EINVAL;
+  if (src == codes) return A2ATS_OK;
+  return launch("encode_merge", enc_merge, dim3(grid_for(heads * n_idx, 256, 4096)), dim3(256), 0,
+                static_cast<hipStream_t>(stream), src, idx, heads, n, n_idx, codes);
+}
+
 extern "C" int a2ats_encode_prepare(const float* codebook, int64_t c, const float* chol,
                                     int64_t heads, int64_t n, int64_t d, void* workspace,
                                     size_t workspace_bytes, void* stream) {

@@ -58,6 +58,7 @@ def test_retrieval_count(L, n, f, want):
 
 
 FAKE = ctypes.c_void_p(4096)  # never dereferenced: every call below fails validation first
+FAKE2 = ctypes.c_void_p(8192)  # a second distinct pointer, also never dereferenced
 
 
 def test_encode_validation(L):
@@ -143,6 +144,21 @@ def test_assign_cosine_validation(L):
     assert call(c=65537) == EINVAL
     assert call(x=None) == EINVAL
     assert call(n=0) == 0
+
+
+def test_merge_codes_validation(L):
+    def call(heads=2, n=100, n_idx=10, src=FAKE, idx=FAKE, codes=FAKE2):
+        return L.a2ats_merge_codes(src, idx, heads, n, n_idx, codes, None)
+
+    assert call(heads=0) == EINVAL
+    assert call(n=-1) == EINVAL
+    assert call(n_idx=101) == EINVAL
+    assert call(n_idx=-1) == EINVAL
+    assert call(src=None) == EINVAL
+    assert call(idx=None) == EINVAL
+    assert call(codes=None) == EINVAL
+    assert call(n_idx=0, src=None, idx=None, codes=None) == 0  # nothing to merge
+    assert call(codes=FAKE) == 0                              # src == codes: nothing changes
 
 
 def test_select_validation(L):

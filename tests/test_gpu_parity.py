@@ -897,6 +897,37 @@ class TestPipeline:
             assert torch.equal(codes, ref_codes)
             assert torch.equal(out.view(torch.int16), ref_out)
 
+    def test_merge_codes(self):
+        rng = np.random.default_rng(11)
+        heads, n = 3, 5000
+        base = rng.integers(0, 65536, (heads, n), dtype=np.uint16)
+        src = rng.integers(0, 65536, (heads, n), dtype=np.uint16)
+        idx = np.stack([np.sort(rng.choice(n, 700, replace=False)) for _ in range(heads)]).astype(np.int32)
+        idx[1, 5] = -3      # skipped
+        idx[2, 9] = n + 4   # skipped
+        want = base.copy()
+        for h in range(heads):
+            ok = (idx[h] >= 0) & (idx[h] < n)
+            want[h, idx[h][ok]] = src[h, idx[h][ok]]
+        codes = u16_to_dev(base)
+        kv.merge_codes(codes, u16_to_dev(src), torch.from_numpy(idx).to(DEV))
+        assert np.array_equal(u16_to_np(codes), want)
+
+    def test_all_plain_then_merge_equals_split_passes(self):
+        # the pages' order (plain codes for every key, query-aware codes at the retrieval
+        # indices) run as two independent passes plus the merge, against bulk + retrieval
+        w = W["layer"]
+        keys = synth.keys(w.cfg, w.heads, w.n, w.key_dtype)
+        kd, cbd = keys_to_dev(keys), f32_to_dev(synth.codebook(w.cfg, w.heads, w.c))
+        H, L = kv.calibrate(f32_to_dev(synth.queries(w.cfg, w.heads, w.m)), 1e-4)
+        ret, bulk = kv.select_retrieval(kd, kd[:, -1].contiguous(), w.fraction)
+        ref = kv.encode(kd, cbd, None, idx=bulk)
+        ref = kv.encode(kd, cbd, L, idx=ret, codes=ref)
+        allp = kv.encode(kd, cbd, None)
+        hcodes = kv.encode(kd, cbd, L, idx=ret)
+        kv.merge_codes(allp, hcodes, ret)
+        assert torch.equal(allp.view(torch.int16), ref.view(torch.int16))
+
     @pytest.mark.parametrize("name", ["layer", "long_context"])
     def test_split_encode_reconstruct(self, name):
         w = W[name]
