@@ -341,3 +341,14 @@ def test_binding_fails_loudly_without_device_tensors():
     import torch
     with pytest.raises(ValueError):
         kv.calibrate(torch.zeros(1, 4, 128))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the benchmark is for one GPU: --gpus above 1 exits with a message before touching a device
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
