@@ -1,23 +1,32 @@
 #!/usr/bin/env python3
 """Benchmark of the A2ATS key-cache hot path on one MI355X.
 
-Headline: the per-layer cache update of a Llama-3.2-3B-shaped layer (8 KV heads x 32768
-tokens x d=128, bf16 keys, C=1024 centroids per head, H from 4096 queries, W=512, retrieval
-fraction 0.1).  One step = retrieval split (with the codebook side of both encodes on a
-second stream) -> plain encode of the bulk rows and, on the second stream, H-weighted encode
-of the retrieval rows (every key gets exactly its pipeline code) -> windowed-RoPE
-reconstruct (bf16) of the whole cache.  Calibration
-(H and L) is the pages' one-time offline job: it runs once before timing and is reported
-separately.  `value` = keys encoded per second.
+Headline: the large-codebook H-weighted encode (8 KV heads x 131072 bf16 keys, d = 128,
+C = 4096 centroids per head, L from 8192 correlated queries per head, codes + argmin
+distances).  One step = one a2ats_encode call: the codebook side (M = L L^T, v = c M,
+b = ||c L||^2, fp16 fragments) and the key side (the MFMA pass with its certificate and
+fp64 rerank, the rescan of the keys left open).  `value` = keys encoded per second of that
+call, inputs resident in HBM.  `roofline` describes the MFMA pass (enc_coarse): 2 N C d
+flop per launch over its average launch duration, recorded with HIP events around the
+library's own launches on the launch stream.
 
-Also reported (field "extra"): the large-codebook H-weighted encode (8 x 131072 keys,
-C=4096, codes + distances) with its MFMA fraction; the decode step (32 x 8 x 16384 tokens,
-fp32 reconstruct + cosine-blend of the new keys) and the long-context pipeline (8 x 131072
-keys, 5% split, C=2048, W=1024) with HBM fractions.
+Also reported (field "extra"): the same encode with the codebook prepared once; the
+per-layer cache update of a Llama-3.2-3B-shaped layer (split, plain + H-weighted encode,
+bf16 reconstruct; HIP graph replays); the decode step (fp32 reconstruct of 32 x 8 x 16384
+tokens, blend of the new keys, far-unrotated update, top-K over codes) and the long-context
+pipeline (5% split, C = 2048, W = 1024) with HBM fractions; the sub-vector default
+configuration and codebook training.
+
+Modes for the committed counter summaries (rocprofv3 runs these; see profiles/):
+  --pmc-probe WORKLOAD     a few calls of one workload plus a 256 MiB reference copy
+  --pmc-summarize DIR      turns the --pmc passes under DIR into profiles/*_pmc.{json,md}
+  --trace-summarize DIR    turns a --kernel-trace --stats run into profiles/*_trace.md
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -34,6 +43,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (256 CU x 2.4 GHz x 256 flop/clk with FMA)
 PEAK_FP64_TFLOPS = 78.6        # MI355X fp64 vector (an FMA counted as two operations)
 METRIC = "keys encoded/sec (H-weighted VQ, d=128) + % MFMA peak; reconstruct GB/s"
+COPY_REF_BYTES = 256 * 2 ** 20
+D = 128
 
 
 def log(*a):
@@ -48,18 +59,29 @@ def sha_of(path):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pmc-probe", action="store_true",
-                    help="run 3 layer steps and a 256 MiB reference copy, for rocprofv3 --pmc")
-    ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="turn two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) of "
-                         "--pmc-probe into profiles/encode_coarse_plain_layer_pmc.{json,md}")
+    ap.add_argument("--pmc-probe", metavar="WORKLOAD",
+                    choices=sorted(PROBES),
+                    help="a few calls of one workload and a 256 MiB reference copy, for "
+                         "rocprofv3 --pmc")
+    ap.add_argument("--pmc-summarize", metavar="DIR",
+                    help="turn the rocprofv3 --pmc passes under DIR (subdirectories named "
+                         "<workload>_<pass>) into profiles/<kernel>_<workload>_pmc.{json,md}")
+    ap.add_argument("--trace-summarize", metavar="DIR",
+                    help="turn a rocprofv3 --kernel-trace --stats output under DIR into "
+                         "profiles/encode_stress_trace.md")
+    ap.add_argument("--command", default="",
+                    help="the command line that produced the profiler output (recorded in the "
+                         "summary)")
     args = ap.parse_args()
     if args.pmc_summarize:
-        pmc_summarize(*args.pmc_summarize)
+        pmc_summarize(args.pmc_summarize, args.command)
+        return
+    if args.trace_summarize:
+        trace_summarize(args.trace_summarize, args.command)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -74,38 +96,226 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    W = synth.WORKLOADS
+    ctx = Ctx(torch, kv, synth, dev)
+    if args.pmc_probe:
+        PROBES[args.pmc_probe](ctx)
+        ctx.copy_reference()
+        print(json.dumps({"pmc_probe": args.pmc_probe, "copy_ref_bytes": COPY_REF_BYTES}), flush=True)
+        return
 
-    def keys_dev(k):
-        return torch.from_numpy(k.bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    head = headline(ctx, args.steps, args.warmup)
+    extra = dict(head.pop("extra"))
+    if not args.no_extra:
+        extra.update(extra_workloads(ctx, args.steps, args.warmup))
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(synth)
+    w = synth.WORKLOADS["encode_stress"]
+    line = {
+        "metric": METRIC, "value": head["value"], "unit": "keys/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "encode_stress: 8 KV heads x 131072 tokens x d=128 bf16 keys, "
+                               "C=4096 centroids per head, H-weighted (L from 8192 queries per "
+                               "head, ridge 1e-4), codes + argmin distances; step = one "
+                               "a2ats_encode call (codebook side + key side)",
+                   "heads": w.heads, "tokens": w.n, "centroids": w.c, "head_dim": D,
+                   "calibration_queries": w.m, "distances": True},
+        "roofline": head["roofline"], "cpu_baseline": cpu, "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
 
-    def f32(a):
-        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
 
-    # ------------------------------------------------------------------ headline workload
-    w = W["layer"]
+class Ctx:
+    """Device, modules and helpers shared by the workloads."""
+
+    def __init__(self, torch, kv, synth, dev):
+        self.torch, self.kv, self.synth, self.dev = torch, kv, synth, dev
+        self._flush = None
+
+    def keys_dev(self, k):
+        return self.torch.from_numpy(k.bits.view(np.int16)).to(self.dev).view(self.torch.bfloat16)
+
+    def f32(self, a):
+        return self.torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(self.dev)
+
+    def profile(self, fn, reps):
+        """{kernel: (launches, mean ms)} from the HIP events the library records around each
+        of its own launches, on the stream each kernel is launched on."""
+        kv = self.kv
+        kv.profile_reset()
+        kv.profile_enable(True)
+        for _ in range(reps):
+            fn()
+        self.torch.cuda.synchronize()
+        prof = kv.profile_read()
+        kv.profile_enable(False)
+        kv.profile_reset()
+        return {k: (c, t / c) for k, (c, t) in prof.items()}
+
+    def flush_buf(self):
+        if self._flush is None:
+            self._flush = self.torch.ones(2 ** 28, dtype=self.torch.float32, device=self.dev)  # 1 GiB
+            self._flush.sum()  # the first reduction launch carries a one-time setup cost
+            self.torch.cuda.synchronize()
+        return self._flush
+
+    def timed(self, fn, reps, flush=False):
+        """ms per call of fn, calls issued back to back on the stream so the host's issue time
+        overlaps the GPU's work.  With flush, a read of a 1 GiB buffer (which evicts the
+        256 MB last-level cache with clean lines) precedes every call, and the same number of
+        reads timed alone is subtracted.  A kernel that follows a large streaming kernel runs
+        measurably slower than in a back-to-back steady state on this GPU, so both figures
+        are reported for the HBM paths."""
+        torch = self.torch
+        buf = self.flush_buf() if flush else None
+
+        def run(with_fn):
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                if flush:
+                    buf.sum()
+                if with_fn:
+                    fn()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b)
+
+        fn()
+        t = run(True)
+        if flush:
+            t -= run(False)
+        return t / reps
+
+    def copy_reference(self):
+        """A plain elementwise kernel that reads and writes COPY_REF_BYTES: the scale of the
+        FETCH_SIZE / WRITE_SIZE counters."""
+        torch = self.torch
+        src = torch.ones(COPY_REF_BYTES // 4, dtype=torch.float32, device=self.dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------- headline
+class EncodeStress:
+    """The large-codebook encode inputs, resident on the device, and its one-call step."""
+
+    def __init__(self, ctx):
+        torch, kv, synth = ctx.torch, ctx.kv, ctx.synth
+        w = synth.WORKLOADS["encode_stress"]
+        self.w = w
+        log("generating encode_stress inputs")
+        self.kd = ctx.keys_dev(synth.keys(w.cfg, w.heads, w.n, "bf16"))
+        self.cbd = ctx.f32(synth.codebook(w.cfg, w.heads, w.c))
+        self.qd = ctx.f32(synth.queries(w.cfg, w.heads, w.m))
+        t0 = time.perf_counter()
+        _, self.L = kv.calibrate(self.qd, 1e-4)  # waits: reports a non-positive-definite H
+        self.calib_ms = (time.perf_counter() - t0) * 1e3
+        self.codes = torch.zeros((w.heads, w.n), dtype=torch.uint16, device=ctx.dev)
+        self.dist = torch.zeros((w.heads, w.n), dtype=torch.float32, device=ctx.dev)
+        self.stats = torch.zeros(8, dtype=torch.int32, device=ctx.dev)
+        self.ws = torch.empty(kv.encode_workspace_bytes(w.heads, w.n, w.c), dtype=torch.uint8,
+                              device=ctx.dev)
+        self.kv = kv
+        self.flops = 2.0 * w.heads * w.n * w.c * D
+
+    def step(self, stats=False):
+        self.kv.encode(self.kd, self.cbd, self.L, codes=self.codes, dist=self.dist,
+                       stats=self.stats if stats else None, workspace=self.ws)
+
+
+def headline(ctx, steps, warmup):
+    torch, kv = ctx.torch, ctx.kv
+    e = EncodeStress(ctx)
+    w = e.w
+    for _ in range(max(warmup, 1)):
+        e.step()
+    torch.cuda.synchronize()
+    log("timing %d encode calls" % steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        e.step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    keys = w.heads * w.n
+    value = keys / (ms * 1e-3)
+    log("encode_stress call %.4f ms -> %.4g keys/s" % (ms, value))
+    pr = ctx.profile(e.step, min(steps, 10))
+    log("kernels: " + ", ".join("%s %.1fus" % (k, v[1] * 1e3) for k, v in pr.items()))
+    coarse_ms = pr["encode_coarse_h"][1]
+    achieved = e.flops / (coarse_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "encode_coarse_h (enc_coarse, bf16 keys, H, distances)",
+                "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+                "traffic": traffic_from_profiles("enc_coarse", "encode_stress"),
+                "launch_us": round(coarse_ms * 1e3, 2), "flops_per_launch": e.flops,
+                "call_achieved": round(e.flops / (ms * 1e-3) / 1e12, 2),
+                "call_frac": round(e.flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
+    # decision statistics of one call; the key side alone with the codebook prepared once
+    e.step(stats=True)
+    torch.cuda.synchronize()
+    st = e.stats.cpu().numpy().tolist()
+    prep = kv.encode_prepare(e.cbd, e.L, w.n)
+
+    def prepared():
+        kv.encode_prepared(e.kd, prep, codes=e.codes, dist=e.dist)
+
+    ms_p = ctx.timed(prepared, steps)
+    pr_p = ctx.profile(lambda: prep.prepare(e.cbd, e.L), 5)
+    extra = {
+        "encode_stress_kernels_us": {k: round(v[1] * 1e3, 2) for k, v in pr.items()},
+        "encode_stress_decided": {"keys": st[0], "direct": st[1], "reranked": st[2],
+                                  "rescanned": st[3], "full_scan": st[4]},
+        "encode_stress_prepared_ms": round(ms_p, 4),
+        "encode_stress_prepared_keys_per_s": round(keys / (ms_p * 1e-3), 1),
+        "encode_stress_prepared_mfma_frac": round(e.flops / (ms_p * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+        "encode_stress_prepare_us": round(sum(v[1] for v in pr_p.values()) * 1e3, 2),
+        "encode_stress_calibrate_ms_host_clock": round(e.calib_ms, 3),
+    }
+    log("encode_stress extra %s" % extra)
+    del prep
+    return {"value": round(value, 1), "ms": round(ms, 5), "roofline": roofline, "extra": extra}
+
+
+# ---------------------------------------------------------------------------- extra workloads
+def layer_step(ctx, steps, warmup):
+    """The per-layer cache update of a Llama-3.2-3B-shaped layer: 8 KV heads x 32768 bf16
+    keys, C = 1024, H from 4096 queries, W = 512, retrieval fraction 0.1.  One step = split
+    (with the codebook side of both encodes on a second stream) -> plain encode of the bulk
+    rows and, on the second stream, H-weighted encode of the retrieval rows -> bf16
+    reconstruct.  Timed as K replays of the step captured in a HIP graph; the same K steps
+    launched one by one are reported too."""
+    torch, kv, synth, dev = ctx.torch, ctx.kv, ctx.synth, ctx.dev
+    w = synth.WORKLOADS["layer"]
     log("generating layer inputs")
     keys = synth.keys(w.cfg, w.heads, w.n, "bf16")
-    kd = keys_dev(keys)
-    cbd = f32(synth.codebook(w.cfg, w.heads, w.c))
-    qd = f32(synth.queries(w.cfg, w.heads, w.m))
+    kd = ctx.keys_dev(keys)
+    cbd = ctx.f32(synth.codebook(w.cfg, w.heads, w.c))
+    qd = ctx.f32(synth.queries(w.cfg, w.heads, w.m))
     pos = torch.arange(w.n, dtype=torch.int32, device=dev)[None]
     proxy = kd[:, -1].contiguous()
     H, L = kv.calibrate(qd, 1e-4)
     codes = torch.zeros((w.heads, w.n), dtype=torch.uint16, device=dev)
     out = torch.empty((1, w.heads, w.n, 128), dtype=torch.bfloat16, device=dev)
-
     # Every step redoes the codebook side of both encodes (it depends on the codebook and L
     # only) on a second stream (default priority) while the split runs; the two key-side
     # passes write disjoint rows (bulk: plain, retrieval: H-weighted), so the small
     # H-weighted one also runs on the second stream beside the plain one.
     aux = torch.cuda.Stream(device=dev)
-    main_s = torch.cuda.current_stream(dev)
+    main_s = torch.cuda.current_stream(ctx.dev)
     prep_plain = kv.encode_prepare(cbd, None, w.n)
     prep_h = kv.encode_prepare(cbd, L, w.n)
 
     def step():
-        main_s = torch.cuda.current_stream(dev)  # the capturing stream inside a graph capture
+        main_s = torch.cuda.current_stream(ctx.dev)  # the capturing stream inside a graph capture
         aux.wait_event(main_s.record_event())
         with torch.cuda.stream(aux):
             prep_plain.prepare(cbd, None)
@@ -121,37 +331,18 @@ def main():
         main_s.wait_event(aux.record_event())
         kv.reconstruct(codes[None], pos, cbd, w.cur_pos, w.window, out=out)
 
-    if args.pmc_probe:
-        for _ in range(2):
-            step()
-        torch.cuda.synchronize()
-        for _ in range(3):
-            step()
-        torch.cuda.synchronize()
-        src = torch.ones(COPY_REF_BYTES // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)  # reads and writes COPY_REF_BYTES: the counter scale
-        torch.cuda.synchronize()
-        print(json.dumps({"pmc_probe": "done", "copy_ref_bytes": COPY_REF_BYTES}), flush=True)
-        return
-
-    log("warmup %d" % args.warmup)
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    log("timing %d steps" % args.steps)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     e1.record()
     torch.cuda.synchronize()
-    ms_eager = e0.elapsed_time(e1) / args.steps
-    log("layer step, launched one by one: %.4f ms" % ms_eager)
+    ms_eager = e0.elapsed_time(e1) / steps
     # The same step captured once in a HIP graph (the launches of both streams, replayed as
-    # one): the timed steps are K replays.  A replay must reproduce the eager step's codes
-    # and keys bit for bit.
+    # one).  A replay must reproduce the eager step's codes and keys bit for bit.
     ref_codes, ref_out = codes.clone(), out.view(torch.int16).clone()
     side = torch.cuda.Stream(device=dev)
     side.wait_stream(main_s)
@@ -167,30 +358,15 @@ def main():
     torch.cuda.synchronize()
     if not (torch.equal(codes, ref_codes) and torch.equal(out.view(torch.int16), ref_out)):
         raise SystemExit("graph replay differs from the eager step")
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         graph.replay()
     torch.cuda.synchronize()
     e0.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         graph.replay()
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    keys_per_step = w.heads * w.n
-    value = keys_per_step / (ms * 1e-3)
-    log("layer step %.4f ms (graph replay) -> %.4g keys/s" % (ms, value))
-
-    # per-kernel durations: same step, same launches, with HIP events around every kernel
-    def profile(fn, reps):
-        kv.profile_reset()
-        kv.profile_enable(True)
-        for _ in range(reps):
-            fn()
-        torch.cuda.synchronize()
-        prof = kv.profile_read()
-        kv.profile_enable(False)
-        kv.profile_reset()
-        return {k: (c, t / c) for k, (c, t) in prof.items()}
+    ms = e0.elapsed_time(e1) / steps
 
     def step_seq():  # the same launches on one stream: per-kernel times without overlap
         prep_plain.prepare(cbd, None)
@@ -200,207 +376,36 @@ def main():
         kv.encode_prepared(kd, prep_plain, idx=bulk, codes=codes)
         kv.reconstruct(codes[None], pos, cbd, w.cur_pos, w.window, out=out)
 
-    prof = profile(step_seq, min(args.steps, 20))
-    log("kernels: " + ", ".join("%s %.1fus" % (k, v[1] * 1e3) for k, v in prof.items()))
+    prof = ctx.profile(step_seq, min(steps, 20))
     coarse_ms = prof["encode_coarse_plain"][1]
     n_bulk = w.n - kv.retrieval_count(w.n, w.fraction)  # rows of the plain pass
     flops = 2.0 * w.heads * n_bulk * w.c * 128
-    achieved = flops / (coarse_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "encode_coarse_plain", "achieved": round(achieved, 2),
-                "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
-                "traffic": traffic_from_profiles("encode_coarse_plain", "layer"),
-                "launch_us": round(coarse_ms * 1e3, 2), "flops_per_launch": flops}
-    t0 = time.perf_counter()
-    kv.calibrate(qd, 1e-4)
-    calib_ms = (time.perf_counter() - t0) * 1e3
-
-    extra = {"layer_step_ms_eager": round(ms_eager, 5),
-             "layer_kernels_us": {k: round(v[1] * 1e3, 2) for k, v in prof.items()},
-             "layer_calibrate_ms_host_clock": round(calib_ms, 3)}
-    if not args.no_extra:
-        extra.update(extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile))
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, keys, synth)
-
-    line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "keys/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
-        "data": "synthetic",
-        "config": {"workload": "layer: 8 KV heads x 32768 tokens x d=128 bf16 keys, C=1024, "
-                               "H from 4096 queries, W=512, retrieval fraction 0.1; step = split + "
-                               "plain encode of bulk rows || H-weighted encode of retrieval rows + "
-                               "bf16 reconstruct",
-                   "heads": w.heads, "tokens": w.n, "centroids": w.c, "window": w.window,
-                   "fraction": w.fraction},
-        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+    res = {
+        "workload": "8 KV heads x 32768 bf16 keys, C=1024, H from 4096 queries, W=512, retrieval "
+                    "fraction 0.1; step = split + plain encode of bulk rows || H-weighted encode "
+                    "of retrieval rows + bf16 reconstruct",
+        "step_ms_graph": round(ms, 5), "keys_per_s_graph": round(w.heads * w.n / (ms * 1e-3), 1),
+        "step_ms_eager": round(ms_eager, 5),
+        "coarse_plain_us": round(coarse_ms * 1e3, 2),
+        "coarse_plain_mfma_frac": round(flops / (coarse_ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+        "kernels_us": {k: round(v[1] * 1e3, 2) for k, v in prof.items()},
     }
-    print(json.dumps(line), flush=True)
+    log("layer %s" % res)
+    return res
 
 
-COPY_REF_BYTES = 256 * 2 ** 20
-COARSE_SOURCE = "kv_cache_vector_windowed_amd/csrc/encode.hip"
-
-
-def _pmc_rows(d, counter):
-    """{dispatch id: (kernel name, grid size, value summed over instances)} for one counter."""
-    import csv
-    import glob
-    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
-    if not files:
-        raise SystemExit("no counter_collection.csv under %s" % d)
-    out = {}
-    for f in files:
-        with open(f) as fh:
-            for r in csv.DictReader(fh):
-                if r["Counter_Name"] != counter:
-                    continue
-                k = (f, r["Dispatch_Id"])
-                name, grid, v = out.get(k, (r["Kernel_Name"], int(r["Grid_Size"]), 0.0))
-                out[k] = (name, grid, v + float(r["Counter_Value"]))
-    return out
-
-
-def pmc_summarize(fetch_dir, write_dir):
-    """HBM bytes per launch of the plain coarse encode pass on the layer workload: FETCH_SIZE
-    and WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads for a
-    reference elementwise kernel that reads and writes COPY_REF_BYTES."""
-    # the plain pass of the layer step encodes the bulk rows: 32768 - ceil(0.1 * 32768) a head
-    n_bulk = 32768 - 3277
-    layer_grid = (8 * ((n_bulk + 255) // 256) + 7) // 8 * 8 * 256  # workgroups x 256 threads
-    res = {}
-    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        rows = _pmc_rows(d, counter)
-        coarse = sorted(v for n, g, v in rows.values() if "enc_coarse" in n and "Lb0ELb0E" in n
-                        and g == layer_grid)
-        ref = sorted(v for n, g, v in rows.values() if "neg" in n)
-        if not coarse or not ref:
-            raise SystemExit("%s: missing dispatches (coarse %d, reference %d)" % (counter, len(coarse), len(ref)))
-        kib = coarse[len(coarse) // 2]
-        ref_kib = ref[len(ref) // 2]
-        scale = (COPY_REF_BYTES / 1024.0) / ref_kib
-        res[counter] = {"kib_per_dispatch": kib, "reference_kib": ref_kib, "scale": scale,
-                        "bytes": kib * 1024.0 * scale}
-    total = res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"]
-    # bf16 keys, fp16 codebook fragments, fp32 bias, int32 row indices, uint16 codes
-    algorithmic = 8 * n_bulk * (128 * 2 + 4 + 2) + 8 * 1024 * (128 * 2 + 4)
-    cmd = ["cd /tmp && export TMPDIR=/tmp",
-           "rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o p -- "
-           "python <repo>/bench.py --pmc-probe" % fetch_dir,
-           "rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o p -- "
-           "python <repo>/bench.py --pmc-probe" % write_dir,
-           "python bench.py --pmc-summarize %s %s" % (fetch_dir, write_dir)]
-    d = {"kernel": "encode_coarse_plain", "workload": "layer", "source": COARSE_SOURCE,
-         "source_sha": sha_of(os.path.join(ROOT, COARSE_SOURCE)),
-         "hbm_bytes_per_launch": round(total), "algorithmic_bytes_per_launch": algorithmic,
-         "counters": res, "commands": cmd}
-    base = os.path.join(ROOT, "profiles", "encode_coarse_plain_layer_pmc")
-    with open(base + ".json", "w") as f:
-        json.dump(d, f, indent=1)
-    with open(base + ".md", "w") as f:
-        f.write("# encode_coarse_plain, layer workload: HBM traffic per launch\n\n")
-        f.write("Commands:\n\n```\n%s\n```\n\n" % "\n".join(cmd))
-        f.write("| counter | KiB / dispatch | reference KiB (%d MiB read + write) | scale | bytes |\n"
-                "|---|---|---|---|---|\n" % (COPY_REF_BYTES >> 20))
-        for k, v in res.items():
-            f.write("| %s | %.0f | %.0f | %.4f | %.4g |\n" % (k, v["kib_per_dispatch"], v["reference_kib"],
-                                                         v["scale"], v["bytes"]))
-        f.write("\nTotal %.4g bytes per launch; algorithmic %.4g (bulk keys, fp16 codebook, bias, "
-                "row indices, codes); "
-                "source %s @ %s\n" % (total, algorithmic, COARSE_SOURCE, d["source_sha"]))
-    print(json.dumps(d))
-
-
-def traffic_from_profiles(kernel, workload):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken on
-    the current kernel source (else None)."""
-    p = os.path.join(ROOT, "profiles", "%s_%s_pmc.json" % (kernel, workload))
-    if not os.path.exists(p):
-        return None
-    try:
-        with open(p) as f:
-            d = json.load(f)
-        src = os.path.join(ROOT, d["source"])
-        if sha_of(src) != d["source_sha"]:
-            return None
-        return d["hbm_bytes_per_launch"]
-    except (OSError, KeyError, ValueError):
-        return None
-
-
-def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
+def extra_workloads(ctx, steps, warmup):
+    torch, kv, synth = ctx.torch, ctx.kv, ctx.synth
     W = synth.WORKLOADS
-    res = {}
-    flush_buf = torch.ones(2 ** 28, dtype=torch.float32, device=dev)  # 1 GiB, finite values
-    flush_buf.sum()  # the first reduction launch carries a one-time setup cost of ~20 ms
-    torch.cuda.synchronize()
-
-    def timed(fn, reps, flush=False):
-        """ms per call of fn, calls issued back to back on the stream so the host's issue time
-        overlaps the GPU's work.  With flush, a read of a 1 GiB buffer (which evicts the
-        256 MB last-level cache with clean lines) precedes every call, and the same number of
-        reads timed alone is subtracted.  A kernel that follows a large streaming kernel runs
-        measurably slower than in a back-to-back steady state on this GPU (the gap does not
-        come from cache contents: it appears after a read of 256 MB as after a write of the
-        kernel's own output), so both figures are reported."""
-        def run(with_fn):
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(reps):
-                if flush:
-                    flush_buf.sum()
-                if with_fn:
-                    fn()
-            b.record()
-            torch.cuda.synchronize()
-            return a.elapsed_time(b)
-
-        fn()
-        t = run(True)
-        if flush:
-            t -= run(False)
-        return t / reps
-
-    # large-codebook encode
-    w = W["encode_stress"]
-    log("generating encode_stress inputs")
-    kd = keys_dev(synth.keys(w.cfg, w.heads, w.n, "bf16"))
-    cbd = f32(synth.codebook(w.cfg, w.heads, w.c))
-    _, L = kv.calibrate(f32(synth.queries(w.cfg, w.heads, w.m)), 1e-4)
-    stats = torch.zeros(8, dtype=torch.int32, device=dev)
-
-    def enc():
-        kv.encode(kd, cbd, L, want_dist=True, stats=stats)
-
-    enc()
-    torch.cuda.synchronize()
-    ms = timed(enc, 5)
-    pr = profile(enc, 3)
-    flops = 2.0 * w.heads * w.n * w.c * 128
-    cms = pr["encode_coarse_h"][1]
-    st = stats.cpu().numpy().tolist()
-    res["encode_stress"] = {
-        "workload": "8 heads x 131072 bf16 keys, C=4096, H-weighted, codes + distances",
-        "ms_per_call": round(ms, 4), "keys_per_s": round(w.heads * w.n / (ms * 1e-3), 1),
-        "mfma_frac_call": round(flops / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
-        "coarse_us": round(cms * 1e3, 2),
-        "mfma_frac_coarse": round(flops / (cms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
-        "kernels_us": {k: round(v[1] * 1e3, 2) for k, v in pr.items()},
-        "decided": {"direct": st[1], "reranked": st[2], "rescanned": st[3], "full_scan": st[4]},
-    }
-    log("encode_stress %s" % res["encode_stress"])
-    del kd
+    res = {"layer": layer_step(ctx, min(steps, 50), warmup)}
     # decode step
     w = W["decode"]
     log("generating decode inputs")
-    cbd = f32(synth.codebook(w.cfg, w.heads, w.c))
-    codes = torch.from_numpy(synth.uniform_codes(w.cfg, (w.batch, w.heads, w.n), w.c).view(np.int16)).to(dev).view(torch.uint16)
-    pos = torch.arange(w.n, dtype=torch.int32, device=dev)[None].repeat(w.batch, 1).contiguous()
-    out = torch.empty((w.batch, w.heads, w.n, 128), dtype=torch.float32, device=dev)
-    newk = f32(synth.new_keys(w.cfg, w.heads, w.batch))
+    cbd = ctx.f32(synth.codebook(w.cfg, w.heads, w.c))
+    codes = torch.from_numpy(synth.uniform_codes(w.cfg, (w.batch, w.heads, w.n), w.c).view(np.int16)).to(ctx.dev).view(torch.uint16)
+    pos = torch.arange(w.n, dtype=torch.int32, device=ctx.dev)[None].repeat(w.batch, 1).contiguous()
+    out = torch.empty((w.batch, w.heads, w.n, 128), dtype=torch.float32, device=ctx.dev)
+    newk = ctx.f32(synth.new_keys(w.cfg, w.heads, w.batch))
 
     def rec():
         kv.reconstruct(codes, pos, cbd, w.cur_pos, w.window, out=out)
@@ -411,12 +416,12 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
     rec()
     blend()
     torch.cuda.synchronize()
-    ms_r = timed(rec, 5, flush=True)
-    ms_r_steady = timed(rec, 10)
-    ms_b = timed(blend, 10)
+    ms_r = ctx.timed(rec, 5, flush=True)
+    ms_r_steady = ctx.timed(rec, 10)
+    ms_b = ctx.timed(blend, 10)
     tokens = w.batch * w.heads * w.n
     alg = tokens * (2 + 128 * 4) + w.batch * w.n * 4 + w.heads * w.c * 128 * 4
-    pr = profile(rec, 3)
+    pr = ctx.profile(rec, 3)
     kr = pr["reconstruct"][1]
     res["decode"] = {
         "workload": "32 sequences x 8 heads x 16384 tokens, fp32 out, W=256; blend of 256 new keys",
@@ -443,7 +448,7 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
         kv.reconstruct(codes, pos, cbd, cur, w.window, far_mode=kv.FAR_UNROTATED, out=out)
 
     qh = 24  # query heads of the 8-KV-head layer (grouped-query attention, 3 per KV head)
-    qd = torch.randn((w.batch, qh, 128), dtype=torch.float32, device=dev)
+    qd = torch.randn((w.batch, qh, 128), dtype=torch.float32, device=ctx.dev)
     qo = torch.empty_like(qd)
 
     def qrope():
@@ -451,10 +456,10 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
 
     upd()
     torch.cuda.synchronize()
-    ms_u = timed(upd, 20)
-    ms_fu = timed(full_unrot, 5)
-    ms_q = timed(qrope, 20)
-    pr_u = profile(upd, 5)
+    ms_u = ctx.timed(upd, 20)
+    ms_fu = ctx.timed(full_unrot, 5)
+    ms_q = ctx.timed(qrope, 20)
+    pr_u = ctx.profile(upd, 5)
     rows_step = w.batch * w.heads * 2  # the token leaving the window and the appended token
     res["decode_unrotated"] = {
         "workload": "same cache, far keys unrotated; one decode step (cur-1 -> cur, one token "
@@ -472,9 +477,9 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
     wt = W["topk_decode"]
     kt = int(np.ceil(wt.fraction * wt.n))
     qt = torch.from_numpy(np.ascontiguousarray(
-        synth.queries(wt.cfg, wt.q_heads, wt.batch).transpose(1, 0, 2))).to(dev)
+        synth.queries(wt.cfg, wt.q_heads, wt.batch).transpose(1, 0, 2))).to(ctx.dev)
     qtb = torch.empty_like(qt)
-    t_idx = torch.empty((wt.batch, wt.q_heads, kt), dtype=torch.int32, device=dev)
+    t_idx = torch.empty((wt.batch, wt.q_heads, kt), dtype=torch.int32, device=ctx.dev)
 
     def topk_step():
         kv.far_query_rope(qt, wt.far_b, out=qtb)
@@ -482,9 +487,9 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
 
     topk_step()
     torch.cuda.synchronize()
-    ms_t = timed(topk_step, 20)
-    ms_tf = timed(topk_step, 5, flush=True)
-    pr_t = profile(topk_step, 5)
+    ms_t = ctx.timed(topk_step, 20)
+    ms_tf = ctx.timed(topk_step, 5, flush=True)
+    pr_t = ctx.profile(topk_step, 5)
     kt_us = pr_t["topk_codes"][1] * 1e3
     t_bytes = (wt.batch * wt.heads * wt.n * 2 + wt.heads * wt.c * 128 * 4
                + wt.batch * wt.q_heads * (128 * 4 + kt * 8))
@@ -503,13 +508,13 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
     # long-context pipeline
     w = W["long_context"]
     log("generating long_context inputs")
-    kd = keys_dev(synth.keys(w.cfg, w.heads, w.n, "bf16"))
-    cbd = f32(synth.codebook(w.cfg, w.heads, w.c))
-    _, L = kv.calibrate(f32(synth.queries(w.cfg, w.heads, w.m)), 1e-4)
+    kd = ctx.keys_dev(synth.keys(w.cfg, w.heads, w.n, "bf16"))
+    cbd = ctx.f32(synth.codebook(w.cfg, w.heads, w.c))
+    _, L = kv.calibrate(ctx.f32(synth.queries(w.cfg, w.heads, w.m)), 1e-4)
     proxy = kd[:, -1].contiguous()
-    codes = torch.zeros((w.heads, w.n), dtype=torch.uint16, device=dev)
-    pos = torch.arange(w.n, dtype=torch.int32, device=dev)[None]
-    out = torch.empty((1, w.heads, w.n, 128), dtype=torch.bfloat16, device=dev)
+    codes = torch.zeros((w.heads, w.n), dtype=torch.uint16, device=ctx.dev)
+    pos = torch.arange(w.n, dtype=torch.int32, device=ctx.dev)[None]
+    out = torch.empty((1, w.heads, w.n, 128), dtype=torch.bfloat16, device=ctx.dev)
 
     def split():
         return kv.select_retrieval(kd, proxy, w.fraction)
@@ -517,8 +522,8 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
     def rec2():
         kv.reconstruct(codes[None], pos, cbd, w.cur_pos, w.window, out=out)
 
-    aux = torch.cuda.Stream(device=dev)
-    main_s = torch.cuda.current_stream(dev)
+    aux = torch.cuda.Stream(device=ctx.dev)
+    main_s = torch.cuda.current_stream(ctx.dev)
     prep_plain = kv.encode_prepare(cbd, None, w.n)
     prep_h = kv.encode_prepare(cbd, L, w.n)
 
@@ -540,15 +545,15 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
 
     pipe()
     torch.cuda.synchronize()
-    ms_s = timed(split, 10, flush=True)
-    ms_r = timed(rec2, 10, flush=True)
-    ms_s_steady = timed(split, 20)
-    ms_r_steady = timed(rec2, 20)
-    ms_p = timed(pipe, 5)
+    ms_s = ctx.timed(split, 10, flush=True)
+    ms_r = ctx.timed(rec2, 10, flush=True)
+    ms_s_steady = ctx.timed(split, 20)
+    ms_r_steady = ctx.timed(rec2, 20)
+    ms_p = ctx.timed(pipe, 5)
     split_bytes = w.heads * w.n * (128 * 2 + 4)
     rec_bytes = w.heads * w.n * (2 + 128 * 2) + w.n * 4 + w.heads * w.c * 128 * 4
-    pr_s = profile(split, 5)
-    pr_r = profile(rec2, 5)
+    pr_s = ctx.profile(split, 5)
+    pr_r = ctx.profile(rec2, 5)
     res["long_context"] = {
         "workload": "8 heads x 131072 bf16 keys, 5% split, C=2048, W=1024, bf16 reconstruct",
         "pipeline_ms": round(ms_p, 4), "keys_per_s": round(w.heads * w.n / (ms_p * 1e-3), 1),
@@ -562,7 +567,7 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
         "reconstruct_steady_ms": round(ms_r_steady, 4),
         "reconstruct_steady_hbm_frac": round(rec_bytes / (ms_r_steady * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "reconstruct_kernels_us": {k: round(v[1] * 1e3, 2) for k, v in pr_r.items()},
-        "pipeline_kernels_us": {k: round(v[1] * 1e3, 2) for k, v in profile(pipe, 3).items()},
+        "pipeline_kernels_us": {k: round(v[1] * 1e3, 2) for k, v in ctx.profile(pipe, 3).items()},
     }
     log("long_context %s" % res["long_context"])
     del kd, codes, out
@@ -572,19 +577,19 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
     # reconstructed with W = 128, values gathered without rotation.
     w = W["pq_layer"]
     log("generating pq_layer inputs")
-    kd = keys_dev(synth.keys(w.cfg, w.heads, w.n, "bf16"))
-    vd = keys_dev(synth.keys(w.cfg, w.heads, w.n, "bf16", stream=8))  # value rows
-    cbk = f32(synth.pq_codebook(w.cfg, w.heads, w.c, 8))
-    cbv = f32(synth.pq_codebook(w.cfg + 100, w.heads, w.c, 8))
+    kd = ctx.keys_dev(synth.keys(w.cfg, w.heads, w.n, "bf16"))
+    vd = ctx.keys_dev(synth.keys(w.cfg, w.heads, w.n, "bf16", stream=8))  # value rows
+    cbk = ctx.f32(synth.pq_codebook(w.cfg, w.heads, w.c, 8))
+    cbv = ctx.f32(synth.pq_codebook(w.cfg + 100, w.heads, w.c, 8))
     qs = synth.queries(w.cfg, w.heads, w.m)
-    _, lq = kv.calibrate(f32(qs.reshape(1, -1, 8)), 1e-4)
+    _, lq = kv.calibrate(ctx.f32(qs.reshape(1, -1, 8)), 1e-4)
     lq = lq[0].contiguous()
     proxy = kd[:, -1].contiguous()
     ret, bulk = kv.select_retrieval(kd, proxy, w.fraction)
-    kc = torch.zeros((w.heads, w.n, 16), dtype=torch.uint8, device=dev)
-    vc = torch.zeros((w.heads, w.n, 16), dtype=torch.uint8, device=dev)
-    pos = torch.arange(w.n, dtype=torch.int32, device=dev)[None]
-    kout = torch.empty((1, w.heads, w.n, 128), dtype=torch.bfloat16, device=dev)
+    kc = torch.zeros((w.heads, w.n, 16), dtype=torch.uint8, device=ctx.dev)
+    vc = torch.zeros((w.heads, w.n, 16), dtype=torch.uint8, device=ctx.dev)
+    pos = torch.arange(w.n, dtype=torch.int32, device=ctx.dev)[None]
+    kout = torch.empty((1, w.heads, w.n, 128), dtype=torch.bfloat16, device=ctx.dev)
     vout = torch.empty_like(kout)
 
     def enc_plain_all():
@@ -616,12 +621,12 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
     for f in (enc_plain_all, enc_blend, enc_h, enc_values, rec_keys, rec_values, step):
         f()
     torch.cuda.synchronize()
-    t_plain = timed(enc_plain_all, 10)
-    t_blend = timed(enc_blend, 5)
-    t_h = timed(enc_h, 10)
-    t_rk = timed(rec_keys, 10)
-    t_rv = timed(rec_values, 10)
-    t_step = timed(step, 5)
+    t_plain = ctx.timed(enc_plain_all, 10)
+    t_blend = ctx.timed(enc_blend, 5)
+    t_h = ctx.timed(enc_h, 10)
+    t_rk = ctx.timed(rec_keys, 10)
+    t_rv = ctx.timed(rec_values, 10)
+    t_step = ctx.timed(step, 5)
     subvecs = w.heads * w.n * 16
     flops_plain = 2.0 * subvecs * w.c * 8  # the sub-vector contraction, 2 k sub_dim per sub-vector
     acc = kv.pq_accounting(w.n, w.heads, 128, 8, 8)
@@ -644,8 +649,8 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
     # codebooks of the layer workload (8 x 32768 bf16 keys, k = 1024), and the pages' shared
     # sub-vector codebook (k = 256, sub_dim 8) over the same keys pooled as 4.2M sub-vectors.
     wl = W["layer"]
-    kl = keys_dev(synth.keys(wl.cfg, wl.heads, wl.n, "bf16"))
-    _, ll = kv.calibrate(f32(synth.queries(wl.cfg, wl.heads, wl.m)), 1e-4)
+    kl = ctx.keys_dev(synth.keys(wl.cfg, wl.heads, wl.n, "bf16"))
+    _, ll = kv.calibrate(ctx.f32(synth.queries(wl.cfg, wl.heads, wl.m)), 1e-4)
     cb_init = kl[:, ::wl.n // wl.c][:, :wl.c].float().contiguous()
     cbw = cb_init.clone()
     sub_x = kd.reshape(-1, 8)
@@ -663,9 +668,9 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
     train_whole()
     train_sub()
     torch.cuda.synchronize()
-    t_w = timed(train_whole, 3)
-    t_s = timed(train_sub, 3)
-    pr_w = profile(train_whole, 1)
+    t_w = ctx.timed(train_whole, 3)
+    t_s = ctx.timed(train_sub, 3)
+    pr_w = ctx.profile(train_whole, 1)
     res["kmeans"] = {
         "workload": "5 Lloyd rounds + final assignment, H-weighted: 8 heads x 32768 bf16 keys with "
                     "k=1024 per head; 4.2M pooled sub-vectors (sub_dim 8) with one k=256 codebook",
@@ -677,35 +682,275 @@ def extra_workloads(torch, kv, synth, dev, keys_dev, f32, profile):
     return res
 
 
-def cpu_baseline(w, keys, synth):
-    """The oracle (as it stands) on a bounded sample of the headline step: whole heads of the
-    layer workload, each running split, plain encode of the bulk rows, H-weighted encode of
-    the retrieval rows and the fp64 reconstruct; as many heads as fit in about 15 s."""
+
+
+# ---------------------------------------------------------------------------- counter probes
+def probe_encode_stress(ctx):
+    e = EncodeStress(ctx)
+    for _ in range(3):
+        e.step()
+    ctx.torch.cuda.synchronize()
+
+
+def probe_long_context(ctx):
+    """The long-context split and bf16 reconstruct, three calls each."""
+    torch, kv, synth, dev = ctx.torch, ctx.kv, ctx.synth, ctx.dev
+    w = synth.WORKLOADS["long_context"]
+    kd = ctx.keys_dev(synth.keys(w.cfg, w.heads, w.n, "bf16"))
+    cbd = ctx.f32(synth.codebook(w.cfg, w.heads, w.c))
+    codes = torch.from_numpy(synth.uniform_codes(w.cfg, (1, w.heads, w.n), w.c).view(np.int16)).to(dev).view(torch.uint16)
+    pos = torch.arange(w.n, dtype=torch.int32, device=dev)[None]
+    out = torch.empty((1, w.heads, w.n, D), dtype=torch.bfloat16, device=dev)
+    proxy = kd[:, -1].contiguous()
+    for _ in range(3):
+        kv.select_retrieval(kd, proxy, w.fraction)
+    for _ in range(3):
+        kv.reconstruct(codes, pos, cbd, w.cur_pos, w.window, out=out)
+    torch.cuda.synchronize()
+
+
+def probe_decode(ctx):
+    """The decode workload's fp32 reconstruct (32 x 8 x 16384 tokens), three calls."""
+    torch, kv, synth, dev = ctx.torch, ctx.kv, ctx.synth, ctx.dev
+    w = synth.WORKLOADS["decode"]
+    cbd = ctx.f32(synth.codebook(w.cfg, w.heads, w.c))
+    codes = torch.from_numpy(synth.uniform_codes(w.cfg, (w.batch, w.heads, w.n), w.c).view(np.int16)).to(dev).view(torch.uint16)
+    pos = torch.arange(w.n, dtype=torch.int32, device=dev)[None].repeat(w.batch, 1).contiguous()
+    out = torch.empty((w.batch, w.heads, w.n, D), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        kv.reconstruct(codes, pos, cbd, w.cur_pos, w.window, out=out)
+    torch.cuda.synchronize()
+
+
+PROBES = {"encode_stress": probe_encode_stress, "long_context": probe_long_context,
+          "decode": probe_decode}
+
+
+def _algorithmic():
+    """Per kernel and workload: (kernel-name pattern, what it is, algorithmic bytes per launch,
+    algorithmic flops per launch or None, source file).  Bytes count what the method must move:
+    encode, keys (bf16) + codes + distances + the fp16 codebook fragments and bias of every
+    head once; split, keys + one index per key; reconstruct, codes + positions + output + the
+    codebook of every head once."""
+    enc = 8 * 131072 * (D * 2 + 2 + 4) + 8 * 4096 * (D * 2 + 4)
+    split = 8 * 131072 * (D * 2 + 4)
+    rec_lc = 8 * 131072 * (2 + D * 2) + 131072 * 4 + 8 * 2048 * D * 4
+    rec_dec = 32 * 8 * 16384 * (2 + D * 4) + 32 * 16384 * 4 + 8 * 1024 * D * 4
+    return {
+        ("encode_stress", "enc_coarse"): ("the MFMA pass of the H-weighted encode with distances",
+                                          enc, 2.0 * 8 * 131072 * 4096 * D, "kv_cache_vector_windowed_amd/csrc/encode.hip"),
+        ("long_context", "sel_"): ("the five kernels of the retrieval split, per call", split, None,
+                                   "kv_cache_vector_windowed_amd/csrc/select.hip"),
+        ("long_context", "rope_gather"): ("the bf16 reconstruct gather", rec_lc, None,
+                                          "kv_cache_vector_windowed_amd/csrc/reconstruct.hip"),
+        ("decode", "rope_gather"): ("the fp32 reconstruct gather", rec_dec, None,
+                                    "kv_cache_vector_windowed_amd/csrc/reconstruct.hip"),
+    }
+
+
+def _pmc_dispatches(d):
+    """[(kernel name, dispatch id, {counter: value summed over instances})] of one pass."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % d)
+    disp = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                k = (f, r["Dispatch_Id"])
+                name, vals = disp.setdefault(k, (r["Kernel_Name"], {}))
+                vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [(name, k[1], vals) for k, (name, vals) in sorted(disp.items(), key=lambda kv_: int(kv_[0][1]))]
+
+
+def _median(v):
+    v = sorted(v)
+    return v[len(v) // 2] if v else None
+
+
+def pmc_summarize(root, command):
+    """Every pass under root/<workload>_<pass>/: per kernel of interest, the median per launch
+    of every counter; HBM bytes = FETCH_SIZE and WRITE_SIZE (KiB) scaled by what the same
+    counter reads for the reference copy (reads and writes COPY_REF_BYTES)."""
+    alg = _algorithmic()
+    passes = sorted(p for p in os.listdir(root) if os.path.isdir(os.path.join(root, p)))
+    by_wl = {}
+    for p in passes:
+        wl, _, tag = p.rpartition("_")
+        by_wl.setdefault(wl, []).append((tag, os.path.join(root, p)))
+    written = []
+    for (wl, pat), (what, abytes, aflops, src) in alg.items():
+        if wl not in by_wl:
+            continue
+        counters, scales = {}, {}
+        for tag, d in by_wl[wl]:
+            rows = _pmc_dispatches(d)
+            ref = [v for n, _, v in rows if "neg" in n.lower()]
+            # one launch = all dispatches of the pattern between two calls: the split is five
+            # kernels, summed per call (calls follow each other, three of them)
+            mine = [(n, v) for n, _, v in rows if pat in n]
+            if not mine:
+                continue
+            per_call = {}
+            if pat == "sel_":
+                names = []
+                for n, _ in mine:
+                    if n not in names:
+                        names.append(n)
+                calls = len(mine) // len(names)
+                for c in range(calls):
+                    chunk = mine[c * len(names):(c + 1) * len(names)]
+                    for n, v in chunk:
+                        for cn, cv in v.items():
+                            per_call.setdefault(cn, [0.0] * calls)[c] += cv
+            else:
+                for n, v in mine:
+                    for cn, cv in v.items():
+                        per_call.setdefault(cn, []).append(cv)
+            for cn, vals in per_call.items():
+                counters[cn] = _median(vals)
+                if cn in ("FETCH_SIZE", "WRITE_SIZE") and ref:
+                    rv = _median([r[cn] for r in ref if cn in r])
+                    if rv:
+                        scales[cn] = (COPY_REF_BYTES / 1024.0) / rv
+        if not counters:
+            continue
+        out = {"kernel": pat, "workload": wl, "what": what, "source": src,
+               "source_sha": sha_of(os.path.join(ROOT, src)), "counters_per_launch": counters,
+               "reference_scale": scales, "algorithmic_bytes_per_launch": abytes,
+               "algorithmic_flops_per_launch": aflops, "command": command}
+        hbm = 0.0
+        have = True
+        for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+            if cn in counters and cn in scales:
+                b = counters[cn] * 1024.0 * scales[cn]
+                out[cn.lower() + "_bytes"] = round(b)
+                hbm += b
+            else:
+                have = False
+        out["hbm_bytes_per_launch"] = round(hbm) if have else None
+        if have:
+            out["hbm_over_algorithmic"] = round(hbm / abytes, 4)
+        if "SQ_INSTS_MFMA" in counters and aflops:
+            # v_mfma_f32_32x32x16_f16: 32 x 32 x 16 multiply-adds per wave instruction
+            out["mfma_insts_algorithmic"] = aflops / (2 * 32 * 32 * 16)
+            out["mfma_insts_over_algorithmic"] = round(counters["SQ_INSTS_MFMA"] / out["mfma_insts_algorithmic"], 4)
+        name = "%s_%s_pmc" % (pat.strip("_") if pat != "sel_" else "select", wl)
+        base = os.path.join(ROOT, "profiles", name)
+        with open(base + ".json", "w") as f:
+            json.dump(out, f, indent=1)
+        with open(base + ".md", "w") as f:
+            f.write("# %s, %s workload: counters per launch\n\n%s.\n\n" % (pat, wl, what))
+            f.write("Command (rocprofv3 --pmc passes, one counter group each, then the summary):\n\n"
+                    "```\n%s\n```\n\n" % command)
+            f.write("| counter | median per launch |\n|---|---|\n")
+            for cn in sorted(counters):
+                f.write("| %s | %.6g |\n" % (cn, counters[cn]))
+            if scales:
+                f.write("\nReference copy (%d MiB read + %d MiB written): scale per counter %s.\n"
+                        % (COPY_REF_BYTES >> 20, COPY_REF_BYTES >> 20,
+                           ", ".join("%s %.4f" % kv_ for kv_ in scales.items())))
+            if out["hbm_bytes_per_launch"]:
+                f.write("\nHBM bytes per launch %.6g (fetch %.6g, write %.6g) against %.6g "
+                        "algorithmic: %.3f x.\n" % (out["hbm_bytes_per_launch"], out["fetch_size_bytes"],
+                                                   out["write_size_bytes"], abytes,
+                                                   out["hbm_over_algorithmic"]))
+            if "mfma_insts_over_algorithmic" in out:
+                f.write("\nMFMA instructions %.6g against %.6g for the algorithmic 2NCd flop: %.4f x.\n"
+                        % (counters["SQ_INSTS_MFMA"], out["mfma_insts_algorithmic"],
+                           out["mfma_insts_over_algorithmic"]))
+            f.write("\nSource %s @ %s.\n" % (src, out["source_sha"]))
+        written.append(base + ".json")
+    print(json.dumps({"written": written}))
+
+
+def trace_summarize(root, command):
+    """Kernel statistics of a rocprofv3 --kernel-trace --stats run of the headline, read from
+    the rocpd database it writes: calls, mean / min / max duration and registers per kernel."""
+    import sqlite3
+
+    dbs = glob.glob(os.path.join(root, "**", "*.db"), recursive=True)
+    if not dbs:
+        raise SystemExit("no rocpd database under %s" % root)
+    con = sqlite3.connect(dbs[0])
+    rows = con.execute(
+        "select name, count(*), avg(duration), min(duration), max(duration), sum(duration), "
+        "max(vgpr_count), max(accum_vgpr_count), max(sgpr_count), max(lds_size), "
+        "max(grid_x), max(workgroup_x) from kernels group by name").fetchall()
+    total = sum(r[5] for r in rows)
+    rows.sort(key=lambda r: -r[5])
+
+    def short(name):
+        for pre in ("void ", "a2ats::(anonymous namespace)::"):
+            name = name.replace(pre, "")
+        if name.startswith("_ZN5a2ats12_GLOBAL__N_1"):  # mangled: keep the kernel's own name
+            rest = name[len("_ZN5a2ats12_GLOBAL__N_1"):]
+            k = 0
+            while k < len(rest) and rest[k].isdigit():
+                k += 1
+            ln = int(rest[:k])
+            tmpl = rest[k + ln:]
+            name = rest[k:k + ln] + ("<" + tmpl[1:tmpl.index("EE") + 1] + ">" if tmpl.startswith("I") else "")
+        return name.split("(")[0][:80]
+
+    path = os.path.join(ROOT, "profiles", "encode_stress_trace.md")
+    with open(path, "w") as f:
+        f.write("# encode_stress headline: kernel trace statistics\n\n"
+                "Command:\n\n```\n%s\n```\n\n" % command)
+        f.write("| kernel | calls | average us | min us | max us | share % | VGPR | AGPR | SGPR | LDS B | grid | block |\n"
+                "|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+        for r in rows:
+            f.write("| %s | %d | %.2f | %.2f | %.2f | %.2f | %s | %s | %s | %s | %s | %s |\n" % (
+                short(r[0]), r[1], r[2] / 1e3, r[3] / 1e3, r[4] / 1e3, 100.0 * r[5] / total,
+                r[6], r[7], r[8], r[9], r[10], r[11]))
+    print(json.dumps({"written": path}))
+
+
+def traffic_from_profiles(kernel, workload):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken on
+    the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", "%s_%s_pmc.json" % (kernel, workload))
+    if not os.path.exists(p):
+        return None
+    try:
+        with open(p) as f:
+            d = json.load(f)
+        if sha_of(os.path.join(ROOT, d["source"])) != d["source_sha"]:
+            return None
+        return d["hbm_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(synth):
+    """The oracle (as it stands) on a bounded sample of the headline workload: the H-weighted
+    assignment with distances of the first rows of every head (fp64, z-space form), as many
+    1024-row blocks per head as fit in about 15 s."""
     import oracle
 
+    w = synth.WORKLOADS["encode_stress"]
     log("cpu baseline (oracle)")
+    rows = 32768
+    keys = synth.keys(w.cfg, w.heads, rows, "bf16")  # the first rows of every head
     cb = synth.codebook(w.cfg, w.heads, w.c)
     q = synth.queries(w.cfg, w.heads, w.m)
     _, L = oracle.calibrate(q, 1e-4)
     done = 0
     t0 = time.perf_counter()
-    for h in range(w.heads):
-        x = keys.values[h]
-        ret, bulk, _ = oracle.select_retrieval(x, x[-1], w.fraction)
-        code = np.zeros(w.n, dtype=np.int32)
-        code[bulk], _, _ = oracle.assign_h(x[bulk], cb[h], None)
-        code[ret], _, _ = oracle.assign_h(x[ret], cb[h], L[h])
-        oracle.reconstruct(code.astype(np.uint16), np.arange(w.n, dtype=np.int32), cb[h],
-                           w.cur_pos, w.window)
-        done += 1
+    blk = 0
+    while blk * 1024 < rows:
+        for h in range(w.heads):
+            oracle.assign_h(keys.values[h, blk * 1024:(blk + 1) * 1024], cb[h], L[h])
+            done += 1024
+        blk += 1
         if time.perf_counter() - t0 > 15.0:
             break
     dt = time.perf_counter() - t0
-    return {"value": round(done * w.n / dt, 1), "unit": "keys/s", "cores": oracle.threads(),
+    return {"value": round(done / dt, 1), "unit": "keys/s", "cores": oracle.threads(),
             "kind": "oracle",
-            "sample": "%d of %d heads of the layer step (%d keys each): split, plain encode of "
-                      "bulk rows, H-weighted encode of retrieval rows, reconstruct; %.1f s"
-                      % (done, w.heads, w.n, dt)}
+            "sample": "%d keys (the first %d rows of each of the 8 heads) of the encode_stress "
+                      "workload: H-weighted assignment with distances against C=4096, fp64; "
+                      "%.1f s" % (done, done // w.heads, dt)}
 
 
 if __name__ == "__main__":

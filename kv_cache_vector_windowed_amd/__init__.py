@@ -148,13 +148,16 @@ def calibrate(queries: torch.Tensor, ridge: float = 1e-4):
 
 def encode(keys: torch.Tensor, codebook: torch.Tensor, chol: torch.Tensor | None = None,
            idx: torch.Tensor | None = None, codes: torch.Tensor | None = None,
-           want_dist: bool = False, stats: torch.Tensor | None = None):
+           want_dist: bool = False, stats: torch.Tensor | None = None,
+           dist: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """Nearest-centroid codes under H = L L^T (plain when chol is None).
 
     keys [heads, n, d] fp32/bf16, codebook [heads, c, d] fp32, chol [heads, d, d] fp32,
     idx [heads, n_idx] int32 rows to encode (others of `codes` untouched), codes [heads, n]
     uint16 to write into (allocated when None).  Returns codes, or (codes, dist) with
-    want_dist.  stats: optional int32 tensor of 8 elements receiving a2ats_encode_stats.
+    want_dist (dist [heads, n] fp32 is written into `dist` when given).  stats: optional
+    int32 tensor of 8 elements receiving a2ats_encode_stats.  workspace: an optional uint8
+    device tensor of at least encode_workspace_bytes() bytes (allocated when None).
     """
     _dev(keys, "keys")
     _dev(codebook, "codebook")
@@ -176,10 +179,22 @@ def encode(keys: torch.Tensor, codebook: torch.Tensor, chol: torch.Tensor | None
         codes = torch.zeros((heads, n), dtype=torch.uint16, device=keys.device)
     else:
         _dev(codes, "codes")
-    dist = torch.zeros((heads, n), dtype=torch.float32, device=keys.device) if want_dist else None
+    if dist is not None:
+        _dev(dist, "dist")
+        if dist.dtype != torch.float32 or dist.shape != (heads, n):
+            raise ValueError("dist must be [heads, n] float32")
+        want_dist = True
+    elif want_dist:
+        dist = torch.zeros((heads, n), dtype=torch.float32, device=keys.device)
     if stats is not None:
         _dev(stats, "stats")
-    ws = _workspace(lib().a2ats_encode_workspace(heads, n, d, c), keys.device)
+    need = lib().a2ats_encode_workspace(heads, n, d, c)
+    if workspace is None:
+        ws = _workspace(need, keys.device)
+    else:
+        ws = _dev(workspace, "workspace")
+        if ws.dtype != torch.uint8 or ws.numel() < need:
+            raise ValueError("workspace must be uint8 with at least %d bytes" % need)
     _check(lib().a2ats_encode(_ptr(keys), _dtype_code(keys), heads, n, d, _ptr(idx), n_idx,
                               _ptr(codebook), c, _ptr(chol), _ptr(codes), _ptr(dist),
                               _ptr(stats), _ptr(ws), ws.numel(), _stream(keys.device)), "encode")
@@ -219,9 +234,14 @@ def encode_prepare(codebook: torch.Tensor, chol: torch.Tensor | None, n: int) ->
     return PreparedCodebook(codebook, chol, n)
 
 
+def encode_workspace_bytes(heads: int, n: int, c: int, d: int = HEAD_DIM) -> int:
+    """Bytes of the caller workspace that encode() needs for these sizes."""
+    return int(lib().a2ats_encode_workspace(heads, n, d, c))
+
+
 def encode_prepared(keys: torch.Tensor, prep: PreparedCodebook, idx: torch.Tensor | None = None,
                     codes: torch.Tensor | None = None, want_dist: bool = False,
-                    stats: torch.Tensor | None = None):
+                    stats: torch.Tensor | None = None, dist: torch.Tensor | None = None):
     """Key side of encode with a prepared codebook (keys [heads, n, d], n == prep.n); the
     other arguments and the result as for encode()."""
     _dev(keys, "keys")
@@ -238,7 +258,13 @@ def encode_prepared(keys: torch.Tensor, prep: PreparedCodebook, idx: torch.Tenso
         codes = torch.zeros((heads, n), dtype=torch.uint16, device=keys.device)
     else:
         _dev(codes, "codes")
-    dist = torch.zeros((heads, n), dtype=torch.float32, device=keys.device) if want_dist else None
+    if dist is not None:
+        _dev(dist, "dist")
+        if dist.dtype != torch.float32 or dist.shape != (heads, n):
+            raise ValueError("dist must be [heads, n] float32")
+        want_dist = True
+    elif want_dist:
+        dist = torch.zeros((heads, n), dtype=torch.float32, device=keys.device)
     if stats is not None:
         _dev(stats, "stats")
     _check(lib().a2ats_encode_prepared(_ptr(keys), _dtype_code(keys), heads, n, d, _ptr(idx), n_idx,
