@@ -16,8 +16,8 @@
 //   rope_gather  HBM-write-bound stream: each thread owns a fixed group of P pairs of the
 //                head dimension (P = 4 for fp32 output, 8 for bf16, so every store is 16 B),
 //                takes the far row's cos/sin for its pairs from a copy the workgroup stages
-//                in LDS, gathers the centroid from L2, rotates (fp64 for fp32 output, fp32
-//                for bf16 output), rounds once, and writes with non-temporal stores.  Work
+//                in LDS, gathers the centroid from L2, rotates in fp64, rounds once to the
+//                output type, and writes with non-temporal stores.  Work
 //                items are (batch, head, 64-token chunk); item k has head k % heads and the
 //                grid is a multiple of 8 * heads, so a workgroup always serves one head and,
 //                with 8 heads, each XCD (workgroups are dealt round-robin over the 8 XCDs)
@@ -103,22 +103,51 @@ __device__ __forceinline__ void rotate_pairs(const float (&xl)[P], const float (
   }
 }
 
+// Moves y = fp32(x) one fp32 unit toward x when y lies exactly halfway between two bf16
+// values while x does not.  Only there can the nearest-even rounding of y to bf16 differ
+// from that of x: a bf16 midpoint is itself an fp32 value, so x below (above) a midpoint
+// gives y at or below (above) it, and y equal to the midpoint only in this case.
+__device__ __forceinline__ float bf16_tie_fix(double x, float y) {
+  const unsigned b = __float_as_uint(y);
+  if ((b & 0xFFFFu) != 0x8000u || (double)y == x) return y;
+  return __uint_as_float(fabs(x) > fabs((double)y) ? b + 1u : b - 1u);
+}
+
 // P pairs of one row, rounded once, as two 16-byte non-temporal stores (low half at pair
-// i0, high half at i0 + d/2).
-template <bool BF16, typename real, int P>
-__device__ __forceinline__ void store_pairs(void* out, int64_t ooff, const real (&lo)[P],
-                                            const real (&hi)[P]) {
+// i0, high half at i0 + d/2).  bf16: the fp32 roundings of the fp64 values are rounded to
+// bf16 (nearest even); the rare fp32 value on a bf16 midpoint is corrected first (one
+// branch per thread for all 2P values), so the result is the single nearest-even rounding
+// of the fp64 value.
+template <bool BF16, int P>
+__device__ __forceinline__ void store_pairs(void* out, int64_t ooff, const double (&lo)[P],
+                                            const double (&hi)[P]) {
   if constexpr (BF16) {
     static_assert(P == 8, "bf16 rows: 8 pairs per thread");
+    float fl[P], fh[P];
+    bool tie = false;
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      fl[k] = (float)lo[k];
+      fh[k] = (float)hi[k];
+      tie |= (__float_as_uint(fl[k]) & 0xFFFFu) == 0x8000u;
+      tie |= (__float_as_uint(fh[k]) & 0xFFFFu) == 0x8000u;
+    }
+    if (__builtin_expect(tie, 0)) {
+#pragma unroll
+      for (int k = 0; k < P; ++k) {
+        fl[k] = bf16_tie_fix(lo[k], fl[k]);
+        fh[k] = bf16_tie_fix(hi[k], fh[k]);
+      }
+    }
     u4 a, bb;
-    a.x = pack_bf16x2((float)lo[0], (float)lo[1]);
-    a.y = pack_bf16x2((float)lo[2], (float)lo[3]);
-    a.z = pack_bf16x2((float)lo[4], (float)lo[5]);
-    a.w = pack_bf16x2((float)lo[6], (float)lo[7]);
-    bb.x = pack_bf16x2((float)hi[0], (float)hi[1]);
-    bb.y = pack_bf16x2((float)hi[2], (float)hi[3]);
-    bb.z = pack_bf16x2((float)hi[4], (float)hi[5]);
-    bb.w = pack_bf16x2((float)hi[6], (float)hi[7]);
+    a.x = pack_bf16x2(fl[0], fl[1]);
+    a.y = pack_bf16x2(fl[2], fl[3]);
+    a.z = pack_bf16x2(fl[4], fl[5]);
+    a.w = pack_bf16x2(fl[6], fl[7]);
+    bb.x = pack_bf16x2(fh[0], fh[1]);
+    bb.y = pack_bf16x2(fh[2], fh[3]);
+    bb.z = pack_bf16x2(fh[4], fh[5]);
+    bb.w = pack_bf16x2(fh[6], fh[7]);
     uint16_t* o = static_cast<uint16_t*>(out) + ooff;
     __builtin_nontemporal_store(a, reinterpret_cast<u4*>(o));
     __builtin_nontemporal_store(bb, reinterpret_cast<u4*>(o + kHalf));
@@ -145,11 +174,10 @@ __device__ __forceinline__ void load_pairs(const float* x, float (&xl)[P], float
   }
 }
 
-// fp32 output: 4 pairs per thread, rotation in fp64, one rounding, two 16-byte stores.
-// bf16 output: 8 pairs per thread, rotation in fp32 and one rounding to bf16; the result lies
-// within one bf16 unit of the single rounding of the exact value.  Both rotations are written
-// as one product and one fused multiply-add, so the rounding steps do not depend on how the
-// compiler contracts the expression.
+// fp32 output: 4 pairs per thread; bf16 output: 8 pairs per thread (16-byte stores).  The
+// rotation is fp64 for both, written as one product and one fused multiply-add (so the
+// rounding steps do not depend on how the compiler contracts the expression), and rounded
+// once to the output type.
 // Each thread handles U tokens of a chunk at once.  The codes and positions of the
 // workgroup's next chunk are fetched before the current chunk's centroids are gathered,
 // rotated and stored, so the dependent loads of one chunk overlap the work of the previous.
@@ -163,7 +191,7 @@ __global__ __launch_bounds__(256) void rope_gather(
   constexpr int TOK = 256 / TPT;         // tokens per pass of the workgroup
   constexpr int CH = BF16 ? kChunkBf16 : kChunkF32;
   constexpr int U = CH / TOK;            // tokens per thread per chunk
-  using real = typename std::conditional<BF16, float, double>::type;
+  using real = double;
   const int t = threadIdx.x;
   const int g = t % TPT;                 // pair group: pairs [g*P, g*P + P)
   const int tk = t / TPT;
@@ -242,7 +270,7 @@ __global__ __launch_bounds__(256) void rope_gather(
         }
         rotate_pairs<real, P>(xl[u], xh[u], cs, sn, lo, hi);
       }
-      store_pairs<BF16, real, P>(out, ooff, lo, hi);
+      store_pairs<BF16, P>(out, ooff, lo, hi);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -271,7 +299,7 @@ __global__ __launch_bounds__(256) void pq_gather(
   constexpr int M = kD / SUB;   // codes per token
   constexpr int NW = M / 4;     // 32-bit words of a code row (4 for SUB 8, 8 for SUB 4)
   static_assert(SUB % 4 == 0 && M % 16 == 0, "code rows of whole 16-byte vectors");
-  using real = typename std::conditional<BF16, float, double>::type;
+  using real = double;
   const int t = threadIdx.x;
   const int g = t % TPT;
   const int tk = t / TPT;
@@ -360,7 +388,7 @@ __global__ __launch_bounds__(256) void pq_gather(
         }
         rotate_pairs<real, P>(xl, xh, cs, sn, lo, hi);
       }
-      store_pairs<BF16, real, P>(out, ooff, lo, hi);
+      store_pairs<BF16, P>(out, ooff, lo, hi);
     }
   }
 }
@@ -380,7 +408,7 @@ __global__ __launch_bounds__(256) void rope_update(
   constexpr int P = BF16 ? 8 : 4;
   constexpr int TPT = kHalf / P;
   constexpr int TOK = 256 / TPT;
-  using real = typename std::conditional<BF16, float, double>::type;
+  using real = double;
   __shared__ int s_tok[256];
   __shared__ int s_pos[256];
   __shared__ unsigned s_n;
@@ -445,7 +473,7 @@ __global__ __launch_bounds__(256) void rope_update(
       }
       rotate_pairs<real, P>(xl, xh, cs, sn, lo, hi);
     }
-    store_pairs<BF16, real, P>(out, ooff, lo, hi);
+    store_pairs<BF16, P>(out, ooff, lo, hi);
   }
 }
 

@@ -8,6 +8,12 @@ Comparison rules (the oracle is fp64; each bound covers the GPU path's own round
              the n_r-th place; both outputs ascending and together a cover of 0..n-1
   rotation   fp32: |gpu - ref| <= 1e-5 + 2^-21 (|x_i| + |x_partner|)
              bf16: |gpu - ref| <= 2e-2 |ref| + 2^-21 (|x_i| + |x_partner|)
+             and both: bit-exact equality with the single nearest-even rounding of the
+             oracle's fp64 value, except where that value lies within
+             delta = (pmax 2^-51 + 2^-50)(|x_i| + |x_partner|) of a rounding midpoint (the two
+             sides' fp64 angles p theta come from different pow / cos / sin implementations,
+             each within an ulp or two of the exact function, for |p| <= pmax); there the GPU
+             value must be one of the two values next to that midpoint
 """
 import numpy as np
 import torch
@@ -76,8 +82,43 @@ def check_split(ret, bulk, n, cosv, oracle_ret, what=""):
     return int(diff.size)
 
 
-def check_rotation(gpu, ref, src, dtype, what=""):
-    """gpu: fp32 values (bf16 widened), ref: fp64 oracle, src: the fp64 pre-RoPE rows."""
+def check_rounded_once(gpu, ref, mag, dtype, pmax=2 ** 18, what=""):
+    """gpu: fp32 values (bf16 outputs widened, which is exact), ref: the oracle's fp64 values,
+    mag: |x_i| + |x_partner| per element.  Returns the number of elements inside the band."""
+    g32 = np.ascontiguousarray(gpu, dtype=np.float32)
+    ref = np.asarray(ref, dtype=np.float64)
+    nan_g, nan_r = np.isnan(g32), np.isnan(ref)
+    assert np.array_equal(nan_g, nan_r), "%s: NaN rows differ" % what
+    if dtype == "bf16":
+        gb = synth.f32_to_bf16_bits(g32).astype(np.int64)
+        assert np.array_equal(synth.bf16_bits_to_f32(gb.astype(np.uint16)).view(np.uint32),
+                              g32.view(np.uint32)), "%s: not bf16 values" % what
+        import oracle
+        wb = oracle.round_bf16(np.where(nan_r, 0.0, ref)).astype(np.int64)
+        wv = synth.bf16_bits_to_f32(wb.astype(np.uint16)).astype(np.float64)
+    else:
+        gb = g32.view(np.uint32).astype(np.int64)
+        w32 = np.where(nan_r, 0.0, ref).astype(np.float32)  # nearest even
+        wb = w32.view(np.uint32).astype(np.int64)
+        wv = w32.astype(np.float64)
+    bad = (gb != wb) & ~nan_r
+    if not bad.any():
+        return 0
+    delta = (pmax * 2.0 ** -51 + 2.0 ** -50) * np.asarray(mag, np.float64)
+    gv = g32.astype(np.float64)
+    adjacent = (np.abs(gb - wb) == 1) & (np.signbit(gv) == np.signbit(wv))
+    mid = 0.5 * (gv + wv)
+    ok = adjacent & (np.abs(ref - mid) <= delta)
+    worst = np.nonzero(bad & ~ok)[0] if bad.ndim == 1 else np.argwhere(bad & ~ok)
+    assert np.all(ok[bad]), "%s: %d elements are not the single rounding of the oracle's value, " \
+        "e.g. at %s: gpu %r oracle %r" % (what, int((bad & ~ok).sum()), worst[:3],
+                                          gv[bad & ~ok][:3], ref[bad & ~ok][:3])
+    return int(bad.sum())
+
+
+def check_rotation(gpu, ref, src, dtype, what="", pmax=2 ** 18):
+    """gpu: fp32 values (bf16 widened), ref: fp64 oracle, src: the fp64 pre-RoPE rows.  The
+    tolerance rule, then the single-rounding rule (check_rounded_once)."""
     gpu = np.asarray(gpu, dtype=np.float64)
     h = src.shape[-1] // 2
     partner = np.concatenate([src[..., h:], src[..., :h]], axis=-1)
@@ -86,7 +127,9 @@ def check_rotation(gpu, ref, src, dtype, what=""):
         tol = 1e-5 + 2.0 ** -21 * mag
     else:
         tol = 2e-2 * np.abs(ref) + 2.0 ** -21 * mag
-    err = np.abs(gpu - ref)
+    nan = np.isnan(ref)
+    err = np.where(nan, 0.0, np.abs(gpu - ref))
     ok = err <= tol
     assert np.all(ok), "%s: %d elements out of tolerance, max err %g" % (what, (~ok).sum(), err.max())
+    check_rounded_once(gpu, ref, mag, dtype, pmax, what)
     return float(err.max()), int((err > 1e-5).sum())

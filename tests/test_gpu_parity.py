@@ -12,7 +12,8 @@ import kv_cache_vector_windowed_amd as kv
 import oracle
 from kv_cache_vector_windowed_amd import synth
 
-from parity import (DEV, bf16_to_np_bits, check_codes, check_dist, check_rotation, check_split,
+from parity import (DEV, bf16_to_np_bits, check_codes, check_dist, check_rotation,
+                    check_rounded_once, check_split,
                     f32_to_dev, keys_to_dev, u16_to_dev, u16_to_np)
 
 pytestmark = pytest.mark.gpu
@@ -31,7 +32,7 @@ def z2_of(x, l):
 
 # ====================================================================== calibrate
 class TestCalibrate:
-    @pytest.mark.parametrize("name", ["tiny", "layer"])
+    @pytest.mark.parametrize("name", ["tiny", "layer", "encode_stress"])
     def test_workload(self, name):
         w = W[name]
         q = synth.queries(w.cfg, w.heads, w.m)
@@ -113,8 +114,26 @@ class TestEncode:
         print("layer tie rate %.2e stats %s" % (tie, st[:5]))
 
     def test_encode_stress_sampled(self):
-        tie, st = run_encode("encode_stress", n_sample=192)
+        # 4096 of the 131072 rows of every head: at the measured ~1.2% rescan rate about 50
+        # keys a head that went through the rescan
+        tie, st = run_encode("encode_stress", n_sample=4096)
         print("encode_stress tie rate %.2e stats %s" % (tie, st[:5]))
+
+    @pytest.mark.parametrize("c", [4097, 16384, 65536])
+    @pytest.mark.parametrize("use_h", [False, True])
+    def test_large_codebooks(self, c, use_h):
+        # C beyond the workloads' 4096 up to the uint16 limit: the tile index packed into the
+        # scores' low bits widens (13 bits at 65536), so the packing slack grows and more
+        # keys go to the rerank, the rescan, candidate-list overflow and the full scan;
+        # every row is checked, with distances and the decision counts
+        w = synth.Workload("bigc", 160 + c % 89, 2, 700, c, "bf16", m=512)
+        tie, st = run_encode(w, use_h=use_h)
+        print("C=%d use_h=%s tie rate %.2e stats %s" % (c, use_h, tie, st[:5]))
+
+    def test_large_codebook_fp32_keys(self):
+        w = synth.Workload("bigc32", 171, 1, 900, 4097, "f32", m=512)
+        tie, st = run_encode(w, use_h=True)
+        print("C=4097 fp32 keys tie rate %.2e stats %s" % (tie, st[:5]))
 
     def test_single_centroid_and_duplicate_centroids(self):
         keys = synth.keys(120, 2, 300, "f32")
@@ -345,6 +364,21 @@ class TestSelectRetrieval:
         nr = oracle.retrieval_count(n, f)
         assert np.array_equal(ret.cpu().numpy()[0], np.arange(nr))
 
+    def test_one_head_beyond_lds_offsets(self):
+        # more than 4096 blocks of 1024 scores in one head (n > 4,194,304): the threshold pass
+        # takes the candidates' block offsets from global memory instead of LDS
+        n = 4_194_304 + 300_001
+        rng = np.random.default_rng(77)
+        x = rng.standard_normal((1, n, 128), dtype=np.float32)
+        bits = synth.f32_to_bf16_bits(x)
+        del x
+        vals = synth.bf16_bits_to_f32(bits)
+        kd = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+        ret, bulk = kv.select_retrieval(kd, kd[:, -1].contiguous(), 0.05)
+        ro, _, cosv = oracle.select_retrieval(vals[0], vals[0, -1], 0.05)
+        near = check_split(ret.cpu().numpy()[0], bulk.cpu().numpy()[0], n, cosv, ro, "4.5M keys")
+        print("one head of %d keys: %d indices inside the tie band" % (n, near))
+
     def test_degenerate_long(self):
         # every key identical beyond the one-workgroup size: all ties, lowest indices win
         keys = synth.keys(144, 1, 40000, "f32")
@@ -411,11 +445,8 @@ class TestReconstruct:
         for hh in range(w.heads):
             got = bf16_to_np_bits(out[0, hh, torch.from_numpy(t).to(DEV)])
             ref = oracle_rows(codes[0, hh, t], pos[0, t], cb[hh], w.cur_pos, w.window, w.far_b, 0)
-            ref_bits = oracle.round_bf16(ref)
-            mism = (got != ref_bits).mean()
             check_rotation(synth.bf16_bits_to_f32(got), ref, cb[hh][codes[0, hh, t]].astype(np.float64),
                            "bf16", "long_context head %d" % hh)
-            assert mism < 1e-3, mism  # rounding once from fp64 on both sides
 
     @pytest.mark.parametrize("window,far_mode,far_b", [(0, 0, 2048), (-5, 1, 2048), (10 ** 9, 0, 2048),
                                                        (300, 1, 0), (300, 0, 77), (1, 0, 5000)])
@@ -473,15 +504,12 @@ class TestFarQueryRope:
         odt = torch.float32 if dt_out == "f32" else torch.bfloat16
         got = widen(kv.far_query_rope(xd, b, out_dtype=odt))
         ref = oracle.rope_at(x.astype(np.float64), b)
-        # fp64 rotation rounded once: within one unit of the output format, and exact
-        # (nearest) for nearly every element
+        # fp64 rotation rounded once: within one unit of the output format, and the single
+        # nearest-even rounding of the oracle's value outside the angle band
         err = np.abs(got - ref)
         assert np.all(err <= ulp(ref, dt_out)), err.max()
-        if dt_out == "bf16":
-            exact = (synth.f32_to_bf16_bits(got.astype(np.float32)) == oracle.round_bf16(ref)).mean()
-        else:
-            exact = (got == ref.astype(np.float32).astype(np.float64)).mean()
-        assert exact > 0.999, exact
+        mag = np.abs(x) + np.abs(np.concatenate([x[:, 64:], x[:, :64]], axis=1))
+        check_rounded_once(got, ref, mag.astype(np.float64), dt_out, abs(b) + 1, "far query rope")
 
     def test_in_place_and_batched_shape(self):
         rng = np.random.default_rng(3)
@@ -686,9 +714,6 @@ class TestPQ:
                 if out_dtype == "f32":
                     check_rotation(out[bb, h].cpu().numpy(), ref, full, "f32", "pq %d %d" % (bb, h))
                 else:
-                    gotb = bf16_to_np_bits(out[bb, h])
-                    mism = (gotb != oracle.round_bf16(ref)).mean()
-                    assert mism < 0.01, mism
                     check_rotation(out[bb, h].float().cpu().numpy(), ref, full, "bf16", "pq")
 
     def test_values_are_a_plain_gather_and_invalid_codes_nan(self):
@@ -790,20 +815,38 @@ class TestKmeans:
             assert np.array_equal(got_cb[h], ref_cb.astype(np.float32))
 
     def test_lloyd_pooled_sub_vectors(self):
+        # Round by round: the GPU's assignment of the GPU's current codebook against the
+        # oracle's assignment of that same codebook (bit-exact outside the 1e-5 tie band),
+        # then the GPU's update of those codes against the oracle's update of the same codes
+        # (a cluster's members are summed in interleaved subsets: within one fp32 unit).  The
+        # driver's rounds equal the same rounds taken one call at a time, bit for bit.
         w = W["pq_layer"]
         keys = synth.keys(w.cfg, 1, 2048, "f32")
         x = np.ascontiguousarray(keys.values[0].reshape(-1, 8))  # the pages' reshape(-1, sub_dim)
         cb0 = x[::x.shape[0] // 256][:256].copy()
         q = synth.queries(w.cfg, 1, 512)
         _, lt = kv.calibrate(f32_to_dev(np.ascontiguousarray(q.reshape(1, -1, 8))), 1e-4)
-        cbd, codes = kv.kmeans(f32_to_dev(x), f32_to_dev(cb0), lt[0].contiguous(), iters=2)
-        lref = lt[0].cpu().numpy().astype(np.float64)
-        ref_cb, ref_code = oracle.kmeans(x, cb0, lref, iters=2)
-        got_code = codes.cpu().numpy()
-        # updates agree within one fp32 unit (interleaved sums), so near-ties may flip a few
-        # assignments; the codebooks stay within a tight relative band
-        assert (got_code == ref_code).mean() > 0.999
-        np.testing.assert_allclose(cbd.cpu().numpy(), ref_cb, rtol=1e-3, atol=1e-3)
+        l0 = lt[0].contiguous()
+        lref = l0.cpu().numpy().astype(np.float64)
+        xd = f32_to_dev(x)
+        cb = f32_to_dev(cb0)
+        rounds = 3
+        for r in range(rounds + 1):
+            _, codes = kv.kmeans(xd, cb.clone(), l0, iters=0)  # assignment of the current codebook
+            got_code = codes.cpu().numpy().astype(np.int64)
+            cur = cb.cpu().numpy()
+            code, d1, d2 = oracle.assign_h(x, cur, lref)
+            check_codes(got_code, code, d1, d2, "pooled round %d" % r)
+            if r == rounds:
+                break
+            new = kv.kmeans_update(xd[None], codes[None], cb[None])[0]
+            ref, _ = oracle.kmeans_update(x, got_code, cur)
+            ref32 = ref.astype(np.float32)
+            assert np.all(np.abs(new.cpu().numpy() - ref32) <= f32_ulp(ref32)), r
+            cb = new.contiguous()
+        cbd, codes = kv.kmeans(xd, f32_to_dev(cb0), l0, iters=rounds)
+        assert torch.equal(cbd, cb)
+        assert np.array_equal(codes.cpu().numpy().astype(np.int64), got_code)
         # the H-weighted objective of the trained codebook is no worse than the initial one
         _, d_init, _ = oracle.assign_h(x, cb0, lref)
         _, d_fin, _ = oracle.assign_h(x, cbd.cpu().numpy(), lref)
