@@ -49,6 +49,7 @@ extern "C" {
 #define A2ATS_EWORKSPACE (-3) /* workspace missing, too small or misaligned */
 #define A2ATS_ENOTSPD (-4)    /* calibrate: H is not positive definite */
 #define A2ATS_EHIP (-5)       /* the HIP runtime reported an error */
+#define A2ATS_ESCRATCH (-6)   /* larger than the fixed scratch of an allocation-free call */
 
 /* Element types of key / query / output arrays. */
 #define A2ATS_F32 0
@@ -236,6 +237,25 @@ int a2ats_reconstruct(const uint16_t* codes, const int32_t* positions, int64_t b
                       int64_t cur_pos, int64_t window, int64_t far_offset, int far_mode,
                       double rope_base, void* out, int out_dtype, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* reconstruct_noalloc -- a2ats_reconstruct for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * arguments, results and arithmetic are those of a2ats_reconstruct (same kernels); instead
+ * of a caller workspace the rope table lives in a fixed device array of the library,
+ * A2ATS_NOALLOC_TABLE_ROWS rows, one per GPU the library runs on, held until the process
+ * ends.  The call allocates nothing.  Requires min(max(window, 0), cur_pos + 1) + 1 <=
+ * A2ATS_NOALLOC_TABLE_ROWS (windows up to 8191 tokens), else returns A2ATS_ESCRATCH before
+ * launching anything.  The array belongs to the device that is current when the call is made
+ * (the device of `stream`); its address is looked up on that device's first call.  Every call
+ * on one GPU uses the same array: calls whose work overlaps on one GPU (concurrent streams,
+ * or host threads sharing a device) race on it and must be ordered by the caller.
+ */
+#define A2ATS_NOALLOC_TABLE_ROWS 8192
+int a2ats_reconstruct_noalloc(const uint16_t* codes, const int32_t* positions, int64_t batch,
+                              int64_t heads, int64_t n, int64_t d, const float* codebook,
+                              int64_t c, int64_t cur_pos, int64_t window, int64_t far_offset,
+                              int far_mode, double rope_base, void* out, int out_dtype,
+                              void* stream);
 
 /* reconstruct_update -- the decode-time use of far keys left unrotated ("A2ATS-adapted"
  * docs, "paper fidelity" section, Eq. 12: far keys are returned as the centroid itself).  With

@@ -25,7 +25,9 @@ LIB_PATH = os.path.join(HERE, "liba2ats.so")
 F32, BF16 = 0, 1
 FAR_FIXED_OFFSET, FAR_UNROTATED = 0, 1
 HEAD_DIM = 128
-STATUS = {0: "ok", -1: "EINVAL", -2: "EDTYPE", -3: "EWORKSPACE", -4: "ENOTSPD", -5: "EHIP"}
+STATUS = {0: "ok", -1: "EINVAL", -2: "EDTYPE", -3: "EWORKSPACE", -4: "ENOTSPD", -5: "EHIP",
+          -6: "ESCRATCH"}
+NOALLOC_TABLE_ROWS = 8192  # A2ATS_NOALLOC_TABLE_ROWS: windows up to 8191 tokens
 
 _lib = None
 
@@ -65,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.a2ats_reconstruct_workspace.restype = sz
         L.a2ats_reconstruct.argtypes = [p, p, i64, i64, i64, i64, p, i64, i64, i64, i64, i32, dbl,
                                         p, i32, p, sz, p]
+        L.a2ats_reconstruct_noalloc.argtypes = [p, p, i64, i64, i64, i64, p, i64, i64, i64, i64,
+                                                i32, dbl, p, i32, p]
         L.a2ats_reconstruct_update.argtypes = [p, p, i64, i64, i64, i64, p, i64, i64, i64, i64,
                                                i64, dbl, p, i32, p]
         L.a2ats_far_query_rope.argtypes = [p, i32, i64, i64, i64, dbl, p, i32, p]
@@ -85,7 +89,8 @@ def lib() -> ctypes.CDLL:
         L.a2ats_profile_read.argtypes, L.a2ats_profile_read.restype = [ctypes.c_char_p, sz], i64
         for f in ("a2ats_calibrate", "a2ats_encode", "a2ats_encode_prepare", "a2ats_encode_prepared",
                   "a2ats_assign_cosine",
-                  "a2ats_select_retrieval", "a2ats_reconstruct", "a2ats_reconstruct_update",
+                  "a2ats_select_retrieval", "a2ats_reconstruct", "a2ats_reconstruct_noalloc",
+                  "a2ats_reconstruct_update",
                   "a2ats_far_query_rope", "a2ats_pq_encode", "a2ats_pq_reconstruct",
                   "a2ats_kmeans_update", "a2ats_kmeans", "a2ats_topk_codes"):
             getattr(L, f).restype = i32
@@ -348,6 +353,30 @@ def reconstruct(codes: torch.Tensor, positions: torch.Tensor, codebook: torch.Te
                                    _ptr(codebook), c, int(cur_pos), int(window), int(far_offset),
                                    int(far_mode), float(rope_base), _ptr(out), _dtype_code(out),
                                    _ptr(ws), ws.numel(), _stream(codes.device)), "reconstruct")
+    return out
+
+
+def reconstruct_noalloc(codes: torch.Tensor, positions: torch.Tensor, codebook: torch.Tensor,
+                        cur_pos: int, window: int, out: torch.Tensor, far_offset: int = 2048,
+                        far_mode: int = FAR_FIXED_OFFSET, rope_base: float = 10000.0):
+    """reconstruct() into the caller's `out` without allocating device memory: the rope
+    table lives in a fixed per-GPU array of the library (min(max(window, 0), cur_pos + 1) + 1
+    <= NOALLOC_TABLE_ROWS).  Calls on one GPU whose work overlaps race on that array."""
+    _dev(codes, "codes")
+    _dev(positions, "positions")
+    _dev(codebook, "codebook")
+    _dev(out, "out")
+    batch, heads, n = codes.shape
+    c, d = codebook.shape[1], codebook.shape[2]
+    if positions.dtype != torch.int32 or positions.shape != (batch, n):
+        raise ValueError("positions must be [batch, n] int32")
+    if out.shape != (batch, heads, n, d):
+        raise ValueError("out must be [batch, heads, n, d]")
+    _check(lib().a2ats_reconstruct_noalloc(_ptr(codes), _ptr(positions), batch, heads, n, d,
+                                           _ptr(codebook), c, int(cur_pos), int(window),
+                                           int(far_offset), int(far_mode), float(rope_base),
+                                           _ptr(out), _dtype_code(out), _stream(codes.device)),
+           "reconstruct_noalloc")
     return out
 
 

@@ -51,6 +51,7 @@ const char* a2ats_strerror(int status) {
     case A2ATS_EWORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case A2ATS_ENOTSPD: return "matrix is not positive definite";
     case A2ATS_EHIP: return "HIP runtime error";
+    case A2ATS_ESCRATCH: return "larger than the fixed scratch of an allocation-free call";
     default: return "unknown status";
   }
 }

@@ -22,7 +22,7 @@
 //                grid is a multiple of 8 * heads, so a workgroup always serves one head and,
 //                with 8 heads, each XCD (workgroups are dealt round-robin over the 8 XCDs)
 //                keeps a single head's codebook in its L2.
-#include <type_traits>
+#include <mutex>
 
 #include "common.hpp"
 
@@ -520,22 +520,34 @@ extern "C" size_t a2ats_reconstruct_workspace(int64_t d, int64_t cur_pos, int64_
   return align_up((size_t)(near_rows(cur_pos, window) + 1) * kHalf * sizeof(d2));
 }
 
-extern "C" int a2ats_reconstruct(const uint16_t* codes, const int32_t* positions, int64_t batch,
-                                 int64_t heads, int64_t n, int64_t d, const float* codebook,
-                                 int64_t c, int64_t cur_pos, int64_t window, int64_t far_offset,
-                                 int far_mode, double rope_base, void* out, int out_dtype,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+namespace a2ats {
+namespace {
+
+// Argument checks shared by a2ats_reconstruct and a2ats_reconstruct_noalloc (A2ATS_OK with
+// *empty set when there is nothing to do).
+int reconstruct_check(const uint16_t* codes, const int32_t* positions, int64_t batch,
+                      int64_t heads, int64_t n, int64_t d, const float* codebook, int64_t c,
+                      int64_t cur_pos, int far_mode, double rope_base, const void* out,
+                      int out_dtype, bool* empty) {
+  *empty = false;
   if (out_dtype != A2ATS_F32 && out_dtype != A2ATS_BF16) return A2ATS_EDTYPE;
   if (d != kD || batch < 1 || heads < 1 || n < 0 || c < 1 || c > 65536) return A2ATS_EINVAL;
   if (cur_pos < 0 || !(rope_base > 0.0) || !std::isfinite(rope_base)) return A2ATS_EINVAL;
   if (far_mode != A2ATS_FAR_FIXED_OFFSET && far_mode != A2ATS_FAR_UNROTATED) return A2ATS_EINVAL;
-  if (n == 0) return A2ATS_OK;
+  if (n == 0) {
+    *empty = true;
+    return A2ATS_OK;
+  }
   if (!codes || !positions || !codebook || !out) return A2ATS_EINVAL;
+  return A2ATS_OK;
+}
+
+// The table and gather launches of a reconstruct, the table in `table` (rows + 1 rows).
+int reconstruct_launch(const uint16_t* codes, const int32_t* positions, int64_t batch,
+                       int64_t heads, int64_t n, const float* codebook, int64_t c,
+                       int64_t cur_pos, int64_t window, int64_t far_offset, int far_mode,
+                       double rope_base, void* out, int out_dtype, d2* table, hipStream_t s) {
   const int64_t rows = near_rows(cur_pos, window);
-  const size_t need = a2ats_reconstruct_workspace(d, cur_pos, window);
-  if (!ws_ok(workspace, workspace_bytes, need)) return A2ATS_EWORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  d2* table = static_cast<d2*>(workspace);
   A2ATS_TRY(launch("rope_table", rope_table, dim3(grid_for((rows + 1) * kHalf, 256)), dim3(256), 0,
                    s, rows, cur_pos, cur_pos - far_offset, (int)(far_mode == A2ATS_FAR_UNROTATED),
                    rope_base, (int)kD, table));
@@ -553,6 +565,71 @@ extern "C" int a2ats_reconstruct(const uint16_t* codes, const int32_t* positions
                   positions, heads, n, codebook, c, cur_pos, window, rows, table, out, items);
   return launch("reconstruct", rope_gather<true>, dim3((unsigned)g), dim3(256), 0, s, codes,
                 positions, heads, n, codebook, c, cur_pos, window, rows, table, out, items);
+}
+
+}  // namespace
+}  // namespace a2ats
+
+extern "C" int a2ats_reconstruct(const uint16_t* codes, const int32_t* positions, int64_t batch,
+                                 int64_t heads, int64_t n, int64_t d, const float* codebook,
+                                 int64_t c, int64_t cur_pos, int64_t window, int64_t far_offset,
+                                 int far_mode, double rope_base, void* out, int out_dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  A2ATS_TRY(reconstruct_check(codes, positions, batch, heads, n, d, codebook, c, cur_pos,
+                              far_mode, rope_base, out, out_dtype, &empty));
+  if (empty) return A2ATS_OK;
+  const size_t need = a2ats_reconstruct_workspace(d, cur_pos, window);
+  if (!ws_ok(workspace, workspace_bytes, need)) return A2ATS_EWORKSPACE;
+  return reconstruct_launch(codes, positions, batch, heads, n, codebook, c, cur_pos, window,
+                            far_offset, far_mode, rope_base, out, out_dtype,
+                            static_cast<d2*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------------------------ allocation-free variant
+// The rope table of a2ats_reconstruct_noalloc: (cos, sin) of the 64 pairs, A2ATS_NOALLOC_TABLE_ROWS
+// rows, in a fixed device array (one per GPU, held until the process ends).  In host code the
+// name `scratch` stands for the host-side shadow of the symbol; the device address of each
+// GPU's copy is looked up once per device (with that device current) and kept in
+// g_scratch_dev, which is what the kernels receive.
+static __device__ __align__(256) double scratch[A2ATS_NOALLOC_TABLE_ROWS * kD];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];
+
+// Device address of the current device's table (looked up on the device's first call).
+int scratch_table(d2** table) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return A2ATS_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return A2ATS_EHIP;
+    g_scratch_dev[dev] = p;
+  }
+  *table = static_cast<d2*>(g_scratch_dev[dev]);
+  return A2ATS_OK;
+}
+}  // namespace
+
+extern "C" int a2ats_reconstruct_noalloc(const uint16_t* codes, const int32_t* positions,
+                                         int64_t batch, int64_t heads, int64_t n, int64_t d,
+                                         const float* codebook, int64_t c, int64_t cur_pos,
+                                         int64_t window, int64_t far_offset, int far_mode,
+                                         double rope_base, void* out, int out_dtype,
+                                         void* stream) {
+  bool empty = false;
+  A2ATS_TRY(reconstruct_check(codes, positions, batch, heads, n, d, codebook, c, cur_pos,
+                              far_mode, rope_base, out, out_dtype, &empty));
+  if (empty) return A2ATS_OK;
+  if (near_rows(cur_pos, window) + 1 > A2ATS_NOALLOC_TABLE_ROWS) return A2ATS_ESCRATCH;
+  d2* table = nullptr;
+  A2ATS_TRY(scratch_table(&table));
+  return reconstruct_launch(codes, positions, batch, heads, n, codebook, c, cur_pos, window,
+                            far_offset, far_mode, rope_base, out, out_dtype, table,
+                            static_cast<hipStream_t>(stream));
 }
 
 extern "C" int a2ats_reconstruct_update(const uint16_t* codes, const int32_t* positions,

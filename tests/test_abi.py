@@ -43,7 +43,7 @@ def test_exports_every_declared_function(L):
 
 def test_version_and_strerror(L):
     assert L.a2ats_version() == 1
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         assert L.a2ats_strerror(st).decode() not in ("", "unknown status")
     assert L.a2ats_strerror(42).decode() == "unknown status"
 
@@ -198,6 +198,32 @@ def test_reconstruct_validation(L):
     assert call(codes=None) == EINVAL
     assert call(wsb=0) == EWORKSPACE
     assert call(n=0) == 0
+
+
+def test_reconstruct_noalloc_validation(L):
+    # every failing case returns before the library touches a device
+    def call(out_dt=0, d=128, cur=100, window=16, far_mode=0, base=10000.0, c=10, n=50,
+             codes=FAKE):
+        return L.a2ats_reconstruct_noalloc(codes, FAKE, 1, 2, n, d, FAKE, c, cur, window, 2048,
+                                           far_mode, base, FAKE, out_dt, None)
+
+    ESCRATCH = -6
+    assert call(out_dt=7) == EDTYPE
+    assert call(d=64) == EINVAL
+    assert call(cur=-1) == EINVAL
+    assert call(far_mode=2) == EINVAL
+    assert call(base=0.0) == EINVAL
+    assert call(c=0) == EINVAL
+    assert call(codes=None) == EINVAL
+    assert call(n=0) == 0
+    # the fixed table holds A2ATS_NOALLOC_TABLE_ROWS rows: min(max(W, 0), cur + 1) near rows + 1
+    rows = kv.NOALLOC_TABLE_ROWS
+    assert call(cur=10 ** 6, window=rows) == ESCRATCH
+    assert call(cur=10 ** 6, window=10 ** 9) == ESCRATCH
+    assert call(cur=rows - 1, window=10 ** 9) == ESCRATCH   # cur + 1 = rows near rows
+    assert "scratch" in L.a2ats_strerror(ESCRATCH).decode()
+    text = open(HEADER).read()
+    assert "#define A2ATS_NOALLOC_TABLE_ROWS %d" % rows in text
 
 
 def test_reconstruct_update_validation(L):
