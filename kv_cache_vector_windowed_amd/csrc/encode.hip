@@ -346,8 +346,9 @@ __global__ __launch_bounds__(256) void enc_prep_frag(const double* __restrict__ 
           (j < c) ? (float)(-0.5 * (double)hs.S * b64[(int64_t)head * c + j]) : kPadBias;
     }
   } else if (want_l && rid < rows + kD) {
-    // Row a of L^T (output z_a = sum_b k_b L_ba) as A-operand fragments: 4 tiles of 32
-    // rows; tiles 0..3 the fp16 high parts, 4..7 the residuals.
+    // Row a of L^T (output z_a = sum_b k_b L_ba) as A-operand fragments: 4 output tiles of
+    // 32 rows, each as two tiles, the fp16 high parts (tile 2 tz) and the residuals (2 tz + 1),
+    // so that the coarse pass streams them as two stages of four tiles.
     const int a = (int)(rid - rows);
     const float* L = chol + (int64_t)head * kD * kD;
     const int tile = a / kRows, i = a % kRows;
@@ -361,8 +362,8 @@ __global__ __launch_bounds__(256) void enc_prep_frag(const double* __restrict__ 
       fl[e] = (_Float16)(x - (double)qh);
     }
     half8* lt = lfrag + (int64_t)head * 8 * kFragPerTile;
-    lt[(int64_t)tile * kFragPerTile + s * 64 + i + 32 * hh] = fh;
-    lt[(int64_t)(tile + 4) * kFragPerTile + s * 64 + i + 32 * hh] = fl;
+    lt[(int64_t)(2 * tile) * kFragPerTile + s * 64 + i + 32 * hh] = fh;
+    lt[(int64_t)(2 * tile + 1) * kFragPerTile + s * 64 + i + 32 * hh] = fl;
   }
   // row norms over the 16 threads of the row, then the workgroup maxima
   for (int o = 8; o > 0; o >>= 1) {
@@ -879,17 +880,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int nst = (T + kTPS - 1) / kTPS;
   const unsigned lds_sv[2] = {lds_offset(&sv0[0][0]), lds_offset(&sv1[0][0])};
   const unsigned lds_sb[2] = {lds_offset(&sb0[0][0]), lds_offset(&sb1[0][0])};
-  auto load_stage = [&](int st, int buf) {
-    const half8* src = vh + (int64_t)st * kTPS * kFragPerTile;
+  auto load_frags = [&](const half8* src, int buf) {  // kTPS tiles of fragments
     const unsigned dst = lds_sv[buf] + (unsigned)(wave * 64 * sizeof(half8));
 #pragma unroll
     for (int q = 0; q < kTPS; ++q) {
       lds_dma16(src + q * kFragPerTile + t, dst + q * kFragPerTile * sizeof(half8));
       lds_dma16(src + q * kFragPerTile + 256 + t, dst + (q * kFragPerTile + 256) * sizeof(half8));
     }
+  };
+  auto load_stage = [&](int st, int buf) {
+    load_frags(vh + (int64_t)st * kTPS * kFragPerTile, buf);
     if (t < 8 * kTPS) lds_dma16(bh + (int64_t)st * kTPS * 32 + t * 4, lds_sb[buf]);
   };
-  load_stage(0, 0);
+  // With ||kL||^2 the stream starts with two stages of L^T fragments (z stages), then the
+  // codebook; without, with the codebook.
+  const half8* lt = lfrag + head * 8 * kFragPerTile;
+  if (ZNORM) load_frags(lt, 0);
+  else load_stage(0, 0);
 
   KeyFrags<2> kf;
   load_key_frags<DT, 2>(keys, head, n, row, hh, kf);
@@ -909,27 +916,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
 
-  // ||k L||^2 from fp16 hi/lo fragments of L^T (bf16 keys are exact in fp16).
+  // ||k L||^2 from fp16 hi/lo fragments of L^T (bf16 keys are exact in fp16), on the MFMA
+  // with the fragments streamed through the stage buffers like codebook tiles: z stage zs
+  // holds [hi, lo] of output tiles 2 zs and 2 zs + 1; each output tile's hi and lo products
+  // accumulate into one fp32 result, whose squares are summed.  The second z stage issues
+  // the loads of codebook stage 0 into buffer 0.
   float zn[2] = {0.f, 0.f};
   if (ZNORM) {
-    const half8* lt = lfrag + head * 8 * kFragPerTile;
-    for (int tz = 0; tz < 4; ++tz) {
-      f16v z0 = {}, z1 = {};
+    lds_dma_barrier();  // z stage 0 in LDS, s_red visible
+    auto zstage = [&](half8 (&svb)[kTPS][kFragPerTile], int zs) {
+      if (zs == 0) load_frags(lt + kTPS * kFragPerTile, 1);
+      else load_stage(0, 0);
 #pragma unroll
-      for (int part = 0; part < 2; ++part) {
+      for (int p = 0; p < 2; ++p) {
+        f16v z0 = {}, z1 = {};
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-          const half8 a = lt[(int64_t)(tz + 4 * part) * kFragPerTile + s * 64 + lane];
-          z0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf.f[0][s], z0, 0, 0, 0);
-          z1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf.f[1][s], z1, 0, 0, 0);
+        for (int part = 0; part < 2; ++part) {
+#pragma unroll
+          for (int s = 0; s < kSteps; ++s) {
+            const half8 a = svb[2 * p + part][s * 64 + lane];
+            z0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf.f[0][s], z0, 0, 0, 0);
+            z1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf.f[1][s], z1, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          zn[0] += z0[r] * z0[r];
+          zn[1] += z1[r] * z1[r];
         }
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        zn[0] += z0[r] * z0[r];
-        zn[1] += z1[r] * z1[r];
-      }
-    }
+      lds_dma_barrier();  // the next stage landed; this buffer free everywhere
+    };
+    zstage(sv0, 0);
+    zstage(sv1, 1);
     const float inv = 1.f / (hs.SL * hs.SL);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) zn[blk] = (zn[blk] + __shfl_xor(zn[blk], 32)) * inv;
