@@ -14,19 +14,23 @@
 //     |acc_j - S s_j| <= E = |k| rho + |k - k16| nu + gamma (B + |k16| nu) + u B,
 // (rho = max_j |S v_j - v16_j|, nu = max_j |v16_j|, B = max_j S b_j / 2, gamma covers the
 // fp32 accumulation of 129 terms).  The MFMA winner is accepted only when the bound proves
-// it; close calls are settled by exact fp64 scores, and whatever is still open is rescanned.
+// it; close calls are settled by fp32 scores of the two leading candidates under a rigorous
+// error bound, and whatever is still open is rescanned and decided in fp64.
 //
 // Kernels (in launch order)
 //   enc_prep_gram       M = L L^T in fp64 (H-weighted only).
-//   enc_prep_rows       v = c M, b = v . c in fp64 (fp64 MFMA), per-workgroup maxima.
+//   enc_prep_rows       v = c M, b = v . c in fp64 (fp64 MFMA), ||fp32(v)|| per centroid,
+//                       per-workgroup maxima.
 //   enc_prep_frag       fp16 fragments of S v in MFMA A-operand order, fp32 bias -S b / 2 per
 //                       accumulator slot, per-workgroup rho / nu; optional fp16 hi/lo
 //                       fragments of L^T for ||kL||^2; clears the list and candidate
 //                       counters.
 //   enc_znorm64         ||kL||^2 in fp64 (fp32 keys with distances and L only).
-//   enc_coarse          the MFMA pass; writes directly certified codes; in its tail, fp64
-//                       scores of the two leading candidates of the other keys settle most
-//                       of them and list the rest for the rescan.
+//   enc_coarse          the MFMA pass (with ||kL||^2 from L^T fragments when distances are
+//                       wanted); writes directly certified codes; in its tail, fp32 scores of
+//                       the two leading candidates of the other keys, formed from the exact
+//                       key fragments in registers, settle most of them and list the rest
+//                       for the rescan.
 //   enc_rescan_collect  second MFMA pass over the keys still open: collects every centroid
 //                       whose score could reach the best exact score.
 //   enc_rescan_decide   fp64 over the collected candidates; fp64 over the whole codebook for
@@ -61,19 +65,10 @@ struct Counters {
   unsigned unc[1];           // per-head rescan list lengths follow (heads entries)
 };
 
-struct RefEntry {       // a key whose code needs fp64 scores
-  int32_t head, row;
-  int32_t j0, j1;       // leading candidates (j1 < 0: none)
-  double thr;           // certified if the best exact score exceeds thr + eps (unscaled)
-  double e_unscaled;    // E / S, for the rescan threshold
-  float z2;             // ||kL||^2 (distances), or -1: ||k||^2 computed here
-  int32_t pad;
-};
-
-struct UncEntry {       // a key left open after the rerank
+struct UncEntry {       // a key left open by the coarse pass
   int32_t row;
-  int32_t jbest;
-  double sbest;         // exact score of jbest (a lower bound of the maximum)
+  int32_t jbest;        // the leading candidate
+  double sbest;         // a lower bound of the best score (of jbest's at least)
   double e_unscaled;
   float z2;
   int32_t pad;
@@ -170,9 +165,11 @@ __global__ __launch_bounds__(256) void enc_prep_rows(const float* __restrict__ c
                                                      double* __restrict__ v64,
                                                      float* __restrict__ v32,
                                                      double* __restrict__ b64,
+                                                     float* __restrict__ vnorm,
                                                      float* __restrict__ part_a, int nwg) {
   __shared__ float cr[32 * kD];
   __shared__ double bsum[4][32];
+  __shared__ double nsum[4][32];
   __shared__ float red[2][4];
   const int head = blockIdx.y;
   const int64_t j0 = (int64_t)blockIdx.x * 32;
@@ -213,19 +210,21 @@ __global__ __launch_bounds__(256) void enc_prep_rows(const float* __restrict__ c
           acc[rt][ct][r] = (double)cr[(16 * rt + 4 * r + lane / 16) * kD + 32 * wave + 16 * ct + lane % 16];
   }
   float vmax = 0.f;
-  double bp[2][4];
+  double bp[2][4], np_[2][4];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * rt + 4 * r + lane / 16;
       const int64_t j = j0 + row;
-      double p = 0.0;
+      double p = 0.0, q = 0.0;
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         const int col = 32 * wave + 16 * ct + lane % 16;
         const double x = acc[rt][ct][r];
+        const double x32 = (double)(float)x;
         p += x * (double)cr[row * kD + col];
+        q += x32 * x32;
         if (j < c) {
           v64[((int64_t)head * c + j) * kD + col] = x;
           v32[((int64_t)head * c + j) * kD + col] = (float)x;
@@ -233,15 +232,22 @@ __global__ __launch_bounds__(256) void enc_prep_rows(const float* __restrict__ c
         }
       }
       bp[rt][r] = p;
+      np_[rt][r] = q;
     }
-  // b: sum over the 16 lanes of a row, then over the four waves
+  // b and ||v32||^2: sums over the 16 lanes of a row, then over the four waves
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      double p = bp[rt][r];
-      for (int o = 8; o > 0; o >>= 1) p += __shfl_xor(p, o);
-      if (lane % 16 == 0) bsum[wave][16 * rt + 4 * r + lane / 16] = p;
+      double p = bp[rt][r], q = np_[rt][r];
+      for (int o = 8; o > 0; o >>= 1) {
+        p += __shfl_xor(p, o);
+        q += __shfl_xor(q, o);
+      }
+      if (lane % 16 == 0) {
+        bsum[wave][16 * rt + 4 * r + lane / 16] = p;
+        nsum[wave][16 * rt + 4 * r + lane / 16] = q;
+      }
     }
   for (int o = 32; o > 0; o >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, o));
   if (lane == 0) red[0][wave] = vmax;
@@ -252,6 +258,9 @@ __global__ __launch_bounds__(256) void enc_prep_rows(const float* __restrict__ c
     if (j0 + t < c) {
       b64[(int64_t)head * c + j0 + t] = bj;
       bmax = round_up_f(bj);
+      // ||v32_j|| rounded up (the fp64 sum of 128 squares is within 2^-45 of exact)
+      const double nj = ((nsum[0][t] + nsum[1][t]) + nsum[2][t]) + nsum[3][t];
+      vnorm[(int64_t)head * c + j0 + t] = round_up_f(sqrt(nj) * (1.0 + 0x1p-40));
     }
     for (int o = 16; o > 0; o >>= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, o));
   }
@@ -432,7 +441,14 @@ __device__ __forceinline__ void load_key_frags(const void* keys, int64_t head, i
       const int64_t off = (head * n + (row[blk] >= 0 ? row[blk] : 0)) * kD + 8 * hh;
 #pragma unroll
       for (int s = 0; s < kSteps; ++s)
-        raw[blk][s] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(keys) + off + 16 * s);
+      {
+        // non-temporal: the keys are read once, and should not evict the codebook tables
+        // that the tail reads from L2
+        typedef unsigned u4x __attribute__((ext_vector_type(4)));
+        const u4x r = __builtin_nontemporal_load(
+            reinterpret_cast<const u4x*>(static_cast<const uint16_t*>(keys) + off + 16 * s));
+        raw[blk][s] = uint4{r.x, r.y, r.z, r.w};
+      }
     }
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
@@ -542,43 +558,7 @@ __device__ __forceinline__ unsigned vgpr_of(unsigned s) {
   return v;
 }
 
-// Exact fp64 score of one candidate, 16 lanes cooperating (lane g of the group owns dims
-// 8g .. 8g+7).  Returns the score (valid in every lane of the group) and, in z2, ||k||^2.
-template <int DT>
-__device__ __forceinline__ double coop_score(const void* keys, int64_t off_key, const double* vrow,
-                                             double bj, int g, double* z2) {
-  double x[8];
-  if (DT == A2ATS_BF16) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(keys) + off_key + 8 * g);
-    const unsigned wv[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[2 * e] = (double)__uint_as_float(wv[e] << 16);
-      x[2 * e + 1] = (double)__uint_as_float(wv[e] & 0xFFFF0000u);
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(keys) + off_key + 8 * g);
-    const float4 a = p[0], b = p[1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-  }
-  double s = 0.0, k2 = 0.0;
-  const double2* v2 = reinterpret_cast<const double2*>(vrow + 8 * g);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const double2 vv = v2[e];
-    s += x[2 * e] * vv.x + x[2 * e + 1] * vv.y;
-    k2 += x[2 * e] * x[2 * e] + x[2 * e + 1] * x[2 * e + 1];
-  }
-  for (int o = 8; o > 0; o >>= 1) {
-    s += __shfl_xor(s, o);
-    k2 += __shfl_xor(k2, o);
-  }
-  *z2 = k2;
-  return s - 0.5 * bj;
-}
-
-// ------------------------------------------------------------------ fp64 rerank
+// ------------------------------------------------------------------ exact fp64 scores
 // Exact fp64 score of one candidate, G lanes cooperating (lane g of the group owns dims
 // (128/G)g .. (128/G)(g+1)-1).  Returns the score (valid in every lane of the group) and, in
 // z2, ||k||^2.
@@ -647,83 +627,6 @@ __device__ __forceinline__ void full_append(FullEntry* full, Counters* cnt, int3
   fe.z2 = z2;
   fe.pad = 0;
   full[atomicAdd(&cnt->full, 1u)] = fe;
-}
-
-// fp64 rerank of one listed key per group of 2G lanes (the first G score j0, the next G j1):
-// certified when the better exact score beats re.thr, else handed to the rescan (or, when
-// its list is full, the full scan).  Without L the rows are the fp32 codebook itself (v = c
-// exactly), half the bytes of the fp64 copy.  Returns 1 in the group's first lane when the
-// key was decided here.
-template <int DT, int G>
-__device__ __forceinline__ unsigned rerank_group(
-    bool live, const RefEntry& re, const void* keys, int64_t n, int64_t c,
-    const double* v64, const float* v32, bool plain, const double* b64, uint16_t* codes,
-    float* dist, UncEntry* unc, int64_t unc_cap, FullEntry* full, Counters* cnt, int lane) {
-  const int which = (lane / G) & 1;  // candidate 0 or 1
-  const int g = lane % G;
-  const int32_t head = live ? re.head : 0, row = live ? re.row : 0;
-  const int32_t ja = live ? re.j0 : -1, jb = live ? re.j1 : -1;
-  const int j = which ? jb : ja;
-  double s = -INFINITY, k2 = 0.0;
-  if (j >= 0) {
-    const int64_t off = ((int64_t)head * n + row) * kD;
-    const int64_t vo = ((int64_t)head * c + j) * kD;
-    s = plain ? coop_score_g<DT, G>(keys, off, v32 + vo, b64[(int64_t)head * c + j], g, &k2)
-              : coop_score_g<DT, G>(keys, off, v64 + vo, b64[(int64_t)head * c + j], g, &k2);
-  }
-  const double s_other = __shfl_xor(s, G);
-  const double k2_other = __shfl_xor(k2, G);
-  unsigned decided = 0;
-  bool listed = false;  // this group's key joins the rescan list
-  int best = ja;
-  double sbest = s;
-  if (live && lane % (2 * G) == 0) {
-    const double sa = s, sb = s_other;  // the group's first lane scored ja, lane G jb
-    if (ja < 0) k2 = k2_other;
-    if (jb >= 0 && (ja < 0 || sb > sa || (sb == sa && jb < ja))) {
-      best = jb;
-      sbest = sb;
-    }
-    const double z2 = re.z2 >= 0.f ? (double)re.z2 : k2;
-    const double eps = 0x1p-40 * (fabs(sbest) + k2 + 1.0);
-    if (best >= 0 && sbest - eps > re.thr) {
-      codes[(int64_t)head * n + row] = (uint16_t)best;
-      if (dist) dist[(int64_t)head * n + row] = (float)fmax(z2 - 2.0 * sbest, 0.0);
-      decided = 1;
-    } else if (best >= 0) {
-      listed = true;
-    } else {
-      full_append(full, cnt, head, row, re.z2);
-    }
-  }
-  // One list append per wave: the live entries of a wave are keys of one head (a workgroup
-  // serves one head's key block), and device-scope atomics on one address serialise at the
-  // memory side.
-  const unsigned long long m = __ballot(listed);
-  if (m) {  // wave-uniform
-    const int first = __builtin_ctzll(m);
-    const int32_t h0 = __shfl(head, first);
-    unsigned base = 0u;
-    if (lane == first) base = atomicAdd(&cnt->unc[h0], (unsigned)__popcll(m));
-    base = __shfl(base, first);
-    if (listed) {
-      const unsigned slot = base + (unsigned)__builtin_amdgcn_mbcnt_hi(
-                                       (unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
-      if (slot < unc_cap) {
-        UncEntry ue;
-        ue.row = row;
-        ue.jbest = best;
-        ue.sbest = sbest;
-        ue.e_unscaled = re.e_unscaled;
-        ue.z2 = re.z2;
-        ue.pad = 0;
-        unc[(int64_t)head * unc_cap + slot] = ue;
-      } else {
-        full_append(full, cnt, head, row, re.z2);
-      }
-    }
-  }
-  return decided;
 }
 
 // Number of listed open keys of a head (capped to the list capacity).
@@ -811,6 +714,26 @@ __device__ int64_t find_head(const Counters* cnt, const HeadSet& hs, int64_t cap
   return hs.head(hs.count - 1);
 }
 
+// Half of a key's dot with a row of v: the lane's 64 dims (8 per k-step, from its exact fp16
+// fragments) against the fp32 row, one fp32 multiply-add chain.
+__device__ __forceinline__ float half_dot(const half8 (&k)[kSteps], const float* v) {
+  float acc = 0.f;
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const f4 a = *reinterpret_cast<const f4*>(v + 16 * s);
+    const f4 b = *reinterpret_cast<const f4*>(v + 16 * s + 4);
+    acc = fmaf((float)k[s][0], a.x, acc);
+    acc = fmaf((float)k[s][1], a.y, acc);
+    acc = fmaf((float)k[s][2], a.z, acc);
+    acc = fmaf((float)k[s][3], a.w, acc);
+    acc = fmaf((float)k[s][4], b.x, acc);
+    acc = fmaf((float)k[s][5], b.y, acc);
+    acc = fmaf((float)k[s][6], b.z, acc);
+    acc = fmaf((float)k[s][7], b.w, acc);
+  }
+  return acc;
+}
+
 // ------------------------------------------------------------------ the MFMA pass
 // Workgroup: 256 keys of one head (4 waves x two 32-key column blocks).  Lane l serves key
 // column l % 32 of both blocks and, in every 32-centroid tile, the 16 rows
@@ -822,7 +745,8 @@ __device__ int64_t find_head(const Counters* cnt, const HeadSet& hs, int64_t cap
 // row parity packed into the low bits, plus one value U bounding every score that is not a
 // slot maximum.  At the end each key has 16 slot maxima and U:
 //   direct  t1 - max(t2, U) > 2E (+ packing slack)  -> code j(t1)
-//   else    listed for the fp64 rerank of j(t1), j(t2) against max(t3, U) + E.
+//   else    fp32 scores of j(t1), j(t2) (error e << E) against max(t3, U) + E: the better
+//           one when the bounds prove it, else the key is listed for the rescan.
 // Workgroups are dealt to XCDs round-robin; the mapping gives each XCD a contiguous range of
 // (head, key block) pairs so a head's codebook stays in one L2.
 template <int DT, bool ZNORM, bool DIST>
@@ -833,7 +757,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const double* __restrict__ b64, int64_t c, const half8* __restrict__ lfrag,
     const HeadScale* __restrict__ hsc, const float* __restrict__ part_b, int nwg_b,
     float* __restrict__ znorm, uint16_t* __restrict__ codes, float* __restrict__ dist,
-    const double* __restrict__ v64, UncEntry* __restrict__ unc, int64_t unc_cap,
+    const float* __restrict__ vnorm, UncEntry* __restrict__ unc, int64_t unc_cap,
     FullEntry* __restrict__ full, Counters* __restrict__ cnt, int want_stats) {
   // two stage buffers as separate arrays: the compiler then sees that the loads streaming
   // into one buffer cannot alias the LDS reads of the other, and does not wait for them
@@ -1089,90 +1013,148 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   const int j0 = jdec(a0, i0), j1 = jdec(a1, i1);
   const int64_t myrow = hh ? row[1] : row[0];
-  int outcome = 0;  // 1 direct, 2 listed for the rerank, 4 listed for the full scan
-  RefEntry re;
+  const bool mybad = hh ? kf.bad[1] : kf.bad[0];
+  // The fragments hold the key exactly (a bf16 key within fp16's normal range): its scores
+  // can then be formed from them below.
+  const bool exact_k = DT == A2ATS_BF16 && !mybad && (hh ? kf.e2[1] : kf.e2[0]) == 0.f;
+  int outcome = 0;  // 1 direct, 2 scored from the fragments, 3 open, 4 full scan
   float z2 = -1.f;
+  const double S = (double)hs.S;
+  double E = 0.0, thr = 0.0, lb3 = 0.0;
   if (myrow >= 0) {
-    const double S = (double)hs.S;
     const double rho = (double)fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
     const double nu = (double)fmaxf(fmaxf(s_red[1][0], s_red[1][1]), fmaxf(s_red[1][2], s_red[1][3]));
     const double B = 0.5 * S * (double)hs.maxb;
-    const double E = score_bound(hh ? kf.n2[1] : kf.n2[0], hh ? kf.e2[1] : kf.e2[0], rho, nu, B);
+    E = score_bound(hh ? kf.n2[1] : kf.n2[0], hh ? kf.e2[1] : kf.e2[0], rho, nu, B);
     const float t1u = fmaxf(a1, um);  // bound on every score but the best
     const double s0 = pack_slack(a0, tbits), s1 = pack_slack(t1u, tbits);
-    if (ZNORM) {
-      z2 = hh ? zn[1] : zn[0];
-      znorm[head * n + myrow] = z2;
-    } else if (znorm) {
-      z2 = znorm[head * n + myrow];
-    }
-    if (hh ? kf.bad[1] : kf.bad[0]) {
+    if (ZNORM) z2 = hh ? zn[1] : zn[0];
+    else if (znorm) z2 = znorm[head * n + myrow];
+    if (mybad || j0 >= c) {
       outcome = 4;
       if (ZNORM) z2 = -2.f;  // the fp16 fragments do not hold this key: ||kL||^2 in the scan
-    } else if (j0 < c && (double)a0 - s0 - E > (double)t1u + s1 + E) {
+    } else if ((double)a0 - s0 - E > (double)t1u + s1 + E) {
       outcome = 1;
       codes[head * n + myrow] = (uint16_t)j0;
-      if (DIST) {
-        // distance of the certified code: fp32 dot with the fp32 copy of v_code
-        const float* vr = v32 + (head * c + j0) * kD;
-        const int64_t off = (head * n + myrow) * kD;
-        float sdot = 0.f, k2 = 0.f;
-        for (int a = 0; a < kD; a += 8) {
-          const f4 va = *reinterpret_cast<const f4*>(vr + a);
-          const f4 vb = *reinterpret_cast<const f4*>(vr + a + 4);
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = load_elem(keys, DT, off + a + e);
-          sdot += x[0] * va.x + x[1] * va.y + x[2] * va.z + x[3] * va.w;
-          sdot += x[4] * vb.x + x[5] * vb.y + x[6] * vb.z + x[7] * vb.w;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) k2 += x[e] * x[e];
-        }
-        const double zz = (ZNORM || znorm) ? (double)z2 : (double)k2;
-        const double sc = (double)sdot - 0.5 * b64[head * c + j0];
-        dist[head * n + myrow] = (float)fmax(zz - 2.0 * sc, 0.0);
-      }
     } else {
-      outcome = 2;
+      outcome = exact_k ? 2 : 3;
+      // every score but those of j0 and j1 lies below thr; s_j0 >= lb3
       const double Ub = fmax((double)a2, (double)um);
-      re.head = (int32_t)head;
-      re.row = (int32_t)myrow;
-      re.j0 = j0 < c ? j0 : -1;
-      re.j1 = j1 < c ? j1 : -1;
-      re.thr = (Ub + pack_slack((float)Ub, tbits) + E) / S;
-      re.e_unscaled = E / S;
-      re.z2 = z2;
-      re.pad = 0;
+      thr = (Ub + pack_slack((float)Ub, tbits) + E) / S;
+      lb3 = ((double)a0 - s0 - E) / S;
     }
   }
-  // Rerank entries stay in LDS (in the stage buffers, free after the loop) and are settled
-  // here, 8 per wave and pass; full-scan entries (rare) go to the global list.
-  RefEntry* s_ref = reinterpret_cast<RefEntry*>(&sv0[0][0]);
-  static_assert(sizeof(RefEntry) * kKeysPerWG <= sizeof(sv0), "rerank list fits a stage buffer");
-  __shared__ unsigned s_cnt, s_base, s_stat[3], s_nref;
-  const unsigned xcd = blockIdx.x % 8;
-  if (t == 0) s_nref = 0u;
-  __syncthreads();
+  // fp32 scores of the leading candidates from the key fragments: j0 for a key decided
+  // directly whose distance is wanted, j0 and j1 for a key not decided.  Lane (col, hh) holds
+  // dims 16s + 8hh .. 16s + 8hh + 7 of key col of both blocks, so each lane forms half of
+  // every dot and the halves are added across the lane pair.  Bound of a score's error:
+  // 70 u ||k|| ||v32_j|| (a 65-term fp32 dot, the fp32 copy of v) plus the fp64 subtraction.
+  const bool w0 = (outcome == 1 && DIST && exact_k) || outcome == 2;
+  const bool w1 = outcome == 2 && j1 < c;
+  const int jj0 = w0 ? j0 : 0, jj1 = w1 ? j1 : 0;
+  const int pj0 = __shfl_xor(jj0, 32), pj1 = __shfl_xor(jj1, 32);
+  const int pw = __shfl_xor((w0 ? 1 : 0) | (w1 ? 2 : 0), 32);
+  const double bq0 = w0 ? b64[head * c + jj0] : 0.0, bq1 = w1 ? b64[head * c + jj1] : 0.0;
+  const float vn0 = w0 ? vnorm[head * c + jj0] : 0.f, vn1 = w1 ? vnorm[head * c + jj1] : 0.f;
+  float hd0[2] = {0.f, 0.f}, hd1[2] = {0.f, 0.f};
+  const float* v32h = v32 + head * c * kD + 8 * hh;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const bool mine = blk == hh;
+    if (mine ? w0 : (pw & 1) != 0) hd0[blk] = half_dot(kf.f[blk], v32h + (int64_t)(mine ? jj0 : pj0) * kD);
+    if (mine ? w1 : (pw & 2) != 0) hd1[blk] = half_dot(kf.f[blk], v32h + (int64_t)(mine ? jj1 : pj1) * kD);
+  }
+  float q0, q1;
   {
-    const unsigned long long m = __ballot(outcome == 2);
-    unsigned base = 0u;
-    if (lane == 0 && m) base = atomicAdd(&s_nref, (unsigned)__popcll(m));
-    base = __shfl(base, 0);
-    if (outcome == 2) s_ref[base + (unsigned)__popcll(m & ((1ull << lane) - 1ull))] = re;
+    const float f00 = hd0[0] + __shfl_xor(hd0[0], 32), f01 = hd0[1] + __shfl_xor(hd0[1], 32);
+    const float f10 = hd1[0] + __shfl_xor(hd1[0], 32), f11 = hd1[1] + __shfl_xor(hd1[1], 32);
+    q0 = hh ? f01 : f00;
+    q1 = hh ? f11 : f10;
   }
-  __syncthreads();
-  const unsigned nref = s_nref;
+  const double kn = sqrt((double)(hh ? kf.n2[1] : kf.n2[0])) * (1.0 + 0x1p-16);
+  const double zz = (ZNORM || znorm) ? (double)z2 : (double)(hh ? kf.n2[1] : kf.n2[0]);
+  bool open = outcome == 3;
+  int jbest = j0;
+  double sbest = lb3;
   unsigned reranked = 0;
-  constexpr int kRrG = 4;                  // lanes per candidate: 8 keys per wave and pass
-  constexpr unsigned kRrKeys = 64 / (2 * kRrG);
-  for (unsigned e0 = (unsigned)wave * kRrKeys; e0 < nref; e0 += 4u * kRrKeys) {
-    const unsigned e = e0 + (unsigned)lane / (2 * kRrG);
-    const bool live = e < nref;
-    RefEntry rl;
-    if (live) rl = s_ref[e];
-    reranked += rerank_group<DT, kRrG>(live, rl, keys, n, c, v64, v32, v64 == nullptr, b64,
-                                       codes, dist, unc, unc_cap, full, cnt, lane);
+  if (outcome == 1 && DIST) {
+    if (exact_k) {
+      const double sc = (double)q0 - 0.5 * bq0;
+      dist[head * n + myrow] = (float)fmax(zz - 2.0 * sc, 0.0);
+    } else {
+      // a key the fragments do not hold exactly: fp32 dot with the key read again
+      const float* vr = v32 + (head * c + j0) * kD;
+      const int64_t off = (head * n + myrow) * kD;
+      float sdot = 0.f, k2 = 0.f;
+      for (int a = 0; a < kD; a += 8) {
+        const f4 va = *reinterpret_cast<const f4*>(vr + a);
+        const f4 vb = *reinterpret_cast<const f4*>(vr + a + 4);
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = load_elem(keys, DT, off + a + e);
+        sdot += x[0] * va.x + x[1] * va.y + x[2] * va.z + x[3] * va.w;
+        sdot += x[4] * vb.x + x[5] * vb.y + x[6] * vb.z + x[7] * vb.w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) k2 += x[e] * x[e];
+      }
+      const double zk = (ZNORM || znorm) ? (double)z2 : (double)k2;
+      const double sc = (double)sdot - 0.5 * b64[head * c + j0];
+      dist[head * n + myrow] = (float)fmax(zk - 2.0 * sc, 0.0);
+    }
+  } else if (outcome == 2) {
+    constexpr double kU70 = 70.0 * 0x1p-24;
+    const double sa = (double)q0 - 0.5 * bq0;
+    const double ea = kU70 * kn * (double)vn0 + 0x1p-52 * (fabs((double)q0) + 0.5 * bq0);
+    double sb = -INFINITY, eb = 0.0;
+    if (w1) {
+      sb = (double)q1 - 0.5 * bq1;
+      eb = kU70 * kn * (double)vn1 + 0x1p-52 * (fabs((double)q1) + 0.5 * bq1);
+    }
+    // the better of the two, when the bounds order them; then certified when its lower
+    // bound clears every other score
+    const bool b_wins = sb > sa;
+    jbest = b_wins ? j1 : j0;
+    const double s_hi = b_wins ? sb : sa, e_hi = b_wins ? eb : ea;
+    const bool ordered = !w1 || fabs(sa - sb) > ea + eb;
+    if (ordered && s_hi - e_hi > thr) {
+      codes[head * n + myrow] = (uint16_t)jbest;
+      if (DIST) dist[head * n + myrow] = (float)fmax(zz - 2.0 * s_hi, 0.0);
+      reranked = 1;
+    } else {
+      open = true;
+      sbest = fmax(sa - ea, sb - eb);  // a lower bound of the larger of s_j0, s_j1
+      jbest = (sa - ea >= sb - eb) ? j0 : j1;
+    }
   }
+  // Open keys go to the rescan list: one list append per wave (the keys of a workgroup are
+  // one head's, and device-scope atomics on one address serialise at the memory side).  The
+  // entry's score is a lower bound of the best score, which is all the rescan needs.
+  {
+    const unsigned long long m = __ballot(open);
+    if (m) {  // wave-uniform
+      unsigned base = 0u;
+      if (lane == __builtin_ctzll(m)) base = atomicAdd(&cnt->unc[head], (unsigned)__popcll(m));
+      base = __shfl(base, __builtin_ctzll(m));
+      if (open) {
+        const unsigned slot = base + (unsigned)__builtin_amdgcn_mbcnt_hi(
+                                         (unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+        if (slot < unc_cap) {
+          UncEntry ue;
+          ue.row = (int32_t)myrow;
+          ue.jbest = jbest;
+          ue.sbest = sbest;
+          ue.e_unscaled = E / S;
+          ue.z2 = z2;
+          ue.pad = 0;
+          unc[head * unc_cap + slot] = ue;
+        } else {
+          full_append(full, cnt, (int32_t)head, (int32_t)myrow, z2);
+        }
+      }
+    }
+  }
+  __shared__ unsigned s_cnt, s_base, s_stat[3];
+  const unsigned xcd = blockIdx.x % 8;
   const unsigned fslot = block_append(&cnt->full, outcome == 4, &s_cnt, &s_base);
   if (outcome == 4) {
     FullEntry fe;
@@ -1378,11 +1360,13 @@ __global__ __launch_bounds__(256) void enc_rescan_decide(
       continue;
     }
     const int64_t off = ((int64_t)head * n + ue.row) * kD;
-    double best = ue.sbest;
-    int bj = ue.jbest;
+    // exact fp64 scores of the collected candidates and of jbest (the entry's score is only a
+    // lower bound of the best score, so jbest is scored here too)
+    double best = -INFINITY;
+    int bj = 0x7FFFFFFF;
     // ||k||^2 (for distances without a precomputed ||kL||^2) comes with the first batch
     double k2 = 0.0;
-    for (unsigned q0 = 0; q0 < (nc > 0 ? nc : 1u); q0 += 16) {
+    for (unsigned q0 = 0; q0 <= nc; q0 += 16) {
       const unsigned q = q0 + q16;
       double s = -INFINITY, kk = 0.0;
       int j = 0x7FFFFFFF;
@@ -1391,7 +1375,7 @@ __global__ __launch_bounds__(256) void enc_rescan_decide(
       const double bjj = b64[(int64_t)head * c + jj];
       const double sj = plain ? coop_score_g<DT, 4>(keys, off, v32 + vo, bjj, g, &kk)
                               : coop_score_g<DT, 4>(keys, off, v64 + vo, bjj, g, &kk);
-      if (q < nc) {
+      if (q <= nc) {
         s = sj;
         j = jj;
       }
@@ -1548,6 +1532,7 @@ struct EncLayout {
   unsigned* cand_n;
   int32_t* cand;
   float* znorm;
+  float* vnorm;
   HeadScale* hsc;
   double* gram;
   int nwg_a, nwg_b, ncnt;
@@ -1570,6 +1555,7 @@ EncLayout carve(void* ws, int64_t heads, int64_t n, int64_t c) {
   L.v64 = cv.take<double>((size_t)heads * c * kD);
   L.v32 = cv.take<float>((size_t)heads * c * kD);
   L.b64 = cv.take<double>((size_t)heads * c);
+  L.vnorm = cv.take<float>((size_t)heads * c);
   L.v16 = cv.take<half8>((size_t)heads * T * kFragPerTile);
   L.bias = cv.take<float>((size_t)heads * T * 32);
   L.lfrag = cv.take<half8>((size_t)heads * 8 * kFragPerTile);
@@ -1601,7 +1587,7 @@ int encode_prepare(int64_t heads, const float* codebook, int64_t c, const float*
                      chol, L.gram, L.part_a, L.nwg_a));
   A2ATS_TRY(launch("encode_prep_rows", enc_prep_rows, dim3((unsigned)L.nwg_a, (unsigned)heads),
                    dim3(256), 0, s, codebook, c, plain ? nullptr : L.gram, L.v64, L.v32, L.b64,
-                   L.part_a, L.nwg_a));
+                   L.vnorm, L.part_a, L.nwg_a));
   return launch("encode_prep_frag", enc_prep_frag, dim3((unsigned)L.nwg_b, (unsigned)heads),
                 dim3(256), 0, s, L.v64, L.b64, c, T, chol, (int)!plain, L.part_a, L.nwg_a,
                 L.part_b, L.v16, L.bias, L.lfrag, L.hsc);
@@ -1633,7 +1619,7 @@ int encode_run(const void* keys, int64_t heads, int64_t n, const int32_t* idx, i
 #define A2ATS_COARSE(Z, DI)                                                                       \
   launch(name, enc_coarse<DT, Z, DI>, dim3((unsigned)G), dim3(256), 0, s, keys, n, idx, n_sel,   \
          heads, nkb, T, tbits, L.v16, L.bias, L.v32, L.b64, c, L.lfrag, L.hsc,                    \
-         L.part_b, L.nwg_b, znorm, codes, dist, plain ? nullptr : L.v64, L.unc, L.unc_cap, L.full,   \
+         L.part_b, L.nwg_b, znorm, codes, dist, L.vnorm, L.unc, L.unc_cap, L.full,                   \
          cnt, stats ? 1 : 0)
   if (znorm_mfma) A2ATS_TRY(A2ATS_COARSE(true, true));
   else if (dist) A2ATS_TRY(A2ATS_COARSE(false, true));
