@@ -46,11 +46,12 @@ def lib():
         L.orc_rope_at.argtypes = [_dp, _i64, _i64, ctypes.c_double, ctypes.c_double, _dp]
         L.orc_kmeans_update.argtypes = [_dp, _i64, _i64, _ip, _i64, _dp, _dp, _lp]
         L.orc_kmeans.argtypes = [_dp, _i64, _i64, _i64, _dp, ctypes.c_int, _dp, _ip]
+        L.orc_kmeans_init.argtypes = [_dp, _i64, _i64, _i64, _dp, ctypes.POINTER(ctypes.c_uint64), _ip]
         L.orc_topk_codes.argtypes = [_dp, _i64, _up, _i64, _dp, _i64, _i64, _ip, _dp]
         L.orc_round_bf16.argtypes = [_dp, _i64, _up]
         for f in (L.orc_second_moment, L.orc_cholesky, L.orc_assign_h, L.orc_assign_cosine,
                   L.orc_select_retrieval, L.orc_reconstruct, L.orc_rope_at,
-                  L.orc_kmeans_update, L.orc_kmeans, L.orc_topk_codes):
+                  L.orc_kmeans_update, L.orc_kmeans, L.orc_kmeans_init, L.orc_topk_codes):
             f.restype = ctypes.c_int
         L.orc_round_bf16.restype = None
         L.orc_threads.argtypes, L.orc_threads.restype = [], ctypes.c_int
@@ -214,6 +215,21 @@ def kmeans(x, cb, l=None, iters=5):
     _check(lib().orc_kmeans(_ptr(x, _dp), n, d, k, _ptr(lf, _dp), int(iters), _ptr(cb, _dp),
                             _ptr(code, _ip)))
     return cb, code
+
+
+def kmeans_init(x, k, r, l=None):
+    """k-means++ seeding in z-space: x [n,d], k centers, r [k] uint64 draws, l [d,d] or None
+    -> idx int32 [k] (the rows chosen as centers, in order)."""
+    x = _f64(x)
+    n, d = x.shape
+    r = np.ascontiguousarray(r, dtype=np.uint64)
+    if r.shape != (k,):
+        raise ValueError("r must hold k draws")
+    lf = _f64(l) if l is not None else None
+    idx = np.empty(k, np.int32)
+    _check(lib().orc_kmeans_init(_ptr(x, _dp), n, d, int(k), _ptr(lf, _dp),
+                                 r.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), _ptr(idx, _ip)))
+    return idx
 
 
 def topk_codes(qb, codes, cb, k):

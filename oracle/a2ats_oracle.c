@@ -346,6 +346,98 @@ int orc_kmeans(const double* x, int64_t n, int64_t d, int64_t k, const double* l
   return st;
 }
 
+/* ------------------------------------------------------------------ k-means++ seeding */
+
+/* ceil(log2(x)) for x > 0, exactly (frexp: x = m 2^p with m in [0.5, 1)). */
+static int orc_clog2(double x) {
+  int p = 0;
+  const double m = frexp(x, &p);
+  return m == 0.5 ? p - 1 : p;
+}
+
+/* floor(a * b / 2^64) for unsigned 64-bit a, b: the draw r (uniform over [0, 2^64)) scaled
+ * to [0, b). */
+static uint64_t orc_mulhi(uint64_t a, uint64_t b) {
+  return (uint64_t)(((unsigned __int128)a * (unsigned __int128)b) >> 64);
+}
+
+/* k-means++ seeding in z-space ([API] a2ats_cholesky_factor: Eq. 16-18 turn the H-weighted
+ * objective into a plain Euclidean one on z = x L, "what lets conventional k-means++ build
+ * the codebook"; the docs' calibration trains with a seed).  The random draws are inputs:
+ * r[t], uniform over [0, 2^64), for center t.  Steps, k-means++ as Arthur and Vassilvitskii
+ * define it:
+ *   z_i = x_i L (each z_ia the fp64 sum over b in order of x_ib L_ba, rounded to fp32; x_i
+ *         itself without L), Z = max_i ||z_i||^2;
+ *   c_0 = floor(r_0 n / 2^64)  (uniform over the rows);
+ *   for t = 1 .. k-1:  D2_i = min over s < t of ||z_i - z_{c_s}||^2  (fp64, dimensions in
+ *         order), each D2_i taken as the integer w_i = floor(D2_i 2^e) with the fixed
+ *         e = 60 - ceil(log2 n) - ceil(log2 4Z) (so the sum cannot overflow; D2 <= 4Z), and
+ *         c_t = the first row i whose running integer sum w_0 + .. + w_i exceeds
+ *         floor(r_t W / 2^64), W = sum of all w (row i is drawn with probability w_i / W,
+ *         the D^2 weighting); c_t = floor(r_t n / 2^64) when W = 0.
+ * A chosen row has D2 = 0 and is never drawn again while W > 0.  idx[t] = c_t. */
+int orc_kmeans_init(const double* x, int64_t n, int64_t d, int64_t k, const double* l,
+                    const uint64_t* r, int32_t* idx) {
+  if (n <= 0 || d <= 0 || k <= 0) return ORC_EINVAL;
+  double* z = (double*)malloc(sizeof(double) * (size_t)(n * d));
+  double* d2 = (double*)malloc(sizeof(double) * (size_t)n);
+  uint64_t* w = (uint64_t*)malloc(sizeof(uint64_t) * (size_t)n);
+  if (!z || !d2 || !w) { free(z); free(d2); free(w); return ORC_EINVAL; }
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    for (int64_t a = 0; a < d; ++a) {
+      double s = 0.0;
+      if (l) {
+        for (int64_t b = 0; b < d; ++b) s += x[i * d + b] * l[b * d + a];
+      } else {
+        s = x[i * d + a];
+      }
+      z[i * d + a] = (double)(float)s;
+    }
+  }
+  double zmax = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    double s = 0.0;
+    for (int64_t a = 0; a < d; ++a) s += z[i * d + a] * z[i * d + a];
+    if (s > zmax) zmax = s;
+  }
+  int e = 60 - orc_clog2((double)n);
+  if (zmax > 0.0) e -= orc_clog2(4.0 * zmax);
+  int64_t c = (int64_t)orc_mulhi(r[0], (uint64_t)n);
+  idx[0] = (int32_t)c;
+  for (int64_t t = 1; t < k; ++t) {
+    const double* zc = z + c * d;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+      double s = 0.0;
+      for (int64_t a = 0; a < d; ++a) {
+        const double df = z[i * d + a] - zc[a];
+        s += df * df;
+      }
+      if (t == 1 || s < d2[i]) d2[i] = s;
+      w[i] = (uint64_t)floor(ldexp(d2[i], e));
+    }
+    uint64_t tot = 0;
+    for (int64_t i = 0; i < n; ++i) tot += w[i];
+    if (tot == 0) {
+      c = (int64_t)orc_mulhi(r[t], (uint64_t)n);
+    } else {
+      const uint64_t target = orc_mulhi(r[t], tot);
+      uint64_t run = 0;
+      c = n - 1;
+      for (int64_t i = 0; i < n; ++i) {
+        run += w[i];
+        if (run > target) { c = i; break; }
+      }
+    }
+    idx[t] = (int32_t)c;
+  }
+  free(z);
+  free(d2);
+  free(w);
+  return ORC_OK;
+}
+
 /* ------------------------------------------------------------------ top-K over codes */
 
 static int orc_cmp_score_desc(const void* a, const void* b) {

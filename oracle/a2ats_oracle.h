@@ -75,6 +75,14 @@ int orc_kmeans_update(const double* x, int64_t n, int64_t d, const int32_t* code
 int orc_kmeans(const double* x, int64_t n, int64_t d, int64_t k, const double* l, int iters,
                double* cb, int32_t* code);
 
+/* k-means++ seeding in z-space: z = fp32(x L) (x without L), c_0 = floor(r_0 n / 2^64), then
+ * each next center drawn with probability D^2 / sum D^2 (D^2: squared z-space distance to the
+ * nearest chosen center, fp64), the weights taken as integers floor(D^2 2^e) with
+ * e = 60 - ceil(log2 n) - ceil(log2 (4 max ||z||^2)) and the draw floor(r_t W / 2^64) located
+ * in their running sum.  idx[t] = the row chosen as center t. */
+int orc_kmeans_init(const double* x, int64_t n, int64_t d, int64_t k, const double* l,
+                    const uint64_t* r, int32_t* idx);
+
 /* Approximate-score top-K over codes: table lut_j = fl32(qb . c_j) (fp64 products and sum in
  * dimension order), score_t = lut[codes[t]] (-inf for codes >= c); the k largest (equal
  * scores: lower index first) in ascending index order, with their scores. */

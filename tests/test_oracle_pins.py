@@ -571,6 +571,109 @@ class TestKmeans:
         np.testing.assert_allclose(good @ l, wrong, rtol=1e-12, atol=1e-12)
 
 
+def _u64(fraction):
+    """A draw that is the given fraction of 2^64 (exact for fractions with few bits)."""
+    return np.uint64(int(fraction * 2 ** 64) if fraction < 1 else 2 ** 64 - 1)
+
+
+def _strata(m):
+    """m evenly spaced draws, one in the middle of each of m equal strata of [0, 2^64)."""
+    return np.array([(2 * j + 1) * 2 ** 64 // (2 * m) for j in range(m)], dtype=np.uint64)
+
+
+class TestKmeansInit:
+    """k-means++ seeding in z-space ([API] a2ats_cholesky_factor: Eq. 16-18 let conventional
+    k-means++ build the codebook on z = x L), with the draws passed in."""
+
+    def test_hand_case(self):
+        # four points on a line, no H: c0 = floor(r0 4 / 2^64); then D^2 weights
+        x = np.array([[0.0], [1.0], [3.0], [10.0]])
+        assert oracle.kmeans_init(x, 1, [_u64(0.25)]).tolist() == [1]
+        assert oracle.kmeans_init(x, 1, [_u64(0.0)]).tolist() == [0]
+        assert oracle.kmeans_init(x, 1, [_u64(0.99)]).tolist() == [3]
+        # after c0 = 1: D^2 = [1, 0, 4, 81] (total 86); a draw of 1/2 falls in row 3's share
+        # (rows 0 and 2 hold the first 5/86), 1/64 falls in row 2's (1/86 .. 5/86), 1/128 in
+        # row 0's
+        assert oracle.kmeans_init(x, 2, [_u64(0.25), _u64(0.5)]).tolist() == [1, 3]
+        assert oracle.kmeans_init(x, 2, [_u64(0.25), _u64(1 / 64)]).tolist() == [1, 2]
+        assert oracle.kmeans_init(x, 2, [_u64(0.25), _u64(1 / 128)]).tolist() == [1, 0]
+        # after c0 = 1, c1 = 3: D^2 = [1, 0, 4, 0]: a draw of 0 takes row 0, 1/2 row 2
+        assert oracle.kmeans_init(x, 3, [_u64(0.25), _u64(0.5), _u64(0.0)]).tolist() == [1, 3, 0]
+        assert oracle.kmeans_init(x, 3, [_u64(0.25), _u64(0.5), _u64(0.5)]).tolist() == [1, 3, 2]
+
+    @pytest.mark.parametrize("use_h", [False, True])
+    def test_draw_frequencies_are_d2_under_h(self, use_h):
+        # Over evenly spaced draws the share of draws choosing each row is its D^2 share,
+        # D^2 from the H-weighted quadratic form (x - c) H (x - c)^T with H = L L^T (Eq. 14,
+        # computed here independently of the z = xL route)
+        rng = np.random.default_rng(50)
+        n, d, m = 12, 3, 8192
+        x = rng.standard_normal((n, d)) * np.array([1.0, 3.0, 0.5])
+        l = random_spd_l(rng, d, cond=20.0) if use_h else None
+        h = l @ l.T if use_h else np.eye(d)
+        first = [0, 7]
+        chosen = {}
+        for r2 in _strata(m):
+            idx = oracle.kmeans_init(x, 3, [_u64(0.0), _u64(7.5 / 12), r2], l)
+            assert idx[:2].tolist() == first
+            chosen[idx[2]] = chosen.get(idx[2], 0) + 1
+        diff = [x - x[c] for c in first]
+        d2 = np.minimum(*[np.einsum("ia,ab,ib->i", df, h, df) for df in diff])
+        want = d2 / d2.sum()
+        got = np.array([chosen.get(i, 0) for i in range(n)]) / m
+        assert got[first].sum() == 0
+        assert np.abs(got - want).max() <= 2.0 / m + 1e-6, (got, want)
+
+    def test_transposed_factor_is_caught(self):
+        # planted mistake: L^T in place of L gives the wrong metric; the frequency pin sees it
+        rng = np.random.default_rng(51)
+        n, d, m = 10, 3, 4096
+        x = rng.standard_normal((n, d))
+        l = np.tril(rng.standard_normal((d, d)) * 2.0)  # strong off-diagonal terms
+        l[np.diag_indices(d)] = 1.0
+        h = l @ l.T
+        counts = np.zeros(n)
+        for r1 in _strata(m):
+            counts[oracle.kmeans_init(x, 2, [_u64(0.0), r1], l.T.copy())[1]] += 1
+        df = x - x[0]
+        want = np.einsum("ia,ab,ib->i", df, h, df)
+        assert np.abs(counts / m - want / want.sum()).max() > 0.01
+
+    def test_identity_factor_is_plain_and_z_space_identity(self):
+        # L = I is plain k-means++; and (Eq. 16-18) seeding x with L is seeding z = xL without
+        # it (z formed here with the same fp64 sum in order, rounded to fp32)
+        rng = np.random.default_rng(52)
+        n, d, k = 300, 6, 25
+        x = (rng.standard_normal((n, d)) * 2).astype(np.float32).astype(np.float64)
+        r = rng.integers(0, 2 ** 63, k, dtype=np.uint64) * np.uint64(2) + rng.integers(0, 2, k, dtype=np.uint64)
+        plain = oracle.kmeans_init(x, k, r)
+        assert np.array_equal(plain, oracle.kmeans_init(x, k, r, np.eye(d)))
+        l = random_spd_l(rng, d, cond=15.0)
+        z = np.empty((n, d))
+        for i in range(n):
+            for a in range(d):
+                acc = 0.0
+                for b in range(d):
+                    acc += float(x[i, b]) * float(l[b, a])
+                z[i, a] = float(np.float32(acc))
+        assert np.array_equal(oracle.kmeans_init(x, k, r, l), oracle.kmeans_init(z, k, r))
+        assert not np.array_equal(plain, oracle.kmeans_init(x, k, r, l))
+
+    def test_distinct_rows_and_uniform_fallback(self):
+        rng = np.random.default_rng(53)
+        x = rng.standard_normal((50, 4))
+        r = rng.integers(0, 2 ** 63, 50, dtype=np.uint64) * np.uint64(2)
+        idx = oracle.kmeans_init(x, 50, r)
+        assert sorted(idx.tolist()) == list(range(50))  # every row once: a chosen row weighs 0
+        # two distinct rows only: after both are chosen every weight is 0 and the draw is
+        # uniform over the rows, floor(r n / 2^64)
+        y = np.repeat(np.array([[1.0, 2.0], [5.0, -1.0]]), 5, axis=0)
+        r = np.array([_u64(0.05), _u64(0.3), _u64(0.55), _u64(0.95)], dtype=np.uint64)
+        idx = oracle.kmeans_init(y, 4, r)
+        assert idx[0] == 0 and idx[1] >= 5
+        assert idx[2:].tolist() == [int(int(v) * 10 >> 64) for v in r[2:]]
+
+
 class TestTopkCodes:
     """[ABS] top-K retrieval by approximate attention scores over the quantised keys."""
 
