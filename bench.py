@@ -671,12 +671,30 @@ def extra_workloads(ctx, steps, warmup):
     t_w = ctx.timed(train_whole, 3)
     t_s = ctx.timed(train_sub, 3)
     pr_w = ctx.profile(train_whole, 1)
+    # k-means++ seeding in z-space (the initial codebooks of the same two trainings)
+    rd_w = torch.from_numpy(np.random.default_rng(7).integers(0, 2 ** 64, (wl.heads, wl.c), dtype=np.uint64).view(np.int64)).to(ctx.dev)
+    rd_s = torch.from_numpy(np.random.default_rng(8).integers(0, 2 ** 64, 256, dtype=np.uint64).view(np.int64)).to(ctx.dev)
+
+    def seed_whole():
+        kv.kmeans_init(kl, wl.c, rd_w, ll)
+
+    def seed_sub():
+        kv.kmeans_init(sub_x, 256, rd_s, lq)
+
+    seed_whole()
+    seed_sub()
+    torch.cuda.synchronize()
+    t_iw = ctx.timed(seed_whole, 2)
+    t_is = ctx.timed(seed_sub, 2)
     res["kmeans"] = {
         "workload": "5 Lloyd rounds + final assignment, H-weighted: 8 heads x 32768 bf16 keys with "
-                    "k=1024 per head; 4.2M pooled sub-vectors (sub_dim 8) with one k=256 codebook",
+                    "k=1024 per head; 4.2M pooled sub-vectors (sub_dim 8) with one k=256 codebook; "
+                    "k-means++ seeding in z-space of the same two",
         "whole_ms_per_round": round(t_w / 6, 4),
         "sub_ms_per_round": round(t_s / 6, 4),
         "whole_update_us": round(sum(v[1] for kk, v in pr_w.items() if kk.startswith("kmeans_")) * 1e3, 2),
+        "seed_whole_ms": round(t_iw, 3),
+        "seed_sub_ms": round(t_is, 3),
     }
     log("kmeans %s" % res["kmeans"])
     return res

@@ -361,6 +361,32 @@ int a2ats_kmeans_update(const void* x, int x_dtype, int64_t heads, int64_t n, in
                         float* codebook_out, int32_t* counts, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* kmeans_init: k-means++ seeding in z-space -- the pages' "conventional k-means++" on
+ * z = x L (a2ats_cholesky_factor, Eq. 16-18; the docs' calibration trains with a seed).  The
+ * random draws are inputs: draws[h, t] uniform over [0, 2^64) for center t of head h.
+ *   z_i = x_i L (each component the fp64 sum over b in order of x_ib L_ba, rounded to fp32;
+ *         x_i itself when chol is NULL), Z = max_i ||z_i||^2 per head
+ *   c_0 = floor(draws[h, 0] n / 2^64)
+ *   c_t = the first row whose running sum of w exceeds floor(draws[h, t] W / 2^64), where
+ *         w_i = floor(D2_i 2^e), D2_i = min over chosen c of ||z_i - z_c||^2 (fp64, in
+ *         dimension order), e = 60 - ceil(log2 n) - ceil(log2 4Z), W = sum of w
+ *         (floor(draws[h, t] n / 2^64) when W = 0): each row is drawn with probability
+ *         D2 / sum D2, and the integer weights make the choice independent of how the
+ *         rows are split over workgroups.
+ *   x         [heads, n, d] fp32 or bf16, d in {4, 8, 16, 32, 64, 128}; 1 <= k <= n
+ *   chol      [heads, d, d] fp32 lower-triangular L, or NULL (plain k-means++)
+ *   draws     [heads, k] uint64 (device)
+ *   codebook  [heads, k, d] fp32 output: the chosen rows, in order
+ *   idx       [heads, k] int32 output (may be NULL): the chosen row indices
+ * Pooled sub-vectors (one shared codebook) are heads = 1 with x viewed as [1, n, sub_dim].
+ * One launch per center; returns without waiting.  Workspace:
+ * a2ats_kmeans_init_workspace(heads, n, d, k) bytes.
+ */
+size_t a2ats_kmeans_init_workspace(int64_t heads, int64_t n, int64_t d, int64_t k);
+int a2ats_kmeans_init(const void* x, int x_dtype, int64_t heads, int64_t n, int64_t d,
+                      int64_t k, const float* chol, const uint64_t* draws, float* codebook,
+                      int32_t* idx, void* workspace, size_t workspace_bytes, void* stream);
+
 /* kmeans: `iters` Lloyd rounds on the device from the initial codebook (updated in place),
  * then the final assignment into codes.  chol (optional) is L for the H-weighted assignment.
  *   d = 128   x [heads, n, 128], per-head codebooks [heads, k, 128] and L [heads, 128, 128]

@@ -83,6 +83,9 @@ def lib() -> ctypes.CDLL:
         L.a2ats_kmeans_workspace.argtypes = [i64, i64, i64, i64]
         L.a2ats_kmeans_workspace.restype = sz
         L.a2ats_kmeans.argtypes = [p, i32, i64, i64, i64, i64, p, i32, p, p, p, sz, p]
+        L.a2ats_kmeans_init_workspace.argtypes = [i64, i64, i64, i64]
+        L.a2ats_kmeans_init_workspace.restype = sz
+        L.a2ats_kmeans_init.argtypes = [p, i32, i64, i64, i64, i64, p, p, p, p, p, sz, p]
         L.a2ats_topk_codes.argtypes = [p, i32, i64, i64, i64, i64, p, i64, p, i64, i64, p, p, p]
         L.a2ats_profile_enable.argtypes, L.a2ats_profile_enable.restype = [i32], i32
         L.a2ats_profile_reset.argtypes, L.a2ats_profile_reset.restype = [], i32
@@ -92,7 +95,7 @@ def lib() -> ctypes.CDLL:
                   "a2ats_select_retrieval", "a2ats_reconstruct", "a2ats_reconstruct_noalloc",
                   "a2ats_reconstruct_update",
                   "a2ats_far_query_rope", "a2ats_pq_encode", "a2ats_pq_reconstruct",
-                  "a2ats_kmeans_update", "a2ats_kmeans", "a2ats_topk_codes"):
+                  "a2ats_kmeans_update", "a2ats_kmeans", "a2ats_kmeans_init", "a2ats_topk_codes"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -533,6 +536,34 @@ def kmeans(x: torch.Tensor, codebook: torch.Tensor, chol: torch.Tensor | None = 
                               _ptr(codebook), _ptr(codes), _ptr(ws), ws.numel(), _stream(x.device)),
            "kmeans")
     return codebook, codes
+
+
+def kmeans_init(x: torch.Tensor, k: int, draws: torch.Tensor, chol: torch.Tensor | None = None,
+                want_idx: bool = False):
+    """k-means++ seeding in z-space.  x [heads, n, d] (or pooled sub-vectors [n, d], one
+    codebook), draws [heads, k] (or [k]) uint64 held in an int64 tensor, chol [heads, d, d]
+    (or [d, d]) or None -> codebook [heads, k, d] (or [k, d]) fp32 [, idx int32]."""
+    _dev(x, "x")
+    _dev(draws, "draws")
+    pooled = x.dim() == 2
+    xv = x[None] if pooled else x
+    heads, n, d = xv.shape
+    if draws.dtype != torch.int64 or draws.numel() != heads * k:
+        raise ValueError("draws must hold heads * k 64-bit values (int64 tensor)")
+    if chol is not None:
+        _dev(chol, "chol")
+        if chol.dtype != torch.float32 or chol.numel() != heads * d * d:
+            raise ValueError("chol must be [heads, d, d] float32")
+    cb = torch.empty((heads, k, d), dtype=torch.float32, device=x.device)
+    idx = torch.empty((heads, k), dtype=torch.int32, device=x.device) if want_idx else None
+    ws = _workspace(lib().a2ats_kmeans_init_workspace(heads, n, d, k), x.device)
+    _check(lib().a2ats_kmeans_init(_ptr(xv), _dtype_code(x), heads, n, d, int(k), _ptr(chol),
+                                   _ptr(draws), _ptr(cb), _ptr(idx), _ptr(ws), ws.numel(),
+                                   _stream(x.device)), "kmeans_init")
+    if pooled:
+        cb = cb[0]
+        idx = idx[0] if idx is not None else None
+    return (cb, idx) if want_idx else cb
 
 
 def topk_codes(qb: torch.Tensor, codes: torch.Tensor, codebook: torch.Tensor, k: int,

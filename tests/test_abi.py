@@ -329,6 +329,28 @@ def test_kmeans_validation(L):
     assert km(n=0) == 0
 
 
+def test_kmeans_init_validation(L):
+    need = L.a2ats_kmeans_init_workspace(2, 1000, 128, 16)
+    assert need >= 2 * 1000 * 128 * 4 + 2 * 2 * 1000 * 8
+    assert L.a2ats_kmeans_init_workspace(1, 10, 128, 11) == 0  # k > n
+
+    def call(dt=1, heads=2, n=1000, d=128, k=16, x=FAKE, draws=FAKE, cb=FAKE, wsb=None):
+        wsb = need if wsb is None else wsb
+        return L.a2ats_kmeans_init(x, dt, heads, n, d, k, None, draws, cb, None, FAKE, wsb, None)
+
+    assert call(dt=5) == EDTYPE
+    assert call(d=12) == EINVAL
+    assert call(d=256) == EINVAL
+    assert call(k=0) == EINVAL
+    assert call(k=1001) == EINVAL
+    assert call(n=0) == EINVAL
+    assert call(heads=0) == EINVAL
+    assert call(x=None) == EINVAL
+    assert call(draws=None) == EINVAL
+    assert call(cb=None) == EINVAL
+    assert call(wsb=need - 1) == EWORKSPACE
+
+
 def test_topk_codes_validation(L):
     def call(qdt=0, batch=2, hq=6, hkv=2, d=128, n=64, c=16, k=8, qb=FAKE, idx=FAKE):
         return L.a2ats_topk_codes(qb, qdt, batch, hq, hkv, d, FAKE, n, FAKE, c, k, idx, None,

@@ -853,6 +853,85 @@ class TestKmeans:
         assert d_fin.sum() < d_init.sum()
 
 
+def draws_u64(seed, shape):
+    return np.random.default_rng(seed).integers(0, 2 ** 64, size=shape, dtype=np.uint64)
+
+
+def u64_to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int64)).to(DEV)
+
+
+class TestKmeansInit:
+    """k-means++ seeding in z-space: the chosen rows equal the oracle's, bit for bit."""
+
+    def test_layer_shape_h_weighted(self):
+        # 2 heads of the layer workload (32768 bf16 keys each), k = 1024, L from calibration
+        w = W["layer"]
+        heads = 2
+        keys = synth.keys(w.cfg, heads, w.n, "bf16")
+        _, lt = kv.calibrate(f32_to_dev(synth.queries(w.cfg, heads, w.m)), 1e-4)
+        r = draws_u64(60, (heads, w.c))
+        cb, idx = kv.kmeans_init(keys_to_dev(keys), w.c, u64_to_dev(r), lt, want_idx=True)
+        idx, cb = idx.cpu().numpy(), cb.cpu().numpy()
+        lref = lt.cpu().numpy().astype(np.float64)
+        for h in range(heads):
+            want = oracle.kmeans_init(keys.values[h], w.c, r[h], lref[h])
+            assert np.array_equal(idx[h], want), (h, np.nonzero(idx[h] != want)[0][:5])
+            assert np.array_equal(cb[h], keys.values[h][want])
+            assert len(np.unique(want)) == w.c
+
+    def test_pooled_sub_vectors(self):
+        # the pages' shared sub-vector codebook: keys pooled as [-1, 8] (131072 sub-vectors of
+        # 8192 keys), k = 256, one 8x8 L from the pooled query sub-vectors
+        w = W["pq_layer"]
+        keys = synth.keys(w.cfg, 1, 8192, "bf16")
+        x = np.ascontiguousarray(keys.values[0].reshape(-1, 8))
+        xb = keys_to_dev(keys).reshape(-1, 8)
+        q = synth.queries(w.cfg, 1, 1024)
+        _, lt = kv.calibrate(f32_to_dev(np.ascontiguousarray(q.reshape(1, -1, 8))), 1e-4)
+        r = draws_u64(61, 256)
+        cb, idx = kv.kmeans_init(xb, 256, u64_to_dev(r), lt[0].contiguous(), want_idx=True)
+        want = oracle.kmeans_init(x, 256, r, lt[0].cpu().numpy().astype(np.float64))
+        assert np.array_equal(idx.cpu().numpy(), want)
+        assert np.array_equal(cb.cpu().numpy(), x[want])
+
+    @pytest.mark.parametrize("n,d,k,dtype,use_h", [(1000, 128, 37, "f32", True),
+                                                   (3000, 8, 300, "bf16", False),
+                                                   (777, 4, 777, "f32", True),
+                                                   (5, 16, 1, "bf16", True),
+                                                   (2049, 32, 64, "bf16", True)])
+    def test_shapes(self, n, d, k, dtype, use_h):
+        rng = np.random.default_rng(n + d)
+        x = (rng.standard_normal((2, n, d)) * rng.uniform(0.3, 3.0, d)).astype(np.float32)
+        if dtype == "bf16":
+            x = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(x))
+        xd = torch.from_numpy(x).to(DEV)
+        if dtype == "bf16":
+            xd = xd.to(torch.bfloat16)  # exact: x is on the bf16 grid
+        l = None
+        if use_h:
+            l = np.stack([np.tril(rng.standard_normal((d, d)) * 0.2) + np.diag(rng.uniform(0.5, 2.0, d))
+                          for _ in range(2)]).astype(np.float32)
+        r = draws_u64(n * 7 + k, (2, k))
+        cb, idx = kv.kmeans_init(xd, k, u64_to_dev(r), f32_to_dev(l) if use_h else None, want_idx=True)
+        idx, cb = idx.cpu().numpy(), cb.cpu().numpy()
+        for h in range(2):
+            want = oracle.kmeans_init(x[h], k, r[h], None if l is None else l[h].astype(np.float64))
+            assert np.array_equal(idx[h], want), (h, np.nonzero(idx[h] != want)[0][:5])
+            assert np.array_equal(cb[h], x[h][want])
+
+    def test_duplicates_fall_back_to_uniform_draws(self):
+        # 3 distinct rows repeated: after the three are chosen every weight is 0
+        base = np.array([[1.0, 2.0, 0.5, -1.0], [4.0, 0.0, 1.0, 2.0], [-3.0, 1.0, 1.0, 0.0]],
+                        np.float32)
+        x = np.repeat(base, 700, axis=0)[None]
+        r = draws_u64(62, (1, 10))
+        cb, idx = kv.kmeans_init(torch.from_numpy(x).to(DEV), 10, u64_to_dev(r), want_idx=True)
+        want = oracle.kmeans_init(x[0], 10, r[0])
+        assert np.array_equal(idx.cpu().numpy()[0], want)
+        assert len({tuple(v) for v in x[0][want[:3]]}) == 3
+
+
 class TestPipeline:
     def test_two_streams_prepared_equals_sequential(self):
         # the benchmark's step: prepares and the H-weighted encode on a second stream
