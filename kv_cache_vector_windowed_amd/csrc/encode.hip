@@ -23,8 +23,8 @@
 //                       per-workgroup maxima.
 //   enc_prep_frag       fp16 fragments of S v in MFMA A-operand order, fp32 bias -S b / 2 per
 //                       accumulator slot, per-workgroup rho / nu; optional fp16 hi/lo
-//                       fragments of L^T for ||kL||^2; clears the list and candidate
-//                       counters.
+//                       fragments of L^T for ||kL||^2; clears the run state (list lengths,
+//                       decision counters, candidate counts).
 //   enc_znorm64         ||kL||^2 in fp64 (fp32 keys with distances and L only).
 //   enc_coarse          the MFMA pass (with ||kL||^2 from L^T fragments when distances are
 //                       wanted); writes directly certified codes; in its tail, fp32 scores of
@@ -53,7 +53,7 @@ constexpr int kFragPerTile = kSteps * 64; // half8 fragments per tile (8 KiB)
 constexpr int kTPS = 4;                   // tiles per LDS stage of the coarse pass
 constexpr int kKeysPerWG = 256;           // 4 waves x 64 keys
 constexpr int kCandCap = 32;              // rescan candidates per key
-constexpr int kDecideWgs = 256;           // workgroups of the rescan decide pass (a multiple of 8)
+constexpr int kDecideWgs = 1024;          // workgroups of the rescan decide pass (a multiple of 8)
 constexpr float kPadBias = -1.0e38f;      // bias of padding rows: finite, never competitive
 
 struct Counters {
@@ -190,11 +190,20 @@ __global__ __launch_bounds__(256) void enc_prep_rows(const float* __restrict__ c
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = d4{0.0, 0.0, 0.0, 0.0};
     const int li = lane % 16, lk = lane / 16;
+    // every M element this lane needs is loaded before the first MFMA (one memory round
+    // trip instead of one per k-step)
+    double mb0[kD / 4], mb1[kD / 4];
+#pragma unroll
+    for (int q = 0; q < kD / 4; ++q) {
+      mb0[q] = M[(4 * q + lk) * kD + 32 * wave + li];
+      mb1[q] = M[(4 * q + lk) * kD + 32 * wave + 16 + li];
+    }
+#pragma unroll
     for (int k0 = 0; k0 < kD; k0 += 4) {
       const double a0 = (double)cr[li * kD + k0 + lk];
       const double a1 = (double)cr[(16 + li) * kD + k0 + lk];
-      const double b0 = M[(k0 + lk) * kD + 32 * wave + li];
-      const double b1 = M[(k0 + lk) * kD + 32 * wave + 16 + li];
+      const double b0 = mb0[k0 / 4];
+      const double b1 = mb1[k0 / 4];
       acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
       acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
       acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
@@ -322,9 +331,17 @@ __global__ __launch_bounds__(256) void enc_prep_frag(const double* __restrict__ 
                                                      half8* __restrict__ v16,
                                                      float* __restrict__ bias,
                                                      half8* __restrict__ lfrag,
-                                                     HeadScale* __restrict__ hsc) {
+                                                     HeadScale* __restrict__ hsc,
+                                                     unsigned* __restrict__ clr0, int nclr0,
+                                                     unsigned* __restrict__ clr1, int64_t nclr1) {
   const int head = blockIdx.y;
   const int t = threadIdx.x;
+  {  // the run state (list lengths, decision counters, candidate counts) starts at zero
+    const int64_t g = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 256 + t;
+    const int64_t stride = (int64_t)gridDim.x * gridDim.y * 256;
+    for (int64_t k = g; k < nclr0; k += stride) clr0[k] = 0u;
+    for (int64_t k = g; k < nclr1; k += stride) clr1[k] = 0u;
+  }
   const HeadScale hs = head_scale_wg(part_a, head, nwg_a);
   if (blockIdx.x == 0 && t == 0) hsc[head] = hs;  // for the later passes
   const int64_t rows = (int64_t)T * kRows;
@@ -714,22 +731,27 @@ __device__ int64_t find_head(const Counters* cnt, const HeadSet& hs, int64_t cap
   return hs.head(hs.count - 1);
 }
 
-// Half of a key's dot with a row of v: the lane's 64 dims (8 per k-step, from its exact fp16
-// fragments) against the fp32 row, one fp32 multiply-add chain.
-__device__ __forceinline__ float half_dot(const half8 (&k)[kSteps], const float* v) {
+// Half of a key's dot with a row of v: the lane's 64 dims (8 per k-step, its exact fp16
+// fragments, parked in LDS at kp[256 s]) against the fp32 row, one fp32 multiply-add chain.
+__device__ __forceinline__ float half_dot_lds(const half8* kp, const float* v) {
+  f4 va[kSteps], vb[kSteps];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    va[s] = *reinterpret_cast<const f4*>(v + 16 * s);
+    vb[s] = *reinterpret_cast<const f4*>(v + 16 * s + 4);
+  }
   float acc = 0.f;
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
-    const f4 a = *reinterpret_cast<const f4*>(v + 16 * s);
-    const f4 b = *reinterpret_cast<const f4*>(v + 16 * s + 4);
-    acc = fmaf((float)k[s][0], a.x, acc);
-    acc = fmaf((float)k[s][1], a.y, acc);
-    acc = fmaf((float)k[s][2], a.z, acc);
-    acc = fmaf((float)k[s][3], a.w, acc);
-    acc = fmaf((float)k[s][4], b.x, acc);
-    acc = fmaf((float)k[s][5], b.y, acc);
-    acc = fmaf((float)k[s][6], b.z, acc);
-    acc = fmaf((float)k[s][7], b.w, acc);
+    const half8 k = kp[256 * s];
+    acc = fmaf((float)k[0], va[s].x, acc);
+    acc = fmaf((float)k[1], va[s].y, acc);
+    acc = fmaf((float)k[2], va[s].z, acc);
+    acc = fmaf((float)k[3], va[s].w, acc);
+    acc = fmaf((float)k[4], vb[s].x, acc);
+    acc = fmaf((float)k[5], vb[s].y, acc);
+    acc = fmaf((float)k[6], vb[s].z, acc);
+    acc = fmaf((float)k[7], vb[s].w, acc);
   }
   return acc;
 }
@@ -1057,12 +1079,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const double bq0 = w0 ? b64[head * c + jj0] : 0.0, bq1 = w1 ? b64[head * c + jj1] : 0.0;
   const float vn0 = w0 ? vnorm[head * c + jj0] : 0.f, vn1 = w1 ? vnorm[head * c + jj1] : 0.f;
   float hd0[2] = {0.f, 0.f}, hd1[2] = {0.f, 0.f};
-  const float* v32h = v32 + head * c * kD + 8 * hh;
+  if constexpr (DT == A2ATS_BF16) {
+    // The key fragments move to the stage buffers (free after the loop; each lane reads back
+    // only its own), so that a round of row loads (both blocks' rows, 512 bytes a lane) fits
+    // in registers: two rounds, j0 then j1, where row 0 stands in for a row not needed.
+    half8* kst0 = &sv0[0][0] + t;
+    half8* kst1 = &sv1[0][0] + t;
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    const bool mine = blk == hh;
-    if (mine ? w0 : (pw & 1) != 0) hd0[blk] = half_dot(kf.f[blk], v32h + (int64_t)(mine ? jj0 : pj0) * kD);
-    if (mine ? w1 : (pw & 2) != 0) hd1[blk] = half_dot(kf.f[blk], v32h + (int64_t)(mine ? jj1 : pj1) * kD);
+    for (int q = 0; q < kSteps; ++q) {
+      kst0[q * 256] = kf.f[0][q];
+      kst1[q * 256] = kf.f[1][q];
+    }
+    const float* v32h = v32 + head * c * kD + 8 * hh;
+    {
+      const int r0 = hh ? ((pw & 1) ? pj0 : 0) : (w0 ? jj0 : 0);   // block 0's key's j0
+      const int r1 = hh ? (w0 ? jj0 : 0) : ((pw & 1) ? pj0 : 0);   // block 1's
+      hd0[0] = half_dot_lds(kst0, v32h + (int64_t)r0 * kD);
+      hd0[1] = half_dot_lds(kst1, v32h + (int64_t)r1 * kD);
+    }
+    if (__ballot(w1)) {  // wave-uniform
+      int r0 = hh ? ((pw & 2) ? pj1 : 0) : (w1 ? jj1 : 0);
+      int r1 = hh ? (w1 ? jj1 : 0) : ((pw & 2) ? pj1 : 0);
+      // the rows of this round depend (opaquely) on the first round's products, so that
+      // the compiler does not issue both rounds' loads at once (their registers would spill)
+      asm volatile("" : "+v"(r0), "+v"(r1) : "v"(hd0[0]), "v"(hd0[1]));
+      hd1[0] = half_dot_lds(kst0, v32h + (int64_t)r0 * kD);
+      hd1[1] = half_dot_lds(kst1, v32h + (int64_t)r1 * kD);
+    }
   }
   float q0, q1;
   {
@@ -1082,20 +1125,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const double sc = (double)q0 - 0.5 * bq0;
       dist[head * n + myrow] = (float)fmax(zz - 2.0 * sc, 0.0);
     } else {
-      // a key the fragments do not hold exactly: fp32 dot with the key read again
+      // a key the fragments do not hold exactly: fp32 dot with the key read again, in two
+      // halves whose loads are all issued before their products
       const float* vr = v32 + (head * c + j0) * kD;
       const int64_t off = (head * n + myrow) * kD;
       float sdot = 0.f, k2 = 0.f;
-      for (int a = 0; a < kD; a += 8) {
-        const f4 va = *reinterpret_cast<const f4*>(vr + a);
-        const f4 vb = *reinterpret_cast<const f4*>(vr + a + 4);
-        float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = load_elem(keys, DT, off + a + e);
-        sdot += x[0] * va.x + x[1] * va.y + x[2] * va.z + x[3] * va.w;
-        sdot += x[4] * vb.x + x[5] * vb.y + x[6] * vb.z + x[7] * vb.w;
+      for (int half = 0; half < 2; ++half) {
+        f4 vv[16];
+        float x[64];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) k2 += x[e] * x[e];
+        for (int q = 0; q < 16; ++q) vv[q] = *reinterpret_cast<const f4*>(vr + 64 * half + 4 * q);
+        if constexpr (DT == A2ATS_BF16) {
+          const uint4* kp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(keys) + off + 64 * half);
+          uint4 raw[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) raw[q] = kp[q];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const unsigned wv[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[8 * q + 2 * e] = __uint_as_float(wv[e] << 16);
+              x[8 * q + 2 * e + 1] = __uint_as_float(wv[e] & 0xFFFF0000u);
+            }
+          }
+        } else {
+          const f4* kp = reinterpret_cast<const f4*>(static_cast<const float*>(keys) + off + 64 * half);
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const f4 a = kp[q];
+            x[4 * q] = a.x; x[4 * q + 1] = a.y; x[4 * q + 2] = a.z; x[4 * q + 3] = a.w;
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          sdot += x[4 * q] * vv[q].x + x[4 * q + 1] * vv[q].y + x[4 * q + 2] * vv[q].z +
+                  x[4 * q + 3] * vv[q].w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) k2 += x[4 * q + e] * x[4 * q + e];
+        }
       }
       const double zk = (ZNORM || znorm) ? (double)z2 : (double)k2;
       const double sc = (double)sdot - 0.5 * b64[head * c + j0];
@@ -1476,17 +1545,6 @@ __global__ __launch_bounds__(256) void enc_znorm64(const float* __restrict__ key
   }
 }
 
-// The run state (list lengths, decision counters, candidate counts) starts at zero: cleared
-// when the codebook side is prepared (a fill kernel, not a memset node), and left cleared by
-// the last kernel of every run.
-__global__ void enc_clear(unsigned* __restrict__ cnt, int ncnt, unsigned* __restrict__ cand_n,
-                          int64_t ncand) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t k = i; k < ncnt; k += stride) cnt[k] = 0u;
-  for (int64_t k = i; k < ncand; k += stride) cand_n[k] = 0u;
-}
-
 // Copies the run's decision counts out, then leaves the run counters cleared.
 __global__ void enc_stats_out(Counters* __restrict__ cnt, a2ats_encode_stats* out, int clear_words) {
   if (threadIdx.x == 0) {
@@ -1580,8 +1638,6 @@ int encode_prepare(int64_t heads, const float* codebook, int64_t c, const float*
   const int T = (int)tiles_of(c);
   const bool plain = chol == nullptr;
   const int64_t ncand = heads * L.unc_cap;
-  A2ATS_TRY(launch("encode_clear", enc_clear, dim3(grid_for(std::max<int64_t>(ncand, L.ncnt), 256, 1024)),
-                   dim3(256), 0, s, L.cnt, L.ncnt, L.cand_n, ncand));
   if (!plain)
     A2ATS_TRY(launch("encode_prep_gram", enc_prep_gram, dim3(kD / 8, (unsigned)heads), dim3(256), 0, s,
                      chol, L.gram, L.part_a, L.nwg_a));
@@ -1590,7 +1646,7 @@ int encode_prepare(int64_t heads, const float* codebook, int64_t c, const float*
                    L.vnorm, L.part_a, L.nwg_a));
   return launch("encode_prep_frag", enc_prep_frag, dim3((unsigned)L.nwg_b, (unsigned)heads),
                 dim3(256), 0, s, L.v64, L.b64, c, T, chol, (int)!plain, L.part_a, L.nwg_a,
-                L.part_b, L.v16, L.bias, L.lfrag, L.hsc);
+                L.part_b, L.v16, L.bias, L.lfrag, L.hsc, L.cnt, L.ncnt, L.cand_n, ncand);
 }
 
 // Key-side pass over a prepared workspace.
