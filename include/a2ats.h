@@ -231,7 +231,11 @@ int a2ats_select_retrieval(const void* keys, int keys_dtype, int64_t heads, int6
  * A token whose code is >= c or whose position is negative gets a row of NaN.
  * Requires cur_pos >= 0 and rope_base > 0.
  */
-size_t a2ats_reconstruct_workspace(int64_t d, int64_t cur_pos, int64_t window);
+/* Workspace: a2ats_reconstruct_workspace(heads, c, d, cur_pos, window, out_dtype) bytes: the
+ * rope table and, for the far tokens (which all share one rotation), every centroid's far row
+ * rotated and rounded once, which far tokens copy (the same values, bit for bit). */
+size_t a2ats_reconstruct_workspace(int64_t heads, int64_t c, int64_t d, int64_t cur_pos,
+                                   int64_t window, int out_dtype);
 int a2ats_reconstruct(const uint16_t* codes, const int32_t* positions, int64_t batch,
                       int64_t heads, int64_t n, int64_t d, const float* codebook, int64_t c,
                       int64_t cur_pos, int64_t window, int64_t far_offset, int far_mode,
@@ -322,8 +326,9 @@ int a2ats_pq_encode(const void* x, int x_dtype, int64_t heads, int64_t n, int64_
  * codebook[codes[b, h, t, s]] (codes uint8 [batch, heads, n, d / sub_dim]).  The value path of
  * the pages (values are never rotated) is this call with window <= 0 and A2ATS_FAR_UNROTATED:
  * a plain gather.  A token with any code >= k, or a negative position, gets a row of NaN.
- * Workspace: a2ats_reconstruct_workspace(d, cur_pos, window) bytes.
+ * Workspace: a2ats_pq_reconstruct_workspace(d, cur_pos, window) bytes.
  */
+size_t a2ats_pq_reconstruct_workspace(int64_t d, int64_t cur_pos, int64_t window);
 int a2ats_pq_reconstruct(const uint8_t* codes, const int32_t* positions, int64_t batch,
                          int64_t heads, int64_t n, int64_t d, int64_t sub_dim,
                          const float* codebook, int64_t k, int64_t cur_pos, int64_t window,

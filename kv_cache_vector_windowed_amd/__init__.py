@@ -63,8 +63,10 @@ def lib() -> ctypes.CDLL:
         L.a2ats_select_retrieval_workspace.argtypes = [i64, i64]
         L.a2ats_select_retrieval_workspace.restype = sz
         L.a2ats_select_retrieval.argtypes = [p, i32, i64, i64, i64, p, dbl, p, p, p, sz, p]
-        L.a2ats_reconstruct_workspace.argtypes = [i64, i64, i64]
+        L.a2ats_reconstruct_workspace.argtypes = [i64, i64, i64, i64, i64, i32]
         L.a2ats_reconstruct_workspace.restype = sz
+        L.a2ats_pq_reconstruct_workspace.argtypes = [i64, i64, i64]
+        L.a2ats_pq_reconstruct_workspace.restype = sz
         L.a2ats_reconstruct.argtypes = [p, p, i64, i64, i64, i64, p, i64, i64, i64, i64, i32, dbl,
                                         p, i32, p, sz, p]
         L.a2ats_reconstruct_noalloc.argtypes = [p, p, i64, i64, i64, i64, p, i64, i64, i64, i64,
@@ -351,7 +353,8 @@ def reconstruct(codes: torch.Tensor, positions: torch.Tensor, codebook: torch.Te
         out = torch.empty((batch, heads, n, d), dtype=out_dtype, device=codes.device)
     else:
         _dev(out, "out")
-    ws = _workspace(lib().a2ats_reconstruct_workspace(d, int(cur_pos), int(window)), codes.device)
+    ws = _workspace(lib().a2ats_reconstruct_workspace(heads, c, d, int(cur_pos), int(window),
+                                                      _dtype_code(out)), codes.device)
     _check(lib().a2ats_reconstruct(_ptr(codes), _ptr(positions), batch, heads, n, d,
                                    _ptr(codebook), c, int(cur_pos), int(window), int(far_offset),
                                    int(far_mode), float(rope_base), _ptr(out), _dtype_code(out),
@@ -477,7 +480,7 @@ def pq_reconstruct(codes: torch.Tensor, positions: torch.Tensor, codebook: torch
         out = torch.empty((batch, heads, n, d), dtype=out_dtype, device=codes.device)
     else:
         _dev(out, "out")
-    ws = _workspace(lib().a2ats_reconstruct_workspace(d, int(cur_pos), int(window)), codes.device)
+    ws = _workspace(lib().a2ats_pq_reconstruct_workspace(d, int(cur_pos), int(window)), codes.device)
     _check(lib().a2ats_pq_reconstruct(_ptr(codes), _ptr(positions), batch, heads, n, d, sub,
                                       _ptr(codebook), k, int(cur_pos), int(window), int(far_offset),
                                       int(far_mode), float(rope_base), _ptr(out), _dtype_code(out),

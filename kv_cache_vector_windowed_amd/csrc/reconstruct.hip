@@ -12,12 +12,16 @@
 // Kernels
 //   rope_table   (R + 1) rows of fp64 (cos, sin): row r < R is position cur - r,
 //                R = min(max(W, 0), cur + 1); row R is the far rotation (identity when far
-//                keys stay unrotated).
+//                keys stay unrotated).  With a workspace that has room for them
+//                (rope_prep), the same launch also writes every centroid's far row, rotated
+//                and rounded once: all far tokens of a head share the rotation, so a far
+//                token's row is a copy of its centroid's far row.
 //   rope_gather  HBM-write-bound stream: each thread owns a fixed group of P pairs of the
 //                head dimension (P = 4 for fp32 output, 8 for bf16, so every store is 16 B),
 //                takes the far row's cos/sin for its pairs from a copy the workgroup stages
 //                in LDS, gathers the centroid from L2, rotates in fp64, rounds once to the
-//                output type, and writes with non-temporal stores.  Work
+//                output type, and writes with non-temporal stores (a far token with far rows
+//                prepared: its centroid's far row copied).  Work
 //                items are (batch, head, 64-token chunk); item k has head k % heads and the
 //                grid is a multiple of 8 * heads, so a workgroup always serves one head and,
 //                with 8 heads, each XCD (workgroups are dealt round-robin over the 8 XCDs)
@@ -38,11 +42,13 @@ constexpr int kHalf = kD / 2;
 constexpr int kChunkF32 = 64;   // tokens per work item, fp32 output
 constexpr int kChunkBf16 = 64;  // tokens per work item, bf16 output
 // Work items per workgroup (the grid is rounded to a multiple of 8 * heads and is at least
-// kGridMin).  Few items per workgroup measure best: a later item's loads would wait, in
-// order, behind the earlier item's stores (one vector memory counter), while the far
-// rotation a workgroup stages in LDS is still shared by 64-128 tokens.
+// kGridMin).  A later item's loads wait, in order, behind the earlier item's stores (one
+// vector memory counter); measured on the long-context and decode workloads, four bf16
+// items (mostly copies of prepared far rows) and one fp32 item per workgroup are best (a
+// software-pipelined variant that issues the next item's loads before the current item's
+// stores needs more registers and measured slower).
 constexpr int kItemsPerWgF32 = 1;
-constexpr int kItemsPerWgBf16 = 2;
+constexpr int kItemsPerWgBf16 = 4;
 constexpr int kGridMin = 256;
 
 // (cos, sin) of the rotation of pair i at position p: angle p * base^(-2i/d), fp64.  The
@@ -113,14 +119,14 @@ __device__ __forceinline__ float bf16_tie_fix(double x, float y) {
   return __uint_as_float(fabs(x) > fabs((double)y) ? b + 1u : b - 1u);
 }
 
-// P pairs of one row, rounded once, as two 16-byte non-temporal stores (low half at pair
-// i0, high half at i0 + d/2).  bf16: the fp32 roundings of the fp64 values are rounded to
-// bf16 (nearest even); the rare fp32 value on a bf16 midpoint is corrected first (one
-// branch per thread for all 2P values), so the result is the single nearest-even rounding
-// of the fp64 value.
+// P pairs of one row rounded once to the output type, as the two 16-byte words of the row
+// (low half at pair i0, high half at i0 + d/2).  bf16: the fp32 roundings of the fp64
+// values are rounded to bf16 (nearest even); the rare fp32 value on a bf16 midpoint is
+// corrected first (one branch per thread for all 2P values), so the result is the single
+// nearest-even rounding of the fp64 value.
 template <bool BF16, int P>
-__device__ __forceinline__ void store_pairs(void* out, int64_t ooff, const double (&lo)[P],
-                                            const double (&hi)[P]) {
+__device__ __forceinline__ void round_pairs(const double (&lo)[P], const double (&hi)[P], u4& a,
+                                            u4& bb) {
   if constexpr (BF16) {
     static_assert(P == 8, "bf16 rows: 8 pairs per thread");
     float fl[P], fh[P];
@@ -139,7 +145,6 @@ __device__ __forceinline__ void store_pairs(void* out, int64_t ooff, const doubl
         fh[k] = bf16_tie_fix(hi[k], fh[k]);
       }
     }
-    u4 a, bb;
     a.x = pack_bf16x2(fl[0], fl[1]);
     a.y = pack_bf16x2(fl[2], fl[3]);
     a.z = pack_bf16x2(fl[4], fl[5]);
@@ -148,17 +153,48 @@ __device__ __forceinline__ void store_pairs(void* out, int64_t ooff, const doubl
     bb.y = pack_bf16x2(fh[2], fh[3]);
     bb.z = pack_bf16x2(fh[4], fh[5]);
     bb.w = pack_bf16x2(fh[6], fh[7]);
+  } else {
+    static_assert(P == 4, "fp32 rows: 4 pairs per thread");
+    a.x = __float_as_uint((float)lo[0]); a.y = __float_as_uint((float)lo[1]);
+    a.z = __float_as_uint((float)lo[2]); a.w = __float_as_uint((float)lo[3]);
+    bb.x = __float_as_uint((float)hi[0]); bb.y = __float_as_uint((float)hi[1]);
+    bb.z = __float_as_uint((float)hi[2]); bb.w = __float_as_uint((float)hi[3]);
+  }
+}
+
+// The two words of P pairs written with non-temporal stores at element offset ooff.
+template <bool BF16>
+__device__ __forceinline__ void store_words(void* out, int64_t ooff, const u4& a, const u4& bb) {
+  if constexpr (BF16) {
     uint16_t* o = static_cast<uint16_t*>(out) + ooff;
     __builtin_nontemporal_store(a, reinterpret_cast<u4*>(o));
     __builtin_nontemporal_store(bb, reinterpret_cast<u4*>(o + kHalf));
   } else {
-    static_assert(P == 4, "fp32 rows: 4 pairs per thread");
-    f4 a, bb;
-    a.x = (float)lo[0]; a.y = (float)lo[1]; a.z = (float)lo[2]; a.w = (float)lo[3];
-    bb.x = (float)hi[0]; bb.y = (float)hi[1]; bb.z = (float)hi[2]; bb.w = (float)hi[3];
     float* o = static_cast<float*>(out) + ooff;
-    __builtin_nontemporal_store(a, reinterpret_cast<f4*>(o));
-    __builtin_nontemporal_store(bb, reinterpret_cast<f4*>(o + kHalf));
+    __builtin_nontemporal_store(a, reinterpret_cast<u4*>(o));
+    __builtin_nontemporal_store(bb, reinterpret_cast<u4*>(o + kHalf));
+  }
+}
+
+template <bool BF16, int P>
+__device__ __forceinline__ void store_pairs(void* out, int64_t ooff, const double (&lo)[P],
+                                            const double (&hi)[P]) {
+  u4 a, bb;
+  round_pairs<BF16, P>(lo, hi, a, bb);
+  store_words<BF16>(out, ooff, a, bb);
+}
+
+// The two words of P pairs at element offset off of a row store (for copying).
+template <bool BF16>
+__device__ __forceinline__ void load_words(const void* src, int64_t off, u4& a, u4& bb) {
+  if constexpr (BF16) {
+    const uint16_t* p = static_cast<const uint16_t*>(src) + off;
+    a = *reinterpret_cast<const u4*>(p);
+    bb = *reinterpret_cast<const u4*>(p + kHalf);
+  } else {
+    const float* p = static_cast<const float*>(src) + off;
+    a = *reinterpret_cast<const u4*>(p);
+    bb = *reinterpret_cast<const u4*>(p + kHalf);
   }
 }
 
@@ -174,6 +210,73 @@ __device__ __forceinline__ void load_pairs(const float* x, float (&xl)[P], float
   }
 }
 
+// The rope table (as rope_table, blocks [0, tab_blocks)) and, in the blocks after it, the far
+// rotation of every codebook row, rounded once to the output type: farcb [heads][c][d].  A far
+// token's reconstructed row is then a copy of its centroid's far row, bit for bit what
+// rope_gather computes for it (the same fp64 angles from rope_cs, rotation and rounding).
+// Far rows: 256 / (d/2 / P) rows per workgroup; the workgroup first forms the 64 far
+// (cos, sin) in LDS.
+template <bool BF16>
+__global__ __launch_bounds__(256) void rope_prep(int64_t rows_near, int64_t cur, int64_t far_pos,
+                                                 int far_identity, double base, d2* __restrict__ table,
+                                                 int64_t tab_blocks, const float* __restrict__ cb,
+                                                 int64_t rows_far, void* __restrict__ farcb) {
+  constexpr int P = BF16 ? 8 : 4;
+  constexpr int TPT = kHalf / P;          // threads per row
+  constexpr int RPW = 256 / TPT;          // rows per workgroup
+  const int t = threadIdx.x;
+  if ((int64_t)blockIdx.x < tab_blocks) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + t;
+    if (e >= (rows_near + 1) * kHalf) return;
+    const int64_t r = e / kHalf;
+    const int i = (int)(e % kHalf);
+    d2 v;
+    if (r == rows_near && far_identity) {
+      v.x = 1.0;
+      v.y = 0.0;
+    } else {
+      v = rope_cs((r == rows_near) ? (double)far_pos : (double)(cur - r), i, kD, base);
+    }
+    table[e] = v;
+    return;
+  }
+  __shared__ d2 s_far[kHalf];
+  if (t < kHalf) {
+    d2 v;
+    if (far_identity) {
+      v.x = 1.0;
+      v.y = 0.0;
+    } else {
+      v = rope_cs((double)far_pos, t, kD, base);
+    }
+    s_far[t] = v;
+  }
+  __syncthreads();
+  const int64_t row = ((int64_t)blockIdx.x - tab_blocks) * RPW + t / TPT;
+  if (row >= rows_far) return;
+  const int i0 = (t % TPT) * P;
+  float xl[P], xh[P];
+  load_pairs<P>(cb + row * kD + i0, xl, xh);
+  double cs[P], sn[P], lo[P], hi[P];
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    cs[k] = s_far[i0 + k].x;
+    sn[k] = s_far[i0 + k].y;
+  }
+  rotate_pairs<double, P>(xl, xh, cs, sn, lo, hi);
+  u4 a, bb;
+  round_pairs<BF16, P>(lo, hi, a, bb);
+  if constexpr (BF16) {
+    uint16_t* o = static_cast<uint16_t*>(farcb) + row * kD + i0;
+    *reinterpret_cast<u4*>(o) = a;
+    *reinterpret_cast<u4*>(o + kHalf) = bb;
+  } else {
+    float* o = static_cast<float*>(farcb) + row * kD + i0;
+    *reinterpret_cast<u4*>(o) = a;
+    *reinterpret_cast<u4*>(o + kHalf) = bb;
+  }
+}
+
 // fp32 output: 4 pairs per thread; bf16 output: 8 pairs per thread (16-byte stores).  The
 // rotation is fp64 for both, written as one product and one fused multiply-add (so the
 // rounding steps do not depend on how the compiler contracts the expression), and rounded
@@ -185,7 +288,8 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void rope_gather(
     const uint16_t* __restrict__ codes, const int32_t* __restrict__ positions, int64_t heads,
     int64_t n, const float* __restrict__ cb, int64_t c, int64_t cur, int64_t window,
-    int64_t rows_near, const d2* __restrict__ table, void* __restrict__ out, int64_t items) {
+    int64_t rows_near, const d2* __restrict__ table, const void* __restrict__ farcb,
+    void* __restrict__ out, int64_t items) {
   constexpr int P = BF16 ? 8 : 4;        // pairs per thread
   constexpr int TPT = kHalf / P;         // threads per token
   constexpr int TOK = 256 / TPT;         // tokens per pass of the workgroup
@@ -235,17 +339,26 @@ __global__ __launch_bounds__(256) void rope_gather(
     const int64_t t0 = (rest % chunks) * CH;
     const float* cbh = cb + h * c * kD;
     float xl[U][P], xh[U][P];
+    u4 wa[U], wb[U];
+    bool copy[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t tok = t0 + u * TOK + tk;
       const bool ok = tok < n && code[u] < c && pos[u] >= 0;
-      load_pairs<P>(cbh + (int64_t)(ok ? code[u] : 0) * kD + i0, xl[u], xh[u]);
+      // a far token with pre-rotated far rows: its row is copied
+      copy[u] = ok && farcb != nullptr && !in_window(cur, pos[u], window);
+      if (copy[u]) load_words<BF16>(farcb, (h * c + code[u]) * kD + i0, wa[u], wb[u]);
+      else load_pairs<P>(cbh + (int64_t)(ok ? code[u] : 0) * kD + i0, xl[u], xh[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t tok = t0 + u * TOK + tk;
       if (tok >= n) continue;
       const int64_t ooff = ((b * heads + h) * n + tok) * kD + i0;
+      if (copy[u]) {
+        store_words<BF16>(out, ooff, wa[u], wb[u]);
+        continue;
+      }
       real lo[P], hi[P];
       if ((int64_t)code[u] >= c || pos[u] < 0) {
 #pragma unroll
@@ -515,9 +628,25 @@ inline int64_t near_rows(int64_t cur, int64_t window) {
 
 using namespace a2ats;
 
-extern "C" size_t a2ats_reconstruct_workspace(int64_t d, int64_t cur_pos, int64_t window) {
-  if (d != kD || cur_pos < 0) return 0;
+namespace a2ats {
+namespace {
+size_t table_bytes(int64_t cur_pos, int64_t window) {
   return align_up((size_t)(near_rows(cur_pos, window) + 1) * kHalf * sizeof(d2));
+}
+}  // namespace
+}  // namespace a2ats
+
+extern "C" size_t a2ats_reconstruct_workspace(int64_t heads, int64_t c, int64_t d,
+                                              int64_t cur_pos, int64_t window, int out_dtype) {
+  if (d != kD || cur_pos < 0 || heads < 1 || c < 1 || c > 65536) return 0;
+  if (out_dtype != A2ATS_F32 && out_dtype != A2ATS_BF16) return 0;
+  const size_t far_rows = align_up((size_t)(heads * c * kD) * (out_dtype == A2ATS_F32 ? 4 : 2));
+  return table_bytes(cur_pos, window) + far_rows;
+}
+
+extern "C" size_t a2ats_pq_reconstruct_workspace(int64_t d, int64_t cur_pos, int64_t window) {
+  if (d != kD || cur_pos < 0) return 0;
+  return table_bytes(cur_pos, window);
 }
 
 namespace a2ats {
@@ -542,15 +671,35 @@ int reconstruct_check(const uint16_t* codes, const int32_t* positions, int64_t b
   return A2ATS_OK;
 }
 
-// The table and gather launches of a reconstruct, the table in `table` (rows + 1 rows).
+// The table and gather launches of a reconstruct, the table in `table` (rows + 1 rows); with
+// farcb (room for [heads][c][d] in the output type) the same launch as the table also
+// writes every centroid's far row, which far tokens then copy.
 int reconstruct_launch(const uint16_t* codes, const int32_t* positions, int64_t batch,
                        int64_t heads, int64_t n, const float* codebook, int64_t c,
                        int64_t cur_pos, int64_t window, int64_t far_offset, int far_mode,
-                       double rope_base, void* out, int out_dtype, d2* table, hipStream_t s) {
+                       double rope_base, void* out, int out_dtype, d2* table, void* farcb,
+                       hipStream_t s) {
   const int64_t rows = near_rows(cur_pos, window);
-  A2ATS_TRY(launch("rope_table", rope_table, dim3(grid_for((rows + 1) * kHalf, 256)), dim3(256), 0,
-                   s, rows, cur_pos, cur_pos - far_offset, (int)(far_mode == A2ATS_FAR_UNROTATED),
-                   rope_base, (int)kD, table));
+  const int far_identity = (int)(far_mode == A2ATS_FAR_UNROTATED);
+  if (farcb) {
+    const int64_t tab_blocks = ((rows + 1) * kHalf + 255) / 256;
+    const int64_t rows_far = heads * c;
+    const int rpw = out_dtype == A2ATS_F32 ? 16 : 32;  // 256 / (64 / P)
+    const int64_t far_blocks = (rows_far + rpw - 1) / rpw;
+    if (tab_blocks + far_blocks > 0x7FFFFFFF) return A2ATS_EINVAL;
+    const dim3 g((unsigned)(tab_blocks + far_blocks));
+    if (out_dtype == A2ATS_F32)
+      A2ATS_TRY(launch("rope_table", rope_prep<false>, g, dim3(256), 0, s, rows, cur_pos,
+                       cur_pos - far_offset, far_identity, rope_base, table, tab_blocks, codebook,
+                       rows_far, farcb));
+    else
+      A2ATS_TRY(launch("rope_table", rope_prep<true>, g, dim3(256), 0, s, rows, cur_pos,
+                       cur_pos - far_offset, far_identity, rope_base, table, tab_blocks, codebook,
+                       rows_far, farcb));
+  } else {
+    A2ATS_TRY(launch("rope_table", rope_table, dim3(grid_for((rows + 1) * kHalf, 256)), dim3(256), 0,
+                     s, rows, cur_pos, cur_pos - far_offset, far_identity, rope_base, (int)kD, table));
+  }
   const int64_t chunk = out_dtype == A2ATS_F32 ? kChunkF32 : kChunkBf16;
   const int64_t items = batch * heads * ((n + chunk - 1) / chunk);
   // A multiple of 8 * heads workgroups, enough to fill the chip several times over.
@@ -562,9 +711,9 @@ int reconstruct_launch(const uint16_t* codes, const int32_t* positions, int64_t 
   if (g > (int64_t)1 << 30) g = (int64_t)1 << 30;
   if (out_dtype == A2ATS_F32)
     return launch("reconstruct", rope_gather<false>, dim3((unsigned)g), dim3(256), 0, s, codes,
-                  positions, heads, n, codebook, c, cur_pos, window, rows, table, out, items);
+                  positions, heads, n, codebook, c, cur_pos, window, rows, table, farcb, out, items);
   return launch("reconstruct", rope_gather<true>, dim3((unsigned)g), dim3(256), 0, s, codes,
-                positions, heads, n, codebook, c, cur_pos, window, rows, table, out, items);
+                positions, heads, n, codebook, c, cur_pos, window, rows, table, farcb, out, items);
 }
 
 }  // namespace
@@ -579,11 +728,13 @@ extern "C" int a2ats_reconstruct(const uint16_t* codes, const int32_t* positions
   A2ATS_TRY(reconstruct_check(codes, positions, batch, heads, n, d, codebook, c, cur_pos,
                               far_mode, rope_base, out, out_dtype, &empty));
   if (empty) return A2ATS_OK;
-  const size_t need = a2ats_reconstruct_workspace(d, cur_pos, window);
+  const size_t need = a2ats_reconstruct_workspace(heads, c, d, cur_pos, window, out_dtype);
   if (!ws_ok(workspace, workspace_bytes, need)) return A2ATS_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
   return reconstruct_launch(codes, positions, batch, heads, n, codebook, c, cur_pos, window,
                             far_offset, far_mode, rope_base, out, out_dtype,
-                            static_cast<d2*>(workspace), static_cast<hipStream_t>(stream));
+                            reinterpret_cast<d2*>(ws), ws + table_bytes(cur_pos, window),
+                            static_cast<hipStream_t>(stream));
 }
 
 // ------------------------------------------------------------------ allocation-free variant
@@ -628,7 +779,7 @@ extern "C" int a2ats_reconstruct_noalloc(const uint16_t* codes, const int32_t* p
   d2* table = nullptr;
   A2ATS_TRY(scratch_table(&table));
   return reconstruct_launch(codes, positions, batch, heads, n, codebook, c, cur_pos, window,
-                            far_offset, far_mode, rope_base, out, out_dtype, table,
+                            far_offset, far_mode, rope_base, out, out_dtype, table, nullptr,
                             static_cast<hipStream_t>(stream));
 }
 
@@ -699,7 +850,7 @@ extern "C" int a2ats_pq_reconstruct(const uint8_t* codes, const int32_t* positio
   if (n == 0) return A2ATS_OK;
   if (!codes || !positions || !codebook || !out) return A2ATS_EINVAL;
   const int64_t rows = near_rows(cur_pos, window);
-  const size_t need = a2ats_reconstruct_workspace(d, cur_pos, window);
+  const size_t need = a2ats_pq_reconstruct_workspace(d, cur_pos, window);
   if (!ws_ok(workspace, workspace_bytes, need)) return A2ATS_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   d2* table = static_cast<d2*>(workspace);

@@ -178,9 +178,11 @@ def test_select_validation(L):
 
 
 def test_reconstruct_validation(L):
-    need = L.a2ats_reconstruct_workspace(128, 16384, 256)
-    assert need >= (256 + 1) * 64 * 16
-    assert L.a2ats_reconstruct_workspace(128, 10, 1 << 40) >= 11 * 64 * 16  # rows capped at cur+1
+    need = L.a2ats_reconstruct_workspace(2, 10, 128, 16384, 256, 0)
+    assert need >= (256 + 1) * 64 * 16 + 2 * 10 * 128 * 4  # table + far rows
+    assert L.a2ats_reconstruct_workspace(2, 10, 128, 10, 1 << 40, 1) >= 11 * 64 * 16 + 2 * 10 * 128 * 2
+    assert L.a2ats_reconstruct_workspace(2, 10, 128, 10, 5, 7) == 0  # dtype
+    assert L.a2ats_pq_reconstruct_workspace(128, 10, 1 << 40) >= 11 * 64 * 16  # rows capped at cur+1
 
     def call(out_dt=0, d=128, cur=100, window=16, far_mode=0, base=10000.0, c=10, n=50,
              wsb=None, codes=FAKE):
