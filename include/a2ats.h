@@ -314,8 +314,11 @@ int a2ats_far_query_rope(const void* q, int q_dtype, int64_t rows, int64_t d, in
  *                  slice of query [heads, nq, d] (nq 1 or n, dtype of x), rules as for
  *                  a2ats_assign_cosine            -- a2ats_query_aware_assignment
  *   both NULL      argmin_j ||x_s - c_j||^2 (bulk rows; values)
- * Ties go to the lowest index; the decision is exact (fp32 scan under a proven error bound,
- * fp64 for close calls; the blend entirely in fp64).  No workspace; returns without waiting.
+ * Ties go to the lowest index; the decision is exact: fp16 matrix-core scores (table split
+ * hi + lo) folded per accumulator slot, the winning slot rescored in fp64 and accepted under
+ * a proven error bound, the rare rest decided in fp64 over the whole table (the blend the
+ * same way, its maximum error from a first pass).  A sub-vector with a non-finite element
+ * gets code 0 (all its distances are inf or NaN).  No workspace; returns without waiting.
  */
 int a2ats_pq_encode(const void* x, int x_dtype, int64_t heads, int64_t n, int64_t d,
                     int64_t sub_dim, const int32_t* idx, int64_t n_idx, const float* codebook,

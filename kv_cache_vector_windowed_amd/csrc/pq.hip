@@ -13,279 +13,981 @@
 //   plain       argmin_j ||x_s - c_j||^2                         (bulk rows and values)
 // Ties go to the lowest index.
 //
-// Kernel pq_encode: one thread per (row, group of four consecutive sub-spaces), groups of a
-// row on consecutive lanes (coalesced loads of whole rows); the four sub-vectors share every
-// centroid read from LDS.  Each workgroup first stages the transformed codebook in LDS: w_j = c_j L and b_j = ||w_j||^2 in fp64 (w_j = c_j without L), plus fp32
-// copies and, per centroid, the terms of its error bound.  A thread forms z = x_s L in fp64
-// and scans the K scores s_j = z . w_j - b_j / 2 in fp32.  Each fp32 score is within
-// E_j = c (||z|| ||w_j|| + b_j) of the exact one (c = 18 u, u = 2^-24: the roundings of z, w
-// and b to fp32 and the (sub_dim + 1)-term fp32 sum, with room to spare), so the thread
-// keeps the two largest t_j = s_j + E_j and the winner a is certain when s_a - E_a exceeds
-// the other t; otherwise it rescans the K scores in fp64 (about 3 in 10^5 sub-vectors on
-// the workloads; a single codebook-wide bound sent 2% there).  The blend is evaluated in
-// fp64 throughout (two passes: max e, then the blended argmax, with the per-centroid and
-// per-row reciprocals taken once), as the whole-vector blend is.
+// Encode on the matrix cores.  With v_j = c_j H (c_j itself without H), b_j = c_j H c_j^T,
+//     argmin_j (x_s - c_j) H (x_s - c_j)^T = argmax_j s_j,   s_j = x_s . v_j - b_j / 2,
+// so the code is a contraction of every sub-vector against the (at most 256-row) table plus a
+// row argmax.  A wave takes 64 sub-vectors, two blocks of 32 MFMA columns, against the whole
+// table, 8 tiles of 32 rows, on v_mfma_f32_32x32x16_f16.  The table side is scaled by a
+// power of two S and split into fp16 hi + lo parts; the sub-vectors are exact in fp16 (bf16
+// inputs in fp16's range) or split the same way (fp32 inputs); the bias -S b_j / 2 enters as
+// fp16 hi + lo parts times a power of two (sub_dim 8: a small MFMA per tile whose result seeds
+// both blocks' accumulators; sub_dim 4: spare K slots of the same MFMA).  The whole table
+// operand stays in registers.
+//   Fold: each accumulator register keeps its maximum over the 8 tiles (v_maximum3, half an
+// operation per score, no index).  A sub-vector's 32 register maxima ("slots", 16 in each
+// lane of a lane pair, exchanged with v_permlane32_swap) are packed with their slot number
+// and the largest two taken: the winning slot and a bound on every other slot.  The winning
+// slot's 8 centroids are scored again in fp64, and the best of them is the code when its
+// score beats the second slot's maximum by more than the rigorous bound E on an MFMA score's
+// error (hi/lo residuals, the bias residual, fp32 accumulation of up to 25 terms, the packed
+// low bits).  The rest, rare, is decided by the whole wave in fp64 over the whole table.
+//   Blend: e_j = ||x - c_j||^2 = ||x||^2 - 2 s_j (plain s_j), so max_j e_j comes from a first
+// pass folding the smallest s_j the same way (the farthest slot rescored in fp64, exactly as
+// the definition sums).  Up to a constant per sub-vector the blended score is
+//     (2 beta / max e) s_j + ((1 - beta) / ||q_s||) (q_s . c_j / ||c_j||),
+// formed in fp32 from two accumulators (the second against the unit-norm table) and folded as
+// above; the winning slot is rescored in fp64 by the blend's own formula (reciprocals of
+// max e, ||q_s|| and ||c_j|| taken once: a few ulps from the divided form).
 #include "common.hpp"
 
 namespace a2ats {
 namespace {
 
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef __fp16 h2rtz __attribute__((ext_vector_type(2)));
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+
 constexpr int kD = A2ATS_HEAD_DIM;
-constexpr int kPqThreads = 256;
 constexpr int kPqMaxK = 256;
-// fp32 score bound factor (sub_dim + 10) u, u = 2^-24: the roundings of z and w to fp32
-// (2u ||z|| ||w||), the (sub_dim + 1)-term fp32 sum ((sub_dim + 1) u of the magnitudes),
-// b_j's rounding (u b_j) and the rounding of t_j itself (u |t_j|), with room to spare
-constexpr double kBoundC = 18.0 * 0x1p-24;
-constexpr int kPqRows = 4;  // sub-vectors per thread: each LDS centroid read serves four
+constexpr int kPqTiles = kPqMaxK / 32;
+constexpr int kPqWaves = 4;
+constexpr int kPqThreads = 64 * kPqWaves;  // one table row per thread in the preparation
+constexpr int kPqWgPerCu = 2;
+constexpr int kPqCus = 256;
+constexpr float kPadMark = 65504.f;        // the largest fp16: x 2^15, a pad row's bias
+constexpr double kRnd = 0x1p-23;           // one fp32 rounding, doubled (truncation allowed)
+constexpr double kHalfMin = 0x1p-14;       // smallest normal fp16
 
 enum PqMode { kPlain = 0, kHWeighted = 1, kBlend = 2 };
 
-// x rounded to fp32 towards +infinity.
-__device__ __forceinline__ float round_up_f(double x) {
-  float f = (float)x;
-  if ((double)f < x) f = __uint_as_float(__float_as_uint(f) + (f >= 0.f ? 1u : 0xFFFFFFFFu));
-  return f;
+// Two floats to packed fp16, rounded toward zero (exact for values fp16 holds).
+__device__ __forceinline__ unsigned pk16(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+__device__ __forceinline__ float lo16(unsigned p) { return (float)__builtin_bit_cast(h2rtz, p)[0]; }
+__device__ __forceinline__ float hi16(unsigned p) { return (float)__builtin_bit_cast(h2rtz, p)[1]; }
+__device__ __forceinline__ half8 h8(unsigned a, unsigned b, unsigned c, unsigned d) {
+  const u4v v = {a, b, c, d};
+  return __builtin_bit_cast(half8, v);
+}
+__device__ __forceinline__ unsigned pkh(_Float16 a, _Float16 b) {
+  return (unsigned)__builtin_bit_cast(unsigned short, a) |
+         ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
+}
+__device__ __forceinline__ float fmax3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+__device__ __forceinline__ double up(double x) { return x * (1.0 + 0x1p-40); }  // x >= 0
+
+// fp16 nearest to x, with values below fp16's normal range flushed to zero (the residual is
+// then carried by the next part or the error bound; no subnormal reaches the matrix cores
+// from the table side).
+__device__ __forceinline__ _Float16 half_of(double x) {
+  const _Float16 h = (_Float16)(float)x;
+  return fabs((double)h) < kHalfMin ? (_Float16)0.f : h;
 }
 
-__device__ __forceinline__ bool better(double s, int j, double bs, int bj) {
-  return s > bs || (s == bs && j < bj);
+// Workgroup-wide maxima of N doubles (every thread receives them).
+template <int N>
+__device__ __forceinline__ void block_max(double (&v)[N], double (*red)[kPqWaves]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v[i] = fmax(v[i], __shfl_xor(v[i], o));
+  if (lane == 0)
+#pragma unroll
+    for (int i = 0; i < N; ++i) red[i][wave] = v[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmax(fmax(red[i][0], red[i][1]), fmax(red[i][2], red[i][3]));
+  __syncthreads();
 }
 
-template <int DT, int MODE, int SUB, int R>
-__global__ __launch_bounds__(kPqThreads) void pq_encode(
+template <int SUB, bool BLEND>
+struct PqShared {
+  half8 fa[kPqTiles][64];            // table operand, MFMA A order
+  unsigned fb[kPqTiles][64][2];      // bias operand (sub_dim 8; zero in lanes 32-63)
+  half8 fq[BLEND ? kPqTiles : 1][64];  // unit-norm table operand (blend)
+  // per row in fp64: v_j (c_j for the blend), then b_j / 2 and 1 / ||c_j|| (0 for a zero row;
+  // blend).  The row stride (80 or 48 bytes) puts 8 consecutive rows' 16-byte reads in 8
+  // different LDS bank groups (a 64-byte stride would use 2).
+  double v64[kPqMaxK][SUB + 2];
+  double lsh[SUB][SUB];
+  float l32[SUB][SUB];               // the fp32 factor (H-weighted)
+  double red[16][kPqWaves];
+};
+
+// Per-call constants of the preparation (identical in every thread).
+struct PqConsts {
+  int se, eb, sq;      // S = 2^se (table), bias parts x 2^eb, Sq = 2^sq (unit-norm table)
+  bool finite;         // every table entry finite (else every sub-vector takes the fp64 scan)
+  double rho, nu, nul, B, betab, Mv, Shb;  // bound terms of the table side (S units)
+  double kv, kr, kl, kb, kbeta;            // the same per row, over ||w_j|| or ||w_j||^2
+  double lf;                               // ||L||_F rounded up (H-weighted)
+  double c_rr, c_x, c_d, c_l;              // E(R) = R (c_rr R + c_x ||x|| + c_d ||x - x'|| + c_l ||lo||)
+  double rhoq, nuq, nulq;                  // the same for the unit-norm table (Sq units)
+};
+
+// The table operands and bound terms.  Thread t handles row t (rows >= k are pads: zero
+// operand, bias -65504 x 2^15).
+template <int SUB, int MODE, int DT>
+__device__ __forceinline__ PqConsts pq_prep(const float* __restrict__ cb, int k,
+                                            const float* __restrict__ chol,
+                                            PqShared<SUB, MODE == kBlend>& sh) {
+  const int t = threadIdx.x;
+  if (MODE == kHWeighted && t < SUB * SUB) {
+    sh.lsh[t / SUB][t % SUB] = (double)chol[t];
+    sh.l32[t / SUB][t % SUB] = chol[t];
+  }
+  __syncthreads();
+  double lf2 = 0.0;
+  if constexpr (MODE == kHWeighted) {
+#pragma unroll 1
+    for (int i = 0; i < SUB * SUB; ++i) lf2 += sh.lsh[i / SUB][i % SUB] * sh.lsh[i / SUB][i % SUB];
+  }
+  const bool real = t < k;
+  double c[SUB], v[SUB], hb;
+#pragma unroll
+  for (int e = 0; e < SUB; ++e) c[e] = real ? (double)cb[(int64_t)t * SUB + e] : 0.0;
+  if constexpr (MODE == kHWeighted) {
+    double w[SUB], b2 = 0.0;
+#pragma unroll
+    for (int a = 0; a < SUB; ++a) {
+      double s = 0.0;
+#pragma unroll
+      for (int b = 0; b < SUB; ++b) s += c[b] * sh.lsh[b][a];  // (c L)_a
+      w[a] = s;
+      b2 += s * s;
+    }
+    hb = 0.5 * b2;
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) {
+      double s = 0.0;
+#pragma unroll
+      for (int a = 0; a < SUB; ++a) s += w[a] * sh.lsh[e][a];  // (w L^T)_e = (c H)_e
+      v[e] = s;
+    }
+  } else {
+    double b2 = 0.0;
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) {
+      v[e] = c[e];
+      b2 += c[e] * c[e];
+    }
+    hb = 0.5 * b2;
+  }
+  double mv = 0.0, ic = 0.0, mq = 0.0, fin = 0.0;
+#pragma unroll
+  for (int e = 0; e < SUB; ++e) {
+    sh.v64[t][e] = v[e];
+    mv = fmax(mv, fabs(v[e]));
+    fin += 0.0 * v[e];
+  }
+  sh.v64[t][SUB] = hb;
+  sh.v64[t][SUB + 1] = 0.0;
+  fin += 0.0 * hb;
+  if constexpr (MODE == kBlend) {
+    double cn2 = 0.0;
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) cn2 += c[e] * c[e];
+    const double cn = sqrt(cn2);
+    ic = cn > 0.0 ? 1.0 / cn : 0.0;
+    sh.v64[t][SUB + 1] = ic;
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) mq = fmax(mq, fabs(c[e] * ic));
+  }
+  double r1[4] = {mv, hb, mq, fin == 0.0 ? 0.0 : 1.0};  // fin: NaN for a non-finite row
+  block_max(r1, sh.red);
+  PqConsts pc;
+  pc.finite = r1[3] == 0.0;
+  pc.lf = up(sqrt(lf2)) * (1.0 + 0x1p-30);
+  int se = 0;
+  if (r1[0] > 0.0) se = 14 - ilogb(r1[0]);
+  if (r1[1] > 0.0) se = min(se, 28 - ilogb(r1[1]));
+  se = max(-900, min(900, se));
+  const double S = ldexp(1.0, se);
+  int eb = r1[1] > 0.0 ? ilogb(S * r1[1]) - 14 : -14;
+  eb = max(-14, min(15, eb));
+  const int sq = r1[2] > 0.0 ? 14 - ilogb(r1[2]) : 0;
+  pc.se = se;
+  pc.eb = eb;
+  pc.sq = sq;
+
+  // fp16 parts of S v_j and their residuals
+  _Float16 vh[SUB], vl[SUB];
+  double rr = 0.0, nh2 = 0.0, nl2 = 0.0, nv2 = 0.0;
+#pragma unroll
+  for (int e = 0; e < SUB; ++e) {
+    const double sv = S * v[e];
+    vh[e] = half_of(sv);
+    const double d1 = sv - (double)vh[e];
+    vl[e] = half_of(d1);
+    const double d2 = d1 - (double)vl[e];
+    rr += d2 * d2;
+    nh2 += (double)vh[e] * (double)vh[e];
+    nl2 += (double)vl[e] * (double)vl[e];
+    nv2 += sv * sv;
+  }
+  // the bias -S b_j / 2 as (h1 + h2) 2^eb
+  const double bias = -S * hb;
+  const double bs = ldexp(bias, -eb);
+  const _Float16 h1 = half_of(bs);
+  const _Float16 h2 = half_of(bs - (double)h1);
+  const double cbm = ldexp(fabs((double)h1) + fabs((double)h2), eb);
+  const double cbx = ldexp((double)h1 + (double)h2, eb);
+  const _Float16 pm = real ? (_Float16)0.f : (_Float16)(-kPadMark);
+  const _Float16 z16 = (_Float16)0.f;
+  const int tile = t >> 5, r = t & 31;
+  if constexpr (SUB == 8) {
+    sh.fa[tile][r] = h8(pkh(vh[0], vh[1]), pkh(vh[2], vh[3]), pkh(vh[4], vh[5]), pkh(vh[6], vh[7]));
+    sh.fa[tile][r + 32] = h8(pkh(vl[0], vl[1]), pkh(vl[2], vl[3]), pkh(vl[4], vl[5]), pkh(vl[6], vl[7]));
+    sh.fb[tile][r][0] = pkh(h1, h2);
+    sh.fb[tile][r][1] = pkh(pm, z16);
+    sh.fb[tile][r + 32][0] = 0u;
+    sh.fb[tile][r + 32][1] = 0u;
+  } else {
+    // K slots, lanes 0-31: vh vl; lanes 32-63: h1 h2 pad-mark, then (fp32 inputs) vh again
+    // against the inputs' lo parts
+    sh.fa[tile][r] = h8(pkh(vh[0], vh[1]), pkh(vh[2], vh[3]), pkh(vl[0], vl[1]), pkh(vl[2], vl[3]));
+    if (DT == A2ATS_F32)
+      sh.fa[tile][r + 32] = h8(pkh(h1, h2), pkh(pm, vh[0]), pkh(vh[1], vh[2]), pkh(vh[3], z16));
+    else
+      sh.fa[tile][r + 32] = h8(pkh(h1, h2), pkh(pm, z16), 0u, 0u);
+  }
+  // row terms, and the same divided by the row's size: n_j = ||w_j|| (||c_j|| without H), so
+  // that b_j / 2 = n_j^2 / 2 (a zero row has no error terms at all)
+  const double rho_j = up(sqrt(rr)), nu_j = up(up(sqrt(nh2)) + up(sqrt(nl2))), nul_j = up(sqrt(nl2));
+  const double cb_j = up(cbm * (1.0 + 0x1p-22)), beta_j = up(fabs(cbx - bias) + kRnd * cbm);
+  const double nj = sqrt(2.0 * hb) * (1.0 - 0x1p-40);
+  const double inj = nj > 0.0 ? 1.0 / nj : 0.0, inj2 = inj * inj;
+  double r2[14] = {rho_j, nu_j, nul_j, up(sqrt(nv2)), cb_j, beta_j, 0.0, 0.0, 0.0,
+                   up(nu_j * inj), up(rho_j * inj), up(nul_j * inj), up(up(cb_j * inj2)),
+                   up(up(beta_j * inj2))};
+  if constexpr (MODE == kBlend) {
+    const double Sq = ldexp(1.0, sq);
+    _Float16 ch[SUB], cl[SUB];
+    double rq = 0.0, qh2 = 0.0, ql2 = 0.0;
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) {
+      const double u = Sq * (c[e] * ic);
+      ch[e] = half_of(u);
+      const double d1 = u - (double)ch[e];
+      cl[e] = half_of(d1);
+      const double d2 = d1 - (double)cl[e];
+      rq += d2 * d2;
+      qh2 += (double)ch[e] * (double)ch[e];
+      ql2 += (double)cl[e] * (double)cl[e];
+    }
+    if constexpr (SUB == 8) {
+      sh.fq[tile][r] = h8(pkh(ch[0], ch[1]), pkh(ch[2], ch[3]), pkh(ch[4], ch[5]), pkh(ch[6], ch[7]));
+      sh.fq[tile][r + 32] = h8(pkh(cl[0], cl[1]), pkh(cl[2], cl[3]), pkh(cl[4], cl[5]), pkh(cl[6], cl[7]));
+    } else {
+      sh.fq[tile][r] = h8(pkh(ch[0], ch[1]), pkh(ch[2], ch[3]), pkh(cl[0], cl[1]), pkh(cl[2], cl[3]));
+      if (DT == A2ATS_F32)
+        sh.fq[tile][r + 32] = h8(0u, pkh(z16, ch[0]), pkh(ch[1], ch[2]), pkh(ch[3], z16));
+      else
+        sh.fq[tile][r + 32] = h8(0u, 0u, 0u, 0u);
+    }
+    r2[6] = up(sqrt(rq));
+    r2[7] = up(up(sqrt(qh2)) + up(sqrt(ql2)));
+    r2[8] = up(sqrt(ql2));
+  }
+  block_max(r2, sh.red);  // also publishes the operands written above
+  pc.rho = r2[0];
+  pc.nu = r2[1];
+  pc.nul = r2[2];
+  pc.Mv = r2[3];
+  pc.B = r2[4];
+  pc.betab = r2[5];
+  pc.Shb = up(ldexp(r1[1], se));
+  pc.rhoq = r2[6];
+  pc.nuq = r2[7];
+  pc.nulq = r2[8];
+  pc.kv = r2[9];
+  pc.kr = r2[10];
+  pc.kl = r2[11];
+  pc.kb = r2[12];
+  pc.kbeta = r2[13];
+  {
+    // the bound for rows of size at most R (score_bound_r), its terms collected
+    constexpr int terms = (SUB == 8 ? 2 * SUB + 1 : 2 * SUB + 3) + (DT == A2ATS_F32 ? SUB : 0);
+    const double g = (terms + 2) * kRnd, f = (1.0 + 0x1p-16) * (1.0 + 0x1p-30);
+    pc.c_rr = (g * pc.kb + pc.kbeta) * f + 0x1p-40 * pc.kb;
+    pc.c_x = (g * pc.kv + pc.kr) * f + 0x1p-40 * pc.kv;
+    pc.c_d = (g * pc.kv + pc.kr + pc.kv + pc.kr) * f;
+    pc.c_l = (2.0 * g * pc.kv + pc.kl) * f;
+  }
+  return pc;
+}
+
+// The raw dwords of one sub-vector: SUB bf16 (SUB / 2 dwords) or SUB fp32.
+template <int DT, int SUB>
+struct Raw {
+  static constexpr int W = DT == A2ATS_BF16 ? SUB / 2 : SUB;
+  unsigned w[W];
+};
+
+template <int DT, int SUB>
+__device__ __forceinline__ Raw<DT, SUB> load_raw(const void* base, int64_t elem, bool ok) {
+  Raw<DT, SUB> r;
+  constexpr int W = Raw<DT, SUB>::W;
+  const unsigned* p = reinterpret_cast<const unsigned*>(
+      static_cast<const char*>(base) + (ok ? elem : 0) * (DT == A2ATS_BF16 ? 2 : 4));
+  if constexpr (W == 2) {
+    const uint2 a = ok ? *reinterpret_cast<const uint2*>(p) : make_uint2(0u, 0u);
+    r.w[0] = a.x;
+    r.w[1] = a.y;
+  } else {
+#pragma unroll
+    for (int q = 0; q < W / 4; ++q) {
+      const uint4 a = ok ? reinterpret_cast<const uint4*>(p)[q] : make_uint4(0u, 0u, 0u, 0u);
+      r.w[4 * q] = a.x;
+      r.w[4 * q + 1] = a.y;
+      r.w[4 * q + 2] = a.z;
+      r.w[4 * q + 3] = a.w;
+    }
+  }
+  return r;
+}
+
+template <int DT, int SUB>
+__device__ __forceinline__ void raw_floats(const Raw<DT, SUB>& r, float (&x)[SUB]) {
+  if constexpr (DT == A2ATS_BF16) {
+#pragma unroll
+    for (int i = 0; i < SUB / 2; ++i) {
+      x[2 * i] = __uint_as_float(r.w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(r.w[i] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) x[i] = __uint_as_float(r.w[i]);
+  }
+}
+
+template <int DT, int SUB>
+__device__ __forceinline__ Raw<DT, SUB> raw_sel(const Raw<DT, SUB>& a, const Raw<DT, SUB>& b, bool second) {
+  Raw<DT, SUB> r;
+#pragma unroll
+  for (int i = 0; i < Raw<DT, SUB>::W; ++i) r.w[i] = second ? b.w[i] : a.w[i];
+  return r;
+}
+
+// B operands of one block column.  hi: the fp16 parts (x itself for bf16); lo: fp32 inputs'
+// second parts.  sub_dim 8: B1 = [hi | hi], B2 = [lo | 0].  sub_dim 4: lanes 0-31 [hi hi],
+// lanes 32-63 [2^eb 2^eb 2^15 lo 0] (the bias and pad-mark slots; `tail` for a table without
+// bias, the unit-norm one, has zeros there).
+template <int DT, int SUB>
+__device__ __forceinline__ void make_b(const Raw<DT, SUB>& r, int hh, unsigned bias_pk,
+                                       unsigned mark_pk, half8& B1, half8& B2) {
+  float x[SUB];
+  raw_floats<DT, SUB>(r, x);
+  unsigned p[SUB / 2], l[SUB / 2];
+#pragma unroll
+  for (int i = 0; i < SUB / 2; ++i) {
+    p[i] = pk16(x[2 * i], x[2 * i + 1]);
+    if (DT == A2ATS_F32) l[i] = pk16(x[2 * i] - lo16(p[i]), x[2 * i + 1] - hi16(p[i]));
+  }
+  if constexpr (SUB == 8) {
+    B1 = h8(p[0], p[1], p[2], p[3]);
+    if (DT == A2ATS_F32) B2 = hh ? h8(0u, 0u, 0u, 0u) : h8(l[0], l[1], l[2], l[3]);
+  } else {
+    if (DT == A2ATS_F32) {
+      const unsigned mk = mark_pk & 0xFFFFu;  // 2^15 in the low half
+      B1 = hh ? h8(bias_pk, mk | (l[0] << 16), (l[0] >> 16) | (l[1] << 16), l[1] >> 16)
+              : h8(p[0], p[1], p[0], p[1]);
+    } else {
+      B1 = hh ? h8(bias_pk, mark_pk, 0u, 0u) : h8(p[0], p[1], p[0], p[1]);
+    }
+  }
+}
+
+// Norm terms of one sub-vector against what the matrix cores see of it, in fp32 rounded
+// up: ||x||, ||x - x'|| (x' = the fp16 parts, a subnormal part possibly flushed) and ||lo||
+// (fp32 inputs' second parts).  x - hi - lo is exact in fp32 (each part is the other's
+// truncation).  A square that overflows makes the bound infinite (the fp64 scan decides).
+template <int DT, int SUB>
+__device__ __forceinline__ void norms(const Raw<DT, SUB>& r, float& nx, float& nd, float& nl) {
+  float x[SUB];
+  raw_floats<DT, SUB>(r, x);
+  if constexpr (DT == A2ATS_BF16) {
+    // a bf16 value is exact in fp16 when 2^-14 <= |x| <= 65504 (its 8 significant bits fit);
+    // otherwise x' is 0, a subnormal or 65504 and |x - x'| <= |x|
+    float sx = 0.f, sd = 0.f;
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) {
+      const float ax = fabsf(x[e]);
+      const float d = __builtin_amdgcn_fmed3f(ax, (float)kHalfMin, 65504.f) == ax ? 0.f : x[e];
+      sx = __fmaf_rn(x[e], x[e], sx);
+      sd = __fmaf_rn(d, d, sd);
+    }
+    nx = sqrtf(sx * (1.f + 0x1p-18f)) * (1.f + 0x1p-20f);
+    nd = sqrtf(sd * (1.f + 0x1p-18f)) * (1.f + 0x1p-20f);
+    nl = 0.f;
+    return;
+  }
+  float sx = 0.f, sd = 0.f, sl = 0.f;
+#pragma unroll
+  for (int i = 0; i < SUB / 2; ++i) {
+    const unsigned p = pk16(x[2 * i], x[2 * i + 1]);
+    const float h[2] = {lo16(p), hi16(p)};
+    float lw[2] = {0.f, 0.f};
+    if (DT == A2ATS_F32) {
+      const unsigned q = pk16(x[2 * i] - h[0], x[2 * i + 1] - h[1]);
+      lw[0] = lo16(q);
+      lw[1] = hi16(q);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float xe = x[2 * i + u], he = h[u], le = lw[u];
+      float d = fabsf(xe - he - le);
+      if (fabsf(he) < (float)kHalfMin) d += fabsf(he);
+      if (DT == A2ATS_F32 && fabsf(le) < (float)kHalfMin) d += fabsf(le);
+      sx = __fmaf_rn(xe, xe, sx);
+      sd = __fmaf_rn(d, d, sd);
+      sl = __fmaf_rn(le, le, sl);
+    }
+  }
+  // SUB-term fp32 sums: within 2^-20 relative; sqrt within an ulp
+  nx = sqrtf(sx * (1.f + 0x1p-18f)) * (1.f + 0x1p-20f);
+  nd = sqrtf(sd * (1.f + 0x1p-18f)) * (1.f + 0x1p-20f);
+  nl = sqrtf(sl * (1.f + 0x1p-18f)) * (1.f + 0x1p-20f);
+}
+
+// Rigorous bound on |acc_j - S s_j| for every row j (S units).
+template <int DT, int SUB>
+__device__ __forceinline__ double score_bound(double nx, double nd, double nl, double rho,
+                                              double nu, double nul, double B, double betab) {
+  constexpr int terms = (SUB == 8 ? 2 * SUB + 1 : 2 * SUB + 3) + (DT == A2ATS_F32 ? SUB : 0);
+  const double g = (terms + 2) * kRnd;
+  const double nxh = nx + nl + nd;
+  return (g * (B + (nxh + nl) * nu) + (nx + nd) * rho + nd * (nu + rho) + nl * nul + betab) *
+             (1.0 + 0x1p-16) +
+         0x1p-40 * (B + nx * nu) + 0x1p-120;
+}
+
+// An empty use that pins a fold's result where it is written (the compiler would otherwise
+// sink the fold below later tiles' MFMAs, keeping every tile's accumulators live).
+__device__ __forceinline__ void pin(const f16v& a, const f16v& b) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) asm volatile("" ::"v"(a[r]), "v"(b[r]));
+}
+
+// The bound for the rows that can reach a score s (the certificate of the plain and
+// H-weighted codes): only rows with n_j <= R do (s_j <= ||z|| n_j - n_j^2 / 2 in the metric of
+// H, z = x L), and every term of a row's bound grows with n_j, so the per-row ratios times R
+// (or R^2) bound it; the preparation collects the terms into E(R) = R (c_rr R + c_x ||x|| +
+// c_d ||x - x'|| + c_l ||lo||).
+
+// Largest change of a slot value by its packed low bits.
+__device__ __forceinline__ double pack_slack(float a) { return fabs((double)a) * 0x1p-18 + 0x1p-140; }
+
+// Exchange the lane pair's slot maxima (block hh's 32 slots end in lane (col, hh)), pack the
+// slot number into the low 5 bits and return the largest two values.
+__device__ __forceinline__ void top2_slots(const f16v& m0, const f16v& m1, float& a0, float& a1) {
+  float v[32];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(m0[r]), __float_as_uint(m1[r]),
+                                                     false, false);
+    v[r] = __uint_as_float((pr[0] & 0xFFFFFFE0u) | (unsigned)r);            // rows of half 0
+    v[16 + r] = __uint_as_float((pr[1] & 0xFFFFFFE0u) | (unsigned)(16 + r));  // half 1
+  }
+  float b0 = -INFINITY, b1 = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 32; i += 2) {
+    const float md = __builtin_amdgcn_fmed3f(b0, v[i], v[i + 1]);
+    b0 = fmax3(b0, v[i], v[i + 1]);
+    b1 = __builtin_elementwise_maximum(b1, md);
+  }
+  a0 = b0;
+  a1 = b1;
+}
+
+// Row (within a tile) of slot i: accumulator register r = i & 15 of lane half i >> 4.
+__device__ __forceinline__ int slot_row(unsigned i) {
+  return 8 * ((i & 15u) >> 2) + 4 * (i >> 4) + (i & 3u);
+}
+
+// Wave-wide argmax of (s, j): larger s, then smaller j; lanes with j < 0 hold nothing.
+__device__ __forceinline__ void wave_argmax(double& s, int& j) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const double so = __shfl_xor(s, o);
+    const int jo = __shfl_xor(j, o);
+    if (jo >= 0 && (j < 0 || so > s || (so == s && jo < j))) {
+      s = so;
+      j = jo;
+    }
+  }
+}
+
+// ||x - c||^2 summed in the definition's order, without fused multiply-adds.
+template <int SUB>
+__device__ __forceinline__ double sq_dist(const double (&x)[SUB], const double* c) {
+#pragma clang fp contract(off)
+  double s = 0.0;
+#pragma unroll
+  for (int e = 0; e < SUB; ++e) {
+    const double df = x[e] - c[e];
+    s += df * df;
+  }
+  return s;
+}
+
+// The blended score of one row in fp64: beta (-e_j / max e) + (1 - beta) cos(q, c_j), the
+// divisions replaced by the reciprocals iem = 1 / max e, iqn = 1 / ||q||, icn = 1 / ||c_j||;
+// zero norms and a zero maximum error as the definition has them.
+template <int SUB>
+__device__ __forceinline__ double blend_score(const double (&x)[SUB], const double (&q)[SUB],
+                                              const double* c, double icn, double iem, double qn,
+                                              double iqn, double beta) {
+#pragma clang fp contract(off)
+  double e2 = 0.0, dot = 0.0;
+#pragma unroll
+  for (int e = 0; e < SUB; ++e) {
+    const double df = x[e] - c[e];
+    e2 += df * df;
+    dot += q[e] * c[e];
+  }
+  const double cosv = (qn > 0.0 && icn > 0.0) ? dot * (iqn * icn) : 0.0;
+  const double err = iem > 0.0 ? e2 * iem : 0.0;
+  return beta * (-err) + (1.0 - beta) * cosv;
+}
+
+template <int DT, int SUB, int MODE>
+__global__ __launch_bounds__(kPqThreads, kPqWgPerCu) void pq_encode_mfma(
     const void* __restrict__ x, int64_t n, const int32_t* __restrict__ idx, int64_t n_sel,
     int64_t heads, const float* __restrict__ cb, int k, const float* __restrict__ chol,
     const void* __restrict__ query, int64_t nq, double beta, uint8_t* __restrict__ codes) {
-  constexpr int M = kD / SUB;  // sub-spaces per row
-  __shared__ double w64[kPqMaxK][SUB];
-  __shared__ float w32[kPqMaxK][SUB];
-  __shared__ double b64[kPqMaxK];
-  __shared__ float b32[kPqMaxK];
-  __shared__ float wn32[kPqMaxK];   // ||w_j|| rounded up (bound term)
-  __shared__ float eb32[kPqMaxK];   // c b_j rounded up (bound term)
-  __shared__ double icn[kPqMaxK];   // 1 / ||c_j|| (0 for a zero centroid; blend)
-  __shared__ double lsh[SUB][SUB];
-  const int t = threadIdx.x;
-  // ---- the transformed codebook (or, for the blend, the codebook and its norms)
-  if (MODE == kHWeighted && t < SUB * SUB) lsh[t / SUB][t % SUB] = (double)chol[t];
-  __syncthreads();
-  for (int j = t; j < k; j += kPqThreads) {
-    double c[SUB];
-#pragma unroll
-    for (int e = 0; e < SUB; ++e) c[e] = (double)cb[(int64_t)j * SUB + e];
-    double w[SUB];
-#pragma unroll
-    for (int e = 0; e < SUB; ++e) {
-      if (MODE == kHWeighted) {
-        double s = 0.0;
-#pragma unroll
-        for (int a = 0; a < SUB; ++a) s += c[a] * lsh[a][e];  // (c L)_e
-        w[e] = s;
-      } else {
-        w[e] = c[e];
-      }
-    }
-    double b = 0.0;
-#pragma unroll
-    for (int e = 0; e < SUB; ++e) {
-      b += w[e] * w[e];
-      w64[j][e] = w[e];
-      w32[j][e] = (float)w[e];
-    }
-    b64[j] = b;  // ||w_j||^2 (for the blend: ||c_j||^2)
-    b32[j] = (float)b;
-    const double wn = sqrt(b);
-    wn32[j] = round_up_f(wn * (1.0 + 0x1p-40));
-    eb32[j] = round_up_f(kBoundC * b * (1.0 + 0x1p-40));
-    icn[j] = wn > 0.0 ? 1.0 / wn : 0.0;
-  }
-  __syncthreads();
+  constexpr bool BLEND = MODE == kBlend;
+  constexpr int M = kD / SUB;   // sub-spaces per row
+  constexpr int RPI = 64 / M;   // rows per wave iteration
+  __shared__ PqShared<SUB, BLEND> sh;
+  const PqConsts pc = pq_prep<SUB, MODE, DT>(cb, k, chol, sh);
 
-  // items: (head, selected row, group of R consecutive sub-spaces); every centroid read from
-  // LDS serves the thread's R sub-vectors
-  constexpr int G = M / R;  // groups per row
-  const int64_t items = heads * n_sel * G;
-  for (int64_t it = (int64_t)blockIdx.x * kPqThreads + t; it < items;
-       it += (int64_t)gridDim.x * kPqThreads) {
-    const int grp = (int)(it % G);
-    const int64_t hi = it / G;  // head * n_sel + selected row
-    const int64_t head = hi / n_sel;
-    const int64_t sel = hi % n_sel;
-    const int64_t row = idx ? (int64_t)idx[head * n_sel + sel] : sel;
-    if (row < 0 || row >= n) continue;  // out-of-range index entries are skipped
-    const int64_t xoff = (head * n + row) * kD + (int64_t)grp * R * SUB;
-    float xs[R][SUB];  // exact: the inputs are fp32 or bf16
+  const int lane = threadIdx.x & 63, col = lane & 31, hh = lane >> 5;
+  // the table operand in registers, sub_dim 8: the bias operand (lanes 0-31) too; the blend,
+  // which needs more registers, reads them from LDS at each tile
+  constexpr int RT = BLEND ? 1 : kPqTiles;
+  half8 A[RT];
+  unsigned fb0[RT], fb1[RT];
+  if constexpr (!BLEND) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int tt = 0; tt < kPqTiles; ++tt) {
+      A[tt] = sh.fa[tt][lane];
+      fb0[tt] = sh.fb[tt][lane][0];
+      fb1[tt] = sh.fb[tt][lane][1];
+    }
+  }
+  // (lds_lane: the lane index plus an opaque zero set in each iteration, so that the
+  // loop-invariant reads are not hoisted out of the loop into registers)
+  int lds_lane = lane, lds_zero = 0;
+  auto a_op = [&](int tt) { return BLEND ? sh.fa[tt][lds_lane] : A[BLEND ? 0 : tt]; };
+  auto fb_op = [&](int tt, int w) {
+    return BLEND ? sh.fb[tt][lds_lane][w] : (w ? fb1[BLEND ? 0 : tt] : fb0[BLEND ? 0 : tt]);
+  };
+  const unsigned e2 = pk16(ldexpf(1.f, pc.eb), ldexpf(1.f, pc.eb));
+  const unsigned mk = pk16(32768.f, 0.f);
+  const half8 Bb = hh ? h8(0u, 0u, 0u, 0u) : h8(e2, mk, 0u, 0u);  // bias operand, sub_dim 8
+  const f16v zero = {};
+
+  // this lane's column in each block: row offset within the iteration and sub-space
+  int lr[2], ss[2];
 #pragma unroll
-      for (int e = 0; e < SUB; ++e) xs[r][e] = load_elem(x, DT, xoff + r * SUB + e);
-    if (MODE == kBlend) {
-      const int64_t qoff = (head * nq + (nq == 1 ? 0 : row)) * kD + (int64_t)grp * R * SUB;
-      double qs[R][SUB], qn[R], emax[R];
+  for (int b = 0; b < 2; ++b) {
+    lr[b] = (32 * b + col) / M;
+    ss[b] = (32 * b + col) % M;
+  }
+  const int lr_own = lane / M, ss_own = lane % M;  // the sub-vector this lane decides
+
+  // Iterations: (head, group of RPI selected rows), wave-uniform (scalar registers); a wave
+  // takes every stride-th one, advanced without a division per step.
+  const int64_t G = (n_sel + RPI - 1) / RPI;
+  const int64_t stride = (int64_t)gridDim.x * kPqWaves;
+  const int64_t st_h = stride / G, st_g = stride % G;
+  const int64_t it0 = (int64_t)blockIdx.x * kPqWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t h_cur = it0 / G, g_cur = it0 % G;
+  auto advance = [&](int64_t& h, int64_t& g) {
+    h += st_h;
+    g += st_g;
+    if (g >= G) {
+      g -= G;
+      ++h;
+    }
+  };
+  // the row of this lane's column in block row l_r of iteration (h, g); false when none
+  auto locate = [&](int64_t h, int64_t g, int l_r, int64_t& row) {
+    const int64_t sel = g * RPI + l_r;
+    row = -1;
+    if (h < heads && sel < n_sel) row = idx ? (int64_t)idx[h * n_sel + sel] : sel;
+    return row >= 0 && row < n;
+  };
+
+  Raw<DT, SUB> nx_raw[2], nq_raw[2];
+  auto fetch = [&](int64_t h, int64_t g, Raw<DT, SUB> (&xr)[2], Raw<DT, SUB> (&qr)[2]) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        double qn2 = 0.0;
+    for (int b = 0; b < 2; ++b) {
+      int64_t row = 0;
+      const bool ok = locate(h, g, lr[b], row);
+      xr[b] = load_raw<DT, SUB>(x, ((h * n + row) * kD + ss[b] * SUB), ok);
+      if constexpr (BLEND)
+        qr[b] = load_raw<DT, SUB>(query, ((h * nq + (nq == 1 ? 0 : row)) * kD + ss[b] * SUB), ok);
+    }
+  };
+  fetch(h_cur, g_cur, nx_raw, nq_raw);
+
+  for (; h_cur < heads; advance(h_cur, g_cur)) {
+    if constexpr (BLEND || MODE == kHWeighted) {
+      int z = 0;
+      asm volatile("" : "+v"(z));
+      lds_zero = z;
+      lds_lane = lane + z;
+    }
+    const Raw<DT, SUB> xr[2] = {nx_raw[0], nx_raw[1]};
+    Raw<DT, SUB> qr[2];
+    if constexpr (BLEND) {
+      qr[0] = nq_raw[0];
+      qr[1] = nq_raw[1];
+    }
+    {
+      int64_t h_nx = h_cur, g_nx = g_cur;
+      advance(h_nx, g_nx);
+      fetch(h_nx, g_nx, nx_raw, nq_raw);  // the next iteration's inputs stay in flight
+    }
+
+    int64_t orow;
+    const int64_t ohead = h_cur;
+    const bool own_ok = locate(h_cur, g_cur, lr_own, orow);
+    const Raw<DT, SUB> xo = raw_sel<DT, SUB>(xr[0], xr[1], hh);
+
+    half8 B1[2], B2[2];
 #pragma unroll
-        for (int e = 0; e < SUB; ++e) {
-          qs[r][e] = (double)load_elem(query, DT, qoff + r * SUB + e);
-          qn2 += qs[r][e] * qs[r][e];
+    for (int b = 0; b < 2; ++b) make_b<DT, SUB>(xr[b], hh, e2, mk, B1[b], B2[b]);
+
+    // scores of tile tt for both blocks (S units, bias included)
+    auto tile_scores = [&](int tt, const half8 (&b1)[2], const half8 (&b2)[2], unsigned mark_flip,
+                           f16v& s0, f16v& s1) {
+      const half8 at0 = a_op(tt);
+      if constexpr (SUB == 8) {
+        const f16v cbias = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            h8(fb_op(tt, 0), fb_op(tt, 1) ^ (hh ? 0u : mark_flip), 0u, 0u), Bb, zero, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(at0, b1[0], cbias, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(at0, b1[1], cbias, 0, 0, 0);
+        if constexpr (DT == A2ATS_F32) {
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(at0, b2[0], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(at0, b2[1], s1, 0, 0, 0);
         }
-        const double qnr = sqrt(qn2);
-        qn[r] = qnr > 0.0 ? 1.0 / qnr : 0.0;  // held as 1 / ||q_s|| (0: cosine 0)
-        emax[r] = 0.0;
+      } else {
+        u4v a = __builtin_bit_cast(u4v, at0);
+        a[1] ^= hh ? mark_flip : 0u;  // the pad mark: lanes 32-63, low half of dword 1
+        const half8 at = __builtin_bit_cast(half8, a);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(at, b1[0], zero, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(at, b1[1], zero, 0, 0, 0);
       }
-      for (int j = 0; j < k; ++j) {
-        double cv[SUB];
+    };
+
+    int code = 0;
+    bool open = false;
+    // this lane's sub-vector, exact, and the bound E on its MFMA scores' error (formed after
+    // the fold, which needs the registers)
+    double xs[SUB], nx, E, xnd, xnl;
+    auto finals = [&]() {
+      Raw<DT, SUB> xw = xo;
 #pragma unroll
-        for (int a = 0; a < SUB; ++a) cv[a] = w64[j][a];
+      for (int i = 0; i < Raw<DT, SUB>::W; ++i) asm volatile("" : "+v"(xw.w[i]));
+      float xf[SUB];
+      raw_floats<DT, SUB>(xw, xf);
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          double e2 = 0.0;
+      for (int e = 0; e < SUB; ++e) xs[e] = xf[e];
+      float fx, fd, fl;
+      norms<DT, SUB>(xw, fx, fd, fl);
+      nx = fx;
+      xnd = fd;
+      xnl = fl;
+      if constexpr (BLEND) E = score_bound<DT, SUB>(nx, xnd, xnl, pc.rho, pc.nu, pc.nul, pc.B, pc.betab);
+    };
+    // all of a broadcast sub-vector finite (a non-finite one has code 0: every distance is
+    // inf or NaN)
+    auto all_finite = [](const double (&v)[SUB]) {
+      bool f = true;
 #pragma unroll
-          for (int a = 0; a < SUB; ++a) {
-            const double df = (double)xs[r][a] - cv[a];
-            e2 += df * df;
+      for (int e = 0; e < SUB; ++e) f = f && (v[e] - v[e] == 0.0);
+      return f;
+    };
+
+    if constexpr (!BLEND) {
+      f16v m0, m1;
+#pragma unroll
+      for (int tp = 0; tp < kPqTiles / 2; ++tp) {
+        f16v a0, a1, c0, c1;
+        tile_scores(2 * tp, B1, B2, 0u, a0, a1);
+        tile_scores(2 * tp + 1, B1, B2, 0u, c0, c1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          m0[r] = tp ? fmax3(m0[r], a0[r], c0[r]) : __builtin_elementwise_maximum(a0[r], c0[r]);
+          m1[r] = tp ? fmax3(m1[r], a1[r], c1[r]) : __builtin_elementwise_maximum(a1[r], c1[r]);
+        }
+        pin(m0, m1);
+        __builtin_amdgcn_sched_barrier(0);  // one tile pair's accumulators live at a time
+      }
+      float t0, t1;
+      top2_slots(m0, m1, t0, t1);
+      finals();
+      const int row = slot_row(__float_as_uint(t0) & 31u);
+      double sa = -INFINITY;
+      int ja = -1;
+#pragma unroll
+      for (int tt = 0; tt < kPqTiles; ++tt) {
+        const int j = 32 * tt + row;
+        if (j < k) {
+          double s = -sh.v64[j][SUB];
+#pragma unroll
+          for (int e = 0; e < SUB; ++e) s = fma(xs[e], sh.v64[j][e], s);
+          if (s > sa) {
+            sa = s;
+            ja = j;
           }
-          emax[r] = fmax(emax[r], e2);
         }
       }
-      double bs[R];
-      int bj[R];
+      // every row outside the winning slot: its MFMA score is at most t1 (plus the packing),
+      // its error at most E, or, when it could reach s_a at all, the bound for rows of size R
+      double Z = nx;  // ||z|| (z = x L; x itself without L), rounded up
+      if constexpr (MODE == kHWeighted) {
+        // z in fp32: each element within 2^-21 sum_b |x_b L_ba|, so ||z|| within
+        // 2^-21 ||x|| ||L||_F of the fp32 vector's norm
+        float xf[SUB];
+        raw_floats<DT, SUB>(xo, xf);
+        float z2 = 0.f;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        bs[r] = -INFINITY;
-        bj[r] = 0x7FFFFFFF;
-        emax[r] = emax[r] > 0.0 ? 1.0 / emax[r] : 0.0;  // held as 1 / max e (0: no error term)
+        for (int a = 0; a < SUB; ++a) {
+          float za = 0.f;
+#pragma unroll
+          for (int b = 0; b < SUB; ++b) za = __fmaf_rn(xf[b], sh.l32[b][a + lds_zero], za);
+          z2 = __fmaf_rn(za, za, z2);
+        }
+        Z = (double)(sqrtf(z2 * (1.f + 0x1p-18f)) * (1.f + 0x1p-20f)) + 0x1p-21 * nx * pc.lf;
       }
-      for (int j = 0; j < k; ++j) {
-        double cv[SUB];
+      const float disc = (float)fmax(0.0, Z * Z - 2.0 * sa) * (1.f + 0x1p-18f);
+      const double R = (Z + (double)(sqrtf(disc) * (1.f + 0x1p-20f))) * (1.0 + 0x1p-20) + 0x1p-60;
+      const double Ec = R * (pc.c_rr * R + pc.c_x * nx + pc.c_d * xnd + pc.c_l * xnl) + 0x1p-120;
+      const double lhs = ldexp(sa, pc.se);
+      const double rhs = (double)t1 + pack_slack(t1) + Ec;
+      code = ja;
+      open = own_ok && !(pc.finite && ja >= 0 && lhs > rhs);
+      // the rest: the whole wave scores the whole table in fp64 for one sub-vector at a time
+      unsigned long long todo = __ballot(open);
+      while (todo) {
+        const int src = __ffsll((long long)todo) - 1;
+        todo &= todo - 1;
+        double xb[SUB];
 #pragma unroll
-        for (int a = 0; a < SUB; ++a) cv[a] = w64[j][a];
-        const double ic = icn[j];
+        for (int e = 0; e < SUB; ++e) xb[e] = __shfl(xs[e], src);
+        const bool fin = all_finite(xb);
+        double bs = -INFINITY;
+        int bj = -1;
+        for (int j = lane; j < k; j += 64) {
+          double s = -sh.v64[j][SUB];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          double e2 = 0.0, dot = 0.0;
-#pragma unroll
-          for (int a = 0; a < SUB; ++a) {
-            const double df = (double)xs[r][a] - cv[a];
-            e2 += df * df;
-            dot += qs[r][a] * cv[a];
-          }
-          // the blend with reciprocals (fp64 throughout; rounding differs from the divided
-          // form by a few ulps, far inside any decided margin)
-          const double cosv = dot * qn[r] * ic;
-          const double err = e2 * emax[r];
-          const double sc = beta * (-err) + (1.0 - beta) * cosv;
-          if (better(sc, j, bs[r], bj[r])) {
-            bs[r] = sc;
-            bj[r] = j;
+          for (int e = 0; e < SUB; ++e) s = fma(xb[e], sh.v64[j][e], s);
+          if (s > bs) {  // a NaN score (a non-finite table row) never wins
+            bs = s;
+            bj = j;
           }
         }
+        wave_argmax(bs, bj);
+        if (lane == src) code = fin && bj >= 0 ? bj : 0;  // non-finite input: every distance
+                                                          // is inf or NaN, code 0
       }
-      uint8_t* cp = codes + (head * n + row) * M + grp * R;
-#pragma unroll
-      for (int r = 0; r < R; ++r) cp[r] = (uint8_t)bj[r];
     } else {
-      // z = x_s L in fp64 (x_s itself without L); the fp64 values are formed again for a
-      // close call rather than kept, which keeps the register count down
-      // (L is read from LDS at each use: an opaque zero offset keeps the compiler from
-      // hoisting all SUB x SUB fp64 entries into registers for the whole loop)
-      int opq = 0;
-      asm volatile("" : "+v"(opq));
-      const double* lp = &lsh[0][0] + opq;
-      auto z_of = [&](int r, double (&z)[SUB]) {
+      // ---- pass 1: max_j e_j through the smallest s_j (pad rows' mark flipped to +)
+      const unsigned flip = 0x8000u;  // sign of the pad mark's fp16
+      f16v m0, m1;
 #pragma unroll
-        for (int e = 0; e < SUB; ++e) {
-          if (MODE == kHWeighted) {
-            double sacc = 0.0;
+      for (int tp = 0; tp < kPqTiles / 2; ++tp) {
+        f16v a0, a1, c0, c1;
+        tile_scores(2 * tp, B1, B2, flip, a0, a1);
+        tile_scores(2 * tp + 1, B1, B2, flip, c0, c1);
 #pragma unroll
-            for (int a = 0; a < SUB; ++a) sacc += (double)xs[r][a] * lp[a * SUB + e];
-            z[e] = sacc;
-          } else {
-            z[e] = (double)xs[r][e];
-          }
+        for (int r = 0; r < 16; ++r) {
+          m0[r] = tp ? fmax3(m0[r], -a0[r], -c0[r]) : __builtin_elementwise_maximum(-a0[r], -c0[r]);
+          m1[r] = tp ? fmax3(m1[r], -a1[r], -c1[r]) : __builtin_elementwise_maximum(-a1[r], -c1[r]);
         }
-      };
-      double zn[R];
-      float zf[R][SUB];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        double z[SUB];
-        z_of(r, z);
-        double zn2 = 0.0;
-#pragma unroll
-        for (int e = 0; e < SUB; ++e) {
-          zn2 += z[e] * z[e];
-          zf[r][e] = (float)z[e];
-        }
-        zn[r] = sqrt(zn2);
+        pin(m0, m1);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // t_j = s~_j + E_j with E_j = c (||z|| ||w_j|| + b_j): the best a by t is certain when
-      // s~_a - E_a exceeds every other t_j (the second largest t)
-      float cz[R], t1[R], t2[R];
-      int ja[R];
+      double emax;
+      {
+        float t0, t1;
+        top2_slots(m0, m1, t0, t1);
+        finals();
+        double nx2 = 0.0;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        cz[r] = round_up_f(kBoundC * zn[r] * (1.0 + 0x1p-40));
-        t1[r] = -INFINITY;
-        t2[r] = -INFINITY;
-        ja[r] = 0;
-      }
-      for (int j = 0; j < k; ++j) {
-        float wv[SUB];
-#pragma unroll
-        for (int e = 0; e < SUB; ++e) wv[e] = w32[j][e];
-        const float hb = -0.5f * b32[j];
-        const float wn = wn32[j], eb = eb32[j];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          float sc = 0.f;
-#pragma unroll
-          for (int e = 0; e < SUB; ++e) sc = __fmaf_rn(zf[r][e], wv[e], sc);
-          sc += hb;  // -b/2 is exact in fp32 (a power-of-two scale of b32)
-          const float tj = sc + __fmaf_rn(cz[r], wn, eb);
-          t2[r] = fmaxf(t2[r], fminf(t1[r], tj));
-          if (tj > t1[r]) {
-            t1[r] = tj;
-            ja[r] = j;
-          }
-        }
-      }
-      int best[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int a = ja[r];
-        float sa = 0.f;  // the candidate's fp32 score, formed exactly as in the scan
-#pragma unroll
-        for (int e = 0; e < SUB; ++e) sa = __fmaf_rn(zf[r][e], w32[a][e], sa);
-        sa += -0.5f * b32[a];
-        const float ea = __fmaf_rn(cz[r], wn32[a], eb32[a]);
-        if ((double)sa - (double)ea > (double)t2[r]) {
-          best[r] = a;
-        } else {  // close call: every score in fp64
-          double z[SUB];
-          z_of(r, z);
-          double bs = -INFINITY;
-          int bj = 0x7FFFFFFF;
-          for (int j = 0; j < k; ++j) {
-            double sc = 0.0;
-#pragma unroll
-            for (int e = 0; e < SUB; ++e) sc += z[e] * w64[j][e];
-            sc -= 0.5 * b64[j];
-            if (better(sc, j, bs, bj)) {
-              bs = sc;
-              bj = j;
+        for (int e = 0; e < SUB; ++e) nx2 = fma(xs[e], xs[e], nx2);
+        const int row = slot_row(__float_as_uint(t0) & 31u);
+        double em = -INFINITY;
+        int je = -1;
+#pragma unroll 2
+        for (int tt = 0; tt < kPqTiles; ++tt) {
+          const int j = 32 * tt + row;
+          if (j < k) {
+            const double e2v = sq_dist<SUB>(xs, sh.v64[j]);
+            if (e2v > em) {
+              em = e2v;
+              je = j;
             }
           }
-          best[r] = bj;
+        }
+        const double tb = 2.0 * ldexp((double)t1 + pack_slack(t1) + E, -pc.se);
+        const double ub = nx2 + tb;
+        const double margin = 0x1p-44 * (nx2 + fabs(tb) + fabs(em));
+        emax = em;
+        bool open1 = own_ok && !(pc.finite && je >= 0 && em - margin > ub);
+        unsigned long long todo = __ballot(open1);
+        while (todo) {
+          const int src = __ffsll((long long)todo) - 1;
+          todo &= todo - 1;
+          double xb[SUB];
+#pragma unroll
+          for (int e = 0; e < SUB; ++e) xb[e] = __shfl(xs[e], src);
+          double mx = -INFINITY;
+          for (int j = lane; j < k; j += 64) mx = fmax(mx, sq_dist<SUB>(xb, sh.v64[j]));
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+          if (lane == src) emax = mx;
         }
       }
-      uint8_t* cp = codes + (head * n + row) * M + grp * R;
+      // ---- pass 2: the blend, up to the constant beta ||x||^2 / max e
+      const Raw<DT, SUB> qo = raw_sel<DT, SUB>(qr[0], qr[1], hh);
+      double qn;
+      {
+        float qf[SUB];
+        raw_floats<DT, SUB>(qo, qf);
+        double qn2 = 0.0;
 #pragma unroll
-      for (int r = 0; r < R; ++r) cp[r] = (uint8_t)best[r];
-      continue;
+        for (int e = 0; e < SUB; ++e) qn2 += (double)qf[e] * (double)qf[e];
+        qn = sqrt(qn2);
+      }
+      const double iqn = qn > 0.0 ? 1.0 / qn : 0.0;
+      const double iem = emax > 0.0 ? 1.0 / emax : 0.0;
+      const float al_own = (float)(2.0 * beta * ldexp(iem, -pc.se));
+      const float ga_own = (float)((1.0 - beta) * ldexp(iqn, -pc.sq));
+      float al[2], ga[2];
+      {
+        const float alp = __shfl_xor(al_own, 32), gap = __shfl_xor(ga_own, 32);
+        al[0] = hh ? alp : al_own;
+        al[1] = hh ? al_own : alp;
+        ga[0] = hh ? gap : ga_own;
+        ga[1] = hh ? ga_own : gap;
+      }
+      half8 Q1[2], Q2[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) make_b<DT, SUB>(qr[b], hh, 0u, 0u, Q1[b], Q2[b]);
+      // the blended fold value of tile tt, one block's q-accumulator at a time
+      auto blended = [&](int tt, f16v& s0, f16v& s1) {
+        tile_scores(tt, B1, B2, 0u, s0, s1);
+        const half8 fq = sh.fq[tt][lds_lane];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          f16v q = __builtin_amdgcn_mfma_f32_32x32x16_f16(fq, Q1[b], zero, 0, 0, 0);
+          if constexpr (SUB == 8 && DT == A2ATS_F32)
+            q = __builtin_amdgcn_mfma_f32_32x32x16_f16(fq, Q2[b], q, 0, 0, 0);
+          f16v& sb = b ? s1 : s0;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sb[r] = __fmaf_rn(al[b], sb[r], ga[b] * q[r]);
+        }
+      };
+#pragma unroll
+      for (int tt = 0; tt < kPqTiles; ++tt) {
+        f16v a0, a1;
+        blended(tt, a0, a1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          m0[r] = tt ? __builtin_elementwise_maximum(m0[r], a0[r]) : a0[r];
+          m1[r] = tt ? __builtin_elementwise_maximum(m1[r], a1[r]) : a1[r];
+        }
+        pin(m0, m1);
+        __builtin_amdgcn_sched_barrier(0);  // one tile's accumulators live at a time
+      }
+      finals();  // x and its bound again (not kept across the fold)
+      double qs[SUB];
+      {
+        float qf[SUB];
+        raw_floats<DT, SUB>(qo, qf);
+#pragma unroll
+        for (int e = 0; e < SUB; ++e) qs[e] = qf[e];
+      }
+      float t0, t1;
+      top2_slots(m0, m1, t0, t1);
+      const int row = slot_row(__float_as_uint(t0) & 31u);
+      double sa = -INFINITY;
+      int ja = -1;
+#pragma unroll 2
+      for (int tt = 0; tt < kPqTiles; ++tt) {
+        const int j = 32 * tt + row;
+        if (j < k) {
+          const double sc = blend_score<SUB>(xs, qs, sh.v64[j], sh.v64[j][SUB + 1], iem, qn, iqn, beta);
+          if (sc > sa) {
+            sa = sc;
+            ja = j;
+          }
+        }
+      }
+      // the fp32 fold value of row j approximates score_j + K0; its error bound
+      double nx2 = 0.0;
+#pragma unroll
+      for (int e = 0; e < SUB; ++e) nx2 = fma(xs[e], xs[e], nx2);
+      const double K0 = beta * nx2 * iem;
+      const double Ms = nx * pc.Mv + pc.Shb;
+      const double Mq = ldexp(qn, pc.sq) * (1.0 + 0x1p-40);
+      float qnf, qd, ql;
+      norms<DT, SUB>(qo, qnf, qd, ql);
+      const double Eq = score_bound<DT, SUB>(qnf, qd, ql, pc.rhoq, pc.nuq, pc.nulq, 0.0, 0.0) +
+                        0x1p-40 * Mq;
+      const double aa = fabs((double)al_own), gg = fabs((double)ga_own);
+      const double E2 = (aa * (E * (1.0 + kRnd) + 3.0 * kRnd * Ms) +
+                         gg * (Eq * (1.0 + 2.0 * kRnd) + 4.0 * kRnd * Mq)) * (1.0 + 0x1p-16) +
+                        0x1p-120;
+      const double lhs = sa + K0 - 0x1p-44 * (fabs(sa) + K0 + 1.0);
+      const double rhs = (double)t1 + pack_slack(t1) + E2;
+      code = ja;
+      open = own_ok && !(pc.finite && ja >= 0 && emax > 0.0 && lhs > rhs);
+      unsigned long long todo = __ballot(open);
+      while (todo) {
+        const int src = __ffsll((long long)todo) - 1;
+        todo &= todo - 1;
+        double xb[SUB], qb[SUB];
+#pragma unroll
+        for (int e = 0; e < SUB; ++e) {
+          xb[e] = __shfl(xs[e], src);
+          qb[e] = __shfl(qs[e], src);
+        }
+        const bool fin = all_finite(xb);
+        double mx = -INFINITY;
+        for (int j = lane; j < k; j += 64) mx = fmax(mx, sq_dist<SUB>(xb, sh.v64[j]));
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+        double qq = 0.0;
+#pragma unroll
+        for (int e = 0; e < SUB; ++e) qq += qb[e] * qb[e];
+        const double qnb = sqrt(qq);
+        const double iqb = qnb > 0.0 ? 1.0 / qnb : 0.0;
+        const double ieb = mx > 0.0 ? 1.0 / mx : 0.0;
+        double bs = -INFINITY;
+        int bj = -1;
+        for (int j = lane; j < k; j += 64) {
+          const double sc = blend_score<SUB>(xb, qb, sh.v64[j], sh.v64[j][SUB + 1], ieb, qnb, iqb, beta);
+          if (sc > bs) {
+            bs = sc;
+            bj = j;
+          }
+        }
+        wave_argmax(bs, bj);
+        if (lane == src) code = fin && bj >= 0 ? bj : 0;
+      }
     }
+    if (own_ok) codes[(ohead * n + orow) * M + ss_own] = (uint8_t)code;
   }
 }
 
@@ -293,20 +995,19 @@ template <int DT, int SUB>
 int launch_pq(int mode, const void* x, int64_t n, const int32_t* idx, int64_t n_sel,
               int64_t heads, const float* cb, int k, const float* chol, const void* query,
               int64_t nq, double beta, uint8_t* codes, hipStream_t s) {
-  constexpr int R = kPqRows;
-  const int64_t items = heads * n_sel * (kD / SUB / R);
-  int64_t g = (items + kPqThreads - 1) / kPqThreads;
-  if (g > 4096) g = 4096;
-  if (g < 1) g = 1;
+  const int64_t rpi = 64 / (kD / SUB);
+  const int64_t waves = heads * ((n_sel + rpi - 1) / rpi);  // one wave iteration each
+  int64_t g = (waves + kPqWaves - 1) / kPqWaves;
+  if (g > (int64_t)kPqCus * kPqWgPerCu) g = (int64_t)kPqCus * kPqWgPerCu;
   const dim3 grid((unsigned)g), block(kPqThreads);
   if (mode == kHWeighted)
-    return launch("pq_encode_h", pq_encode<DT, kHWeighted, SUB, R>, grid, block, 0, s, x, n, idx,
-                  n_sel, heads, cb, k, chol, query, nq, beta, codes);
+    return launch("pq_encode_h", pq_encode_mfma<DT, SUB, kHWeighted>, grid, block, 0, s, x, n,
+                  idx, n_sel, heads, cb, k, chol, query, nq, beta, codes);
   if (mode == kBlend)
-    return launch("pq_encode_blend", pq_encode<DT, kBlend, SUB, R>, grid, block, 0, s, x, n, idx,
-                  n_sel, heads, cb, k, chol, query, nq, beta, codes);
-  return launch("pq_encode_plain", pq_encode<DT, kPlain, SUB, R>, grid, block, 0, s, x, n, idx, n_sel,
-                heads, cb, k, chol, query, nq, beta, codes);
+    return launch("pq_encode_blend", pq_encode_mfma<DT, SUB, kBlend>, grid, block, 0, s, x, n,
+                  idx, n_sel, heads, cb, k, chol, query, nq, beta, codes);
+  return launch("pq_encode_plain", pq_encode_mfma<DT, SUB, kPlain>, grid, block, 0, s, x, n, idx,
+                n_sel, heads, cb, k, chol, query, nq, beta, codes);
 }
 
 template <int DT>
