@@ -105,6 +105,35 @@ __device__ __forceinline__ void block_max(double (&v)[N], double (*red)[kPqWaves
   __syncthreads();
 }
 
+// Workgroup-wide maxima of N floats (every thread receives them).
+template <int N>
+__device__ __forceinline__ void block_maxf(float (&v)[N], float (*red)[kPqWaves]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v[i] = fmaxf(v[i], __shfl_xor(v[i], o));
+  if (lane == 0)
+#pragma unroll
+    for (int i = 0; i < N; ++i) red[i][wave] = v[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = fmaxf(fmaxf(red[i][0], red[i][1]), fmaxf(red[i][2], red[i][3]));
+  __syncthreads();
+}
+
+// x rounded to fp32 upward / downward (x >= 0).
+__device__ __forceinline__ float round_up_f(double x) {
+  float f = (float)x;
+  if ((double)f < x) f = __uint_as_float(__float_as_uint(f) + 1u);
+  return f;
+}
+__device__ __forceinline__ float round_down_f(double x) {
+  float f = (float)x;
+  if ((double)f > x) f = __uint_as_float(__float_as_uint(f) - 1u);
+  return f;
+}
+
 template <int SUB, bool BLEND>
 struct PqShared {
   half8 fa[kPqTiles][64];            // table operand, MFMA A order
@@ -116,7 +145,8 @@ struct PqShared {
   double v64[kPqMaxK][SUB + 2];
   double lsh[SUB][SUB];
   float l32[SUB][SUB];               // the fp32 factor (H-weighted)
-  double red[16][kPqWaves];
+  double red[4][kPqWaves];
+  float redf[9][kPqWaves];
 };
 
 // Per-call constants of the preparation (identical in every thread).
@@ -185,7 +215,7 @@ __device__ __forceinline__ PqConsts pq_prep(const float* __restrict__ cb, int k,
     mv = fmax(mv, fabs(v[e]));
     fin += 0.0 * v[e];
   }
-  sh.v64[t][SUB] = hb;
+  sh.v64[t][SUB] = real ? hb : 0x1p1000;  // a pad row scores about -2^1000 in fp64
   sh.v64[t][SUB + 1] = 0.0;
   fin += 0.0 * hb;
   if constexpr (MODE == kBlend) {
@@ -256,15 +286,17 @@ __device__ __forceinline__ PqConsts pq_prep(const float* __restrict__ cb, int k,
     else
       sh.fa[tile][r + 32] = h8(pkh(h1, h2), pkh(pm, z16), 0u, 0u);
   }
-  // row terms, and the same divided by the row's size: n_j = ||w_j|| (||c_j|| without H), so
-  // that b_j / 2 = n_j^2 / 2 (a zero row has no error terms at all)
-  const double rho_j = up(sqrt(rr)), nu_j = up(up(sqrt(nh2)) + up(sqrt(nl2))), nul_j = up(sqrt(nl2));
-  const double cb_j = up(cbm * (1.0 + 0x1p-22)), beta_j = up(fabs(cbx - bias) + kRnd * cbm);
-  const double nj = sqrt(2.0 * hb) * (1.0 - 0x1p-40);
-  const double inj = nj > 0.0 ? 1.0 / nj : 0.0, inj2 = inj * inj;
-  double r2[14] = {rho_j, nu_j, nul_j, up(sqrt(nv2)), cb_j, beta_j, 0.0, 0.0, 0.0,
-                   up(nu_j * inj), up(rho_j * inj), up(nul_j * inj), up(up(cb_j * inj2)),
-                   up(up(beta_j * inj2))};
+  // Row terms in fp32 rounded up; the blend keeps their maxima, the plain and H-weighted codes
+  // the maxima of the same divided by the row's size n_j = ||w_j|| (||c_j|| without H, so
+  // b_j / 2 = n_j^2 / 2; a zero row has no error terms at all).  n_j below 2^-60 counts as
+  // 2^-60 (R is never smaller).
+  auto sq_up = [](double s2) { return sqrtf(round_up_f(s2)) * (1.f + 0x1p-20f); };
+  const float rho_j = sq_up(rr), nul_j = sq_up(nl2);
+  const float nu_j = (sq_up(nh2) + nul_j) * (1.f + 0x1p-22f);
+  const float cb_j = round_up_f(cbm * (1.0 + 0x1p-22));
+  const float beta_j = round_up_f(fabs(cbx - bias) + kRnd * cbm);
+  constexpr int NR = MODE == kBlend ? 9 : 5;
+  float r2[NR];
   if constexpr (MODE == kBlend) {
     const double Sq = ldexp(1.0, sq);
     _Float16 ch[SUB], cl[SUB];
@@ -290,26 +322,44 @@ __device__ __forceinline__ PqConsts pq_prep(const float* __restrict__ cb, int k,
       else
         sh.fq[tile][r + 32] = h8(0u, 0u, 0u, 0u);
     }
-    r2[6] = up(sqrt(rq));
-    r2[7] = up(up(sqrt(qh2)) + up(sqrt(ql2)));
-    r2[8] = up(sqrt(ql2));
+    const float nulq = sq_up(ql2);
+    const float vals[9] = {rho_j, nu_j, nul_j, sq_up(nv2), cb_j, beta_j, sq_up(rq),
+                           (sq_up(qh2) + nulq) * (1.f + 0x1p-22f), nulq};
+#pragma unroll
+    for (int q = 0; q < 9; ++q) r2[q] = vals[q];
+  } else {
+    const double n2 = 2.0 * hb;
+    float inj = 0.f;  // 1 / max(n_j, 2^-60), rounded up
+    if (n2 > 0.0) {
+      float nlo = sqrtf(round_down_f(n2)) * (1.f - 0x1p-20f);
+      nlo = fmaxf(nlo, 0x1p-60f);
+      inj = n2 < 3.0e38 ? (1.f / nlo) * (1.f + 0x1p-20f) : INFINITY;
+    }
+    const float inj2 = inj * inj * (1.f + 0x1p-20f), f = 1.f + 0x1p-20f;
+    const float vals[5] = {nu_j * inj * f, rho_j * inj * f, nul_j * inj * f, cb_j * inj2 * f,
+                           beta_j * inj2 * f};
+#pragma unroll
+    for (int q = 0; q < 5; ++q) r2[q] = n2 > 0.0 ? vals[q] : 0.f;
   }
-  block_max(r2, sh.red);  // also publishes the operands written above
-  pc.rho = r2[0];
-  pc.nu = r2[1];
-  pc.nul = r2[2];
-  pc.Mv = r2[3];
-  pc.B = r2[4];
-  pc.betab = r2[5];
+  block_maxf(r2, sh.redf);  // also publishes the operands written above
   pc.Shb = up(ldexp(r1[1], se));
-  pc.rhoq = r2[6];
-  pc.nuq = r2[7];
-  pc.nulq = r2[8];
-  pc.kv = r2[9];
-  pc.kr = r2[10];
-  pc.kl = r2[11];
-  pc.kb = r2[12];
-  pc.kbeta = r2[13];
+  if constexpr (MODE == kBlend) {
+    pc.rho = r2[0];
+    pc.nu = r2[1];
+    pc.nul = r2[2];
+    pc.Mv = r2[3];
+    pc.B = r2[4];
+    pc.betab = r2[5];
+    pc.rhoq = r2[6];
+    pc.nuq = r2[7];
+    pc.nulq = r2[8];
+  } else {
+    pc.kv = r2[0];
+    pc.kr = r2[1];
+    pc.kl = r2[2];
+    pc.kb = r2[3];
+    pc.kbeta = r2[4];
+  }
   {
     // the bound for rows of size at most R (score_bound_r), its terms collected
     constexpr int terms = (SUB == 8 ? 2 * SUB + 1 : 2 * SUB + 3) + (DT == A2ATS_F32 ? SUB : 0);
@@ -403,6 +453,20 @@ __device__ __forceinline__ void make_b(const Raw<DT, SUB>& r, int hh, unsigned b
   }
 }
 
+// An upper bound of sqrt(s) for s >= 0: the hardware square root (within an ulp), a relative
+// margin, and 2^-60 for an input the hardware flushes (below 2^-126).
+__device__ __forceinline__ float sqrt_up(float s) {
+  return __builtin_amdgcn_sqrtf(s * (1.f + 0x1p-18f)) * (1.f + 0x1p-20f) + 0x1p-60f;
+}
+
+// Maximum of two finite fp64 values (a single v_max_f64: the operands are bit-packed
+// scores, never NaN, so no canonicalising is needed).
+__device__ __forceinline__ double max_f64(double a, double b) {
+  double r;
+  asm("v_max_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Norm terms of one sub-vector against what the matrix cores see of it, in fp32 rounded
 // up: ||x||, ||x - x'|| (x' = the fp16 parts, a subnormal part possibly flushed) and ||lo||
 // (fp32 inputs' second parts).  x - hi - lo is exact in fp32 (each part is the other's
@@ -422,8 +486,8 @@ __device__ __forceinline__ void norms(const Raw<DT, SUB>& r, float& nx, float& n
       sx = __fmaf_rn(x[e], x[e], sx);
       sd = __fmaf_rn(d, d, sd);
     }
-    nx = sqrtf(sx * (1.f + 0x1p-18f)) * (1.f + 0x1p-20f);
-    nd = sqrtf(sd * (1.f + 0x1p-18f)) * (1.f + 0x1p-20f);
+    nx = sqrt_up(sx);
+    nd = sd > 0.f ? sqrt_up(sd) : 0.f;
     nl = 0.f;
     return;
   }
@@ -450,9 +514,9 @@ __device__ __forceinline__ void norms(const Raw<DT, SUB>& r, float& nx, float& n
     }
   }
   // SUB-term fp32 sums: within 2^-20 relative; sqrt within an ulp
-  nx = sqrtf(sx * (1.f + 0x1p-18f)) * (1.f + 0x1p-20f);
-  nd = sqrtf(sd * (1.f + 0x1p-18f)) * (1.f + 0x1p-20f);
-  nl = sqrtf(sl * (1.f + 0x1p-18f)) * (1.f + 0x1p-20f);
+  nx = sqrt_up(sx);
+  nd = sd > 0.f ? sqrt_up(sd) : 0.f;
+  nl = sl > 0.f ? sqrt_up(sl) : 0.f;
 }
 
 // Rigorous bound on |acc_j - S s_j| for every row j (S units).
@@ -565,33 +629,7 @@ __global__ __launch_bounds__(kPqThreads, kPqWgPerCu) void pq_encode_mfma(
   constexpr int M = kD / SUB;   // sub-spaces per row
   constexpr int RPI = 64 / M;   // rows per wave iteration
   __shared__ PqShared<SUB, BLEND> sh;
-  const PqConsts pc = pq_prep<SUB, MODE, DT>(cb, k, chol, sh);
-
   const int lane = threadIdx.x & 63, col = lane & 31, hh = lane >> 5;
-  // the table operand in registers, sub_dim 8: the bias operand (lanes 0-31) too; the blend,
-  // which needs more registers, reads them from LDS at each tile
-  constexpr int RT = BLEND ? 1 : kPqTiles;
-  half8 A[RT];
-  unsigned fb0[RT], fb1[RT];
-  if constexpr (!BLEND) {
-#pragma unroll
-    for (int tt = 0; tt < kPqTiles; ++tt) {
-      A[tt] = sh.fa[tt][lane];
-      fb0[tt] = sh.fb[tt][lane][0];
-      fb1[tt] = sh.fb[tt][lane][1];
-    }
-  }
-  // (lds_lane: the lane index plus an opaque zero set in each iteration, so that the
-  // loop-invariant reads are not hoisted out of the loop into registers)
-  int lds_lane = lane, lds_zero = 0;
-  auto a_op = [&](int tt) { return BLEND ? sh.fa[tt][lds_lane] : A[BLEND ? 0 : tt]; };
-  auto fb_op = [&](int tt, int w) {
-    return BLEND ? sh.fb[tt][lds_lane][w] : (w ? fb1[BLEND ? 0 : tt] : fb0[BLEND ? 0 : tt]);
-  };
-  const unsigned e2 = pk16(ldexpf(1.f, pc.eb), ldexpf(1.f, pc.eb));
-  const unsigned mk = pk16(32768.f, 0.f);
-  const half8 Bb = hh ? h8(0u, 0u, 0u, 0u) : h8(e2, mk, 0u, 0u);  // bias operand, sub_dim 8
-  const f16v zero = {};
 
   // this lane's column in each block: row offset within the iteration and sub-space
   int lr[2], ss[2];
@@ -636,7 +674,34 @@ __global__ __launch_bounds__(kPqThreads, kPqWgPerCu) void pq_encode_mfma(
         qr[b] = load_raw<DT, SUB>(query, ((h * nq + (nq == 1 ? 0 : row)) * kD + ss[b] * SUB), ok);
     }
   };
-  fetch(h_cur, g_cur, nx_raw, nq_raw);
+  fetch(h_cur, g_cur, nx_raw, nq_raw);  // in flight during the preparation
+
+  const PqConsts pc = pq_prep<SUB, MODE, DT>(cb, k, chol, sh);
+  // the table operand in registers, sub_dim 8: the bias operand (lanes 0-31) too; the blend,
+  // which needs more registers, reads them from LDS at each tile
+  constexpr int RT = BLEND ? 1 : kPqTiles;
+  half8 A[RT];
+  unsigned fb0[RT], fb1[RT];
+  if constexpr (!BLEND) {
+#pragma unroll
+    for (int tt = 0; tt < kPqTiles; ++tt) {
+      A[tt] = sh.fa[tt][lane];
+      fb0[tt] = sh.fb[tt][lane][0];
+      fb1[tt] = sh.fb[tt][lane][1];
+    }
+  }
+  // (lds_lane: the lane index plus an opaque zero set in each iteration, so that the
+  // loop-invariant reads are not hoisted out of the loop into registers)
+  int lds_lane = lane, lds_zero = 0;
+  auto a_op = [&](int tt) { return BLEND ? sh.fa[tt][lds_lane] : A[BLEND ? 0 : tt]; };
+  auto fb_op = [&](int tt, int w) {
+    return BLEND ? sh.fb[tt][lds_lane][w] : (w ? fb1[BLEND ? 0 : tt] : fb0[BLEND ? 0 : tt]);
+  };
+  const unsigned e2 = pk16(ldexpf(1.f, pc.eb), ldexpf(1.f, pc.eb));
+  const unsigned mk = pk16(32768.f, 0.f);
+  const half8 Bb = hh ? h8(0u, 0u, 0u, 0u) : h8(e2, mk, 0u, 0u);  // bias operand, sub_dim 8
+  const f16v zero = {};
+
 
   for (; h_cur < heads; advance(h_cur, g_cur)) {
     if constexpr (BLEND || MODE == kHWeighted) {
@@ -736,21 +801,24 @@ __global__ __launch_bounds__(kPqThreads, kPqWgPerCu) void pq_encode_mfma(
       top2_slots(m0, m1, t0, t1);
       finals();
       const int row = slot_row(__float_as_uint(t0) & 31u);
-      double sa = -INFINITY;
-      int ja = -1;
+      // the winning slot's rows in fp64 (a pad row scores about -2^1000); each score carries
+      // its tile in its lowest 3 bits, ordered so that the larger packed value is the lower
+      // tile between equal scores, and the best is a plain maximum
+      double sa = 0.0;
 #pragma unroll
       for (int tt = 0; tt < kPqTiles; ++tt) {
         const int j = 32 * tt + row;
-        if (j < k) {
-          double s = -sh.v64[j][SUB];
+        double s = -sh.v64[j][SUB];
 #pragma unroll
-          for (int e = 0; e < SUB; ++e) s = fma(xs[e], sh.v64[j][e], s);
-          if (s > sa) {
-            sa = s;
-            ja = j;
-          }
-        }
+        for (int e = 0; e < SUB; ++e) s = fma(xs[e], sh.v64[j][e], s);
+        const int hi = __double2hiint(s);
+        const unsigned c3 = (unsigned)(7 - tt) ^ ((unsigned)(hi >> 31) & 7u);
+        s = __hiloint2double(hi, (int)(((unsigned)__double2loint(s) & ~7u) | c3));
+        sa = tt ? max_f64(sa, s) : s;
       }
+      const int hia = __double2hiint(sa);
+      const int tta = 7 - (int)(((unsigned)__double2loint(sa) & 7u) ^ ((unsigned)(hia >> 31) & 7u));
+      const int ja = sa > -0x1p999 ? 32 * tta + row : -1;
       // every row outside the winning slot: its MFMA score is at most t1 (plus the packing),
       // its error at most E, or, when it could reach s_a at all, the bound for rows of size R
       double Z = nx;  // ||z|| (z = x L; x itself without L), rounded up
@@ -767,12 +835,12 @@ __global__ __launch_bounds__(kPqThreads, kPqWgPerCu) void pq_encode_mfma(
           for (int b = 0; b < SUB; ++b) za = __fmaf_rn(xf[b], sh.l32[b][a + lds_zero], za);
           z2 = __fmaf_rn(za, za, z2);
         }
-        Z = (double)(sqrtf(z2 * (1.f + 0x1p-18f)) * (1.f + 0x1p-20f)) + 0x1p-21 * nx * pc.lf;
+        Z = (double)sqrt_up(z2) + 0x1p-21 * nx * pc.lf;
       }
       const float disc = (float)fmax(0.0, Z * Z - 2.0 * sa) * (1.f + 0x1p-18f);
-      const double R = (Z + (double)(sqrtf(disc) * (1.f + 0x1p-20f))) * (1.0 + 0x1p-20) + 0x1p-60;
+      const double R = (Z + (double)sqrt_up(disc)) * (1.0 + 0x1p-20) + 0x1p-60;
       const double Ec = R * (pc.c_rr * R + pc.c_x * nx + pc.c_d * xnd + pc.c_l * xnl) + 0x1p-120;
-      const double lhs = ldexp(sa, pc.se);
+      const double lhs = ldexp(sa, pc.se) * (1.0 - 0x1p-47 * (sa < 0.0 ? -1.0 : 1.0));  // the packed bits
       const double rhs = (double)t1 + pack_slack(t1) + Ec;
       code = ja;
       open = own_ok && !(pc.finite && ja >= 0 && lhs > rhs);
