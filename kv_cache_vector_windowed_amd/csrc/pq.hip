@@ -21,16 +21,20 @@
 // power of two S and split into fp16 hi + lo parts; the sub-vectors are exact in fp16 (bf16
 // inputs in fp16's range) or split the same way (fp32 inputs); the bias -S b_j / 2 enters as
 // fp16 hi + lo parts times a power of two (sub_dim 8: a small MFMA per tile whose result seeds
-// both blocks' accumulators; sub_dim 4: spare K slots of the same MFMA).  The whole table
-// operand stays in registers.
+// both blocks' accumulators; sub_dim 4: spare K slots of the same MFMA).  The table operands
+// live in LDS, prepared by each workgroup.
 //   Fold: each accumulator register keeps its maximum over the 8 tiles (v_maximum3, half an
 // operation per score, no index).  A sub-vector's 32 register maxima ("slots", 16 in each
 // lane of a lane pair, exchanged with v_permlane32_swap) are packed with their slot number
 // and the largest two taken: the winning slot and a bound on every other slot.  The winning
 // slot's 8 centroids are scored again in fp64, and the best of them is the code when its
-// score beats the second slot's maximum by more than the rigorous bound E on an MFMA score's
+// score beats the second slot's maximum by more than a rigorous bound on an MFMA score's
 // error (hi/lo residuals, the bias residual, fp32 accumulation of up to 25 terms, the packed
-// low bits).  The rest, rare, is decided by the whole wave in fp64 over the whole table.
+// low bits), taken only over the rows that could reach that score at all: s_j <= ||z|| n_j -
+// n_j^2 / 2 with n_j = ||c_j L|| (z = x L) limits them to n_j <= R = ||z|| + sqrt(||z||^2 -
+// 2 s_a), and every error term of a row grows with n_j (a table with a few far-out rows would
+// otherwise set the bound for all).  The rest, about 1 in 10^4 on the workloads, is decided by
+// the whole wave in fp64 over the whole table.
 //   Blend: e_j = ||x - c_j||^2 = ||x||^2 - 2 s_j (plain s_j), so max_j e_j comes from a first
 // pass folding the smallest s_j the same way (the farthest slot rescored in fp64, exactly as
 // the definition sums).  Up to a constant per sub-vector the blended score is
@@ -620,15 +624,18 @@ __device__ __forceinline__ double blend_score(const double (&x)[SUB], const doub
   return beta * (-err) + (1.0 - beta) * cosv;
 }
 
-template <int DT, int SUB, int MODE>
-__global__ __launch_bounds__(kPqThreads, kPqWgPerCu) void pq_encode_mfma(
+// The blend.  Each wave iteration: pass 1 (the smallest s_j, folded and certified like the
+// codes, for max e), pass 2 (the blended fp32 scores folded), the winning slot rescored by the
+// blend's formula in fp64, the certificate, the rare fp64 scans and the stores.  The table
+// operands are read from LDS at each tile.
+template <int DT, int SUB>
+__global__ __launch_bounds__(kPqThreads, kPqWgPerCu) void pq_encode_blend(
     const void* __restrict__ x, int64_t n, const int32_t* __restrict__ idx, int64_t n_sel,
-    int64_t heads, const float* __restrict__ cb, int k, const float* __restrict__ chol,
-    const void* __restrict__ query, int64_t nq, double beta, uint8_t* __restrict__ codes) {
-  constexpr bool BLEND = MODE == kBlend;
+    int64_t heads, const float* __restrict__ cb, int k, const void* __restrict__ query,
+    int64_t nq, double beta, uint8_t* __restrict__ codes) {
   constexpr int M = kD / SUB;   // sub-spaces per row
   constexpr int RPI = 64 / M;   // rows per wave iteration
-  __shared__ PqShared<SUB, BLEND> sh;
+  __shared__ PqShared<SUB, true> sh;
   const int lane = threadIdx.x & 63, col = lane & 31, hh = lane >> 5;
 
   // this lane's column in each block: row offset within the iteration and sub-space
@@ -670,33 +677,17 @@ __global__ __launch_bounds__(kPqThreads, kPqWgPerCu) void pq_encode_mfma(
       int64_t row = 0;
       const bool ok = locate(h, g, lr[b], row);
       xr[b] = load_raw<DT, SUB>(x, ((h * n + row) * kD + ss[b] * SUB), ok);
-      if constexpr (BLEND)
-        qr[b] = load_raw<DT, SUB>(query, ((h * nq + (nq == 1 ? 0 : row)) * kD + ss[b] * SUB), ok);
+      qr[b] = load_raw<DT, SUB>(query, ((h * nq + (nq == 1 ? 0 : row)) * kD + ss[b] * SUB), ok);
     }
   };
   fetch(h_cur, g_cur, nx_raw, nq_raw);  // in flight during the preparation
 
-  const PqConsts pc = pq_prep<SUB, MODE, DT>(cb, k, chol, sh);
-  // the table operand in registers, sub_dim 8: the bias operand (lanes 0-31) too; the blend,
-  // which needs more registers, reads them from LDS at each tile
-  constexpr int RT = BLEND ? 1 : kPqTiles;
-  half8 A[RT];
-  unsigned fb0[RT], fb1[RT];
-  if constexpr (!BLEND) {
-#pragma unroll
-    for (int tt = 0; tt < kPqTiles; ++tt) {
-      A[tt] = sh.fa[tt][lane];
-      fb0[tt] = sh.fb[tt][lane][0];
-      fb1[tt] = sh.fb[tt][lane][1];
-    }
-  }
+  const PqConsts pc = pq_prep<SUB, kBlend, DT>(cb, k, nullptr, sh);
   // (lds_lane: the lane index plus an opaque zero set in each iteration, so that the
-  // loop-invariant reads are not hoisted out of the loop into registers)
-  int lds_lane = lane, lds_zero = 0;
-  auto a_op = [&](int tt) { return BLEND ? sh.fa[tt][lds_lane] : A[BLEND ? 0 : tt]; };
-  auto fb_op = [&](int tt, int w) {
-    return BLEND ? sh.fb[tt][lds_lane][w] : (w ? fb1[BLEND ? 0 : tt] : fb0[BLEND ? 0 : tt]);
-  };
+  // loop-invariant table reads are not hoisted out of the loop into registers)
+  int lds_lane = lane;
+  auto a_op = [&](int tt) { return sh.fa[tt][lds_lane]; };
+  auto fb_op = [&](int tt, int w) { return sh.fb[tt][lds_lane][w]; };
   const unsigned e2 = pk16(ldexpf(1.f, pc.eb), ldexpf(1.f, pc.eb));
   const unsigned mk = pk16(32768.f, 0.f);
   const half8 Bb = hh ? h8(0u, 0u, 0u, 0u) : h8(e2, mk, 0u, 0u);  // bias operand, sub_dim 8
@@ -704,18 +695,13 @@ __global__ __launch_bounds__(kPqThreads, kPqWgPerCu) void pq_encode_mfma(
 
 
   for (; h_cur < heads; advance(h_cur, g_cur)) {
-    if constexpr (BLEND || MODE == kHWeighted) {
+    {
       int z = 0;
       asm volatile("" : "+v"(z));
-      lds_zero = z;
       lds_lane = lane + z;
     }
     const Raw<DT, SUB> xr[2] = {nx_raw[0], nx_raw[1]};
-    Raw<DT, SUB> qr[2];
-    if constexpr (BLEND) {
-      qr[0] = nq_raw[0];
-      qr[1] = nq_raw[1];
-    }
+    const Raw<DT, SUB> qr[2] = {nq_raw[0], nq_raw[1]};
     {
       int64_t h_nx = h_cur, g_nx = g_cur;
       advance(h_nx, g_nx);
@@ -771,7 +757,7 @@ __global__ __launch_bounds__(kPqThreads, kPqWgPerCu) void pq_encode_mfma(
       nx = fx;
       xnd = fd;
       xnl = fl;
-      if constexpr (BLEND) E = score_bound<DT, SUB>(nx, xnd, xnl, pc.rho, pc.nu, pc.nul, pc.B, pc.betab);
+      E = score_bound<DT, SUB>(nx, xnd, xnl, pc.rho, pc.nu, pc.nul, pc.B, pc.betab);
     };
     // all of a broadcast sub-vector finite (a non-finite one has code 0: every distance is
     // inf or NaN)
@@ -782,280 +768,461 @@ __global__ __launch_bounds__(kPqThreads, kPqWgPerCu) void pq_encode_mfma(
       return f;
     };
 
-    if constexpr (!BLEND) {
-      f16v m0, m1;
+    // ---- pass 1: max_j e_j through the smallest s_j (pad rows' mark flipped to +)
+    const unsigned flip = 0x8000u;  // sign of the pad mark's fp16
+    f16v m0, m1;
 #pragma unroll
-      for (int tp = 0; tp < kPqTiles / 2; ++tp) {
-        f16v a0, a1, c0, c1;
-        tile_scores(2 * tp, B1, B2, 0u, a0, a1);
-        tile_scores(2 * tp + 1, B1, B2, 0u, c0, c1);
+    for (int tp = 0; tp < kPqTiles / 2; ++tp) {
+      f16v a0, a1, c0, c1;
+      tile_scores(2 * tp, B1, B2, flip, a0, a1);
+      tile_scores(2 * tp + 1, B1, B2, flip, c0, c1);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          m0[r] = tp ? fmax3(m0[r], a0[r], c0[r]) : __builtin_elementwise_maximum(a0[r], c0[r]);
-          m1[r] = tp ? fmax3(m1[r], a1[r], c1[r]) : __builtin_elementwise_maximum(a1[r], c1[r]);
-        }
-        pin(m0, m1);
-        __builtin_amdgcn_sched_barrier(0);  // one tile pair's accumulators live at a time
+      for (int r = 0; r < 16; ++r) {
+        m0[r] = tp ? fmax3(m0[r], -a0[r], -c0[r]) : __builtin_elementwise_maximum(-a0[r], -c0[r]);
+        m1[r] = tp ? fmax3(m1[r], -a1[r], -c1[r]) : __builtin_elementwise_maximum(-a1[r], -c1[r]);
       }
+      pin(m0, m1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    double emax;
+    {
       float t0, t1;
       top2_slots(m0, m1, t0, t1);
       finals();
-      const int row = slot_row(__float_as_uint(t0) & 31u);
-      // the winning slot's rows in fp64 (a pad row scores about -2^1000); each score carries
-      // its tile in its lowest 3 bits, ordered so that the larger packed value is the lower
-      // tile between equal scores, and the best is a plain maximum
-      double sa = 0.0;
+      double nx2 = 0.0;
 #pragma unroll
+      for (int e = 0; e < SUB; ++e) nx2 = fma(xs[e], xs[e], nx2);
+      const int row = slot_row(__float_as_uint(t0) & 31u);
+      double em = -INFINITY;
+      int je = -1;
+#pragma unroll 2
       for (int tt = 0; tt < kPqTiles; ++tt) {
         const int j = 32 * tt + row;
-        double s = -sh.v64[j][SUB];
-#pragma unroll
-        for (int e = 0; e < SUB; ++e) s = fma(xs[e], sh.v64[j][e], s);
-        const int hi = __double2hiint(s);
-        const unsigned c3 = (unsigned)(7 - tt) ^ ((unsigned)(hi >> 31) & 7u);
-        s = __hiloint2double(hi, (int)(((unsigned)__double2loint(s) & ~7u) | c3));
-        sa = tt ? max_f64(sa, s) : s;
-      }
-      const int hia = __double2hiint(sa);
-      const int tta = 7 - (int)(((unsigned)__double2loint(sa) & 7u) ^ ((unsigned)(hia >> 31) & 7u));
-      const int ja = sa > -0x1p999 ? 32 * tta + row : -1;
-      // every row outside the winning slot: its MFMA score is at most t1 (plus the packing),
-      // its error at most E, or, when it could reach s_a at all, the bound for rows of size R
-      double Z = nx;  // ||z|| (z = x L; x itself without L), rounded up
-      if constexpr (MODE == kHWeighted) {
-        // z in fp32: each element within 2^-21 sum_b |x_b L_ba|, so ||z|| within
-        // 2^-21 ||x|| ||L||_F of the fp32 vector's norm
-        float xf[SUB];
-        raw_floats<DT, SUB>(xo, xf);
-        float z2 = 0.f;
-#pragma unroll
-        for (int a = 0; a < SUB; ++a) {
-          float za = 0.f;
-#pragma unroll
-          for (int b = 0; b < SUB; ++b) za = __fmaf_rn(xf[b], sh.l32[b][a + lds_zero], za);
-          z2 = __fmaf_rn(za, za, z2);
+        if (j < k) {
+          const double e2v = sq_dist<SUB>(xs, sh.v64[j]);
+          if (e2v > em) {
+            em = e2v;
+            je = j;
+          }
         }
-        Z = (double)sqrt_up(z2) + 0x1p-21 * nx * pc.lf;
       }
-      const float disc = (float)fmax(0.0, Z * Z - 2.0 * sa) * (1.f + 0x1p-18f);
-      const double R = (Z + (double)sqrt_up(disc)) * (1.0 + 0x1p-20) + 0x1p-60;
-      const double Ec = R * (pc.c_rr * R + pc.c_x * nx + pc.c_d * xnd + pc.c_l * xnl) + 0x1p-120;
-      const double lhs = ldexp(sa, pc.se) * (1.0 - 0x1p-47 * (sa < 0.0 ? -1.0 : 1.0));  // the packed bits
-      const double rhs = (double)t1 + pack_slack(t1) + Ec;
-      code = ja;
-      open = own_ok && !(pc.finite && ja >= 0 && lhs > rhs);
-      // the rest: the whole wave scores the whole table in fp64 for one sub-vector at a time
-      unsigned long long todo = __ballot(open);
+      const double tb = 2.0 * ldexp((double)t1 + pack_slack(t1) + E, -pc.se);
+      const double ub = nx2 + tb;
+      const double margin = 0x1p-44 * (nx2 + fabs(tb) + fabs(em));
+      emax = em;
+      bool open1 = own_ok && !(pc.finite && je >= 0 && em - margin > ub);
+      unsigned long long todo = __ballot(open1);
       while (todo) {
         const int src = __ffsll((long long)todo) - 1;
         todo &= todo - 1;
         double xb[SUB];
 #pragma unroll
         for (int e = 0; e < SUB; ++e) xb[e] = __shfl(xs[e], src);
-        const bool fin = all_finite(xb);
-        double bs = -INFINITY;
-        int bj = -1;
-        for (int j = lane; j < k; j += 64) {
-          double s = -sh.v64[j][SUB];
-#pragma unroll
-          for (int e = 0; e < SUB; ++e) s = fma(xb[e], sh.v64[j][e], s);
-          if (s > bs) {  // a NaN score (a non-finite table row) never wins
-            bs = s;
-            bj = j;
-          }
-        }
-        wave_argmax(bs, bj);
-        if (lane == src) code = fin && bj >= 0 ? bj : 0;  // non-finite input: every distance
-                                                          // is inf or NaN, code 0
-      }
-    } else {
-      // ---- pass 1: max_j e_j through the smallest s_j (pad rows' mark flipped to +)
-      const unsigned flip = 0x8000u;  // sign of the pad mark's fp16
-      f16v m0, m1;
-#pragma unroll
-      for (int tp = 0; tp < kPqTiles / 2; ++tp) {
-        f16v a0, a1, c0, c1;
-        tile_scores(2 * tp, B1, B2, flip, a0, a1);
-        tile_scores(2 * tp + 1, B1, B2, flip, c0, c1);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          m0[r] = tp ? fmax3(m0[r], -a0[r], -c0[r]) : __builtin_elementwise_maximum(-a0[r], -c0[r]);
-          m1[r] = tp ? fmax3(m1[r], -a1[r], -c1[r]) : __builtin_elementwise_maximum(-a1[r], -c1[r]);
-        }
-        pin(m0, m1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      double emax;
-      {
-        float t0, t1;
-        top2_slots(m0, m1, t0, t1);
-        finals();
-        double nx2 = 0.0;
-#pragma unroll
-        for (int e = 0; e < SUB; ++e) nx2 = fma(xs[e], xs[e], nx2);
-        const int row = slot_row(__float_as_uint(t0) & 31u);
-        double em = -INFINITY;
-        int je = -1;
-#pragma unroll 2
-        for (int tt = 0; tt < kPqTiles; ++tt) {
-          const int j = 32 * tt + row;
-          if (j < k) {
-            const double e2v = sq_dist<SUB>(xs, sh.v64[j]);
-            if (e2v > em) {
-              em = e2v;
-              je = j;
-            }
-          }
-        }
-        const double tb = 2.0 * ldexp((double)t1 + pack_slack(t1) + E, -pc.se);
-        const double ub = nx2 + tb;
-        const double margin = 0x1p-44 * (nx2 + fabs(tb) + fabs(em));
-        emax = em;
-        bool open1 = own_ok && !(pc.finite && je >= 0 && em - margin > ub);
-        unsigned long long todo = __ballot(open1);
-        while (todo) {
-          const int src = __ffsll((long long)todo) - 1;
-          todo &= todo - 1;
-          double xb[SUB];
-#pragma unroll
-          for (int e = 0; e < SUB; ++e) xb[e] = __shfl(xs[e], src);
-          double mx = -INFINITY;
-          for (int j = lane; j < k; j += 64) mx = fmax(mx, sq_dist<SUB>(xb, sh.v64[j]));
-#pragma unroll
-          for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
-          if (lane == src) emax = mx;
-        }
-      }
-      // ---- pass 2: the blend, up to the constant beta ||x||^2 / max e
-      const Raw<DT, SUB> qo = raw_sel<DT, SUB>(qr[0], qr[1], hh);
-      double qn;
-      {
-        float qf[SUB];
-        raw_floats<DT, SUB>(qo, qf);
-        double qn2 = 0.0;
-#pragma unroll
-        for (int e = 0; e < SUB; ++e) qn2 += (double)qf[e] * (double)qf[e];
-        qn = sqrt(qn2);
-      }
-      const double iqn = qn > 0.0 ? 1.0 / qn : 0.0;
-      const double iem = emax > 0.0 ? 1.0 / emax : 0.0;
-      const float al_own = (float)(2.0 * beta * ldexp(iem, -pc.se));
-      const float ga_own = (float)((1.0 - beta) * ldexp(iqn, -pc.sq));
-      float al[2], ga[2];
-      {
-        const float alp = __shfl_xor(al_own, 32), gap = __shfl_xor(ga_own, 32);
-        al[0] = hh ? alp : al_own;
-        al[1] = hh ? al_own : alp;
-        ga[0] = hh ? gap : ga_own;
-        ga[1] = hh ? ga_own : gap;
-      }
-      half8 Q1[2], Q2[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) make_b<DT, SUB>(qr[b], hh, 0u, 0u, Q1[b], Q2[b]);
-      // the blended fold value of tile tt, one block's q-accumulator at a time
-      auto blended = [&](int tt, f16v& s0, f16v& s1) {
-        tile_scores(tt, B1, B2, 0u, s0, s1);
-        const half8 fq = sh.fq[tt][lds_lane];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          f16v q = __builtin_amdgcn_mfma_f32_32x32x16_f16(fq, Q1[b], zero, 0, 0, 0);
-          if constexpr (SUB == 8 && DT == A2ATS_F32)
-            q = __builtin_amdgcn_mfma_f32_32x32x16_f16(fq, Q2[b], q, 0, 0, 0);
-          f16v& sb = b ? s1 : s0;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sb[r] = __fmaf_rn(al[b], sb[r], ga[b] * q[r]);
-        }
-      };
-#pragma unroll
-      for (int tt = 0; tt < kPqTiles; ++tt) {
-        f16v a0, a1;
-        blended(tt, a0, a1);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          m0[r] = tt ? __builtin_elementwise_maximum(m0[r], a0[r]) : a0[r];
-          m1[r] = tt ? __builtin_elementwise_maximum(m1[r], a1[r]) : a1[r];
-        }
-        pin(m0, m1);
-        __builtin_amdgcn_sched_barrier(0);  // one tile's accumulators live at a time
-      }
-      finals();  // x and its bound again (not kept across the fold)
-      double qs[SUB];
-      {
-        float qf[SUB];
-        raw_floats<DT, SUB>(qo, qf);
-#pragma unroll
-        for (int e = 0; e < SUB; ++e) qs[e] = qf[e];
-      }
-      float t0, t1;
-      top2_slots(m0, m1, t0, t1);
-      const int row = slot_row(__float_as_uint(t0) & 31u);
-      double sa = -INFINITY;
-      int ja = -1;
-#pragma unroll 2
-      for (int tt = 0; tt < kPqTiles; ++tt) {
-        const int j = 32 * tt + row;
-        if (j < k) {
-          const double sc = blend_score<SUB>(xs, qs, sh.v64[j], sh.v64[j][SUB + 1], iem, qn, iqn, beta);
-          if (sc > sa) {
-            sa = sc;
-            ja = j;
-          }
-        }
-      }
-      // the fp32 fold value of row j approximates score_j + K0; its error bound
-      double nx2 = 0.0;
-#pragma unroll
-      for (int e = 0; e < SUB; ++e) nx2 = fma(xs[e], xs[e], nx2);
-      const double K0 = beta * nx2 * iem;
-      const double Ms = nx * pc.Mv + pc.Shb;
-      const double Mq = ldexp(qn, pc.sq) * (1.0 + 0x1p-40);
-      float qnf, qd, ql;
-      norms<DT, SUB>(qo, qnf, qd, ql);
-      const double Eq = score_bound<DT, SUB>(qnf, qd, ql, pc.rhoq, pc.nuq, pc.nulq, 0.0, 0.0) +
-                        0x1p-40 * Mq;
-      const double aa = fabs((double)al_own), gg = fabs((double)ga_own);
-      const double E2 = (aa * (E * (1.0 + kRnd) + 3.0 * kRnd * Ms) +
-                         gg * (Eq * (1.0 + 2.0 * kRnd) + 4.0 * kRnd * Mq)) * (1.0 + 0x1p-16) +
-                        0x1p-120;
-      const double lhs = sa + K0 - 0x1p-44 * (fabs(sa) + K0 + 1.0);
-      const double rhs = (double)t1 + pack_slack(t1) + E2;
-      code = ja;
-      open = own_ok && !(pc.finite && ja >= 0 && emax > 0.0 && lhs > rhs);
-      unsigned long long todo = __ballot(open);
-      while (todo) {
-        const int src = __ffsll((long long)todo) - 1;
-        todo &= todo - 1;
-        double xb[SUB], qb[SUB];
-#pragma unroll
-        for (int e = 0; e < SUB; ++e) {
-          xb[e] = __shfl(xs[e], src);
-          qb[e] = __shfl(qs[e], src);
-        }
-        const bool fin = all_finite(xb);
         double mx = -INFINITY;
         for (int j = lane; j < k; j += 64) mx = fmax(mx, sq_dist<SUB>(xb, sh.v64[j]));
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
-        double qq = 0.0;
-#pragma unroll
-        for (int e = 0; e < SUB; ++e) qq += qb[e] * qb[e];
-        const double qnb = sqrt(qq);
-        const double iqb = qnb > 0.0 ? 1.0 / qnb : 0.0;
-        const double ieb = mx > 0.0 ? 1.0 / mx : 0.0;
-        double bs = -INFINITY;
-        int bj = -1;
-        for (int j = lane; j < k; j += 64) {
-          const double sc = blend_score<SUB>(xb, qb, sh.v64[j], sh.v64[j][SUB + 1], ieb, qnb, iqb, beta);
-          if (sc > bs) {
-            bs = sc;
-            bj = j;
-          }
-        }
-        wave_argmax(bs, bj);
-        if (lane == src) code = fin && bj >= 0 ? bj : 0;
+        if (lane == src) emax = mx;
       }
     }
+    // ---- pass 2: the blend, up to the constant beta ||x||^2 / max e
+    const Raw<DT, SUB> qo = raw_sel<DT, SUB>(qr[0], qr[1], hh);
+    double qn;
+    {
+      float qf[SUB];
+      raw_floats<DT, SUB>(qo, qf);
+      double qn2 = 0.0;
+#pragma unroll
+      for (int e = 0; e < SUB; ++e) qn2 += (double)qf[e] * (double)qf[e];
+      qn = sqrt(qn2);
+    }
+    const double iqn = qn > 0.0 ? 1.0 / qn : 0.0;
+    const double iem = emax > 0.0 ? 1.0 / emax : 0.0;
+    const float al_own = (float)(2.0 * beta * ldexp(iem, -pc.se));
+    const float ga_own = (float)((1.0 - beta) * ldexp(iqn, -pc.sq));
+    float al[2], ga[2];
+    {
+      const float alp = __shfl_xor(al_own, 32), gap = __shfl_xor(ga_own, 32);
+      al[0] = hh ? alp : al_own;
+      al[1] = hh ? al_own : alp;
+      ga[0] = hh ? gap : ga_own;
+      ga[1] = hh ? ga_own : gap;
+    }
+    half8 Q1[2], Q2[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) make_b<DT, SUB>(qr[b], hh, 0u, 0u, Q1[b], Q2[b]);
+    // the blended fold value of tile tt, one block's q-accumulator at a time
+    auto blended = [&](int tt, f16v& s0, f16v& s1) {
+      tile_scores(tt, B1, B2, 0u, s0, s1);
+      const half8 fq = sh.fq[tt][lds_lane];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        f16v q = __builtin_amdgcn_mfma_f32_32x32x16_f16(fq, Q1[b], zero, 0, 0, 0);
+        if constexpr (SUB == 8 && DT == A2ATS_F32)
+          q = __builtin_amdgcn_mfma_f32_32x32x16_f16(fq, Q2[b], q, 0, 0, 0);
+        f16v& sb = b ? s1 : s0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sb[r] = __fmaf_rn(al[b], sb[r], ga[b] * q[r]);
+      }
+    };
+#pragma unroll
+    for (int tt = 0; tt < kPqTiles; ++tt) {
+      f16v a0, a1;
+      blended(tt, a0, a1);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        m0[r] = tt ? __builtin_elementwise_maximum(m0[r], a0[r]) : a0[r];
+        m1[r] = tt ? __builtin_elementwise_maximum(m1[r], a1[r]) : a1[r];
+      }
+      pin(m0, m1);
+      __builtin_amdgcn_sched_barrier(0);  // one tile's accumulators live at a time
+    }
+    finals();  // x and its bound again (not kept across the fold)
+    double qs[SUB];
+    {
+      float qf[SUB];
+      raw_floats<DT, SUB>(qo, qf);
+#pragma unroll
+      for (int e = 0; e < SUB; ++e) qs[e] = qf[e];
+    }
+    float t0, t1;
+    top2_slots(m0, m1, t0, t1);
+    const int row = slot_row(__float_as_uint(t0) & 31u);
+    double sa = -INFINITY;
+    int ja = -1;
+#pragma unroll 2
+    for (int tt = 0; tt < kPqTiles; ++tt) {
+      const int j = 32 * tt + row;
+      if (j < k) {
+        const double sc = blend_score<SUB>(xs, qs, sh.v64[j], sh.v64[j][SUB + 1], iem, qn, iqn, beta);
+        if (sc > sa) {
+          sa = sc;
+          ja = j;
+        }
+      }
+    }
+    // the fp32 fold value of row j approximates score_j + K0; its error bound
+    double nx2 = 0.0;
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) nx2 = fma(xs[e], xs[e], nx2);
+    const double K0 = beta * nx2 * iem;
+    const double Ms = nx * pc.Mv + pc.Shb;
+    const double Mq = ldexp(qn, pc.sq) * (1.0 + 0x1p-40);
+    float qnf, qd, ql;
+    norms<DT, SUB>(qo, qnf, qd, ql);
+    const double Eq = score_bound<DT, SUB>(qnf, qd, ql, pc.rhoq, pc.nuq, pc.nulq, 0.0, 0.0) +
+                      0x1p-40 * Mq;
+    const double aa = fabs((double)al_own), gg = fabs((double)ga_own);
+    const double E2 = (aa * (E * (1.0 + kRnd) + 3.0 * kRnd * Ms) +
+                       gg * (Eq * (1.0 + 2.0 * kRnd) + 4.0 * kRnd * Mq)) * (1.0 + 0x1p-16) +
+                      0x1p-120;
+    const double lhs = sa + K0 - 0x1p-44 * (fabs(sa) + K0 + 1.0);
+    const double rhs = (double)t1 + pack_slack(t1) + E2;
+    code = ja;
+    open = own_ok && !(pc.finite && ja >= 0 && emax > 0.0 && lhs > rhs);
+    unsigned long long todo = __ballot(open);
+    while (todo) {
+      const int src = __ffsll((long long)todo) - 1;
+      todo &= todo - 1;
+      double xb[SUB], qb[SUB];
+#pragma unroll
+      for (int e = 0; e < SUB; ++e) {
+        xb[e] = __shfl(xs[e], src);
+        qb[e] = __shfl(qs[e], src);
+      }
+      const bool fin = all_finite(xb);
+      double mx = -INFINITY;
+      for (int j = lane; j < k; j += 64) mx = fmax(mx, sq_dist<SUB>(xb, sh.v64[j]));
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+      double qq = 0.0;
+#pragma unroll
+      for (int e = 0; e < SUB; ++e) qq += qb[e] * qb[e];
+      const double qnb = sqrt(qq);
+      const double iqb = qnb > 0.0 ? 1.0 / qnb : 0.0;
+      const double ieb = mx > 0.0 ? 1.0 / mx : 0.0;
+      double bs = -INFINITY;
+      int bj = -1;
+      for (int j = lane; j < k; j += 64) {
+        const double sc = blend_score<SUB>(xb, qb, sh.v64[j], sh.v64[j][SUB + 1], ieb, qnb, iqb, beta);
+        if (sc > bs) {
+          bs = sc;
+          bj = j;
+        }
+      }
+      wave_argmax(bs, bj);
+      if (lane == src) code = fin && bj >= 0 ? bj : 0;
+    }
     if (own_ok) codes[(ohead * n + orow) * M + ss_own] = (uint8_t)code;
+  }
+}
+
+// Plain and H-weighted codes.  Each wave iteration: the 8 tiles' MFMAs folded into the slot
+// maxima (the table operand read from LDS at each tile pair), then the finalisation in
+// parts: the top two slots, the fp64 rescoring of the winning slot, the certificate, the rare
+// fp64 scans and the stores.  The inputs are fetched two iterations ahead; bf16 plain codes
+// run three workgroups per CU (their registers fit).
+template <int DT, int SUB, int MODE>
+constexpr int pq_wg_per_cu() {
+  return (DT == A2ATS_BF16 && MODE == kPlain) ? 3 : kPqWgPerCu;
+}
+
+template <int DT, int SUB, int MODE>
+__global__ __launch_bounds__(kPqThreads, (pq_wg_per_cu<DT, SUB, MODE>())) void pq_encode_codes(
+    const void* __restrict__ x, int64_t n, const int32_t* __restrict__ idx, int64_t n_sel,
+    int64_t heads, const float* __restrict__ cb, int k, const float* __restrict__ chol,
+    uint8_t* __restrict__ codes) {
+  constexpr int M = kD / SUB;   // sub-spaces per row
+  constexpr int RPI = 64 / M;   // rows per wave iteration
+  __shared__ PqShared<SUB, false> sh;
+  const int lane = threadIdx.x & 63, col = lane & 31, hh = lane >> 5;
+  int lr[2], ss[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    lr[b] = (32 * b + col) / M;
+    ss[b] = (32 * b + col) % M;
+  }
+  const int lr_own = lane / M, ss_own = lane % M;  // the sub-vector this lane decides
+
+  // iterations (head, group of RPI selected rows), wave-uniform, every stride-th one
+  const int64_t G = (n_sel + RPI - 1) / RPI;
+  const int64_t stride = (int64_t)gridDim.x * kPqWaves;
+  const int64_t st_h = stride / G, st_g = stride % G;
+  const int64_t it0 = (int64_t)blockIdx.x * kPqWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t h_cur = it0 / G, g_cur = it0 % G;
+  auto advance = [&](int64_t& h, int64_t& g) {
+    h += st_h;
+    g += st_g;
+    if (g >= G) {
+      g -= G;
+      ++h;
+    }
+  };
+  auto locate = [&](int64_t h, int64_t g, int l_r, int64_t& row) {
+    const int64_t sel = g * RPI + l_r;
+    row = -1;
+    if (h < heads && sel < n_sel) row = idx ? (int64_t)idx[h * n_sel + sel] : sel;
+    return row >= 0 && row < n;
+  };
+  // inputs are fetched two iterations ahead (nx_raw: the next, nn_raw: the one after)
+  Raw<DT, SUB> nx_raw[2], nn_raw[2];
+  auto fetch = [&](int64_t h, int64_t g, Raw<DT, SUB> (&dst)[2]) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      int64_t row = 0;
+      const bool ok = locate(h, g, lr[b], row);
+      dst[b] = load_raw<DT, SUB>(x, ((h * n + row) * kD + ss[b] * SUB), ok);
+    }
+  };
+  int64_t h_nx = h_cur, g_nx = g_cur;  // the iteration after the current one
+  advance(h_nx, g_nx);
+  fetch(h_cur, g_cur, nx_raw);  // in flight during the preparation
+  fetch(h_nx, g_nx, nn_raw);
+
+  const PqConsts pc = pq_prep<SUB, MODE, DT>(cb, k, chol, sh);
+  if (h_cur >= heads) return;  // no iteration for this wave (the preparation's barriers are past)
+
+  const unsigned e2 = pk16(ldexpf(1.f, pc.eb), ldexpf(1.f, pc.eb));
+  const unsigned mk = pk16(32768.f, 0.f);
+  const half8 Bb = hh ? h8(0u, 0u, 0u, 0u) : h8(e2, mk, 0u, 0u);  // bias operand, sub_dim 8
+  const f16v zero = {};
+  int lds_lane = lane, lds_zero = 0;
+
+  // The table operand of a tile pair, read from LDS.
+  struct PairOps {
+    half8 a[2];
+    unsigned b0[2], b1[2];
+  };
+  auto load_ops = [&](int tp) {
+    PairOps o;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      o.a[q] = sh.fa[2 * tp + q][lds_lane];
+      if constexpr (SUB == 8) {
+        o.b0[q] = sh.fb[2 * tp + q][lds_lane][0];
+        o.b1[q] = sh.fb[2 * tp + q][lds_lane][1];
+      }
+    }
+    return o;
+  };
+  // scores of tile tt for both blocks (S units, bias included)
+  auto tile_scores = [&](const PairOps& o, int q, const half8 (&b1)[2], const half8 (&b2)[2],
+                         f16v& s0, f16v& s1) {
+    const half8 at = o.a[q];
+    if constexpr (SUB == 8) {
+      const f16v cbias = __builtin_amdgcn_mfma_f32_32x32x16_f16(h8(o.b0[q], o.b1[q], 0u, 0u), Bb,
+                                                                zero, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(at, b1[0], cbias, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(at, b1[1], cbias, 0, 0, 0);
+      if constexpr (DT == A2ATS_F32) {
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(at, b2[0], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(at, b2[1], s1, 0, 0, 0);
+      }
+    } else {
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(at, b1[0], zero, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(at, b1[1], zero, 0, 0, 0);
+    }
+  };
+  // tile pair tp of one iteration folded into the slot maxima (n0, n1)
+  auto fold_pair = [&](int tp, const PairOps& o, const half8 (&b1)[2], const half8 (&b2)[2],
+                       f16v& n0, f16v& n1) {
+    f16v a0, a1, c0, c1;
+    tile_scores(o, 0, b1, b2, a0, a1);
+    tile_scores(o, 1, b1, b2, c0, c1);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      n0[r] = tp ? fmax3(n0[r], a0[r], c0[r]) : __builtin_elementwise_maximum(a0[r], c0[r]);
+      n1[r] = tp ? fmax3(n1[r], a1[r], c1[r]) : __builtin_elementwise_maximum(a1[r], c1[r]);
+    }
+    pin(n0, n1);
+  };
+
+  // ---- an iteration's state and its finalisation, in parts
+  f16v m0, m1;          // its slot maxima
+  Raw<DT, SUB> xo_p;    // this lane's sub-vector of it
+  int64_t orow_p = -1, ohead_p = 0;
+  bool ok_p = false;
+  float t0, t1;         // its top two slot values (packed)
+  int row;              // the winning slot's row within a tile
+  double xs[SUB];       // the sub-vector, exact
+  double sa = 0.0;      // the best packed fp64 score of the winning slot
+  float fx, fd, fl;     // ||x||, ||x - x'||, ||lo||
+  int code = 0;
+  bool open = false;
+  auto fin_a = [&]() {
+    top2_slots(m0, m1, t0, t1);
+    row = slot_row(__float_as_uint(t0) & 31u);
+    asm volatile("" ::"v"(t1), "v"(row));
+  };
+  // rows tt0 .. tt0 + 3 of the winning slot in fp64 (a pad row scores about -2^1000); each
+  // score carries its tile in its lowest 3 bits, ordered so that the larger packed value is
+  // the lower tile between equal scores, and the best is a plain maximum
+  auto fin_rows = [&](int tt0) {
+#pragma unroll
+    for (int tt = tt0; tt < tt0 + 4; ++tt) {
+      const int j = 32 * tt + row;
+      double s = -sh.v64[j][SUB];
+#pragma unroll
+      for (int e = 0; e < SUB; ++e) s = fma(xs[e], sh.v64[j][e], s);
+      const int hi = __double2hiint(s);
+      const unsigned c3 = (unsigned)(7 - tt) ^ ((unsigned)(hi >> 31) & 7u);
+      s = __hiloint2double(hi, (int)(((unsigned)__double2loint(s) & ~7u) | c3));
+      sa = tt ? max_f64(sa, s) : s;
+    }
+    asm volatile("" ::"v"(sa));
+  };
+  auto fin_b = [&]() {
+    float xf[SUB];
+    raw_floats<DT, SUB>(xo_p, xf);
+#pragma unroll
+    for (int e = 0; e < SUB; ++e) xs[e] = xf[e];
+    fin_rows(0);
+  };
+  auto fin_c = [&]() {
+    fin_rows(4);
+    norms<DT, SUB>(xo_p, fx, fd, fl);
+    asm volatile("" ::"v"(fx), "v"(fd), "v"(fl));
+  };
+  auto fin_d = [&]() {
+    const int hia = __double2hiint(sa);
+    const int tta = 7 - (int)(((unsigned)__double2loint(sa) & 7u) ^ ((unsigned)(hia >> 31) & 7u));
+    const int ja = sa > -0x1p999 ? 32 * tta + row : -1;
+    // every row outside the winning slot: its MFMA score is at most t1 (plus the packing), its
+    // error, when it could reach s_a at all, at most the bound for rows of size R
+    const double nx = fx;
+    double Z = nx;  // ||z|| (z = x L; x itself without L), rounded up
+    if constexpr (MODE == kHWeighted) {
+      // z in fp32: each element within 2^-21 sum_b |x_b L_ba|, so ||z|| within
+      // 2^-21 ||x|| ||L||_F of the fp32 vector's norm
+      float xf[SUB];
+      raw_floats<DT, SUB>(xo_p, xf);
+      float z2 = 0.f;
+#pragma unroll
+      for (int a = 0; a < SUB; ++a) {
+        float za = 0.f;
+#pragma unroll
+        for (int b = 0; b < SUB; ++b) za = __fmaf_rn(xf[b], sh.l32[b][a + lds_zero], za);
+        z2 = __fmaf_rn(za, za, z2);
+      }
+      Z = (double)sqrt_up(z2) + 0x1p-21 * nx * pc.lf;
+    }
+    const float disc = (float)fmax(0.0, Z * Z - 2.0 * sa) * (1.f + 0x1p-18f);
+    const double R = (Z + (double)sqrt_up(disc)) * (1.0 + 0x1p-20) + 0x1p-60;
+    const double Ec = R * (pc.c_rr * R + pc.c_x * nx + pc.c_d * (double)fd + pc.c_l * (double)fl) + 0x1p-120;
+    const double lhs = ldexp(sa, pc.se) * (1.0 - 0x1p-47 * (sa < 0.0 ? -1.0 : 1.0));  // the packed bits
+    const double rhs = (double)t1 + pack_slack(t1) + Ec;
+    code = ja;
+    open = ok_p && !(pc.finite && ja >= 0 && lhs > rhs);
+    asm volatile("" ::"v"(code), "v"(open ? 1 : 0));
+  };
+  // the rest (rare): the whole wave scores the whole table in fp64 for one sub-vector at a
+  // time; then the codes are stored
+  auto fin_tail = [&]() {
+    unsigned long long todo = __ballot(open);
+    while (todo) {
+      const int src = __ffsll((long long)todo) - 1;
+      todo &= todo - 1;
+      double xb[SUB];
+      bool fin = true;
+#pragma unroll
+      for (int e = 0; e < SUB; ++e) {
+        xb[e] = __shfl(xs[e], src);
+        fin = fin && (xb[e] - xb[e] == 0.0);
+      }
+      double bs = -INFINITY;
+      int bj = -1;
+      for (int j = lane; j < k; j += 64) {
+        double s = -sh.v64[j][SUB];
+#pragma unroll
+        for (int e = 0; e < SUB; ++e) s = fma(xb[e], sh.v64[j][e], s);
+        if (s > bs) {  // a NaN score (a non-finite table row) never wins
+          bs = s;
+          bj = j;
+        }
+      }
+      wave_argmax(bs, bj);
+      // a non-finite input: every distance is inf or NaN, code 0
+      if (lane == src) code = fin && bj >= 0 ? bj : 0;
+    }
+    if (ok_p) codes[(ohead_p * n + orow_p) * M + ss_own] = (uint8_t)code;
+  };
+
+  // ---- each iteration: the fold of all tiles, then the finalisation
+  for (;;) {
+    {
+      int z = 0;
+      asm volatile("" : "+v"(z));
+      lds_zero = z;
+      lds_lane = lane + z;
+    }
+    const Raw<DT, SUB> xr[2] = {nx_raw[0], nx_raw[1]};
+    nx_raw[0] = nn_raw[0];
+    nx_raw[1] = nn_raw[1];
+    {
+      int64_t h2 = h_nx, g2 = g_nx;
+      advance(h2, g2);
+      fetch(h2, g2, nn_raw);  // two iterations ahead: stays in flight
+    }
+    half8 B1[2], B2[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) make_b<DT, SUB>(xr[b], hh, e2, mk, B1[b], B2[b]);
+#pragma unroll
+    for (int tp = 0; tp < kPqTiles / 2; ++tp) {
+      fold_pair(tp, load_ops(tp), B1, B2, m0, m1);
+      __builtin_amdgcn_sched_barrier(0);  // one tile pair's accumulators live at a time
+    }
+    xo_p = raw_sel<DT, SUB>(xr[0], xr[1], hh);
+    ohead_p = h_cur;
+    ok_p = locate(h_cur, g_cur, lr_own, orow_p);
+    fin_a();
+    fin_b();
+    fin_c();
+    fin_d();
+    fin_tail();
+    h_cur = h_nx;
+    g_cur = g_nx;
+    advance(h_nx, g_nx);
+    if (h_cur >= heads) break;
   }
 }
 
@@ -1066,16 +1233,19 @@ int launch_pq(int mode, const void* x, int64_t n, const int32_t* idx, int64_t n_
   const int64_t rpi = 64 / (kD / SUB);
   const int64_t waves = heads * ((n_sel + rpi - 1) / rpi);  // one wave iteration each
   int64_t g = (waves + kPqWaves - 1) / kPqWaves;
-  if (g > (int64_t)kPqCus * kPqWgPerCu) g = (int64_t)kPqCus * kPqWgPerCu;
+  const int per_cu = mode == kPlain ? pq_wg_per_cu<DT, SUB, kPlain>()
+                                    : (mode == kHWeighted ? pq_wg_per_cu<DT, SUB, kHWeighted>()
+                                                          : kPqWgPerCu);
+  if (g > (int64_t)kPqCus * per_cu) g = (int64_t)kPqCus * per_cu;
   const dim3 grid((unsigned)g), block(kPqThreads);
   if (mode == kHWeighted)
-    return launch("pq_encode_h", pq_encode_mfma<DT, SUB, kHWeighted>, grid, block, 0, s, x, n,
-                  idx, n_sel, heads, cb, k, chol, query, nq, beta, codes);
+    return launch("pq_encode_h", pq_encode_codes<DT, SUB, kHWeighted>, grid, block, 0, s, x, n,
+                  idx, n_sel, heads, cb, k, chol, codes);
   if (mode == kBlend)
-    return launch("pq_encode_blend", pq_encode_mfma<DT, SUB, kBlend>, grid, block, 0, s, x, n,
-                  idx, n_sel, heads, cb, k, chol, query, nq, beta, codes);
-  return launch("pq_encode_plain", pq_encode_mfma<DT, SUB, kPlain>, grid, block, 0, s, x, n, idx,
-                n_sel, heads, cb, k, chol, query, nq, beta, codes);
+    return launch("pq_encode_blend", pq_encode_blend<DT, SUB>, grid, block, 0, s, x, n, idx,
+                  n_sel, heads, cb, k, query, nq, beta, codes);
+  return launch("pq_encode_plain", pq_encode_codes<DT, SUB, kPlain>, grid, block, 0, s, x, n, idx,
+                n_sel, heads, cb, k, chol, codes);
 }
 
 template <int DT>
