@@ -424,14 +424,23 @@ int a2ats_kmeans(const void* x, int x_dtype, int64_t heads, int64_t n, int64_t d
  *               +0 are equal), in ascending index order; score[b, h] (optional) their scores
  *   qb        [batch, hq, d] fp32 or bf16 (q_dtype): the query already rotated by R_b
  *               (a2ats_far_query_rope)
- *   codes     [batch, hkv, n] uint16; codebook [hkv, c, d] fp32, 1 <= c <= 4096, d = 128
+ *   codes     [batch, hkv, n] uint16; codebook [hkv, c, d] fp32 (16-byte aligned),
+ *               1 <= c <= 4096, d = 128
  *   idx       [batch, hq, k] int32; score [batch, hq, k] fp32 or NULL; 0 <= k <= n
- * hq must be a multiple of hkv.  Nothing is written when n or k is 0.  No workspace; one
- * workgroup reads the codes and the codebook once for up to four query heads of a group.
+ * hq must be a multiple of hkv and batch * hq < 2^31.  Nothing is written when n or k is 0.
+ * Two launches: every query's table into the workspace (a codebook tile staged once for 16
+ * queries of its head), then the selection, one workgroup reading a code row once for up to
+ * four query heads of a group: the K-th largest score by passes of monotone 1024-bin
+ * histograms over the C + 1 table entries weighted by their token counts, then the output by
+ * wave ballots in token order.  Workspace: a2ats_topk_workspace(batch, hq, c) bytes (the
+ * tables; 256-byte aligned), A2ATS_EWORKSPACE when missing or short.  A2ATS_EINVAL for a
+ * misaligned codebook.  Returns without waiting.
  */
+size_t a2ats_topk_workspace(int64_t batch, int64_t hq, int64_t c);
 int a2ats_topk_codes(const void* qb, int q_dtype, int64_t batch, int64_t hq, int64_t hkv,
                      int64_t d, const uint16_t* codes, int64_t n, const float* codebook,
-                     int64_t c, int64_t k, int32_t* idx, float* score, void* stream);
+                     int64_t c, int64_t k, int32_t* idx, float* score, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * Kernel timing (diagnostics).  While enabled, every kernel the library launches is

@@ -88,7 +88,10 @@ def lib() -> ctypes.CDLL:
         L.a2ats_kmeans_init_workspace.argtypes = [i64, i64, i64, i64]
         L.a2ats_kmeans_init_workspace.restype = sz
         L.a2ats_kmeans_init.argtypes = [p, i32, i64, i64, i64, i64, p, p, p, p, p, sz, p]
-        L.a2ats_topk_codes.argtypes = [p, i32, i64, i64, i64, i64, p, i64, p, i64, i64, p, p, p]
+        L.a2ats_topk_workspace.argtypes = [i64, i64, i64]
+        L.a2ats_topk_workspace.restype = sz
+        L.a2ats_topk_codes.argtypes = [p, i32, i64, i64, i64, i64, p, i64, p, i64, i64, p, p, p,
+                                       sz, p]
         L.a2ats_profile_enable.argtypes, L.a2ats_profile_enable.restype = [i32], i32
         L.a2ats_profile_reset.argtypes, L.a2ats_profile_reset.restype = [], i32
         L.a2ats_profile_read.argtypes, L.a2ats_profile_read.restype = [ctypes.c_char_p, sz], i64
@@ -588,9 +591,10 @@ def topk_codes(qb: torch.Tensor, codes: torch.Tensor, codebook: torch.Tensor, k:
         raise ValueError("qb, codes and codebook shapes disagree")
     idx = torch.empty((batch, hq, k), dtype=torch.int32, device=qb.device)
     sc = torch.empty((batch, hq, k), dtype=torch.float32, device=qb.device) if want_scores else None
+    ws = _workspace(lib().a2ats_topk_workspace(batch, hq, c), qb.device)
     _check(lib().a2ats_topk_codes(_ptr(qb), _dtype_code(qb), batch, hq, hkv, d, _ptr(codes), n,
-                                  _ptr(codebook), c, int(k), _ptr(idx), _ptr(sc),
-                                  _stream(qb.device)), "topk_codes")
+                                  _ptr(codebook), c, int(k), _ptr(idx), _ptr(sc), _ptr(ws),
+                                  ws.numel(), _stream(qb.device)), "topk_codes")
     return (idx, sc) if want_scores else idx
 
 

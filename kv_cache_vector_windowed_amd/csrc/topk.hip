@@ -4,28 +4,16 @@
 // docs, "paper fidelity" section, Eq. 11-12) the approximate logit of token t is
 // (q R_b) . c_{code_t}: one table of C values per query, gathered by code.
 //
-// Kernel topk_codes_rows: one 1024-thread workgroup per (sequence, key/value head, group of up
-// to four of the query heads that share that key/value head).  The codes and the codebook are
-// read once for the whole group.
-//   1. table: lut_gj = fp32(sum_a qb_ga * c_ja) with the sum taken in fp64 in dimension order
-//      and rounded to fp32 once.  Both factors have at most 24 significant bits, so each fp64
-//      product is exact and fma(q, c, acc) equals acc + q*c rounded once: the fma loop is the
-//      plain product-then-add sum.  The codebook streams through LDS in 1024-centroid x
-//      8-dimension tiles, double-buffered and stored transposed by eight loader waves while
-//      four table waves compute; each table thread owns four adjacent centroids (one 16-byte
-//      LDS read a dimension) and reads the query values with wave-uniform scalar loads, so
-//      one codebook read serves every query of the group.
-//   2. the code row goes to LDS (rows up to 32768 tokens; longer rows are read from global
-//      memory in each pass) and its histogram over the C codes (+1 bin for codes >= C) is taken.
-//   3. for all queries of the group at once: the K-th largest score T_g by a radix select
-//      (8 bits a pass, four passes) over the C + 1 table entries weighted by their counts, not
-//      over the n tokens; r_g = how many of the tokens scoring exactly T_g are taken (the
-//      lowest indices among them).  Then one class byte per code: bit 2g = above T_g, bit
-//      2g+1 = equal to T_g.
-//   4. ordered compaction.  Each wave owns a contiguous token range, 256 tokens a step (four
-//      a lane, slot-major so that one ballot per slot orders them); a first pass counts every
-//      query's tokens above and at T_g per wave, a second writes every query's taken indices
-//      (and scores) in ascending order.
+// Two kernels (their own comments say more):
+//   topk_table       every query's table, lut_gj = fp32(sum_a qb_ga * c_ja) with the sum taken
+//                    in fp64 in dimension order and rounded to fp32 once.  Both factors have at
+//                    most 24 significant bits, so each fp64 product is exact and fma(q, c, acc)
+//                    equals acc + q*c rounded once: the fma loop is the plain product-then-add
+//                    sum.  Each codebook tile is staged once for 16 queries of its head.
+//   topk_codes_rows  per (sequence, key/value head, up to four query heads): the histogram of
+//                    the code row, the K-th largest score by monotone-bin histogram passes over
+//                    the C + 1 weighted table entries (not over the n tokens), and the ordered
+//                    output by wave ballots.
 // Scores compare through the order-preserving map of fp32 onto u32 (-0 and +0 equal); a code
 // >= C scores -inf.
 #include "common.hpp"
@@ -36,18 +24,7 @@ namespace {
 constexpr int kD = A2ATS_HEAD_DIM;
 constexpr int kTkThreads = 1024;
 constexpr int kTkMaxC = 4096;                        // table entries per query in LDS
-constexpr int kTkEnt = (kTkMaxC + 1 + kTkThreads - 1) / kTkThreads;  // table entries per thread
-constexpr int kTkTile = 1024;                        // centroids per codebook tile
-constexpr int kTkDims = 8;                           // dimensions per codebook tile
-// A tile is stored transposed, one row of 1024 centroids per dimension.  The pitch makes the
-// transposing scalar writes conflict-free (the two half-rows a wave writes land 32 banks
-// apart) and keeps rows 16-byte aligned for the four-centroid reads.
-constexpr int kTkPitch = kTkTile + 8;
-constexpr int kTkR = 4;                              // centroids per table thread
-constexpr int kTkStage = 2 * kTkDims * kTkPitch;     // floats: two tiles; also the code row
-constexpr int kTkLdsCodes = 32768;                   // longest code row kept in LDS
-static_assert(kTkLdsCodes * 2 <= kTkStage * 4, "code row must fit the staging area");
-static_assert(kTkTile == kTkR * 256, "256 table threads");
+constexpr int kTkLdsCodes = 16384;                   // longest code row kept in LDS
 
 __device__ __forceinline__ unsigned tk_order_key(float s) {
   if (s == 0.0f) s = 0.0f;  // -0 and +0 rank equal
@@ -55,53 +32,258 @@ __device__ __forceinline__ unsigned tk_order_key(float s) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ int tk_wave_sum(int v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
+// Kernel topk_table: every query's score table, lut[b * hq + h, j] = fp32(sum_a q[b, h, a] *
+// c[kvh, j, a]), the fp64 products added in dimension order and rounded to fp32 once.  A
+// 256-thread workgroup takes one key/value head, a tile of 64 centroids (fp32 rows in LDS, one
+// a lane) and four groups of 4 of that head's queries (all sequences and query heads of the
+// group, converted to fp64 into LDS once), one group a wave; each centroid value a lane
+// converts serves the wave's 4 queries, read as broadcasts.  Workgroups sharing a codebook tile
+// are numbered so that they land on one XCD (launch order deals workgroups to the 8 XCDs in
+// turn).
+constexpr int kTbQg = 4;       // queries a wave
+constexpr int kTbWaves = 4;    // waves (query groups) a workgroup
+constexpr int kTbCent = 64;    // centroids a workgroup (one a lane)
 
-constexpr int kTkLoaders = 512;  // threads 512 .. 1023 stage the codebook tiles
-
-// Codebook tile [cb0, cb0 + 1024) x [8 ch, 8 ch + 8) into a loader thread's registers (u =
-// its index among the loaders): four float4, two loaders a centroid row segment (32 bytes).
-__device__ __forceinline__ void tk_load_tile(float4 (&pre)[4], const float* __restrict__ cbh,
-                                             int c, int cb0, int ch, int u) {
+template <int QDT>
+__global__ __launch_bounds__(kTbWaves * 64) void topk_table(const void* __restrict__ qb, int hq,
+                                                            int group, int nqh, int nqb, int nct,
+                                                            const float* __restrict__ cb, int c,
+                                                            float* __restrict__ lut) {
+  constexpr int kPitch = kD + 1;  // floats: lane j reads row j, so a column read is conflict-free
+  __shared__ float ct[kTbCent * kPitch];
+  __shared__ __align__(16) double qt[kTbWaves][kD][kTbQg];  // [wave][a][v]
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int ntiles = (int)gridDim.x;
+  int tile = (int)blockIdx.x;
+  if ((ntiles & 7) == 0) tile = (tile & 7) * (ntiles >> 3) + (tile >> 3);
+  const int qblk = tile % nqb;
+  const int ctile = (tile / nqb) % nct;
+  const int kvh = tile / (nqb * nct);
+  const float* cbh = cb + ((int64_t)kvh * c + (int64_t)ctile * kTbCent) * kD;
+  const int rows = c - ctile * kTbCent < kTbCent ? c - ctile * kTbCent : kTbCent;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = u + kTkLoaders * i, j = cb0 + (q >> 1);
-    pre[i] = j < c ? *reinterpret_cast<const float4*>(cbh + (int64_t)j * kD + ch * kTkDims +
-                                                      (q & 1) * 4)
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < kTbCent * kD / 4 / (kTbWaves * 64); ++i) {  // the codebook tile
+    const int f = t + kTbWaves * 64 * i, jr = f >> 5, a4 = (f & 31) * 4;
+    const float4 v = jr < rows ? *reinterpret_cast<const float4*>(cbh + (int64_t)jr * kD + a4)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    float* d = &ct[jr * kPitch + a4];
+    d[0] = v.x;
+    d[1] = v.y;
+    d[2] = v.z;
+    d[3] = v.w;
+  }
+  {  // the queries: thread t converts 32 dimensions of query t / 16 of the block (0 past the end)
+    const int qq = t >> 4, a0 = (t & 15) * 8, r = qblk * kTbWaves * kTbQg + qq;
+    double* dst = &qt[qq / kTbQg][0][qq % kTbQg];
+    if (r < nqh) {
+      const int64_t row = (int64_t)(r / group) * hq + (int64_t)kvh * group + r % group;
+#pragma unroll
+      for (int a = 0; a < 8; ++a) dst[(a0 + a) * kTbQg] = (double)load_elem(qb, QDT, row * kD + a0 + a);
+    } else {
+#pragma unroll
+      for (int a = 0; a < 8; ++a) dst[(a0 + a) * kTbQg] = 0.0;
+    }
+  }
+  __syncthreads();
+  const int qg = qblk * kTbWaves + wave;
+  if (kTbQg * qg >= nqh) return;  // the whole wave; no barriers follow
+  const float* crow = &ct[lane * kPitch];
+  const double* qs = &qt[wave][0][0];
+  double acc[kTbQg];
+#pragma unroll
+  for (int v = 0; v < kTbQg; ++v) acc[v] = 0.0;
+#pragma unroll 4
+  for (int a = 0; a < kD; ++a) {
+    const double x = (double)crow[a];
+    const double2 q01 = *reinterpret_cast<const double2*>(&qs[a * kTbQg]);
+    const double2 q23 = *reinterpret_cast<const double2*>(&qs[a * kTbQg + 2]);
+    acc[0] = __fma_rn(q01.x, x, acc[0]);
+    acc[1] = __fma_rn(q01.y, x, acc[1]);
+    acc[2] = __fma_rn(q23.x, x, acc[2]);
+    acc[3] = __fma_rn(q23.y, x, acc[3]);
+  }
+  const int j = ctile * kTbCent + lane;
+  if (j >= c) return;
+#pragma unroll
+  for (int v = 0; v < kTbQg; ++v) {
+    const int r = kTbQg * qg + v;
+    if (r >= nqh) break;
+    const int64_t row = (int64_t)(r / group) * hq + (int64_t)kvh * group + r % group;
+    lut[row * c + j] = (float)acc[v];
   }
 }
 
-// Transposed store: dimension 4h + e of centroid j goes to buf[(4h + e) * pitch + j].
-__device__ __forceinline__ void tk_store_tile(float* buf, const float4 (&pre)[4], int u) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = u + kTkLoaders * i, j = q >> 1;
-    float* s = buf + (q & 1) * 4 * kTkPitch + j;
-    s[0] = pre[i].x;
-    s[kTkPitch] = pre[i].y;
-    s[2 * kTkPitch] = pre[i].z;
-    s[3 * kTkPitch] = pre[i].w;
+// Kernel topk_codes_rows: one 1024-thread workgroup per (sequence, key/value head, group of up
+// to four query heads sharing it).  LDS is laid out per call (TkLayout): the group's tables,
+// the select histograms, the code histogram (then the class bytes) and the code row when it
+// fits.
+//   1. the group's tables from the workspace (their key ranges reduced on the way), the code
+//      row and its histogram over the C codes (+1 bin for codes >= C): the weight of table
+//      entry j is the number of tokens holding it.
+//   2. for all queries at once, the K-th largest score T_g over the C + 1 weighted entries
+//      (thread t holds entries t, t + 1024, ... < C in registers, thread 0 also the -inf entry
+//      of the codes >= C) and r_g = how many of the tokens
+//      scoring exactly T_g are taken (the lowest indices).  A pass bins the live entries into
+//      1024 bins by a monotone map of the score (linear in the fp32 value while the range is
+//      finite, else a shift of the order key), wave g finds the bin holding the remaining
+//      rank, and that bin's entries stay live.  A pass over keys closer than 1024 units is
+//      exact; a bin of at most 64 entries is settled by wave g comparing them pairwise.
+//   3. one class byte per code: bit 2g = above T_g, bit 2g+1 = equal to T_g.
+//   4. rounds of 16384 tokens, 1024 contiguous tokens a wave: the wave counts its tokens above
+//      and at T_g from ballots, the counts are scanned over the waves, and each wave writes
+//      its taken tokens (ascending) at offsets from lane-masked bit counts.
+struct TkLayout {
+  unsigned lut, hist, cnt, cl, total;
+};
+
+constexpr unsigned kTkLdsMax = 156 * 1024;  // dynamic LDS; the static arrays take the rest
+constexpr int kNb = 1024;                   // bins of a select pass
+constexpr int kNbPad = kNb + kNb / 16;      // a pad slot after every 16 bins
+constexpr int kCand = 64;                   // largest bin settled pairwise
+constexpr int kTkRound = kTkThreads * 16;   // tokens of an output round
+
+inline unsigned tk_al16(unsigned x) { return (x + 15u) & ~15u; }
+
+// The LDS layout of a call; cl is 0xFFFFFFFF when the code row does not fit.
+inline TkLayout tk_layout(int gn, int c, int64_t n) {
+  TkLayout L;
+  unsigned off = 0;
+  L.lut = off;
+  off = tk_al16(off + (unsigned)(gn * (c + 1)) * 4u);
+  L.hist = off;
+  off = tk_al16(off + (unsigned)(gn * kNbPad) * 8u);
+  L.cnt = off;
+  off = tk_al16(off + (unsigned)(c + 1) * 4u);
+  L.cl = 0xFFFFFFFFu;
+  if (n <= kTkLdsCodes && off + (unsigned)n * 2u <= kTkLdsMax) {
+    L.cl = off;
+    off = tk_al16(off + (unsigned)n * 2u);
   }
+  L.total = off;
+  return L;
 }
 
-template <int QDT, int GN, bool CLDS>
+// the histogram slot of bin b: a pad after every 16 bins, so that lanes reading 16 bins each
+// (a stride of 17 eight-byte slots) hit distinct banks
+__device__ __forceinline__ int tk_hslot(unsigned b) { return (int)(b + (b >> 4)); }
+
+template <int CTRL, int ROWS = 0xF, bool BOUND = false>
+__device__ __forceinline__ unsigned tk_dpp(unsigned x) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xF, BOUND);
+}
+// minimum / maximum over each row of 16 lanes, in every lane of the row
+__device__ __forceinline__ unsigned row_min(unsigned x) {
+  x = min(x, tk_dpp<0xB1>(x));   // quad_perm 1,0,3,2
+  x = min(x, tk_dpp<0x4E>(x));   // quad_perm 2,3,0,1
+  x = min(x, tk_dpp<0x141>(x));  // row_half_mirror
+  return min(x, tk_dpp<0x140>(x));  // row_mirror
+}
+__device__ __forceinline__ unsigned row_max(unsigned x) {
+  x = max(x, tk_dpp<0xB1>(x));
+  x = max(x, tk_dpp<0x4E>(x));
+  x = max(x, tk_dpp<0x141>(x));
+  return max(x, tk_dpp<0x140>(x));
+}
+__device__ __forceinline__ unsigned rdlane(unsigned x, int l) {
+  return (unsigned)__builtin_amdgcn_readlane((int)x, l);
+}
+__device__ __forceinline__ unsigned wave_min(unsigned x) {
+  x = row_min(x);
+  return min(min(rdlane(x, 0), rdlane(x, 16)), min(rdlane(x, 32), rdlane(x, 48)));
+}
+__device__ __forceinline__ unsigned wave_max(unsigned x) {
+  x = row_max(x);
+  return max(max(rdlane(x, 0), rdlane(x, 16)), max(rdlane(x, 32), rdlane(x, 48)));
+}
+// inclusive sum over each row of 16 lanes
+__device__ __forceinline__ unsigned row_incl_sum(unsigned x) {
+  x += tk_dpp<0x111, 0xF, true>(x);  // row_shr 1, 0 past the row start
+  x += tk_dpp<0x112, 0xF, true>(x);
+  x += tk_dpp<0x114, 0xF, true>(x);
+  return x + tk_dpp<0x118, 0xF, true>(x);
+}
+// inclusive sum over the wave
+__device__ __forceinline__ unsigned wave_incl_sum(unsigned x) {
+  x = row_incl_sum(x);
+  x += tk_dpp<0x142, 0xA>(x);  // row_bcast15: row 0's total into row 1, row 2's into row 3
+  return x + tk_dpp<0x143, 0xC>(x);  // row_bcast31: rows 0-1's total into rows 2 and 3
+}
+// bit count of the lanes below this one in m, plus base
+__device__ __forceinline__ unsigned lanes_below(unsigned long long m, unsigned base) {
+  return __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, base));
+}
+__device__ __forceinline__ unsigned long long tk_ballot(bool p) {
+  return __builtin_amdgcn_ballot_w64(p);
+}
+// the fp32 value of an order key (the inverse of tk_order_key; +0 for the zero key)
+__device__ __forceinline__ float tk_key_value(unsigned u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// One select pass's monotone bin map: linear in the fp32 value, or the order key shifted right.
+struct TkBins {
+  bool lin;
+  float lo, scale;
+  unsigned kmin, sh;
+  __device__ __forceinline__ unsigned operator()(unsigned key) const {
+    if (lin) {
+      const float d = (tk_key_value(key) - lo) * scale;
+      return d >= (float)(kNb - 1) ? (unsigned)(kNb - 1) : (unsigned)d;
+    }
+    return (key - kmin) >> sh;
+  }
+};
+
+// The bin map of a pass over keys [lo, hi], lo < hi: linear bins while both ends are finite
+// (keys strictly between those of -inf and +inf) and the scale is finite, for the first two
+// passes only, so that the shift passes (each narrowing the key range at least 512-fold) bound
+// the pass count.  Both maps send lo to bin 0 and hi to a bin >= 511, so every pass drops
+// entries.
+__device__ __forceinline__ TkBins tk_bin_map(unsigned lo, unsigned hi, int pass) {
+  TkBins B;
+  B.kmin = lo;
+  B.sh = 0u;
+  B.lin = false;
+  B.lo = 0.0f;
+  B.scale = 0.0f;
+  if (pass < 2 && lo > 0x007FFFFFu && hi < 0xFF800000u) {
+    const float vlo = tk_key_value(lo), span = tk_key_value(hi) - vlo;
+    const float scale = (float)kNb / span;
+    if (span > 0.0f && span <= 3.0e38f && scale > 0.0f && scale <= 3.0e38f) {
+      B.lin = true;
+      B.lo = vlo;
+      B.scale = scale;
+      return B;
+    }
+  }
+  const int bits = 32 - __clz((int)(hi - lo));
+  B.sh = bits > 10 ? (unsigned)(bits - 10) : 0u;
+  return B;
+}
+
+template <int GN, int E, bool CLDS>
 __global__ __launch_bounds__(kTkThreads) void topk_codes_rows(
-    const void* __restrict__ qb, int64_t hq, int64_t hkv, int group, int nchunk,
-    const uint16_t* __restrict__ codes, int64_t n, const float* __restrict__ cb, int c,
-    int64_t k, int32_t* __restrict__ idx, float* __restrict__ score) {
+    const float* __restrict__ lut_ws, int64_t hq, int64_t hkv, int group, int nchunk,
+    const uint16_t* __restrict__ codes, int64_t n, int c, int64_t k, int32_t* __restrict__ idx,
+    float* __restrict__ score, TkLayout ly) {
   constexpr int kWaves = kTkThreads / 64;
-  __shared__ float lut[GN][kTkMaxC + 1];
-  __shared__ __align__(16) float stage[kTkStage];
-  __shared__ unsigned cnt[kTkMaxC + 1];  // code histogram; then the class bytes
-  __shared__ unsigned hist[GN][256];
-  __shared__ unsigned s_prefix[GN], s_rem[GN];
-  __shared__ int wcnt[kWaves][2 * GN];   // per wave and query: tokens above, tokens equal
+  constexpr unsigned kNegInfKey = 0x007FFFFFu;  // the order key of -inf
+  extern __shared__ __align__(16) unsigned char tk_smem[];
+  float* lut = reinterpret_cast<float*>(tk_smem + ly.lut);  // [GN][c + 1]
+  unsigned long long* hist =
+      reinterpret_cast<unsigned long long*>(tk_smem + ly.hist);  // [GN][kNbPad]
+  unsigned* cnt = reinterpret_cast<unsigned*>(tk_smem + ly.cnt);  // [c + 1]
+  uint16_t* cl = reinterpret_cast<uint16_t*>(tk_smem + (CLDS ? ly.cl : 0u));
+  __shared__ unsigned rng[GN][2];                 // a live set's key range (atomic min / max)
+  __shared__ unsigned sel[GN][4];                 // a pass's bin, remaining rank, its entries
+  __shared__ unsigned long long cand[GN][kCand];  // (weight << 32) | key of a small bin
+  __shared__ unsigned ccnt[GN], s_tr[GN][2];
+  __shared__ unsigned wsum[2][kWaves][2 * GN];    // per round parity and wave: above, equal
+  const int cp = c + 1;  // table row pitch
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t wg = blockIdx.x;
   const int chunk = (int)(wg % nchunk);
   const int64_t bk = wg / nchunk;  // sequence * hkv + key/value head
@@ -110,90 +292,54 @@ __global__ __launch_bounds__(kTkThreads) void topk_codes_rows(
   const int gv = group - g0 < GN ? group - g0 : GN;  // query heads of this group in use
   const int64_t row0 = b * hq + kvh * group + g0;    // their first output row
 
-  int64_t qoff[GN];  // query rows (a slot past the group's last query repeats it)
-#pragma unroll
-  for (int g = 0; g < GN; ++g) qoff[g] = (row0 + (g < gv ? g : gv - 1)) * kD;
-
-  // ---- 1. score table
-  const float* cbh = cb + kvh * (int64_t)c * kD;
-  // Warp-specialised and double-buffered: the table threads (waves 0-3; thread t owns
-  // centroids 4t .. 4t + 3) work on one tile while the loader threads (waves 8-15) store the
-  // next into the other buffer; each tile is loaded two steps before it is stored.
-  constexpr int kChunks = kD / kTkDims;
-  const bool table_thread = t < kTkTile / kTkR, loader = t >= kTkThreads - kTkLoaders;
-  const int u = t - (kTkThreads - kTkLoaders);
-  for (int cb0 = 0; cb0 < c; cb0 += kTkTile) {
-    float4 pre[2][4];
-    double acc[kTkR][GN];
-#pragma unroll
-    for (int r = 0; r < kTkR; ++r)
-#pragma unroll
-      for (int g = 0; g < GN; ++g) acc[r][g] = 0.0;
-    if (loader) {
-      tk_load_tile(pre[0], cbh, c, cb0, 0, u);
-      tk_load_tile(pre[1], cbh, c, cb0, 1, u);
-    }
-    __syncthreads();  // the previous tile's readers are done with both buffers
-    if (loader) {
-      tk_store_tile(stage, pre[0], u);
-      tk_load_tile(pre[0], cbh, c, cb0, 2, u);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ch = 0; ch < kChunks; ++ch) {
-      if (loader && ch + 1 < kChunks) {
-        tk_store_tile(stage + ((ch + 1) & 1) * kTkDims * kTkPitch, pre[(ch + 1) & 1], u);
-        if (ch + 3 < kChunks) tk_load_tile(pre[(ch + 1) & 1], cbh, c, cb0, ch + 3, u);
-      }
-      if (table_thread) {
-        const float* sb = stage + (ch & 1) * kTkDims * kTkPitch + 4 * t;
-#pragma unroll
-        for (int a = 0; a < kTkDims; ++a) {
-          const float4 xv = *reinterpret_cast<const float4*>(sb + a * kTkPitch);
-          const double x[kTkR] = {(double)xv.x, (double)xv.y, (double)xv.z, (double)xv.w};
-#pragma unroll
-          for (int g = 0; g < GN; ++g) {
-            const double qv = (double)load_elem(qb, QDT, qoff[g] + ch * kTkDims + a);
-#pragma unroll
-            for (int r = 0; r < kTkR; ++r) acc[r][g] = __fma_rn(qv, x[r], acc[r][g]);
-          }
-        }
-      }
-      __syncthreads();
-    }
-    if (table_thread) {
-#pragma unroll
-      for (int r = 0; r < kTkR; ++r) {
-        const int j = cb0 + 4 * t + r;
-        if (j < c)
-#pragma unroll
-          for (int g = 0; g < GN; ++g) lut[g][j] = (float)acc[r][g];
-      }
-    }
-  }
-  if (t < GN) lut[t][c] = -INFINITY;  // the score of every code >= c
-  __syncthreads();
-
-  // ---- 2. code row and its histogram
+  // ---- 1. tables (a slot past the group's last query repeats it) with their key ranges
+  for (int j = t; j < GN * kNbPad; j += kTkThreads) hist[j] = 0ull;
   for (int j = t; j <= c; j += kTkThreads) cnt[j] = 0u;
+  if (t < GN) {
+    rng[t][0] = 0xFFFFFFFFu;
+    rng[t][1] = 0u;
+    ccnt[t] = 0u;
+  }
+  unsigned key[GN][E], klo[GN], khi[GN];
+#pragma unroll
+  for (int g = 0; g < GN; ++g) {
+    const float* src = lut_ws + (row0 + (g < gv ? g : gv - 1)) * c;
+    klo[g] = 0xFFFFFFFFu;
+    khi[g] = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = t + kTkThreads * e;
+      const float v = j < c ? src[j] : 0.0f;
+      key[g][e] = tk_order_key(v);
+      if (j < c) {
+        lut[g * cp + j] = v;
+        klo[g] = min(klo[g], key[g][e]);
+        khi[g] = max(khi[g], key[g][e]);
+      }
+    }
+    if (t == 0) lut[g * cp + c] = -INFINITY;  // the score of every code >= c
+    klo[g] = wave_min(klo[g]);
+    khi[g] = wave_max(khi[g]);
+  }
   __syncthreads();
+  if (lane == 0)
+#pragma unroll
+    for (int g = 0; g < GN; ++g) {
+      atomicMin(&rng[g][0], klo[g]);
+      atomicMax(&rng[g][1], khi[g]);
+    }
   const uint16_t* cg = codes + bk * n;
-  uint16_t* cl = reinterpret_cast<uint16_t*>(stage);
   const unsigned cu = (unsigned)c;
   if (CLDS && (n & 7) == 0) {  // 16-byte rows: eight codes a load
     const uint4* src = reinterpret_cast<const uint4*>(cg);
     uint4* dst = reinterpret_cast<uint4*>(cl);
     const int n8 = (int)(n >> 3);
-    for (int i = t; i < n8; i += 2 * kTkThreads) {
-      const bool two = i + kTkThreads < n8;
-      const uint4 v0 = src[i];
-      const uint4 v1 = two ? src[i + kTkThreads] : make_uint4(0u, 0u, 0u, 0u);
-      dst[i] = v0;
-      if (two) dst[i + kTkThreads] = v1;
-      const unsigned w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    for (int i = t; i < n8; i += kTkThreads) {
+      const uint4 v = src[i];
+      dst[i] = v;
+      const unsigned w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (q >= 4 && !two) break;
+      for (int q = 0; q < 4; ++q) {
         const unsigned lo = w[q] & 0xFFFFu, hi = w[q] >> 16;
         atomicAdd(&cnt[lo < cu ? lo : cu], 1u);
         atomicAdd(&cnt[hi < cu ? hi : cu], 1u);
@@ -208,211 +354,306 @@ __global__ __launch_bounds__(kTkThreads) void topk_codes_rows(
   }
   __syncthreads();
 
-  // ---- 3. weighted radix select over the table entries, every query at once
-  const unsigned neg_inf_key = tk_order_key(-INFINITY);
-  unsigned ek[GN][kTkEnt], ec[kTkEnt];
+  // ---- 2. select.  The live set of a query is the weighted entries with keys in [plo, phi]:
+  // a bin of a monotone map holds a key interval.
+  unsigned wgt[E];
 #pragma unroll
-  for (int e = 0; e < kTkEnt; ++e) {
+  for (int e = 0; e < E; ++e) {
     const int j = t + kTkThreads * e;
-    ec[e] = j <= c ? cnt[j] : 0u;
-#pragma unroll
-    for (int g = 0; g < GN; ++g) ek[g][e] = j < c ? tk_order_key(lut[g][j]) : neg_inf_key;
+    wgt[e] = j < c ? cnt[j] : 0u;
   }
-  if (t < GN) s_rem[t] = (unsigned)k;
-  unsigned prefix[GN], mask = 0u;
+  const unsigned wneg = t == 0 ? cnt[c] : 0u;  // the -inf entry's weight, held by thread 0
+  unsigned act = (1u << gv) - 1u;  // queries still selecting (uniform)
+  unsigned plo[GN], phi[GN], rem[GN], bsel[GN], T[GN], R[GN];
+  TkBins mp[GN];
+  {
+    const bool inv = cnt[c] != 0u;  // a code >= c occurs: -inf is a weighted score
 #pragma unroll
-  for (int g = 0; g < GN; ++g) prefix[g] = 0u;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = t; i < GN * 256; i += kTkThreads) (&hist[0][0])[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < kTkEnt; ++e) {
-      if (ec[e] == 0u) continue;
-#pragma unroll
-      for (int g = 0; g < GN; ++g)
-        if ((ek[g][e] & mask) == prefix[g]) atomicAdd(&hist[g][(ek[g][e] >> shift) & 0xFFu], ec[e]);
+    for (int g = 0; g < GN; ++g) {
+      plo[g] = inv ? kNegInfKey : rng[g][0];
+      phi[g] = rng[g][1];
+      rem[g] = (unsigned)k;
+      bsel[g] = 0u;
+      T[g] = R[g] = 0u;
     }
-    __syncthreads();
-    if (wave < GN) {  // wave g: the digit holding query g's remaining rank
-      const int g = wave;
-      unsigned h[4], sum = 0u;
+  }
+  for (int pass = 0; act != 0u; ++pass) {
+    if (pass > 0) {  // the range of what the last pass kept
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {  // lane l: digits 255 - 4l .. 252 - 4l (descending)
-        h[q] = hist[g][255 - 4 * lane - q];
-        sum += h[q];
-      }
-      unsigned incl = sum;
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned u = __shfl_up(incl, o);
-        if (lane >= o) incl += u;
-      }
-      unsigned cum = incl - sum;
-      const unsigned rem = s_rem[g];
+      for (int g = 0; g < GN; ++g) {
+        if (!((act >> g) & 1u)) continue;
+        unsigned lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (cum < rem && cum + h[q] >= rem) {
-          s_rem[g] = rem - cum;
-          s_prefix[g] = prefix[g] | ((unsigned)(255 - 4 * lane - q) << shift);
+        for (int e = 0; e <= E; ++e) {
+          const unsigned x = e < E ? key[g][e] : kNegInfKey, w = e < E ? wgt[e] : wneg;
+          if (w != 0u && x >= plo[g] && x <= phi[g] && mp[g](x) == bsel[g]) {
+            lo = min(lo, x);
+            hi = max(hi, x);
+          }
         }
-        cum += h[q];
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        if (lane == 0) {
+          atomicMin(&rng[g][0], lo);
+          atomicMax(&rng[g][1], hi);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int g = 0; g < GN; ++g) {
+        if (!((act >> g) & 1u)) continue;
+        plo[g] = rng[g][0];
+        phi[g] = rng[g][1];
+      }
+    }
+    // one score left is T_g; else the weighted histogram of the live entries over the bins
+#pragma unroll
+    for (int g = 0; g < GN; ++g) {
+      if (!((act >> g) & 1u)) continue;
+      if (plo[g] == phi[g]) {
+        T[g] = plo[g];
+        R[g] = rem[g];
+        act &= ~(1u << g);
+        continue;
+      }
+      mp[g] = tk_bin_map(plo[g], phi[g], pass);
+#pragma unroll
+      for (int e = 0; e <= E; ++e) {
+        const unsigned x = e < E ? key[g][e] : kNegInfKey, w = e < E ? wgt[e] : wneg;
+        if (w != 0u && x >= plo[g] && x <= phi[g])
+          atomicAdd(&hist[g * kNbPad + tk_hslot(mp[g](x))], (1ull << 32) | (unsigned long long)w);
+      }
+    }
+    if (act == 0u) break;  // uniform
+    __syncthreads();
+    // wave g: the bin holding rank rem_g from the top.  Lane l holds bins 1023 - 16 l down to
+    // 1008 - 16 l, and clears them for the next pass.
+    if (wave < GN && ((act >> wave) & 1u)) {
+      const int g = wave;
+      unsigned long long* hg = hist + g * kNbPad + tk_hslot(kNb - 16 - 16 * lane);
+      unsigned long long h[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) h[q] = hg[15 - q];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) hg[q] = 0ull;
+      unsigned sum = 0u;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) sum += (unsigned)h[q];
+      unsigned r = 0u;
+#pragma unroll
+      for (int q = 0; q < GN; ++q)
+        if (q == g) r = rem[q];
+      unsigned cum = wave_incl_sum(sum) - sum;
+      int hit = -1;
+      unsigned nrem = 0u, ne = 0u;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const unsigned w = (unsigned)h[q];
+        if (hit < 0 && cum < r && cum + w >= r) {
+          hit = kNb - 1 - 16 * lane - q;
+          nrem = r - cum;
+          ne = (unsigned)(h[q] >> 32);
+        }
+        cum += w;
+      }
+      // one lane holds the bin (the live weights add up to at least rem_g >= 1)
+      if (hit >= 0) {
+        sel[g][0] = (unsigned)hit;
+        sel[g][1] = nrem;
+        sel[g][2] = ne;
+      }
+      if (lane == 0) {  // the next pass's range reduction starts empty
+        rng[g][0] = 0xFFFFFFFFu;
+        rng[g][1] = 0u;
+      }
+    }
+    __syncthreads();
+    unsigned settle = 0u;
+#pragma unroll
+    for (int g = 0; g < GN; ++g) {
+      if (!((act >> g) & 1u)) continue;
+      bsel[g] = sel[g][0];
+      rem[g] = sel[g][1];
+      if (!mp[g].lin && mp[g].sh == 0u) {  // the bin is one key
+        T[g] = mp[g].kmin + bsel[g];
+        R[g] = rem[g];
+        act &= ~(1u << g);
+      } else if (sel[g][2] <= (unsigned)kCand) {
+#pragma unroll
+        for (int e = 0; e <= E; ++e) {
+          const unsigned x = e < E ? key[g][e] : kNegInfKey, w = e < E ? wgt[e] : wneg;
+          if (w != 0u && x >= plo[g] && x <= phi[g] && mp[g](x) == bsel[g])
+            cand[g][atomicAdd(&ccnt[g], 1u)] = ((unsigned long long)w << 32) | (unsigned long long)x;
+        }
+        settle |= 1u << g;
+      }
+    }
+    if (settle == 0u) continue;  // uniform
+    __syncthreads();
+    // wave g settles a small bin: the key with less than rem_g weight above it and at least
+    // rem_g at or above it
+    if (wave < GN && ((settle >> wave) & 1u)) {
+      const int g = wave;
+      unsigned r = 0u;
+#pragma unroll
+      for (int q = 0; q < GN; ++q)
+        if (q == g) r = rem[q];
+      const unsigned m = ccnt[g];
+      const unsigned long long me = lane < (int)m ? cand[g][lane] : 0ull;
+      const unsigned mk = (unsigned)me;
+      unsigned above = 0u, eq = 0u;
+      for (unsigned j = 0; j < m; ++j) {
+        const unsigned long long o = cand[g][j];
+        const unsigned ok = (unsigned)o, ow = (unsigned)(o >> 32);
+        above += ok > mk ? ow : 0u;
+        eq += ok == mk ? ow : 0u;
+      }
+      if (lane < (int)m && above < r && r <= above + eq) {  // equal keys write equal values
+        s_tr[g][0] = mk;
+        s_tr[g][1] = r - above;
       }
     }
     __syncthreads();
 #pragma unroll
-    for (int g = 0; g < GN; ++g) prefix[g] = s_prefix[g];
-    mask |= 0xFFu << shift;
+    for (int g = 0; g < GN; ++g)
+      if ((settle >> g) & 1u) {
+        T[g] = s_tr[g][0];
+        R[g] = s_tr[g][1];
+      }
+    act &= ~settle;
   }
-  // prefix[g] is now T_g, the K-th largest score key; s_rem[g] of the tokens at T_g are taken
 
-  // class byte per code (the histogram is no longer needed)
+  // ---- 3. class byte per code (the code histogram is no longer needed)
   uint8_t* cls = reinterpret_cast<uint8_t*>(cnt);
+  __syncthreads();  // every thread has read the code histogram
   for (int j = t; j <= c; j += kTkThreads) {
     unsigned v = 0u;
 #pragma unroll
     for (int g = 0; g < GN; ++g) {
-      const unsigned u = j < c ? tk_order_key(lut[g][j]) : neg_inf_key;
-      v |= (u > prefix[g] ? 1u : 0u) << (2 * g);
-      v |= (u == prefix[g] ? 1u : 0u) << (2 * g + 1);
+      const unsigned u = tk_order_key(lut[g * cp + j]);
+      v |= (u > T[g] ? 1u : 0u) << (2 * g);
+      v |= (u == T[g] ? 1u : 0u) << (2 * g + 1);
     }
     cls[j] = (uint8_t)v;
   }
   __syncthreads();
 
-  // ---- 4. ordered compaction: wave ranges of whole 256-token steps; in a step, slot e of
-  // lane l is token base + 64 e + l, so a ballot per slot orders the wave's tokens
-  const int64_t per = ((n + kWaves - 1) / kWaves + 255) / 256 * 256;
-  const int64_t w0 = (int64_t)wave * per < n ? (int64_t)wave * per : n;
-  const int64_t w1 = w0 + per < n ? w0 + per : n;
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  // codes (clamped to c) and class bytes of the lane's four tokens; class 0 past the range
-  auto step = [&](int64_t base, unsigned (&cc)[4], unsigned (&v)[4]) {
+  // ---- 4. output
+  unsigned run_a[GN], run_e[GN];  // tokens above / at T_g in the rounds before
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t i = base + 64 * e + lane;
-      const unsigned code = i < w1 ? (CLDS ? (unsigned)cl[i] : (unsigned)cg[i]) : cu;
-      cc[e] = code < cu ? code : cu;
-      v[e] = i < w1 ? (unsigned)cls[cc[e]] : 0u;
-    }
+  for (int g = 0; g < GN; ++g) run_a[g] = run_e[g] = 0u;
+  auto token_code = [&](int64_t i) -> unsigned {
+    const unsigned x = i < n ? (CLDS ? (unsigned)cl[i] : (unsigned)cg[i]) : cu;
+    return x < cu ? x : cu;
   };
-  {
-    int na[GN], ne[GN];
+  for (int64_t r0 = 0, par = 0; r0 < n; r0 += kTkRound, par ^= 1) {
+    const int64_t wb = r0 + (int64_t)wave * (kTkRound / kWaves);
+    unsigned ca[GN], ce[GN];
 #pragma unroll
-    for (int g = 0; g < GN; ++g) na[g] = ne[g] = 0;
-    for (int64_t base = w0; base < w1; base += 256) {
-      unsigned cc[4], v[4];
-      step(base, cc, v);
-      const unsigned x = v[0] | (v[1] << 8) | (v[2] << 16) | (v[3] << 24);
+    for (int g = 0; g < GN; ++g) ca[g] = ce[g] = 0u;
+#pragma unroll 4
+    for (int q = 0; q < 16; ++q) {
+      const int64_t i = wb + 64 * q + lane;
+      const unsigned v = i < n ? (unsigned)cls[token_code(i)] : 0u;
 #pragma unroll
       for (int g = 0; g < GN; ++g) {
-        na[g] += __popc(x & (0x01010101u << (2 * g)));
-        ne[g] += __popc(x & (0x02020202u << (2 * g)));
+        ca[g] += (unsigned)__popcll(tk_ballot((v >> (2 * g)) & 1u));
+        ce[g] += (unsigned)__popcll(tk_ballot((v >> (2 * g + 1)) & 1u));
       }
     }
+    if (lane == 0)
+#pragma unroll
+      for (int g = 0; g < GN; ++g) {
+        wsum[par][wave][2 * g] = ca[g];
+        wsum[par][wave][2 * g + 1] = ce[g];
+      }
+    __syncthreads();  // wsum[par] is rewritten two rounds on, after the next round's barrier
+    unsigned pa[GN], pe[GN];  // taken tokens / tokens at T_g before the next of this wave's
 #pragma unroll
     for (int g = 0; g < GN; ++g) {
-      const int a = tk_wave_sum(na[g]), e = tk_wave_sum(ne[g]);
-      if (lane == 0) {
-        wcnt[wave][2 * g] = a;
-        wcnt[wave][2 * g + 1] = e;
-      }
+      const unsigned xa = lane < kWaves ? wsum[par][lane][2 * g] : 0u;
+      const unsigned xe = lane < kWaves ? wsum[par][lane][2 * g + 1] : 0u;
+      const unsigned ia = row_incl_sum(xa), ie = row_incl_sum(xe);
+      pa[g] = run_a[g] + rdlane(ia, wave) - rdlane(xa, wave);
+      pe[g] = run_e[g] + rdlane(ie, wave) - rdlane(xe, wave);
+      run_a[g] += rdlane(ia, kWaves - 1);
+      run_e[g] += rdlane(ie, kWaves - 1);
+      pa[g] += min(pe[g], R[g]);  // the tokens at T_g taken before this wave's
     }
-  }
-  __syncthreads();
-
-  // per query: this wave's first output slot and its share of the tokens at T_g
-  int out[GN], eq_take[GN], eq_seen[GN];
+    // every token above T_g is taken, and of those at T_g the first R_g
+#pragma unroll 2
+    for (int q = 0; q < 16; ++q) {
+      const int64_t i = wb + 64 * q + lane;
+      const unsigned code = token_code(i);
+      const unsigned v = i < n ? (unsigned)cls[code] : 0u;
 #pragma unroll
-  for (int g = 0; g < GN; ++g) {
-    const int r_eq = (int)s_rem[g];
-    int o = 0, eq_before = 0;
-    for (int w = 0; w < wave; ++w) {
-      const int e = wcnt[w][2 * g + 1];
-      int take = r_eq - eq_before;
-      take = take < 0 ? 0 : (take > e ? e : take);
-      o += wcnt[w][2 * g] + take;
-      eq_before += e;
-    }
-    const int mine = wcnt[wave][2 * g + 1];
-    const int et = r_eq - eq_before;
-    out[g] = o;
-    eq_take[g] = et < 0 ? 0 : (et > mine ? mine : et);
-    eq_seen[g] = 0;
-  }
-  auto below = [](unsigned long long m) {  // set bits of m in the lanes below this one
-    return (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
-                                          __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
-  };
-  const unsigned ku = (unsigned)k;
-  for (int64_t base = w0; base < w1; base += 256) {
-    unsigned cc[4], v[4];
-    step(base, cc, v);
-    const unsigned vor = v[0] | v[1] | v[2] | v[3];
-#pragma unroll
-    for (int g = 0; g < GN; ++g) {
-      if (g >= gv) break;
-      bool take[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) take[e] = (v[e] >> (2 * g)) & 1u;
-      if (__ballot((vor >> (2 * g + 1)) & 1u)) {  // tokens at T_g: the first eq_take of the range
-        int seen = eq_seen[g];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool eq = (v[e] >> (2 * g + 1)) & 1u;
-          const unsigned long long m = __ballot(eq);
-          take[e] = take[e] || (eq && seen + below(m) < eq_take[g]);
-          seen += __popcll(m);
+      for (int g = 0; g < GN; ++g) {
+        if (g >= gv) break;
+        bool take = (v >> (2 * g)) & 1u;
+        const bool at = (v >> (2 * g + 1)) & 1u;
+        const unsigned long long em = tk_ballot(at);
+        if (em != 0ull) {  // uniform
+          take = take || (at && lanes_below(em, pe[g]) < R[g]);
+          pe[g] += (unsigned)__popcll(em);
         }
-        eq_seen[g] = seen;
-      }
-      int32_t* orow = idx + (row0 + g) * k;
-      float* srow = score ? score + (row0 + g) * k : nullptr;
-      float sv[4];  // read ahead: one LDS wait for the four stores
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sv[e] = lut[g][cc[e]];
-      int o = out[g];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const unsigned long long m = __ballot(take[e]);
-        const unsigned pos = (unsigned)(o + below(m));
-        if (take[e] && pos < ku) {  // the bound turns any inconsistency into a wrong answer
-          orow[pos] = (int32_t)(base + 64 * e + lane);
-          if (srow) srow[pos] = sv[e];
+        const unsigned long long tm = tk_ballot(take);
+        const unsigned pos = lanes_below(tm, pa[g]);
+        if (take && pos < (unsigned)k) {  // the bound turns any inconsistency into a wrong answer
+          idx[(row0 + g) * k + pos] = (int32_t)i;
+          if (score) score[(row0 + g) * k + pos] = lut[g * cp + code];
         }
-        o += __popcll(m);
+        pa[g] += (unsigned)__popcll(tm);
       }
-      out[g] = o;
     }
   }
 }
 
-template <int QDT, int GN>
-int topk_launch(bool clds, dim3 grid, hipStream_t s, const void* qb, int64_t hq, int64_t hkv,
-                int group, int nchunk, const uint16_t* codes, int64_t n, const float* cb, int c,
-                int64_t k, int32_t* idx, float* score) {
-  if (clds)
-    return launch("topk_codes", topk_codes_rows<QDT, GN, true>, grid, dim3(kTkThreads), 0, s, qb,
-                  hq, hkv, group, nchunk, codes, n, cb, c, k, idx, score);
-  return launch("topk_codes", topk_codes_rows<QDT, GN, false>, grid, dim3(kTkThreads), 0, s, qb,
-                hq, hkv, group, nchunk, codes, n, cb, c, k, idx, score);
+template <int GN, int E, bool CLDS>
+int topk_launch3(dim3 grid, hipStream_t s, const float* lut, int64_t hq, int64_t hkv, int group,
+                 int nchunk, const uint16_t* codes, int64_t n, int c, int64_t k, int32_t* idx,
+                 float* score, const TkLayout& ly) {
+  auto kern = topk_codes_rows<GN, E, CLDS>;
+  A2ATS_TRY(set_dynamic_lds(kern, ly.total));
+  return launch("topk_codes", kern, grid, dim3(kTkThreads), ly.total, s, lut, hq, hkv, group,
+                nchunk, codes, n, c, k, idx, score, ly);
 }
 
-template <int QDT>
-int topk_dispatch(int gn, bool clds, dim3 grid, hipStream_t s, const void* qb, int64_t hq,
-                  int64_t hkv, int group, int nchunk, const uint16_t* codes, int64_t n,
-                  const float* cb, int c, int64_t k, int32_t* idx, float* score) {
+template <int GN, int E>
+int topk_launch2(dim3 grid, hipStream_t s, const float* lut, int64_t hq, int64_t hkv, int group,
+                 int nchunk, const uint16_t* codes, int64_t n, int c, int64_t k, int32_t* idx,
+                 float* score) {
+  const TkLayout ly = tk_layout(GN, c, n);
+  if (ly.cl != 0xFFFFFFFFu)
+    return topk_launch3<GN, E, true>(grid, s, lut, hq, hkv, group, nchunk, codes, n, c, k, idx,
+                                     score, ly);
+  return topk_launch3<GN, E, false>(grid, s, lut, hq, hkv, group, nchunk, codes, n, c, k, idx,
+                                    score, ly);
+}
+
+// table entries a thread holds: C <= 1024, 2048, 4096
+template <int GN>
+int topk_launch(dim3 grid, hipStream_t s, const float* lut, int64_t hq, int64_t hkv, int group,
+                int nchunk, const uint16_t* codes, int64_t n, int c, int64_t k, int32_t* idx,
+                float* score) {
+  if (c <= kTkThreads)
+    return topk_launch2<GN, 1>(grid, s, lut, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
+  if (c <= 2 * kTkThreads)
+    return topk_launch2<GN, 2>(grid, s, lut, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
+  return topk_launch2<GN, 4>(grid, s, lut, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
+}
+
+int topk_dispatch(int gn, dim3 grid, hipStream_t s, const float* lut, int64_t hq, int64_t hkv,
+                  int group, int nchunk, const uint16_t* codes, int64_t n, int c, int64_t k,
+                  int32_t* idx, float* score) {
   switch (gn) {
     case 1:
-      return topk_launch<QDT, 1>(clds, grid, s, qb, hq, hkv, group, nchunk, codes, n, cb, c, k,
-                                 idx, score);
+      return topk_launch<1>(grid, s, lut, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
     case 2:
-      return topk_launch<QDT, 2>(clds, grid, s, qb, hq, hkv, group, nchunk, codes, n, cb, c, k,
-                                 idx, score);
+      return topk_launch<2>(grid, s, lut, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
     case 3:
-      return topk_launch<QDT, 3>(clds, grid, s, qb, hq, hkv, group, nchunk, codes, n, cb, c, k,
-                                 idx, score);
+      return topk_launch<3>(grid, s, lut, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
     default:
-      return topk_launch<QDT, 4>(clds, grid, s, qb, hq, hkv, group, nchunk, codes, n, cb, c, k,
-                                 idx, score);
+      return topk_launch<4>(grid, s, lut, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
   }
 }
 
@@ -421,10 +662,16 @@ int topk_dispatch(int gn, bool clds, dim3 grid, hipStream_t s, const void* qb, i
 
 using namespace a2ats;
 
+extern "C" size_t a2ats_topk_workspace(int64_t batch, int64_t hq, int64_t c) {
+  if (batch < 1 || hq < 1 || c < 1 || c > kTkMaxC) return 0;
+  return align_up((size_t)(batch * hq * c) * sizeof(float));
+}
+
 extern "C" int a2ats_topk_codes(const void* qb, int q_dtype, int64_t batch, int64_t hq,
                                 int64_t hkv, int64_t d, const uint16_t* codes, int64_t n,
                                 const float* codebook, int64_t c, int64_t k, int32_t* idx,
-                                float* score, void* stream) {
+                                float* score, void* workspace, size_t workspace_bytes,
+                                void* stream) {
   if (q_dtype != A2ATS_F32 && q_dtype != A2ATS_BF16) return A2ATS_EDTYPE;
   if (d != kD || batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0) return A2ATS_EINVAL;
   if (n < 0 || n > 0x7FFFFFFF || c < 1 || c > kTkMaxC || k < 0 || k > n) return A2ATS_EINVAL;
@@ -432,14 +679,27 @@ extern "C" int a2ats_topk_codes(const void* qb, int q_dtype, int64_t batch, int6
   const int gn = group < 4 ? group : 4;
   const int nchunk = (group + gn - 1) / gn;
   if (batch * hkv * nchunk > 0x7FFFFFFF) return A2ATS_EINVAL;
+  if (batch * hq > 0x7FFFFFFF) return A2ATS_EINVAL;
+  const int nqh = (int)(batch * group);  // queries of one key/value head
+  const int nqb = (nqh + kTbWaves * kTbQg - 1) / (kTbWaves * kTbQg);
+  const int nct = (int)((c + kTbCent - 1) / kTbCent);
+  const int64_t table_wgs = hkv * nqb * nct;
+  if (table_wgs > 0x7FFFFFFF) return A2ATS_EINVAL;
   if (n == 0 || k == 0) return A2ATS_OK;
   if (!qb || !codes || !codebook || !idx) return A2ATS_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(codebook) & 15) != 0) return A2ATS_EINVAL;
+  if (!ws_ok(workspace, workspace_bytes, a2ats_topk_workspace(batch, hq, c)))
+    return A2ATS_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)(batch * hkv * nchunk));
-  const bool clds = n <= kTkLdsCodes;
+  float* lut = static_cast<float*>(workspace);
   if (q_dtype == A2ATS_F32)
-    return topk_dispatch<A2ATS_F32>(gn, clds, grid, s, qb, hq, hkv, group, nchunk, codes, n,
-                                    codebook, (int)c, k, idx, score);
-  return topk_dispatch<A2ATS_BF16>(gn, clds, grid, s, qb, hq, hkv, group, nchunk, codes, n,
-                                   codebook, (int)c, k, idx, score);
+    A2ATS_TRY(launch("topk_table", topk_table<A2ATS_F32>, dim3((unsigned)table_wgs),
+                     dim3(kTbWaves * 64), 0, s, qb, (int)hq, group, nqh, nqb, nct, codebook,
+                     (int)c, lut));
+  else
+    A2ATS_TRY(launch("topk_table", topk_table<A2ATS_BF16>, dim3((unsigned)table_wgs),
+                     dim3(kTbWaves * 64), 0, s, qb, (int)hq, group, nqh, nqb, nct, codebook,
+                     (int)c, lut));
+  const dim3 grid((unsigned)(batch * hkv * nchunk));
+  return topk_dispatch(gn, grid, s, lut, hq, hkv, group, nchunk, codes, n, (int)c, k, idx, score);
 }

@@ -354,9 +354,14 @@ def test_kmeans_init_validation(L):
 
 
 def test_topk_codes_validation(L):
-    def call(qdt=0, batch=2, hq=6, hkv=2, d=128, n=64, c=16, k=8, qb=FAKE, idx=FAKE):
-        return L.a2ats_topk_codes(qb, qdt, batch, hq, hkv, d, FAKE, n, FAKE, c, k, idx, None,
-                                  None)
+    need = L.a2ats_topk_workspace(2, 6, 16)
+    assert need >= 2 * 6 * 16 * 4 and need % 256 == 0
+    assert L.a2ats_topk_workspace(0, 6, 16) == 0 and L.a2ats_topk_workspace(2, 6, 4097) == 0
+
+    def call(qdt=0, batch=2, hq=6, hkv=2, d=128, n=64, c=16, k=8, qb=FAKE, idx=FAKE, ws=FAKE,
+             wsb=None, cb=FAKE):
+        return L.a2ats_topk_codes(qb, qdt, batch, hq, hkv, d, FAKE, n, cb, c, k, idx, None,
+                                  ws, need if wsb is None else wsb, None)
 
     assert call(qdt=2) == EDTYPE
     assert call(d=64) == EINVAL
@@ -368,6 +373,11 @@ def test_topk_codes_validation(L):
     assert call(k=-1) == EINVAL
     assert call(qb=None) == EINVAL
     assert call(idx=None) == EINVAL
+    assert call(cb=None) == EINVAL
+    assert call(cb=ctypes.c_void_p(4100)) == EINVAL  # codebook not 16-byte aligned
+    assert call(batch=1 << 28, hq=8) == EINVAL       # batch * hq >= 2^31
+    assert call(ws=None) == EWORKSPACE
+    assert call(wsb=need - 1) == EWORKSPACE
     assert call(k=0) == 0                # nothing to select: no launch
     assert call(n=0, k=0) == 0
 
