@@ -422,19 +422,17 @@ int a2ats_kmeans(const void* x, int x_dtype, int64_t heads, int64_t n, int64_t d
  *   score_t   = lut[codes[b, kvh, t]], or -inf for a code >= c
  *   idx[b, h] = the k tokens with the largest scores (equal scores: lower index first; -0 and
  *               +0 are equal), in ascending index order; score[b, h] (optional) their scores
- *   qb        [batch, hq, d] fp32 or bf16 (q_dtype): the query already rotated by R_b
- *               (a2ats_far_query_rope)
- *   codes     [batch, hkv, n] uint16; codebook [hkv, c, d] fp32 (16-byte aligned),
- *               1 <= c <= 4096, d = 128
+ *   qb        [batch, hq, d] fp32 or bf16 (q_dtype), 16-byte aligned: the query already
+ *               rotated by R_b (a2ats_far_query_rope)
+ *   codes     [batch, hkv, n] uint16; codebook [hkv, c, d] fp32, 1 <= c <= 4096, d = 128
  *   idx       [batch, hq, k] int32; score [batch, hq, k] fp32 or NULL; 0 <= k <= n
  * hq must be a multiple of hkv and batch * hq < 2^31.  Nothing is written when n or k is 0.
- * Two launches: every query's table into the workspace (a codebook tile staged once for 16
- * queries of its head), then the selection, one workgroup reading a code row once for up to
- * four query heads of a group: the K-th largest score by passes of monotone 1024-bin
- * histograms over the C + 1 table entries weighted by their token counts, then the output by
- * wave ballots in token order.  Workspace: a2ats_topk_workspace(batch, hq, c) bytes (the
- * tables; 256-byte aligned), A2ATS_EWORKSPACE when missing or short.  A2ATS_EINVAL for a
- * misaligned codebook.  Returns without waiting.
+ * Two launches: the queries in fp64 and the codebook transposed into the workspace, then one
+ * workgroup per code row and up to four query heads of a group: their tables in LDS, the
+ * K-th largest score by passes of monotone 1024-bin histograms over the C + 1 table entries
+ * weighted by their token counts, then the taken tokens in token order.  Workspace:
+ * a2ats_topk_workspace(batch, hq, c) bytes (256-byte aligned), A2ATS_EWORKSPACE when missing
+ * or short; A2ATS_EINVAL for misaligned queries.  Returns without waiting.
  */
 size_t a2ats_topk_workspace(int64_t batch, int64_t hq, int64_t c);
 int a2ats_topk_codes(const void* qb, int q_dtype, int64_t batch, int64_t hq, int64_t hkv,

@@ -5,15 +5,15 @@
 // (q R_b) . c_{code_t}: one table of C values per query, gathered by code.
 //
 // Two kernels (their own comments say more):
-//   topk_table       every query's table, lut_gj = fp32(sum_a qb_ga * c_ja) with the sum taken
-//                    in fp64 in dimension order and rounded to fp32 once.  Both factors have at
-//                    most 24 significant bits, so each fp64 product is exact and fma(q, c, acc)
-//                    equals acc + q*c rounded once: the fma loop is the plain product-then-add
-//                    sum.  Each codebook tile is staged once for 16 queries of its head.
-//   topk_codes_rows  per (sequence, key/value head, up to four query heads): the histogram of
-//                    the code row, the K-th largest score by monotone-bin histogram passes over
-//                    the C + 1 weighted table entries (not over the n tokens), and the ordered
-//                    output by wave ballots.
+//   topk_prep        the queries in fp64 and the codebook transposed, into the workspace.
+//   topk_codes_rows  per (sequence, key/value head, up to four query heads): the queries'
+//                    tables in LDS, lut_gj = fp32(sum_a qb_ga * c_ja) with the sum taken in fp64
+//                    in dimension order and rounded to fp32 once (both factors have at most 24
+//                    significant bits, so each fp64 product is exact and fma(q, c, acc) equals
+//                    acc + q*c rounded once: the fma loop is the plain product-then-add sum),
+//                    the histogram of the code row, the K-th largest score by monotone-bin
+//                    histogram passes over the C + 1 weighted table entries (not over the n
+//                    tokens), and the taken tokens in token order.
 // Scores compare through the order-preserving map of fp32 onto u32 (-0 and +0 equal); a code
 // >= C scores -inf.
 #include "common.hpp"
@@ -32,135 +32,111 @@ __device__ __forceinline__ unsigned tk_order_key(float s) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Kernel topk_table: every query's score table, lut[b * hq + h, j] = fp32(sum_a q[b, h, a] *
-// c[kvh, j, a]), the fp64 products added in dimension order and rounded to fp32 once.  A
-// 256-thread workgroup takes one key/value head, a tile of 64 centroids (fp32 rows in LDS, one
-// a lane) and four groups of 4 of that head's queries (all sequences and query heads of the
-// group, converted to fp64 into LDS once), one group a wave; each centroid value a lane
-// converts serves the wave's 4 queries, read as broadcasts.  Workgroups sharing a codebook tile
-// are numbered so that they land on one XCD (launch order deals workgroups to the 8 XCDs in
-// turn).
-constexpr int kTbQg = 4;       // queries a wave
-constexpr int kTbWaves = 4;    // waves (query groups) a workgroup
-constexpr int kTbCent = 64;    // centroids a workgroup (one a lane)
-
+// Kernel topk_prep, two jobs in one launch, both into the workspace:
+//   workgroups [0, nqw): the queries in fp64 (exact), same layout, four elements a thread, so
+//     that the selection kernel reads them with scalar loads;
+//   the rest: the codebook transposed to [kvh][a][j] through 64 x 64 LDS tiles, so that a
+//     wave reading dimension a of 64 consecutive centroids reads 256 contiguous bytes.
 template <int QDT>
-__global__ __launch_bounds__(kTbWaves * 64) void topk_table(const void* __restrict__ qb, int hq,
-                                                            int group, int nqh, int nqb, int nct,
-                                                            const float* __restrict__ cb, int c,
-                                                            float* __restrict__ lut) {
-  constexpr int kPitch = kD + 1;  // floats: lane j reads row j, so a column read is conflict-free
-  __shared__ float ct[kTbCent * kPitch];
-  __shared__ __align__(16) double qt[kTbWaves][kD][kTbQg];  // [wave][a][v]
-  const int t = threadIdx.x, lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int ntiles = (int)gridDim.x;
-  int tile = (int)blockIdx.x;
-  if ((ntiles & 7) == 0) tile = (tile & 7) * (ntiles >> 3) + (tile >> 3);
-  const int qblk = tile % nqb;
-  const int ctile = (tile / nqb) % nct;
-  const int kvh = tile / (nqb * nct);
-  const float* cbh = cb + ((int64_t)kvh * c + (int64_t)ctile * kTbCent) * kD;
-  const int rows = c - ctile * kTbCent < kTbCent ? c - ctile * kTbCent : kTbCent;
-#pragma unroll
-  for (int i = 0; i < kTbCent * kD / 4 / (kTbWaves * 64); ++i) {  // the codebook tile
-    const int f = t + kTbWaves * 64 * i, jr = f >> 5, a4 = (f & 31) * 4;
-    const float4 v = jr < rows ? *reinterpret_cast<const float4*>(cbh + (int64_t)jr * kD + a4)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
-    float* d = &ct[jr * kPitch + a4];
-    d[0] = v.x;
-    d[1] = v.y;
-    d[2] = v.z;
-    d[3] = v.w;
-  }
-  {  // the queries: thread t converts 32 dimensions of query t / 16 of the block (0 past the end)
-    const int qq = t >> 4, a0 = (t & 15) * 8, r = qblk * kTbWaves * kTbQg + qq;
-    double* dst = &qt[qq / kTbQg][0][qq % kTbQg];
-    if (r < nqh) {
-      const int64_t row = (int64_t)(r / group) * hq + (int64_t)kvh * group + r % group;
-#pragma unroll
-      for (int a = 0; a < 8; ++a) dst[(a0 + a) * kTbQg] = (double)load_elem(qb, QDT, row * kD + a0 + a);
+__global__ __launch_bounds__(256) void topk_prep(const void* __restrict__ qb, int64_t quads,
+                                                 int nqw, const float* __restrict__ cb, int c,
+                                                 int njt, double* __restrict__ q64,
+                                                 float* __restrict__ cbt) {
+  __shared__ float tile[64][65];
+  const int t = threadIdx.x;
+  if ((int)blockIdx.x < nqw) {
+    const int64_t f = (int64_t)blockIdx.x * 256 + t;
+    if (f >= quads) return;
+    float v[4];
+    if (QDT == A2ATS_F32) {
+      const float4 x = reinterpret_cast<const float4*>(qb)[f];
+      v[0] = x.x;
+      v[1] = x.y;
+      v[2] = x.z;
+      v[3] = x.w;
     } else {
-#pragma unroll
-      for (int a = 0; a < 8; ++a) dst[(a0 + a) * kTbQg] = 0.0;
+      const uint2 x = reinterpret_cast<const uint2*>(qb)[f];
+      v[0] = __uint_as_float(x.x << 16);
+      v[1] = __uint_as_float(x.x & 0xFFFF0000u);
+      v[2] = __uint_as_float(x.y << 16);
+      v[3] = __uint_as_float(x.y & 0xFFFF0000u);
     }
+    double2* dst = reinterpret_cast<double2*>(q64) + 2 * f;
+    dst[0] = make_double2((double)v[0], (double)v[1]);
+    dst[1] = make_double2((double)v[2], (double)v[3]);
+    return;
+  }
+  const int w = (int)blockIdx.x - nqw;  // (kvh, j tile, a half)
+  const int ah = w & 1, jt = (w >> 1) % njt, kvh = (w >> 1) / njt;
+  const int j0 = jt * 64, a0 = ah * 64;
+  const float* src = cb + ((int64_t)kvh * c + j0) * kD + a0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {  // rows j0 .. j0 + 63, dimensions a0 .. a0 + 63
+    const int r = (t >> 6) + 4 * i, a = t & 63;
+    tile[r][a] = j0 + r < c ? src[(int64_t)r * kD + a] : 0.0f;
   }
   __syncthreads();
-  const int qg = qblk * kTbWaves + wave;
-  if (kTbQg * qg >= nqh) return;  // the whole wave; no barriers follow
-  const float* crow = &ct[lane * kPitch];
-  const double* qs = &qt[wave][0][0];
-  double acc[kTbQg];
+  float* dst = cbt + ((int64_t)kvh * kD + a0) * c + j0;
 #pragma unroll
-  for (int v = 0; v < kTbQg; ++v) acc[v] = 0.0;
-#pragma unroll 4
-  for (int a = 0; a < kD; ++a) {
-    const double x = (double)crow[a];
-    const double2 q01 = *reinterpret_cast<const double2*>(&qs[a * kTbQg]);
-    const double2 q23 = *reinterpret_cast<const double2*>(&qs[a * kTbQg + 2]);
-    acc[0] = __fma_rn(q01.x, x, acc[0]);
-    acc[1] = __fma_rn(q01.y, x, acc[1]);
-    acc[2] = __fma_rn(q23.x, x, acc[2]);
-    acc[3] = __fma_rn(q23.y, x, acc[3]);
-  }
-  const int j = ctile * kTbCent + lane;
-  if (j >= c) return;
-#pragma unroll
-  for (int v = 0; v < kTbQg; ++v) {
-    const int r = kTbQg * qg + v;
-    if (r >= nqh) break;
-    const int64_t row = (int64_t)(r / group) * hq + (int64_t)kvh * group + r % group;
-    lut[row * c + j] = (float)acc[v];
+  for (int i = 0; i < 16; ++i) {
+    const int a = (t >> 6) + 4 * i, r = t & 63;
+    if (j0 + r < c) dst[(int64_t)a * c + r] = tile[r][a];
   }
 }
 
 // Kernel topk_codes_rows: one 1024-thread workgroup per (sequence, key/value head, group of up
 // to four query heads sharing it).  LDS is laid out per call (TkLayout): the group's tables,
-// the select histograms, the code histogram (then the class bytes) and the code row when it
-// fits.
-//   1. the group's tables from the workspace (their key ranges reduced on the way), the code
-//      row and its histogram over the C codes (+1 bin for codes >= C): the weight of table
-//      entry j is the number of tokens holding it.
+// the select histograms (later the output lists), the code histogram (then the class bytes)
+// and the code row when it fits.
+//   1. the group's tables, computed (their key ranges reduced on the way); the code row and
+//      its histogram over the C codes (+1 bin for codes >= C): the weight of table entry j is
+//      the number of tokens holding it.
 //   2. for all queries at once, the K-th largest score T_g over the C + 1 weighted entries
 //      (thread t holds entries t, t + 1024, ... < C in registers, thread 0 also the -inf entry
-//      of the codes >= C) and r_g = how many of the tokens
-//      scoring exactly T_g are taken (the lowest indices).  A pass bins the live entries into
-//      1024 bins by a monotone map of the score (linear in the fp32 value while the range is
-//      finite, else a shift of the order key), wave g finds the bin holding the remaining
-//      rank, and that bin's entries stay live.  A pass over keys closer than 1024 units is
-//      exact; a bin of at most 64 entries is settled by wave g comparing them pairwise.
+//      of the codes >= C) and r_g = how many of the tokens scoring exactly T_g are taken (the
+//      lowest indices).  A pass bins the live entries into 1024 bins by a monotone map of the
+//      score (linear in the fp32 value while the range is finite, else a shift of the order
+//      key), wave g finds the bin holding the remaining rank, and that bin's entries stay
+//      live.  A pass over keys closer than 1024 units is exact; a bin of at most 64 entries is
+//      settled by wave g comparing them pairwise.
 //   3. one class byte per code: bit 2g = above T_g, bit 2g+1 = equal to T_g.
-//   4. rounds of 16384 tokens, 1024 contiguous tokens a wave: the wave counts its tokens above
-//      and at T_g from ballots, the counts are scanned over the waves, and each wave writes
-//      its taken tokens (ascending) at offsets from lane-masked bit counts.
+//   4. rounds of 16384 tokens, 16 contiguous tokens a lane: per query, lane counts by bit
+//      counts and wave scans, one barrier for the counts across waves, then each wave lists
+//      its taken tokens (ascending) in LDS and copies the list out whole.
 struct TkLayout {
   unsigned lut, hist, cnt, cl, total;
+  int scap;  // output staging slots per (wave, query)
 };
 
 constexpr unsigned kTkLdsMax = 156 * 1024;  // dynamic LDS; the static arrays take the rest
 constexpr int kNb = 1024;                   // bins of a select pass
 constexpr int kNbPad = kNb + kNb / 16;      // a pad slot after every 16 bins
 constexpr int kCand = 64;                   // largest bin settled pairwise
-constexpr int kTkRound = kTkThreads * 16;   // tokens of an output round
+constexpr int kTkRound = kTkThreads * 16;   // tokens of an output round (16 a thread)
 
 inline unsigned tk_al16(unsigned x) { return (x + 15u) & ~15u; }
 
-// The LDS layout of a call; cl is 0xFFFFFFFF when the code row does not fit.
+// The LDS layout of a call; cl is 0xFFFFFFFF when the code row does not fit.  The select
+// histograms' region later holds each wave's output list per query (scap slots, as many as fit
+// up to 256) and a trash slot per thread.
 inline TkLayout tk_layout(int gn, int c, int64_t n) {
+  const int waves = kTkThreads / 64;
+  const unsigned lutb = tk_al16((unsigned)(gn * (c + 1)) * 4u);
+  const unsigned histb = tk_al16((unsigned)(gn * kNbPad) * 8u);
+  const unsigned cntb = tk_al16((unsigned)(c + 1) * 4u);
+  unsigned clb = 0;
+  if (n <= kTkLdsCodes && lutb + histb + cntb + (unsigned)n * 2u <= kTkLdsMax)
+    clb = tk_al16((unsigned)n * 2u);
+  const unsigned room = kTkLdsMax - lutb - cntb - clb;  // >= histb
+  const int scap0 = (int)((room / 4u - (unsigned)kTkThreads) / (unsigned)(waves * gn));
   TkLayout L;
-  unsigned off = 0;
-  L.lut = off;
-  off = tk_al16(off + (unsigned)(gn * (c + 1)) * 4u);
-  L.hist = off;
-  off = tk_al16(off + (unsigned)(gn * kNbPad) * 8u);
-  L.cnt = off;
-  off = tk_al16(off + (unsigned)(c + 1) * 4u);
-  L.cl = 0xFFFFFFFFu;
-  if (n <= kTkLdsCodes && off + (unsigned)n * 2u <= kTkLdsMax) {
-    L.cl = off;
-    off = tk_al16(off + (unsigned)n * 2u);
-  }
-  L.total = off;
+  L.scap = scap0 < 256 ? scap0 : 256;
+  const unsigned stageb = tk_al16((unsigned)(waves * gn * L.scap + kTkThreads) * 4u);
+  L.lut = 0;
+  L.hist = lutb;
+  L.cnt = L.hist + (histb > stageb ? histb : stageb);
+  L.cl = clb ? L.cnt + cntb : 0xFFFFFFFFu;
+  L.total = L.cnt + cntb + clb;
   return L;
 }
 
@@ -264,9 +240,9 @@ __device__ __forceinline__ TkBins tk_bin_map(unsigned lo, unsigned hi, int pass)
 
 template <int GN, int E, bool CLDS>
 __global__ __launch_bounds__(kTkThreads) void topk_codes_rows(
-    const float* __restrict__ lut_ws, int64_t hq, int64_t hkv, int group, int nchunk,
-    const uint16_t* __restrict__ codes, int64_t n, int c, int64_t k, int32_t* __restrict__ idx,
-    float* __restrict__ score, TkLayout ly) {
+    const double* __restrict__ q64, const float* __restrict__ cbt, int64_t hq, int64_t hkv,
+    int group, int nchunk, const uint16_t* __restrict__ codes, int64_t n, int c, int64_t k,
+    int32_t* __restrict__ idx, float* __restrict__ score, TkLayout ly) {
   constexpr int kWaves = kTkThreads / 64;
   constexpr unsigned kNegInfKey = 0x007FFFFFu;  // the order key of -inf
   extern __shared__ __align__(16) unsigned char tk_smem[];
@@ -292,7 +268,12 @@ __global__ __launch_bounds__(kTkThreads) void topk_codes_rows(
   const int gv = group - g0 < GN ? group - g0 : GN;  // query heads of this group in use
   const int64_t row0 = b * hq + kvh * group + g0;    // their first output row
 
-  // ---- 1. tables (a slot past the group's last query repeats it) with their key ranges
+  // ---- 1. the group's tables (a slot past the group's last query repeats it), lut[g][j] =
+  // fp32(sum_a q_ga c_ja): thread t takes centroids t + 1024 e, read from the transposed
+  // codebook (a wave reads 256 contiguous bytes a dimension), and the queries' fp64 values come
+  // from scalar loads.  Both factors have at most 24 significant bits, so each fp64 product is
+  // exact and fma(q, c, acc) is acc + q c rounded once: the sum is formed in fp64 in dimension
+  // order and rounded to fp32 once.  Their key ranges are reduced on the way.
   for (int j = t; j < GN * kNbPad; j += kTkThreads) hist[j] = 0ull;
   for (int j = t; j <= c; j += kTkThreads) cnt[j] = 0u;
   if (t < GN) {
@@ -301,25 +282,68 @@ __global__ __launch_bounds__(kTkThreads) void topk_codes_rows(
     ccnt[t] = 0u;
   }
   unsigned key[GN][E], klo[GN], khi[GN];
-#pragma unroll
-  for (int g = 0; g < GN; ++g) {
-    const float* src = lut_ws + (row0 + (g < gv ? g : gv - 1)) * c;
-    klo[g] = 0xFFFFFFFFu;
-    khi[g] = 0u;
+  {
+    const float* cth = cbt + kvh * (int64_t)kD * c;  // [a][j]
+    int jc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = t + kTkThreads * e;
-      const float v = j < c ? src[j] : 0.0f;
-      key[g][e] = tk_order_key(v);
-      if (j < c) {
-        lut[g * cp + j] = v;
-        klo[g] = min(klo[g], key[g][e]);
-        khi[g] = max(khi[g], key[g][e]);
-      }
+      jc[e] = j < c ? j : c - 1;
     }
-    if (t == 0) lut[g * cp + c] = -INFINITY;  // the score of every code >= c
-    klo[g] = wave_min(klo[g]);
-    khi[g] = wave_max(khi[g]);
+    const double* qr[GN];
+#pragma unroll
+    for (int g = 0; g < GN; ++g) qr[g] = q64 + (row0 + (g < gv ? g : gv - 1)) * kD;
+    double acc[E][GN];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int g = 0; g < GN; ++g) acc[e][g] = 0.0;
+    // eight dimensions a step, the next step's centroid values loaded before this step's fmas
+    float cv[E][8];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int d = 0; d < 8; ++d) cv[e][d] = cth[(int64_t)d * c + jc[e]];
+#pragma unroll 2
+    for (int a = 0; a < kD; a += 8) {
+      float cn[E][8];
+      const int an = a + 8 < kD ? a + 8 : a;
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int d = 0; d < 8; ++d) cn[e][d] = cth[(int64_t)(an + d) * c + jc[e]];
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const double x = (double)cv[e][d];
+#pragma unroll
+          for (int g = 0; g < GN; ++g) acc[e][g] = __fma_rn(qr[g][a + d], x, acc[e][g]);
+        }
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int d = 0; d < 8; ++d) cv[e][d] = cn[e][d];
+    }
+#pragma unroll
+    for (int g = 0; g < GN; ++g) {
+      klo[g] = 0xFFFFFFFFu;
+      khi[g] = 0u;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int j = t + kTkThreads * e;
+        const float v = (float)acc[e][g];
+        key[g][e] = tk_order_key(v);
+        if (j < c) {
+          lut[g * cp + j] = v;
+          klo[g] = min(klo[g], key[g][e]);
+          khi[g] = max(khi[g], key[g][e]);
+        }
+      }
+      if (t == 0) lut[g * cp + c] = -INFINITY;  // the score of every code >= c
+      klo[g] = wave_min(klo[g]);
+      khi[g] = wave_max(khi[g]);
+    }
   }
   __syncthreads();
   if (lane == 0)
@@ -538,122 +562,203 @@ __global__ __launch_bounds__(kTkThreads) void topk_codes_rows(
   }
   __syncthreads();
 
-  // ---- 4. output
+  // ---- 4. output.  Rounds of 16384 tokens; lane l of wave w takes tokens r0 + 1024 w + 16 l
+  // + b (b < 16), their class bytes packed four to a register.  Per query: lane counts by bit
+  // counts, wave scans by DPP, one barrier for the counts across waves, then each wave lists its
+  // taken tokens in LDS (a token not taken goes to the thread's trash slot) and copies the list
+  // out whole.
+  unsigned* stage = reinterpret_cast<unsigned*>(tk_smem + ly.hist);  // [kWaves][GN][scap]
+  unsigned* trash = stage + kWaves * GN * ly.scap + t;
   unsigned run_a[GN], run_e[GN];  // tokens above / at T_g in the rounds before
 #pragma unroll
   for (int g = 0; g < GN; ++g) run_a[g] = run_e[g] = 0u;
   auto token_code = [&](int64_t i) -> unsigned {
-    const unsigned x = i < n ? (CLDS ? (unsigned)cl[i] : (unsigned)cg[i]) : cu;
+    const unsigned x = CLDS ? (unsigned)cl[i] : (unsigned)cg[i];
     return x < cu ? x : cu;
   };
   for (int64_t r0 = 0, par = 0; r0 < n; r0 += kTkRound, par ^= 1) {
-    const int64_t wb = r0 + (int64_t)wave * (kTkRound / kWaves);
-    unsigned ca[GN], ce[GN];
+    const int64_t tb = r0 + (int64_t)wave * (kTkRound / kWaves) + 16 * lane;
+    unsigned V[4];
+    {
+      unsigned cc[16];
+      if (CLDS && tb + 16 <= n) {
+        const uint4 x0 = *reinterpret_cast<const uint4*>(cl + tb);
+        const uint4 x1 = *reinterpret_cast<const uint4*>(cl + tb + 8);
+        const unsigned w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-    for (int g = 0; g < GN; ++g) ca[g] = ce[g] = 0u;
-#pragma unroll 4
-    for (int q = 0; q < 16; ++q) {
-      const int64_t i = wb + 64 * q + lane;
-      const unsigned v = i < n ? (unsigned)cls[token_code(i)] : 0u;
+        for (int h = 0; h < 8; ++h) {
+          cc[2 * h] = min(w[h] & 0xFFFFu, cu);
+          cc[2 * h + 1] = min(w[h] >> 16, cu);
+        }
+      } else {
 #pragma unroll
-      for (int g = 0; g < GN; ++g) {
-        ca[g] += (unsigned)__popcll(tk_ballot((v >> (2 * g)) & 1u));
-        ce[g] += (unsigned)__popcll(tk_ballot((v >> (2 * g + 1)) & 1u));
+        for (int b = 0; b < 16; ++b) cc[b] = tb + b < n ? token_code(tb + b) : cu;
       }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        unsigned v = 0u;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int b = 4 * q + h;
+          v |= (tb + b < n ? (unsigned)cls[cc[b]] : 0u) << (8 * h);
+        }
+        V[q] = v;
+      }
+    }
+    unsigned xa[GN], xe[GN], ta[GN], te[GN];  // lane-exclusive and wave counts: above, at T_g
+#pragma unroll
+    for (int g = 0; g < GN; ++g) {
+      const unsigned sa = 0x01010101u << (2 * g), se = sa << 1;
+      unsigned na = 0u, ne = 0u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        na += __popc(V[q] & sa);
+        ne += __popc(V[q] & se);
+      }
+      const unsigned ia = wave_incl_sum(na), ie = wave_incl_sum(ne);
+      xa[g] = ia - na;
+      xe[g] = ie - ne;
+      ta[g] = rdlane(ia, 63);
+      te[g] = rdlane(ie, 63);
     }
     if (lane == 0)
 #pragma unroll
       for (int g = 0; g < GN; ++g) {
-        wsum[par][wave][2 * g] = ca[g];
-        wsum[par][wave][2 * g + 1] = ce[g];
+        wsum[par][wave][2 * g] = ta[g];
+        wsum[par][wave][2 * g + 1] = te[g];
       }
     __syncthreads();  // wsum[par] is rewritten two rounds on, after the next round's barrier
-    unsigned pa[GN], pe[GN];  // taken tokens / tokens at T_g before the next of this wave's
 #pragma unroll
     for (int g = 0; g < GN; ++g) {
-      const unsigned xa = lane < kWaves ? wsum[par][lane][2 * g] : 0u;
-      const unsigned xe = lane < kWaves ? wsum[par][lane][2 * g + 1] : 0u;
-      const unsigned ia = row_incl_sum(xa), ie = row_incl_sum(xe);
-      pa[g] = run_a[g] + rdlane(ia, wave) - rdlane(xa, wave);
-      pe[g] = run_e[g] + rdlane(ie, wave) - rdlane(xe, wave);
-      run_a[g] += rdlane(ia, kWaves - 1);
-      run_e[g] += rdlane(ie, kWaves - 1);
-      pa[g] += min(pe[g], R[g]);  // the tokens at T_g taken before this wave's
-    }
-    // every token above T_g is taken, and of those at T_g the first R_g
-#pragma unroll 2
-    for (int q = 0; q < 16; ++q) {
-      const int64_t i = wb + 64 * q + lane;
-      const unsigned code = token_code(i);
-      const unsigned v = i < n ? (unsigned)cls[code] : 0u;
+      const unsigned wa = lane < kWaves ? wsum[par][lane][2 * g] : 0u;
+      const unsigned we = lane < kWaves ? wsum[par][lane][2 * g + 1] : 0u;
+      const unsigned iwa = row_incl_sum(wa), iwe = row_incl_sum(we);
+      const unsigned pe = run_e[g] + rdlane(iwe, wave) - rdlane(we, wave);  // at T_g before
+      const unsigned pa = run_a[g] + rdlane(iwa, wave) - rdlane(wa, wave) + min(pe, R[g]);
+      run_a[g] += rdlane(iwa, kWaves - 1);
+      run_e[g] += rdlane(iwe, kWaves - 1);
+      if (g >= gv) continue;
+      // the taken bit of each token, at bit 8 h of T[q] for token 4 q + h
+      const unsigned ab = 0x01010101u;
+      unsigned T[4], excl, cnt_w;
+      if (pe + te[g] <= R[g]) {  // every token at T_g in this wave is taken (uniform)
 #pragma unroll
-      for (int g = 0; g < GN; ++g) {
-        if (g >= gv) break;
-        bool take = (v >> (2 * g)) & 1u;
-        const bool at = (v >> (2 * g + 1)) & 1u;
-        const unsigned long long em = tk_ballot(at);
-        if (em != 0ull) {  // uniform
-          take = take || (at && lanes_below(em, pe[g]) < R[g]);
-          pe[g] += (unsigned)__popcll(em);
+        for (int q = 0; q < 4; ++q) T[q] = ((V[q] >> (2 * g)) | (V[q] >> (2 * g + 1))) & ab;
+        excl = xa[g] + xe[g];
+        cnt_w = ta[g] + te[g];
+      } else if (pe >= R[g]) {  // none is
+#pragma unroll
+        for (int q = 0; q < 4; ++q) T[q] = (V[q] >> (2 * g)) & ab;
+        excl = xa[g];
+        cnt_w = ta[g];
+      } else {  // the wave holding the R_g-th: each lane takes its first m tokens at T_g
+        const unsigned before = pe + xe[g];
+        unsigned m = before < R[g] ? R[g] - before : 0u;
+        unsigned ct = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          unsigned tq = 0u;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const unsigned byte = V[q] >> (8 * h + 2 * g);
+            unsigned tk = byte & 1u;
+            if ((byte & 2u) && m != 0u) {
+              tk = 1u;
+              --m;
+            }
+            tq |= tk << (8 * h);
+            ct += tk;
+          }
+          T[q] = tq;
         }
-        const unsigned long long tm = tk_ballot(take);
-        const unsigned pos = lanes_below(tm, pa[g]);
-        if (take && pos < (unsigned)k) {  // the bound turns any inconsistency into a wrong answer
-          idx[(row0 + g) * k + pos] = (int32_t)i;
-          if (score) score[(row0 + g) * k + pos] = lut[g * cp + code];
+        const unsigned ic = wave_incl_sum(ct);
+        excl = ic - ct;
+        cnt_w = rdlane(ic, 63);
+      }
+      int32_t* orow = idx + (row0 + g) * k;
+      float* srow = score ? score + (row0 + g) * k : nullptr;
+      if (cnt_w <= (unsigned)ly.scap) {  // uniform
+        unsigned* sg = stage + (wave * GN + g) * ly.scap;
+        unsigned p = excl;
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {
+          const unsigned bit = (T[b >> 2] >> (8 * (b & 3))) & 1u;
+          *(bit ? sg + p : trash) = (unsigned)(tb + b);
+          p += bit;
         }
-        pa[g] += (unsigned)__popcll(tm);
+        // the wave's list (its own LDS operations complete in order)
+        for (unsigned i = lane; i < cnt_w; i += 64) {
+          const unsigned tok = sg[i], pos = pa + i;
+          if (pos < (unsigned)k) {  // the bound turns any inconsistency into a wrong answer
+            orow[pos] = (int32_t)tok;
+            if (srow) srow[pos] = lut[g * cp + token_code(tok)];
+          }
+        }
+      } else {  // longer than the staging slots: straight to global memory
+        unsigned p = pa + excl;
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {
+          const unsigned bit = (T[b >> 2] >> (8 * (b & 3))) & 1u;
+          if (bit && p < (unsigned)k) {
+            orow[p] = (int32_t)(tb + b);
+            if (srow) srow[p] = lut[g * cp + token_code(tb + b)];
+          }
+          p += bit;
+        }
       }
     }
   }
 }
 
 template <int GN, int E, bool CLDS>
-int topk_launch3(dim3 grid, hipStream_t s, const float* lut, int64_t hq, int64_t hkv, int group,
-                 int nchunk, const uint16_t* codes, int64_t n, int c, int64_t k, int32_t* idx,
-                 float* score, const TkLayout& ly) {
+int topk_launch3(dim3 grid, hipStream_t s, const double* q64, const float* cb, int64_t hq,
+                 int64_t hkv, int group, int nchunk, const uint16_t* codes, int64_t n, int c,
+                 int64_t k, int32_t* idx, float* score, const TkLayout& ly) {
   auto kern = topk_codes_rows<GN, E, CLDS>;
   A2ATS_TRY(set_dynamic_lds(kern, ly.total));
-  return launch("topk_codes", kern, grid, dim3(kTkThreads), ly.total, s, lut, hq, hkv, group,
+  return launch("topk_codes", kern, grid, dim3(kTkThreads), ly.total, s, q64, cb, hq, hkv, group,
                 nchunk, codes, n, c, k, idx, score, ly);
 }
 
 template <int GN, int E>
-int topk_launch2(dim3 grid, hipStream_t s, const float* lut, int64_t hq, int64_t hkv, int group,
-                 int nchunk, const uint16_t* codes, int64_t n, int c, int64_t k, int32_t* idx,
-                 float* score) {
+int topk_launch2(dim3 grid, hipStream_t s, const double* q64, const float* cb, int64_t hq,
+                 int64_t hkv, int group, int nchunk, const uint16_t* codes, int64_t n, int c,
+                 int64_t k, int32_t* idx, float* score) {
   const TkLayout ly = tk_layout(GN, c, n);
   if (ly.cl != 0xFFFFFFFFu)
-    return topk_launch3<GN, E, true>(grid, s, lut, hq, hkv, group, nchunk, codes, n, c, k, idx,
-                                     score, ly);
-  return topk_launch3<GN, E, false>(grid, s, lut, hq, hkv, group, nchunk, codes, n, c, k, idx,
-                                    score, ly);
+    return topk_launch3<GN, E, true>(grid, s, q64, cb, hq, hkv, group, nchunk, codes, n, c, k,
+                                     idx, score, ly);
+  return topk_launch3<GN, E, false>(grid, s, q64, cb, hq, hkv, group, nchunk, codes, n, c, k,
+                                    idx, score, ly);
 }
 
 // table entries a thread holds: C <= 1024, 2048, 4096
 template <int GN>
-int topk_launch(dim3 grid, hipStream_t s, const float* lut, int64_t hq, int64_t hkv, int group,
-                int nchunk, const uint16_t* codes, int64_t n, int c, int64_t k, int32_t* idx,
-                float* score) {
+int topk_launch(dim3 grid, hipStream_t s, const double* q64, const float* cb, int64_t hq,
+                int64_t hkv, int group, int nchunk, const uint16_t* codes, int64_t n, int c,
+                int64_t k, int32_t* idx, float* score) {
   if (c <= kTkThreads)
-    return topk_launch2<GN, 1>(grid, s, lut, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
+    return topk_launch2<GN, 1>(grid, s, q64, cb, hq, hkv, group, nchunk, codes, n, c, k, idx,
+                               score);
   if (c <= 2 * kTkThreads)
-    return topk_launch2<GN, 2>(grid, s, lut, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
-  return topk_launch2<GN, 4>(grid, s, lut, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
+    return topk_launch2<GN, 2>(grid, s, q64, cb, hq, hkv, group, nchunk, codes, n, c, k, idx,
+                               score);
+  return topk_launch2<GN, 4>(grid, s, q64, cb, hq, hkv, group, nchunk, codes, n, c, k, idx,
+                             score);
 }
 
-int topk_dispatch(int gn, dim3 grid, hipStream_t s, const float* lut, int64_t hq, int64_t hkv,
-                  int group, int nchunk, const uint16_t* codes, int64_t n, int c, int64_t k,
-                  int32_t* idx, float* score) {
+int topk_dispatch(int gn, dim3 grid, hipStream_t s, const double* q64, const float* cb,
+                  int64_t hq, int64_t hkv, int group, int nchunk, const uint16_t* codes,
+                  int64_t n, int c, int64_t k, int32_t* idx, float* score) {
   switch (gn) {
     case 1:
-      return topk_launch<1>(grid, s, lut, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
+      return topk_launch<1>(grid, s, q64, cb, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
     case 2:
-      return topk_launch<2>(grid, s, lut, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
+      return topk_launch<2>(grid, s, q64, cb, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
     case 3:
-      return topk_launch<3>(grid, s, lut, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
+      return topk_launch<3>(grid, s, q64, cb, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
     default:
-      return topk_launch<4>(grid, s, lut, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
+      return topk_launch<4>(grid, s, q64, cb, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
   }
 }
 
@@ -662,9 +767,14 @@ int topk_dispatch(int gn, dim3 grid, hipStream_t s, const float* lut, int64_t hq
 
 using namespace a2ats;
 
+// The workspace: the queries in fp64, then the codebook transposed (bounded with hq >= hkv).
+static size_t topk_q64_bytes(int64_t batch, int64_t hq) {
+  return align_up((size_t)(batch * hq * kD) * sizeof(double));
+}
+
 extern "C" size_t a2ats_topk_workspace(int64_t batch, int64_t hq, int64_t c) {
   if (batch < 1 || hq < 1 || c < 1 || c > kTkMaxC) return 0;
-  return align_up((size_t)(batch * hq * c) * sizeof(float));
+  return topk_q64_bytes(batch, hq) + align_up((size_t)(hq * c * kD) * sizeof(float));
 }
 
 extern "C" int a2ats_topk_codes(const void* qb, int q_dtype, int64_t batch, int64_t hq,
@@ -678,28 +788,25 @@ extern "C" int a2ats_topk_codes(const void* qb, int q_dtype, int64_t batch, int6
   const int group = (int)(hq / hkv);
   const int gn = group < 4 ? group : 4;
   const int nchunk = (group + gn - 1) / gn;
-  if (batch * hkv * nchunk > 0x7FFFFFFF) return A2ATS_EINVAL;
-  if (batch * hq > 0x7FFFFFFF) return A2ATS_EINVAL;
-  const int nqh = (int)(batch * group);  // queries of one key/value head
-  const int nqb = (nqh + kTbWaves * kTbQg - 1) / (kTbWaves * kTbQg);
-  const int nct = (int)((c + kTbCent - 1) / kTbCent);
-  const int64_t table_wgs = hkv * nqb * nct;
-  if (table_wgs > 0x7FFFFFFF) return A2ATS_EINVAL;
+  if (batch * hkv * nchunk > 0x7FFFFFFF || batch * hq > 0x7FFFFFFF) return A2ATS_EINVAL;
   if (n == 0 || k == 0) return A2ATS_OK;
   if (!qb || !codes || !codebook || !idx) return A2ATS_EINVAL;
-  if ((reinterpret_cast<uintptr_t>(codebook) & 15) != 0) return A2ATS_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(qb) & 15) != 0) return A2ATS_EINVAL;
   if (!ws_ok(workspace, workspace_bytes, a2ats_topk_workspace(batch, hq, c)))
     return A2ATS_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* lut = static_cast<float*>(workspace);
+  double* q64 = static_cast<double*>(workspace);
+  float* cbt = reinterpret_cast<float*>(static_cast<char*>(workspace) + topk_q64_bytes(batch, hq));
+  const int64_t quads = batch * hq * kD / 4;
+  const int nqw = (int)((quads + 255) / 256), njt = (int)((c + 63) / 64);
+  const dim3 pgrid((unsigned)(nqw + hkv * njt * 2));
   if (q_dtype == A2ATS_F32)
-    A2ATS_TRY(launch("topk_table", topk_table<A2ATS_F32>, dim3((unsigned)table_wgs),
-                     dim3(kTbWaves * 64), 0, s, qb, (int)hq, group, nqh, nqb, nct, codebook,
-                     (int)c, lut));
+    A2ATS_TRY(launch("topk_prep", topk_prep<A2ATS_F32>, pgrid, dim3(256), 0, s, qb, quads, nqw,
+                     codebook, (int)c, njt, q64, cbt));
   else
-    A2ATS_TRY(launch("topk_table", topk_table<A2ATS_BF16>, dim3((unsigned)table_wgs),
-                     dim3(kTbWaves * 64), 0, s, qb, (int)hq, group, nqh, nqb, nct, codebook,
-                     (int)c, lut));
+    A2ATS_TRY(launch("topk_prep", topk_prep<A2ATS_BF16>, pgrid, dim3(256), 0, s, qb, quads, nqw,
+                     codebook, (int)c, njt, q64, cbt));
   const dim3 grid((unsigned)(batch * hkv * nchunk));
-  return topk_dispatch(gn, grid, s, lut, hq, hkv, group, nchunk, codes, n, (int)c, k, idx, score);
+  return topk_dispatch(gn, grid, s, q64, cbt, hq, hkv, group, nchunk, codes, n, (int)c, k, idx,
+                       score);
 }

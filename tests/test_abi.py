@@ -374,7 +374,7 @@ def test_topk_codes_validation(L):
     assert call(qb=None) == EINVAL
     assert call(idx=None) == EINVAL
     assert call(cb=None) == EINVAL
-    assert call(cb=ctypes.c_void_p(4100)) == EINVAL  # codebook not 16-byte aligned
+    assert call(qb=ctypes.c_void_p(4100)) == EINVAL  # queries not 16-byte aligned
     assert call(batch=1 << 28, hq=8) == EINVAL       # batch * hq >= 2^31
     assert call(ws=None) == EWORKSPACE
     assert call(wsb=need - 1) == EWORKSPACE
