@@ -490,7 +490,9 @@ def extra_workloads(ctx, steps, warmup):
     ms_t = ctx.timed(topk_step, 20)
     ms_tf = ctx.timed(topk_step, 5, flush=True)
     pr_t = ctx.profile(topk_step, 5)
-    kt_us = pr_t["topk_codes"][1] * 1e3
+    prep_us = pr_t["topk_prep"][1] * 1e3 if "topk_prep" in pr_t else 0.0
+    sel_us = pr_t["topk_codes"][1] * 1e3
+    kt_us = prep_us + sel_us  # both launches of a2ats_topk_codes
     t_bytes = (wt.batch * wt.heads * wt.n * 2 + wt.heads * wt.c * 128 * 4
                + wt.batch * wt.q_heads * (128 * 4 + kt * 8))
     t_flops = 2.0 * wt.batch * wt.q_heads * wt.c * 128  # fp64 table: one mul + one add a term
@@ -499,6 +501,7 @@ def extra_workloads(ctx, steps, warmup):
                     "k=%d (10%%); far query rotation + table + top-K" % kt,
         "step_us": round(ms_t * 1e3, 2), "step_flushed_us": round(ms_tf * 1e3, 2),
         "topk_kernel_us": round(kt_us, 2),
+        "topk_prep_us": round(prep_us, 2), "topk_select_us": round(sel_us, 2),
         "far_query_rope_us": round(pr_t["far_query_rope"][1] * 1e3, 2),
         "algorithmic_bytes": t_bytes, "kernel_GBps": round(t_bytes / (kt_us * 1e-6) / 1e9, 1),
         "table_fp64_ops": t_flops,
