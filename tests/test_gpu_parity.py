@@ -1111,7 +1111,8 @@ class TestTopkCodes:
     @pytest.mark.parametrize("batch,hq,hkv,n,c,k", [
         (2, 6, 2, 3000, 256, 300), (1, 3, 3, 1000, 1000, 1), (3, 4, 2, 4097, 1024, 4097),
         (1, 8, 2, 5000, 300, 777), (2, 4, 1, 2048, 4096, 1500), (1, 5, 1, 999, 64, 100),
-        (1, 2, 1, 40000, 1024, 4000), (1, 1, 1, 1, 1, 1), (2, 2, 2, 65, 7, 64)])
+        (1, 2, 1, 40000, 1024, 4000), (1, 1, 1, 1, 1, 1), (2, 2, 2, 65, 7, 64),
+        (1, 3, 1, 3000, 1500, 700)])
     @pytest.mark.parametrize("qdt", ["f32", "bf16"])
     def test_matches_oracle(self, batch, hq, hkv, n, c, k, qdt):
         rng = np.random.default_rng(batch * 1000 + hq * 100 + n + c)
@@ -1137,6 +1138,45 @@ class TestTopkCodes:
         valid = np.flatnonzero(codes[0, 0] < 4)
         want = np.sort(np.concatenate([valid, np.flatnonzero(codes[0, 0] >= 4)])[:k])
         assert np.array_equal(idx[0, 1], want) and np.array_equal(idx[0, 2], want)
+
+    def test_clustered_scores_several_passes(self):
+        # q = e_0 makes score_j = cb[j, 0] exactly: 1500 entries spread over [-100, 100] and
+        # a run of 500 consecutive fp32 values at 1.0 (two groups of 24 equal to members of the
+        # run), so the first select pass's bin holding the cut has far more than 64 entries
+        # and a second pass over the run's range splits them (C = 2048: two entries a thread)
+        rng = np.random.default_rng(11)
+        c, n = 2048, 20000
+        cb = rng.standard_normal((1, c, 128)).astype(np.float32)
+        run = np.float32(1.0) + np.arange(500, dtype=np.float32) * np.float32(2.0 ** -23)
+        v = rng.uniform(-100, 100, c).astype(np.float32)
+        v[:500] = run
+        v[500:524] = run[100]
+        v[524:548] = run[300]
+        cb[0, :, 0] = rng.permutation(v)
+        qb = np.zeros((1, 2, 128), np.float32)
+        qb[0, :, 0] = 1.0
+        qb[0, 1, 0] = 2.0  # the same order at twice the scale
+        codes = rng.integers(0, c, (1, 1, n)).astype(np.uint16)
+        s = cb[0, codes[0, 0], 0]
+        above = int(np.sum(s > run[250]))
+        for k in (above, above + 1, above + 37, int(np.sum(s >= run[100]))):
+            topk_case(qb, codes, cb, k)
+
+    @pytest.mark.parametrize("k", [1, 400, 1000, 4990])
+    def test_infinite_scores(self, k):
+        # scores beyond the fp32 range round to +inf or -inf, so the select bins by shifts of
+        # the order key; hundreds of tokens tie at +inf, and -inf scores tie with the invalid
+        # codes (codes >= c)
+        rng = np.random.default_rng(12)
+        c, n = 600, 5000
+        cb = rng.standard_normal((1, c, 128)).astype(np.float32)
+        cb[0, :100, 0] = 3e38
+        cb[0, 100:200, 0] = -3e38
+        qb = np.zeros((1, 2, 128), np.float32)
+        qb[0, :, 0] = 10.0
+        qb[0, 1, 1:] = rng.standard_normal(127)
+        codes = rng.integers(0, c + 3, (1, 1, n)).astype(np.uint16)
+        topk_case(qb, codes, cb, k)
 
     def test_decode_shape(self):
         # 32 sequences x 24 query heads over 8 key heads, 16384 uniform codes, C = 1024,
