@@ -72,16 +72,18 @@ def main():
                          "<workload>_<pass>) into profiles/<kernel>_<workload>_pmc.{json,md}")
     ap.add_argument("--trace-summarize", metavar="DIR",
                     help="turn a rocprofv3 --kernel-trace --stats output under DIR into "
-                         "profiles/encode_stress_trace.md")
+                         "profiles/<name>_trace.md")
+    ap.add_argument("--trace-name", default="encode_stress",
+                    help="the workload the trace covers, naming its summary file")
     ap.add_argument("--command", default="",
-                    help="the command line that produced the profiler output (recorded in the "
-                         "summary)")
+                    help="the command lines that produced the profiler output (recorded in the "
+                         "summary); by default they are rebuilt from what the profiler recorded")
     args = ap.parse_args()
     if args.pmc_summarize:
         pmc_summarize(args.pmc_summarize, args.command)
         return
     if args.trace_summarize:
-        trace_summarize(args.trace_summarize, args.command)
+        trace_summarize(args.trace_summarize, args.command, args.trace_name)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -803,9 +805,25 @@ def pmc_summarize(root, command):
         wl, _, tag = p.rpartition("_")
         by_wl.setdefault(wl, []).append((tag, os.path.join(root, p)))
     written = []
+    absroot = os.path.abspath(root)
     for (wl, pat), (what, abytes, aflops, src) in alg.items():
         if wl not in by_wl:
             continue
+        if command:
+            cmd = command
+        else:
+            # one rocprofv3 pass per counter group, as recorded in each pass's own output
+            lines = ["cd /tmp && export TMPDIR=/tmp"]
+            for tag, d in by_wl[wl]:
+                names = []
+                for n, _, v in _pmc_dispatches(d):
+                    names += [cn for cn in v if cn not in names]
+                lines.append("timeout -s KILL 90 rocprofv3 --pmc %s --output-format csv -d %s -o p "
+                             "-- python3 %s --pmc-probe %s"
+                             % (" ".join(names), os.path.join(absroot, os.path.basename(d)),
+                                os.path.join(ROOT, "bench.py"), wl))
+            lines.append("python3 %s --pmc-summarize %s" % (os.path.join(ROOT, "bench.py"), absroot))
+            cmd = "\n".join(lines)
         counters, scales = {}, {}
         for tag, d in by_wl[wl]:
             rows = _pmc_dispatches(d)
@@ -842,7 +860,7 @@ def pmc_summarize(root, command):
         out = {"kernel": pat, "workload": wl, "what": what, "source": src,
                "source_sha": sha_of(os.path.join(ROOT, src)), "counters_per_launch": counters,
                "reference_scale": scales, "algorithmic_bytes_per_launch": abytes,
-               "algorithmic_flops_per_launch": aflops, "command": command}
+               "algorithmic_flops_per_launch": aflops, "command": cmd}
         hbm = 0.0
         have = True
         for cn in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -866,7 +884,7 @@ def pmc_summarize(root, command):
         with open(base + ".md", "w") as f:
             f.write("# %s, %s workload: counters per launch\n\n%s.\n\n" % (pat, wl, what))
             f.write("Command (rocprofv3 --pmc passes, one counter group each, then the summary):\n\n"
-                    "```\n%s\n```\n\n" % command)
+                    "```\n%s\n```\n\n" % cmd)
             f.write("| counter | median per launch |\n|---|---|\n")
             for cn in sorted(counters):
                 f.write("| %s | %.6g |\n" % (cn, counters[cn]))
@@ -888,9 +906,10 @@ def pmc_summarize(root, command):
     print(json.dumps({"written": written}))
 
 
-def trace_summarize(root, command):
-    """Kernel statistics of a rocprofv3 --kernel-trace --stats run of the headline, read from
-    the rocpd database it writes: calls, mean / min / max duration and registers per kernel."""
+def trace_summarize(root, command, name="encode_stress"):
+    """Kernel statistics of a rocprofv3 --kernel-trace --stats run, read from the rocpd
+    database it writes: calls, mean / min / max duration and registers per kernel, into
+    profiles/<name>_trace.md."""
     import sqlite3
 
     dbs = glob.glob(os.path.join(root, "**", "*.db"), recursive=True)
@@ -917,10 +936,22 @@ def trace_summarize(root, command):
             name = rest[k:k + ln] + ("<" + tmpl[1:tmpl.index("EE") + 1] + ">" if tmpl.startswith("I") else "")
         return name.split("(")[0][:80]
 
-    path = os.path.join(ROOT, "profiles", "encode_stress_trace.md")
+    if not command:
+        # the profiled program's command line is in the database; the profiler's own options
+        # are those of every trace summarized here
+        prog = con.execute("select command from rocpd_info_process").fetchone()
+        if not prog or not prog[0]:
+            raise SystemExit("the database records no command: pass --command")
+        absroot = os.path.abspath(root)
+        prefix = os.path.basename(dbs[0])[:-len("_results.db")]
+        command = ("cd /tmp && export TMPDIR=/tmp\n"
+                   "timeout -k 10 300 rocprofv3 --kernel-trace --stats -d %s -o %s -- %s\n"
+                   "python3 %s --trace-summarize %s --trace-name %s"
+                   % (absroot, prefix, prog[0], os.path.join(ROOT, "bench.py"), absroot, name))
+    path = os.path.join(ROOT, "profiles", "%s_trace.md" % name)
     with open(path, "w") as f:
-        f.write("# encode_stress headline: kernel trace statistics\n\n"
-                "Command:\n\n```\n%s\n```\n\n" % command)
+        f.write("# %s: kernel trace statistics\n\n"
+                "Command:\n\n```\n%s\n```\n\n" % (name, command))
         f.write("| kernel | calls | average us | min us | max us | share % | VGPR | AGPR | SGPR | LDS B | grid | block |\n"
                 "|---|---|---|---|---|---|---|---|---|---|---|---|\n")
         for r in rows:
