@@ -427,10 +427,11 @@ int a2ats_kmeans(const void* x, int x_dtype, int64_t heads, int64_t n, int64_t d
  *   codes     [batch, hkv, n] uint16; codebook [hkv, c, d] fp32, 1 <= c <= 4096, d = 128
  *   idx       [batch, hq, k] int32; score [batch, hq, k] fp32 or NULL; 0 <= k <= n
  * hq must be a multiple of hkv and batch * hq < 2^31.  Nothing is written when n or k is 0.
- * Two launches: the queries in fp64 and the codebook transposed into the workspace, then one
- * workgroup per code row and up to four query heads of a group: their tables in LDS, the
- * K-th largest score by passes of monotone 1024-bin histograms over the C + 1 table entries
- * weighted by their token counts, then the taken tokens in token order.  Workspace:
+ * Two launches: every query's table into the workspace (fp64 matrix cores, whose fma-chain
+ * accumulation in k order gives the dimension-ordered sum exactly), then one workgroup per
+ * code row and up to four query heads of a group: their tables in LDS, the K-th largest
+ * score by passes of monotone 1024-bin histograms over the C + 1 table entries weighted by
+ * their token counts, then the taken tokens in token order.  Workspace:
  * a2ats_topk_workspace(batch, hq, c) bytes (256-byte aligned), A2ATS_EWORKSPACE when missing
  * or short; A2ATS_EINVAL for misaligned queries.  Returns without waiting.
  */

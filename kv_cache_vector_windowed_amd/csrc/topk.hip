@@ -5,13 +5,13 @@
 // (q R_b) . c_{code_t}: one table of C values per query, gathered by code.
 //
 // Two kernels (their own comments say more):
-//   topk_prep        the queries in fp64 and the codebook transposed, into the workspace.
-//   topk_codes_rows  per (sequence, key/value head, up to four query heads): the queries'
-//                    tables in LDS, lut_gj = fp32(sum_a qb_ga * c_ja) with the sum taken in fp64
-//                    in dimension order and rounded to fp32 once (both factors have at most 24
-//                    significant bits, so each fp64 product is exact and fma(q, c, acc) equals
-//                    acc + q*c rounded once: the fma loop is the plain product-then-add sum),
-//                    the histogram of the code row, the K-th largest score by monotone-bin
+//   topk_table       every query's table, lut_gj = fp32(sum_a qb_ga * c_ja) with the sum taken
+//                    in fp64 in dimension order and rounded to fp32 once (both factors have at
+//                    most 24 significant bits, so each fp64 product is exact and fma(q, c, acc)
+//                    equals acc + q*c rounded once: the fma chain is the plain product-then-add
+//                    sum), on the fp64 matrix cores, into the workspace.
+//   topk_codes_rows  per (sequence, key/value head, up to four query heads): the tables in
+//                    LDS, the histogram of the code row, the K-th largest score by monotone-bin
 //                    histogram passes over the C + 1 weighted table entries (not over the n
 //                    tokens), and the taken tokens in token order.
 // Scores compare through the order-preserving map of fp32 onto u32 (-0 and +0 equal); a code
@@ -25,6 +25,7 @@ constexpr int kD = A2ATS_HEAD_DIM;
 constexpr int kTkThreads = 1024;
 constexpr int kTkMaxC = 4096;                        // table entries per query in LDS
 constexpr int kTkLdsCodes = 16384;                   // longest code row kept in LDS
+typedef unsigned tk_u4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ unsigned tk_order_key(float s) {
   if (s == 0.0f) s = 0.0f;  // -0 and +0 rank equal
@@ -32,65 +33,118 @@ __device__ __forceinline__ unsigned tk_order_key(float s) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Kernel topk_prep, two jobs in one launch, both into the workspace:
-//   workgroups [0, nqw): the queries in fp64 (exact), same layout, four elements a thread, so
-//     that the selection kernel reads them with scalar loads;
-//   the rest: the codebook transposed to [kvh][a][j] through 64 x 64 LDS tiles, so that a
-//     wave reading dimension a of 64 consecutive centroids reads 256 contiguous bytes.
+// Kernel topk_table, on the fp64 matrix cores.  v_mfma_f64_16x16x4f64 adds its four products to
+// C in k order with one rounding each (an fma chain), so a chain of 32 of them over the
+// dimensions in order forms exactly the dimension-ordered fp64 sum.  One 768-thread workgroup per
+// (key/value head, strip of 32 centroids, chunk of up to 96 of that head's batch * group queries,
+// taken in (sequence, query head) order).  The strip and the chunk's queries are staged in LDS
+// as fp32 (exact for fp32 and bf16 queries), rows padded to 132 floats so that the 16 rows x 4
+// dimensions a wave reads at once fall in distinct banks.  Wave w (of 12, three a SIMD) runs one
+// chain: centroid tile w & 1 (16 centroids) against query tile w >> 1 (16 queries; a tile past
+// the chunk multiplies zero rows and is never stored).  Operands: A lane l = query l % 16 of the
+// tile, dimension 4 s + l / 16; B lane l = centroid l % 16, same dimension; result register r of
+// lane l = query 4 r + l / 16, centroid l % 16, stored rounded to fp32 at
+// lut[(sequence * hq + query head) * c + j].
+typedef double tb_d4 __attribute__((ext_vector_type(4)));
+typedef float tb_f4 __attribute__((ext_vector_type(4)));
+constexpr int kTbPitch = kD + 4;
+constexpr int kTbStrip = 32;        // centroids a workgroup (two tiles)
+constexpr int kTbChunk = 96;        // queries a workgroup (six tiles)
+constexpr int kTbThreads = 64 * (kTbStrip / 16) * (kTbChunk / 16);
+
 template <int QDT>
-__global__ __launch_bounds__(256) void topk_prep(const void* __restrict__ qb, int64_t quads,
-                                                 int nqw, const float* __restrict__ cb, int c,
-                                                 int njt, double* __restrict__ q64,
-                                                 float* __restrict__ cbt) {
-  __shared__ float tile[64][65];
-  const int t = threadIdx.x;
-  if ((int)blockIdx.x < nqw) {
-    const int64_t f = (int64_t)blockIdx.x * 256 + t;
-    if (f >= quads) return;
-    float v[4];
-    if (QDT == A2ATS_F32) {
-      const float4 x = reinterpret_cast<const float4*>(qb)[f];
-      v[0] = x.x;
-      v[1] = x.y;
-      v[2] = x.z;
-      v[3] = x.w;
-    } else {
-      const uint2 x = reinterpret_cast<const uint2*>(qb)[f];
-      v[0] = __uint_as_float(x.x << 16);
-      v[1] = __uint_as_float(x.x & 0xFFFF0000u);
-      v[2] = __uint_as_float(x.y << 16);
-      v[3] = __uint_as_float(x.y & 0xFFFF0000u);
-    }
-    double2* dst = reinterpret_cast<double2*>(q64) + 2 * f;
-    dst[0] = make_double2((double)v[0], (double)v[1]);
-    dst[1] = make_double2((double)v[2], (double)v[3]);
-    return;
-  }
-  const int w = (int)blockIdx.x - nqw;  // (kvh, j tile, a half)
-  const int ah = w & 1, jt = (w >> 1) % njt, kvh = (w >> 1) / njt;
-  const int j0 = jt * 64, a0 = ah * 64;
-  const float* src = cb + ((int64_t)kvh * c + j0) * kD + a0;
+__global__ __launch_bounds__(kTbThreads) void topk_table(const void* __restrict__ qb,
+                                                         const float* __restrict__ cb,
+                                                         int64_t batch, int64_t hq, int group,
+                                                         int c, int nstrip, int nchunk,
+                                                         float* __restrict__ lut) {
+  __shared__ __align__(16) float cs[kTbStrip * kTbPitch];  // [centroid of the strip][dimension]
+  __shared__ __align__(16) float qs[kTbChunk * kTbPitch];  // [query of the chunk][dimension]
+  constexpr int kCv = (kTbStrip * 32 + kTbThreads - 1) / kTbThreads;  // strip float4 a thread
+  constexpr int kQv = kTbChunk * 32 / kTbThreads;                     // query float4 a thread
+  static_assert(kTbChunk * 32 % kTbThreads == 0, "query staging");
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  unsigned w = blockIdx.x;
+  const int qc = (int)(w % (unsigned)nchunk);
+  w /= (unsigned)nchunk;
+  const int strip = (int)(w % (unsigned)nstrip);
+  const int64_t kvh = w / (unsigned)nstrip;
+  const int j0 = strip * kTbStrip, q0 = qc * kTbChunk;
+  const int nq = (int)(batch * group);  // this head's queries (batch * hq < 2^31)
+  const int nqc = nq - q0 < kTbChunk ? nq - q0 : kTbChunk;
+  auto qrow = [&](int qi) {  // row of query qi of this head in qb and lut
+    const int sq = qi / group;
+    return (int64_t)sq * hq + kvh * group + (qi - sq * group);
+  };
+  {
+    // every load in flight before the LDS writes; rows past c or past the chunk are zero
+    const float* src = cb + kvh * c * kD;
+    tb_f4 cv[kCv];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {  // rows j0 .. j0 + 63, dimensions a0 .. a0 + 63
-    const int r = (t >> 6) + 4 * i, a = t & 63;
-    tile[r][a] = j0 + r < c ? src[(int64_t)r * kD + a] : 0.0f;
+    for (int i = 0; i < kCv; ++i) {
+      const int f = t + kTbThreads * i, r = j0 + (f >> 5);
+      if (f < kTbStrip * 32)
+        cv[i] = reinterpret_cast<const tb_f4*>(src + (int64_t)(r < c ? r : c - 1) * kD)[f & 31];
+    }
+    tb_f4 qv[kQv];
+#pragma unroll
+    for (int i = 0; i < kQv; ++i) {
+      const int f = t + kTbThreads * i, r = f >> 5;
+      const int64_t row = qrow(q0 + (r < nqc ? r : nqc - 1));  // past the chunk: zeroed below
+      if (QDT == A2ATS_F32) {
+        qv[i] = reinterpret_cast<const tb_f4*>(qb)[row * (kD / 4) + (f & 31)];
+      } else {
+        const uint2 x = reinterpret_cast<const uint2*>(qb)[row * (kD / 4) + (f & 31)];
+        qv[i] = (tb_f4){__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xFFFF0000u),
+                        __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xFFFF0000u)};
+      }
+    }
+    const tb_f4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kCv; ++i) {
+      const int f = t + kTbThreads * i, r = f >> 5;
+      if (f < kTbStrip * 32)
+        *reinterpret_cast<tb_f4*>(cs + r * kTbPitch + 4 * (f & 31)) = j0 + r < c ? cv[i] : z;
+    }
+#pragma unroll
+    for (int i = 0; i < kQv; ++i) {
+      const int f = t + kTbThreads * i, r = f >> 5;
+      *reinterpret_cast<tb_f4*>(qs + r * kTbPitch + 4 * (f & 31)) = r < nqc ? qv[i] : z;
+    }
   }
   __syncthreads();
-  float* dst = cbt + ((int64_t)kvh * kD + a0) * c + j0;
+  const int li = lane & 15, lk = lane >> 4, ct = wave & 1, qt = wave >> 1;
+  const float* bp = cs + (16 * ct + li) * kTbPitch + lk;
+  const float* ap = qs + (16 * qt + li) * kTbPitch + lk;
+  // every operand read into registers first, so that the chain runs without LDS waits
+  float bv[kD / 4], av[kD / 4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int a = (t >> 6) + 4 * i, r = t & 63;
-    if (j0 + r < c) dst[(int64_t)a * c + r] = tile[r][a];
+  for (int s = 0; s < kD / 4; ++s) {
+    bv[s] = bp[4 * s];
+    av[s] = ap[4 * s];
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the chain
+  tb_d4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int s = 0; s < kD / 4; ++s)
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av[s], (double)bv[s], acc, 0, 0, 0);
+  const int j = j0 + 16 * ct + li;
+  if (j < c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int qi = 16 * qt + 4 * r + lk;
+      if (qi < nqc) lut[qrow(q0 + qi) * c + j] = (float)acc[r];
+    }
 }
 
 // Kernel topk_codes_rows: one 1024-thread workgroup per (sequence, key/value head, group of up
 // to four query heads sharing it).  LDS is laid out per call (TkLayout): the group's tables,
 // the select histograms (later the output lists), the code histogram (then the class bytes)
 // and the code row when it fits.
-//   1. the group's tables, computed (their key ranges reduced on the way); the code row and
-//      its histogram over the C codes (+1 bin for codes >= C): the weight of table entry j is
-//      the number of tokens holding it.
+//   1. the group's tables, read from the workspace (their key ranges reduced on the way); the
+//      code row and its histogram over the C codes (+1 bin for codes >= C): the weight of
+//      table entry j is the number of tokens holding it.
 //   2. for all queries at once, the K-th largest score T_g over the C + 1 weighted entries
 //      (thread t holds entries t, t + 1024, ... < C in registers, thread 0 also the -inf entry
 //      of the codes >= C) and r_g = how many of the tokens scoring exactly T_g are taken (the
@@ -240,7 +294,7 @@ __device__ __forceinline__ TkBins tk_bin_map(unsigned lo, unsigned hi, int pass)
 
 template <int GN, int E, bool CLDS>
 __global__ __launch_bounds__(kTkThreads) void topk_codes_rows(
-    const double* __restrict__ q64, const float* __restrict__ cbt, int64_t hq, int64_t hkv,
+    const float* __restrict__ tab, int64_t hq, int64_t hkv,
     int group, int nchunk, const uint16_t* __restrict__ codes, int64_t n, int c, int64_t k,
     int32_t* __restrict__ idx, float* __restrict__ score, TkLayout ly) {
   constexpr int kWaves = kTkThreads / 64;
@@ -268,12 +322,18 @@ __global__ __launch_bounds__(kTkThreads) void topk_codes_rows(
   const int gv = group - g0 < GN ? group - g0 : GN;  // query heads of this group in use
   const int64_t row0 = b * hq + kvh * group + g0;    // their first output row
 
-  // ---- 1. the group's tables (a slot past the group's last query repeats it), lut[g][j] =
-  // fp32(sum_a q_ga c_ja): thread t takes centroids t + 1024 e, read from the transposed
-  // codebook (a wave reads 256 contiguous bytes a dimension), and the queries' fp64 values come
-  // from scalar loads.  Both factors have at most 24 significant bits, so each fp64 product is
-  // exact and fma(q, c, acc) is acc + q c rounded once: the sum is formed in fp64 in dimension
-  // order and rounded to fp32 once.  Their key ranges are reduced on the way.
+  // ---- 1. the group's tables from the table kernel (a slot past the group's last query
+  // repeats it); their key ranges are reduced on the way.  A code row kept in LDS in 16-byte
+  // pieces (at most two a thread) is loaded first, so that both loads are in flight together.
+  const uint16_t* cg = codes + bk * n;
+  const unsigned cu = (unsigned)c;
+  const bool rows16 = CLDS && (n & 7) == 0;
+  const int n8 = (int)(n >> 3);
+  tk_u4 pre[kTkLdsCodes / 8 / kTkThreads];
+  if (rows16)
+#pragma unroll
+    for (int q = 0; q < kTkLdsCodes / 8 / kTkThreads; ++q)
+      if (t + kTkThreads * q < n8) pre[q] = reinterpret_cast<const tk_u4*>(cg)[t + kTkThreads * q];
   for (int j = t; j < GN * kNbPad; j += kTkThreads) hist[j] = 0ull;
   for (int j = t; j <= c; j += kTkThreads) cnt[j] = 0u;
   if (t < GN) {
@@ -283,47 +343,15 @@ __global__ __launch_bounds__(kTkThreads) void topk_codes_rows(
   }
   unsigned key[GN][E], klo[GN], khi[GN];
   {
-    const float* cth = cbt + kvh * (int64_t)kD * c;  // [a][j]
-    int jc[E];
+    float acc[E][GN];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int j = t + kTkThreads * e;
-      jc[e] = j < c ? j : c - 1;
-    }
-    const double* qr[GN];
+    for (int g = 0; g < GN; ++g) {
+      const float* tr = tab + (row0 + (g < gv ? g : gv - 1)) * c;
 #pragma unroll
-    for (int g = 0; g < GN; ++g) qr[g] = q64 + (row0 + (g < gv ? g : gv - 1)) * kD;
-    double acc[E][GN];
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-#pragma unroll
-      for (int g = 0; g < GN; ++g) acc[e][g] = 0.0;
-    // eight dimensions a step, the next step's centroid values loaded before this step's fmas
-    float cv[E][8];
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-#pragma unroll
-      for (int d = 0; d < 8; ++d) cv[e][d] = cth[(int64_t)d * c + jc[e]];
-#pragma unroll 2
-    for (int a = 0; a < kD; a += 8) {
-      float cn[E][8];
-      const int an = a + 8 < kD ? a + 8 : a;
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-#pragma unroll
-        for (int d = 0; d < 8; ++d) cn[e][d] = cth[(int64_t)(an + d) * c + jc[e]];
-#pragma unroll
-      for (int d = 0; d < 8; ++d)
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const double x = (double)cv[e][d];
-#pragma unroll
-          for (int g = 0; g < GN; ++g) acc[e][g] = __fma_rn(qr[g][a + d], x, acc[e][g]);
-        }
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-#pragma unroll
-        for (int d = 0; d < 8; ++d) cv[e][d] = cn[e][d];
+      for (int e = 0; e < E; ++e) {
+        const int j = t + kTkThreads * e;
+        acc[e][g] = tr[j < c ? j : c - 1];
+      }
     }
 #pragma unroll
     for (int g = 0; g < GN; ++g) {
@@ -332,7 +360,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_codes_rows(
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int j = t + kTkThreads * e;
-        const float v = (float)acc[e][g];
+        const float v = acc[e][g];
         key[g][e] = tk_order_key(v);
         if (j < c) {
           lut[g * cp + j] = v;
@@ -352,19 +380,16 @@ __global__ __launch_bounds__(kTkThreads) void topk_codes_rows(
       atomicMin(&rng[g][0], klo[g]);
       atomicMax(&rng[g][1], khi[g]);
     }
-  const uint16_t* cg = codes + bk * n;
-  const unsigned cu = (unsigned)c;
-  if (CLDS && (n & 7) == 0) {  // 16-byte rows: eight codes a load
-    const uint4* src = reinterpret_cast<const uint4*>(cg);
-    uint4* dst = reinterpret_cast<uint4*>(cl);
-    const int n8 = (int)(n >> 3);
-    for (int i = t; i < n8; i += kTkThreads) {
-      const uint4 v = src[i];
-      dst[i] = v;
-      const unsigned w[4] = {v.x, v.y, v.z, v.w};
+  if (rows16) {  // eight codes a piece
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const unsigned lo = w[q] & 0xFFFFu, hi = w[q] >> 16;
+    for (int q = 0; q < kTkLdsCodes / 8 / kTkThreads; ++q) {
+      const int i = t + kTkThreads * q;
+      if (i >= n8) break;
+      const tk_u4 v = pre[q];
+      reinterpret_cast<tk_u4*>(cl)[i] = v;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const unsigned lo = v[h] & 0xFFFFu, hi = v[h] >> 16;
         atomicAdd(&cnt[lo < cu ? lo : cu], 1u);
         atomicAdd(&cnt[hi < cu ? hi : cu], 1u);
       }
@@ -711,54 +736,54 @@ __global__ __launch_bounds__(kTkThreads) void topk_codes_rows(
 }
 
 template <int GN, int E, bool CLDS>
-int topk_launch3(dim3 grid, hipStream_t s, const double* q64, const float* cb, int64_t hq,
+int topk_launch3(dim3 grid, hipStream_t s, const float* cb, int64_t hq,
                  int64_t hkv, int group, int nchunk, const uint16_t* codes, int64_t n, int c,
                  int64_t k, int32_t* idx, float* score, const TkLayout& ly) {
   auto kern = topk_codes_rows<GN, E, CLDS>;
   A2ATS_TRY(set_dynamic_lds(kern, ly.total));
-  return launch("topk_codes", kern, grid, dim3(kTkThreads), ly.total, s, q64, cb, hq, hkv, group,
+  return launch("topk_codes", kern, grid, dim3(kTkThreads), ly.total, s, cb, hq, hkv, group,
                 nchunk, codes, n, c, k, idx, score, ly);
 }
 
 template <int GN, int E>
-int topk_launch2(dim3 grid, hipStream_t s, const double* q64, const float* cb, int64_t hq,
+int topk_launch2(dim3 grid, hipStream_t s, const float* cb, int64_t hq,
                  int64_t hkv, int group, int nchunk, const uint16_t* codes, int64_t n, int c,
                  int64_t k, int32_t* idx, float* score) {
   const TkLayout ly = tk_layout(GN, c, n);
   if (ly.cl != 0xFFFFFFFFu)
-    return topk_launch3<GN, E, true>(grid, s, q64, cb, hq, hkv, group, nchunk, codes, n, c, k,
+    return topk_launch3<GN, E, true>(grid, s, cb, hq, hkv, group, nchunk, codes, n, c, k,
                                      idx, score, ly);
-  return topk_launch3<GN, E, false>(grid, s, q64, cb, hq, hkv, group, nchunk, codes, n, c, k,
+  return topk_launch3<GN, E, false>(grid, s, cb, hq, hkv, group, nchunk, codes, n, c, k,
                                     idx, score, ly);
 }
 
 // table entries a thread holds: C <= 1024, 2048, 4096
 template <int GN>
-int topk_launch(dim3 grid, hipStream_t s, const double* q64, const float* cb, int64_t hq,
+int topk_launch(dim3 grid, hipStream_t s, const float* cb, int64_t hq,
                 int64_t hkv, int group, int nchunk, const uint16_t* codes, int64_t n, int c,
                 int64_t k, int32_t* idx, float* score) {
   if (c <= kTkThreads)
-    return topk_launch2<GN, 1>(grid, s, q64, cb, hq, hkv, group, nchunk, codes, n, c, k, idx,
+    return topk_launch2<GN, 1>(grid, s, cb, hq, hkv, group, nchunk, codes, n, c, k, idx,
                                score);
   if (c <= 2 * kTkThreads)
-    return topk_launch2<GN, 2>(grid, s, q64, cb, hq, hkv, group, nchunk, codes, n, c, k, idx,
+    return topk_launch2<GN, 2>(grid, s, cb, hq, hkv, group, nchunk, codes, n, c, k, idx,
                                score);
-  return topk_launch2<GN, 4>(grid, s, q64, cb, hq, hkv, group, nchunk, codes, n, c, k, idx,
+  return topk_launch2<GN, 4>(grid, s, cb, hq, hkv, group, nchunk, codes, n, c, k, idx,
                              score);
 }
 
-int topk_dispatch(int gn, dim3 grid, hipStream_t s, const double* q64, const float* cb,
+int topk_dispatch(int gn, dim3 grid, hipStream_t s, const float* cb,
                   int64_t hq, int64_t hkv, int group, int nchunk, const uint16_t* codes,
                   int64_t n, int c, int64_t k, int32_t* idx, float* score) {
   switch (gn) {
     case 1:
-      return topk_launch<1>(grid, s, q64, cb, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
+      return topk_launch<1>(grid, s, cb, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
     case 2:
-      return topk_launch<2>(grid, s, q64, cb, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
+      return topk_launch<2>(grid, s, cb, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
     case 3:
-      return topk_launch<3>(grid, s, q64, cb, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
+      return topk_launch<3>(grid, s, cb, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
     default:
-      return topk_launch<4>(grid, s, q64, cb, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
+      return topk_launch<4>(grid, s, cb, hq, hkv, group, nchunk, codes, n, c, k, idx, score);
   }
 }
 
@@ -767,14 +792,11 @@ int topk_dispatch(int gn, dim3 grid, hipStream_t s, const double* q64, const flo
 
 using namespace a2ats;
 
-// The workspace: the queries in fp64, then the codebook transposed (bounded with hq >= hkv).
-static size_t topk_q64_bytes(int64_t batch, int64_t hq) {
-  return align_up((size_t)(batch * hq * kD) * sizeof(double));
-}
+// The workspace: the queries' tables [batch * hq][c] in fp32.
 
 extern "C" size_t a2ats_topk_workspace(int64_t batch, int64_t hq, int64_t c) {
   if (batch < 1 || hq < 1 || c < 1 || c > kTkMaxC) return 0;
-  return topk_q64_bytes(batch, hq) + align_up((size_t)(hq * c * kD) * sizeof(float));
+  return align_up((size_t)(batch * hq * c) * sizeof(float));
 }
 
 extern "C" int a2ats_topk_codes(const void* qb, int q_dtype, int64_t batch, int64_t hq,
@@ -789,24 +811,27 @@ extern "C" int a2ats_topk_codes(const void* qb, int q_dtype, int64_t batch, int6
   const int gn = group < 4 ? group : 4;
   const int nchunk = (group + gn - 1) / gn;
   if (batch * hkv * nchunk > 0x7FFFFFFF || batch * hq > 0x7FFFFFFF) return A2ATS_EINVAL;
+  if (hkv * ((c + kTbStrip - 1) / kTbStrip) * ((batch * group + kTbChunk - 1) / kTbChunk) >
+      0x7FFFFFFF)
+    return A2ATS_EINVAL;
   if (n == 0 || k == 0) return A2ATS_OK;
   if (!qb || !codes || !codebook || !idx) return A2ATS_EINVAL;
   if ((reinterpret_cast<uintptr_t>(qb) & 15) != 0) return A2ATS_EINVAL;
   if (!ws_ok(workspace, workspace_bytes, a2ats_topk_workspace(batch, hq, c)))
     return A2ATS_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  double* q64 = static_cast<double*>(workspace);
-  float* cbt = reinterpret_cast<float*>(static_cast<char*>(workspace) + topk_q64_bytes(batch, hq));
-  const int64_t quads = batch * hq * kD / 4;
-  const int nqw = (int)((quads + 255) / 256), njt = (int)((c + 63) / 64);
-  const dim3 pgrid((unsigned)(nqw + hkv * njt * 2));
+  float* tab = static_cast<float*>(workspace);
+  const int nstrip = (int)((c + kTbStrip - 1) / kTbStrip);
+  const int64_t nqch = (batch * group + kTbChunk - 1) / kTbChunk;
+  const dim3 tgrid((unsigned)(hkv * nstrip * nqch));
+  const dim3 tblock(kTbThreads);
   if (q_dtype == A2ATS_F32)
-    A2ATS_TRY(launch("topk_prep", topk_prep<A2ATS_F32>, pgrid, dim3(256), 0, s, qb, quads, nqw,
-                     codebook, (int)c, njt, q64, cbt));
+    A2ATS_TRY(launch("topk_table", topk_table<A2ATS_F32>, tgrid, tblock, 0, s, qb, codebook, batch,
+                     hq, group, (int)c, nstrip, (int)nqch, tab));
   else
-    A2ATS_TRY(launch("topk_prep", topk_prep<A2ATS_BF16>, pgrid, dim3(256), 0, s, qb, quads, nqw,
-                     codebook, (int)c, njt, q64, cbt));
+    A2ATS_TRY(launch("topk_table", topk_table<A2ATS_BF16>, tgrid, tblock, 0, s, qb, codebook, batch,
+                     hq, group, (int)c, nstrip, (int)nqch, tab));
   const dim3 grid((unsigned)(batch * hkv * nchunk));
-  return topk_dispatch(gn, grid, s, q64, cbt, hq, hkv, group, nchunk, codes, n, (int)c, k, idx,
+  return topk_dispatch(gn, grid, s, tab, hq, hkv, group, nchunk, codes, n, (int)c, k, idx,
                        score);
 }
