@@ -1162,6 +1162,32 @@ class TestTopkCodes:
         for k in (above, above + 1, above + 37, int(np.sum(s >= run[100]))):
             topk_case(qb, codes, cb, k)
 
+    def test_table_sum_order_under_cancellation(self):
+        # every table entry is a score (each code once, k = n); the terms of dimensions 64..127
+        # are those of 0..63 negated, with magnitudes over 80 binades, so each entry is the
+        # rounding left over by the fp64 sum in dimension order: another order (a pairwise tree,
+        # checked here on the CPU) changes most entries, and bit-exact scores pin the order
+        rng = np.random.default_rng(21)
+        c, batch, hq = 4096, 2, 4
+
+        def wide(shape):
+            return (rng.uniform(1, 2, shape) * np.exp2(rng.integers(-20, 21, shape))
+                    * rng.choice([-1, 1], shape)).astype(np.float32)
+        half = wide((1, c, 64))
+        cb = np.concatenate([half, half], axis=2)
+        qh = wide((batch, hq, 64))
+        qb = np.concatenate([qh, -qh], axis=2)
+        qb[:, :, 0] = 1.0
+        cb[0, :, 0] = rng.standard_normal(c).astype(np.float32)
+        terms = cb[0].astype(np.float64) * qb[0, 0].astype(np.float64)  # exact products
+        seq = np.zeros(c)
+        for a in range(128):
+            seq = seq + terms[:, a]
+        changed = np.sum(seq.astype(np.float32) != np.sum(terms, axis=1).astype(np.float32))
+        assert changed > c // 2, changed
+        codes = np.stack([rng.permutation(c) for _ in range(batch)])[:, None].astype(np.uint16)
+        topk_case(qb, codes, cb, c)
+
     @pytest.mark.parametrize("k", [1, 400, 1000, 4990])
     def test_infinite_scores(self, k):
         # scores beyond the fp32 range round to +inf or -inf, so the select bins by shifts of
