@@ -141,7 +141,8 @@ __device__ __forceinline__ float round_down_f(double x) {
 template <int SUB, bool BLEND>
 struct PqShared {
   half8 fa[kPqTiles][64];            // table operand, MFMA A order
-  unsigned fb[kPqTiles][64][2];      // bias operand (sub_dim 8; zero in lanes 32-63)
+  unsigned fb[kPqTiles][64][4];      // bias operand (sub_dim 8; zero in lanes 32-63 and in
+                                     // dwords 2-3, so one 16-byte read is the operand)
   half8 fq[BLEND ? kPqTiles : 1][64];  // unit-norm table operand (blend)
   // per row in fp64: v_j (c_j for the blend), then b_j / 2 and 1 / ||c_j|| (0 for a zero row;
   // blend).  The row stride (80 or 48 bytes) puts 8 consecutive rows' 16-byte reads in 8
@@ -279,8 +280,12 @@ __device__ __forceinline__ PqConsts pq_prep(const float* __restrict__ cb, int k,
     sh.fa[tile][r + 32] = h8(pkh(vl[0], vl[1]), pkh(vl[2], vl[3]), pkh(vl[4], vl[5]), pkh(vl[6], vl[7]));
     sh.fb[tile][r][0] = pkh(h1, h2);
     sh.fb[tile][r][1] = pkh(pm, z16);
+    sh.fb[tile][r][2] = 0u;
+    sh.fb[tile][r][3] = 0u;
     sh.fb[tile][r + 32][0] = 0u;
     sh.fb[tile][r + 32][1] = 0u;
+    sh.fb[tile][r + 32][2] = 0u;
+    sh.fb[tile][r + 32][3] = 0u;
   } else {
     // K slots, lanes 0-31: vh vl; lanes 32-63: h1 h2 pad-mark, then (fp32 inputs) vh again
     // against the inputs' lo parts
@@ -960,7 +965,7 @@ __global__ __launch_bounds__(kPqThreads, kPqWgPerCu) void pq_encode_blend(
 // Plain and H-weighted codes.  Each wave iteration: the 8 tiles' MFMAs folded into the slot
 // maxima (the table operand read from LDS at each tile pair), then the finalisation in
 // parts: the top two slots, the fp64 rescoring of the winning slot, the certificate, the rare
-// fp64 scans and the stores.  The inputs are fetched two iterations ahead; bf16 plain codes
+// fp64 scans and the stores.  The inputs are fetched one iteration ahead; bf16 plain codes
 // run three workgroups per CU (their registers fit).
 template <int DT, int SUB, int MODE>
 constexpr int pq_wg_per_cu() {
@@ -1004,8 +1009,7 @@ __global__ __launch_bounds__(kPqThreads, (pq_wg_per_cu<DT, SUB, MODE>())) void p
     if (h < heads && sel < n_sel) row = idx ? (int64_t)idx[h * n_sel + sel] : sel;
     return row >= 0 && row < n;
   };
-  // inputs are fetched two iterations ahead (nx_raw: the next, nn_raw: the one after)
-  Raw<DT, SUB> nx_raw[2], nn_raw[2];
+  Raw<DT, SUB> nx_raw[2];
   auto fetch = [&](int64_t h, int64_t g, Raw<DT, SUB> (&dst)[2]) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -1017,7 +1021,6 @@ __global__ __launch_bounds__(kPqThreads, (pq_wg_per_cu<DT, SUB, MODE>())) void p
   int64_t h_nx = h_cur, g_nx = g_cur;  // the iteration after the current one
   advance(h_nx, g_nx);
   fetch(h_cur, g_cur, nx_raw);  // in flight during the preparation
-  fetch(h_nx, g_nx, nn_raw);
 
   const PqConsts pc = pq_prep<SUB, MODE, DT>(cb, k, chol, sh);
   if (h_cur >= heads) return;  // no iteration for this wave (the preparation's barriers are past)
@@ -1031,7 +1034,7 @@ __global__ __launch_bounds__(kPqThreads, (pq_wg_per_cu<DT, SUB, MODE>())) void p
   // The table operand of a tile pair, read from LDS.
   struct PairOps {
     half8 a[2];
-    unsigned b0[2], b1[2];
+    half8 bb[2];
   };
   auto load_ops = [&](int tp) {
     PairOps o;
@@ -1039,8 +1042,7 @@ __global__ __launch_bounds__(kPqThreads, (pq_wg_per_cu<DT, SUB, MODE>())) void p
     for (int q = 0; q < 2; ++q) {
       o.a[q] = sh.fa[2 * tp + q][lds_lane];
       if constexpr (SUB == 8) {
-        o.b0[q] = sh.fb[2 * tp + q][lds_lane][0];
-        o.b1[q] = sh.fb[2 * tp + q][lds_lane][1];
+        o.bb[q] = *reinterpret_cast<const half8*>(&sh.fb[2 * tp + q][lds_lane][0]);
       }
     }
     return o;
@@ -1050,8 +1052,7 @@ __global__ __launch_bounds__(kPqThreads, (pq_wg_per_cu<DT, SUB, MODE>())) void p
                          f16v& s0, f16v& s1) {
     const half8 at = o.a[q];
     if constexpr (SUB == 8) {
-      const f16v cbias = __builtin_amdgcn_mfma_f32_32x32x16_f16(h8(o.b0[q], o.b1[q], 0u, 0u), Bb,
-                                                                zero, 0, 0, 0);
+      const f16v cbias = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.bb[q], Bb, zero, 0, 0, 0);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(at, b1[0], cbias, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(at, b1[1], cbias, 0, 0, 0);
       if constexpr (DT == A2ATS_F32) {
@@ -1196,22 +1197,16 @@ __global__ __launch_bounds__(kPqThreads, (pq_wg_per_cu<DT, SUB, MODE>())) void p
       lds_lane = lane + z;
     }
     const Raw<DT, SUB> xr[2] = {nx_raw[0], nx_raw[1]};
-    nx_raw[0] = nn_raw[0];
-    nx_raw[1] = nn_raw[1];
-    {
-      int64_t h2 = h_nx, g2 = g_nx;
-      advance(h2, g2);
-      fetch(h2, g2, nn_raw);  // two iterations ahead: stays in flight
-    }
     half8 B1[2], B2[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) make_b<DT, SUB>(xr[b], hh, e2, mk, B1[b], B2[b]);
+    xo_p = raw_sel<DT, SUB>(xr[0], xr[1], hh);
+    fetch(h_nx, g_nx, nx_raw);  // the next iteration's inputs stay in flight through this one
 #pragma unroll
     for (int tp = 0; tp < kPqTiles / 2; ++tp) {
       fold_pair(tp, load_ops(tp), B1, B2, m0, m1);
       __builtin_amdgcn_sched_barrier(0);  // one tile pair's accumulators live at a time
     }
-    xo_p = raw_sel<DT, SUB>(xr[0], xr[1], hh);
     ohead_p = h_cur;
     ok_p = locate(h_cur, g_cur, lr_own, orow_p);
     fin_a();
