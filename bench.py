@@ -192,6 +192,22 @@ class Ctx:
             t -= run(False)
         return t / reps
 
+    def fill_rate(self, nbytes):
+        """(flushed ms, steady ms) of a plain fill (torch's fill_) of nbytes: the write-only rate
+        this GPU reaches under the same timing, the yardstick of a pass whose traffic is almost
+        all writes (the reconstruct)."""
+        torch = self.torch
+        buf = torch.empty(nbytes // 4, dtype=torch.float32, device=self.dev)
+
+        def fill():
+            buf.fill_(1.0)
+
+        fill()
+        torch.cuda.synchronize()
+        out = (self.timed(fill, 5, flush=True), self.timed(fill, 10))
+        del buf
+        return out
+
     def copy_reference(self):
         """A plain elementwise kernel that reads and writes COPY_REF_BYTES: the scale of the
         FETCH_SIZE / WRITE_SIZE counters."""
@@ -436,6 +452,11 @@ def extra_workloads(ctx, steps, warmup):
         "reconstruct_hbm_frac": round(alg / (kr * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "algorithmic_bytes": alg, "blend_us": round(ms_b * 1e3, 2),
     }
+    fl_ms, fs_ms = ctx.fill_rate(tokens * 128 * 4)  # a plain fill of the output's bytes
+    res["decode"]["fill_output_bytes_flushed_hbm_frac"] = round(
+        tokens * 128 * 4 / (fl_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    res["decode"]["fill_output_bytes_steady_hbm_frac"] = round(
+        tokens * 128 * 4 / (fs_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
     log("decode %s" % res["decode"])
     # Far keys left unrotated (Eq. 12) with R_b on the query (Eq. 11): a decode step then
     # rewrites only the rows that cross the window edge plus the appended token, and rotates
@@ -575,6 +596,12 @@ def extra_workloads(ctx, steps, warmup):
         "reconstruct_kernels_us": {k: round(v[1] * 1e3, 2) for k, v in pr_r.items()},
         "pipeline_kernels_us": {k: round(v[1] * 1e3, 2) for k, v in ctx.profile(pipe, 3).items()},
     }
+    out_bytes = w.heads * w.n * 128 * 2
+    fl_ms, fs_ms = ctx.fill_rate(out_bytes)  # a plain fill of the reconstruct output's bytes
+    res["long_context"]["fill_output_bytes_flushed_hbm_frac"] = round(
+        out_bytes / (fl_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    res["long_context"]["fill_output_bytes_steady_hbm_frac"] = round(
+        out_bytes / (fs_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
     log("long_context %s" % res["long_context"])
     del kd, codes, out
     # The pages' default configuration: sub-vector codes (sub_dim 8, one shared 256-entry

@@ -19,9 +19,10 @@
 //   rope_gather  HBM-write-bound stream: each thread owns a fixed group of P pairs of the
 //                head dimension (P = 4 for fp32 output, 8 for bf16, so every store is 16 B),
 //                takes the far row's cos/sin for its pairs from a copy the workgroup stages
-//                in LDS, gathers the centroid from L2, rotates in fp64, rounds once to the
-//                output type, and writes with non-temporal stores (a far token with far rows
-//                prepared: its centroid's far row copied).  Work
+//                in LDS (with the codes and positions of all its work items), gathers the
+//                centroid from L2, rotates in fp64, rounds once to the output type, and
+//                writes with non-temporal stores (a far token with far rows prepared: its
+//                centroid's far row copied).  Work
 //                items are (batch, head, 64-token chunk); item k has head k % heads and the
 //                grid is a multiple of 8 * heads, so a workgroup always serves one head and,
 //                with 8 heads, each XCD (workgroups are dealt round-robin over the 8 XCDs)
@@ -42,11 +43,16 @@ constexpr int kHalf = kD / 2;
 constexpr int kChunkF32 = 64;   // tokens per work item, fp32 output
 constexpr int kChunkBf16 = 64;  // tokens per work item, bf16 output
 // Work items per workgroup (the grid is rounded to a multiple of 8 * heads and is at least
-// kGridMin).  A later item's loads wait, in order, behind the earlier item's stores (one
-// vector memory counter); measured on the long-context and decode workloads, four bf16
-// items (mostly copies of prepared far rows) and one fp32 item per workgroup are best (a
-// software-pipelined variant that issues the next item's loads before the current item's
-// stores needs more registers and measured slower).
+// kGridMin).  rope_gather stages the codes and positions of all of a workgroup's items in LDS
+// first, so that their reads, which miss every cache in a decode step, are in flight
+// together; eight items a workgroup, measured on the decode and long-context workloads after
+// a cache-evicting read (0.50 -> 0.61 and 0.36 -> 0.45-0.49 of HBM; back to back 0.67 ->
+// 0.66 and 0.55 -> 0.55-0.59).  pq_gather reads each item's codes in its loop: one fp32 and
+// four bf16 items a workgroup.  A later item's loads wait, in order, behind the earlier
+// item's stores (one vector memory counter); a software-pipelined variant that issues the
+// next item's row loads before the current item's stores needs more registers and measured
+// slower.
+constexpr int kGatherItems = 8;
 constexpr int kItemsPerWgF32 = 1;
 constexpr int kItemsPerWgBf16 = 4;
 constexpr int kGridMin = 256;
@@ -329,10 +335,41 @@ __global__ __launch_bounds__(256) void rope_gather(
       }
     }
   };
-  fetch(blockIdx.x, code, pos);
+  // the codes and positions of this workgroup's items (at most kGatherItems; more would be
+  // read in the loop), staged in LDS
+  __shared__ int s_code[kGatherItems][CH], s_pos[kGatherItems][CH];
+  for (int f = t; f < kGatherItems * CH; f += 256) {
+    const int k = f / CH, j = f % CH;
+    const int64_t item = (int64_t)blockIdx.x + (int64_t)k * gridDim.x;
+    const int64_t h = item % heads;
+    const int64_t rest = item / heads;
+    const int64_t b = rest / chunks;
+    const int64_t tok = (rest % chunks) * CH + j;
+    int cd = 0, ps = -1;
+    if (item < items && tok < n) {
+      cd = codes[(b * heads + h) * n + tok];
+      ps = positions[b * n + tok];
+    }
+    s_code[k][j] = cd;
+    s_pos[k][j] = ps;
+  }
+  __syncthreads();
+  auto take = [&](int k, int64_t item, int* cd, int* ps) {
+    if (k < kGatherItems) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        cd[u] = s_code[k][u * TOK + tk];
+        ps[u] = s_pos[k][u * TOK + tk];
+      }
+    } else {
+      fetch(item, cd, ps);
+    }
+  };
+  take(0, blockIdx.x, code, pos);
+  int kn = 0;  // the next item's slot
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
     int ncode[U], npos[U];
-    fetch(item + gridDim.x, ncode, npos);
+    take(++kn, item + gridDim.x, ncode, npos);
     const int64_t h = item % heads;
     const int64_t rest = item / heads;
     const int64_t b = rest / chunks;
@@ -395,7 +432,7 @@ __global__ __launch_bounds__(256) void rope_gather(
 
 // Sub-vector (product) codes: a token's key is the concatenation of d / SUB sub-centroids
 // of one shared codebook [k, SUB] ("A2ATS-adapted" docs, "What you get with the
-// defaults").  Same work items, grid and arithmetic as rope_gather; each thread reads the
+// defaults").  Same work items and arithmetic as rope_gather; each thread reads the
 // token's whole code row (d / SUB bytes), takes for each 4-dimension group of its pairs the
 // sub-centroid slice that covers it, and rotates and stores exactly as rope_gather does.  A
 // token with any code >= k, or a negative position, gets a row of NaN.
@@ -704,7 +741,7 @@ int reconstruct_launch(const uint16_t* codes, const int32_t* positions, int64_t 
   const int64_t items = batch * heads * ((n + chunk - 1) / chunk);
   // A multiple of 8 * heads workgroups, enough to fill the chip several times over.
   int64_t per = 8 * heads;
-  int64_t g = items / (out_dtype == A2ATS_F32 ? kItemsPerWgF32 : kItemsPerWgBf16);
+  int64_t g = items / kGatherItems;
   if (g < kGridMin) g = kGridMin;
   g = (g + per - 1) / per * per;
   if (g > items) g = items;
