@@ -45,14 +45,16 @@ constexpr int kChunkBf16 = 64;  // tokens per work item, bf16 output
 // Work items per workgroup (the grid is rounded to a multiple of 8 * heads and is at least
 // kGridMin).  rope_gather stages the codes and positions of all of a workgroup's items in LDS
 // first, so that their reads, which miss every cache in a decode step, are in flight
-// together; eight items a workgroup, measured on the decode and long-context workloads after
-// a cache-evicting read (0.50 -> 0.61 and 0.36 -> 0.45-0.49 of HBM; back to back 0.67 ->
-// 0.66 and 0.55 -> 0.55-0.59).  pq_gather reads each item's codes in its loop: one fp32 and
-// four bf16 items a workgroup.  A later item's loads wait, in order, behind the earlier
-// item's stores (one vector memory counter); a software-pipelined variant that issues the
-// next item's row loads before the current item's stores needs more registers and measured
-// slower.
-constexpr int kGatherItems = 8;
+// together; four items a workgroup, measured on the decode and long-context workloads after
+// a cache-evicting read (0.48-0.51 -> 0.62-0.66 and 0.36-0.41 -> 0.50 of HBM; back to back
+// within about 7% of the one-item grid either way; two and eight items measured lower).
+// pq_gather reads each item's code rows in
+// its loop (staging them the same way measured no faster on the sub-vector layer workload):
+// one fp32 and four bf16 items a workgroup.  A later item's loads wait, in order, behind the
+// earlier item's stores (one vector memory counter); a software-pipelined variant that
+// issues the next item's row loads before the current item's stores needs more registers and
+// measured slower.
+constexpr int kGatherItems = 4;
 constexpr int kItemsPerWgF32 = 1;
 constexpr int kItemsPerWgBf16 = 4;
 constexpr int kGridMin = 256;
