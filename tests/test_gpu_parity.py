@@ -1107,12 +1107,13 @@ def bf16_grid(x):
 class TestTopkCodes:
     # (batch, hq, hkv, n, c, k): every group size the kernel templates on (1..4), groups split
     # over workgroups (8 = 4 + 4, 5 = 4 + 1 partial), ragged token counts, partial codebook
-    # tiles, several tiles (c = 4096), and rows too long for LDS (n > 32768)
+    # tiles, several tiles (c = 4096), rows too long for LDS (n > 32768), and more of a key
+    # head's queries than one table workgroup takes (96): 100 = 96 + 4 and 320 = 3 x 96 + 32
     @pytest.mark.parametrize("batch,hq,hkv,n,c,k", [
         (2, 6, 2, 3000, 256, 300), (1, 3, 3, 1000, 1000, 1), (3, 4, 2, 4097, 1024, 4097),
         (1, 8, 2, 5000, 300, 777), (2, 4, 1, 2048, 4096, 1500), (1, 5, 1, 999, 64, 100),
         (1, 2, 1, 40000, 1024, 4000), (1, 1, 1, 1, 1, 1), (2, 2, 2, 65, 7, 64),
-        (1, 3, 1, 3000, 1500, 700)])
+        (1, 3, 1, 3000, 1500, 700), (50, 4, 2, 600, 300, 50), (40, 8, 1, 300, 100, 30)])
     @pytest.mark.parametrize("qdt", ["f32", "bf16"])
     def test_matches_oracle(self, batch, hq, hkv, n, c, k, qdt):
         rng = np.random.default_rng(batch * 1000 + hq * 100 + n + c)
