@@ -32,7 +32,8 @@
 //                       key fragments in registers, settle most of them and list the rest
 //                       for the rescan.
 //   enc_rescan_collect  second MFMA pass over the keys still open: collects every centroid
-//                       whose score could reach the best exact score.
+//                       whose score could reach the best exact score (per wave in LDS, then
+//                       one global atomic per key and work item to append them).
 //   enc_rescan_decide   fp64 over the collected candidates; fp64 over the whole codebook for
 //                       the keys listed for it (fp16 overflow, list overflow).
 #include "common.hpp"
@@ -1280,7 +1281,14 @@ __global__ __launch_bounds__(256) void enc_rescan_collect(
   tpi = (tpi + 1) & ~1;  // whole tile pairs (T is a multiple of kTPS)
   chunks = (T + tpi - 1) / tpi;
   const int64_t items = ngroups * chunks;
+  // candidates gathered per wave in LDS (one slot list per key column) and appended to the
+  // key's global list with one atomic per key and item, after the item's tiles
+  __shared__ int s_cand[4][32][kCandCap];
+  __shared__ unsigned s_cn[4][32];
+  const int wv = t >> 6;
   for (int64_t it = hsx.rank * 4 + (t >> 6); it < items; it += hsx.ranks * 4) {
+    if (lane < 32) s_cn[wv][lane] = 0u;
+    __builtin_amdgcn_wave_barrier();
     int64_t rest = 0;
     const int64_t head = find_head(cnt, hsx, unc_cap, pre, it / chunks, groups, &rest);
     const int chunk = (int)(it % chunks);
@@ -1321,8 +1329,8 @@ __global__ __launch_bounds__(256) void enc_rescan_collect(
         if (acc[r] >= thr) {
           const int j = tile * kRows + slot_row(r, hh);
           if (j < c) {
-            const unsigned pos = atomicAdd(&cand_n[head * unc_cap + slot], 1u);
-            if (pos < (unsigned)kCandCap) cand[(head * unc_cap + slot) * kCandCap + pos] = j;
+            const unsigned pos = atomicAdd(&s_cn[wv][col], 1u);
+            if (pos < (unsigned)kCandCap) s_cand[wv][col][pos] = j;
           }
         }
       }
@@ -1336,6 +1344,17 @@ __global__ __launch_bounds__(256) void enc_rescan_collect(
       if (q + 2 < nt) load_tile(tb + q + 2, fa0, acc0);
       score_tile(tb + q + 1, fa1, acc1);
     }
+    __builtin_amdgcn_wave_barrier();
+    if (live && hh == 0) {
+      const unsigned nl = s_cn[wv][col];
+      if (nl != 0u) {
+        const unsigned base = atomicAdd(&cand_n[head * unc_cap + slot], nl);
+        for (unsigned i = 0; i < nl && i < (unsigned)kCandCap && base + i < (unsigned)kCandCap;
+             ++i)
+          cand[(head * unc_cap + slot) * kCandCap + base + i] = s_cand[wv][col][i];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
