@@ -1413,9 +1413,11 @@ __device__ void full_scan_wave(const void* keys, int64_t n, int64_t c, const dou
   }
 }
 
-// One wave per open key: fp64 over its candidates (4 lanes per candidate, 16 at a time); a
-// key whose candidate list overflowed gets the full scan at once.  Then the keys the coarse
-// pass listed for the full scan (fp16-range keys, rescan list overflow).  Decision counts
+// Four open keys a wave: fp64 over each key's candidates (4 lanes per candidate, 4 candidates
+// of each key at a time), so that the keys' chains of dependent reads overlap (one key a wave
+// took 55 us on the large-codebook workload, four take 32 us); a key whose candidate list
+// overflowed gets the full scan, by the whole wave.  Then the keys the coarse pass listed for
+// the full scan (fp16-range keys, rescan list overflow).  Decision counts
 // are gathered per workgroup and added once, and only when statistics were asked for (a
 // same-address atomic per wave would serialise at the end of the pass).
 template <int DT>
@@ -1434,41 +1436,47 @@ __global__ __launch_bounds__(256) void enc_rescan_decide(
   auto per = [](int64_t m) { return m; };
   const int64_t total = head_prefix(cnt, hsx, unc_cap, pre, per);
   unsigned decided = 0, full_scans = 0;
-  for (int64_t e = hsx.rank * 4 + (t >> 6); e < total; e += hsx.ranks * 4) {
-    int64_t rest = 0;
-    const int64_t head = find_head(cnt, hsx, unc_cap, pre, e, per, &rest);
-    const int64_t slot = head * unc_cap + rest;
-    const UncEntry ue = unc[slot];
-    const unsigned nc = cand_n[slot];
-    if (lane == 0) cand_n[slot] = 0u;  // left cleared for the next run
-    if (nc > (unsigned)kCandCap) {
-      full_scan_wave<DT>(keys, n, c, v64, b64, chol, head, ue.row, ue.z2, codes, dist, kx[t >> 6],
-                         lane);
-      if (lane == 0) full_scans += 1;
-      continue;
+  // Four keys a wave, sixteen lanes a key (lanes 16 kq ..): four candidates a round, four
+  // lanes a candidate (lane quarter g of the dimensions), so that the four keys' chains of
+  // dependent reads (entry, candidate list, rows) overlap.
+  const int kq = lane >> 4, sub = (lane >> 2) & 3;
+  for (int64_t e0 = (hsx.rank * 4 + (t >> 6)) * 4; e0 < total; e0 += hsx.ranks * 16) {
+    const int64_t e = e0 + kq;
+    const bool valid = e < total;
+    int64_t rest = 0, head = 0, slot = 0;
+    UncEntry ue;
+    ue.row = 0;
+    ue.jbest = 0;
+    ue.z2 = 0.f;
+    unsigned nc = 0u;
+    if (valid) {
+      head = find_head(cnt, hsx, unc_cap, pre, e, per, &rest);
+      slot = head * unc_cap + rest;
+      ue = unc[slot];
+      nc = cand_n[slot];
     }
+    if (valid && (lane & 15) == 0) cand_n[slot] = 0u;  // left cleared for the next run
+    const bool full_key = valid && nc > (unsigned)kCandCap;
+    const bool dec = valid && !full_key;
     const int64_t off = ((int64_t)head * n + ue.row) * kD;
     // exact fp64 scores of the collected candidates and of jbest (the entry's score is only a
-    // lower bound of the best score, so jbest is scored here too)
-    double best = -INFINITY;
+    // lower bound of the best score, so jbest is scored here too); candidate nc is jbest
+    double best = -INFINITY, k2 = 0.0;
     int bj = 0x7FFFFFFF;
-    // ||k||^2 (for distances without a precomputed ||kL||^2) comes with the first batch
-    double k2 = 0.0;
-    for (unsigned q0 = 0; q0 <= nc; q0 += 16) {
-      const unsigned q = q0 + q16;
-      double s = -INFINITY, kk = 0.0;
-      int j = 0x7FFFFFFF;
-      const int jj = q < nc ? cand[slot * kCandCap + q] : ue.jbest;
+    for (unsigned q0 = 0;; q0 += 4) {
+      if (!__builtin_amdgcn_ballot_w64(dec && q0 <= nc)) break;
+      const unsigned q = q0 + sub;
+      const bool live = dec && q <= nc;
+      const int jj = dec && q < nc ? cand[slot * kCandCap + q] : ue.jbest;
       const int64_t vo = ((int64_t)head * c + jj) * kD;
       const double bjj = b64[(int64_t)head * c + jj];
+      double kk = 0.0;
       const double sj = plain ? coop_score_g<DT, 4>(keys, off, v32 + vo, bjj, g, &kk)
                               : coop_score_g<DT, 4>(keys, off, v64 + vo, bjj, g, &kk);
-      if (q <= nc) {
-        s = sj;
-        j = jj;
-      }
-      k2 = kk;
-      for (int o = 4; o < 64; o <<= 1) {
+      double s = live ? sj : -INFINITY;
+      int j = live ? jj : 0x7FFFFFFF;
+      if (q0 == 0) k2 = kk;  // ||k||^2, for distances without a precomputed ||kL||^2
+      for (int o = 4; o < 16; o <<= 1) {  // within the key's sixteen lanes
         const double os = __shfl_xor(s, o);
         const int oj = __shfl_xor(j, o);
         if (os > s || (os == s && oj < j)) {
@@ -1481,13 +1489,26 @@ __global__ __launch_bounds__(256) void enc_rescan_decide(
         bj = j;
       }
     }
-    if (lane == 0) {
+    if (dec && (lane & 15) == 0) {
       codes[(int64_t)head * n + ue.row] = (uint16_t)bj;
       if (dist) {
         const double z2 = ue.z2 >= 0.f ? (double)ue.z2 : k2;
         dist[(int64_t)head * n + ue.row] = (float)fmax(z2 - 2.0 * best, 0.0);
       }
-      decided += 1;
+    }
+    const unsigned long long dm = __builtin_amdgcn_ballot_w64(dec && (lane & 15) == 0);
+    if (lane == 0) decided += (unsigned)__popcll(dm);
+    // a key whose candidate list overflowed gets the full scan, by the whole wave
+    unsigned long long fm = __builtin_amdgcn_ballot_w64(full_key && (lane & 15) == 0);
+    while (fm) {
+      const int src = __ffsll((long long)fm) - 1;
+      fm &= fm - 1;
+      const int64_t fh = __shfl((int)head, src);
+      const int64_t frow = __shfl(ue.row, src);
+      const float fz2 = __shfl(ue.z2, src);
+      full_scan_wave<DT>(keys, n, c, v64, b64, chol, fh, frow, fz2, codes, dist, kx[t >> 6],
+                         lane);
+      if (lane == 0) full_scans += 1;
     }
   }
   const unsigned nfull = __hip_atomic_load(&cnt->full, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
