@@ -433,6 +433,24 @@ class TestReconstruct:
             check_rotation(got[m], ref, cb[hh][codes[b[m], hh, t[m]]].astype(np.float64), "f32",
                            "decode head %d" % hh)
 
+    @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+    def test_more_items_than_staged(self, out_dtype):
+        # one head of 1027 work items (64 tokens each): the grid of 256 workgroups gives some
+        # workgroup five items, one more than it stages in LDS (that one is read in the loop)
+        w = W["long_context"]
+        n = 1027 * 64
+        cb = synth.codebook(w.cfg, 1, 256)
+        codes = synth.uniform_codes(w.cfg, (1, 1, n), 256)
+        pos = np.arange(n, dtype=np.int32)[None]
+        dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+        out = kv.reconstruct(u16_to_dev(codes), torch.from_numpy(pos).to(DEV), f32_to_dev(cb),
+                             n - 1, 300, out_dtype=dt)
+        got = out[0, 0].cpu()
+        got = got.numpy() if out_dtype == "f32" else synth.bf16_bits_to_f32(bf16_to_np_bits(got))
+        ref = oracle_rows(codes[0, 0], pos[0], cb[0], n - 1, 300, 2048, 0)
+        check_rotation(got, ref, cb[0][codes[0, 0]].astype(np.float64), out_dtype,
+                       "five items a workgroup")
+
     def test_long_context_bf16_sampled(self):
         w = W["long_context"]
         cb = synth.codebook(w.cfg, w.heads, w.c)
