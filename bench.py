@@ -512,6 +512,7 @@ def extra_workloads(ctx, steps, warmup):
     torch.cuda.synchronize()
     ms_t = ctx.timed(topk_step, 20)
     ms_tf = ctx.timed(topk_step, 5, flush=True)
+    ms_tc = ctx.timed(lambda: kv.topk_codes(qtb, codes, cbd, kt), 20)  # both launches, no events
     pr_t = ctx.profile(topk_step, 5)
     tab_us = pr_t["topk_table"][1] * 1e3
     sel_us = pr_t["topk_codes"][1] * 1e3
@@ -523,6 +524,7 @@ def extra_workloads(ctx, steps, warmup):
         "workload": "32 sequences x 24 query heads over 8 key heads x 16384 codes, C=1024, "
                     "k=%d (10%%); far query rotation + table + top-K" % kt,
         "step_us": round(ms_t * 1e3, 2), "step_flushed_us": round(ms_tf * 1e3, 2),
+        "topk_call_us": round(ms_tc * 1e3, 2),
         "topk_kernel_us": round(kt_us, 2),
         "topk_table_us": round(tab_us, 2), "topk_select_us": round(sel_us, 2),
         "far_query_rope_us": round(pr_t["far_query_rope"][1] * 1e3, 2),
