@@ -130,6 +130,38 @@ class TestEncode:
         tie, st = run_encode(w, use_h=use_h)
         print("C=%d use_h=%s tie rate %.2e stats %s" % (c, use_h, tie, st[:5]))
 
+    @pytest.mark.parametrize("use_h", [False, True])
+    def test_candidate_list_overflow(self, use_h):
+        # 48 copies of one centroid (perturbed by 2^-26 relative, which fp32 mostly rounds
+        # away) and every third key drawn around it: those keys' rescan collects more
+        # candidates than a key's list holds (32), so the decide pass gives them the fp64 scan
+        # of the whole codebook; equal scores resolve to the lowest index
+        heads, n, c = 2, 600, 256
+        keys = synth.keys(131, heads, n, "f32")
+        cb = synth.codebook(131, heads, c)
+        rng = np.random.default_rng(131)
+        near = np.arange(0, n, 3)
+        for h in range(heads):
+            base = cb[h, 40].astype(np.float64)
+            for j in range(40, 88):
+                cb[h, j] = (base * (1.0 + rng.uniform(-2.0 ** -26, 2.0 ** -26, 128))).astype(np.float32)
+            noise = rng.standard_normal((len(near), 128)) * 0.05 * np.abs(base).mean()
+            keys.values[h, near] = (base + noise).astype(np.float32)
+        L = oracle_L(131, heads, 256) if use_h else None
+        stats = torch.zeros(8, dtype=torch.int32, device=DEV)
+        codes, dist = kv.encode(keys_to_dev(keys), f32_to_dev(cb), f32_to_dev(L) if use_h else None,
+                                want_dist=True, stats=stats)
+        codes, dist = u16_to_np(codes), dist.cpu().numpy()
+        for h in range(heads):
+            lh = L[h] if use_h else None
+            code, d1, d2 = oracle.assign_h(keys.values[h], cb[h], lh)
+            check_codes(codes[h], code, d1, d2, "overflow head %d" % h)
+            check_dist(dist[h], d1, z2_of(keys.values[h], lh), "overflow head %d" % h)
+        st = stats.cpu().numpy()
+        print("candidate overflow use_h=%s stats %s" % (use_h, st[:5]))
+        assert st[0] == heads * n and st[1] + st[2] + st[3] + st[4] == st[0]
+        assert st[4] > 0  # the full scans ran
+
     def test_large_codebook_fp32_keys(self):
         w = synth.Workload("bigc32", 171, 1, 900, 4097, "f32", m=512)
         tie, st = run_encode(w, use_h=True)
