@@ -385,6 +385,9 @@ def layer_step(ctx, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    # the replays above keep the step's 64 MB of keys in the 256 MB last-level cache; after a
+    # cache-evicting read each replay reads them from HBM
+    ms_flushed = ctx.timed(graph.replay, 5, flush=True)
 
     def step_seq():  # the same launches on one stream: per-kernel times without overlap
         prep_plain.prepare(cbd, None)
@@ -403,6 +406,8 @@ def layer_step(ctx, steps, warmup):
                     "fraction 0.1; step = split + plain encode of bulk rows || H-weighted encode "
                     "of retrieval rows + bf16 reconstruct",
         "step_ms_graph": round(ms, 5), "keys_per_s_graph": round(w.heads * w.n / (ms * 1e-3), 1),
+        "step_ms_graph_flushed": round(ms_flushed, 5),
+        "keys_per_s_graph_flushed": round(w.heads * w.n / (ms_flushed * 1e-3), 1),
         "step_ms_eager": round(ms_eager, 5),
         "coarse_plain_us": round(coarse_ms * 1e3, 2),
         "coarse_plain_mfma_frac": round(flops / (coarse_ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
