@@ -7,19 +7,21 @@
 // (u << 32) | (0xffffffff - index), so equal scores keep the lower index first and every
 // element has a distinct key.
 //
-// Kernels (5 launches, no host round trip, no workgroup waits for another, no global atomics):
+// Kernels (4 launches, no host round trip, no workgroup waits for another, no global atomics):
 //   sel_score    HBM-bound pass over the keys (8 lanes per key, 8 keys in flight per lane
 //                group): writes u, and the workgroup's 1024-bin histogram of a monotone
 //                binning of s/||q|| in [-1, 1] (LDS counts, written out whole; at most 64
-//                workgroups per head).
-//   sel_bstar    one workgroup per head: sums the partial histograms and finds, with a
-//                parallel prefix sum, the bin b* that holds the n_r-th largest score.
-//   sel_collect  pass over u: per block of 1024 scores, the count above b* and the keys in
-//                b* (into the block's own region of the candidate array).
+//                workgroups per head), with its 32 coarse counts of 32 bins each.
+//   sel_collect  pass over u: every workgroup first finds the bin b* that holds the n_r-th
+//                largest score from the partial histograms (coarse counts, then the fine
+//                counts of one coarse bin: 16 KB of reads), then, per block of 1024 scores,
+//                counts the keys above b* and writes those in b* (into the block's own
+//                region of the candidate array).
 //   sel_thresh   one workgroup per head: the exact n_r-th largest 64-bit key among the
-//                candidates (gathered into LDS in parallel, bitonic sort; radix select when
-//                they do not fit), the selected count of every block from the block-ordered
-//                copy, and every block's output offset (parallel prefix sums).
+//                candidates (gathered into LDS in parallel; rank counting, a bitonic sort,
+//                or a radix select when they do not fit), the selected count of every block
+//                from the block-ordered copy, and every block's output offset (parallel
+//                prefix sums).
 //   sel_scatter  pass over u: ordered compaction of the predicate key64 >= threshold into
 //                the retrieval and bulk index arrays.
 #include "common.hpp"
@@ -40,7 +42,8 @@ constexpr int kScoreThreads = 512;  // sel_score workgroup size
 constexpr int kBlock = 1024;        // scores per sel_collect / sel_scatter workgroup
 constexpr int kSortCap = 4096;      // candidates sorted in LDS; more take the radix path
 constexpr int kOffCap = 4096;       // blocks whose candidate offsets fit in LDS (n <= 4M)
-constexpr int kRankCap = 512;       // up to this many candidates: rank counting instead of a sort
+constexpr int kRankCap = 1024;      // up to this many candidates: rank counting instead of a sort
+constexpr int kCoarse = 32;         // coarse bins (of kBins / kCoarse bins each) for the b* search
 
 struct HeadInfo {
   float inv_scale;        // (kBins / 2) / ||q||, or 0 when q == 0
@@ -110,6 +113,7 @@ __global__ __launch_bounds__(kScoreThreads) void sel_score(const void* __restric
                                                            int64_t per_wg,
                                                            unsigned* __restrict__ scores,
                                                            unsigned* __restrict__ part,
+                                                           unsigned* __restrict__ coarse,
                                                            HeadInfo* __restrict__ info) {
   constexpr int kKeysPerRound = kScoreThreads / 8;
   constexpr int kWords = DT == A2ATS_BF16 ? 2 : 4;  // 16-byte words per lane and key
@@ -187,90 +191,120 @@ __global__ __launch_bounds__(kScoreThreads) void sel_score(const void* __restric
   uint4* dst = reinterpret_cast<uint4*>(part + ((int64_t)head * wg_per_head + wg) * kBins);
   const uint4* src = reinterpret_cast<const uint4*>(lh);
   for (int i = t; i < kBins / 4; i += kScoreThreads) dst[i] = src[i];
+  if (t < kBins / 4) {  // coarse counts: 8 lanes sum the 32 bins of one coarse bin
+    unsigned c = lh[4 * t] + lh[4 * t + 1] + lh[4 * t + 2] + lh[4 * t + 3];
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) c += __shfl_xor(c, o);
+    if ((t & 7) == 0) coarse[((int64_t)head * wg_per_head + wg) * kCoarse + (t >> 3)] = c;
+  }
 }
 
-// One workgroup of 1024 threads per head: total histogram over the sel_score partials, then
-// b*.  Thread t sums the 4 bins kBins-4(q+1) .. kBins-4q-1 (q = t % 256, taken in
-// descending order) over the partials w = t / 256 (mod 4), all its loads in flight at once;
-// the four groups meet in LDS and a prefix sum over the quads finds the bin of the n_r-th
-// largest.
-constexpr int kBstarThreads = 1024;
-__global__ __launch_bounds__(kBstarThreads) void sel_bstar(const unsigned* __restrict__ part,
-                                                           int wg_per_head, int64_t n_r,
-                                                           HeadInfo* __restrict__ info) {
-  constexpr int kGroups = kBstarThreads / (kBins / 4);
-  constexpr int kPerGroup = kScoreWgPerHead / kGroups;
-  const int head = blockIdx.x;
-  const int t = threadIdx.x;
-  const int q = t % (kBins / 4), g = t / (kBins / 4);
-  const uint4* p = reinterpret_cast<const uint4*>(part + (int64_t)head * wg_per_head * kBins) +
-                   (kBins / 4 - 1 - q);
-  uint4 v[kPerGroup];
+// Sum over the `rows` partial rows (stride `stride` words) of the 32 consecutive counts at
+// `base`, into s_out[32], by a workgroup of 256 threads: thread t loads the 4 counts 4 (t % 8)
+// .. of rows t / 8 and t / 8 + 32 (both loads in flight), lanes with the same t % 8 meet by
+// butterfly shuffles, the four waves in LDS.  Every thread must call it.
+__device__ __forceinline__ void sum_rows32(const unsigned* __restrict__ base, int64_t stride, int rows,
+                                           unsigned* s_out) {
+  static_assert(kScoreWgPerHead == 64, "two rows a thread");
+  __shared__ uint4 s_q[4][8];
+  const int t = threadIdx.x, lane = t & 63, q = t & 7, rw = t >> 3;
+  uint4 x[2];
 #pragma unroll
-  for (int k = 0; k < kPerGroup; ++k) {
-    const int w = g + kGroups * k;
-    v[k] = w < wg_per_head ? p[(int64_t)w * (kBins / 4)] : make_uint4(0u, 0u, 0u, 0u);
+  for (int k = 0; k < 2; ++k) {
+    const int r = rw + 32 * k;
+    x[k] = r < rows ? *reinterpret_cast<const uint4*>(base + (int64_t)r * stride + 4 * q)
+                    : make_uint4(0u, 0u, 0u, 0u);
   }
-  uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+  uint4 a = make_uint4(x[0].x + x[1].x, x[0].y + x[1].y, x[0].z + x[1].z, x[0].w + x[1].w);
 #pragma unroll
-  for (int k = 0; k < kPerGroup; ++k) {
-    acc.x += v[k].x; acc.y += v[k].y; acc.z += v[k].z; acc.w += v[k].w;
+  for (int o = 8; o < 64; o <<= 1) {
+    a.x += __shfl_xor(a.x, o);
+    a.y += __shfl_xor(a.y, o);
+    a.z += __shfl_xor(a.z, o);
+    a.w += __shfl_xor(a.w, o);
   }
-  __shared__ uint4 s_acc[kGroups - 1][kBins / 4];
-  if (g > 0) s_acc[g - 1][q] = acc;
+  if (lane < 8) s_q[t >> 6][lane] = a;
   __syncthreads();
-  if (g == 0) {
+  if (t < 8) {
+    uint4 m = s_q[0][t];
 #pragma unroll
-    for (int k = 0; k < kGroups - 1; ++k) {
-      const uint4 o = s_acc[k][q];
-      acc.x += o.x; acc.y += o.y; acc.z += o.z; acc.w += o.w;
+    for (int wv = 1; wv < 4; ++wv) {
+      const uint4 o = s_q[wv][t];
+      m.x += o.x; m.y += o.y; m.z += o.z; m.w += o.w;
     }
+    s_out[4 * t] = m.x;
+    s_out[4 * t + 1] = m.y;
+    s_out[4 * t + 2] = m.z;
+    s_out[4 * t + 3] = m.w;
   }
-  const unsigned c4[4] = {acc.w, acc.z, acc.y, acc.x};
-  const unsigned s4 = g == 0 ? c4[0] + c4[1] + c4[2] + c4[3] : 0u;
-  unsigned total;
-  unsigned cum = block_exclusive_scan<kBstarThreads>(s4, &total);
-  if (t == 0) {
-    info[head].n_r = (int)n_r;
-    info[head].thr = ~0ull;
-    if (n_r == 0) {
-      info[head].bstar = kBins;
-      info[head].count_above = 0;
-    }
-  }
-  if (g == 0 && n_r > 0 && cum < (unsigned)n_r && cum + s4 >= (unsigned)n_r) {
+  __syncthreads();
+}
+
+// In wave 0: the slot i of counts[32] (taken in descending order from slot 31) at which the
+// running sum, starting at `from`, reaches `need`; *pick = i and *before = the sum of the
+// slots above it.  Counts must reach need.
+__device__ __forceinline__ void pick_desc32(const unsigned* counts, unsigned from, unsigned need,
+                                            int* pick, unsigned* before) {
+  const int lane = threadIdx.x & 63;
+  const unsigned c = lane < 32 ? counts[31 - lane] : 0u;
+  unsigned incl = c;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (cum < (unsigned)n_r && cum + c4[i] >= (unsigned)n_r) {
-        info[head].bstar = kBins - 1 - 4 * q - i;
-        info[head].count_above = (int)cum;
-      }
-      cum += c4[i];
-    }
+  for (int o = 1; o < 32; o <<= 1) {
+    const unsigned u = __shfl_up(incl, o);
+    if (lane >= o) incl += u;
   }
+  const unsigned cum = from + incl - c;
+  if (lane < 32 && cum < need && cum + c >= need) {
+    *pick = 31 - lane;
+    *before = cum;
+  }
+}
+
+// b* of a head and the count above it, in every workgroup that needs them: the 32 coarse
+// counts (32 bins each) summed over the head's sel_score partials give the coarse bin of the
+// n_r-th largest, then its 32 fine counts the bin.  Two rounds of 8 KB of reads in place of
+// the whole 1024-bin partials.  b* = kBins (nothing selected) when n_r is 0.
+__device__ void bstar_two_level(const unsigned* __restrict__ part_head,
+                                const unsigned* __restrict__ coarse_head, int wg_per_head,
+                                int64_t n_r, int* bstar, int* count_above) {
+  __shared__ unsigned s_cnt[kCoarse];
+  __shared__ int s_pick;
+  __shared__ unsigned s_before;
+  const int t = threadIdx.x;
+  if (n_r == 0) {
+    *bstar = kBins;
+    *count_above = 0;
+    return;
+  }
+  sum_rows32(coarse_head, kCoarse, wg_per_head, s_cnt);
+  if (t < 64) pick_desc32(s_cnt, 0u, (unsigned)n_r, &s_pick, &s_before);
+  __syncthreads();
+  const int cbin = s_pick;
+  const unsigned above_c = s_before;
+  sum_rows32(part_head + cbin * (kBins / kCoarse), kBins, wg_per_head, s_cnt);
+  if (t < 64) pick_desc32(s_cnt, above_c, (unsigned)n_r, &s_pick, &s_before);
+  __syncthreads();
+  *bstar = cbin * (kBins / kCoarse) + s_pick;
+  *count_above = (int)s_before;
 }
 
 // Per block of kBlock scores: the count above b* and the keys in b*, appended to the
 // block's own region of the candidate array (no global atomics).
 __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ scores, int64_t n,
-                                                   int nblk, const HeadInfo* __restrict__ info,
+                                                   int nblk, const unsigned* __restrict__ part,
+                                                   const unsigned* __restrict__ coarse,
+                                                   int wg_per_head, int64_t n_r,
+                                                   HeadInfo* __restrict__ info,
                                                    unsigned* __restrict__ above_blk,
                                                    unsigned* __restrict__ cand_blk,
                                                    unsigned long long* __restrict__ cand) {
   const int head = blockIdx.x / nblk;
   const int blk = blockIdx.x % nblk;
   const int t = threadIdx.x;
-  const int bstar = info[head].bstar;
-  const float inv = info[head].inv_scale;
   const int64_t hoff = (int64_t)head * n;
   const int64_t i_begin = (int64_t)blk * kBlock;
   const int64_t i_end = i_begin + kBlock < n ? i_begin + kBlock : n;
-  unsigned above = 0;
-  __shared__ unsigned s_cnt;
-  __shared__ unsigned red[4];
-  if (t == 0) s_cnt = 0u;
-  __syncthreads();
-  const int64_t i0 = i_begin + 4 * t;  // 4 consecutive scores per thread
+  const int64_t i0 = i_begin + 4 * t;  // 4 consecutive scores per thread, read before b* is known
   unsigned uv[4];
   if (i0 + 3 < i_end && ((hoff + i0) & 3) == 0) {
     const uint4 q = *reinterpret_cast<const uint4*>(scores + hoff + i0);
@@ -279,6 +313,22 @@ __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ 
 #pragma unroll
     for (int k = 0; k < 4; ++k) uv[k] = (i0 + k < i_end) ? scores[hoff + i0 + k] : 0u;
   }
+  const float inv = info[head].inv_scale;
+  int bstar, count_above;
+  bstar_two_level(part + (int64_t)head * wg_per_head * kBins,
+                  coarse + (int64_t)head * wg_per_head * kCoarse, wg_per_head, n_r, &bstar,
+                  &count_above);
+  if (blk == 0 && t == 0) {  // every block of the head finds the same; block 0 records it
+    info[head].n_r = (int)n_r;
+    info[head].thr = ~0ull;
+    info[head].bstar = bstar;
+    info[head].count_above = count_above;
+  }
+  unsigned above = 0;
+  __shared__ unsigned s_cnt;
+  __shared__ unsigned red[4];
+  if (t == 0) s_cnt = 0u;
+  __syncthreads();
   unsigned mine = 0, local = 0;  // candidates of this thread, and their slot base
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -300,22 +350,27 @@ __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ 
   }
 }
 
-// One workgroup per head: the exact n_r-th largest 64-bit key among the candidates of bin
-// b*, the selected candidates per block, and the exclusive output offset of every block.
-// When the candidates fit (at most kSortCap of them, at most kOffCap blocks) they are
-// gathered into LDS in parallel (each thread finds the block of its slot by binary search
-// over the block offsets), kept in block order in `su` and sorted descending (bitonic) in
-// `sk`; otherwise a radix select runs over the candidate regions in global memory.
-__global__ __launch_bounds__(256) void sel_thresh(int64_t n, int nblk, HeadInfo* __restrict__ info,
-                                                  const unsigned* __restrict__ above_blk,
-                                                  const unsigned* __restrict__ cand_blk,
-                                                  const unsigned long long* __restrict__ cand,
-                                                  unsigned* __restrict__ blk_off) {
+// One workgroup of 1024 threads per head: the exact n_r-th largest 64-bit key among the
+// candidates of bin b*, the selected candidates per block, and the exclusive output offset of
+// every block.  When the candidates fit (at most kSortCap of them, at most kOffCap blocks)
+// they are gathered into LDS in parallel (each thread finds the block of its slot by binary
+// search over the block offsets), kept in block order in `su`; up to kRankCap of them each
+// candidate counts the larger ones (1, 2 or 4 threads a candidate, each over its part of the
+// list), more are sorted descending (bitonic) in `sk`.  Otherwise a radix select runs over
+// the candidate regions in global memory.
+constexpr int kThreshThreads = 1024;
+__global__ __launch_bounds__(kThreshThreads) void sel_thresh(int64_t n, int nblk,
+                                                             HeadInfo* __restrict__ info,
+                                                             const unsigned* __restrict__ above_blk,
+                                                             const unsigned* __restrict__ cand_blk,
+                                                             const unsigned long long* __restrict__ cand,
+                                                             unsigned* __restrict__ blk_off) {
+  constexpr int NT = kThreshThreads;
   const int head = blockIdx.x;
   const int t = threadIdx.x;
   const int64_t hoff = (int64_t)head * n;
   const int64_t cbase = (int64_t)head * nblk;
-  // the first 256 blocks' above-b* counts are fetched up front, beside the head's record
+  // the first NT blocks' above-b* counts are fetched up front, beside the head's record
   const unsigned above0 = t < nblk ? above_blk[cbase + t] : 0u;
   const int r = info[head].n_r - info[head].count_above;  // 1-based rank inside bin b*
   __shared__ unsigned long long sk[kSortCap];
@@ -323,11 +378,11 @@ __global__ __launch_bounds__(256) void sel_thresh(int64_t n, int nblk, HeadInfo*
   __shared__ unsigned s_off[kOffCap + 1];
   // candidate count and per-block candidate offsets
   unsigned n_cand = 0;
-  for (int b0 = 0; b0 < nblk; b0 += 256) {
+  for (int b0 = 0; b0 < nblk; b0 += NT) {
     const int b = b0 + t;
     const unsigned cb = b < nblk ? cand_blk[cbase + b] : 0u;
     unsigned chunk;
-    const unsigned ex = block_exclusive_scan(cb, &chunk);
+    const unsigned ex = block_exclusive_scan<NT>(cb, &chunk);
     if (b < nblk && b < kOffCap) s_off[b] = n_cand + ex;
     n_cand += chunk;
   }
@@ -341,7 +396,7 @@ __global__ __launch_bounds__(256) void sel_thresh(int64_t n, int nblk, HeadInfo*
   if (t == 0) s_remaining = (unsigned)(r > 0 ? r : 0);
   if (r > 0 && fits) {
     const bool by_rank = n_cand <= (unsigned)kRankCap;
-    for (int j = t; j < (int)n_cand; j += 256) {
+    for (int j = t; j < (int)n_cand; j += NT) {
       int lo = 0, hi = nblk - 1;  // the last block whose offset is <= j holds slot j
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -353,44 +408,38 @@ __global__ __launch_bounds__(256) void sel_thresh(int64_t n, int nblk, HeadInfo*
       if (!by_rank) sk[j] = v;
     }
     if (by_rank) {
-      // few candidates: each one counts the larger keys (all distinct); rank r - 1 is it
+      // P threads a candidate, each counting the larger keys (all distinct) in its part of
+      // the list; the candidate with r - 1 larger ones is it.  Slots past n_cand hold 0,
+      // which counts nothing.
+      const int lp = n_cand <= (unsigned)(NT / 4) ? 2 : (n_cand <= (unsigned)(NT / 2) ? 1 : 0);
+      const int P = 1 << lp;
+      const int L = (((int)n_cand + P - 1) / P + 7) & ~7;
+      for (int i = (int)n_cand + t; i < P * L; i += NT) su[i] = 0ull;
       __syncthreads();
-      constexpr int J = kRankCap / 256;
-      unsigned long long mine[J];
-      unsigned rank[J];
-#pragma unroll
-      for (int k = 0; k < J; ++k) {
-        const int j = t + 256 * k;
-        mine[k] = j < (int)n_cand ? su[j] : ~0ull;
-        rank[k] = 0u;
-      }
-      // 8 independent LDS reads per round (slots past n_cand hold 0, which counts nothing)
-      const int n_pad = ((int)n_cand + 7) & ~7;
-      for (int i = (int)n_cand + t; i < n_pad; i += 256) su[i] = 0ull;
-      __syncthreads();
-      for (int i = 0; i < n_pad; i += 8) {
+      const int c = t >> lp, q = t & (P - 1);
+      const unsigned long long mine = c < (int)n_cand ? su[c] : ~0ull;
+      unsigned rank = 0;
+      for (int i = q * L; i < q * L + L; i += 8) {
         unsigned long long x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = su[i + e];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-#pragma unroll
-          for (int k = 0; k < J; ++k) rank[k] += x[e] > mine[k] ? 1u : 0u;
+        for (int e = 0; e < 8; ++e) rank += x[e] > mine ? 1u : 0u;
       }
-#pragma unroll
-      for (int k = 0; k < J; ++k)
-        if (t + 256 * k < (int)n_cand && rank[k] == (unsigned)(r - 1)) s_prefix = mine[k];
+      if (P > 1) rank += __shfl_xor(rank, 1);
+      if (P > 2) rank += __shfl_xor(rank, 2);
+      if (c < (int)n_cand && q == 0 && rank == (unsigned)(r - 1)) s_prefix = mine;
       __syncthreads();
       prefix = s_prefix;
     } else {
       int P = 1;
       while (P < (int)n_cand) P <<= 1;
-      for (int i = (int)n_cand + t; i < P; i += 256) sk[i] = 0ull;
+      for (int i = (int)n_cand + t; i < P; i += NT) sk[i] = 0ull;
       __syncthreads();
       // bitonic sort, descending; every thread takes whole compare-exchange pairs
       for (int k = 2; k <= P; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
-          for (int q = t; q < P / 2; q += 256) {
+          for (int q = t; q < P / 2; q += NT) {
             const int i = (q / j) * 2 * j + (q % j);
             const int l = i + j;
             const unsigned long long a = sk[i], b = sk[l];
@@ -409,9 +458,9 @@ __global__ __launch_bounds__(256) void sel_thresh(int64_t n, int nblk, HeadInfo*
     __syncthreads();
     // radix select over the per-block candidate regions, 8 bits at a time
     for (int shift = 56; shift >= 0; shift -= 8) {
-      dh[t] = 0u;
+      if (t < 256) dh[t] = 0u;
       __syncthreads();
-      for (int b = t; b < nblk; b += 256) {
+      for (int b = t; b < nblk; b += NT) {
         const unsigned cb = cand_blk[cbase + b];
         for (unsigned i = 0; i < cb; ++i) {
           const unsigned long long kv = cand[hoff + (int64_t)b * kBlock + i];
@@ -419,12 +468,12 @@ __global__ __launch_bounds__(256) void sel_thresh(int64_t n, int nblk, HeadInfo*
         }
       }
       __syncthreads();
-      {  // digit holding the rem-th largest: thread t takes digit 255 - t (descending)
+      {  // digit holding the rem-th largest: thread t < 256 takes digit 255 - t (descending)
         const unsigned rem = s_remaining;
-        const unsigned cdg = dh[255 - t];
+        const unsigned cdg = t < 256 ? dh[255 - t] : 0u;
         unsigned all;
-        const unsigned cum = block_exclusive_scan(cdg, &all);
-        if (cum < rem && cum + cdg >= rem) {
+        const unsigned cum = block_exclusive_scan<NT>(cdg, &all);
+        if (t < 256 && cum < rem && cum + cdg >= rem) {
           s_remaining = rem - cum;
           s_prefix = prefix | ((unsigned long long)(255 - t) << shift);
         }
@@ -439,7 +488,7 @@ __global__ __launch_bounds__(256) void sel_thresh(int64_t n, int nblk, HeadInfo*
   if (t == 0) info[head].thr = thr;
   // per block: keys above b* plus its selected candidates, then exclusive offsets
   unsigned run = 0;
-  for (int b0 = 0; b0 < nblk; b0 += 256) {
+  for (int b0 = 0; b0 < nblk; b0 += NT) {
     const int b = b0 + t;
     unsigned cnt = 0;
     if (b < nblk) {
@@ -453,7 +502,7 @@ __global__ __launch_bounds__(256) void sel_thresh(int64_t n, int nblk, HeadInfo*
       }
     }
     unsigned chunk;
-    const unsigned ex = block_exclusive_scan(cnt, &chunk);
+    const unsigned ex = block_exclusive_scan<NT>(cnt, &chunk);
     if (b < nblk) blk_off[cbase + b] = run + ex;
     run += chunk;
   }
@@ -527,6 +576,7 @@ __global__ __launch_bounds__(256) void sel_scatter(const unsigned* __restrict__ 
 struct SelLayout {
   HeadInfo* info;
   unsigned* part;
+  unsigned* coarse;
   unsigned* scores;
   unsigned long long* cand;
   unsigned* above_blk;
@@ -552,6 +602,7 @@ SelLayout carve(void* ws, int64_t heads, int64_t n) {
   int64_t wgph, per;
   score_split(n, &wgph, &per);
   L.part = c.take<unsigned>((size_t)(heads * wgph * kBins));
+  L.coarse = c.take<unsigned>((size_t)(heads * wgph * kCoarse));
   L.scores = c.take<unsigned>((size_t)heads * n);
   L.cand = c.take<unsigned long long>((size_t)heads * n);
   L.above_blk = c.take<unsigned>((size_t)heads * nblk);
@@ -593,17 +644,16 @@ extern "C" int a2ats_select_retrieval(const void* keys, int keys_dtype, int64_t 
   if (keys_dtype == A2ATS_BF16)
     A2ATS_TRY(launch("select_score", sel_score<A2ATS_BF16>, dim3((unsigned)(heads * wg_per_head)),
                      dim3(kScoreThreads), 0, s, keys, query, n, (int)wg_per_head, per_wg, L.scores, L.part,
-                     L.info));
+                     L.coarse, L.info));
   else
     A2ATS_TRY(launch("select_score", sel_score<A2ATS_F32>, dim3((unsigned)(heads * wg_per_head)),
                      dim3(kScoreThreads), 0, s, keys, query, n, (int)wg_per_head, per_wg, L.scores, L.part,
-                     L.info));
-  A2ATS_TRY(launch("select_bstar", sel_bstar, dim3((unsigned)heads), dim3(kBstarThreads), 0, s, L.part,
-                   (int)wg_per_head, n_r, L.info));
+                     L.coarse, L.info));
   A2ATS_TRY(launch("select_collect", sel_collect, dim3((unsigned)(heads * nblk)), dim3(256), 0, s,
-                   L.scores, n, (int)nblk, L.info, L.above_blk, L.cand_blk, L.cand));
-  A2ATS_TRY(launch("select_thresh", sel_thresh, dim3((unsigned)heads), dim3(256), 0, s, n, (int)nblk,
-                   L.info, L.above_blk, L.cand_blk, L.cand, L.blk_off));
+                   L.scores, n, (int)nblk, L.part, L.coarse, (int)wg_per_head, n_r, L.info,
+                   L.above_blk, L.cand_blk, L.cand));
+  A2ATS_TRY(launch("select_thresh", sel_thresh, dim3((unsigned)heads), dim3(kThreshThreads), 0, s, n,
+                   (int)nblk, L.info, L.above_blk, L.cand_blk, L.cand, L.blk_off));
   return launch("select_scatter", sel_scatter, dim3((unsigned)(heads * nblk)), dim3(256), 0, s,
                 L.scores, n, (int)nblk, L.info, L.blk_off, retrieval_idx, bulk_idx);
 }
