@@ -396,19 +396,18 @@ class TestSelectRetrieval:
         nr = oracle.retrieval_count(n, f)
         assert np.array_equal(ret.cpu().numpy()[0], np.arange(nr))
 
-    @pytest.mark.parametrize("n", [100_001, 262_144, 262_145, 300_000])
-    def test_around_the_one_launch_limit(self, n):
-        # up to 262144 keys a head one more launch finishes the split, one workgroup per 32768
-        # keys (100001: a ragged head of unaligned rows; 262144: eight workgroups and over 512
-        # keys in the cut's bin); above it the five-launch path, its candidates sorted in LDS
+    @pytest.mark.parametrize("n", [100_001, 262_144, 300_000])
+    def test_large_heads(self, n):
+        # 100001: a ragged head of unaligned rows; 262144 and 300000: 500 to 1000 keys in the
+        # cut's bin (rank counting one thread a candidate)
         keys = synth.keys(145, 1, n, "bf16")
         band = run_split(keys, keys.values[:, -1].copy(), 0.05, "n=%d" % n)
         print("n=%d: %d indices in the tie band" % (n, band))
 
     @pytest.mark.parametrize("n", [40_000, 300_000])
     def test_tie_group_and_identical_keys_both_paths(self, n):
-        # a tie group of 2500 around the cut, and a head of identical keys (all ties, lowest
-        # indices win), on the one-launch finish and on the five-launch path
+        # a tie group of 2500 around the cut (sorted in LDS), and a head of identical keys (all
+        # ties, lowest indices win; a radix select over the candidates in global memory)
         keys = synth.keys(146, 2, n, "f32")
         k0 = keys.values[0, 0].copy()
         keys.values[0, :2500] = k0[None, :] * (2.0 ** (np.arange(2500) % 8 - 4))[:, None]
