@@ -201,21 +201,25 @@ __global__ __launch_bounds__(kScoreThreads) void sel_score(const void* __restric
 
 // Sum over the `rows` partial rows (stride `stride` words) of the 32 consecutive counts at
 // `base`, into s_out[32], by a workgroup of 256 threads: thread t loads the 4 counts 4 (t % 8)
-// .. of rows t / 8 and t / 8 + 32 (both loads in flight), lanes with the same t % 8 meet by
-// butterfly shuffles, the four waves in LDS.  Every thread must call it.
+// .. of rows t / 8, t / 8 + 32, ... (all its loads in flight), lanes with the same t % 8 meet
+// by butterfly shuffles, the four waves in LDS.  Every thread must call it.
 __device__ __forceinline__ void sum_rows32(const unsigned* __restrict__ base, int64_t stride, int rows,
                                            unsigned* s_out) {
-  static_assert(kScoreWgPerHead == 64, "two rows a thread");
+  constexpr int kRowsPerThread = (kScoreWgPerHead + 31) / 32;
   __shared__ uint4 s_q[4][8];
   const int t = threadIdx.x, lane = t & 63, q = t & 7, rw = t >> 3;
-  uint4 x[2];
+  uint4 x[kRowsPerThread];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < kRowsPerThread; ++k) {
     const int r = rw + 32 * k;
     x[k] = r < rows ? *reinterpret_cast<const uint4*>(base + (int64_t)r * stride + 4 * q)
                     : make_uint4(0u, 0u, 0u, 0u);
   }
-  uint4 a = make_uint4(x[0].x + x[1].x, x[0].y + x[1].y, x[0].z + x[1].z, x[0].w + x[1].w);
+  uint4 a = x[0];
+#pragma unroll
+  for (int k = 1; k < kRowsPerThread; ++k) {
+    a.x += x[k].x; a.y += x[k].y; a.z += x[k].z; a.w += x[k].w;
+  }
 #pragma unroll
   for (int o = 8; o < 64; o <<= 1) {
     a.x += __shfl_xor(a.x, o);
