@@ -800,7 +800,7 @@ def _algorithmic():
     return {
         ("encode_stress", "enc_coarse"): ("the MFMA pass of the H-weighted encode with distances",
                                           enc, 2.0 * 8 * 131072 * 4096 * D, "kv_cache_vector_windowed_amd/csrc/encode.hip"),
-        ("long_context", "sel_"): ("the five kernels of the retrieval split, per call", split, None,
+        ("long_context", "sel_"): ("the four kernels of the retrieval split, per call", split, None,
                                    "kv_cache_vector_windowed_amd/csrc/select.hip"),
         ("long_context", "rope_gather"): ("the bf16 reconstruct gather", rec_lc, None,
                                           "kv_cache_vector_windowed_amd/csrc/reconstruct.hip"),
@@ -863,7 +863,7 @@ def pmc_summarize(root, command):
         for tag, d in by_wl[wl]:
             rows = _pmc_dispatches(d)
             ref = [v for n, _, v in rows if "neg" in n.lower()]
-            # one launch = all dispatches of the pattern between two calls: the split is five
+            # one launch = all dispatches of the pattern between two calls: the split is four
             # kernels, summed per call (calls follow each other, three of them)
             mine = [(n, v) for n, _, v in rows if pat in n]
             if not mine:

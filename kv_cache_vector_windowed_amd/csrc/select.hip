@@ -8,7 +8,7 @@
 // element has a distinct key.
 //
 // Kernels (4 launches, no host round trip, no workgroup waits for another, no global atomics):
-//   sel_score    HBM-bound pass over the keys (8 lanes per key, 8 keys in flight per lane
+//   sel_score    HBM-bound pass over the keys (8 lanes per key, 4 keys in flight per lane
 //                group): writes u, and the workgroup's 1024-bin histogram of a monotone
 //                binning of s/||q|| in [-1, 1] (LDS counts, written out whole; at most 64
 //                workgroups per head), with its 32 coarse counts of 32 bins each.
