@@ -8,7 +8,7 @@
 // element has a distinct key.
 //
 // Kernels (4 launches, no host round trip, no workgroup waits for another, no global atomics):
-//   sel_score    HBM-bound pass over the keys (8 lanes per key, 4 keys in flight per lane
+//   sel_score    HBM-bound pass over the keys (8 lanes per key, 2 keys in flight per lane
 //                group): writes u, and the workgroup's 1024-bin histogram of a monotone
 //                binning of s/||q|| in [-1, 1] (LDS counts, written out whole; at most 64
 //                workgroups per head), with its 32 coarse counts of 32 bins each.
@@ -37,7 +37,7 @@ constexpr int kBins = 1024;
 constexpr float kHalfBins = 512.0f;
 constexpr int kScoreWgPerHead = 64; // at most this many sel_score workgroups (partial histograms) per head
 constexpr int kScoreMinKeys = 512;  // and at least this many keys per workgroup
-constexpr int kScoreUnroll = 4;     // keys in flight per 8-lane group
+constexpr int kScoreUnroll = 2;     // keys in flight per 8-lane group
 constexpr int kScoreThreads = 512;  // sel_score workgroup size
 constexpr int kBlock = 1024;        // scores per sel_collect / sel_scatter workgroup
 constexpr int kSortCap = 4096;      // candidates sorted in LDS; more take the radix path
