@@ -359,8 +359,8 @@ __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ 
 // every block.  When the candidates fit (at most kSortCap of them, at most kOffCap blocks)
 // they are gathered into LDS in parallel (each thread finds the block of its slot by binary
 // search over the block offsets), kept in block order in `su`; up to kRankCap of them each
-// candidate counts the larger ones (1, 2 or 4 threads a candidate, each over its part of the
-// list), more are sorted descending (bitonic) in `sk`.  Otherwise a radix select runs over
+// candidate counts the larger ones (pairs of candidates, up to 8 threads a pair, each over its
+// part of the list), more are sorted descending (bitonic) in `sk`.  Otherwise a radix select runs over
 // the candidate regions in global memory.
 constexpr int kThreshThreads = 1024;
 __global__ __launch_bounds__(kThreshThreads) void sel_thresh(int64_t n, int nblk,
@@ -412,27 +412,44 @@ __global__ __launch_bounds__(kThreshThreads) void sel_thresh(int64_t n, int nblk
       if (!by_rank) sk[j] = v;
     }
     if (by_rank) {
-      // P threads a candidate, each counting the larger keys (all distinct) in its part of
-      // the list; the candidate with r - 1 larger ones is it.  Slots past n_cand hold 0,
-      // which counts nothing.
-      const int lp = n_cand <= (unsigned)(NT / 4) ? 2 : (n_cand <= (unsigned)(NT / 2) ? 1 : 0);
+      // Candidates in pairs (2c, 2c + 1), P threads a pair (at most 8), each counting the
+      // larger keys (all distinct) in its part of the list for both; the candidate with r - 1
+      // larger ones is it.  Slots past n_cand hold 0, which counts nothing.
+      const unsigned pairs = (n_cand + 1u) / 2u;
+      int lp = 0;
+      while (lp < 3 && (pairs << (lp + 1)) <= (unsigned)NT) ++lp;
       const int P = 1 << lp;
       const int L = (((int)n_cand + P - 1) / P + 7) & ~7;
       for (int i = (int)n_cand + t; i < P * L; i += NT) su[i] = 0ull;
       __syncthreads();
       const int c = t >> lp, q = t & (P - 1);
-      const unsigned long long mine = c < (int)n_cand ? su[c] : ~0ull;
-      unsigned rank = 0;
-      for (int i = q * L; i < q * L + L; i += 8) {
-        unsigned long long x[8];
+      const bool two = 2 * c + 1 < (int)n_cand;
+      unsigned long long m0 = ~0ull, m1 = ~0ull;
+      unsigned r0 = 0, r1 = 0;
+      if (c < (int)pairs) {  // waves past the last pair skip the loop
+        m0 = su[2 * c];
+        m1 = two ? su[2 * c + 1] : ~0ull;
+        for (int i = q * L; i < q * L + L; i += 8) {
+          unsigned long long x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = su[i + e];
+          for (int e = 0; e < 8; ++e) x[e] = su[i + e];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) rank += x[e] > mine ? 1u : 0u;
+          for (int e = 0; e < 8; ++e) {
+            r0 += x[e] > m0 ? 1u : 0u;
+            r1 += x[e] > m1 ? 1u : 0u;
+          }
+        }
       }
-      if (P > 1) rank += __shfl_xor(rank, 1);
-      if (P > 2) rank += __shfl_xor(rank, 2);
-      if (c < (int)n_cand && q == 0 && rank == (unsigned)(r - 1)) s_prefix = mine;
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1)
+        if (o < P) {
+          r0 += __shfl_xor(r0, o);
+          r1 += __shfl_xor(r1, o);
+        }
+      if (c < (int)pairs && q == 0) {
+        if (r0 == (unsigned)(r - 1)) s_prefix = m0;
+        if (two && r1 == (unsigned)(r - 1)) s_prefix = m1;
+      }
       __syncthreads();
       prefix = s_prefix;
     } else {
