@@ -292,8 +292,10 @@ __device__ void bstar_two_level(const unsigned* __restrict__ part_head,
   *count_above = (int)s_before;
 }
 
-// Per block of kBlock scores: the count above b* and the keys in b*, appended to the
-// block's own region of the candidate array (no global atomics).
+// Per block of kBlock scores: b* (every workgroup finds it from the partial histograms, its
+// scores' reads already in flight; block 0 of the head records it), then the count above b*
+// and the keys in b*, appended to the block's own region of the candidate array (no global
+// atomics).
 __global__ __launch_bounds__(256) void sel_collect(const unsigned* __restrict__ scores, int64_t n,
                                                    int nblk, const unsigned* __restrict__ part,
                                                    const unsigned* __restrict__ coarse,
