@@ -343,22 +343,38 @@ __global__ __launch_bounds__(256) void enc_prep_frag(const double* __restrict__ 
     for (int64_t k = g; k < nclr0; k += stride) clr0[k] = 0u;
     for (int64_t k = g; k < nclr1; k += stride) clr1[k] = 0u;
   }
-  const HeadScale hs = head_scale_wg(part_a, head, nwg_a);
-  if (blockIdx.x == 0 && t == 0) hsc[head] = hs;  // for the later passes
   const int64_t rows = (int64_t)T * kRows;
   const int64_t rid = (int64_t)blockIdx.x * 16 + t / 16;  // padded row (or L^T row after rows)
   const int chunk = t % 16;                                // k = 8 chunk .. 8 chunk + 7
   const int s = chunk / 2, hh = chunk % 2;
+  const bool is_row = rid < rows;
+  const bool is_l = !is_row && want_l && rid < rows + kD;
+  // this thread's inputs are read before the head's scales are reduced, so that both reads
+  // are in flight together (the scales only multiply them)
+  double vin[8];
+  double bin = 0.0;
+  if (is_row) {
+    const int64_t j = rid;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vin[e] = (j < c) ? v64[((int64_t)head * c + j) * kD + 8 * chunk + e] : 0.0;
+    if (chunk == 0 && j < c) bin = b64[(int64_t)head * c + j];
+  } else if (is_l) {
+    const int a = (int)(rid - rows);
+    const float* L = chol + (int64_t)head * kD * kD;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vin[e] = (double)L[(8 * chunk + e) * kD + a];
+  }
+  const HeadScale hs = head_scale_wg(part_a, head, nwg_a);
+  if (blockIdx.x == 0 && t == 0) hsc[head] = hs;  // for the later passes
   double rho2 = 0.0, nu2 = 0.0;
-  if (rid < rows) {
+  if (is_row) {
     const int64_t j = rid;
     const int64_t tile = j / kRows;
     const int i = (int)(j % kRows);
     half8 f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int a = 8 * chunk + e;
-      const double sv = (j < c) ? (double)hs.S * v64[((int64_t)head * c + j) * kD + a] : 0.0;
+      const double sv = (j < c) ? (double)hs.S * vin[e] : 0.0;
       const _Float16 q = (_Float16)sv;  // fp64 -> fp16, round to nearest even
       const double dq = (double)q;
       rho2 += (sv - dq) * (sv - dq);
@@ -370,20 +386,18 @@ __global__ __launch_bounds__(256) void enc_prep_frag(const double* __restrict__ 
       const int bh = (i >> 2) & 1;
       const int r = (i >> 3) * 4 + (i & 3);
       bias[((int64_t)head * T + tile) * 32 + bh * 16 + r] =
-          (j < c) ? (float)(-0.5 * (double)hs.S * b64[(int64_t)head * c + j]) : kPadBias;
+          (j < c) ? (float)(-0.5 * (double)hs.S * bin) : kPadBias;
     }
-  } else if (want_l && rid < rows + kD) {
+  } else if (is_l) {
     // Row a of L^T (output z_a = sum_b k_b L_ba) as A-operand fragments: 4 output tiles of
     // 32 rows, each as two tiles, the fp16 high parts (tile 2 tz) and the residuals (2 tz + 1),
     // so that the coarse pass streams them as two stages of four tiles.
     const int a = (int)(rid - rows);
-    const float* L = chol + (int64_t)head * kD * kD;
     const int tile = a / kRows, i = a % kRows;
     half8 fh, fl;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int b = 8 * chunk + e;
-      const double x = (double)hs.SL * (double)L[b * kD + a];
+      const double x = (double)hs.SL * vin[e];
       const _Float16 qh = (_Float16)x;
       fh[e] = qh;
       fl[e] = (_Float16)(x - (double)qh);
