@@ -543,6 +543,7 @@ __global__ __launch_bounds__(256) void sel_scatter(const unsigned* __restrict__ 
   const float inv = info[head].inv_scale;
   const unsigned long long thr = info[head].thr;
   const int n_r = info[head].n_r;
+  const unsigned blk_base = offsets[(int64_t)head * nblk + blk];  // read up front, beside the record
   const int64_t hoff = (int64_t)head * n;
   const int64_t i_begin = (int64_t)blk * kBlock;
   constexpr int kPer = kBlock / 256;  // consecutive elements per thread
@@ -574,7 +575,7 @@ __global__ __launch_bounds__(256) void sel_scatter(const unsigned* __restrict__ 
   __syncthreads();
   int wbase = 0;
   for (int w = 0; w < (t >> 6); ++w) wbase += wsum[w];
-  const int64_t sel_before = (int64_t)offsets[(int64_t)head * nblk + blk] + wbase + incl - cnt;
+  const int64_t sel_before = (int64_t)blk_base + wbase + incl - cnt;
   int64_t rpos = sel_before;
   int64_t bpos = my0 - sel_before;  // non-selected before my0
   int32_t* rh = ret + (int64_t)head * n_r;
