@@ -416,7 +416,9 @@ __global__ __launch_bounds__(kThreshThreads) void sel_thresh(int64_t n, int nblk
     if (by_rank) {
       // Candidates in pairs (2c, 2c + 1), P threads a pair (at most 8), each counting the
       // larger keys (all distinct) in its part of the list for both; the candidate with r - 1
-      // larger ones is it.  Slots past n_cand hold 0, which counts nothing.
+      // larger ones is it.  Part q holds every P-th slot from q, so the P parts a wave reads
+      // at once are adjacent slots (distinct banks); slots past n_cand hold 0, which counts
+      // nothing.
       const unsigned pairs = (n_cand + 1u) / 2u;
       int lp = 0;
       while (lp < 3 && (pairs << (lp + 1)) <= (unsigned)NT) ++lp;
@@ -431,10 +433,10 @@ __global__ __launch_bounds__(kThreshThreads) void sel_thresh(int64_t n, int nblk
       if (c < (int)pairs) {  // waves past the last pair skip the loop
         m0 = su[2 * c];
         m1 = two ? su[2 * c + 1] : ~0ull;
-        for (int i = q * L; i < q * L + L; i += 8) {
+        for (int i = 0; i < L; i += 8) {  // part q: slots q, q + P, q + 2P, ...
           unsigned long long x[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = su[i + e];
+          for (int e = 0; e < 8; ++e) x[e] = su[(i + e) * P + q];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             r0 += x[e] > m0 ? 1u : 0u;
