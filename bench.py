@@ -943,7 +943,7 @@ def pmc_summarize(root, command):
 
 def trace_summarize(root, command, name="encode_stress"):
     """Kernel statistics of a rocprofv3 --kernel-trace --stats run, read from the rocpd
-    database it writes: calls, mean / min / max duration and registers per kernel, into
+    database it writes: calls, mean / median / min / max duration and registers per kernel, into
     profiles/<name>_trace.md."""
     import sqlite3
 
@@ -957,6 +957,12 @@ def trace_summarize(root, command, name="encode_stress"):
         "max(grid_x), max(workgroup_x) from kernels group by name").fetchall()
     total = sum(r[5] for r in rows)
     rows.sort(key=lambda r: -r[5])
+    med = {}
+    for nm, dur in con.execute("select name, duration from kernels"):
+        med.setdefault(nm, []).append(dur)
+    for nm in med:
+        d = sorted(med[nm])
+        med[nm] = d[len(d) // 2] if len(d) % 2 else 0.5 * (d[len(d) // 2 - 1] + d[len(d) // 2])
 
     def short(name):
         for pre in ("void ", "a2ats::(anonymous namespace)::"):
@@ -987,12 +993,12 @@ def trace_summarize(root, command, name="encode_stress"):
     with open(path, "w") as f:
         f.write("# %s: kernel trace statistics\n\n"
                 "Command:\n\n```\n%s\n```\n\n" % (name, command))
-        f.write("| kernel | calls | average us | min us | max us | share % | VGPR | AGPR | SGPR | LDS B | grid | block |\n"
-                "|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+        f.write("| kernel | calls | average us | median us | min us | max us | share % | VGPR | AGPR | SGPR | LDS B | grid | block |\n"
+                "|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
         for r in rows:
-            f.write("| %s | %d | %.2f | %.2f | %.2f | %.2f | %s | %s | %s | %s | %s | %s |\n" % (
-                short(r[0]), r[1], r[2] / 1e3, r[3] / 1e3, r[4] / 1e3, 100.0 * r[5] / total,
-                r[6], r[7], r[8], r[9], r[10], r[11]))
+            f.write("| %s | %d | %.2f | %.2f | %.2f | %.2f | %.2f | %s | %s | %s | %s | %s | %s |\n" % (
+                short(r[0]), r[1], r[2] / 1e3, med[r[0]] / 1e3, r[3] / 1e3, r[4] / 1e3,
+                100.0 * r[5] / total, r[6], r[7], r[8], r[9], r[10], r[11]))
     print(json.dumps({"written": path}))
 
 
