@@ -396,6 +396,12 @@ class TestSelectRetrieval:
         nr = oracle.retrieval_count(n, f)
         assert np.array_equal(ret.cpu().numpy()[0], np.arange(nr))
 
+    def test_many_small_heads(self):
+        # 200 heads of 777 keys: one partial histogram and one block a head, so every launch's
+        # head index comes from the workgroup index alone
+        keys = synth.keys(147, 200, 777, "bf16")
+        run_split(keys, keys.values[:, 3].copy(), 0.13, "200 heads")
+
     @pytest.mark.parametrize("n", [100_001, 262_144, 300_000])
     def test_large_heads(self, n):
         # 100001: a ragged head of unaligned rows; 262144 and 300000: 500 to 1000 keys in the
