@@ -55,6 +55,7 @@ constexpr int kBlRows = 4;     // rows per dot workgroup
 constexpr int kBlTile = 256;   // centroids per dot workgroup (one per thread)
 constexpr int kBlDims = 32;    // dimensions per codebook slice
 constexpr size_t kBlWsCap = (size_t)64 << 20;  // workspace bound (e and g of one batch)
+constexpr int kPickPre = 8;    // e and g entries a blend_pick thread reads up front
 
 __global__ __launch_bounds__(kThreads) void blend_dots(
     const void* __restrict__ x, int xdt, int64_t n, int d, const void* __restrict__ query,
@@ -157,25 +158,45 @@ __global__ __launch_bounds__(kThreads) void blend_pick(
   const int64_t head = item / nrb, row = (item % nrb) * kBlRows + r;
   if (row >= n) return;      // uniform per workgroup
   const int64_t qoff = (head * nq + (nq == 1 ? 0 : row)) * d;
+  const double* er = e_in + ((item - rb0) * kBlRows + r) * c;
+  const double* gr = g_in + ((item - rb0) * kBlRows + r) * c;
+  // the row's first kPickPre * kThreads entries are read with the query, before the
+  // reductions, so that the reads are in flight together (the rest, for larger codebooks,
+  // in the loops below)
+  double ev[kPickPre], gv[kPickPre];
+#pragma unroll
+  for (int i = 0; i < kPickPre; ++i) {
+    const int64_t j = t + (int64_t)kThreads * i;
+    ev[i] = j < c ? er[j] : 0.0;
+    gv[i] = j < c ? gr[j] : 0.0;
+  }
   double qv = 0.0;
   if (t < d) qv = (double)load_elem(query, xdt, qoff + t);
   const double qn = sqrt(block_sum(qv * qv, red));
-  const double* er = e_in + ((item - rb0) * kBlRows + r) * c;
-  const double* gr = g_in + ((item - rb0) * kBlRows + r) * c;
+  constexpr int64_t kHeld = (int64_t)kPickPre * kThreads;
   double emax = 0.0;
-  for (int64_t j = t; j < c; j += kThreads) emax = fmax(emax, er[j]);
+#pragma unroll
+  for (int i = 0; i < kPickPre; ++i)
+    if (t + (int64_t)kThreads * i < c) emax = fmax(emax, ev[i]);
+  for (int64_t j = kHeld + t; j < c; j += kThreads) emax = fmax(emax, er[j]);
   emax = block_max(emax, red);
   double bs = -INFINITY;
   int bj = 0x7FFFFFFF;
-  for (int64_t j = t; j < c; j += kThreads) {
-    const double cosv = qn > 0.0 ? gr[j] / qn : 0.0;
-    const double err = emax > 0.0 ? er[j] / emax : 0.0;
+  auto consider = [&](int64_t j, double e, double gq) {
+    const double cosv = qn > 0.0 ? gq / qn : 0.0;
+    const double err = emax > 0.0 ? e / emax : 0.0;
     const double s = beta * (-err) + (1.0 - beta) * cosv;
     if (better(s, (int)j, bs, bj)) {
       bs = s;
       bj = (int)j;
     }
+  };
+#pragma unroll
+  for (int i = 0; i < kPickPre; ++i) {
+    const int64_t j = t + (int64_t)kThreads * i;
+    if (j < c) consider(j, ev[i], gv[i]);
   }
+  for (int64_t j = kHeld + t; j < c; j += kThreads) consider(j, er[j], gr[j]);
   for (int o = 32; o > 0; o >>= 1) {
     const double os = __shfl_xor(bs, o);
     const int oj = __shfl_xor(bj, o);
