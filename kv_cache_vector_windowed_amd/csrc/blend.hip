@@ -115,9 +115,13 @@ __global__ __launch_bounds__(kThreads) void blend_dots(
     if (a0 + kBlDims < d) load_slice(a0 + kBlDims);
     auto dim_step = [&](int aa) {
       const double cv = (double)ct[aa][t];
-      const double2* p = reinterpret_cast<const double2*>(&xq[a0 + aa][0]);
-      const double2 x01 = p[0], x23 = p[1], q01 = p[2], q23 = p[3];
-      const double xs[4] = {x01.x, x01.y, x23.x, x23.y}, qs[4] = {q01.x, q01.y, q23.x, q23.y};
+      const double* p = &xq[a0 + aa][0];
+      double xs[kBlRows], qs[kBlRows];
+#pragma unroll
+      for (int r = 0; r < kBlRows; ++r) {
+        xs[r] = p[r];
+        qs[r] = p[kBlRows + r];
+      }
       cn2 = __fma_rn(cv, cv, cn2);
 #pragma unroll
       for (int r = 0; r < kBlRows; ++r) {
